@@ -1,0 +1,90 @@
+"""Seeded synthetic inputs for the compressed-attention hot path.
+
+This module only draws random numbers and lays them out in the shapes of the
+workloads; it contains none of the method's arithmetic (no compression, no
+quantisation, no scoring, no attention).  Both the HIP path and the CPU
+oracle consume what it returns, so the two sides always see identical bytes.
+
+Every tensor comes from its own child of ``numpy.random.SeedSequence(seed)``,
+spawned in a fixed order, drawn as float32 ``standard_normal`` and then cast
+to the storage type (bf16 casts use torch's round-to-nearest-even).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from .configs import Workload, get_workload
+
+
+def _rng_children(seed: int, n: int):
+    return [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(n)]
+
+
+def _normal(rng: np.random.Generator, shape, dtype: torch.dtype) -> torch.Tensor:
+    a = rng.standard_normal(size=shape, dtype=np.float32)
+    t = torch.from_numpy(a)
+    return t if dtype == torch.float32 else t.to(dtype)
+
+
+# Fixed draw order.  Adding a field appends to the end so earlier draws never move.
+_FIELDS = ("q", "kv", "gate", "k_idx", "k_gate", "q_idx", "w", "sinks", "kv_raw",
+           "hca_gate", "q_hca", "sinks_hca")
+
+
+def make_inputs(w: Workload | str, **overrides) -> dict:
+    """Return a dict of CPU tensors for workload ``w`` (a name or a Workload).
+
+    Keys (present when the workload uses them):
+      q       [B,Q,H,D]   query heads (before norm / rotation)
+      kv      decode: compressed KV cache [B,N,D];  prefill: raw KV tokens [B,T,D]
+      gate    [B,T]       compressor gate logits for ``kv`` (prefill only)
+      k_idx   decode: compressed indexer keys [B,N,dI] (float32, before fp8);
+              prefill: raw indexer keys [B,T,dI]
+      k_gate  [B,T]       compressor gate logits for ``k_idx`` (prefill only)
+      q_idx   [B,Q,HI,dI] indexer queries
+      w       [B,Q,HI]    indexer head weights (float32)
+      sinks   [H]         per-head sink logits (float32)
+      kv_raw  [B,R,D]     raw (uncompressed) KV rows for the sliding window
+      raw_pos0 [B]        absolute position of kv_raw row 0 (int32)
+      q_pos   [B,Q]       absolute query positions (int32)
+      hca_gate, q_hca, sinks_hca   the HCA layer's own gate, queries and sinks (prefill)
+    """
+    if isinstance(w, str):
+        w = get_workload(w, **overrides)
+    elif overrides:
+        w = w.replace(**overrides)
+    rngs = dict(zip(_FIELDS, _rng_children(w.seed, len(_FIELDS))))
+    act = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    B, Q, H, D = w.B, w.Q, w.H, w.D
+    out: dict = {"workload": w}
+    out["q"] = _normal(rngs["q"], (B, Q, H, D), act)
+    if w.prefill:
+        T = w.T
+        out["kv"] = _normal(rngs["kv"], (B, T, D), act)
+        out["gate"] = _normal(rngs["gate"], (B, T), torch.float32)
+        if w.csa:
+            out["k_idx"] = _normal(rngs["k_idx"], (B, T, w.dI), act)
+            out["k_gate"] = _normal(rngs["k_gate"], (B, T), torch.float32)
+        if w.hca:
+            out["hca_gate"] = _normal(rngs["hca_gate"], (B, T), torch.float32)
+            out["q_hca"] = _normal(rngs["q_hca"], (B, Q, H, D), act)
+            out["sinks_hca"] = _normal(rngs["sinks_hca"], (H,), torch.float32)
+        # the raw window source is the raw KV itself: row p holds position p
+        out["kv_raw"] = out["kv"]
+        out["raw_pos0"] = torch.zeros(B, dtype=torch.int32)
+        out["q_pos"] = (w.q_pos0 + torch.arange(Q, dtype=torch.int32)).repeat(B, 1)
+    else:
+        N = w.N
+        out["kv"] = _normal(rngs["kv"], (B, N, D), act)
+        if w.csa:
+            out["k_idx"] = _normal(rngs["k_idx"], (B, N, w.dI), torch.float32)
+        R = w.n_win
+        out["kv_raw"] = _normal(rngs["kv_raw"], (B, R, D), act)
+        out["q_pos"] = torch.full((B, Q), w.t, dtype=torch.int32)
+        out["raw_pos0"] = torch.full((B,), w.t - R + 1, dtype=torch.int32)
+    if w.csa:
+        out["q_idx"] = _normal(rngs["q_idx"], (B, Q, w.HI, w.dI), act)
+        out["w"] = _normal(rngs["w"], (B, Q, w.HI), torch.float32)
+    out["sinks"] = _normal(rngs["sinks"], (H,), torch.float32)
+    return out

@@ -1,0 +1,211 @@
+"""CPU oracle of the compressed-attention hot path -- TEST INFRASTRUCTURE.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
+of ``bench.py`` may import this package.  The product path (the HIP library
+and its Python binding) never calls it, and the two share no code.
+
+The arithmetic lives in ``cakv_oracle.c`` (plain C, fp64 except for the
+canonical fp32 indexer score); this module only marshals numpy/torch arrays
+through ctypes.  See the C file's header for the pages each step follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "cakv_oracle.c")
+_SO = os.path.join(_HERE, "libcakv_oracle.so")
+
+GCC_FLAGS = ["-O2", "-ffp-contract=off", "-mfma", "-fopenmp", "-shared", "-fPIC", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no contraction)."""
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        tmp = _SO + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _SO)
+    return _SO
+
+
+_lib = None
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+class AttnParams(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int32), ("n_win", ctypes.c_int32), ("rope_dims", ctypes.c_int32),
+                ("entry_pos_offset", ctypes.c_int32), ("rope_base", ctypes.c_double),
+                ("softmax_scale", ctypes.c_double), ("rms_eps", ctypes.c_double)]
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_SO)
+        lib.oracle_kv_compress.argtypes = [_p, ctypes.c_int, _p, _i64, _i64, _i64, ctypes.c_int, _p]
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_int]
+        lib.oracle_e4m3_decode.restype = ctypes.c_double
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        lib.oracle_q8_quantize.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p]
+        lib.oracle_indexer_scores.argtypes = [_p, ctypes.c_int, _p, _p, _p, _p, _p, _i64, _i64, _i64,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int, _p, _i64, _p, _p]
+        lib.oracle_topk.argtypes = [_p, _p, _i64, _i64, ctypes.c_int, _p]
+        lib.oracle_attention.argtypes = [ctypes.POINTER(AttnParams), _p, _p, _p, ctypes.c_int, _p, _p,
+                                         _p, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
+                                         _i64, _p, _i64, _p, _p]
+        _lib = lib
+    return _lib
+
+
+def _act(t) -> tuple[np.ndarray, int]:
+    """(contiguous host array, dtype code): float32 -> 0, bfloat16 bits -> 1."""
+    if isinstance(t, torch.Tensor):
+        t = t.detach().cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy(), 1
+        return t.to(torch.float32).numpy(), 0
+    return np.ascontiguousarray(t, dtype=np.float32), 0
+
+
+def _np(t, dtype) -> np.ndarray:
+    if isinstance(t, torch.Tensor):
+        t = t.detach().cpu().contiguous().numpy()
+    return np.ascontiguousarray(t, dtype=dtype)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what}: invalid input (rc={rc})")
+
+
+def kv_compress(x, gate, m: int) -> np.ndarray:
+    """Softmax-weighted compression of every m tokens; fp64 [B, T//m, D]."""
+    lib = _load()
+    xa, xd = _act(x)
+    g = _np(gate, np.float32)
+    B, T, D = xa.shape
+    out = np.empty((B, T // m, D), dtype=np.float64)
+    _check(lib.oracle_kv_compress(_ptr(xa), xd, _ptr(g), B, T, D, m, _ptr(out)), "kv_compress")
+    return out
+
+
+def e4m3_decode(code: int) -> float:
+    return _load().oracle_e4m3_decode(int(code))
+
+
+def e4m3_encode(v: float) -> int:
+    return _load().oracle_e4m3_encode(float(v))
+
+
+def q8_quantize(c) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row power-of-two scale + E4M3 codes: (codes uint8 [..., D], scale f32 [...])."""
+    lib = _load()
+    if isinstance(c, torch.Tensor):
+        c = c.detach().cpu().numpy()
+    is64 = c.dtype == np.float64
+    a = np.ascontiguousarray(c, dtype=np.float64 if is64 else np.float32)
+    D = a.shape[-1]
+    n = a.size // D
+    codes = np.empty(a.shape, dtype=np.uint8)
+    scale = np.empty(a.shape[:-1], dtype=np.float32)
+    _check(lib.oracle_q8_quantize(_ptr(a), int(is64), n, D, _ptr(codes), _ptr(scale)), "q8")
+    return codes, scale
+
+
+def q8_dequantize(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """code * scale as float32 (exact)."""
+    table = np.array([e4m3_decode(c) for c in range(256)], dtype=np.float32)
+    return table[codes] * scale[..., None]
+
+
+def _rows(rows, B, Q):
+    if rows is None:
+        return None, B * Q
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    return r, r.size
+
+
+def indexer_scores(q_idx, w, q_pos, m: int, k_f32=None, k_code=None, k_scale=None, rows=None):
+    """Canonical fp32 scores [n_rows, N] (NaN where not visible) and n_vis [n_rows]."""
+    lib = _load()
+    qa, qd = _act(q_idx)
+    B, Q, HI, dI = qa.shape
+    wa = _np(w, np.float32)
+    qp = _np(q_pos, np.int32)
+    if k_code is not None:
+        kc = _np(k_code, np.uint8)
+        ks = _np(k_scale, np.float32)
+        kf = None
+        N = kc.shape[1]
+    else:
+        kf = _np(k_f32, np.float32)
+        kc = ks = None
+        N = kf.shape[1]
+    r, n = _rows(rows, B, Q)
+    scores = np.empty((n, N), dtype=np.float32)
+    nvis = np.empty((n,), dtype=np.int32)
+    _check(lib.oracle_indexer_scores(_ptr(qa), qd, _ptr(wa), _ptr(kf), _ptr(kc), _ptr(ks), _ptr(qp),
+                                     B, Q, N, HI, dI, m, _ptr(r), n, _ptr(scores), _ptr(nvis)),
+           "indexer_scores")
+    return scores, nvis
+
+
+def topk(scores: np.ndarray, n_vis: np.ndarray, k: int) -> np.ndarray:
+    lib = _load()
+    s = np.ascontiguousarray(scores, dtype=np.float32)
+    nv = np.ascontiguousarray(n_vis, dtype=np.int32)
+    n, N = s.shape
+    idx = np.empty((n, k), dtype=np.int32)
+    _check(lib.oracle_topk(_ptr(s), _ptr(nv), n, N, k, _ptr(idx)), "topk")
+    return idx
+
+
+def indexer_topk(q_idx, w, q_pos, m: int, k: int, k_f32=None, k_code=None, k_scale=None, rows=None):
+    s, nv = indexer_scores(q_idx, w, q_pos, m, k_f32=k_f32, k_code=k_code, k_scale=k_scale, rows=rows)
+    return topk(s, nv, k)
+
+
+def attention(q, kv_c, kv_raw, raw_pos0, q_pos, sinks, *, idx=None, m: int, n_win: int,
+              rope_dims: int, rope_base: float = 10000.0, entry_pos_offset: int = 0,
+              softmax_scale: float = 0.0, rms_eps: float = 1e-6, gamma_q=None, gamma_kv=None,
+              rows=None):
+    """Sink-augmented MQA over compressed entries (idx given: sparse, else all visible)
+    plus the raw window.  Returns (out fp64 [n_rows,H,D], lse fp64 [n_rows,H])."""
+    lib = _load()
+    qa, qd = _act(q)
+    ka, kd = _act(kv_c)
+    ra, rd = _act(kv_raw)
+    if not (qd == kd == rd):
+        raise ValueError("q, kv_c and kv_raw must share one storage type")
+    B, Q, H, D = qa.shape
+    N = ka.shape[1]
+    R = ra.shape[1]
+    ia = None
+    K = 0
+    if idx is not None:
+        ia = _np(idx, np.int32)
+        K = ia.shape[-1]
+    rp = _np(raw_pos0, np.int32)
+    qp = _np(q_pos, np.int32)
+    sk = _np(sinks, np.float32)
+    gq = None if gamma_q is None else _np(gamma_q, np.float32)
+    gk = None if gamma_kv is None else _np(gamma_kv, np.float32)
+    r, n = _rows(rows, B, Q)
+    out = np.empty((n, H, D), dtype=np.float64)
+    lse = np.empty((n, H), dtype=np.float64)
+    prm = AttnParams(m, n_win, rope_dims, entry_pos_offset, rope_base, softmax_scale, rms_eps)
+    _check(lib.oracle_attention(ctypes.byref(prm), _ptr(qa), _ptr(ka), _ptr(ia), K, _ptr(ra), _ptr(rp),
+                                _ptr(qp), _ptr(sk), _ptr(gq), _ptr(gk), qd, B, Q, H, D, N, R, _ptr(r), n,
+                                _ptr(out), _ptr(lse)), "attention")
+    return out, lse

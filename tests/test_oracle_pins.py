@@ -1,0 +1,434 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+closed forms, library routines (torch SDPA, torch's fp8 cast, numpy sorting),
+the counts the pages print (tests/golden/page_counts.txt), hand-derived
+values (tests/golden/indexer_canonical_order.txt), invariants and fp64
+brute force on tiny inputs.  Each test names the mistake it would catch.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_counts():
+    vals = {}
+    with open(os.path.join(GOLDEN, "page_counts.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                name, value = line.split()[:2]
+                vals[name] = int(value)
+    return vals
+
+
+# --------------------------------------------------------------------------
+# O1 compression
+# --------------------------------------------------------------------------
+
+def test_compress_counts_match_pages():
+    """1M tokens compress to ~262,000 CSA entries and 8,192 HCA entries."""
+    g = _golden_counts()
+    T = g["context_tokens"]
+    x = torch.zeros(1, T, 1)
+    gate = torch.zeros(1, T)
+    assert oracle.kv_compress(x, gate, g["csa_ratio"]).shape[1] == g["csa_entries_at_1m"]
+    assert oracle.kv_compress(x, gate, g["hca_ratio"]).shape[1] == g["hca_entries_at_1m"]
+    # a partial trailing block produces no entry
+    assert oracle.kv_compress(torch.zeros(1, 131, 1), torch.zeros(1, 131), 4).shape[1] == 32
+
+
+def test_compress_equal_logits_is_block_mean():
+    """Equal gate logits give uniform weights: the block mean (catches a dropped normaliser)."""
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((2, 64, 16)).astype(np.float32)
+    gate = np.full((2, 64), 0.37, np.float32)
+    for m in (1, 4, 16, 64):
+        got = oracle.kv_compress(x, gate, m)
+        want = x.astype(np.float64).reshape(2, 64 // m, m, 16).mean(axis=2)
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-14)
+
+
+def test_compress_known_weights():
+    """Gates [0, ln 3] give weights 1/4 and 3/4 (hand-derived; catches sign of the exponent)."""
+    x = np.array([[[4.0], [8.0]]], np.float32)
+    gate = np.array([[0.0, math.log(3.0)]], np.float32)
+    got = oracle.kv_compress(x, gate, 2)[0, 0, 0]
+    w1 = 3.0 / (1.0 + 3.0)  # exp(ln 3) with ln 3 rounded to fp32 is 3 within 1e-7
+    assert abs(got - (4.0 * (1 - w1) + 8.0 * w1)) < 1e-6
+
+
+def test_compress_dominant_token_and_identity():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((1, 32, 8)).astype(np.float32)
+    gate = np.full((1, 32), -30.0, np.float32)
+    gate[0, 2::4] = 30.0  # third token of each block dominates by e^60
+    got = oracle.kv_compress(x, gate, 4)
+    np.testing.assert_allclose(got[0], x[0, 2::4], rtol=1e-20, atol=1e-20)
+    # m = 1 is the identity whatever the gates
+    np.testing.assert_array_equal(oracle.kv_compress(x, rng.standard_normal((1, 32)).astype(np.float32), 1),
+                                  x.astype(np.float64))
+
+
+def test_compress_linear_and_gate_shift_invariant():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((1, 48, 8)).astype(np.float32)
+    y = rng.standard_normal((1, 48, 8)).astype(np.float32)
+    gate = rng.standard_normal((1, 48)).astype(np.float32)
+    cx, cy = oracle.kv_compress(x, gate, 4), oracle.kv_compress(y, gate, 4)
+    np.testing.assert_allclose(oracle.kv_compress(x + y, gate, 4), cx + cy, atol=1e-6)
+    # constant sequence stays constant
+    c = oracle.kv_compress(np.full((1, 48, 8), 2.5, np.float32), gate, 4)
+    np.testing.assert_allclose(c, 2.5, rtol=1e-14)
+    # adding a constant to the gate logits does not change softmax weights
+    np.testing.assert_allclose(oracle.kv_compress(x, gate + 5.0, 4), cx, atol=1e-6)
+
+
+def test_compress_bf16_input_exact_values():
+    x = torch.randn(1, 16, 8).to(torch.bfloat16)
+    gate = torch.randn(1, 16)
+    a = oracle.kv_compress(x, gate, 4)
+    b = oracle.kv_compress(x.float(), gate, 4)
+    np.testing.assert_array_equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# fp8 E4M3 and the per-entry quantiser
+# --------------------------------------------------------------------------
+
+def test_e4m3_decode_all_codes_match_torch():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.e4m3_decode(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and np.array_equal(nan, np.isnan(got))
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    assert np.nanmax(got) == 448.0
+
+
+def test_e4m3_encode_matches_torch_rne():
+    rng = np.random.default_rng(4)
+    v = np.concatenate([rng.standard_normal(20000) * 50, rng.standard_normal(5000) * 1e-2,
+                        rng.uniform(-448, 448, 5000)])
+    # exact midpoints between neighbouring codes exercise ties-to-even
+    mags = np.array([oracle.e4m3_decode(c) for c in range(0x7F)])
+    mids = (mags[1:] + mags[:-1]) / 2
+    v = np.concatenate([v, mids, -mids]).astype(np.float32)
+    got = np.array([oracle.e4m3_encode(float(x)) for x in v], dtype=np.uint8)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_e4m3_saturates():
+    assert oracle.e4m3_encode(448.0) == 0x7E
+    assert oracle.e4m3_encode(470.0) == 0x7E
+    assert oracle.e4m3_encode(-1e30) == 0xFE
+
+
+def test_q8_scale_rule_and_exact_dequant():
+    c = np.array([[448.0, -1.0], [448.0001, 3.0], [224.0, 0.0], [0.0, 0.0], [-1e-30, 2e-31]], np.float64)
+    codes, scale = oracle.q8_quantize(c)
+    assert list(scale[:4]) == [1.0, 2.0, 0.5, 1.0]
+    assert codes[3].tolist() == [0, 0]
+    assert scale[4] == 2.0 ** -108  # 448 * 2^-109 < 1e-30 <= 448 * 2^-108
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((300, 128)) * rng.uniform(1e-3, 1e3, (300, 1))
+    codes, scale = oracle.q8_quantize(x)
+    deq = oracle.q8_dequantize(codes, scale).astype(np.float64)
+    # every row uses the top of the range and stays within half a code step of the input
+    assert np.all(np.abs(x).max(1) <= 448.0 * scale) and np.all(np.abs(x).max(1) > 224.0 * scale)
+    step = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(x) / scale[:, None], 2.0 ** -6))) - 3),
+                      2.0 ** -9) * scale[:, None]
+    assert np.all(np.abs(deq - x) <= step / 2 + 1e-300)
+    # dequantisation is exact in fp32: code value times a power of two
+    table = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(deq, table[codes] * scale[:, None].astype(np.float64))
+
+
+# --------------------------------------------------------------------------
+# O2 indexer score and O3 top-k
+# --------------------------------------------------------------------------
+
+def test_indexer_canonical_fma_order_golden():
+    with open(os.path.join(GOLDEN, "indexer_canonical_order.txt")) as f:
+        want = [float.fromhex(ln.split()[1]) for ln in f if ln.startswith("score_hex")][0]
+    q = np.array([[[[-1.0, 1.0 + 2.0 ** -12]]]], np.float32)
+    k = np.array([[[1.0, 1.0 + 2.0 ** -12]]], np.float32)
+    s, nv = oracle.indexer_scores(q, np.ones((1, 1, 1), np.float32), np.array([[4]], np.int32), 4, k_f32=k)
+    assert nv[0] == 1 and s[0, 0] == np.float32(want)
+
+
+def test_indexer_single_head_is_relu_dot_and_visibility():
+    """H_I = 1, w = 1: score = ReLU(q . k); ranking equals numpy's argsort on fp64 dots."""
+    rng = np.random.default_rng(6)
+    N, dI, m = 500, 16, 4
+    q = rng.standard_normal((1, 3, 1, dI)).astype(np.float32)
+    k = rng.standard_normal((1, N, dI)).astype(np.float32)
+    qpos = np.array([[4 * 400, 4 * 400 + 3, 5]], np.int32)
+    s, nv = oracle.indexer_scores(q, np.ones((1, 3, 1), np.float32), qpos, m, k_f32=k)
+    assert nv.tolist() == [400, 400, 1]
+    assert np.all(np.isnan(s[0, 400:])) and np.all(np.isnan(s[2, 1:]))
+    dots = np.maximum(k[0].astype(np.float64) @ q[0, 0, 0].astype(np.float64), 0.0)
+    np.testing.assert_allclose(s[0, :400], dots[:400], rtol=1e-5, atol=1e-5)
+    pos = dots[:400] > 0
+    order = np.argsort(-dots[:400][pos], kind="stable")
+    idx = oracle.topk(s, nv, 50)
+    want = np.sort(np.flatnonzero(pos)[order[:50]])
+    np.testing.assert_array_equal(idx[0], want)
+
+
+def test_indexer_fp64_brute_force_and_permutation():
+    rng = np.random.default_rng(7)
+    B, Q, N, HI, dI, m = 2, 2, 64, 4, 8, 1
+    q = rng.standard_normal((B, Q, HI, dI)).astype(np.float32)
+    w = rng.standard_normal((B, Q, HI)).astype(np.float32)
+    k = rng.standard_normal((B, N, dI)).astype(np.float32)
+    qpos = np.full((B, Q), N, np.int32)
+    s, _ = oracle.indexer_scores(q, w, qpos, m, k_f32=k)
+    for b in range(B):
+        for t in range(Q):
+            dots = np.einsum("hd,nd->hn", q[b, t].astype(np.float64), k[b].astype(np.float64))
+            ref = (w[b, t].astype(np.float64)[:, None] * np.maximum(dots, 0)).sum(0)
+            scale = (np.abs(w[b, t])[:, None] * np.abs(dots)).sum(0) + 1e-30
+            assert np.all(np.abs(s[b * Q + t] - ref) <= 1e-6 * scale)
+    perm = rng.permutation(N)
+    s2, _ = oracle.indexer_scores(q, w, qpos, m, k_f32=k[:, perm])
+    np.testing.assert_array_equal(s2, s[:, perm])
+
+
+def test_indexer_fp8_keys_use_exact_dequant():
+    rng = np.random.default_rng(8)
+    kraw = rng.standard_normal((1, 40, 16)).astype(np.float32)
+    codes, scale = oracle.q8_quantize(kraw)
+    deq = oracle.q8_dequantize(codes, scale)
+    q = torch.randn(1, 1, 2, 16).to(torch.bfloat16)
+    w = rng.standard_normal((1, 1, 2)).astype(np.float32)
+    qpos = np.array([[160]], np.int32)
+    a, _ = oracle.indexer_scores(q, w, qpos, 4, k_code=codes, k_scale=scale)
+    b, _ = oracle.indexer_scores(q.float(), w, qpos, 4, k_f32=deq)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_topk_matches_lexsort_with_ties():
+    rng = np.random.default_rng(9)
+    n, N, k = 6, 3000, 100
+    s = rng.integers(-40, 40, size=(n, N)).astype(np.float32)  # many exact ties
+    s[0] = 1.0  # all equal: lowest indices win
+    s[1, ::2] = -0.0
+    s[1, 1::2] = 0.0  # -0 and +0 compare equal
+    nv = np.array([N, N, N, 57, 100, 0], np.int32)
+    idx = oracle.topk(s, nv, k)
+    for r in range(n):
+        v = nv[r]
+        order = np.lexsort((np.arange(v), -s[r, :v].astype(np.float64)))
+        want = np.sort(order[:min(k, v)])
+        assert np.array_equal(idx[r, :len(want)], want)
+        assert np.all(idx[r, len(want):] == -1)
+    assert idx[0].tolist() == list(range(k))
+    assert idx[1].tolist() == list(range(k))
+    assert idx[3].tolist() == list(range(57)) + [-1] * (k - 57)
+
+
+def test_topk_is_associative_over_chunks():
+    """Top-k of the union of per-chunk top-ks equals the global top-k."""
+    rng = np.random.default_rng(10)
+    N, k = 4096, 64
+    s = (rng.standard_normal(N) * 3).round(1).astype(np.float32)
+    full = oracle.topk(s[None], np.array([N], np.int32), k)[0]
+    cand = []
+    for c in range(0, N, 512):
+        loc = oracle.topk(s[None, c:c + 512], np.array([512], np.int32), k)[0] + c
+        cand.extend(loc.tolist())
+    cand = np.array(cand)
+    sub = s[cand]
+    order = np.lexsort((cand, -sub.astype(np.float64)))
+    np.testing.assert_array_equal(np.sort(cand[order[:k]]), full)
+
+
+# --------------------------------------------------------------------------
+# O4 attention
+# --------------------------------------------------------------------------
+
+def _pm1(rng, shape):
+    """Entries +-1: every row already has mean square 1, so RMSNorm with eps 0 is the identity."""
+    return (rng.integers(0, 2, size=shape) * 2 - 1).astype(np.float32)
+
+
+def _sdpa(q, k, v, scale, causal=False):
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=causal, scale=scale).numpy()
+
+
+def test_attention_no_sink_is_textbook_softmax_attention():
+    """Sink -inf, no rotation, pre-normalised rows: equals torch SDPA on K = V (fp64)."""
+    rng = np.random.default_rng(11)
+    H, D, N, m, win = 4, 16, 10, 4, 3
+    t = 4 * N + 2
+    q = _pm1(rng, (1, 1, H, D))
+    kv = _pm1(rng, (1, N, D))
+    raw = _pm1(rng, (1, win, D))
+    sinks = np.full(H, -np.inf, np.float32)
+    out, lse = oracle.attention(q, kv, raw, np.array([t - win + 1], np.int32), np.array([[t]], np.int32),
+                                sinks, m=m, n_win=win, rope_dims=0, rms_eps=0.0)
+    K = np.concatenate([kv[0], raw[0]]).astype(np.float64)
+    ref = _sdpa(q[0, 0].astype(np.float64)[None], K[None], K[None], 1 / math.sqrt(D))[0]
+    np.testing.assert_allclose(out[0], ref, atol=1e-12)
+    logits = q[0, 0].astype(np.float64) @ K.T / math.sqrt(D)
+    np.testing.assert_allclose(lse[0], np.log(np.exp(logits).sum(1)), atol=1e-12)
+
+
+def test_attention_sink_closed_form():
+    rng = np.random.default_rng(12)
+    H, D, N = 6, 32, 20
+    t = 4 * N
+    q = rng.standard_normal((1, 1, H, D)).astype(np.float32)
+    kv = rng.standard_normal((1, N, D)).astype(np.float32)
+    raw = rng.standard_normal((1, 8, D)).astype(np.float32)
+    common = dict(m=4, n_win=8, rope_dims=8)
+    args = (q, kv, raw, np.array([t - 7], np.int32), np.array([[t]], np.int32))
+    o0, l0 = oracle.attention(*args, np.full(H, -np.inf, np.float32), **common)
+    z = rng.standard_normal(H).astype(np.float32) * 2
+    oz, lz = oracle.attention(*args, z, **common)
+    frac = 1.0 / (1.0 + np.exp(z.astype(np.float64) - l0[0]))  # 1 - sigmoid(z - lse)
+    np.testing.assert_allclose(oz[0], o0[0] * frac[:, None], atol=1e-12)
+    np.testing.assert_allclose(lz[0], np.logaddexp(l0[0], z.astype(np.float64)), atol=1e-12)
+
+
+def test_attention_csa_with_all_entries_equals_dense():
+    rng = np.random.default_rng(13)
+    H, D, N, m = 4, 64, 33, 4
+    t = 4 * 30 + 1  # 30 visible entries; entries 30..32 must stay invisible
+    q = torch.randn(1, 1, H, D).to(torch.bfloat16)
+    kv = torch.randn(1, N, D).to(torch.bfloat16)
+    raw = torch.randn(1, 16, D).to(torch.bfloat16)
+    sinks = rng.standard_normal(H).astype(np.float32)
+    args = (q, kv, raw, np.array([t - 15], np.int32), np.array([[t]], np.int32), sinks)
+    kw = dict(m=m, n_win=16, rope_dims=16)
+    dense, ld = oracle.attention(*args, **kw)
+    idx = np.array([[[-1] * 5 + list(range(N)) + [-1] * 4]], np.int32)  # includes invisible 30..32
+    sparse, ls = oracle.attention(*args, idx=idx, **kw)
+    np.testing.assert_allclose(sparse, dense, atol=1e-13)
+    np.testing.assert_allclose(ls, ld, atol=1e-13)
+
+
+def test_attention_m1_is_causal_mqa():
+    """m = 1, window of one token, every earlier token selected, no sink, no rotation:
+    standard causal multi-query attention (torch SDPA, is_causal=True)."""
+    rng = np.random.default_rng(14)
+    H, D, T = 3, 16, 12
+    x = _pm1(rng, (1, T, D))
+    q = _pm1(rng, (1, T, H, D))
+    qpos = np.arange(T, dtype=np.int32)[None]
+    idx = np.tile(np.arange(T, dtype=np.int32), (1, T, 1))  # entries >= t are invisible at m=1
+    out, _ = oracle.attention(q, x, x, np.array([0], np.int32), qpos, np.full(H, -np.inf, np.float32),
+                              idx=idx, m=1, n_win=1, rope_dims=0, rms_eps=0.0)
+    K = x[0].astype(np.float64)
+    ref = _sdpa(q[0].transpose(1, 0, 2).astype(np.float64), np.broadcast_to(K, (H, T, D)).copy(),
+                np.broadcast_to(K, (H, T, D)).copy(), 1 / math.sqrt(D), causal=True)
+    np.testing.assert_allclose(out.transpose(1, 0, 2), ref, atol=1e-12)
+
+
+def test_attention_rotation_closed_forms():
+    """One rotated pair (D = r = 2): the logit depends on cos((t - pi) theta_0) only, and a
+    single key's output is the normalised key rotated by (pi - t)."""
+    D = 2
+    q = np.array([[[[1.0, 0.0]]]], np.float32)
+    kv = np.array([[[0.0, 0.0]] * 3 + [[3.0, 4.0]]], np.float32)  # entry 3 at position 3*m
+    raw = np.zeros((1, 1, D), np.float32)
+    m, t = 5, 27
+    idx = np.array([[[3]]], np.int32)
+    out, lse = oracle.attention(q, kv, raw, np.array([0], np.int32), np.array([[t]], np.int32),
+                                np.array([-np.inf], np.float32), idx=idx, m=m, n_win=0, rope_dims=2,
+                                rms_eps=0.0)
+    kn = np.array([3.0, 4.0]) / math.sqrt((9 + 16) / 2)
+    ang = (3 * m - t) * 1.0  # theta_0 = base^0 = 1
+    rot = np.array([kn[0] * math.cos(ang) - kn[1] * math.sin(ang), kn[0] * math.sin(ang) + kn[1] * math.cos(ang)])
+    np.testing.assert_allclose(out[0, 0], rot, atol=1e-12)
+    qn = np.array([math.sqrt(2), 0.0])
+    np.testing.assert_allclose(lse[0, 0], (qn @ rot) / math.sqrt(2), atol=1e-12)
+
+
+def test_attention_own_token_key_returns_normalised_key():
+    """A single window key at the query's own position: the output is RMSNorm(v) * gamma,
+    whatever the rotation (catches a wrong sign of the output rotation)."""
+    rng = np.random.default_rng(15)
+    D, t = 64, 1000
+    v = rng.standard_normal((1, 1, D)).astype(np.float32)
+    q = rng.standard_normal((1, 1, 2, D)).astype(np.float32)
+    g = rng.uniform(0.5, 2, D).astype(np.float32)
+    out, _ = oracle.attention(q, np.zeros((1, 1, D), np.float32), v, np.array([t], np.int32),
+                              np.array([[t]], np.int32), np.full(2, -np.inf, np.float32), m=4096, n_win=1,
+                              rope_dims=32, gamma_kv=g)
+    vv = v[0, 0].astype(np.float64)
+    want = vv / math.sqrt((vv ** 2).mean() + 1e-6) * g
+    np.testing.assert_allclose(out[0, 0], want, atol=1e-12)
+    np.testing.assert_allclose(out[0, 1], want, atol=1e-12)
+
+
+def test_attention_relative_position_invariance():
+    rng = np.random.default_rng(16)
+    H, D, N, m, win = 4, 64, 40, 4, 8
+    t = 4 * N + 3
+    q = rng.standard_normal((1, 1, H, D)).astype(np.float32)
+    kv = rng.standard_normal((1, N, D)).astype(np.float32)
+    raw = rng.standard_normal((1, win, D)).astype(np.float32)
+    sinks = rng.standard_normal(H).astype(np.float32)
+    kw = dict(m=m, n_win=win, rope_dims=32, rope_base=50.0)
+    a, la = oracle.attention(q, kv, raw, np.array([t - win + 1], np.int32), np.array([[t]], np.int32), sinks, **kw)
+    for delta in (12, 1001):
+        b, lb = oracle.attention(q, kv, raw, np.array([t - win + 1 + delta], np.int32),
+                                 np.array([[t + delta]], np.int32), sinks, entry_pos_offset=delta, **kw)
+        assert min((t + delta) // m, N) == min(t // m, N)  # the same entries stay visible
+        np.testing.assert_allclose(b, a, atol=1e-9)
+        np.testing.assert_allclose(lb, la, atol=1e-9)
+
+
+def test_attention_no_rotation_is_position_free_and_early_rows():
+    rng = np.random.default_rng(17)
+    H, D, N, m, win = 2, 32, 8, 4, 4
+    q = rng.standard_normal((1, 1, H, D)).astype(np.float32)
+    kv = rng.standard_normal((1, N, D)).astype(np.float32)
+    raw = rng.standard_normal((1, win, D)).astype(np.float32)
+    sinks = rng.standard_normal(H).astype(np.float32)
+    # r = 0: moving the window and the query together changes nothing
+    t = 3
+    a, _ = oracle.attention(q, kv, raw, np.array([0], np.int32), np.array([[t]], np.int32), sinks,
+                            m=m, n_win=win, rope_dims=0)
+    # t < m: no compressed entry is visible, so the cache contents do not matter
+    b, _ = oracle.attention(q, kv * 100, raw, np.array([0], np.int32), np.array([[t]], np.int32), sinks,
+                            m=m, n_win=win, rope_dims=0)
+    np.testing.assert_array_equal(a, b)
+    # with N = 0 entries the result is the window-only attention
+    c, _ = oracle.attention(q, kv[:, :0], raw, np.array([0], np.int32), np.array([[t]], np.int32), sinks,
+                            m=m, n_win=win, rope_dims=0)
+    np.testing.assert_array_equal(a, c)
+    # r = 0: moving the query and its window together changes nothing
+    d, _ = oracle.attention(q, kv[:, :0], raw, np.array([5000], np.int32), np.array([[5000 + t]], np.int32),
+                            sinks, m=m, n_win=win, rope_dims=0)
+    np.testing.assert_allclose(d, a, atol=1e-14)
+
+
+def test_attention_empty_key_set():
+    D = 8
+    out, lse = oracle.attention(np.ones((1, 1, 2, D), np.float32), np.zeros((1, 0, D), np.float32),
+                                np.zeros((1, 1, D), np.float32), np.array([100], np.int32),
+                                np.array([[5]], np.int32), np.array([-np.inf, 0.5], np.float32),
+                                m=4, n_win=2, rope_dims=0)
+    assert np.all(out == 0) and lse[0, 0] == -np.inf and lse[0, 1] == pytest.approx(0.5)
+
+
+def test_attention_softmax_scale_and_gamma_q():
+    """gamma_q = 2 everywhere doubles every logit, the same as softmax_scale = 2/sqrt(D)."""
+    rng = np.random.default_rng(18)
+    H, D, N = 2, 16, 12
+    t = 4 * N
+    args = (rng.standard_normal((1, 1, H, D)).astype(np.float32), rng.standard_normal((1, N, D)).astype(np.float32),
+            rng.standard_normal((1, 4, D)).astype(np.float32), np.array([t - 3], np.int32),
+            np.array([[t]], np.int32), rng.standard_normal(H).astype(np.float32))
+    a, la = oracle.attention(*args, m=4, n_win=4, rope_dims=8, gamma_q=np.full(D, 2.0, np.float32))
+    b, lb = oracle.attention(*args, m=4, n_win=4, rope_dims=8, softmax_scale=2.0 / math.sqrt(D))
+    np.testing.assert_allclose(a, b, atol=1e-12)
+    np.testing.assert_allclose(la, lb, atol=1e-12)
