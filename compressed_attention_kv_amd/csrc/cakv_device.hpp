@@ -1,0 +1,111 @@
+// cakv_device.hpp -- device helpers for the gfx950 (CDNA4) kernels of the
+// compressed-attention library: storage conversions, the fp8 E4M3 encoder,
+// rotary sin/cos from exact fractional turns, MFMA operand types and wave
+// reductions.  Written for wave64 and the gfx950 MFMA / conversion units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cakv {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- storage types
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
+
+// float -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// two floats -> packed pair of f16 (round to nearest even, v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    _Float16 x = (_Float16)a, y = (_Float16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// ---------------------------------------------------------------- fp8 E4M3 (OCP)
+// Round-to-nearest-even encode of a finite v with |v| <= 448 (values beyond
+// saturate to the largest finite code).  Normal range: keep 3 mantissa bits of
+// the fp32 pattern with an RNE bias and move the exponent from bias 127 to 7;
+// subnormal range (|v| < 2^-6, step 2^-9): round |v| * 512 to an integer.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+    uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+    float a = __builtin_fabsf(v);
+    uint32_t code;
+    if (a < 0.015625f) {
+        code = (uint32_t)__builtin_rintf(a * 512.0f);
+    } else {
+        uint32_t b = __float_as_uint(a);
+        b += 0x7ffffu + ((b >> 20) & 1u);
+        code = (b >> 20) - (120u << 3);
+        code = code > 0x7eu ? 0x7eu : code;
+    }
+    return code | sign;
+}
+
+// ---------------------------------------------------------------- rotary sin / cos
+// sin and cos of 2*pi*x for a fraction of a turn x (any real, fp64).  The
+// integer part is dropped exactly in fp64, the rest is folded to an octant
+// |y| <= 1/8 turn and evaluated with Taylor polynomials (error < 2e-9 on
+// |angle| <= pi/4, below fp32 rounding).
+__device__ __forceinline__ void sincos_turns(double x, float* s_out, float* c_out) {
+    double f = x - __builtin_floor(x);            // [0, 1)
+    double qd = __builtin_rint(f * 4.0);          // quadrant 0..4
+    float y = (float)(f - qd * 0.25);             // [-1/8, 1/8] turn, exact subtraction
+    int q = ((int)qd) & 3;
+    float a = y * 6.28318530717958647692f;
+    float a2 = a * a;
+    float s = a * (1.0f + a2 * (-1.0f / 6.0f + a2 * (1.0f / 120.0f + a2 * (-1.0f / 5040.0f + a2 * (1.0f / 362880.0f)))));
+    float c = 1.0f + a2 * (-0.5f + a2 * (1.0f / 24.0f + a2 * (-1.0f / 720.0f + a2 * (1.0f / 40320.0f + a2 * (-1.0f / 3628800.0f)))));
+    // quadrant q: (sin, cos) of q*pi/2 + a
+    const float so = ((q & 1) ? c : s) * ((q & 2) ? -1.0f : 1.0f);
+    const float co = ((q & 1) ? s : c) * (((q + 1) & 2) ? -1.0f : 1.0f);
+    *s_out = so;
+    *c_out = co;
+}
+
+// ---------------------------------------------------------------- wave helpers
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+    // sum over aligned groups of W consecutive lanes (W a power of two <= 64)
+#pragma unroll
+    for (int o = 1; o < W; o <<= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// order-preserving image of an fp32 score: a > b  <=>  key(a) > key(b);
+// -0 and +0 share one key.
+__device__ __forceinline__ uint32_t score_key(float s) {
+    uint32_t b = (s == 0.0f) ? 0u : __float_as_uint(s);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+}  // namespace cakv

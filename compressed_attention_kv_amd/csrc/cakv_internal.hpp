@@ -1,0 +1,82 @@
+// cakv_internal.hpp -- host-side launcher interfaces between the C ABI layer
+// (api.cpp) and the kernel translation units.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace cakv {
+
+constexpr int kMaxRopePairs = 32;  // rope_dims <= 64
+constexpr int kTopkCap = 4096;     // largest k
+constexpr int kBoundaryCap = 4096; // boundary-bin candidates kept on the fast path
+constexpr int kHistBins = 2048;    // top 11 bits of the score key
+
+// Everything one attention launch needs; passed by value as the kernel
+// argument block.
+struct AttnArgs {
+    const void* q;
+    const void* kv_c;
+    const int32_t* idx;  // NULL for the dense path
+    const void* kv_raw;
+    const int32_t* raw_pos0;
+    const int32_t* q_pos;
+    const float* sinks;
+    const float* gamma_q;
+    const float* gamma_kv;
+    void* out;
+    float* lse;
+    float* part_o;   // [BQ][S][H][D]   split partial outputs (S > 1)
+    float* part_ml;  // [BQ][S][H][2]   split partial (max, sum), max in log2 units
+    int64_t Q;
+    int64_t N;
+    int64_t R;
+    int32_t H;
+    int32_t K;
+    int32_t m;
+    int32_t n_win;
+    int32_t rope_dims;
+    int32_t entry_pos_offset;
+    float scale_log2;  // softmax scale * log2(e)
+    float rms_eps;
+    int32_t n_splits;
+    int32_t out_f32;   // 1: float32 output, 0: bf16
+    double rope_turns[kMaxRopePairs];  // theta_i / (2 pi): turns per unit position
+};
+
+int launch_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B, int64_t T,
+                       int64_t D, int32_t m, void* out, int out_dtype, float* out_scale,
+                       hipStream_t stream);
+
+// sparse (idx != NULL) or dense MQA forward; act_f32: inputs are float32
+int launch_mqa_fwd(const AttnArgs& a, int64_t BQ, int D, bool act_f32, hipStream_t stream);
+
+struct IndexerArgs {
+    const void* q_idx;
+    const float* w;
+    const void* k_idx;
+    const float* k_scale;
+    const int32_t* q_pos;
+    int32_t* idx;
+    uint32_t* keys;      // [BQ][N]
+    uint32_t* hist;      // [BQ][kHistBins]
+    uint32_t* counters;  // [BQ][4]: above, boundary, ticket, spare
+    int32_t* sel;        // [BQ][k]
+    uint64_t* bnd;       // [BQ][kBoundaryCap]
+    int64_t Q;
+    int64_t N;
+    int32_t HI;
+    int32_t dI;
+    int32_t m;
+    int32_t k;
+    int32_t chunk;       // entries per score workgroup
+    int32_t n_chunks;
+    int32_t sel_chunk;   // entries per select workgroup
+    int32_t n_sel_chunks;
+};
+
+size_t indexer_workspace_bytes(int64_t BQ, int64_t N, int32_t k);
+int launch_indexer_topk(IndexerArgs& a, int64_t BQ, bool fp8_mode, void* ws, hipStream_t stream);
+
+}  // namespace cakv

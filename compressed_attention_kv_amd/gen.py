@@ -32,8 +32,11 @@ _FIELDS = ("q", "kv", "gate", "k_idx", "k_gate", "q_idx", "w", "sinks", "kv_raw"
            "hca_gate", "q_hca", "sinks_hca")
 
 
-def make_inputs(w: Workload | str, **overrides) -> dict:
+def make_inputs(w: Workload | str, only=None, **overrides) -> dict:
     """Return a dict of CPU tensors for workload ``w`` (a name or a Workload).
+
+    ``only``: optional set of field names to draw (others are skipped; every
+    field has its own random stream, so skipping never changes the rest).
 
     Keys (present when the workload uses them):
       q       [B,Q,H,D]   query heads (before norm / rotation)
@@ -56,35 +59,41 @@ def make_inputs(w: Workload | str, **overrides) -> dict:
         w = w.replace(**overrides)
     rngs = dict(zip(_FIELDS, _rng_children(w.seed, len(_FIELDS))))
     act = torch.float32 if w.dtype == "f32" else torch.bfloat16
+
+    def draw(field, shape, dtype):
+        if only is not None and field not in only:
+            return None
+        return _normal(rngs[field], shape, dtype)
+
     B, Q, H, D = w.B, w.Q, w.H, w.D
     out: dict = {"workload": w}
-    out["q"] = _normal(rngs["q"], (B, Q, H, D), act)
+    out["q"] = draw("q", (B, Q, H, D), act)
     if w.prefill:
         T = w.T
-        out["kv"] = _normal(rngs["kv"], (B, T, D), act)
-        out["gate"] = _normal(rngs["gate"], (B, T), torch.float32)
+        out["kv"] = draw("kv", (B, T, D), act)
+        out["gate"] = draw("gate", (B, T), torch.float32)
         if w.csa:
-            out["k_idx"] = _normal(rngs["k_idx"], (B, T, w.dI), act)
-            out["k_gate"] = _normal(rngs["k_gate"], (B, T), torch.float32)
+            out["k_idx"] = draw("k_idx", (B, T, w.dI), act)
+            out["k_gate"] = draw("k_gate", (B, T), torch.float32)
         if w.hca:
-            out["hca_gate"] = _normal(rngs["hca_gate"], (B, T), torch.float32)
-            out["q_hca"] = _normal(rngs["q_hca"], (B, Q, H, D), act)
-            out["sinks_hca"] = _normal(rngs["sinks_hca"], (H,), torch.float32)
+            out["hca_gate"] = draw("hca_gate", (B, T), torch.float32)
+            out["q_hca"] = draw("q_hca", (B, Q, H, D), act)
+            out["sinks_hca"] = draw("sinks_hca", (H,), torch.float32)
         # the raw window source is the raw KV itself: row p holds position p
         out["kv_raw"] = out["kv"]
         out["raw_pos0"] = torch.zeros(B, dtype=torch.int32)
         out["q_pos"] = (w.q_pos0 + torch.arange(Q, dtype=torch.int32)).repeat(B, 1)
     else:
         N = w.N
-        out["kv"] = _normal(rngs["kv"], (B, N, D), act)
+        out["kv"] = draw("kv", (B, N, D), act)
         if w.csa:
-            out["k_idx"] = _normal(rngs["k_idx"], (B, N, w.dI), torch.float32)
+            out["k_idx"] = draw("k_idx", (B, N, w.dI), torch.float32)
         R = w.n_win
-        out["kv_raw"] = _normal(rngs["kv_raw"], (B, R, D), act)
+        out["kv_raw"] = draw("kv_raw", (B, R, D), act)
         out["q_pos"] = torch.full((B, Q), w.t, dtype=torch.int32)
         out["raw_pos0"] = torch.full((B,), w.t - R + 1, dtype=torch.int32)
     if w.csa:
-        out["q_idx"] = _normal(rngs["q_idx"], (B, Q, w.HI, w.dI), act)
-        out["w"] = _normal(rngs["w"], (B, Q, w.HI), torch.float32)
-    out["sinks"] = _normal(rngs["sinks"], (H,), torch.float32)
+        out["q_idx"] = draw("q_idx", (B, Q, w.HI, w.dI), act)
+        out["w"] = draw("w", (B, Q, w.HI), torch.float32)
+    out["sinks"] = draw("sinks", (H,), torch.float32)
     return out

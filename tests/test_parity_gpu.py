@@ -1,0 +1,297 @@
+"""Parity of the HIP path against the CPU oracle, element by element, on the
+same seeded inputs.  Bars (the method's stated tolerances):
+  * kv_compress: bf16 within one bf16 ulp of the fp64 result (+1e-6 rel),
+    f32 within 1e-5 relative to the row scale, fp8 within one E4M3 step of the
+    oracle's dequantised value (same scale except at an exponent boundary);
+  * indexer_topk: indices bit-exact in fp32 mode; fp8 mode recall >= 99.5 %
+    with every miss within 1e-3 relative of the k-th best score;
+  * attention (fed the oracle's indices): max-abs <= 2e-2 and
+    rel-RMS = ||o - o_ref|| / ||o_ref|| <= 5e-3.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_attention_kv_amd as cakv
+import oracle
+from compressed_attention_kv_amd.gen import make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _d(t):
+    return t.to(DEV) if isinstance(t, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(t)).to(DEV)
+
+
+def _bf16_ulp(x):
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+# ------------------------------------------------------------------ kv_compress
+
+@pytest.mark.parametrize("dtype,D,m,T", [("f32", 128, 4, 2048), ("f32", 32, 4, 2048), ("bf16", 512, 4, 8192 + 7),
+                                         ("bf16", 512, 128, 8192 + 100), ("bf16", 512, 1, 64)])
+def test_kv_compress(dtype, D, m, T):
+    say(f"kv_compress {dtype} D={D} m={m} T={T}")
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    g = torch.Generator().manual_seed(D * 7 + m)
+    x = torch.randn(2, T, D, generator=g).to(tdt)
+    gate = torch.randn(2, T, generator=g) * 2
+    ref = oracle.kv_compress(x, gate, m)
+    out = cakv.kv_compress(_d(x), _d(gate), m, tdt).float().cpu().numpy()
+    assert out.shape == ref.shape
+    if dtype == "f32":
+        scale = np.abs(ref).max(axis=-1, keepdims=True) + 1e-30
+        assert np.all(np.abs(out - ref) <= 1e-5 * scale)
+    else:
+        assert np.all(np.abs(out - ref) <= _bf16_ulp(ref) + 1e-6 * np.abs(ref))
+
+
+@pytest.mark.parametrize("T,m", [(8192 + 3, 4), (512, 1)])
+def test_kv_compress_fp8(T, m):
+    say(f"kv_compress fp8 T={T} m={m}")
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn(2, T, 128, generator=g).to(torch.bfloat16)
+    x[0, :m] *= 1e-3  # a small-magnitude entry
+    x[1, 4 * m: 5 * m] = 0  # an all-zero entry
+    gate = torch.randn(2, T, generator=g)
+    c = oracle.kv_compress(x, gate, m)
+    codes_ref, scale_ref = oracle.q8_quantize(c)
+    out, scale = cakv.kv_compress(_d(x), _d(gate), m, torch.float8_e4m3fn)
+    codes = out.view(torch.uint8).cpu().numpy()
+    scale = scale.cpu().numpy()
+    deq = oracle.q8_dequantize(codes, scale).astype(np.float64)
+    deq_ref = oracle.q8_dequantize(codes_ref, scale_ref).astype(np.float64)
+    same = scale == scale_ref
+    assert same.mean() > 0.999  # only entries whose max sits on a power-of-two boundary may differ
+    assert np.all(np.isin(scale[~same] / scale_ref[~same], [0.5, 2.0]))
+    step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(deq_ref) / scale_ref[..., None], 2.0 ** -6))) - 3)
+    step = np.maximum(step, 2.0 ** -9) * np.maximum(scale, scale_ref)[..., None]
+    assert np.all(np.abs(deq - deq_ref) <= step * 1.0001)
+    assert (codes == codes_ref).mean() > 0.999
+    assert np.all(scale[1, 4] == 1.0) and np.all(codes[1, 4] == 0)
+
+
+# ------------------------------------------------------------------ indexer
+
+def _indexer_inputs(name, only=None, **over):
+    inp = make_inputs(name, only=only, **over)
+    w = inp["workload"]
+    if w.prefill:
+        keys = oracle.kv_compress(inp["k_idx"], inp["k_gate"], w.m)
+    else:
+        keys = inp["k_idx"].numpy()
+    return inp, w, keys
+
+
+def test_indexer_fp32_bit_exact_tiny_layer():
+    say("indexer fp32 tiny layer (2048 queries, 512 entries, k=64)")
+    inp, w, keys = _indexer_inputs("tiny_csa_f32")
+    keys = keys.astype(np.float32)
+    ref = oracle.indexer_topk(inp["q_idx"], inp["w"], inp["q_pos"], w.m, w.k, k_f32=keys)
+    got = cakv.indexer_topk(_d(inp["q_idx"]), _d(inp["w"]), _d(keys), None, _d(inp["q_pos"]), w.m, w.k)
+    got = got.cpu().numpy().reshape(ref.shape)
+    assert np.array_equal(got, ref)
+    assert (ref == -1).any(axis=1).sum() >= 256  # rows with fewer visible entries than k
+
+
+@pytest.mark.parametrize("N,k,Q", [(3000, 64, 8), (70000, 1024, 2)])
+def test_indexer_fp32_bit_exact_sizes(N, k, Q):
+    say(f"indexer fp32 N={N} k={k}")
+    rng = np.random.default_rng(N)
+    B, HI, dI, m = 2, 8, 32, 4
+    q = rng.standard_normal((B, Q, HI, dI)).astype(np.float32)
+    wgt = rng.standard_normal((B, Q, HI)).astype(np.float32)
+    keys = rng.standard_normal((B, N, dI)).astype(np.float32)
+    keys[0, 100:200] = keys[0, 50]  # exact ties
+    qpos = rng.integers(0, 4 * N + 50, size=(B, Q)).astype(np.int32)
+    qpos[0, 0] = 4 * N
+    ref = oracle.indexer_topk(q, wgt, qpos, m, k, k_f32=keys)
+    got = cakv.indexer_topk(_d(q), _d(wgt), _d(keys), None, _d(qpos), m, k).cpu().numpy().reshape(ref.shape)
+    assert np.array_equal(got, ref)
+
+
+def _recall_check(got, ref, scores, nvis, k):
+    recalls, worst_gap = [], 0.0
+    for r in range(ref.shape[0]):
+        rs = set(ref[r][ref[r] >= 0].tolist())
+        gs = got[r][got[r] >= 0]
+        assert len(set(gs.tolist())) == len(gs) == len(rs)
+        assert np.all(np.diff(gs) > 0) and np.all(gs < nvis[r])
+        recalls.append(len(rs & set(gs.tolist())) / max(len(rs), 1))
+        s = scores[r, :nvis[r]].astype(np.float64)
+        kth = np.sort(s)[::-1][min(k, nvis[r]) - 1]
+        for j in rs - set(gs.tolist()):
+            gap = abs(s[j] - kth) / abs(kth)
+            worst_gap = max(worst_gap, gap)
+        for j in set(gs.tolist()) - rs:
+            worst_gap = max(worst_gap, abs(s[j] - kth) / abs(kth))
+    return float(np.mean(recalls)), worst_gap
+
+
+@pytest.mark.parametrize("name,over", [("csa_decode_128k", dict(B=4)), ("csa_decode_128k", {}),
+                                       ("csa_decode_1m", {})])
+def test_indexer_fp8_recall(name, over):
+    say(f"indexer fp8 {name} {over}")
+    inp, w, keys = _indexer_inputs(name, only={"k_idx", "q_idx", "w"}, **over)
+    codes, scale = oracle.q8_quantize(keys)
+    scores, nvis = oracle.indexer_scores(inp["q_idx"], inp["w"], inp["q_pos"], w.m, k_code=codes, k_scale=scale)
+    ref = oracle.topk(scores, nvis, w.k)
+    got = cakv.indexer_topk(_d(inp["q_idx"]), _d(inp["w"]), _d(codes), _d(scale), _d(inp["q_pos"]), w.m, w.k)
+    got = got.cpu().numpy().reshape(ref.shape)
+    recall, gap = _recall_check(got, ref, scores, nvis, w.k)
+    say(f"  recall {recall:.5f} worst relative gap of a swapped entry {gap:.2e}")
+    assert recall >= 0.995 and gap <= 1e-3
+
+
+# ------------------------------------------------------------------ attention
+
+def _attn_check(out, ref, what):
+    out = out.astype(np.float64)
+    err = np.abs(out - ref)
+    rel_rms = np.linalg.norm(out - ref) / np.linalg.norm(ref)
+    worst = np.unravel_index(np.argmax(err), err.shape)
+    say(f"  {what}: max-abs {err.max():.3e} rel-RMS {rel_rms:.3e} worst at {worst}")
+    assert np.all(np.isfinite(out))
+    assert err.max() <= 2e-2 and rel_rms <= 5e-3
+
+
+def _attn_kw(w):
+    return dict(m=w.m, n_win=w.n_win, rope_dims=w.rope_dims, rope_base=w.rope_base)
+
+
+def test_sparse_attention_tiny_layer_f32():
+    say("sparse attention tiny layer f32")
+    inp, w, keys = _indexer_inputs("tiny_csa_f32")
+    kvc = oracle.kv_compress(inp["kv"], inp["gate"], w.m).astype(np.float32)
+    idx = oracle.indexer_topk(inp["q_idx"], inp["w"], inp["q_pos"], w.m, w.k,
+                              k_f32=keys.astype(np.float32)).reshape(1, w.Q, w.k)
+    kw = _attn_kw(w)
+    ref, lse_ref = oracle.attention(inp["q"], kvc, inp["kv_raw"], inp["raw_pos0"], inp["q_pos"], inp["sinks"],
+                                    idx=idx, **kw)
+    for odt in (torch.float32, torch.bfloat16):
+        out, lse = cakv.sparse_mqa_fwd(_d(inp["q"]), _d(kvc), _d(idx), _d(inp["kv_raw"]), _d(inp["raw_pos0"]),
+                                       _d(inp["q_pos"]), _d(inp["sinks"]), out_dtype=odt, **kw)
+        _attn_check(out.float().cpu().numpy().reshape(ref.shape), ref, f"out {odt}")
+    assert np.abs(lse.cpu().numpy().reshape(lse_ref.shape) - lse_ref).max() < 1e-3
+
+
+def test_dense_attention_tiny_hca_f32():
+    say("dense attention tiny HCA (m=128) f32")
+    inp = make_inputs("tiny_csa_f32")
+    w = inp["workload"].replace(m=128)
+    kvc = oracle.kv_compress(inp["kv"], inp["gate"], 128).astype(np.float32)
+    kw = _attn_kw(w)
+    ref, lse_ref = oracle.attention(inp["q"], kvc, inp["kv_raw"], inp["raw_pos0"], inp["q_pos"], inp["sinks"], **kw)
+    out, lse = cakv.dense_compressed_mqa_fwd(_d(inp["q"]), _d(kvc), _d(inp["kv_raw"]), _d(inp["raw_pos0"]),
+                                             _d(inp["q_pos"]), _d(inp["sinks"]), out_dtype=torch.float32, **kw)
+    _attn_check(out.cpu().numpy().reshape(ref.shape), ref, "out")
+    assert np.abs(lse.cpu().numpy().reshape(lse_ref.shape) - lse_ref).max() < 1e-3
+
+
+def test_sparse_attention_csa_decode_128k():
+    say("sparse attention CSA decode 128K (32 queries, oracle indices)")
+    inp, w, keys = _indexer_inputs("csa_decode_128k")
+    codes, scale = oracle.q8_quantize(keys)
+    idx = oracle.indexer_topk(inp["q_idx"], inp["w"], inp["q_pos"], w.m, w.k, k_code=codes, k_scale=scale)
+    idx = idx.reshape(w.B, w.Q, w.k)
+    kw = _attn_kw(w)
+    ref, lse_ref = oracle.attention(inp["q"], inp["kv"], inp["kv_raw"], inp["raw_pos0"], inp["q_pos"], inp["sinks"],
+                                    idx=idx, **kw)
+    out, lse = cakv.sparse_mqa_fwd(_d(inp["q"]), _d(inp["kv"]), _d(idx), _d(inp["kv_raw"]), _d(inp["raw_pos0"]),
+                                   _d(inp["q_pos"]), _d(inp["sinks"]), **kw)
+    _attn_check(out.float().cpu().numpy().reshape(ref.shape), ref, "out bf16")
+    assert np.abs(lse.cpu().numpy().reshape(lse_ref.shape) - lse_ref).max() < 1e-2
+
+
+def test_dense_attention_hca_decode_1m():
+    say("dense attention HCA decode 1M (32 queries x 8192 entries)")
+    inp = make_inputs("hca_decode_1m")
+    w = inp["workload"]
+    kw = _attn_kw(w)
+    ref, lse_ref = oracle.attention(inp["q"], inp["kv"], inp["kv_raw"], inp["raw_pos0"], inp["q_pos"], inp["sinks"],
+                                    **kw)
+    out, lse = cakv.dense_compressed_mqa_fwd(_d(inp["q"]), _d(inp["kv"]), _d(inp["kv_raw"]), _d(inp["raw_pos0"]),
+                                             _d(inp["q_pos"]), _d(inp["sinks"]), **kw)
+    _attn_check(out.float().cpu().numpy().reshape(ref.shape), ref, "out bf16")
+    assert np.abs(lse.cpu().numpy().reshape(lse_ref.shape) - lse_ref).max() < 1e-2
+
+
+def test_attention_edge_cases():
+    """Early rows (t < m: window and sink only), an empty key set with a -inf
+    sink, K = 0 slots, duplicate-free padding, positions outside the raw rows."""
+    say("attention edge cases")
+    g = torch.Generator().manual_seed(5)
+    B, Q, H, D, N, R, K = 2, 6, 128, 512, 40, 8, 16
+    q = torch.randn(B, Q, H, D, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, N, D, generator=g).to(torch.bfloat16)
+    raw = torch.randn(B, R, D, generator=g).to(torch.bfloat16)
+    sinks = torch.randn(H, generator=g)
+    sinks[3] = -math.inf
+    qpos = torch.tensor([[0, 1, 3, 5, 100, 1000], [2, 7, 60, 61, 159, 163]], dtype=torch.int32)
+    raw0 = torch.tensor([0, 156], dtype=torch.int32)  # sequence 1: raw rows cover positions 156..163 only
+    idx = torch.randint(0, N, (B, Q, K), generator=g, dtype=torch.int32)
+    for b in range(B):
+        for i in range(Q):
+            idx[b, i] = torch.randperm(N, generator=g)[:K].to(torch.int32)
+    idx[:, :, ::3] = -1
+    kw = dict(m=4, n_win=4, rope_dims=64)
+    ref, lse_ref = oracle.attention(q, kv, raw, raw0, qpos, sinks, idx=idx.numpy(), **kw)
+    out, lse = cakv.sparse_mqa_fwd(_d(q), _d(kv), _d(idx), _d(raw), _d(raw0), _d(qpos), _d(sinks),
+                                   out_dtype=torch.float32, **kw)
+    _attn_check(out.cpu().numpy().reshape(ref.shape), ref, "sparse edge")
+    ref2, _ = oracle.attention(q, kv, raw, raw0, qpos, sinks, **kw)
+    out2, _ = cakv.dense_compressed_mqa_fwd(_d(q), _d(kv), _d(raw), _d(raw0), _d(qpos), _d(sinks),
+                                            out_dtype=torch.float32, **kw)
+    _attn_check(out2.cpu().numpy().reshape(ref2.shape), ref2, "dense edge")
+    # no window, no entries, -inf sinks: zero output, lse -inf
+    sk = torch.full((H,), -math.inf)
+    out3, lse3 = cakv.dense_compressed_mqa_fwd(_d(q), _d(kv[:, :0]), _d(raw), _d(raw0), _d(qpos), _d(sk),
+                                               out_dtype=torch.float32, m=4, n_win=0, rope_dims=64)
+    assert torch.all(out3 == 0) and torch.all(torch.isneginf(lse3))
+
+
+def test_attention_needle_forces_exact_max_pass():
+    """A key equal to the query (logit sqrt(D), far above the rest) sitting in a
+    late tile: the kernel's reference max from the first tiles is too small,
+    so it must take its exact-max second pass."""
+    say("attention needle (second pass)")
+    g = torch.Generator().manual_seed(7)
+    B, Q, H, D, N = 2, 1, 128, 512, 2048
+    q = torch.randn(B, Q, H, D, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, N, D, generator=g).to(torch.bfloat16)
+    kv[0, 1900] = q[0, 0, 5]
+    kv[1, 1500] = q[1, 0, 77]
+    raw = torch.randn(B, 128, D, generator=g).to(torch.bfloat16)
+    t = 4 * N
+    qpos = torch.full((B, Q), t, dtype=torch.int32)
+    raw0 = torch.full((B,), t - 127, dtype=torch.int32)
+    sinks = torch.randn(H, generator=g)
+    kw = dict(m=4, n_win=128, rope_dims=0)
+    ref, _ = oracle.attention(q, kv, raw, raw0, qpos, sinks, **kw)
+    out, _ = cakv.dense_compressed_mqa_fwd(_d(q), _d(kv), _d(raw), _d(raw0), _d(qpos), _d(sinks),
+                                           out_dtype=torch.float32, **kw)
+    _attn_check(out.cpu().numpy().reshape(ref.shape), ref, "needle")
+    assert np.abs(ref[0, 5]).max() > 0.5  # the needle dominates that head
+
+
+def test_determinism():
+    say("determinism")
+    inp = make_inputs("csa_decode_128k", B=4)
+    w = inp["workload"]
+    idx = torch.randint(0, w.N, (w.B, w.Q, w.k), dtype=torch.int32)
+    args = (_d(inp["q"]), _d(inp["kv"]), _d(idx), _d(inp["kv_raw"]), _d(inp["raw_pos0"]), _d(inp["q_pos"]),
+            _d(inp["sinks"]))
+    a, la = cakv.sparse_mqa_fwd(*args, **_attn_kw(w))
+    b, lb = cakv.sparse_mqa_fwd(*args, **_attn_kw(w))
+    assert torch.equal(a, b) and torch.equal(la, lb)
