@@ -144,10 +144,11 @@ __device__ __forceinline__ int vt_offset(int dim, int granule) {
 }
 
 __device__ __forceinline__ void lds_barrier() {
-    // wait only for this wave's LDS traffic, then the workgroup barrier;
-    // outstanding HBM loads stay in flight across it
-    __builtin_amdgcn_s_waitcnt(0xc07f);
+    // workgroup-scope release/acquire around the barrier: on gfx950 this waits
+    // for LDS traffic only, so outstanding HBM loads stay in flight across it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
 // Per-tile row metadata, written one iteration ahead by wave 0.
