@@ -82,6 +82,7 @@ int check_attn_common(const cakv_attn_params* p, const void* q, const void* kv_c
     REQUIRE(H >= 1 && H <= 128, CAKV_EUNSUPPORTED, "H=%d: 1 <= H <= 128 supported", H);
     REQUIRE(D == 128 || D == 512, CAKV_EUNSUPPORTED, "D=%d: head dims 128 and 512 supported", D);
     REQUIRE(act_dtype == CAKV_BF16 || act_dtype == CAKV_F32, CAKV_EINVAL, "act_dtype must be BF16 or F32");
+    REQUIRE(act_dtype == CAKV_BF16 || D <= 128, CAKV_EUNSUPPORTED, "F32 activations support D <= 128 (D=%d)", D);
     REQUIRE(out_dtype == CAKV_BF16 || out_dtype == CAKV_F32, CAKV_EINVAL, "out_dtype must be BF16 or F32");
     REQUIRE(p->m >= 1 && p->m <= 4096, CAKV_EUNSUPPORTED, "m=%d out of 1..4096", p->m);
     REQUIRE(p->n_win >= 0 && p->n_win <= 4096, CAKV_EUNSUPPORTED, "n_win=%d out of 0..4096", p->n_win);
@@ -136,10 +137,7 @@ void fill_attn(cakv::AttnArgs& a, const cakv_attn_params* p, const void* q, cons
     a.scale_log2 = (float)(tau * 1.4426950408889634);
     a.rms_eps = p->rms_eps;
     a.out_f32 = out_dtype == CAKV_F32;
-    const double two_pi = 6.283185307179586476925286766559;
-    for (int i = 0; i < cakv::kMaxRopePairs; ++i)
-        a.rope_turns[i] = (2 * i < p->rope_dims) ? pow((double)p->rope_base, -2.0 * i / (double)p->rope_dims) / two_pi
-                                                 : 0.0;
+    a.rope_base = p->rope_base;
 }
 
 int run_attn(cakv::AttnArgs& a, int64_t BQ, int32_t H, int32_t D, int64_t max_slots, bool act_f32,
@@ -242,14 +240,7 @@ int cakv_indexer_topk(const void* q_idx, int q_dtype, const float* w, const void
     if (per_q < 1) per_q = 1;
     a.chunk = (int32_t)(ceil_div(units, per_q) * 128);
     a.n_chunks = (int32_t)ceil_div(N > 0 ? N : 1, a.chunk);
-    const int64_t sunits = N > 0 ? ceil_div(N, 256) : 1;
-    int64_t sper_q = ceil_div(1024, BQ);
-    if (sper_q > sunits) sper_q = sunits;
-    if (sper_q < 1) sper_q = 1;
-    a.sel_chunk = (int32_t)(ceil_div(sunits, sper_q) * 256);
-    a.n_sel_chunks = (int32_t)ceil_div(N > 0 ? N : 1, a.sel_chunk);
-    REQUIRE(a.n_chunks <= 65535 && a.n_sel_chunks <= 65535 && BQ <= 65535, CAKV_EUNSUPPORTED,
-            "grid too large (B*Q=%lld)", (long long)BQ);
+    REQUIRE(a.n_chunks <= 65535 && BQ <= 65535, CAKV_EUNSUPPORTED, "grid too large (B*Q=%lld)", (long long)BQ);
     return rc_from(cakv::launch_indexer_topk(a, BQ, fp8, workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 

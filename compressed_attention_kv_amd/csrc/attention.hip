@@ -29,6 +29,8 @@
 //     range is safe and its 11-bit significand is 8x finer than bf16's.
 //   * Splits over key tiles write (max, sum, O) partials; a combine kernel
 //     merges them with the sink.  With one split the epilogue is fused.
+#include <type_traits>
+
 #include "cakv_device.hpp"
 #include "cakv_internal.hpp"
 
@@ -143,42 +145,94 @@ __device__ __forceinline__ int vt_offset(int dim, int granule) {
     return P * 64 + phys * 16;
 }
 
-__device__ __forceinline__ void lds_barrier() {
-    // workgroup-scope release/acquire around the barrier: on gfx950 this waits
-    // for LDS traffic only, so outstanding HBM loads stay in flight across it
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
-// Per-tile row metadata, written one iteration ahead by wave 0.
+// Per-tile row metadata, written two tiles ahead by wave 0.
 struct TileMeta {
     uint64_t rowp[TK];  // source row address, 0 for an empty / invalid slot
     int32_t pos[TK];    // rotary position of the row
     uint32_t mask;      // bit rho set when row rho is a valid key
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Asynchronous 16-byte-per-lane HBM -> LDS load (global_load_lds_dwordx4):
+// lane i writes LDS bytes [lds_base + 16 i, +16).  Written as one asm block
+// that saves and restores M0 around the load (M0 carries the LDS base; one
+// wait state after writing it), so the compiler neither sees an LDS store
+// it would have to wait for nor loses its own M0.  There is no register
+// output; completion is awaited explicitly (vmcnt) before the data is read.
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gptr), "s"(lds_base)
+        : "memory");
+}
+
+// The thread index laundered through an empty asm statement: address
+// arithmetic derived from it cannot be hoisted out of the tile loop, which
+// would pin dozens of loop-invariant addresses in VGPRs for the whole loop.
+__device__ __forceinline__ int opaque_tid() {
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
+// Barrier that waits for this wave's LDS traffic only: asynchronous
+// HBM->LDS loads of the next tile stay in flight across it.  Signal fences
+// keep the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Barrier after which this workgroup's asynchronous tile loads have landed.
+__device__ __forceinline__ void barrier_all() {
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int D, bool SPARSE, typename TIn>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mqa_fwd_kernel(const AttnArgs a) {
-    constexpr int G = D / 8;                 // 16-byte granules per row
+    constexpr int G = D / 8;                 // 16-byte f16 granules per K^ row
     constexpr int SWZ = (G < 16 ? G : 16) - 1;
     constexpr int KSTEPS = D / 16;           // QK k-steps
     constexpr int DT = D / 32;               // output dim tiles
     constexpr int KH_BYTES = TK * D * 2;
     constexpr int VT_BYTES = D * TK * 2;
-    constexpr int BUF = KH_BYTES + VT_BYTES;
-    constexpr int CS_BYTES = TK * kMaxRopePairs * 8;
-    static_assert(128 * D * 2 <= 2 * BUF, "query staging must fit the tile buffers");
+    constexpr bool RAW_F32 = sizeof(TIn) == 4;
+    constexpr int RAW_BYTES = TK * D * (int)sizeof(TIn);  // landed (raw) tile rows
+    constexpr int CS_FLOATS = TK * kMaxRopePairs * 2;
+    constexpr int UNITS = TK * D * (int)sizeof(TIn) / 1024;  // 1 KiB load units per tile
+    constexpr int RPU = 1024 / (D * (int)sizeof(TIn));       // rows per unit
+    constexpr int LPR = 64 / RPU;                            // lanes per row in a unit
+    static_assert(UNITS % 4 == 0 && RPU >= 1, "tile geometry");
     typedef ActLoad<TIn> LD;
-    typedef typename LD::raw_t raw_t;
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF + 2 * CS_BYTES];
+    // Raw tile rows land (asynchronously, double-buffered) in raw0/raw1; the
+    // normalised K^ and V^T tiles are single-buffered.  Distinct LDS objects,
+    // so the compiler can tell the asynchronous loads never alias K^ / V^T.
+    __shared__ __attribute__((aligned(16))) uint8_t raw0[RAW_BYTES], raw1[RAW_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t khs[KH_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t vts[VT_BYTES];
+    __shared__ __attribute__((aligned(16))) float cs0[CS_FLOATS], cs1[CS_FLOATS];
     __shared__ TileMeta meta[4];
     __shared__ float2 qcs[kMaxRopePairs];
+    __shared__ double turns[kMaxRopePairs];
+    __shared__ float gkv_s[D];
+    __shared__ uint32_t redo;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
     const int lane = tid & 63;
     const int lrow = lane & 31;
     const int lh = lane >> 5;
@@ -196,131 +250,162 @@ void mqa_fwd_kernel(const AttnArgs a) {
     const int tile1 = min(n_tiles, tile0 + tps);
 
     // wave 0: source rows, positions and validity of tile `tile` -> meta[slot]
-    auto tile_meta = [&](int tile, int slot) {
+    auto tile_meta = [&](int tile, int slot) __attribute__((always_inline)) {
         if (wave != 0) return;
+        const int ol = opaque_tid() & 63;
         int32_t pos = 0;
         const TIn* row = nullptr;
-        if (lane < TK && tile < tile1) row = slot_row<SPARSE, TIn>(a, g, bq, tile * TK + lane, D, &pos);
-        if (lane < TK) {
-            meta[slot].rowp[lane] = reinterpret_cast<uint64_t>(row);
-            meta[slot].pos[lane] = pos;
+        if (ol < TK && tile < tile1) row = slot_row<SPARSE, TIn>(a, g, bq, tile * TK + ol, D, &pos);
+        if (ol < TK) {
+            meta[slot].rowp[ol] = reinterpret_cast<uint64_t>(row);
+            meta[slot].pos[ol] = pos;
         }
         const uint64_t bal = __ballot(row != nullptr);
-        if (lane == 0) meta[slot].mask = (uint32_t)bal;
+        if (ol == 0) meta[slot].mask = (uint32_t)bal;
     };
-    // all threads: rotary (cos, sin) of tile rows -> cs buffer cbuf
-    auto tile_cs = [&](int mslot, int cbuf) {
-        const int rho = tid >> 3, pg = tid & 7;
+    // all threads: rotary (cos, sin) of the tile rows -> cst
+    auto tile_cs = [&](int mslot, float* cst) __attribute__((always_inline)) {
+        const int ot = opaque_tid();
+        const int rho = ot >> 3, pg = ot & 7;
         const int32_t pos = meta[mslot].pos[rho];
-        float2* cst = reinterpret_cast<float2*>(smem + 2 * BUF + cbuf * CS_BYTES);
         for (int i = pg; i < n_pairs; i += 8) {
             float sn, cs;
-            sincos_turns((double)pos * a.rope_turns[i], &sn, &cs);
-            cst[rho * kMaxRopePairs + i] = make_float2(cs, sn);
+            sincos_turns((double)pos * turns[i], &sn, &cs);
+            cst[2 * (rho * kMaxRopePairs + i)] = cs;
+            cst[2 * (rho * kMaxRopePairs + i) + 1] = sn;
+        }
+    };
+    // asynchronous HBM -> LDS copy of the tile's rows (global_load_lds_dwordx4):
+    // one contiguous 1 KiB unit per wave instruction, rows in tile order.
+    auto tile_load = [&](int mslot, uint8_t* dst) __attribute__((always_inline)) {
+        const int ol = opaque_tid() & 63;
+#pragma unroll
+        for (int u = wave; u < UNITS; u += 4) {
+            const int rho = u * RPU + ol / LPR;
+            const int p = ol % LPR;
+            const uint64_t rp = meta[mslot].rowp[rho];
+            const int gsrc = p;
+            if (rp) lds_dma16(reinterpret_cast<const uint8_t*>(rp) + 16 * gsrc, (uint32_t)(uintptr_t)(dst + 1024 * u));
         }
     };
 
     // ---------------------------------------------------------------- prologue
     if (wave == 0 && lane < n_pairs) {
+        const double tn = rope_turns(a.rope_base, lane, a.rope_dims);
+        turns[lane] = tn;
         float sn, cs;
-        sincos_turns((double)g.t * a.rope_turns[lane], &sn, &cs);
+        sincos_turns((double)g.t * tn, &sn, &cs);
         qcs[lane] = make_float2(cs, sn);
     }
+    for (int i = tid; i < D; i += 256) gkv_s[i] = a.gamma_kv ? a.gamma_kv[i] : 1.0f;
     tile_meta(tile0, 0);
     tile_meta(tile0 + 1, 1);
-    lds_barrier();
+    barrier_all();
 
-    // Q^ = RoPE_t(gamma_q * q / rms(q)) for all heads, staged in LDS as f16
-    // (row = head, 16-byte granules XOR-swizzled by row)
+    // Q^ = RoPE_t(gamma_q * q / rms(q)); wave w stages its 32 heads as f16 in
+    // one of the tile buffers (row = head, granules XOR-swizzled by row)
+    static_assert(RAW_BYTES >= KH_BYTES, "query staging needs four 32-head buffers");
     const bool has_heads = 32 * wave < H;
-    {
-        uint8_t* qs = smem;
-        for (int hh = 0; hh < 32; ++hh) {
-            const int head = 32 * wave + hh;  // heads >= H are staged as zeros
-            const TIn* qrow = reinterpret_cast<const TIn*>(a.q) + (bq * H + (head < H ? head : 0)) * (int64_t)D;
-            float v[8];
-            if (lane < G && head < H) LD::to_f32(LD::load(qrow + 8 * lane), v);
-            else
+    uint8_t* qstage = wave == 0 ? khs : wave == 1 ? vts : wave == 2 ? raw0 : raw1;
+    for (int hh = 0; hh < 32; ++hh) {
+        const int head = 32 * wave + hh;  // heads >= H are staged as zeros
+        const TIn* qrow = reinterpret_cast<const TIn*>(a.q) + (bq * H + (head < H ? head : 0)) * (int64_t)D;
+        float v[8];
+        if (lane < G && head < H) LD::to_f32(LD::load(qrow + 8 * lane), v);
+        else
 #pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-            float ss = 0.0f;
+            for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+        float ss = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
-            ss = wave_sum(ss);
-            const float inv = __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps);
-            if (lane < G) {
+        for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
+        ss = wave_sum(ss);
+        const float inv = __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps);
+        if (lane < G) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] *= inv * (a.gamma_q ? a.gamma_q[8 * lane + i] : 1.0f);
-                if (8 * lane >= rope_lo) {
-#pragma unroll
-                    for (int i = 0; i < 8; i += 2) {
-                        const float2 c = qcs[(8 * lane + i - rope_lo) >> 1];
-                        const float x0 = v[i], x1 = v[i + 1];
-                        v[i] = x0 * c.x - x1 * c.y;
-                        v[i + 1] = x0 * c.y + x1 * c.x;
-                    }
-                }
-                u32x4 w4 = {pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]),
-                            pack_f16x2(v[6], v[7])};
-                *reinterpret_cast<u32x4*>(qs + head * (2 * D) + ((lane ^ (head & SWZ)) << 4)) = w4;
-            }
-        }
-    }
-    lds_barrier();
-    f16x8 qf[KSTEPS];
-    {
-        const int head = 32 * wave + lrow;
-        const uint8_t* qrow = smem + head * (2 * D);
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-            qf[s] = *reinterpret_cast<const f16x8*>(qrow + (((2 * s + lh) ^ (head & SWZ)) << 4));
-    }
-
-    // ---------------------------------------------------------------- loader role
-    const int kb = tid / G;  // key block (8 slots)
-    const int db = tid % G;  // 8-channel granule
-    const bool ld_on = tid < 4 * G;
-    raw_t raw[8];
-    auto issue_loads = [&](int mslot) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint64_t rp = ld_on ? meta[mslot].rowp[loader_row(kb, e)] : 0ull;
-            raw[e] = rp ? LD::load(reinterpret_cast<const TIn*>(rp) + 8 * db) : LD::zero();
-        }
-    };
-    // normalise, rotate and store the tile held in raw[] into LDS buffer `buf`
-    auto store_tile = [&](int buf, int cbuf) {
-        if (!ld_on) return;
-        uint8_t* kh = smem + buf * BUF;
-        uint8_t* vt = kh + KH_BYTES;
-        const float2* cst = reinterpret_cast<const float2*>(smem + 2 * BUF + cbuf * CS_BYTES);
-        const bool rot = 8 * db >= rope_lo;
-        uint32_t hk[8][4];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float v[8];
-            LD::to_f32(raw[e], v);
-            float ss = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
-            ss = group_sum<G>(ss);
-            const float inv = __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] *= inv * (a.gamma_kv ? a.gamma_kv[8 * db + i] : 1.0f);
-            const int rho = loader_row(kb, e);
-            if (rot) {
+            for (int i = 0; i < 8; ++i) v[i] *= inv * (a.gamma_q ? a.gamma_q[8 * lane + i] : 1.0f);
+            if (8 * lane >= rope_lo) {
 #pragma unroll
                 for (int i = 0; i < 8; i += 2) {
-                    const float2 c = cst[rho * kMaxRopePairs + ((8 * db + i - rope_lo) >> 1)];
+                    const float2 c = qcs[(8 * lane + i - rope_lo) >> 1];
                     const float x0 = v[i], x1 = v[i + 1];
                     v[i] = x0 * c.x - x1 * c.y;
                     v[i + 1] = x0 * c.y + x1 * c.x;
                 }
             }
+            u32x4 w4 = {pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]),
+                        pack_f16x2(v[6], v[7])};
+            *reinterpret_cast<u32x4*>(qstage + hh * (2 * D) + ((lane ^ (hh & SWZ)) << 4)) = w4;
+        }
+    }
+    barrier_lds();
+    f16x8 qf[KSTEPS];
+    {
+        const uint8_t* qrow = qstage + lrow * (2 * D);
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+            qf[s] = *reinterpret_cast<const f16x8*>(qrow + (((2 * s + lh) ^ (lrow & SWZ)) << 4));
+    }
+
+    // ---------------------------------------------------------------- tile store
+    const int kb = tid / G;  // key block (8 slots)
+    const int db = tid % G;  // 8-channel granule
+    const bool ld_on = tid < 4 * G;
+    // normalise, rotate and convert the landed tile rows in place (bf16) or
+    // from the raw buffer (f32); write K^ and V^T
+    auto store_tile = [&](int mslot, uint8_t* kh, uint8_t* vt, const uint8_t* rawb, const float* cst) __attribute__((always_inline)) {
+        if (!ld_on) return;
+        const int ot = opaque_tid();
+        const int kb = ot / G, db = ot % G;
+        const bool rot = 8 * db >= rope_lo;
+        uint32_t hk[8][4];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int rho = loader_row(kb, e);
+            const bool valid = meta[mslot].rowp[rho] != 0ull;
+            uint8_t* kslot = kh + rho * (2 * D) + ((db ^ (rho & SWZ)) << 4);
+            float v[8];
+            if (valid) {
+                if (RAW_F32) {
+                    const f32x4 x0 = *reinterpret_cast<const f32x4*>(rawb + rho * (4 * D) + 32 * db);
+                    const f32x4 x1 = *reinterpret_cast<const f32x4*>(rawb + rho * (4 * D) + 32 * db + 16);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v[i] = x0[i];
+                        v[4 + i] = x1[i];
+                    }
+                } else {
+                    const u32x4 r = *reinterpret_cast<const u32x4*>(rawb + rho * (2 * D) + 16 * db);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v[2 * i] = bf16_bits_to_f32(r[i] & 0xffffu);
+                        v[2 * i + 1] = bf16_bits_to_f32(r[i] >> 16);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+            }
+            float ss = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
+            ss = group_sum<G>(ss);
+            const float inv = valid ? __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps) : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] *= inv * gkv_s[8 * db + i];
+            if (rot) {
+#pragma unroll
+                for (int i = 0; i < 8; i += 2) {
+                    const int pi = (8 * db + i - rope_lo) >> 1;
+                    const float c = cst[2 * (rho * kMaxRopePairs + pi)], sn = cst[2 * (rho * kMaxRopePairs + pi) + 1];
+                    const float x0 = v[i], x1 = v[i + 1];
+                    v[i] = x0 * c - x1 * sn;
+                    v[i + 1] = x0 * sn + x1 * c;
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) hk[e][i] = pack_f16x2(v[2 * i], v[2 * i + 1]);
-            u32x4 w4 = {hk[e][0], hk[e][1], hk[e][2], hk[e][3]};
-            *reinterpret_cast<u32x4*>(kh + rho * (2 * D) + ((db ^ (rho & SWZ)) << 4)) = w4;
+            *reinterpret_cast<u32x4*>(kslot) = u32x4{hk[e][0], hk[e][1], hk[e][2], hk[e][3]};
+            __builtin_amdgcn_sched_barrier(0);  // one key at a time: bounded register use
         }
         // V^T: channel 8*db+i, virtual slots [8*kb, 8*kb+8) = keys e = 0..7
 #pragma unroll
@@ -332,38 +417,111 @@ void mqa_fwd_kernel(const AttnArgs a) {
                 const uint32_t x = hk[2 * p][wd], y = hk[2 * p + 1][wd];
                 o[p] = half ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
             }
-            u32x4 w4 = {o[0], o[1], o[2], o[3]};
-            *reinterpret_cast<u32x4*>(vt + vt_offset(8 * db + i, kb)) = w4;
+            *reinterpret_cast<u32x4*>(vt + vt_offset(8 * db + i, kb)) = u32x4{o[0], o[1], o[2], o[3]};
         }
     };
 
     // ---------------------------------------------------------------- state
     // The accumulator is only ever written by MFMAs (and zero-filled), never
     // by VALU, so it can live in AGPRs.  Softmax reference max m_use is fixed
-    // per head at the first finite tile max; P = 2^(l - m_use) stays below
+    // per head at the first finite tile max; P = 2^(l - m_use) stays inside
     // f16's range while l <= m_use + 15.  If a later logit exceeds that, the
     // wave flags itself, keeps tracking the true max m_seen, and the tile
     // loop runs a second pass for the flagged waves with m_use = m_seen
     // (then P <= 1).  Typical inputs never take the second pass.
-    // per-lane swizzled LDS offsets of the MFMA operand reads:
-    //   K^ row lrow, granule g = 2s + lh  -> koff[s % 8] + 256 * (s / 8)
-    //   V^T row 32*dt + lrow, granule g   -> vrow_off + voff[g ^ (dt % 4)] + 2048 * dt
-    uint32_t koff[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) koff[s] = ((((2 * s + lh) & SWZ) ^ (lrow & SWZ)) | ((2 * s + lh) & ~SWZ)) << 4;
-    const int lrp = lrow ^ ((lrow >> 3) & 3);  // V^T row placement within a 32-row block
-    const uint32_t vrow_off = (uint32_t)lrp * 64;
-    uint32_t voff[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) voff[x] = (uint32_t)((x ^ ((lrp >> 2) & 3)) << 4);
-
     f32x16 acc[DT];
     float m_use = -INFINITY, m_seen = -INFINITY, l_run = 0.0f;
     bool flagged = false;  // wave-uniform
-    __shared__ uint32_t redo;
+    bool active = has_heads;
 
+    // QK, softmax and PV on a stored tile
+    auto compute_tile = [&](int mslot, const uint8_t* kh, const uint8_t* vt) __attribute__((always_inline)) {
+        if (!active) return;
+        const uint32_t mask = meta[mslot].mask;
+        // per-lane swizzled LDS offsets of the MFMA operand reads, recomputed
+        // per tile (a few VALU ops) instead of being held in VGPRs:
+        //   K^ row lrow, granule g = 2s + lh  -> koff[s % 8] + 256 * (s / 8)
+        //   V^T row 32*dt + lrow, granule g   -> vrow_off + voff[g ^ (dt % 4)] + 2048 * dt
+        const int ol = opaque_tid() & 63;
+        const int orow = ol & 31, oh = ol >> 5;
+        uint32_t koff[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) koff[s] = ((((2 * s + oh) & SWZ) ^ (orow & SWZ)) | ((2 * s + oh) & ~SWZ)) << 4;
+        const int lrp = orow ^ ((orow >> 3) & 3);  // V^T row placement within a 32-row block
+        const uint32_t vrow_off = (uint32_t)lrp * 64;
+        uint32_t voff[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) voff[x] = (uint32_t)((x ^ ((lrp >> 2) & 3)) << 4);
+        f32x16 st;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[r] = 0.0f;
+        const uint8_t* krow = kh + orow * (2 * D);
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+            const f16x8 av = *reinterpret_cast<const f16x8*>(krow + koff[s & 7] + 256 * (s >> 3));
+            st = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qf[s], st, 0, 0, 0);
+        }
+        // softmax numerators for rows 8*(r/4) + 4*lh + r%4 of this tile
+        float mx = -INFINITY;
+        const uint32_t mrow = mask >> (4 * oh);  // rows 8*(r/4) + 4*oh + r%4
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            st[r] = ((mrow >> (8 * (r >> 2) + (r & 3))) & 1u) ? st[r] * a.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, st[r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        m_seen = fmaxf(m_seen, mx);
+        if (m_use == -INFINITY) m_use = mx;  // nothing accumulated for this head yet
+        if (__ballot(mx > m_use + 15.0f)) flagged = true;
+        if (flagged) return;
+        const bool live = m_use != -INFINITY;
+        float psum = 0.0f;
+        uint32_t pk[8];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const float p0 = live ? __builtin_amdgcn_exp2f(st[r] - m_use) : 0.0f;
+            const float p1 = live ? __builtin_amdgcn_exp2f(st[r + 1] - m_use) : 0.0f;
+            psum += p0 + p1;
+            pk[r >> 1] = pack_f16x2(p0, p1);
+        }
+        psum += __shfl_xor(psum, 32, 64);
+        l_run += psum;
+        const f16x8 pa0 = __builtin_bit_cast(f16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+        const f16x8 pa1 = __builtin_bit_cast(f16x8, u32x4{pk[4], pk[5], pk[6], pk[7]});
+        const uint8_t* vrow = vt + vrow_off;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const f16x8 b0 = *reinterpret_cast<const f16x8*>(vrow + voff[oh ^ (dt & 3)] + 2048 * dt);
+            const f16x8 b1 = *reinterpret_cast<const f16x8*>(vrow + voff[(2 + oh) ^ (dt & 3)] + 2048 * dt);
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa0, b0, acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa1, b1, acc[dt], 0, 0, 0);
+        }
+    };
+
+    // one pipeline step on raw buffer B: store tile `tile` from raw B into
+    // K^ / V^T, start loading tile+1 into the other raw buffer, then compute
+    auto step = [&](auto bsel, int tile, int it) __attribute__((always_inline)) {
+        constexpr int B = decltype(bsel)::value;
+        uint8_t* rawc = B == 0 ? raw0 : raw1;
+        uint8_t* rawn = B == 0 ? raw1 : raw0;
+        float* csc = B == 0 ? cs0 : cs1;
+        float* csn = B == 0 ? cs1 : cs0;
+        asm volatile("; tile step on buffer set %0" ::"n"(B));  // keeps the two bodies distinct
+        store_tile(it & 3, khs, vts, rawc, csc);
+        tile_meta(tile + 2, (it + 2) & 3);  // (its index loads complete before the tile loads start)
+        if (tile + 1 < tile1) {
+            tile_load((it + 1) & 3, rawn);
+            tile_cs((it + 1) & 3, csn);
+        }
+        barrier_lds();
+        asm volatile("; compute on buffer set %0" ::"n"(B));
+        compute_tile(it & 3, khs, vts);
+        barrier_all();
+    };
+
+    barrier_lds();  // every wave has read its Q^ block: the buffers are free
     for (int pass = 0; pass < 2; ++pass) {
-        const bool active = has_heads && (pass == 0 || flagged);
+        active = has_heads && (pass == 0 || flagged);
         if (pass == 1) {
             if (flagged) {
                 m_use = m_seen;
@@ -372,7 +530,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
             }
             tile_meta(tile0, 0);
             tile_meta(tile0 + 1, 1);
-            lds_barrier();
+            barrier_lds();
         }
         if (active) {
 #pragma unroll
@@ -381,78 +539,19 @@ void mqa_fwd_kernel(const AttnArgs a) {
                 for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
         }
         if (tile0 < tile1) {
-            issue_loads(0);
-            tile_cs(0, 0);
+            tile_load(0, raw0);
+            tile_cs(0, cs0);
         }
-        lds_barrier();  // also retires every read of the staged Q^
-
-        int it = 0;
-        for (int tile = tile0; tile < tile1; ++tile, ++it) {
-            const int buf = it & 1;
-            store_tile(buf, buf);
-            if (tile + 1 < tile1) {
-                issue_loads((it + 1) & 3);
-                tile_cs((it + 1) & 3, buf ^ 1);
-            }
-            tile_meta(tile + 2, (it + 2) & 3);
-            lds_barrier();
-            if (!active) continue;
-            const uint32_t mask = meta[it & 3].mask;
-            const uint8_t* kh = smem + buf * BUF;
-            const uint8_t* vt = kh + KH_BYTES;
-
-            // S^T[32 keys x 32 heads] = K^ Q^_w^T
-            f32x16 st;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) st[r] = 0.0f;
-            const uint8_t* krow = kh + lrow * (2 * D);
-#pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                const f16x8 av = *reinterpret_cast<const f16x8*>(krow + koff[s & 7] + 256 * (s >> 3));
-                st = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qf[s], st, 0, 0, 0);
-            }
-            // softmax numerators for rows 8*(r/4) + 4*lh + r%4 of this tile
-            float mx = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rho = 8 * (r >> 2) + 4 * lh + (r & 3);
-                st[r] = ((mask >> rho) & 1u) ? st[r] * a.scale_log2 : -INFINITY;
-                mx = fmaxf(mx, st[r]);
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            m_seen = fmaxf(m_seen, mx);
-            if (m_use == -INFINITY) m_use = mx;  // nothing accumulated for this head yet
-            if (__ballot(mx > m_use + 15.0f)) flagged = true;
-            if (flagged) continue;
-            const bool live = m_use != -INFINITY;
-            float psum = 0.0f;
-            uint32_t pk[8];
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = live ? __builtin_amdgcn_exp2f(st[r] - m_use) : 0.0f;
-                const float p1 = live ? __builtin_amdgcn_exp2f(st[r + 1] - m_use) : 0.0f;
-                psum += p0 + p1;
-                pk[r >> 1] = pack_f16x2(p0, p1);
-            }
-            psum += __shfl_xor(psum, 32, 64);
-            l_run += psum;
-            const f16x8 pa0 = __builtin_bit_cast(f16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-            const f16x8 pa1 = __builtin_bit_cast(f16x8, u32x4{pk[4], pk[5], pk[6], pk[7]});
-            // O[32 heads x D] += P V^
-            const uint8_t* vrow = vt + vrow_off;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const f16x8 b0 = *reinterpret_cast<const f16x8*>(vrow + voff[(lh) ^ (dt & 3)] + 2048 * dt);
-                const f16x8 b1 = *reinterpret_cast<const f16x8*>(vrow + voff[(2 + lh) ^ (dt & 3)] + 2048 * dt);
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa0, b0, acc[dt], 0, 0, 0);
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa1, b1, acc[dt], 0, 0, 0);
-            }
+        barrier_all();
+        for (int tile = tile0, it = 0; tile < tile1; tile += 2, it += 2) {
+            step(std::integral_constant<int, 0>(), tile, it);
+            if (tile + 1 < tile1) step(std::integral_constant<int, 1>(), tile + 1, it + 1);
         }
         // does any wave need the second pass?
         if (tid == 0) redo = 0u;
-        lds_barrier();
+        barrier_lds();
         if (lane == 0 && flagged) redo = 1u;
-        lds_barrier();
+        barrier_lds();
         if (redo == 0u) break;
     }
     if (!has_heads) return;
@@ -512,7 +611,7 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(const AttnArgs a) {
         int32_t t = a.q_pos[bq];
         t = t < 0 ? 0 : t;
         float sn, cs;
-        sincos_turns(-(double)t * a.rope_turns[(2 * pr - rope_lo) >> 1], &sn, &cs);
+        sincos_turns(-(double)t * rope_turns(a.rope_base, (2 * pr - rope_lo) >> 1, a.rope_dims), &sn, &cs);
         const float x0 = o0, x1 = o1;
         o0 = x0 * cs - x1 * sn;
         o1 = x0 * sn + x1 * cs;
@@ -541,7 +640,12 @@ static int launch_one(const AttnArgs& a, int64_t BQ, hipStream_t stream) {
 template <int D>
 static int launch_d(const AttnArgs& a, int64_t BQ, bool act_f32, hipStream_t stream) {
     const bool sparse = a.idx != nullptr;
-    if (act_f32) return sparse ? launch_one<D, true, float>(a, BQ, stream) : launch_one<D, false, float>(a, BQ, stream);
+    if constexpr (D <= 128) {
+        if (act_f32)
+            return sparse ? launch_one<D, true, float>(a, BQ, stream) : launch_one<D, false, float>(a, BQ, stream);
+    } else {
+        if (act_f32) return -2;  // f32 activations: head dims up to 128
+    }
     return sparse ? launch_one<D, true, bf16_t>(a, BQ, stream) : launch_one<D, false, bf16_t>(a, BQ, stream);
 }
 

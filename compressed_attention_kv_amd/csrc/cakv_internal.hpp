@@ -10,8 +10,8 @@ namespace cakv {
 
 constexpr int kMaxRopePairs = 32;  // rope_dims <= 64
 constexpr int kTopkCap = 4096;     // largest k
-constexpr int kBoundaryCap = 4096; // boundary-bin candidates kept on the fast path
-constexpr int kHistBins = 2048;    // top 11 bits of the score key
+constexpr int kBoundaryCap = 4096; // top-k candidates held in LDS on the fast path
+constexpr int kHistBins = 2048;    // sample histogram over the top 11 bits of the score key
 
 // Everything one attention launch needs; passed by value as the kernel
 // argument block.
@@ -42,8 +42,13 @@ struct AttnArgs {
     float rms_eps;
     int32_t n_splits;
     int32_t out_f32;   // 1: float32 output, 0: bf16
-    double rope_turns[kMaxRopePairs];  // theta_i / (2 pi): turns per unit position
+    float rope_base;   // theta_i = rope_base^(-2i/rope_dims)
 };
+
+// theta_i / (2 pi) in fp64: turns of rotary pair i per unit of position
+__device__ __forceinline__ double rope_turns(float base, int i, int rope_dims) {
+    return pow((double)base, -2.0 * i / (double)rope_dims) * 0.15915494309189533577;
+}
 
 int launch_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B, int64_t T,
                        int64_t D, int32_t m, void* out, int out_dtype, float* out_scale,
@@ -59,11 +64,7 @@ struct IndexerArgs {
     const float* k_scale;
     const int32_t* q_pos;
     int32_t* idx;
-    uint32_t* keys;      // [BQ][N]
-    uint32_t* hist;      // [BQ][kHistBins]
-    uint32_t* counters;  // [BQ][4]: above, boundary, ticket, spare
-    int32_t* sel;        // [BQ][k]
-    uint64_t* bnd;       // [BQ][kBoundaryCap]
+    uint32_t* keys;      // [BQ][N] order-preserving score keys
     int64_t Q;
     int64_t N;
     int32_t HI;
@@ -72,8 +73,6 @@ struct IndexerArgs {
     int32_t k;
     int32_t chunk;       // entries per score workgroup
     int32_t n_chunks;
-    int32_t sel_chunk;   // entries per select workgroup
-    int32_t n_sel_chunks;
 };
 
 size_t indexer_workspace_bytes(int64_t BQ, int64_t N, int32_t k);

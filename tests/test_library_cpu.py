@@ -85,7 +85,7 @@ def test_indexer_errors_and_workspace(lib):
     f = lib.cakv_indexer_topk
     ws = lib.cakv_indexer_topk_workspace(8, 1, 262144, 1024)
     assert ws >= 8 * 262144 * 4
-    assert lib.cakv_indexer_topk_workspace(8, 1, 262144, 2048) > ws
+    assert lib.cakv_indexer_topk_workspace(8, 1, 262144, 2048) >= ws
     # dtype combinations
     assert f(FAKE, cakv.F32, FAKE, FAKE, cakv.FP8_E4M3, FAKE, FAKE, 1, 1, 64, 64, 128, 4, 16, FAKE, FAKE, ws, None) == -2
     assert f(FAKE, cakv.BF16, FAKE, FAKE, cakv.FP8_E4M3, FAKE, FAKE, 1, 1, 64, 48, 128, 4, 16, FAKE, FAKE, ws, None) == -2
