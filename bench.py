@@ -66,7 +66,6 @@ class Step:
     """Device-resident inputs (several copies of the caches) and one step of the path."""
 
     def __init__(self, name: str):
-        import oracle  # CPU reference: quantises the indexer keys exactly as its spec says
         self.name = name
         inp = make_inputs(name)
         w = self.w = inp["workload"]
@@ -75,8 +74,12 @@ class Step:
         ws_bytes = 0
         nq = w.B * w.Q
         if self.sparse:
-            codes, scale = oracle.q8_quantize(inp["k_idx"].numpy())
-            self.codes_host, self.scale_host = codes, scale
+            # the indexer key cache in fp8 + per-entry scale: kv_compress with
+            # m = 1 is exactly the per-entry quantiser
+            kf = inp["k_idx"].to(dev)
+            codes, scale = cakv.kv_compress(kf, torch.zeros(kf.shape[:2], dtype=torch.float32, device=dev), 1,
+                                            out_dtype=torch.float8_e4m3fn)
+            del kf
             step_bytes = (_alg_bytes_indexer(w) + _alg_bytes_attention(w, True)) * nq
         else:
             step_bytes = _alg_bytes_attention(w, False) * nq
@@ -85,8 +88,8 @@ class Step:
         self.copies = max(1, math.ceil(3 * CACHE_BYTES / step_bytes))
         self.kv = [inp["kv"].to(dev) for _ in range(self.copies)]
         if self.sparse:
-            self.kidx = [torch.from_numpy(codes).to(dev) for _ in range(self.copies)]
-            self.kscale = [torch.from_numpy(scale).to(dev) for _ in range(self.copies)]
+            self.kidx = [codes] + [codes.clone() for _ in range(self.copies - 1)]
+            self.kscale = [scale] + [scale.clone() for _ in range(self.copies - 1)]
             self.q_idx = inp["q_idx"].to(dev)
             self.wts = inp["w"].to(dev)
             self.idx = torch.empty((w.B, w.Q, w.k), dtype=torch.int32, device=dev)
@@ -132,11 +135,13 @@ class Step:
         w, inp = self.w, self.inp
         n = min(max_queries, w.B * w.Q)
         rows = np.arange(n, dtype=np.int64)
+        if self.sparse:  # input preparation, outside the timed region
+            codes, scale = oracle.q8_quantize(inp["k_idx"].numpy())
         t0 = time.perf_counter()
         kw = dict(m=w.m, n_win=w.n_win, rope_dims=w.rope_dims, rope_base=w.rope_base)
         if self.sparse:
-            idx = oracle.indexer_topk(inp["q_idx"], inp["w"], inp["q_pos"], w.m, w.k, k_code=self.codes_host,
-                                      k_scale=self.scale_host, rows=rows)
+            idx = oracle.indexer_topk(inp["q_idx"], inp["w"], inp["q_pos"], w.m, w.k, k_code=codes,
+                                      k_scale=scale, rows=rows)
             full = np.full((w.B * w.Q, w.k), -1, np.int32)
             full[:n] = idx
             oracle.attention(inp["q"], inp["kv"], inp["kv_raw"], inp["raw_pos0"], inp["q_pos"], inp["sinks"],
@@ -152,6 +157,19 @@ class Step:
                 "seconds": round(dt, 3)}
 
 
+def copy_calibration(mib: int):
+    """A plain copy kernel of known size: each launch reads and writes exactly
+    `mib` MiB, the yardstick for the FETCH_SIZE / WRITE_SIZE counters."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,11 +179,16 @@ def main():
                     choices=["csa_decode_128k", "csa_decode_1m", "hca_decode_1m"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-queries", type=int, default=32)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     torch.cuda.init()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     st = Step(args.workload)
     w = st.w
     for _ in range(args.warmup):

@@ -10,7 +10,7 @@ namespace cakv {
 
 constexpr int kMaxRopePairs = 32;  // rope_dims <= 64
 constexpr int kTopkCap = 4096;     // largest k
-constexpr int kBoundaryCap = 4096; // top-k candidates held in LDS on the fast path
+constexpr int kBoundaryCap = 8192; // top-k candidates held in LDS on the fast path
 constexpr int kHistBins = 2048;    // sample histogram over the top 11 bits of the score key
 
 // Everything one attention launch needs; passed by value as the kernel

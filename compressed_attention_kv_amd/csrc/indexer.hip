@@ -20,9 +20,9 @@
 //        fp32 mode: one thread per entry runs the canonical fmaf chains.
 //      Each score is written as an order-preserving 32-bit key.
 //   2. top-k: one workgroup per query, no cross-workgroup hand-off.  A
-//      strided sample of the keys gives a threshold bin (top 11 bits) that a
-//      little more than k keys reach; one coalesced pass collects every key at
-//      or above it into LDS; an LSD-free radix select on (key, index) finds
+//      strided sample of the keys gives a threshold (top 22 bits of the key,
+//      from two 11-bit histogram levels) that a little more than k keys reach;
+//      one coalesced pass collects every key at or above it into LDS; an LSD-free radix select on (key, index) finds
 //      the k-th best exactly; the winners are marked in an LDS bitmap over
 //      the entry range and compacted in index order.  If the guess collects
 //      fewer than k or more than the LDS capacity, an exact radix select over
@@ -168,7 +168,8 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kBitmapWords = 8192;  // LDS bitmap covers 2^18 entries
 
-// Workgroup-wide exclusive prefix sum of one value per thread (kSelThreads).
+// Workgroup-wide exclusive prefix sum of one value per thread (kSelThreads);
+// every thread also receives the workgroup total.  wsum: kSelWaves + 1 words.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t incl = v;
@@ -188,10 +189,11 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
             if (lane >= o) xi += t;
         }
         if (lane < kSelWaves) wsum[lane] = xi - x;
-        if (lane == kSelWaves - 1) *total = xi;
+        if (lane == kSelWaves - 1) wsum[kSelWaves] = xi;
     }
     __syncthreads();
     const uint32_t r = wsum[wave] + incl - v;
+    *total = wsum[kSelWaves];
     __syncthreads();
     return r;
 }
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(kSelThreads) void idx_topk_kernel(const IndexerArgs
     __shared__ uint32_t hist[kHistBins];
     __shared__ uint64_t cand[kBoundaryCap];
     __shared__ uint32_t bits[kBitmapWords];
-    __shared__ uint32_t wsum[kSelWaves];
+    __shared__ uint32_t wsum[kSelWaves + 1];
     __shared__ uint32_t info[16];
     const int64_t bq = blockIdx.x;
     const int tid = threadIdx.x;
@@ -297,11 +299,15 @@ __global__ __launch_bounds__(kSelThreads) void idx_topk_kernel(const IndexerArgs
     }
     const uint32_t* keys = a.keys + bq * a.N;
 
-    // ---- 1. threshold guess from a strided sample of the keys
+    // ---- 1. threshold guess from a strided sample of the keys: the sample's
+    //         want-th best key, to 22 bits (two 11-bit histogram levels)
     for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = 0u;
     if (tid < 16) info[tid] = 0u;
     __syncthreads();
     const int64_t S = nvis < 16384 ? nvis : 16384;
+    // aim at ~1.5 k keys plus a margin at or above the threshold
+    const uint32_t want = (uint32_t)(((1.5 * k) * (double)S) / (double)nvis) + 24u;
+    uint32_t t22 = 0u;  // keys with (key >> 10) >= t22 are collected
     {
         // all of this thread's sample loads are issued before any histogram update
         uint32_t sk[16];
@@ -313,20 +319,42 @@ __global__ __launch_bounds__(kSelThreads) void idx_topk_kernel(const IndexerArgs
 #pragma unroll
         for (int u = 0; u < 16; ++u)
             if (tid + (int64_t)u * kSelThreads < S) atomicAdd(&hist[sk[u] >> 21], 1u);
-    }
-    __syncthreads();
-    // aim at ~1.5 k keys plus a margin at or above the threshold bin
-    const uint32_t want = (uint32_t)(((1.5 * k) * (double)S) / (double)nvis) + 24u;
-    {
-        // bins from the top: thread t owns bins 2047-2t, 2046-2t
+        __syncthreads();
+        // bins from the top: thread t owns bins 2047-2t, 2046-2t; info[0] = the
+        // bin where the running count reaches want, info[2] = samples above it
         const uint32_t h0 = hist[kHistBins - 1 - 2 * tid], h1 = hist[kHistBins - 2 - 2 * tid];
         uint32_t tot;
         const uint32_t excl = block_excl_scan(h0 + h1, wsum, &tot);
-        if (excl < want && want <= excl + h0 + h1) info[0] = (uint32_t)(kHistBins - 1 - 2 * tid - (excl + h0 >= want ? 0 : 1));
-        if (tid == 0 && tot < want) info[0] = 0u;  // sample too thin: take everything
+        if (excl < want && want <= excl + h0) {
+            info[0] = (uint32_t)(kHistBins - 1 - 2 * tid);
+            info[2] = excl;
+        } else if (excl + h0 < want && want <= excl + h0 + h1) {
+            info[0] = (uint32_t)(kHistBins - 2 - 2 * tid);
+            info[2] = excl + h0;
+        }
+        __syncthreads();
+        if (tot >= want) {  // else the sample is too thin: take everything (t22 = 0)
+            const uint32_t tbin = info[0];
+            const uint32_t want2 = want - info[2];
+            for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (tid + (int64_t)u * kSelThreads < S && (sk[u] >> 21) == tbin)
+                    atomicAdd(&hist[(sk[u] >> 10) & (kHistBins - 1)], 1u);
+            __syncthreads();
+            const uint32_t g0 = hist[kHistBins - 1 - 2 * tid], g1 = hist[kHistBins - 2 - 2 * tid];
+            uint32_t tot2;
+            const uint32_t ex2 = block_excl_scan(g0 + g1, wsum, &tot2);
+            if (ex2 < want2 && want2 <= ex2 + g0 + g1)
+                info[1] = (uint32_t)(kHistBins - 1 - 2 * tid - (ex2 + g0 >= want2 ? 0 : 1));
+            __syncthreads();
+            t22 = (tbin << 11) | info[1];
+            __syncthreads();
+            if (tid == 0) info[1] = 0u;
+            __syncthreads();
+        }
     }
-    __syncthreads();
-    const uint32_t tbin = info[0];
 
     // ---- 2. collect every key in a bin >= tbin (coalesced pass over the keys;
     //         eight 16-byte loads per thread in flight per batch)
@@ -349,7 +377,7 @@ __global__ __launch_bounds__(kSelThreads) void idx_topk_kernel(const IndexerArgs
             const int64_t j = j0 + ((int64_t)u * kSelThreads + tid) * 4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                if (j + e < nvis && (kv[u][e] >> 21) >= tbin) {
+                if (j + e < nvis && (kv[u][e] >> 10) >= t22) {
                     const uint32_t p = atomicAdd(&info[1], 1u);
                     if (p < (uint32_t)kBoundaryCap) cand[p] = rank_value(kv[u][e], j + e);
                 }
@@ -363,7 +391,6 @@ __global__ __launch_bounds__(kSelThreads) void idx_topk_kernel(const IndexerArgs
     // ---- 3. exact k-th best in rank order
     uint64_t vth;
     if (fast) {
-        // bits 63..53 of a candidate's rank value hold ~(top 11 key bits) >= ~tbin.. : examine all 64
         vth = radix_select_u64((int64_t)nc, (uint32_t)k, 63, 0,
                                [&](int64_t i, uint64_t* v) { *v = cand[i]; return true; }, hist, info + 4);
     } else {
