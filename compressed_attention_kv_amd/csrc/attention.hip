@@ -113,12 +113,20 @@ __device__ __forceinline__ QueryGeom query_geom(const AttnArgs& a, int64_t bq) {
     return g;
 }
 
-// Source row, position and validity of key slot `slot`.
-template <bool SPARSE, typename TIn>
-__device__ __forceinline__ const TIn* slot_row(const AttnArgs& a, const QueryGeom& g, int64_t bq,
-                                               int slot, int D, int32_t* pos) {
+// Compressed entry index held by key slot `slot` (sparse: the selection,
+// dense: the slot itself); only meaningful for slot < n_c.
+template <bool SPARSE>
+__device__ __forceinline__ int32_t slot_entry(const AttnArgs& a, const QueryGeom& g, int64_t bq, int slot) {
+    if (!SPARSE) return slot;
+    return slot < g.n_c ? a.idx[bq * a.K + slot] : 0;
+}
+
+// Source row and rotary position of key slot `slot` whose entry index is j
+// (from slot_entry); nullptr for an empty or invalid slot.
+template <typename TIn>
+__device__ __forceinline__ const TIn* slot_row(const AttnArgs& a, const QueryGeom& g, int slot, int32_t j,
+                                               int D, int32_t* pos) {
     if (slot < g.n_c) {
-        int32_t j = SPARSE ? a.idx[bq * a.K + slot] : slot;
         if (j < 0 || j >= g.n_vis) return nullptr;
         *pos = j * a.m + a.entry_pos_offset;
         return reinterpret_cast<const TIn*>(a.kv_c) + (g.b * a.N + j) * (int64_t)D;
@@ -132,27 +140,24 @@ __device__ __forceinline__ const TIn* slot_row(const AttnArgs& a, const QueryGeo
     return reinterpret_cast<const TIn*>(a.kv_raw) + (g.b * a.R + row) * (int64_t)D;
 }
 
-// tile row of loader key `e` (0..7) of key block kb (0..3): the order that
-// makes V^T's virtual slot 8*kb+e match the P operand layout
-__device__ __forceinline__ int loader_row(int kb, int e) {
-    return 16 * (kb >> 1) + 4 * (kb & 1) + (e & 3) + 8 * (e >> 2);
+// (sin, cos) of 2 pi x for an angle x in turns: the fractional turn is taken
+// in fp64 (x can exceed 2^17 turns), then the hardware v_sin_f32 / v_cos_f32,
+// whose input is in turns.
+__device__ __forceinline__ void sincos_turns_fast(double x, float* s_out, float* c_out) {
+    const float f = (float)(x - __builtin_floor(x));
+    *s_out = __builtin_amdgcn_sinf(f);
+    *c_out = __builtin_amdgcn_cosf(f);
 }
 
-// V^T row placement and granule swizzle (rows are 64 bytes: 32 f16 slots)
-__device__ __forceinline__ int vt_offset(int dim, int granule) {
-    int P = dim ^ ((dim >> 3) & 3);
-    int phys = granule ^ ((P >> 2) & 3) ^ ((P >> 5) & 3);
-    return P * 64 + phys * 16;
-}
-
-// Per-tile row metadata, written two tiles ahead by wave 0.
+// Per-tile row metadata, written four tiles ahead by wave 0.
 struct TileMeta {
     uint64_t rowp[TK];  // source row address, 0 for an empty / invalid slot
     int32_t pos[TK];    // rotary position of the row
     uint32_t mask;      // bit rho set when row rho is a valid key
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
+typedef __fp16 h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) h4 lds_h4;
 
 // Asynchronous 16-byte-per-lane HBM -> LDS load (global_load_lds_dwordx4):
 // lane i writes LDS bytes [lds_base + 16 i, +16).  Written as one asm block
@@ -167,6 +172,21 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
         "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gptr), "s"(lds_base)
+        : "memory");
+}
+
+// Asynchronous 4-byte-per-lane HBM -> LDS load (global_load_lds_dword):
+// lane i writes LDS bytes [lds_base + 4 i, +4).  Same M0 handling as above.
+__device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, off\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
         : "v"(gptr), "s"(lds_base)
@@ -200,35 +220,58 @@ __device__ __forceinline__ void barrier_all() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Barrier after which all but the last N of this wave's vector-memory loads
+// (in issue order) have completed, and all of its LDS traffic: with N = the
+// loads of the most recently issued tile, everything older has landed.
+template <int N>
+__device__ __forceinline__ void barrier_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);  // vmcnt(N) expcnt(7) lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int D, bool SPARSE, typename TIn>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mqa_fwd_kernel(const AttnArgs a) {
-    constexpr int G = D / 8;                 // 16-byte f16 granules per K^ row
-    constexpr int SWZ = (G < 16 ? G : 16) - 1;
-    constexpr int KSTEPS = D / 16;           // QK k-steps
-    constexpr int DT = D / 32;               // output dim tiles
-    constexpr int KH_BYTES = TK * D * 2;
-    constexpr int VT_BYTES = D * TK * 2;
+    constexpr int G = D / 8;                   // 16-byte f16 granules per K^ row
+    constexpr int KSTEPS = D / 16;             // QK k-steps
+    constexpr int DT = D / 32;                 // output dim tiles
     constexpr bool RAW_F32 = sizeof(TIn) == 4;
-    constexpr int RAW_BYTES = TK * D * (int)sizeof(TIn);  // landed (raw) tile rows
-    constexpr int CS_FLOATS = TK * kMaxRopePairs * 2;
-    constexpr int UNITS = TK * D * (int)sizeof(TIn) / 1024;  // 1 KiB load units per tile
-    constexpr int RPU = 1024 / (D * (int)sizeof(TIn));       // rows per unit
-    constexpr int LPR = 64 / RPU;                            // lanes per row in a unit
-    static_assert(UNITS % 4 == 0 && RPU >= 1, "tile geometry");
+    constexpr int RB = D * (int)sizeof(TIn);   // bytes of one raw row
+    constexpr int RPU = 1024 / RB;             // rows per 1 KiB asynchronous-load unit
+    constexpr int LPR = 64 / RPU;              // lanes per row in a unit
+    // Row stride in LDS.  A 1 KiB row (bf16, D = 512) is one unit and gets 16
+    // bytes of padding, so that 16-byte column reads of consecutive rows fall
+    // in distinct banks and every operand address is a base plus an
+    // immediate; smaller rows share a unit, stay packed and use an XOR
+    // swizzle of the 16-byte granules instead.
+    constexpr int PAD = RPU == 1 ? 16 : 0;
+    constexpr int RS = RB + PAD;               // ring row stride; K^ uses the first 2D bytes of a row
+    constexpr int SWZ = PAD ? 0 : (G < 16 ? G : 16) - 1;
+    constexpr int BUF = TK * RS;               // one tile
+    constexpr int UNITS = TK * RB / 1024;      // units per tile
+    constexpr int NU = UNITS / 4;              // loads per wave per tile
+    constexpr int MS = 8;                      // metadata ring slots
+    constexpr int KBW = 64 / G;                // key blocks (8 keys each) stored per wave
+    constexpr int ROWS_W = 8 * KBW;            // rows a storing wave owns
+    constexpr int ROPE_IT = ROWS_W * kMaxRopePairs / 64;  // rotation items per lane
+    static_assert(UNITS % 4 == 0 && RPU >= 1 && BUF >= 32 * (2 * D + PAD), "tile geometry");
+    static_assert(NU + 1 < 64, "vmcnt range");
     typedef ActLoad<TIn> LD;
 
-    // Raw tile rows land (asynchronously, double-buffered) in raw0/raw1; the
-    // normalised K^ and V^T tiles are single-buffered.  Distinct LDS objects,
-    // so the compiler can tell the asynchronous loads never alias K^ / V^T.
-    __shared__ __attribute__((aligned(16))) uint8_t raw0[RAW_BYTES], raw1[RAW_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t khs[KH_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t vts[VT_BYTES];
-    __shared__ __attribute__((aligned(16))) float cs0[CS_FLOATS], cs1[CS_FLOATS];
-    __shared__ TileMeta meta[4];
+    // Four tile buffers in a ring: at step it, buffer it%4 holds K^ of the
+    // tile being multiplied, (it+1)%4 is normalised in place, (it+2)%4 and
+    // (it+3)%4 are still landing.  Before the tile loop the four buffers
+    // stage the normalised query heads (one 32-head block per wave).
+    __shared__ __attribute__((aligned(16))) uint8_t ring[4][BUF];
+    __shared__ TileMeta meta[MS];
+    __shared__ int32_t idxs[MS][64];  // sparse: entry indices of a tile (lanes >= TK unused)
     __shared__ float2 qcs[kMaxRopePairs];
     __shared__ double turns[kMaxRopePairs];
     __shared__ float gkv_s[D];
+    __shared__ uint32_t dummy[64];    // write target of inactive rotation items
     __shared__ uint32_t redo;
 
     const int tid = threadIdx.x;
@@ -248,14 +291,19 @@ void mqa_fwd_kernel(const AttnArgs a) {
     const int tps = (n_tiles + a.n_splits - 1) / a.n_splits;
     const int tile0 = split * tps;
     const int tile1 = min(n_tiles, tile0 + tps);
+    // a row of this query that always exists: the source of loads for empty slots
+    const uint8_t* spare_row = reinterpret_cast<const uint8_t*>(a.q) + bq * (int64_t)H * RB;
 
     // wave 0: source rows, positions and validity of tile `tile` -> meta[slot]
-    auto tile_meta = [&](int tile, int slot) __attribute__((always_inline)) {
+    auto tile_meta = [&](int tile, int slot, int32_t j) __attribute__((always_inline)) {
         if (wave != 0) return;
         const int ol = opaque_tid() & 63;
         int32_t pos = 0;
         const TIn* row = nullptr;
-        if (ol < TK && tile < tile1) row = slot_row<SPARSE, TIn>(a, g, bq, tile * TK + ol, D, &pos);
+        if (ol < TK && tile < tile1) {
+            const int sl = tile * TK + ol;
+            row = slot_row<TIn>(a, g, sl, SPARSE ? j : sl, D, &pos);
+        }
         if (ol < TK) {
             meta[slot].rowp[ol] = reinterpret_cast<uint64_t>(row);
             meta[slot].pos[ol] = pos;
@@ -263,29 +311,35 @@ void mqa_fwd_kernel(const AttnArgs a) {
         const uint64_t bal = __ballot(row != nullptr);
         if (ol == 0) meta[slot].mask = (uint32_t)bal;
     };
-    // all threads: rotary (cos, sin) of the tile rows -> cst
-    auto tile_cs = [&](int mslot, float* cst) __attribute__((always_inline)) {
-        const int ot = opaque_tid();
-        const int rho = ot >> 3, pg = ot & 7;
-        const int32_t pos = meta[mslot].pos[rho];
-        for (int i = pg; i < n_pairs; i += 8) {
-            float sn, cs;
-            sincos_turns((double)pos * turns[i], &sn, &cs);
-            cst[2 * (rho * kMaxRopePairs + i)] = cs;
-            cst[2 * (rho * kMaxRopePairs + i) + 1] = sn;
-        }
+    // wave 0, sparse: asynchronous copy of the entry indices of `tile` into
+    // idxs[slot] (lanes past the selection copy a harmless word)
+    auto idx_load = [&](int tile, int slot) __attribute__((always_inline)) {
+        const int ol = opaque_tid() & 63;
+        const int sl = tile * TK + ol;
+        const int32_t* src = (ol < TK && sl < g.n_c) ? a.idx + bq * a.K + sl : a.q_pos + bq;
+        lds_dma4(src, (uint32_t)(uintptr_t)&idxs[slot][0]);
     };
-    // asynchronous HBM -> LDS copy of the tile's rows (global_load_lds_dwordx4):
-    // one contiguous 1 KiB unit per wave instruction, rows in tile order.
+    // all waves: asynchronous HBM -> LDS copy of the tile's rows in 1 KiB
+    // units, NU per wave; empty slots copy the spare row so that every wave
+    // always has exactly NU loads per tile in flight
     auto tile_load = [&](int mslot, uint8_t* dst) __attribute__((always_inline)) {
         const int ol = opaque_tid() & 63;
+        uint64_t rp[NU];
 #pragma unroll
-        for (int u = wave; u < UNITS; u += 4) {
-            const int rho = u * RPU + ol / LPR;
-            const int p = ol % LPR;
-            const uint64_t rp = meta[mslot].rowp[rho];
-            const int gsrc = p;
-            if (rp) lds_dma16(reinterpret_cast<const uint8_t*>(rp) + 16 * gsrc, (uint32_t)(uintptr_t)(dst + 1024 * u));
+        for (int k = 0; k < NU; ++k) {
+            rp[k] = meta[mslot].rowp[(wave + 4 * k) * RPU + ol / LPR];
+            if (RPU == 1) {  // one row per unit: the pointer is wave-uniform, keep it in SGPRs
+                // (readfirstlane returns int: widen through uint32_t, never sign-extend)
+                const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(rp[k] >> 32));
+                const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)rp[k]);
+                rp[k] = ((uint64_t)hi << 32) | (uint64_t)lo;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NU; ++k) {
+            const int u = wave + 4 * k;
+            const uint8_t* src = rp[k] ? reinterpret_cast<const uint8_t*>(rp[k]) : spare_row;
+            lds_dma16(src + 16 * (ol % LPR), (uint32_t)(uintptr_t)(dst + (RPU == 1 ? u * RS : 1024 * u)));
         }
     };
 
@@ -298,126 +352,166 @@ void mqa_fwd_kernel(const AttnArgs a) {
         qcs[lane] = make_float2(cs, sn);
     }
     for (int i = tid; i < D; i += 256) gkv_s[i] = a.gamma_kv ? a.gamma_kv[i] : 1.0f;
-    tile_meta(tile0, 0);
-    tile_meta(tile0 + 1, 1);
-    barrier_all();
+    // metadata of the first four tiles and the indices of the fifth
+    auto meta_start = [&]() __attribute__((always_inline)) {
+        if (wave == 0) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int ol = opaque_tid() & 63;
+                const int t = tile0 + k;
+                const int32_t j = (SPARSE && ol < TK && t < tile1) ? slot_entry<SPARSE>(a, g, bq, t * TK + ol) : 0;
+                tile_meta(t, k, j);
+            }
+            if (SPARSE) {
+                const int ol = opaque_tid() & 63;
+                const int t = tile0 + 4;
+                idxs[4][ol] = (ol < TK && t < tile1) ? slot_entry<SPARSE>(a, g, bq, t * TK + ol) : 0;
+            }
+        }
+    };
+    meta_start();
+    barrier_vm<0>();
 
-    // Q^ = RoPE_t(gamma_q * q / rms(q)); wave w stages its 32 heads as f16 in
-    // one of the tile buffers (row = head, granules XOR-swizzled by row)
-    static_assert(RAW_BYTES >= KH_BYTES, "query staging needs four 32-head buffers");
+    // Q^ = RoPE_t(gamma_q * q / rms(q)) * softmax scale * log2(e); wave w
+    // stages its 32 heads as f16 in ring buffer w (row = head, granules
+    // XOR-swizzled by row).  Query rows are read eight heads at a time so
+    // that eight loads are in flight per lane.
     const bool has_heads = 32 * wave < H;
-    uint8_t* qstage = wave == 0 ? khs : wave == 1 ? vts : wave == 2 ? raw0 : raw1;
-    for (int hh = 0; hh < 32; ++hh) {
-        const int head = 32 * wave + hh;  // heads >= H are staged as zeros
-        const TIn* qrow = reinterpret_cast<const TIn*>(a.q) + (bq * H + (head < H ? head : 0)) * (int64_t)D;
-        float v[8];
-        if (lane < G && head < H) LD::to_f32(LD::load(qrow + 8 * lane), v);
-        else
+    {
+        uint8_t* qstage = ring[wave];
+        constexpr int QB = 8;
+        for (int h0 = 0; h0 < 32; h0 += QB) {
+            typename LD::raw_t qr[QB];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-        float ss = 0.0f;
+            for (int u = 0; u < QB; ++u) {
+                const int head = 32 * wave + h0 + u;  // heads >= H are staged as zeros
+                const TIn* qrow = reinterpret_cast<const TIn*>(a.q) + (bq * H + (head < H ? head : 0)) * (int64_t)D;
+                qr[u] = (lane < G && head < H) ? LD::load(qrow + 8 * lane) : LD::zero();
+            }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
-        ss = wave_sum(ss);
-        const float inv = __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps);
-        if (lane < G) {
+            for (int u = 0; u < QB; ++u) {
+                const int hh = h0 + u;
+                float v[8];
+                LD::to_f32(qr[u], v);
+                float ss = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] *= inv * (a.gamma_q ? a.gamma_q[8 * lane + i] : 1.0f);
-            if (8 * lane >= rope_lo) {
+                for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
+                ss = wave_sum_uniform(ss);
+                const float inv = __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps) * a.scale_log2;
+                if (lane < G) {
 #pragma unroll
-                for (int i = 0; i < 8; i += 2) {
-                    const float2 c = qcs[(8 * lane + i - rope_lo) >> 1];
-                    const float x0 = v[i], x1 = v[i + 1];
-                    v[i] = x0 * c.x - x1 * c.y;
-                    v[i + 1] = x0 * c.y + x1 * c.x;
+                    for (int i = 0; i < 8; ++i) v[i] *= inv * (a.gamma_q ? a.gamma_q[8 * lane + i] : 1.0f);
+                    if (8 * lane >= rope_lo) {
+#pragma unroll
+                        for (int i = 0; i < 8; i += 2) {
+                            const float2 c = qcs[(8 * lane + i - rope_lo) >> 1];
+                            const float x0 = v[i], x1 = v[i + 1];
+                            v[i] = x0 * c.x - x1 * c.y;
+                            v[i + 1] = x0 * c.y + x1 * c.x;
+                        }
+                    }
+                    u32x4 w4 = {pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]),
+                                pack_f16x2(v[6], v[7])};
+                    *reinterpret_cast<u32x4*>(qstage + hh * RS + ((lane ^ (hh & SWZ)) << 4)) = w4;
                 }
             }
-            u32x4 w4 = {pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]),
-                        pack_f16x2(v[6], v[7])};
-            *reinterpret_cast<u32x4*>(qstage + hh * (2 * D) + ((lane ^ (hh & SWZ)) << 4)) = w4;
         }
     }
     barrier_lds();
     f16x8 qf[KSTEPS];
     {
-        const uint8_t* qrow = qstage + lrow * (2 * D);
+        const uint8_t* qrow = ring[wave] + lrow * RS;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s)
             qf[s] = *reinterpret_cast<const f16x8*>(qrow + (((2 * s + lh) ^ (lrow & SWZ)) << 4));
     }
 
     // ---------------------------------------------------------------- tile store
-    const int kb = tid / G;  // key block (8 slots)
-    const int db = tid % G;  // 8-channel granule
+    // Normalise the landed rows of a tile in place into f16 K^ (row = key
+    // slot, granules XOR-swizzled by row), then rotate their last r dims.
+    // Thread (kb, db) owns channels 8db..8db+7 of keys 8kb..8kb+7; the eight
+    // sums of squares are reduced together (DPP row sums; with 64 lanes per
+    // key, a wave-uniform total from the four row sums).  Every lane reads
+    // its raw granules of a row before any lane of the wave writes that row.
     const bool ld_on = tid < 4 * G;
-    // normalise, rotate and convert the landed tile rows in place (bf16) or
-    // from the raw buffer (f32); write K^ and V^T
-    auto store_tile = [&](int mslot, uint8_t* kh, uint8_t* vt, const uint8_t* rawb, const float* cst) __attribute__((always_inline)) {
+    auto store_tile = [&](int mslot, uint8_t* buf) __attribute__((always_inline)) {
         if (!ld_on) return;
         const int ot = opaque_tid();
         const int kb = ot / G, db = ot % G;
-        const bool rot = 8 * db >= rope_lo;
-        uint32_t hk[8][4];
+        const uint32_t mask = meta[mslot].mask;
+        float gk[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int rho = loader_row(kb, e);
-            const bool valid = meta[mslot].rowp[rho] != 0ull;
-            uint8_t* kslot = kh + rho * (2 * D) + ((db ^ (rho & SWZ)) << 4);
-            float v[8];
-            if (valid) {
+        for (int i = 0; i < 8; ++i) gk[i] = gkv_s[8 * db + i];
+#pragma unroll
+        for (int e0 = 0; e0 < 8; e0 += 4) {  // four keys at a time: bounded register use
+            uint32_t rw[4][RAW_F32 ? 8 : 4];
+            float ss[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rho = 8 * kb + e0 + e;
+                const bool valid = (mask >> rho) & 1u;
+                float acc2 = 0.0f;
                 if (RAW_F32) {
-                    const f32x4 x0 = *reinterpret_cast<const f32x4*>(rawb + rho * (4 * D) + 32 * db);
-                    const f32x4 x1 = *reinterpret_cast<const f32x4*>(rawb + rho * (4 * D) + 32 * db + 16);
+                    const u32x4 x0 = *reinterpret_cast<const u32x4*>(buf + rho * RS + 32 * db);
+                    const u32x4 x1 = *reinterpret_cast<const u32x4*>(buf + rho * RS + 32 * db + 16);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        v[i] = x0[i];
-                        v[4 + i] = x1[i];
+                        rw[e][i] = valid ? x0[i] : 0u;
+                        rw[e][4 + i] = valid ? x1[i] : 0u;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float f = __builtin_bit_cast(float, rw[e][i]);
+                        acc2 = __builtin_fmaf(f, f, acc2);
                     }
                 } else {
-                    const u32x4 r = *reinterpret_cast<const u32x4*>(rawb + rho * (2 * D) + 16 * db);
+                    const u32x4 r = *reinterpret_cast<const u32x4*>(buf + rho * RS + 16 * db);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        v[2 * i] = bf16_bits_to_f32(r[i] & 0xffffu);
-                        v[2 * i + 1] = bf16_bits_to_f32(r[i] >> 16);
+                        rw[e][i] = valid ? r[i] : 0u;
+                        const bf16x2_t pr = __builtin_bit_cast(bf16x2_t, rw[e][i]);
+                        acc2 = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, acc2, false);
                     }
                 }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+                ss[e] = acc2;
             }
-            float ss = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
-            ss = group_sum<G>(ss);
-            const float inv = valid ? __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps) : 0.0f;
+            for (int e = 0; e < 4; ++e) ss[e] = G == 64 ? wave_sum_uniform(ss[e]) : row16_sum(ss[e]);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] *= inv * gkv_s[8 * db + i];
-            if (rot) {
+            for (int e = 0; e < 4; ++e) {
+                const int rho = 8 * kb + e0 + e;
+                const bool valid = (mask >> rho) & 1u;
+                const float inv = valid ? __builtin_amdgcn_rsqf(ss[e] / (float)D + a.rms_eps) : 0.0f;
+                float v[8];
 #pragma unroll
-                for (int i = 0; i < 8; i += 2) {
-                    const int pi = (8 * db + i - rope_lo) >> 1;
-                    const float c = cst[2 * (rho * kMaxRopePairs + pi)], sn = cst[2 * (rho * kMaxRopePairs + pi) + 1];
-                    const float x0 = v[i], x1 = v[i + 1];
-                    v[i] = x0 * c - x1 * sn;
-                    v[i + 1] = x0 * sn + x1 * c;
+                for (int i = 0; i < 8; ++i) {
+                    float xi;
+                    if (RAW_F32) xi = __builtin_bit_cast(float, rw[e][i]);
+                    else xi = __builtin_bit_cast(float, (i & 1) ? (rw[e][i >> 1] & 0xffff0000u) : (rw[e][i >> 1] << 16));
+                    v[i] = xi * (inv * gk[i]);
                 }
+                *reinterpret_cast<u32x4*>(buf + rho * RS + ((db ^ (rho & SWZ)) << 4)) =
+                    u32x4{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7])};
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) hk[e][i] = pack_f16x2(v[2 * i], v[2 * i + 1]);
-            *reinterpret_cast<u32x4*>(kslot) = u32x4{hk[e][0], hk[e][1], hk[e][2], hk[e][3]};
-            __builtin_amdgcn_sched_barrier(0);  // one key at a time: bounded register use
         }
-        // V^T: channel 8*db+i, virtual slots [8*kb, 8*kb+8) = keys e = 0..7
+        // rotation of this wave's rows: item = pair * ROWS_W + row, ROPE_IT per
+        // lane, branch-free (items past the rotated pairs touch `dummy`)
+        const int ol = ot & 63;
+        const int row0 = 8 * KBW * (ot >> 6);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int half = i & 1, wd = i >> 1;
-            uint32_t o[4];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const uint32_t x = hk[2 * p][wd], y = hk[2 * p + 1][wd];
-                o[p] = half ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-            }
-            *reinterpret_cast<u32x4*>(vt + vt_offset(8 * db + i, kb)) = u32x4{o[0], o[1], o[2], o[3]};
+        for (int k = 0; k < ROPE_IT; ++k) {
+            const int item = ol + 64 * k;
+            const int rr = row0 + item % ROWS_W;
+            const int pr = item / ROWS_W;
+            const bool on = pr < n_pairs;
+            const int dim = rope_lo + 2 * pr;
+            const int off = rr * RS + (((dim >> 3) ^ (rr & SWZ)) << 4) + 2 * (dim & 7);
+            uint32_t* pw = on ? reinterpret_cast<uint32_t*>(buf + off) : &dummy[ol];
+            float sn, cs;
+            sincos_turns_fast((double)meta[mslot].pos[rr] * turns[on ? pr : 0], &sn, &cs);
+            const f16x2_t hv = __builtin_bit_cast(f16x2_t, *pw);
+            const float x0 = (float)hv[0], x1 = (float)hv[1];
+            *pw = pack_f16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
         }
     };
 
@@ -434,41 +528,40 @@ void mqa_fwd_kernel(const AttnArgs a) {
     bool flagged = false;  // wave-uniform
     bool active = has_heads;
 
-    // QK, softmax and PV on a stored tile
-    auto compute_tile = [&](int mslot, const uint8_t* kh, const uint8_t* vt) __attribute__((always_inline)) {
+    // QK, softmax and PV on a stored tile.  S^T = K^ Q^_w^T (keys as rows);
+    // its accumulator layout is the A-operand layout of P for O = P V with
+    // the tile's keys in the order (4 lh + j, then 8 + 4 lh + j): the V
+    // operand is read in that order straight from the row-major K^ with
+    // ds_read_b64_tr_b16 (in each 16-lane group, lane i receives element
+    // i % 4 of the 8-byte chunks addressed by lanes 4k + i / 4, k = 0..3).
+    auto compute_tile = [&](int mslot, const uint8_t* kh) __attribute__((always_inline)) {
         if (!active) return;
-        const uint32_t mask = meta[mslot].mask;
-        // per-lane swizzled LDS offsets of the MFMA operand reads, recomputed
-        // per tile (a few VALU ops) instead of being held in VGPRs:
-        //   K^ row lrow, granule g = 2s + lh  -> koff[s % 8] + 256 * (s / 8)
-        //   V^T row 32*dt + lrow, granule g   -> vrow_off + voff[g ^ (dt % 4)] + 2048 * dt
+        const uint32_t mask = __builtin_amdgcn_readfirstlane(meta[mslot].mask);
         const int ol = opaque_tid() & 63;
         const int orow = ol & 31, oh = ol >> 5;
-        uint32_t koff[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) koff[s] = ((((2 * s + oh) & SWZ) ^ (orow & SWZ)) | ((2 * s + oh) & ~SWZ)) << 4;
-        const int lrp = orow ^ ((orow >> 3) & 3);  // V^T row placement within a 32-row block
-        const uint32_t vrow_off = (uint32_t)lrp * 64;
-        uint32_t voff[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) voff[x] = (uint32_t)((x ^ ((lrp >> 2) & 3)) << 4);
+        // QK A operand: K^ row orow, granule 2s + oh (XOR-swizzled within
+        // each 16-granule block when SWZ != 0)
         f32x16 st;
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[r] = 0.0f;
-        const uint8_t* krow = kh + orow * (2 * D);
+        const uint8_t* krow = kh + orow * RS;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-            const f16x8 av = *reinterpret_cast<const f16x8*>(krow + koff[s & 7] + 256 * (s >> 3));
+            const int gq = (2 * (s & 7) + oh) ^ (orow & SWZ);
+            const f16x8 av = *reinterpret_cast<const f16x8*>(krow + 256 * (s >> 3) + (gq << 4));
             st = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qf[s], st, 0, 0, 0);
         }
-        // softmax numerators for rows 8*(r/4) + 4*lh + r%4 of this tile
+        // softmax numerators for rows 8*(r/4) + 4*lh + r%4 of this tile (the
+        // logits are already in log2 units: Q^ carries the softmax scale)
         float mx = -INFINITY;
-        const uint32_t mrow = mask >> (4 * oh);  // rows 8*(r/4) + 4*oh + r%4
+        if (mask != 0xffffffffu) {
+            const uint32_t mrow = mask >> (4 * oh);  // rows 8*(r/4) + 4*oh + r%4
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            st[r] = ((mrow >> (8 * (r >> 2) + (r & 3))) & 1u) ? st[r] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, st[r]);
+            for (int r = 0; r < 16; ++r)
+                if (!((mrow >> (8 * (r >> 2) + (r & 3))) & 1u)) st[r] = -INFINITY;
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         m_seen = fmaxf(m_seen, mx);
         if (m_use == -INFINITY) m_use = mx;  // nothing accumulated for this head yet
@@ -486,40 +579,58 @@ void mqa_fwd_kernel(const AttnArgs a) {
         }
         psum += __shfl_xor(psum, 32, 64);
         l_run += psum;
-        const f16x8 pa0 = __builtin_bit_cast(f16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-        const f16x8 pa1 = __builtin_bit_cast(f16x8, u32x4{pk[4], pk[5], pk[6], pk[7]});
-        const uint8_t* vrow = vt + vrow_off;
+        const f16x8 pa[2] = {__builtin_bit_cast(f16x8, u32x4{pk[0], pk[1], pk[2], pk[3]}),
+                             __builtin_bit_cast(f16x8, u32x4{pk[4], pk[5], pk[6], pk[7]})};
+        // V operand: lane (group q = ol/16, i = ol%16) addresses row
+        // 16 ks + 8 hf + 4 (q/2) + i/4, dims 32 dt + 16 (q%2) + 4 (i%4) .. +3
+        const int q = ol >> 4, i16 = ol & 15;
+        uint32_t vbase[2][4];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int rr = 8 * hf + 4 * (q >> 1) + (i16 >> 2);  // row within a 16-key step
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int gr = 4 * d + 2 * (q & 1) + ((i16 & 3) >> 1);  // granule within a 64-dim block
+                vbase[hf][d] = (uint32_t)(rr * RS + ((gr ^ (rr & SWZ)) << 4) + 8 * (i16 & 1));
+            }
+        }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const f16x8 b0 = *reinterpret_cast<const f16x8*>(vrow + voff[oh ^ (dt & 3)] + 2048 * dt);
-            const f16x8 b1 = *reinterpret_cast<const f16x8*>(vrow + voff[(2 + oh) ^ (dt & 3)] + 2048 * dt);
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa0, b0, acc[dt], 0, 0, 0);
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa1, b1, acc[dt], 0, 0, 0);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                uint8_t* vb = const_cast<uint8_t*>(kh) + ks * 16 * RS + 256 * (dt >> 2);
+                const h4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)(vb + vbase[0][dt & 3]));
+                const h4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)(vb + vbase[1][dt & 3]));
+                const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+                const f16x8 bv = __builtin_bit_cast(f16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[ks], bv, acc[dt], 0, 0, 0);
+            }
         }
     };
 
-    // one pipeline step on raw buffer B: store tile `tile` from raw B into
-    // K^ / V^T, start loading tile+1 into the other raw buffer, then compute
-    auto step = [&](auto bsel, int tile, int it) __attribute__((always_inline)) {
-        constexpr int B = decltype(bsel)::value;
-        uint8_t* rawc = B == 0 ? raw0 : raw1;
-        uint8_t* rawn = B == 0 ? raw1 : raw0;
-        float* csc = B == 0 ? cs0 : cs1;
-        float* csn = B == 0 ? cs1 : cs0;
-        asm volatile("; tile step on buffer set %0" ::"n"(B));  // keeps the two bodies distinct
-        store_tile(it & 3, khs, vts, rawc, csc);
-        tile_meta(tile + 2, (it + 2) & 3);  // (its index loads complete before the tile loads start)
-        if (tile + 1 < tile1) {
-            tile_load((it + 1) & 3, rawn);
-            tile_cs((it + 1) & 3, csn);
+    // One pipeline step (tile T = tile0 + it):
+    //   wave 0 builds the metadata of T+4 from its indices (landed) and
+    //   starts copying the indices of T+5; all waves start copying the rows
+    //   of T+3; T+1 is normalised in place while T is multiplied (different
+    //   buffers, no barrier between them); the closing barrier waits until
+    //   only T+3's rows are in flight.
+    auto step = [&](int it) __attribute__((always_inline)) {
+        const int T = tile0 + it;
+        if (wave == 0) {
+            const int ol = opaque_tid() & 63;
+            tile_meta(T + 4, (it + 4) & (MS - 1), SPARSE ? idxs[(it + 4) & (MS - 1)][ol] : 0);
+            if (SPARSE && T + 5 < tile1) idx_load(T + 5, (it + 5) & (MS - 1));
         }
-        barrier_lds();
-        asm volatile("; compute on buffer set %0" ::"n"(B));
-        compute_tile(it & 3, khs, vts);
-        barrier_all();
+        const bool more = T + 3 < tile1;
+        if (more) tile_load((it + 3) & (MS - 1), ring[(it + 3) & 3]);
+        if (T + 1 < tile1) store_tile((it + 1) & (MS - 1), ring[(it + 1) & 3]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_tile(it & (MS - 1), ring[it & 3]);
+        if (more) barrier_vm<NU>();
+        else barrier_vm<0>();
     };
 
-    barrier_lds();  // every wave has read its Q^ block: the buffers are free
+    barrier_lds();  // every wave has read its Q^ block: the ring is free
     for (int pass = 0; pass < 2; ++pass) {
         active = has_heads && (pass == 0 || flagged);
         if (pass == 1) {
@@ -528,9 +639,8 @@ void mqa_fwd_kernel(const AttnArgs a) {
                 l_run = 0.0f;
                 flagged = false;
             }
-            tile_meta(tile0, 0);
-            tile_meta(tile0 + 1, 1);
-            barrier_lds();
+            meta_start();
+            barrier_vm<0>();
         }
         if (active) {
 #pragma unroll
@@ -538,15 +648,17 @@ void mqa_fwd_kernel(const AttnArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
         }
-        if (tile0 < tile1) {
-            tile_load(0, raw0);
-            tile_cs(0, cs0);
-        }
-        barrier_all();
-        for (int tile = tile0, it = 0; tile < tile1; tile += 2, it += 2) {
-            step(std::integral_constant<int, 0>(), tile, it);
-            if (tile + 1 < tile1) step(std::integral_constant<int, 1>(), tile + 1, it + 1);
-        }
+        // the first three tiles start landing; T0 is normalised once it has
+        if (tile0 < tile1) tile_load(0, ring[0]);
+        if (tile0 + 1 < tile1) tile_load(1, ring[1]);
+        if (tile0 + 2 < tile1) tile_load(2, ring[2]);
+        if (tile0 + 2 < tile1) barrier_vm<2 * NU>();
+        else if (tile0 + 1 < tile1) barrier_vm<NU>();
+        else barrier_vm<0>();
+        if (tile0 < tile1) store_tile(0, ring[0]);
+        if (tile0 + 2 < tile1) barrier_vm<NU>();
+        else barrier_vm<0>();
+        for (int it = 0; tile0 + it < tile1; ++it) step(it);
         // does any wave need the second pass?
         if (tid == 0) redo = 0u;
         barrier_lds();

@@ -34,9 +34,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 
 // two floats -> packed pair of f16 (round to nearest even, v_cvt_pk_f16_f32)
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef short bf16x2_t __attribute__((ext_vector_type(2)));  // two bf16 bit patterns (v_dot2_f32_bf16)
+// two floats -> packed f16 pair (round to nearest even; one v_cvt_pk_f16_f32)
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-    _Float16 x = (_Float16)a, y = (_Float16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    const f16x2_t h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
 }
 
 // ---------------------------------------------------------------- fp8 E4M3 (OCP)
@@ -99,6 +102,33 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
     return v;
+}
+
+// v + (v of the lane that DPP control CTRL selects), all lanes active
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over each row of 16 lanes, returned in every lane of the row: four DPP
+// butterfly steps (lane ^ 1, lane ^ 2, then the 8- and 16-lane mirrors, which
+// pair each lane with one in the other half), no LDS round trip.
+__device__ __forceinline__ float row16_sum(float v) {
+    v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = dpp_add<0x141>(v);  // row_half_mirror
+    v = dpp_add<0x140>(v);  // row_mirror
+    return v;
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over all 64 lanes as a wave-uniform (scalar) value.
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+    v = row16_sum(v);
+    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
 // order-preserving image of an fp32 score: a > b  <=>  key(a) > key(b);
