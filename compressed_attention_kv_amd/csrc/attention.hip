@@ -232,10 +232,39 @@ __device__ __forceinline__ void barrier_vm() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// MFMA operand element of the attention kernel: bf16 for bf16 activations
+// (key rows are used exactly as they landed, unnormalised), f16 for f32
+// activations (rows are normalised first, so their range is bounded and
+// f16's finer significand keeps more of the f32 input).
+template <bool F16>
+struct MmaOp;
+
+template <>
+struct MmaOp<false> {
+    typedef bf16x8 vec;
+    static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_bf16x2(a, b); }
+    static __device__ __forceinline__ float lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+    static __device__ __forceinline__ f32x16 mfma(vec a, vec b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct MmaOp<true> {
+    typedef f16x8 vec;
+    static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_f16x2(a, b); }
+    static __device__ __forceinline__ float lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[0]; }
+    static __device__ __forceinline__ float hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[1]; }
+    static __device__ __forceinline__ f32x16 mfma(vec a, vec b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
 template <int D, bool SPARSE, typename TIn>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mqa_fwd_kernel(const AttnArgs a) {
-    constexpr int G = D / 8;                   // 16-byte f16 granules per K^ row
+    constexpr int G = D / 8;                   // 16-byte bf16 granules per K row
     constexpr int KSTEPS = D / 16;             // QK k-steps
     constexpr int DT = D / 32;                 // output dim tiles
     constexpr bool RAW_F32 = sizeof(TIn) == 4;
@@ -244,29 +273,27 @@ void mqa_fwd_kernel(const AttnArgs a) {
     constexpr int LPR = 64 / RPU;              // lanes per row in a unit
     // Row stride in LDS.  A 1 KiB row (bf16, D = 512) is one unit and gets 16
     // bytes of padding, so that 16-byte column reads of consecutive rows fall
-    // in distinct banks and every operand address is a base plus an
-    // immediate; smaller rows share a unit, stay packed and use an XOR
-    // swizzle of the 16-byte granules instead.
+    // in distinct banks; smaller rows share a unit and stay packed.
     constexpr int PAD = RPU == 1 ? 16 : 0;
-    constexpr int RS = RB + PAD;               // ring row stride; K^ uses the first 2D bytes of a row
-    constexpr int SWZ = PAD ? 0 : (G < 16 ? G : 16) - 1;
+    constexpr int RS = RB + PAD;               // ring row stride; the bf16 K row is its first 2D bytes
     constexpr int BUF = TK * RS;               // one tile
     constexpr int UNITS = TK * RB / 1024;      // units per tile
     constexpr int NU = UNITS / 4;              // loads per wave per tile
     constexpr int MS = 8;                      // metadata ring slots
-    constexpr int KBW = 64 / G;                // key blocks (8 keys each) stored per wave
-    constexpr int ROWS_W = 8 * KBW;            // rows a storing wave owns
-    constexpr int ROPE_IT = ROWS_W * kMaxRopePairs / 64;  // rotation items per lane
+    constexpr int CH = D / 64;                 // 8-channel chunks per lane in the row-norm pass
     static_assert(UNITS % 4 == 0 && RPU >= 1 && BUF >= 32 * (2 * D + PAD), "tile geometry");
     static_assert(NU + 1 < 64, "vmcnt range");
     typedef ActLoad<TIn> LD;
+    typedef MmaOp<RAW_F32> OP;
+    typedef typename OP::vec opvec;
 
-    // Four tile buffers in a ring: at step it, buffer it%4 holds K^ of the
-    // tile being multiplied, (it+1)%4 is normalised in place, (it+2)%4 and
-    // (it+3)%4 are still landing.  Before the tile loop the four buffers
-    // stage the normalised query heads (one 32-head block per wave).
+    // Four tile buffers in a ring: at step it, buffer it%4 holds the tile
+    // being multiplied, (it+1)%4 gets its row scales and rotation, (it+2)%4
+    // and (it+3)%4 are still landing.  Before the tile loop the four buffers
+    // stage the query heads (one 32-head block per wave).
     __shared__ __attribute__((aligned(16))) uint8_t ring[4][BUF];
     __shared__ TileMeta meta[MS];
+    __shared__ __attribute__((aligned(16))) float invs[MS][TK];  // 1/rms of each row (0: empty slot)
     __shared__ int32_t idxs[MS][64];  // sparse: entry indices of a tile (lanes >= TK unused)
     __shared__ float2 qcs[kMaxRopePairs];
     __shared__ double turns[kMaxRopePairs];
@@ -372,9 +399,10 @@ void mqa_fwd_kernel(const AttnArgs a) {
     meta_start();
     barrier_vm<0>();
 
-    // Q^ = RoPE_t(gamma_q * q / rms(q)) * softmax scale * log2(e); wave w
-    // stages its 32 heads as f16 in ring buffer w (row = head, granules
-    // XOR-swizzled by row).  Query rows are read eight heads at a time so
+    // Q~ = RoPE_t(gamma_q * q / rms(q)) * softmax scale * log2(e), with the
+    // KV gain gamma_kv folded into the unrotated channels (the rotated ones
+    // carry it on the key side); bf16.  Wave w stages its 32 heads in ring
+    // buffer w (row = head).  Query rows are read eight heads at a time so
     // that eight loads are in flight per lane.
     const bool has_heads = 32 * wave < H;
     {
@@ -409,129 +437,121 @@ void mqa_fwd_kernel(const AttnArgs a) {
                             v[i] = x0 * c.x - x1 * c.y;
                             v[i + 1] = x0 * c.y + x1 * c.x;
                         }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) v[i] *= gkv_s[8 * lane + i];
                     }
-                    u32x4 w4 = {pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]),
-                                pack_f16x2(v[6], v[7])};
-                    *reinterpret_cast<u32x4*>(qstage + hh * RS + ((lane ^ (hh & SWZ)) << 4)) = w4;
+                    u32x4 w4 = {OP::pack(v[0], v[1]), OP::pack(v[2], v[3]), OP::pack(v[4], v[5]), OP::pack(v[6], v[7])};
+                    *reinterpret_cast<u32x4*>(qstage + hh * RS + 16 * lane) = w4;
                 }
             }
         }
     }
     barrier_lds();
-    f16x8 qf[KSTEPS];
+    opvec qf[KSTEPS];
     {
         const uint8_t* qrow = ring[wave] + lrow * RS;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-            qf[s] = *reinterpret_cast<const f16x8*>(qrow + (((2 * s + lh) ^ (lrow & SWZ)) << 4));
+        for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const opvec*>(qrow + 16 * (2 * s + lh));
     }
 
-    // ---------------------------------------------------------------- tile store
-    // Normalise the landed rows of a tile in place into f16 K^ (row = key
-    // slot, granules XOR-swizzled by row), then rotate their last r dims.
-    // Thread (kb, db) owns channels 8db..8db+7 of keys 8kb..8kb+7; the eight
-    // sums of squares are reduced together (DPP row sums; with 64 lanes per
-    // key, a wave-uniform total from the four row sums).  Every lane reads
-    // its raw granules of a row before any lane of the wave writes that row.
-    const bool ld_on = tid < 4 * G;
-    auto store_tile = [&](int mslot, uint8_t* buf) __attribute__((always_inline)) {
-        if (!ld_on) return;
+    // ---------------------------------------------------------------- tile prep
+    // K = V = RoPE(gamma_kv * v / rms(v)) is never materialised: the bf16
+    // rows stay as they landed and multiply Q~ directly; 1/rms(v) of each row
+    // (0 for an empty slot) scales its logit and its softmax weight, and
+    // gamma_kv of the unrotated channels sits in Q~ and in the combine step.
+    // Only the last r channels are rewritten, in place, as RoPE(gamma_kv * v)
+    // in bf16.  (f32 rows are first normalised and rounded to f16 in place,
+    // with a row scale of 1; their operands are f16 throughout.)  Lane (row = 8 w + l/8, j = l%8) owns the
+    // 8-channel chunks j, j+8, ...; the eight lanes of a row reduce their sums
+    // of squares with three DPP steps.
+    auto prep_tile = [&](int mslot, uint8_t* buf) __attribute__((always_inline)) {
         const int ot = opaque_tid();
-        const int kb = ot / G, db = ot % G;
-        const uint32_t mask = meta[mslot].mask;
-        float gk[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) gk[i] = gkv_s[8 * db + i];
-#pragma unroll
-        for (int e0 = 0; e0 < 8; e0 += 4) {  // four keys at a time: bounded register use
-            uint32_t rw[4][RAW_F32 ? 8 : 4];
-            float ss[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rho = 8 * kb + e0 + e;
-                const bool valid = (mask >> rho) & 1u;
-                float acc2 = 0.0f;
-                if (RAW_F32) {
-                    const u32x4 x0 = *reinterpret_cast<const u32x4*>(buf + rho * RS + 32 * db);
-                    const u32x4 x1 = *reinterpret_cast<const u32x4*>(buf + rho * RS + 32 * db + 16);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        rw[e][i] = valid ? x0[i] : 0u;
-                        rw[e][4 + i] = valid ? x1[i] : 0u;
-                    }
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float f = __builtin_bit_cast(float, rw[e][i]);
-                        acc2 = __builtin_fmaf(f, f, acc2);
-                    }
-                } else {
-                    const u32x4 r = *reinterpret_cast<const u32x4*>(buf + rho * RS + 16 * db);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        rw[e][i] = valid ? r[i] : 0u;
-                        const bf16x2_t pr = __builtin_bit_cast(bf16x2_t, rw[e][i]);
-                        acc2 = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, acc2, false);
-                    }
-                }
-                ss[e] = acc2;
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ss[e] = G == 64 ? wave_sum_uniform(ss[e]) : row16_sum(ss[e]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rho = 8 * kb + e0 + e;
-                const bool valid = (mask >> rho) & 1u;
-                const float inv = valid ? __builtin_amdgcn_rsqf(ss[e] / (float)D + a.rms_eps) : 0.0f;
-                float v[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    float xi;
-                    if (RAW_F32) xi = __builtin_bit_cast(float, rw[e][i]);
-                    else xi = __builtin_bit_cast(float, (i & 1) ? (rw[e][i >> 1] & 0xffff0000u) : (rw[e][i >> 1] << 16));
-                    v[i] = xi * (inv * gk[i]);
-                }
-                *reinterpret_cast<u32x4*>(buf + rho * RS + ((db ^ (rho & SWZ)) << 4)) =
-                    u32x4{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7])};
-            }
-        }
-        // rotation of this wave's rows: item = pair * ROWS_W + row, ROPE_IT per
-        // lane, branch-free (items past the rotated pairs touch `dummy`)
         const int ol = ot & 63;
-        const int row0 = 8 * KBW * (ot >> 6);
+        const int row = 8 * (ot >> 6) + (ol >> 3);
+        const int jj = ol & 7;
+        const bool valid = (meta[mslot].mask >> row) & 1u;
+        float ss = 0.0f;
+        uint8_t* rb = buf + row * RS;
+        if (RAW_F32) {
+            float xs[CH][8];
 #pragma unroll
-        for (int k = 0; k < ROPE_IT; ++k) {
+            for (int k = 0; k < CH; ++k) {
+                const int c = jj + 8 * k;
+                const f32x4 x0 = *reinterpret_cast<const f32x4*>(rb + 32 * c);
+                const f32x4 x1 = *reinterpret_cast<const f32x4*>(rb + 32 * c + 16);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    xs[k][i] = x0[i];
+                    xs[k][4 + i] = x1[i];
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(xs[k][i], xs[k][i], ss);
+            }
+            ss = row8_sum(ss);
+            const float inv = valid ? __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps) : 0.0f;
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                const int c = jj + 8 * k;
+                *reinterpret_cast<u32x4*>(rb + 16 * c) =
+                    u32x4{OP::pack(xs[k][0] * inv, xs[k][1] * inv), OP::pack(xs[k][2] * inv, xs[k][3] * inv),
+                          OP::pack(xs[k][4] * inv, xs[k][5] * inv), OP::pack(xs[k][6] * inv, xs[k][7] * inv)};
+            }
+            if (jj == 0) invs[mslot][row] = 1.0f;
+        } else {
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                const u32x4 r = *reinterpret_cast<const u32x4*>(rb + 16 * (jj + 8 * k));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bf16x2_t pr = word_as_bf16x2(r[i]);
+                    ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
+                }
+            }
+            ss = row8_sum(ss);
+            const float inv = valid ? __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps) : 0.0f;
+            if (jj == 0) invs[mslot][row] = inv;
+        }
+        // rotation of this wave's 8 rows: item = pair * 8 + row, 4 per lane,
+        // branch-free (items past the rotated pairs touch `dummy`).  Every
+        // lane of the wave has read its chunks above before any of these
+        // writes (LDS operations of one wave complete in order).
+        const int row0 = 8 * (ot >> 6);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
             const int item = ol + 64 * k;
-            const int rr = row0 + item % ROWS_W;
-            const int pr = item / ROWS_W;
+            const int rr = row0 + (item & 7);
+            const int pr = item >> 3;
             const bool on = pr < n_pairs;
             const int dim = rope_lo + 2 * pr;
-            const int off = rr * RS + (((dim >> 3) ^ (rr & SWZ)) << 4) + 2 * (dim & 7);
-            uint32_t* pw = on ? reinterpret_cast<uint32_t*>(buf + off) : &dummy[ol];
+            uint32_t* pw = on ? reinterpret_cast<uint32_t*>(buf + rr * RS + 2 * dim) : &dummy[ol];
             float sn, cs;
             sincos_turns_fast((double)meta[mslot].pos[rr] * turns[on ? pr : 0], &sn, &cs);
-            const f16x2_t hv = __builtin_bit_cast(f16x2_t, *pw);
-            const float x0 = (float)hv[0], x1 = (float)hv[1];
-            *pw = pack_f16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+            const uint32_t hv = *pw;
+            const float x0 = OP::lo(hv) * gkv_s[on ? dim : 0];
+            const float x1 = OP::hi(hv) * gkv_s[on ? dim + 1 : 0];
+            *pw = OP::pack(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
         }
     };
 
     // ---------------------------------------------------------------- state
     // The accumulator is only ever written by MFMAs (and zero-filled), never
     // by VALU, so it can live in AGPRs.  Softmax reference max m_use is fixed
-    // per head at the first finite tile max; P = 2^(l - m_use) stays inside
-    // f16's range while l <= m_use + 15.  If a later logit exceeds that, the
-    // wave flags itself, keeps tracking the true max m_seen, and the tile
-    // loop runs a second pass for the flagged waves with m_use = m_seen
-    // (then P <= 1).  Typical inputs never take the second pass.
+    // per head at the first finite tile max; P = 2^(l - m_use) <= 2^15 while
+    // l <= m_use + 15.  If a later logit exceeds that, the wave flags itself,
+    // keeps tracking the true max m_seen, and the tile loop runs a second
+    // pass for the flagged waves with m_use = m_seen (then P <= 1).  Typical
+    // inputs never take the second pass.
     f32x16 acc[DT];
     float m_use = -INFINITY, m_seen = -INFINITY, l_run = 0.0f;
     bool flagged = false;  // wave-uniform
     bool active = has_heads;
 
-    // QK, softmax and PV on a stored tile.  S^T = K^ Q^_w^T (keys as rows);
-    // its accumulator layout is the A-operand layout of P for O = P V with
-    // the tile's keys in the order (4 lh + j, then 8 + 4 lh + j): the V
-    // operand is read in that order straight from the row-major K^ with
+    // QK, softmax and PV on a prepared tile.  S^T = K Q~_w^T (keys as rows),
+    // each row then scaled by its 1/rms; the accumulator layout is the
+    // A-operand layout of P for O = P V with the tile's keys in the order
+    // (4 lh + j, then 8 + 4 lh + j), P carrying each key's 1/rms: the V
+    // operand is read in that order straight from the row-major tile with
     // ds_read_b64_tr_b16 (in each 16-lane group, lane i receives element
     // i % 4 of the 8-byte chunks addressed by lanes 4k + i / 4, k = 0..3).
     auto compute_tile = [&](int mslot, const uint8_t* kh) __attribute__((always_inline)) {
@@ -539,20 +559,22 @@ void mqa_fwd_kernel(const AttnArgs a) {
         const uint32_t mask = __builtin_amdgcn_readfirstlane(meta[mslot].mask);
         const int ol = opaque_tid() & 63;
         const int orow = ol & 31, oh = ol >> 5;
-        // QK A operand: K^ row orow, granule 2s + oh (XOR-swizzled within
-        // each 16-granule block when SWZ != 0)
         f32x16 st;
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[r] = 0.0f;
-        const uint8_t* krow = kh + orow * RS;
+        const uint8_t* krow = kh + orow * RS + 16 * oh;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-            const int gq = (2 * (s & 7) + oh) ^ (orow & SWZ);
-            const f16x8 av = *reinterpret_cast<const f16x8*>(krow + 256 * (s >> 3) + (gq << 4));
-            st = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qf[s], st, 0, 0, 0);
+            const opvec av = *reinterpret_cast<const opvec*>(krow + 32 * s);
+            st = OP::mfma(av, qf[s], st);
         }
-        // softmax numerators for rows 8*(r/4) + 4*lh + r%4 of this tile (the
-        // logits are already in log2 units: Q^ carries the softmax scale)
+        // row scales of this lane's rows 8*(r/4) + 4*lh + r%4
+        f32x4 iv[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) iv[m] = *reinterpret_cast<const f32x4*>(&invs[mslot][8 * m + 4 * oh]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[r] *= iv[r >> 2][r & 3];
+        // logits are in log2 units (Q~ carries the softmax scale)
         float mx = -INFINITY;
         if (mask != 0xffffffffu) {
             const uint32_t mrow = mask >> (4 * oh);  // rows 8*(r/4) + 4*oh + r%4
@@ -575,35 +597,29 @@ void mqa_fwd_kernel(const AttnArgs a) {
             const float p0 = live ? __builtin_amdgcn_exp2f(st[r] - m_use) : 0.0f;
             const float p1 = live ? __builtin_amdgcn_exp2f(st[r + 1] - m_use) : 0.0f;
             psum += p0 + p1;
-            pk[r >> 1] = pack_f16x2(p0, p1);
+            pk[r >> 1] = OP::pack(p0 * iv[r >> 2][r & 3], p1 * iv[r >> 2][(r & 3) + 1]);
         }
         psum += __shfl_xor(psum, 32, 64);
         l_run += psum;
-        const f16x8 pa[2] = {__builtin_bit_cast(f16x8, u32x4{pk[0], pk[1], pk[2], pk[3]}),
-                             __builtin_bit_cast(f16x8, u32x4{pk[4], pk[5], pk[6], pk[7]})};
+        const opvec pa[2] = {__builtin_bit_cast(opvec, u32x4{pk[0], pk[1], pk[2], pk[3]}),
+                             __builtin_bit_cast(opvec, u32x4{pk[4], pk[5], pk[6], pk[7]})};
         // V operand: lane (group q = ol/16, i = ol%16) addresses row
         // 16 ks + 8 hf + 4 (q/2) + i/4, dims 32 dt + 16 (q%2) + 4 (i%4) .. +3
         const int q = ol >> 4, i16 = ol & 15;
-        uint32_t vbase[2][4];
+        const uint8_t* vrow[2];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const int rr = 8 * hf + 4 * (q >> 1) + (i16 >> 2);  // row within a 16-key step
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const int gr = 4 * d + 2 * (q & 1) + ((i16 & 3) >> 1);  // granule within a 64-dim block
-                vbase[hf][d] = (uint32_t)(rr * RS + ((gr ^ (rr & SWZ)) << 4) + 8 * (i16 & 1));
-            }
-        }
+        for (int hf = 0; hf < 2; ++hf)
+            vrow[hf] = kh + (8 * hf + 4 * (q >> 1) + (i16 >> 2)) * RS + 32 * (q & 1) + 8 * (i16 & 3);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                uint8_t* vb = const_cast<uint8_t*>(kh) + ks * 16 * RS + 256 * (dt >> 2);
-                const h4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)(vb + vbase[0][dt & 3]));
-                const h4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)(vb + vbase[1][dt & 3]));
+                const int off = ks * 16 * RS + 64 * dt;
+                const h4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)const_cast<uint8_t*>(vrow[0] + off));
+                const h4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)const_cast<uint8_t*>(vrow[1] + off));
                 const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
-                const f16x8 bv = __builtin_bit_cast(f16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[ks], bv, acc[dt], 0, 0, 0);
+                const opvec bv = __builtin_bit_cast(opvec, u32x4{w0[0], w0[1], w1[0], w1[1]});
+                acc[dt] = OP::mfma(pa[ks], bv, acc[dt]);
             }
         }
     };
@@ -611,9 +627,9 @@ void mqa_fwd_kernel(const AttnArgs a) {
     // One pipeline step (tile T = tile0 + it):
     //   wave 0 builds the metadata of T+4 from its indices (landed) and
     //   starts copying the indices of T+5; all waves start copying the rows
-    //   of T+3; T+1 is normalised in place while T is multiplied (different
-    //   buffers, no barrier between them); the closing barrier waits until
-    //   only T+3's rows are in flight.
+    //   of T+3; T+1 gets its row scales and rotation while T is multiplied
+    //   (different buffers, no barrier between them); the closing barrier
+    //   waits until only T+3's rows are in flight.
     auto step = [&](int it) __attribute__((always_inline)) {
         const int T = tile0 + it;
         if (wave == 0) {
@@ -623,14 +639,17 @@ void mqa_fwd_kernel(const AttnArgs a) {
         }
         const bool more = T + 3 < tile1;
         if (more) tile_load((it + 3) & (MS - 1), ring[(it + 3) & 3]);
-        if (T + 1 < tile1) store_tile((it + 1) & (MS - 1), ring[(it + 1) & 3]);
+        asm volatile("; prep phase" ::);
+        if (T + 1 < tile1) prep_tile((it + 1) & (MS - 1), ring[(it + 1) & 3]);
         __builtin_amdgcn_sched_barrier(0);
+        asm volatile("; compute phase" ::);
         compute_tile(it & (MS - 1), ring[it & 3]);
+        asm volatile("; end of step" ::);
         if (more) barrier_vm<NU>();
         else barrier_vm<0>();
     };
 
-    barrier_lds();  // every wave has read its Q^ block: the ring is free
+    barrier_lds();  // every wave has read its Q~ block: the ring is free
     for (int pass = 0; pass < 2; ++pass) {
         active = has_heads && (pass == 0 || flagged);
         if (pass == 1) {
@@ -648,14 +667,14 @@ void mqa_fwd_kernel(const AttnArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
         }
-        // the first three tiles start landing; T0 is normalised once it has
+        // the first three tiles start landing; T0 is prepared once it has
         if (tile0 < tile1) tile_load(0, ring[0]);
         if (tile0 + 1 < tile1) tile_load(1, ring[1]);
         if (tile0 + 2 < tile1) tile_load(2, ring[2]);
         if (tile0 + 2 < tile1) barrier_vm<2 * NU>();
         else if (tile0 + 1 < tile1) barrier_vm<NU>();
         else barrier_vm<0>();
-        if (tile0 < tile1) store_tile(0, ring[0]);
+        if (tile0 < tile1) prep_tile(0, ring[0]);
         if (tile0 + 2 < tile1) barrier_vm<NU>();
         else barrier_vm<0>();
         for (int it = 0; tile0 + it < tile1; ++it) step(it);
@@ -719,6 +738,10 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(const AttnArgs a) {
         o1 /= Z;
     }
     const int rope_lo = D - a.rope_dims;
+    if (2 * pr < rope_lo && a.gamma_kv) {  // the unrotated channels' KV gain (kept out of the key tiles)
+        o0 *= a.gamma_kv[2 * pr];
+        o1 *= a.gamma_kv[2 * pr + 1];
+    }
     if (2 * pr >= rope_lo) {
         int32_t t = a.q_pos[bq];
         t = t < 0 ? 0 : t;

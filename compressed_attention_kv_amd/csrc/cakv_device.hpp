@@ -36,6 +36,22 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 // two floats -> packed pair of f16 (round to nearest even, v_cvt_pk_f16_f32)
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef short bf16x2_t __attribute__((ext_vector_type(2)));  // two bf16 bit patterns (v_dot2_f32_bf16)
+
+// A 32-bit word as a bf16 pair.  Goes through a scalar copy: a bit cast
+// applied directly to an element of an ext_vector inside an unrolled loop
+// has been compiled as if it always named element 0.
+__device__ __forceinline__ bf16x2_t word_as_bf16x2(uint32_t w) {
+    bf16x2_t v;
+    __builtin_memcpy(&v, &w, 4);
+    return v;
+}
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+// two floats -> packed bf16 pair (round to nearest even; one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const bf16x2v_t h = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
 // two floats -> packed f16 pair (round to nearest even; one v_cvt_pk_f16_f32)
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
     const f16x2_t h = {(_Float16)a, (_Float16)b};
@@ -118,6 +134,14 @@ __device__ __forceinline__ float row16_sum(float v) {
     v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
     v = dpp_add<0x141>(v);  // row_half_mirror
     v = dpp_add<0x140>(v);  // row_mirror
+    return v;
+}
+
+// Sum over each group of 8 lanes, returned in every lane of the group.
+__device__ __forceinline__ float row8_sum(float v) {
+    v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = dpp_add<0x141>(v);  // row_half_mirror
     return v;
 }
 
