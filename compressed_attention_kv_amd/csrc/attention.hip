@@ -271,13 +271,20 @@ void mqa_fwd_kernel(const AttnArgs a) {
     constexpr int RB = D * (int)sizeof(TIn);   // bytes of one raw row
     constexpr int RPU = 1024 / RB;             // rows per 1 KiB asynchronous-load unit
     constexpr int LPR = 64 / RPU;              // lanes per row in a unit
-    // Row stride in LDS.  A 1 KiB row (bf16, D = 512) is one unit and gets 16
-    // bytes of padding, so that 16-byte column reads of consecutive rows fall
-    // in distinct banks; smaller rows share a unit and stay packed.
-    constexpr int PAD = RPU == 1 ? 16 : 0;
-    constexpr int RS = RB + PAD;               // ring row stride; the bf16 K row is its first 2D bytes
+    // LDS layout of a tile row.  A 1 KiB row (bf16, D = 512) is one load unit;
+    // rows are padded to 1088 bytes and, within each row, 16-byte granule g is
+    // stored at g ^ a(r) with a(r) = (r >> 2) & 3 (the loading lanes fetch
+    // the permuted granule, so the copy stays one contiguous 1 KiB write).
+    // Measured on gfx950, this keeps both operand reads near full LDS rate:
+    // the QK reads (16 B of one row per lane, 32 rows) and the transposed PV
+    // reads (ds_read_b64_tr_b16, 8 rows x 64 B per instruction).  Smaller
+    // rows share a unit and stay packed and unpermuted.
+    constexpr bool PERM = RPU == 1;
+    constexpr int PAD = PERM ? 64 : 0;
+    constexpr int RS = RB + PAD;               // ring row stride; the K row is its first 2D bytes
     constexpr int BUF = TK * RS;               // one tile
     constexpr int UNITS = TK * RB / 1024;      // units per tile
+    auto gperm = [](int row) __attribute__((always_inline)) { return PERM ? (row >> 2) & 3 : 0; };
     constexpr int NU = UNITS / 4;              // loads per wave per tile
     constexpr int MS = 8;                      // metadata ring slots
     constexpr int CH = D / 64;                 // 8-channel chunks per lane in the row-norm pass
@@ -366,7 +373,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
         for (int k = 0; k < NU; ++k) {
             const int u = wave + 4 * k;
             const uint8_t* src = rp[k] ? reinterpret_cast<const uint8_t*>(rp[k]) : spare_row;
-            lds_dma16(src + 16 * (ol % LPR), (uint32_t)(uintptr_t)(dst + (RPU == 1 ? u * RS : 1024 * u)));
+            lds_dma16(src + 16 * ((ol % LPR) ^ gperm(u)), (uint32_t)(uintptr_t)(dst + (RPU == 1 ? u * RS : 1024 * u)));
         }
     };
 
@@ -493,21 +500,24 @@ void mqa_fwd_kernel(const AttnArgs a) {
 #pragma unroll
             for (int k = 0; k < CH; ++k) {
                 const int c = jj + 8 * k;
-                *reinterpret_cast<u32x4*>(rb + 16 * c) =
+                *reinterpret_cast<u32x4*>(rb + 16 * (c ^ gperm(row))) =
                     u32x4{OP::pack(xs[k][0] * inv, xs[k][1] * inv), OP::pack(xs[k][2] * inv, xs[k][3] * inv),
                           OP::pack(xs[k][4] * inv, xs[k][5] * inv), OP::pack(xs[k][6] * inv, xs[k][7] * inv)};
             }
             if (jj == 0) invs[mslot][row] = 1.0f;
         } else {
+            u32x4 r[CH];  // all chunk reads in flight before the first product
 #pragma unroll
-            for (int k = 0; k < CH; ++k) {
-                const u32x4 r = *reinterpret_cast<const u32x4*>(rb + 16 * (jj + 8 * k));
+            for (int k = 0; k < CH; ++k) r[k] = *reinterpret_cast<const u32x4*>(rb + 16 * (jj + 8 * k));
+#pragma unroll
+            for (int k = 0; k < CH; ++k)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const bf16x2_t pr = word_as_bf16x2(r[i]);
+                    const bf16x2_t pr = word_as_bf16x2(r[k][i]);
                     ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
                 }
-            }
+            __builtin_amdgcn_sched_group_barrier(0x100, CH, 1);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4 * CH, 1);
             ss = row8_sum(ss);
             const float inv = valid ? __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps) : 0.0f;
             if (jj == 0) invs[mslot][row] = inv;
@@ -524,7 +534,8 @@ void mqa_fwd_kernel(const AttnArgs a) {
             const int pr = item >> 3;
             const bool on = pr < n_pairs;
             const int dim = rope_lo + 2 * pr;
-            uint32_t* pw = on ? reinterpret_cast<uint32_t*>(buf + rr * RS + 2 * dim) : &dummy[ol];
+            uint32_t* pw = on ? reinterpret_cast<uint32_t*>(buf + rr * RS + 16 * ((dim >> 3) ^ gperm(rr)) + 2 * (dim & 7))
+                              : &dummy[ol];
             float sn, cs;
             sincos_turns_fast((double)meta[mslot].pos[rr] * turns[on ? pr : 0], &sn, &cs);
             const uint32_t hv = *pw;
@@ -562,12 +573,34 @@ void mqa_fwd_kernel(const AttnArgs a) {
         f32x16 st;
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[r] = 0.0f;
-        const uint8_t* krow = kh + orow * RS + 16 * oh;
+        // K row orow, logical granule 2s + oh, stored at (2s + oh) ^ a(orow):
+        // k-step s = 2m + j reads byte 64 m + 32 (j ^ (a >> 1)) + 16 (oh ^ (a & 1))
+        const int ga = gperm(orow);
+        const uint8_t* kq0 = kh + orow * RS + 16 * (oh ^ (ga & 1)) + 32 * (ga >> 1);
+        const uint8_t* kq1 = kh + orow * RS + 16 * (oh ^ (ga & 1)) + 32 * ((ga >> 1) ^ 1);
+        auto kread = [&](int s) __attribute__((always_inline)) -> opvec {
+            return *reinterpret_cast<const opvec*>(((s & 1) ? kq1 : kq0) + 64 * (s >> 1));
+        };
+        // K operands QPF k-steps ahead of their MFMA, order pinned through
+        // scheduling (left alone, the scheduler shortens the prefetch to save
+        // registers and every MFMA waits on LDS latency)
+        constexpr int QPF = 6;
+        opvec kq[QPF];
+#pragma unroll
+        for (int s = 0; s < QPF; ++s) kq[s] = kread(s);
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-            const opvec av = *reinterpret_cast<const opvec*>(krow + 32 * s);
+            const opvec av = kq[s % QPF];
+            if (s + QPF < KSTEPS) kq[s % QPF] = kread(s + QPF);
             st = OP::mfma(av, qf[s], st);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, QPF, 2);
+#pragma unroll
+        for (int s = 0; s + QPF < KSTEPS; ++s) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, QPF, 2);
         // row scales of this lane's rows 8*(r/4) + 4*lh + r%4
         f32x4 iv[4];
 #pragma unroll
@@ -606,22 +639,49 @@ void mqa_fwd_kernel(const AttnArgs a) {
         // V operand: lane (group q = ol/16, i = ol%16) addresses row
         // 16 ks + 8 hf + 4 (q/2) + i/4, dims 32 dt + 16 (q%2) + 4 (i%4) .. +3
         const int q = ol >> 4, i16 = ol & 15;
+        // (logical granule 4 dt + 2 (q%2) + (i%4)/2, stored at granule ^ a(row):
+        // only the low two granule bits change, so dt stays an immediate)
         const uint8_t* vrow[2];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-            vrow[hf] = kh + (8 * hf + 4 * (q >> 1) + (i16 >> 2)) * RS + 32 * (q & 1) + 8 * (i16 & 3);
+        for (int hf = 0; hf < 2; ++hf) {
+            const int rr = 8 * hf + 4 * (q >> 1) + (i16 >> 2);
+            vrow[hf] = kh + rr * RS + 16 * ((2 * (q & 1) + ((i16 & 3) >> 1)) ^ gperm(rr)) + 8 * (i16 & 1);
+        }
+        // V operands of output tile dt+1 are read while tile dt is multiplied
+        auto vread = [&](int dt, int ks) __attribute__((always_inline)) -> opvec {
+            const int off = ks * 16 * RS + 64 * dt;
+            const h4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)const_cast<uint8_t*>(vrow[0] + off));
+            const h4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)const_cast<uint8_t*>(vrow[1] + off));
+            const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+            return __builtin_bit_cast(opvec, u32x4{w0[0], w0[1], w1[0], w1[1]});
+        };
+        constexpr int VPF = 2;  // output tiles of V operands in flight ahead of the MFMAs
+        opvec vb[VPF + 1][2];
+#pragma unroll
+        for (int d = 0; d < VPF; ++d) {
+            vb[d][0] = vread(d, 0);
+            vb[d][1] = vread(d, 1);
+        }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int off = ks * 16 * RS + 64 * dt;
-                const h4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)const_cast<uint8_t*>(vrow[0] + off));
-                const h4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)const_cast<uint8_t*>(vrow[1] + off));
-                const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
-                const opvec bv = __builtin_bit_cast(opvec, u32x4{w0[0], w0[1], w1[0], w1[1]});
-                acc[dt] = OP::mfma(pa[ks], bv, acc[dt]);
+            if (dt + VPF < DT) {
+                vb[(dt + VPF) % (VPF + 1)][0] = vread(dt + VPF, 0);
+                vb[(dt + VPF) % (VPF + 1)][1] = vread(dt + VPF, 1);
             }
+            acc[dt] = OP::mfma(pa[0], vb[dt % (VPF + 1)][0], acc[dt]);
+            acc[dt] = OP::mfma(pa[1], vb[dt % (VPF + 1)][1], acc[dt]);
         }
+        // keep that order through scheduling: the first tiles' reads, then
+        // (MFMA, two reads VPF tiles ahead) pairs, then the last MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * VPF, 0);
+#pragma unroll
+        for (int dt = 0; dt + VPF < DT; ++dt) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * VPF, 0);
     };
 
     // One pipeline step (tile T = tile0 + it):
