@@ -178,6 +178,22 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
         : "memory");
 }
 
+// The same load without a memory clobber, for the fast tile step: there the
+// destination buffer is not touched by any other access until the closing
+// barrier (which waits for the load explicitly), so LDS reads of the other
+// buffers may move across it.
+__device__ __forceinline__ void lds_dma16_nc(const void* gptr, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gptr), "s"(lds_base));
+}
+
 // Asynchronous 4-byte-per-lane HBM -> LDS load (global_load_lds_dword):
 // lane i writes LDS bytes [lds_base + 4 i, +4).  Same M0 handling as above.
 __device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_base) {
@@ -709,6 +725,184 @@ void mqa_fwd_kernel(const AttnArgs a) {
         else barrier_vm<0>();
     };
 
+    // Fast step (bf16 1 KiB rows, a full tile T, T+3 inside the split, an
+    // active wave that has not flagged): everything below is one branch-free
+    // block, so the scheduler can put the prep of T+1 and the asynchronous
+    // copy of T+3 between the MFMAs of T instead of in front of them; the
+    // copy is issued one unit every four QK MFMAs, which keeps the issuing
+    // wave from stalling on the load queue.
+    auto step_fast = [&](int it) __attribute__((always_inline)) {
+        const int T = tile0 + it;
+        if (wave == 0) {
+            const int ol0 = opaque_tid() & 63;
+            tile_meta(T + 4, (it + 4) & (MS - 1), SPARSE ? idxs[(it + 4) & (MS - 1)][ol0] : 0);
+            if (SPARSE && T + 5 < tile1) idx_load(T + 5, (it + 5) & (MS - 1));
+        }
+        const int ms0 = it & (MS - 1), ms1 = (it + 1) & (MS - 1), ms3 = (it + 3) & (MS - 1);
+        const uint8_t* kh = ring[it & 3];
+        uint8_t* pb = ring[(it + 1) & 3];
+        uint8_t* db = ring[(it + 3) & 3];
+        const int ol = opaque_tid() & 63;
+        // row pointers of T+3 (one row per unit: wave-uniform)
+        uint64_t rp[NU];
+#pragma unroll
+        for (int k = 0; k < NU; ++k) {
+            const uint64_t v = meta[ms3].rowp[wave + 4 * k];
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+            rp[k] = ((uint64_t)hi << 32) | (uint64_t)lo;
+        }
+        auto dma_unit = [&](int k) __attribute__((always_inline)) {
+            const int u = wave + 4 * k;
+            const uint8_t* src = rp[k] ? reinterpret_cast<const uint8_t*>(rp[k]) : spare_row;
+            lds_dma16_nc(src + 16 * ((ol % LPR) ^ gperm(u)), (uint32_t)(uintptr_t)(db + u * RS));
+        };
+        // prep of T+1, part 1: row sums of squares -> 1/rms (branch-free); the
+        // chunk reads run two ahead of their products
+        const int prow = 8 * wave + (ol >> 3), pj = ol & 7;
+        constexpr int PPF = 2;
+        u32x4 pr[PPF];
+        auto pread = [&](int k) __attribute__((always_inline)) -> u32x4 {
+            return *reinterpret_cast<const u32x4*>(pb + prow * RS + 16 * (pj + 8 * k));
+        };
+#pragma unroll
+        for (int k = 0; k < PPF; ++k) pr[k] = pread(k);
+        // QK of T
+        const int orow = ol & 31, oh = ol >> 5;
+        const int ga = gperm(orow);
+        const uint8_t* kq0 = kh + orow * RS + 16 * (oh ^ (ga & 1)) + 32 * (ga >> 1);
+        const uint8_t* kq1 = kh + orow * RS + 16 * (oh ^ (ga & 1)) + 32 * ((ga >> 1) ^ 1);
+        auto kread = [&](int s2) __attribute__((always_inline)) -> opvec {
+            return *reinterpret_cast<const opvec*>(((s2 & 1) ? kq1 : kq0) + 64 * (s2 >> 1));
+        };
+        constexpr int QPF = 6;
+        opvec kq[QPF];
+#pragma unroll
+        for (int s2 = 0; s2 < QPF; ++s2) kq[s2] = kread(s2);
+        f32x16 st;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[r] = 0.0f;
+        float ss = 0.0f;
+#pragma unroll
+        for (int s2 = 0; s2 < KSTEPS; ++s2) {
+            const opvec av = kq[s2 % QPF];
+            if (s2 + QPF < KSTEPS) kq[s2 % QPF] = kread(s2 + QPF);
+            st = OP::mfma(av, qf[s2], st);
+            if ((s2 & 3) == 1 && (s2 >> 2) < NU) dma_unit(s2 >> 2);
+            if (s2 < CH) {  // the prep products ride between the MFMAs
+                const u32x4 c4 = pr[s2 % PPF];
+                if (s2 + PPF < CH) pr[s2 % PPF] = pread(s2 + PPF);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bf16x2_t w2 = word_as_bf16x2(c4[i]);
+                    ss = __builtin_amdgcn_fdot2_f32_bf16(w2, w2, ss, false);
+                }
+            }
+        }
+        // pinned order: the first reads, then each MFMA followed by the reads
+        // that run ahead of it (else the prefetch collapses under pressure)
+        __builtin_amdgcn_sched_group_barrier(0x100, QPF + PPF, 2);
+#pragma unroll
+        for (int s2 = 0; s2 < KSTEPS; ++s2) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+            if (s2 + QPF < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+            if (s2 + PPF < CH) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // phases stay apart: bounded live ranges
+        ss = row8_sum(ss);
+        {
+            const bool pvalid = (meta[ms1].mask >> prow) & 1u;
+            invs[ms1][prow] = pvalid ? __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps) : 0.0f;  // 8 lanes, one value
+        }
+        // softmax of T (full tile, logits in log2 units)
+        f32x4 iv[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) iv[m] = *reinterpret_cast<const f32x4*>(&invs[ms0][8 * m + 4 * oh]);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            st[r] *= iv[r >> 2][r & 3];
+            mx = fmaxf(mx, st[r]);
+        }
+        mx = xor32_max(mx);
+        m_seen = fmaxf(m_seen, mx);
+        m_use = (m_use == -INFINITY) ? mx : m_use;
+        if (__ballot(mx > m_use + 15.0f)) flagged = true;
+        const float mm = flagged ? INFINITY : m_use;  // a flagged wave adds nothing until its second pass
+        float psum = 0.0f;
+        uint32_t pk[8];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(st[r] - mm);
+            const float p1 = __builtin_amdgcn_exp2f(st[r + 1] - mm);
+            psum += p0 + p1;
+            pk[r >> 1] = OP::pack(p0 * iv[r >> 2][r & 3], p1 * iv[r >> 2][(r & 3) + 1]);
+        }
+        l_run += xor32_sum(psum);
+        const opvec pa[2] = {__builtin_bit_cast(opvec, u32x4{pk[0], pk[1], pk[2], pk[3]}),
+                             __builtin_bit_cast(opvec, u32x4{pk[4], pk[5], pk[6], pk[7]})};
+        // PV of T
+        const int q = ol >> 4, i16 = ol & 15;
+        const uint8_t* vrow[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int rr = 8 * hf + 4 * (q >> 1) + (i16 >> 2);
+            vrow[hf] = kh + rr * RS + 16 * ((2 * (q & 1) + ((i16 & 3) >> 1)) ^ gperm(rr)) + 8 * (i16 & 1);
+        }
+        auto vread = [&](int dt, int ks) __attribute__((always_inline)) -> opvec {
+            const int off = ks * 16 * RS + 64 * dt;
+            const h4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)const_cast<uint8_t*>(vrow[0] + off));
+            const h4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)const_cast<uint8_t*>(vrow[1] + off));
+            const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+            return __builtin_bit_cast(opvec, u32x4{w0[0], w0[1], w1[0], w1[1]});
+        };
+        // prep of T+1, part 2: rotation items (branch-free)
+        const int prow0 = 8 * wave;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int item = ol + 64 * k;
+            const int rr = prow0 + (item & 7);
+            const int pri = item >> 3;
+            const bool on = pri < n_pairs;
+            const int dim = rope_lo + 2 * pri;
+            uint32_t* pw = on ? reinterpret_cast<uint32_t*>(pb + rr * RS + 16 * ((dim >> 3) ^ gperm(rr)) + 2 * (dim & 7))
+                              : &dummy[ol];
+            float sn, cs;
+            sincos_turns_fast((double)meta[ms1].pos[rr] * turns[on ? pri : 0], &sn, &cs);
+            const uint32_t hv = *pw;
+            const float x0 = OP::lo(hv) * gkv_s[on ? dim : 0];
+            const float x1 = OP::hi(hv) * gkv_s[on ? dim + 1 : 0];
+            *pw = OP::pack(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int VPF = 2;
+        opvec vb[VPF + 1][2];
+#pragma unroll
+        for (int d = 0; d < VPF; ++d) {
+            vb[d][0] = vread(d, 0);
+            vb[d][1] = vread(d, 1);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            if (dt + VPF < DT) {
+                vb[(dt + VPF) % (VPF + 1)][0] = vread(dt + VPF, 0);
+                vb[(dt + VPF) % (VPF + 1)][1] = vread(dt + VPF, 1);
+            }
+            acc[dt] = OP::mfma(pa[0], vb[dt % (VPF + 1)][0], acc[dt]);
+            acc[dt] = OP::mfma(pa[1], vb[dt % (VPF + 1)][1], acc[dt]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * VPF, 0);
+#pragma unroll
+        for (int dt = 0; dt + VPF < DT; ++dt) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * VPF, 0);
+        barrier_vm<NU>();
+    };
+
     barrier_lds();  // every wave has read its Q~ block: the ring is free
     for (int pass = 0; pass < 2; ++pass) {
         active = has_heads && (pass == 0 || flagged);
@@ -737,7 +931,15 @@ void mqa_fwd_kernel(const AttnArgs a) {
         if (tile0 < tile1) prep_tile(0, ring[0]);
         if (tile0 + 2 < tile1) barrier_vm<NU>();
         else barrier_vm<0>();
-        for (int it = 0; tile0 + it < tile1; ++it) step(it);
+        {
+            int it = 0;
+            if constexpr (PERM && !RAW_F32) {
+                for (; tile0 + it + 3 < tile1 && active && !flagged &&
+                       __builtin_amdgcn_readfirstlane(meta[it & (MS - 1)].mask) == 0xffffffffu; ++it)
+                    step_fast(it);
+            }
+            for (; tile0 + it < tile1; ++it) step(it);
+        }
         // does any wave need the second pass?
         if (tid == 0) redo = 0u;
         barrier_lds();

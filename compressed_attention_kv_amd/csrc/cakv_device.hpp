@@ -145,6 +145,30 @@ __device__ __forceinline__ float row8_sum(float v) {
     return v;
 }
 
+// max / sum of v over lanes l and l ^ 32 with v_permlane32_swap (a VALU
+// exchange, no LDS round trip): swapping the upper half of a copy of v with
+// the lower half of another copy leaves v[l % 32] in the first and
+// v[l % 32 + 32] in the second, in every lane.  Written as asm (with the
+// wait states the instruction needs after its operands are written; not
+// volatile, so it does not pin the schedule around it):
+// through the builtin, the compiler has folded the two results into one.
+__device__ __forceinline__ void self_swap32(float v, float* lo, float* hi) {
+    uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    *lo = __builtin_bit_cast(float, a);
+    *hi = __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float xor32_max(float v) {
+    float lo, hi;
+    self_swap32(v, &lo, &hi);
+    return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+    float lo, hi;
+    self_swap32(v, &lo, &hi);
+    return lo + hi;
+}
+
 __device__ __forceinline__ float lane_value(float v, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
