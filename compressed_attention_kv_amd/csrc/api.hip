@@ -233,9 +233,9 @@ int cakv_indexer_topk(const void* q_idx, int q_dtype, const float* w, const void
     a.dI = dI;
     a.m = m;
     a.k = k;
-    // score chunks: ~1024 workgroups in total, 128-entry granules
+    // score chunks: ~512 workgroups in total (two resident per CU), 128-entry granules
     const int64_t units = N > 0 ? ceil_div(N, 128) : 1;
-    int64_t per_q = ceil_div(1024, BQ);
+    int64_t per_q = ceil_div(512, BQ);
     if (per_q > units) per_q = units;
     if (per_q < 1) per_q = 1;
     a.chunk = (int32_t)(ceil_div(units, per_q) * 128);

@@ -159,56 +159,6 @@ struct TileMeta {
 typedef __fp16 h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __attribute__((address_space(3))) h4 lds_h4;
 
-// Asynchronous 16-byte-per-lane HBM -> LDS load (global_load_lds_dwordx4):
-// lane i writes LDS bytes [lds_base + 16 i, +16).  Written as one asm block
-// that saves and restores M0 around the load (M0 carries the LDS base; one
-// wait state after writing it), so the compiler neither sees an LDS store
-// it would have to wait for nor loses its own M0.  There is no register
-// output; completion is awaited explicitly (vmcnt) before the data is read.
-__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(gptr), "s"(lds_base)
-        : "memory");
-}
-
-// The same load without a memory clobber, for the fast tile step: there the
-// destination buffer is not touched by any other access until the closing
-// barrier (which waits for the load explicitly), so LDS reads of the other
-// buffers may move across it.
-__device__ __forceinline__ void lds_dma16_nc(const void* gptr, uint32_t lds_base) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(gptr), "s"(lds_base));
-}
-
-// Asynchronous 4-byte-per-lane HBM -> LDS load (global_load_lds_dword):
-// lane i writes LDS bytes [lds_base + 4 i, +4).  Same M0 handling as above.
-__device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_base) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dword %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(gptr), "s"(lds_base)
-        : "memory");
-}
-
 // The thread index laundered through an empty asm statement: address
 // arithmetic derived from it cannot be hoisted out of the tile loop, which
 // would pin dozens of loop-invariant addresses in VGPRs for the whole loop.
@@ -726,11 +676,15 @@ void mqa_fwd_kernel(const AttnArgs a) {
     };
 
     // Fast step (bf16 1 KiB rows, a full tile T, T+3 inside the split, an
-    // active wave that has not flagged): everything below is one branch-free
-    // block, so the scheduler can put the prep of T+1 and the asynchronous
-    // copy of T+3 between the MFMAs of T instead of in front of them; the
-    // copy is issued one unit every four QK MFMAs, which keeps the issuing
-    // wave from stalling on the load queue.
+    // active wave that has not flagged): one block in three phases whose
+    // VALU work rides under MFMAs (branching only on a pass's first tile).
+    //   A: the QK MFMAs of T, with the copy of T+3 (one row unit every four
+    //      MFMAs), the row sums of T+1 and the rotation of T+1 between them;
+    //   B: P for the first eight keys of T (P no longer waits on the tile
+    //      max: a tile that would flag the wave only spoils a pass that the
+    //      second pass redoes);
+    //   C: the PV MFMAs of T for k-step 0, then 1, with the other eight
+    //      keys' P, the max and the sums between them.
     auto step_fast = [&](int it) __attribute__((always_inline)) {
         const int T = tile0 + it;
         if (wave == 0) {
@@ -757,17 +711,35 @@ void mqa_fwd_kernel(const AttnArgs a) {
             const uint8_t* src = rp[k] ? reinterpret_cast<const uint8_t*>(rp[k]) : spare_row;
             lds_dma16_nc(src + 16 * ((ol % LPR) ^ gperm(u)), (uint32_t)(uintptr_t)(db + u * RS));
         };
-        // prep of T+1, part 1: row sums of squares -> 1/rms (branch-free); the
-        // chunk reads run two ahead of their products
+        // row sums of squares of T+1 (8 lanes per row, rows 8 wave + ol / 8);
+        // the chunk reads run PPF ahead of their products
         const int prow = 8 * wave + (ol >> 3), pj = ol & 7;
         constexpr int PPF = 2;
         u32x4 pr[PPF];
         auto pread = [&](int k) __attribute__((always_inline)) -> u32x4 {
             return *reinterpret_cast<const u32x4*>(pb + prow * RS + 16 * (pj + 8 * k));
         };
+        // rotation of T+1: lane pair rpi, rows 8 wave + ol / 32 + 2 k; the
+        // pair's turn rate and KV gains are per lane, the positions per row
+        const int rpi = ol & 31, rh = ol >> 5;
+        const bool ron = rpi < n_pairs;
+        const int rdim = rope_lo + 2 * (ron ? rpi : 0);
+        const double rturn = turns[ron ? rpi : 0];
+        const float rg0 = gkv_s[rdim], rg1 = gkv_s[rdim + 1];
+        auto rope_item = [&](int k) __attribute__((always_inline)) {
+            const int rr = 8 * wave + rh + 2 * k;
+            uint32_t* pw = ron ? reinterpret_cast<uint32_t*>(pb + rr * RS + 16 * ((rdim >> 3) ^ gperm(rr)) + 2 * (rdim & 7))
+                               : &dummy[ol];
+            float sn, cs;
+            sincos_turns_fast((double)meta[ms1].pos[rr] * rturn, &sn, &cs);
+            const uint32_t hv = *pw;
+            const float x0 = OP::lo(hv) * rg0;
+            const float x1 = OP::hi(hv) * rg1;
+            *pw = OP::pack(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+        };
 #pragma unroll
         for (int k = 0; k < PPF; ++k) pr[k] = pread(k);
-        // QK of T
+        // ---- A: QK of T
         const int orow = ol & 31, oh = ol >> 5;
         const int ga = gperm(orow);
         const uint8_t* kq0 = kh + orow * RS + 16 * (oh ^ (ga & 1)) + 32 * (ga >> 1);
@@ -789,7 +761,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
             if (s2 + QPF < KSTEPS) kq[s2 % QPF] = kread(s2 + QPF);
             st = OP::mfma(av, qf[s2], st);
             if ((s2 & 3) == 1 && (s2 >> 2) < NU) dma_unit(s2 >> 2);
-            if (s2 < CH) {  // the prep products ride between the MFMAs
+            if (s2 < CH) {
                 const u32x4 c4 = pr[s2 % PPF];
                 if (s2 + PPF < CH) pr[s2 % PPF] = pread(s2 + PPF);
 #pragma unroll
@@ -798,6 +770,8 @@ void mqa_fwd_kernel(const AttnArgs a) {
                     ss = __builtin_amdgcn_fdot2_f32_bf16(w2, w2, ss, false);
                 }
             }
+            // rotations after the last chunk read of the row sums (same rows)
+            if (s2 >= 12 && (s2 & 3) == 0 && ((s2 - 12) >> 2) < 4) rope_item((s2 - 12) >> 2);
         }
         // pinned order: the first reads, then each MFMA followed by the reads
         // that run ahead of it (else the prefetch collapses under pressure)
@@ -808,40 +782,38 @@ void mqa_fwd_kernel(const AttnArgs a) {
             if (s2 + QPF < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
             if (s2 + PPF < CH) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
         }
-        __builtin_amdgcn_sched_barrier(0);  // phases stay apart: bounded live ranges
+        __builtin_amdgcn_sched_barrier(0);
         ss = row8_sum(ss);
         {
             const bool pvalid = (meta[ms1].mask >> prow) & 1u;
             invs[ms1][prow] = pvalid ? __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps) : 0.0f;  // 8 lanes, one value
         }
-        // softmax of T (full tile, logits in log2 units)
+        // ---- B: logits relative to m_use (log2 units), P of the first keys
         f32x4 iv[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) iv[m] = *reinterpret_cast<const f32x4*>(&invs[ms0][8 * m + 4 * oh]);
-        float mx = -INFINITY;
+        if (__ballot(m_use == -INFINITY)) {  // first tile of the pass: m_use is its max
+            float m0 = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            st[r] *= iv[r >> 2][r & 3];
-            mx = fmaxf(mx, st[r]);
+            for (int r = 0; r < 16; ++r) m0 = fmaxf(m0, st[r] * iv[r >> 2][r & 3]);
+            m0 = xor32_max(m0);
+            m_use = (m_use == -INFINITY) ? m0 : m_use;
         }
-        mx = xor32_max(mx);
-        m_seen = fmaxf(m_seen, mx);
-        m_use = (m_use == -INFINITY) ? mx : m_use;
-        if (__ballot(mx > m_use + 15.0f)) flagged = true;
-        const float mm = flagged ? INFINITY : m_use;  // a flagged wave adds nothing until its second pass
-        float psum = 0.0f;
-        uint32_t pk[8];
+        float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(st[r] - mm);
-            const float p1 = __builtin_amdgcn_exp2f(st[r + 1] - mm);
+        for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(st[r], iv[r >> 2][r & 3], -m_use);
+        uint32_t pk[8];
+        float psum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 8; r += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(x[r]);
+            const float p1 = __builtin_amdgcn_exp2f(x[r + 1]);
             psum += p0 + p1;
             pk[r >> 1] = OP::pack(p0 * iv[r >> 2][r & 3], p1 * iv[r >> 2][(r & 3) + 1]);
         }
-        l_run += xor32_sum(psum);
-        const opvec pa[2] = {__builtin_bit_cast(opvec, u32x4{pk[0], pk[1], pk[2], pk[3]}),
-                             __builtin_bit_cast(opvec, u32x4{pk[4], pk[5], pk[6], pk[7]})};
-        // PV of T
+        const opvec pa0 = __builtin_bit_cast(opvec, u32x4{pk[0], pk[1], pk[2], pk[3]});
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- C: PV of T, k-step 0 over all column tiles, then k-step 1
         const int q = ol >> 4, i16 = ol & 15;
         const uint8_t* vrow[2];
 #pragma unroll
@@ -849,57 +821,56 @@ void mqa_fwd_kernel(const AttnArgs a) {
             const int rr = 8 * hf + 4 * (q >> 1) + (i16 >> 2);
             vrow[hf] = kh + rr * RS + 16 * ((2 * (q & 1) + ((i16 & 3) >> 1)) ^ gperm(rr)) + 8 * (i16 & 1);
         }
-        auto vread = [&](int dt, int ks) __attribute__((always_inline)) -> opvec {
+        auto vread = [&](int j) __attribute__((always_inline)) -> opvec {
+            const int dt = j & (DT - 1), ks = j / DT;
             const int off = ks * 16 * RS + 64 * dt;
             const h4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)const_cast<uint8_t*>(vrow[0] + off));
             const h4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)const_cast<uint8_t*>(vrow[1] + off));
             const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
             return __builtin_bit_cast(opvec, u32x4{w0[0], w0[1], w1[0], w1[1]});
         };
-        // prep of T+1, part 2: rotation items (branch-free)
-        const int prow0 = 8 * wave;
+        constexpr int VPF = 4, NJ = 2 * DT;
+        opvec vb[VPF];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int item = ol + 64 * k;
-            const int rr = prow0 + (item & 7);
-            const int pri = item >> 3;
-            const bool on = pri < n_pairs;
-            const int dim = rope_lo + 2 * pri;
-            uint32_t* pw = on ? reinterpret_cast<uint32_t*>(pb + rr * RS + 16 * ((dim >> 3) ^ gperm(rr)) + 2 * (dim & 7))
-                              : &dummy[ol];
-            float sn, cs;
-            sincos_turns_fast((double)meta[ms1].pos[rr] * turns[on ? pri : 0], &sn, &cs);
-            const uint32_t hv = *pw;
-            const float x0 = OP::lo(hv) * gkv_s[on ? dim : 0];
-            const float x1 = OP::hi(hv) * gkv_s[on ? dim + 1 : 0];
-            *pw = OP::pack(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        constexpr int VPF = 2;
-        opvec vb[VPF + 1][2];
+        for (int j = 0; j < VPF; ++j) vb[j] = vread(j);
+        opvec pa1;
+        float mx = -INFINITY;
 #pragma unroll
-        for (int d = 0; d < VPF; ++d) {
-            vb[d][0] = vread(d, 0);
-            vb[d][1] = vread(d, 1);
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            if (dt + VPF < DT) {
-                vb[(dt + VPF) % (VPF + 1)][0] = vread(dt + VPF, 0);
-                vb[(dt + VPF) % (VPF + 1)][1] = vread(dt + VPF, 1);
+        for (int j = 0; j < NJ; ++j) {
+            const opvec bv = vb[j % VPF];
+            if (j + VPF < NJ) vb[j % VPF] = vread(j + VPF);
+            if (j < DT) {
+                acc[j] = OP::mfma(pa0, bv, acc[j]);
+            } else {
+                acc[j - DT] = OP::mfma(pa1, bv, acc[j - DT]);
             }
-            acc[dt] = OP::mfma(pa[0], vb[dt % (VPF + 1)][0], acc[dt]);
-            acc[dt] = OP::mfma(pa[1], vb[dt % (VPF + 1)][1], acc[dt]);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 * VPF, 0);
+            // the second keys' P (needed from k-step 1 on), the max, the sums
+            if (j >= 1 && j <= 4) {
+                const int r = 8 + 2 * (j - 1);
+                const float p0 = __builtin_amdgcn_exp2f(x[r]);
+                const float p1 = __builtin_amdgcn_exp2f(x[r + 1]);
+                psum += p0 + p1;
+                pk[4 + (j - 1)] = OP::pack(p0 * iv[r >> 2][r & 3], p1 * iv[r >> 2][(r & 3) + 1]);
+                if (j == 4) pa1 = __builtin_bit_cast(opvec, u32x4{pk[4], pk[5], pk[6], pk[7]});
+            }
+            if (j == 6) {
 #pragma unroll
-        for (int dt = 0; dt + VPF < DT; ++dt) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[r]);
+            }
+            if (j == 8) {
+                mx = xor32_max(mx);
+                l_run += xor32_sum(psum);
+            }
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * VPF, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * VPF, 0);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (j + VPF < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        // the tile max only decides the flag and the second pass's m_use
+        m_seen = fmaxf(m_seen, mx + m_use);
+        if (__ballot(mx > 15.0f)) flagged = true;
         barrier_vm<NU>();
     };
 

@@ -186,4 +186,64 @@ __device__ __forceinline__ uint32_t score_key(float s) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Asynchronous 16-byte-per-lane HBM -> LDS load (global_load_lds_dwordx4):
+// lane i writes LDS bytes [lds_base + 16 i, +16).  Written as one asm block
+// that saves and restores M0 around the load (M0 carries the LDS base; one
+// wait state after writing it), so the compiler neither sees an LDS store
+// it would have to wait for nor loses its own M0.  There is no register
+// output; completion is awaited explicitly (vmcnt) before the data is read.
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gptr), "s"(lds_base)
+        : "memory");
+}
+
+// The same load without a memory clobber, for the fast tile step: there the
+// destination buffer is not touched by any other access until the closing
+// barrier (which waits for the load explicitly), so LDS reads of the other
+// buffers may move across it.
+__device__ __forceinline__ void lds_dma16_nc(const void* gptr, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gptr), "s"(lds_base));
+}
+
+// Asynchronous 4-byte-per-lane HBM -> LDS load (global_load_lds_dword):
+// lane i writes LDS bytes [lds_base + 4 i, +4).  Same M0 handling as above.
+__device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gptr), "s"(lds_base)
+        : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations (loads,
+// stores and asynchronous LDS loads, which complete in issue order) are
+// still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);  // vmcnt(N), other counters untouched
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 }  // namespace cakv

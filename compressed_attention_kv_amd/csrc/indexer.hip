@@ -40,23 +40,88 @@ __device__ __forceinline__ int64_t query_nvis(const IndexerArgs& a, int64_t bq) 
 }
 
 // ------------------------------------------------------------------ fp8 mode
-// HT: head tiles of 32 (HI = 32*HT); KS: MFMA k-steps of 16 (dI = 16*KS)
+// HT: head tiles of 32 (HI = 32*HT); KS: MFMA k-steps of 16 (dI = 16*KS).
+// Each wave streams its own 32-entry key groups (j0 = j_begin + 32 wave +
+// 128 n) through a private ring of kSlots LDS slots filled by asynchronous
+// HBM->LDS copies, kSlots - 1 groups ahead of the group it multiplies: the
+// bytes in flight cost no registers and no barrier (the wave that copies a
+// group is the one that reads it).  In a slot, 16-byte chunk c of row r holds
+// the row's chunk c ^ (r mod chunks-per-row), which makes the per-row operand
+// reads conflict-free.
+constexpr int kSlots = 4;  // at most 4 (wait_groups)
+
+template <int DI>
+struct ScoreRing {
+    static constexpr int GB = 32 * DI;        // key bytes of a group
+    static constexpr int NDMA = GB / 1024;    // 16-byte-per-lane copies of a group
+    static constexpr int CPR = DI / 16;       // 16-byte chunks per row
+    static constexpr int SLOT = GB + 256;     // keys, then 64 scales (32 used)
+    static constexpr int OPS = NDMA + 1;      // vector-memory operations per group
+};
+
+// Wait for a group's copies when nd later groups' copies (ops vector-memory
+// operations each) and ns single stores were issued after them (wave-uniform
+// nd, ns < kSlots).
+template <int OPS>
+__device__ __forceinline__ void wait_groups(int nd, int ns) {
+    switch (nd * 4 + ns) {
+#define CAKV_WAIT_CASE(d, s) \
+    case (d) * 4 + (s): wait_vm<(d) * OPS + (s)>(); break;
+        CAKV_WAIT_CASE(0, 0) CAKV_WAIT_CASE(0, 1) CAKV_WAIT_CASE(0, 2) CAKV_WAIT_CASE(0, 3)
+        CAKV_WAIT_CASE(1, 0) CAKV_WAIT_CASE(1, 1) CAKV_WAIT_CASE(1, 2) CAKV_WAIT_CASE(1, 3)
+        CAKV_WAIT_CASE(2, 0) CAKV_WAIT_CASE(2, 1) CAKV_WAIT_CASE(2, 2) CAKV_WAIT_CASE(2, 3)
+        CAKV_WAIT_CASE(3, 0) CAKV_WAIT_CASE(3, 1) CAKV_WAIT_CASE(3, 2) CAKV_WAIT_CASE(3, 3)
+#undef CAKV_WAIT_CASE
+        default: wait_vm<0>(); break;
+    }
+}
+
 template <int HT, int KS>
-__global__ __launch_bounds__(256) void idx_score_fp8_kernel(const IndexerArgs a) {
+__global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs a) {
+    constexpr int DI = 16 * KS;
+    typedef ScoreRing<DI> R;
+    constexpr int HALF = DI / 2;        // bytes of a key row per half-wave lane
+    constexpr int NLD = HALF / 16;      // 16-byte chunks per lane
+    __shared__ __attribute__((aligned(16))) uint8_t ring[4][kSlots][R::SLOT];
+
     const int64_t bq = blockIdx.y;
     const int64_t nvis = query_nvis(a, bq);
     const int64_t j_begin = (int64_t)blockIdx.x * a.chunk;
     if (nvis <= a.k || j_begin >= nvis) return;
     const int64_t j_end = min(nvis, j_begin + a.chunk);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lrow = lane & 31, lh = lane >> 5;
-    constexpr int DI = 16 * KS;
-    constexpr int HALF = DI / 2;        // bytes of a key row per half-wave lane
-    constexpr int NLD = HALF / 16;      // 16-byte loads per lane
+    const int tid = threadIdx.x, lane = tid & 63, lrow = lane & 31, lh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: ring addresses go to M0
+    const int64_t first = j_begin + 32 * wave;
+    const int ng = first < j_end ? (int)((j_end - first + 127) / 128) : 0;
+    if (ng == 0) return;  // nothing for this wave (no barrier below)
+
+    const int64_t b = bq / a.Q;
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_idx) + b * a.N * DI;
+    const float* sbase = a.k_scale + b * a.N;
+    uint32_t* kout = a.keys + bq * a.N;
+    uint8_t* slots = &ring[wave][0][0];
+
+    // copies of group n into slot n % kSlots (rows past the cache end read
+    // its last row: in bounds, never scored)
+    auto issue = [&](int n) {
+        const int64_t j0 = first + 128 * (int64_t)n;
+        uint8_t* slot = slots + (n % kSlots) * R::SLOT;
+#pragma unroll
+        for (int i = 0; i < R::NDMA; ++i) {
+            const int o = 1024 * i + 16 * lane;
+            const int r = o / DI, c = (o % DI) / 16;
+            const int64_t row = min(j0 + r, a.N - 1);
+            lds_dma16(kbase + row * DI + 16 * (c ^ (r & (R::CPR - 1))), (uint32_t)(uintptr_t)(slot + 1024 * i));
+        }
+        lds_dma4(sbase + min(j0 + lane, a.N - 1), (uint32_t)(uintptr_t)(slot + R::GB));
+    };
+#pragma unroll
+    for (int n = 0; n < kSlots - 1; ++n)
+        if (n < ng) issue(n);
 
     // A operand: query heads (rows) x features, k-permutation (s, half, e) -> half*DI/2 + 8s + e
     bf16x8 qa[HT][KS];
     float wv[HT][16];
-    const int64_t b = bq / a.Q;
     const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.q_idx) + bq * (int64_t)(32 * HT) * DI;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
@@ -68,25 +133,19 @@ __global__ __launch_bounds__(256) void idx_score_fp8_kernel(const IndexerArgs a)
         for (int r = 0; r < 16; ++r) wv[ht][r] = a.w[bq * (32 * HT) + 32 * ht + 8 * (r >> 2) + 4 * lh + (r & 3)];
     }
 
-    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_idx) + b * a.N * DI;
-    const float* sbase = a.k_scale + b * a.N;
-    uint32_t* kout = a.keys + bq * a.N;
-    auto load_group = [&](int64_t j0, u32x4 raw[NLD], float& sc) {
-        const int64_t j = j0 + lrow;
-        const int64_t jj = j < a.N ? j : a.N - 1;
+    for (int n = 0; n < ng; ++n) {
+        // issue order: key store of group n-1, copies of group n+kSlots-1;
+        // then wait for group n: after its copies came the copies of groups
+        // n+1..min(n+kSlots-1, ng-1) and the stores of groups max(n-kSlots+1,0)..n-1
+        const int nd = min(kSlots - 1, ng - 1 - n), ns = min(n, kSlots - 1);
+        if (n + kSlots - 1 < ng) issue(n + kSlots - 1);
+        wait_groups<R::OPS>(nd, ns);
+        const uint8_t* slot = slots + (n % kSlots) * R::SLOT;
+        u32x4 cur[NLD];
 #pragma unroll
         for (int i = 0; i < NLD; ++i)
-            raw[i] = *reinterpret_cast<const u32x4*>(kbase + jj * DI + lh * HALF + 16 * i);
-        sc = sbase[jj];
-    };
-    // each wave walks 32-entry groups j0 = j_begin + 32*wave + 128*i, with the
-    // next group's key bytes in flight while the current group is multiplied
-    u32x4 cur[NLD], nxt[NLD];
-    float sc_cur = 0.0f, sc_nxt = 0.0f;
-    int64_t j0 = j_begin + 32 * wave;
-    if (j0 < j_end) load_group(j0, cur, sc_cur);
-    for (; j0 < j_end; j0 += 128) {
-        if (j0 + 128 < j_end) load_group(j0 + 128, nxt, sc_nxt);
+            cur[i] = *reinterpret_cast<const u32x4*>(slot + lrow * DI + 16 * ((lh * NLD + i) ^ (lrow & (R::CPR - 1))));
+        const float sc = *reinterpret_cast<const float*>(slot + R::GB + 4 * lrow);
         f32x16 acc[HT];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht)
@@ -115,12 +174,9 @@ __global__ __launch_bounds__(256) void idx_score_fp8_kernel(const IndexerArgs a)
                 sum = __builtin_fmaf(wv[ht][r], v > 0.0f ? v : 0.0f, sum);
             }
         sum += __shfl_xor(sum, 32, 64);
-        sum *= sc_cur;
-        const int64_t j = j0 + lrow;
+        sum *= sc;
+        const int64_t j = first + 128 * (int64_t)n + lrow;
         if (lane < 32 && j < j_end) kout[j] = score_key(sum);
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) cur[i] = nxt[i];
-        sc_cur = sc_nxt;
     }
 }
 
