@@ -168,16 +168,6 @@ __device__ __forceinline__ int opaque_tid() {
     return t;
 }
 
-// Barrier that waits for this wave's LDS traffic only: asynchronous
-// HBM->LDS loads of the next tile stay in flight across it.  Signal fences
-// keep the compiler from moving LDS accesses across the barrier.
-__device__ __forceinline__ void barrier_lds() {
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // Barrier after which this workgroup's asynchronous tile loads have landed.
 __device__ __forceinline__ void barrier_all() {
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)

@@ -246,4 +246,14 @@ __device__ __forceinline__ void wait_vm() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Barrier that waits for this wave's LDS traffic only: asynchronous
+// HBM->LDS loads (and other vector-memory operations) stay in flight across
+// it.  Signal fences keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 }  // namespace cakv

@@ -10,8 +10,9 @@ namespace cakv {
 
 constexpr int kMaxRopePairs = 32;  // rope_dims <= 64
 constexpr int kTopkCap = 4096;     // largest k
-constexpr int kBoundaryCap = 8192; // top-k candidates held in LDS on the fast path
-constexpr int kHistBins = 2048;    // sample histogram over the top 11 bits of the score key
+constexpr int kCandCap = 8192;     // entries of the threshold bin listed per query on the fast path
+constexpr int kHistBins = 2048;    // 11-bit histogram levels over the score key
+constexpr int kHistStride = 2 * kHistBins + 64;  // words per query: level 1, level 2, counter
 
 // Everything one attention launch needs; passed by value as the kernel
 // argument block.
@@ -65,6 +66,9 @@ struct IndexerArgs {
     const int32_t* q_pos;
     int32_t* idx;
     uint32_t* keys;      // [BQ][N] order-preserving score keys
+    uint32_t* hist;      // [BQ][kHistStride] key histograms (top 11 bits; next 11 bits) + counters
+    uint32_t* cand_a;    // [BQ][kTopkCap] entries above the threshold bin
+    uint64_t* cand_b;    // [BQ][kCandCap] rank values (~key << 32 | j) of the entries in the threshold bin
     int64_t Q;
     int64_t N;
     int32_t HI;

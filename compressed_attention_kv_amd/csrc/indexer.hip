@@ -7,26 +7,25 @@
 // S(j) = sum_h w_h * ReLU(q_h . k_j); ties go to the lower index; output
 // ascending by index, -1 padded.
 //
-// Two kernels per call:
+// Kernels per call:
+//   0. zero: the per-query histogram blocks.
 //   1. score: one workgroup per (query, chunk of entries).
-//        fp8 mode: keys stream from HBM once, 64 bytes per lane per 32
-//        entries (the next group's bytes are in flight while the current one
-//        is multiplied), decoded exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8)
-//        and multiplied on v_mfma_f32_32x32x16_bf16 against the bf16 query
-//        heads held in VGPRs (heads x entries, fp32 accumulation); ReLU, the
-//        head weights and the head reduction run on the accumulator registers
-//        and one half-wave exchange.  The per-entry scale multiplies the final
-//        sum (a power of two, so exact up to rounding order).
+//        fp8 mode: each wave streams its own 32-entry groups of keys and
+//        scales through a private LDS ring of asynchronous HBM->LDS copies,
+//        three groups ahead; keys are decoded exactly to bf16
+//        (v_cvt_scalef32_pk_bf16_fp8) and multiplied on
+//        v_mfma_f32_32x32x16_bf16 against the bf16 query heads held in VGPRs
+//        (heads x entries, fp32 accumulation); ReLU, the head weights and the
+//        head reduction run on the accumulator registers and one half-wave
+//        exchange.  The per-entry scale multiplies the final sum (a power of
+//        two, so exact up to rounding order).
 //        fp32 mode: one thread per entry runs the canonical fmaf chains.
-//      Each score is written as an order-preserving 32-bit key.
-//   2. top-k: one workgroup per query, no cross-workgroup hand-off.  A
-//      strided sample of the keys gives a threshold (top 22 bits of the key,
-//      from two 11-bit histogram levels) that a little more than k keys reach;
-//      one coalesced pass collects every key at or above it into LDS; an LSD-free radix select on (key, index) finds
-//      the k-th best exactly; the winners are marked in an LDS bitmap over
-//      the entry range and compacted in index order.  If the guess collects
-//      fewer than k or more than the LDS capacity, an exact radix select over
-//      the whole key array takes over (slow, only for adversarial inputs).
+//      Each score is written as an order-preserving 32-bit key, and counted
+//      in an exact histogram of the top 11 key bits (LDS, then HBM atomics).
+//   2. refine (same grid): lists the entries above the threshold bin and in
+//      it; histograms the next 11 bits of the ones in it (see top-k below).
+//   3. select: one workgroup per query ranks the threshold bin's entries and
+//      writes the k winners in index order.
 #include "cakv_device.hpp"
 #include "cakv_internal.hpp"
 
@@ -37,6 +36,15 @@ __device__ __forceinline__ int64_t query_nvis(const IndexerArgs& a, int64_t bq) 
     t = t < 0 ? 0 : t;
     int64_t nv = t / a.m;
     return nv < a.N ? nv : a.N;
+}
+
+// Add a workgroup's LDS histogram into the query's histogram in HBM
+// (nonzero bins only; the HBM copy was zeroed before the score pass).
+__device__ __forceinline__ void flush_hist(const uint32_t* h, uint32_t* g, int nthreads) {
+    for (int i = threadIdx.x; i < kHistBins; i += nthreads) {
+        const uint32_t c = h[i];
+        if (c) __hip_atomic_fetch_add(g + i, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // ------------------------------------------------------------------ fp8 mode
@@ -83,6 +91,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
     constexpr int HALF = DI / 2;        // bytes of a key row per half-wave lane
     constexpr int NLD = HALF / 16;      // 16-byte chunks per lane
     __shared__ __attribute__((aligned(16))) uint8_t ring[4][kSlots][R::SLOT];
+    __shared__ uint32_t hist[kHistBins];
 
     const int64_t bq = blockIdx.y;
     const int64_t nvis = query_nvis(a, bq);
@@ -93,7 +102,6 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: ring addresses go to M0
     const int64_t first = j_begin + 32 * wave;
     const int ng = first < j_end ? (int)((j_end - first + 127) / 128) : 0;
-    if (ng == 0) return;  // nothing for this wave (no barrier below)
 
     const int64_t b = bq / a.Q;
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_idx) + b * a.N * DI;
@@ -118,6 +126,8 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
 #pragma unroll
     for (int n = 0; n < kSlots - 1; ++n)
         if (n < ng) issue(n);
+    for (int i = tid; i < kHistBins; i += 256) hist[i] = 0u;
+    barrier_lds();  // the copies stay in flight
 
     // A operand: query heads (rows) x features, k-permutation (s, half, e) -> half*DI/2 + 8s + e
     bf16x8 qa[HT][KS];
@@ -176,8 +186,14 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
         sum += __shfl_xor(sum, 32, 64);
         sum *= sc;
         const int64_t j = first + 128 * (int64_t)n + lrow;
-        if (lane < 32 && j < j_end) kout[j] = score_key(sum);
+        if (lane < 32 && j < j_end) {
+            const uint32_t key = score_key(sum);
+            kout[j] = key;
+            atomicAdd(&hist[key >> 21], 1u);
+        }
     }
+    barrier_lds();
+    flush_hist(hist, a.hist + bq * kHistStride, 256);
 }
 
 // ------------------------------------------------------------------ fp32 mode
@@ -186,6 +202,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
 __global__ __launch_bounds__(256) void idx_score_f32_kernel(const IndexerArgs a) {
     __shared__ float qs[8192];
     __shared__ float ws[64];
+    __shared__ uint32_t hist[kHistBins];
     const int64_t bq = blockIdx.y;
     const int64_t nvis = query_nvis(a, bq);
     const int64_t j_begin = (int64_t)blockIdx.x * a.chunk;
@@ -196,6 +213,7 @@ __global__ __launch_bounds__(256) void idx_score_f32_kernel(const IndexerArgs a)
     const float* q = reinterpret_cast<const float*>(a.q_idx) + bq * (int64_t)HI * DI;
     for (int i = tid; i < HI * DI; i += 256) qs[i] = q[i];
     for (int i = tid; i < HI; i += 256) ws[i] = a.w[bq * HI + i];
+    for (int i = tid; i < kHistBins; i += 256) hist[i] = 0u;
     __syncthreads();
     const int64_t b = bq / a.Q;
     const float* kb = reinterpret_cast<const float*>(a.k_idx) + b * a.N * DI;
@@ -215,18 +233,33 @@ __global__ __launch_bounds__(256) void idx_score_f32_kernel(const IndexerArgs a)
             const float rl = s > 0.0f ? s : 0.0f;
             S = __builtin_fmaf(ws[h], rl, S);
         }
-        a.keys[bq * a.N + j] = score_key(S);
+        const uint32_t key = score_key(S);
+        a.keys[bq * a.N + j] = key;
+        atomicAdd(&hist[key >> 21], 1u);
     }
+    __syncthreads();
+    flush_hist(hist, a.hist + bq * kHistStride, 256);
 }
 
 // ------------------------------------------------------------------ top-k
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
+// The score pass leaves an exact histogram of the top 11 key bits per query
+// (level 1).  Its threshold bin b1 is where the running count from the top
+// reaches k: the keys above it are fewer than k, with it at least k.  A
+// refine pass on the score grid lists the entries above b1 (all winners) and
+// those in b1, and, unless b1 holds only a few keys (kSmallBin), histograms
+// the next 11 key bits of the ones in b1 (level 2).  One workgroup per query
+// then takes the entries of b1 above the level-2 threshold bin (found the
+// same way), ranks the ones in that bin (or, at level 1, all of b1) by (key,
+// lower index first), and writes the winners in index order.  If b1 holds
+// more than kCandCap keys, a radix select over the whole key array is used.
 constexpr int kBitmapWords = 8192;  // LDS bitmap covers 2^18 entries
+constexpr uint32_t kSmallBin = 512;
 
-// Workgroup-wide exclusive prefix sum of one value per thread (kSelThreads);
-// every thread also receives the workgroup total.  wsum: kSelWaves + 1 words.
+// Workgroup-wide exclusive prefix sum of one value per thread (NT threads);
+// every thread also receives the workgroup total.  wsum: NT/64 + 1 words.
+template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+    constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t incl = v;
 #pragma unroll
@@ -237,21 +270,139 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     if (wave == 0) {
-        uint32_t x = lane < kSelWaves ? wsum[lane] : 0u;
+        uint32_t x = lane < NW ? wsum[lane] : 0u;
         uint32_t xi = x;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const uint32_t t = __shfl_up(xi, o, 64);
             if (lane >= o) xi += t;
         }
-        if (lane < kSelWaves) wsum[lane] = xi - x;
-        if (lane == kSelWaves - 1) wsum[kSelWaves] = xi;
+        if (lane < NW) wsum[lane] = xi - x;
+        if (lane == NW - 1) wsum[NW] = xi;
     }
     __syncthreads();
     const uint32_t r = wsum[wave] + incl - v;
-    *total = wsum[kSelWaves];
+    *total = wsum[NW];
     __syncthreads();
     return r;
+}
+
+// Bin b of an 11-bit histogram h with (count above b) < want <= (count at
+// or above b), scanning from the top bin down; want >= 1 and at most the
+// histogram total.  Whole workgroup (NT threads); every thread gets the bin
+// and the count above it.  info: 2 words, wsum: NT/64 + 1 words.
+template <int NT>
+__device__ void find_bin(const uint32_t* h, uint32_t want, uint32_t* wsum, uint32_t* info, uint32_t* bin,
+                         uint32_t* above) {
+    constexpr int BPT = kHistBins / NT;  // bins per thread, descending from the top
+    const int t = threadIdx.x;
+    uint32_t c[BPT];
+    uint32_t local = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        c[i] = h[kHistBins - 1 - BPT * t - i];
+        local += c[i];
+    }
+    uint32_t tot;
+    const uint32_t excl = block_excl_scan<NT>(local, wsum, &tot);
+    if (excl < want && want <= excl + local) {
+        uint32_t cum = excl;
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            if (cum < want && want <= cum + c[i]) {
+                info[0] = (uint32_t)(kHistBins - 1 - BPT * t - i);
+                info[1] = cum;
+            }
+            cum += c[i];
+        }
+    }
+    __syncthreads();
+    *bin = info[0];
+    *above = info[1];
+    __syncthreads();
+}
+
+// The same search by one wave over an LDS histogram: lane l owns the 32
+// bins just below 2048 - 32 l; no barrier.  Writes (bin, above) to out.
+__device__ void find_bin_wave(const uint32_t* h, uint32_t want, uint32_t* out) {
+    const int lane = threadIdx.x & 63;
+    const u32x4* hb = reinterpret_cast<const u32x4*>(h + kHistBins - 32 * (lane + 1));
+    uint32_t c[32];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const u32x4 v = hb[q];
+        c[4 * q] = v[0];
+        c[4 * q + 1] = v[1];
+        c[4 * q + 2] = v[2];
+        c[4 * q + 3] = v[3];
+    }
+    uint32_t local = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) local += c[i];
+    uint32_t incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+    }
+    const uint32_t excl = incl - local;
+    if (excl < want && want <= incl) {
+        uint32_t cum = excl;
+#pragma unroll
+        for (int i = 31; i >= 0; --i) {  // bin 2048 - 32 lane - 32 + i, from the top down
+            if (cum < want && want <= cum + c[i]) {
+                out[0] = (uint32_t)(kHistBins - 32 * (lane + 1) + i);
+                out[1] = cum;
+            }
+            cum += c[i];
+        }
+    }
+}
+
+// Keys [j_begin, j_end) of a query, KPT per thread per batch, all of a
+// batch's loads issued before any is used; f(j, key) for each.
+template <int NT, int KPT, typename F>
+__device__ __forceinline__ void for_keys(const uint32_t* keys, int64_t j_begin, int64_t j_end, F f) {
+    for (int64_t j0 = j_begin; j0 < j_end; j0 += (int64_t)NT * KPT) {  // uniform trip count
+        uint32_t kv[KPT];
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const int64_t j = j0 + (int64_t)u * NT + threadIdx.x;
+            kv[u] = j < j_end ? keys[j] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) f(j0 + (int64_t)u * NT + threadIdx.x, kv[u]);
+    }
+}
+
+// One workgroup per query's histogram block.
+__global__ __launch_bounds__(256) void idx_zero_kernel(u32x4* p) {
+    u32x4* q = p + (int64_t)blockIdx.x * (kHistStride / 4);
+    for (int i = threadIdx.x; i < kHistStride / 4; i += 256) q[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// Append the val[u] with sel[u] (KPT per lane) to list (counter cnt): one
+// atomic per wave.  Every lane of the wave must call it.
+template <int KPT, typename T>
+__device__ __forceinline__ void wave_append(T* list, uint32_t* cnt, const bool (&sel)[KPT], const T (&val)[KPT]) {
+    const int lane = threadIdx.x & 63;
+    uint32_t c = 0;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) c += sel[u] ? 1u : 0u;
+    uint32_t incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+    }
+    const uint32_t tot = (uint32_t)__shfl((int)incl, 63, 64);
+    if (tot == 0) return;  // wave-uniform
+    uint32_t base = 0;
+    if (lane == 63) base = atomicAdd(cnt, tot);
+    uint32_t p = (uint32_t)__shfl((int)base, 63, 64) + incl - c;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+        if (sel[u]) list[p++] = val[u];
 }
 
 // Wave 0 finds the digit d with below(d) < r <= below(d) + cnt[d] over 256
@@ -338,148 +489,187 @@ __device__ __forceinline__ uint64_t rank_value(uint32_t key, int64_t j) {
     return ((uint64_t)(~key) << 32) | (uint64_t)j;
 }
 
-__global__ __launch_bounds__(kSelThreads) void idx_topk_kernel(const IndexerArgs a) {
-    __shared__ uint32_t hist[kHistBins];
-    __shared__ uint64_t cand[kBoundaryCap];
+// Refine, on the score grid: every workgroup of a query lists its entries
+// above the level-1 threshold bin b1 (list A) and in it (list B) and adds
+// the level-2 histogram of b1.  (Handing the lists to one workgroup inside
+// this kernel would need device-scope release fences, which write back the
+// L2 of the issuing XCD: the kernel boundary does that once.)
+__global__ __launch_bounds__(256) void idx_refine_kernel(const IndexerArgs a) {
+    __shared__ uint32_t h2[kHistBins];
+    __shared__ uint32_t wsum[5];
+    __shared__ uint32_t info[2];
+    constexpr int NT = 256, KPT = 8;
+    const int64_t bq = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int64_t nvis = query_nvis(a, bq);
+    const int k = a.k;
+    const int64_t j_begin = (int64_t)blockIdx.x * a.chunk;
+    if (nvis <= k || j_begin >= nvis) return;
+    const int64_t j_end = min(nvis, j_begin + a.chunk);
+    const uint32_t* keys = a.keys + bq * a.N;
+    uint32_t* qh = a.hist + bq * kHistStride;
+    uint32_t* cnt = qh + 2 * kHistBins;  // [0] list A, [1] list B
+    uint32_t* list_a = a.cand_a + bq * kTopkCap;
+    uint64_t* list_b = a.cand_b + bq * kCandCap;
+    for (int i = tid; i < kHistBins; i += NT) h2[i] = 0u;
+    uint32_t b1, a1;
+    find_bin<NT>(qh, (uint32_t)k, wsum, info, &b1, &a1);  // (syncs, so h2 is clear)
+    const uint32_t nb1 = qh[b1];
+    const bool fits = nb1 <= (uint32_t)kCandCap, level2 = nb1 > kSmallBin;  // uniform
+
+    // ---- this workgroup's entries
+    for (int64_t j0 = j_begin; j0 < j_end; j0 += (int64_t)NT * KPT) {  // uniform trip count
+        uint32_t kv[KPT], jv[KPT];
+        uint64_t rv[KPT];
+        bool sa[KPT], sb[KPT];
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const int64_t j = j0 + (int64_t)u * NT + tid;
+            jv[u] = (uint32_t)j;
+            kv[u] = j < j_end ? keys[j] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const bool in = (int64_t)j0 + (int64_t)u * NT + tid < j_end;
+            const uint32_t top = kv[u] >> 21;
+            sa[u] = in && top > b1;
+            sb[u] = in && top == b1;
+            rv[u] = rank_value(kv[u], jv[u]);
+            if (level2 && sb[u]) atomicAdd(&h2[(kv[u] >> 10) & (kHistBins - 1)], 1u);
+        }
+        wave_append<KPT>(list_a, cnt, sa, jv);
+        if (fits) wave_append<KPT>(list_b, cnt + 1, sb, rv);
+    }
+    if (level2) {
+        __syncthreads();
+        flush_hist(h2, qh + kHistBins, NT);
+    }
+}
+
+// Select: one workgroup per query takes list A, the entries of B above the
+// level-2 threshold bin, and the best of the ones in that bin (or, at level
+// 1, of all of B) by (key, lower index first), then writes the k winners in
+// index order.  If b1 holds more than kCandCap keys, a radix select over the
+// whole key array replaces the lists.
+constexpr int kSelThreads = 1024;
+constexpr int kBndCap = 4096;  // boundary entries ranked in LDS
+
+__global__ __launch_bounds__(kSelThreads) void idx_select_kernel(const IndexerArgs a) {
+    __shared__ uint32_t hs[2 * kHistBins];
+    __shared__ uint64_t bnd[kBndCap];
     __shared__ uint32_t bits[kBitmapWords];
-    __shared__ uint32_t wsum[kSelWaves + 1];
+    __shared__ uint32_t win[kTopkCap];
+    __shared__ uint32_t cnt256[256];
+    __shared__ uint32_t wsum[kSelThreads / 64 + 1];
     __shared__ uint32_t info[16];
+    constexpr int NT = kSelThreads, KPT = kCandCap / kSelThreads;
     const int64_t bq = blockIdx.x;
     const int tid = threadIdx.x;
     const int64_t nvis = query_nvis(a, bq);
     const int k = a.k;
     int32_t* out = a.idx + bq * k;
     if (nvis <= k) {  // every visible entry is selected
-        for (int i = tid; i < k; i += kSelThreads) out[i] = i < nvis ? i : -1;
+        for (int i = tid; i < k; i += NT) out[i] = i < nvis ? i : -1;
         return;
     }
     const uint32_t* keys = a.keys + bq * a.N;
-
-    // ---- 1. threshold guess from a strided sample of the keys: the sample's
-    //         want-th best key, to 22 bits (two 11-bit histogram levels)
-    for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = 0u;
-    if (tid < 16) info[tid] = 0u;
+    const uint32_t* qh = a.hist + bq * kHistStride;
+    const uint32_t* list_a = a.cand_a + bq * kTopkCap;
+    const uint64_t* list_b = a.cand_b + bq * kCandCap;
+    // both histogram levels into LDS with one batch of loads
+    static_assert(2 * kHistBins == 4 * NT, "histogram staging: one u32x4 per thread");
+    reinterpret_cast<u32x4*>(hs)[tid] = reinterpret_cast<const u32x4*>(qh)[tid];
+    if (tid < 8) info[tid] = 0u;
     __syncthreads();
-    const int64_t S = nvis < 16384 ? nvis : 16384;
-    // aim at ~1.5 k keys plus a margin at or above the threshold
-    const uint32_t want = (uint32_t)(((1.5 * k) * (double)S) / (double)nvis) + 24u;
-    uint32_t t22 = 0u;  // keys with (key >> 10) >= t22 are collected
-    {
-        // all of this thread's sample loads are issued before any histogram update
-        uint32_t sk[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int64_t i = tid + (int64_t)u * kSelThreads;
-            sk[u] = i < S ? keys[(i * nvis) / S] : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-            if (tid + (int64_t)u * kSelThreads < S) atomicAdd(&hist[sk[u] >> 21], 1u);
-        __syncthreads();
-        // bins from the top: thread t owns bins 2047-2t, 2046-2t; info[0] = the
-        // bin where the running count reaches want, info[2] = samples above it
-        const uint32_t h0 = hist[kHistBins - 1 - 2 * tid], h1 = hist[kHistBins - 2 - 2 * tid];
-        uint32_t tot;
-        const uint32_t excl = block_excl_scan(h0 + h1, wsum, &tot);
-        if (excl < want && want <= excl + h0) {
-            info[0] = (uint32_t)(kHistBins - 1 - 2 * tid);
-            info[2] = excl;
-        } else if (excl + h0 < want && want <= excl + h0 + h1) {
-            info[0] = (uint32_t)(kHistBins - 2 - 2 * tid);
-            info[2] = excl + h0;
-        }
-        __syncthreads();
-        if (tot >= want) {  // else the sample is too thin: take everything (t22 = 0)
-            const uint32_t tbin = info[0];
-            const uint32_t want2 = want - info[2];
-            for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = 0u;
-            __syncthreads();
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-                if (tid + (int64_t)u * kSelThreads < S && (sk[u] >> 21) == tbin)
-                    atomicAdd(&hist[(sk[u] >> 10) & (kHistBins - 1)], 1u);
-            __syncthreads();
-            const uint32_t g0 = hist[kHistBins - 1 - 2 * tid], g1 = hist[kHistBins - 2 - 2 * tid];
-            uint32_t tot2;
-            const uint32_t ex2 = block_excl_scan(g0 + g1, wsum, &tot2);
-            if (ex2 < want2 && want2 <= ex2 + g0 + g1)
-                info[1] = (uint32_t)(kHistBins - 1 - 2 * tid - (ex2 + g0 >= want2 ? 0 : 1));
-            __syncthreads();
-            t22 = (tbin << 11) | info[1];
-            __syncthreads();
-            if (tid == 0) info[1] = 0u;
-            __syncthreads();
-        }
+    // wave 0 finds both threshold bins (level 2 only where it was built)
+    if (tid < 64) {
+        find_bin_wave(hs, (uint32_t)k, info + 8);
+        const uint32_t b = (uint32_t)__shfl((int)info[8], 0, 64), ab = (uint32_t)__shfl((int)info[9], 0, 64);
+        if (hs[b] > kSmallBin && hs[b] <= (uint32_t)kCandCap) find_bin_wave(hs + kHistBins, (uint32_t)k - ab, info + 10);
     }
+    __syncthreads();
+    const uint32_t b1 = info[8], a1 = info[9];
+    const uint32_t nb1 = hs[b1];
+    const bool fits = nb1 <= (uint32_t)kCandCap, level2 = nb1 > kSmallBin;
 
-    // ---- 2. collect every key in a bin >= tbin (coalesced pass over the keys;
-    //         eight 16-byte loads per thread in flight per batch)
-    constexpr int BATCH = 8;
-    const bool vec_ok = (reinterpret_cast<uintptr_t>(keys) & 15u) == 0;
-    for (int64_t j0 = 0; j0 < nvis; j0 += (int64_t)kSelThreads * 4 * BATCH) {
-        u32x4 kv[BATCH];
+    // winners' entry indices go to win[0..k)
+    if (fits) {
+        const uint32_t b2 = level2 ? info[10] : 0u, a2 = level2 ? info[11] : 0u;
+        for (uint32_t i = tid; i < a1; i += NT) win[i] = list_a[i];
+        for (uint32_t i0 = 0; i0 < nb1; i0 += NT * KPT) {
+            uint64_t rv[KPT];
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const int64_t j = j0 + ((int64_t)u * kSelThreads + tid) * 4;
-            if (vec_ok && j + 3 < nvis) {
-                kv[u] = *reinterpret_cast<const u32x4*>(keys + j);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) kv[u][e] = (j + e < nvis) ? keys[j + e] : 0u;
+            for (int u = 0; u < KPT; ++u) {
+                const uint32_t i = i0 + u * NT + tid;
+                rv[u] = i < nb1 ? list_b[i] : 0u;
             }
-        }
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const int64_t j = j0 + ((int64_t)u * kSelThreads + tid) * 4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (j + e < nvis && (kv[u][e] >> 10) >= t22) {
+            for (int u = 0; u < KPT; ++u) {
+                if (i0 + u * NT + tid >= nb1) continue;
+                const uint32_t key = ~(uint32_t)(rv[u] >> 32), j = (uint32_t)(rv[u] & 0xffffffffu);
+                const uint32_t lo = (key >> 10) & (kHistBins - 1);
+                if (level2 && lo > b2) {
+                    win[a1 + atomicAdd(&info[0], 1u)] = j;
+                } else if (!level2 || lo == b2) {
                     const uint32_t p = atomicAdd(&info[1], 1u);
-                    if (p < (uint32_t)kBoundaryCap) cand[p] = rank_value(kv[u][e], j + e);
+                    if (p < (uint32_t)kBndCap) bnd[p] = rv[u];
                 }
             }
         }
+        __syncthreads();
+        const uint32_t above = a1 + a2, nb = info[1];
+        const uint32_t need = (uint32_t)k - above;  // 1 .. nb
+        if (need >= nb) {  // (then nb <= k <= kBndCap... or all of them win)
+            if (nb <= (uint32_t)kBndCap) {
+                for (uint32_t i = tid; i < nb; i += NT) win[above + i] = (uint32_t)(bnd[i] & 0xffffffffu);
+            } else {
+                for (uint32_t i = tid; i < nb1; i += NT) {
+                    const uint64_t v = list_b[i];
+                    const uint32_t lo = (~(uint32_t)(v >> 32) >> 10) & (kHistBins - 1);
+                    if (!level2 || lo == b2) win[above + atomicAdd(&info[2], 1u)] = (uint32_t)(v & 0xffffffffu);
+                }
+            }
+        } else if (nb <= (uint32_t)kBndCap) {
+            for (uint32_t i = tid; i < nb; i += NT) {
+                const uint64_t v = bnd[i];
+                uint32_t r = 0;
+                for (uint32_t l = 0; l < nb; ++l) r += bnd[l] < v ? 1u : 0u;
+                if (r < need) win[above + r] = (uint32_t)(v & 0xffffffffu);  // ranks are distinct
+            }
+        } else {  // a crowded bin: radix select straight from list B
+            auto get = [&](int64_t i, uint64_t* v) {
+                *v = list_b[i];
+                return !level2 || ((~(uint32_t)(*v >> 32) >> 10) & (kHistBins - 1)) == b2;
+            };
+            const uint64_t vth = radix_select_u64((int64_t)nb1, need, 63, 0, get, cnt256, info + 4);
+            for (uint32_t i = tid; i < nb1; i += NT) {
+                uint64_t v;
+                if (get(i, &v) && v <= vth) win[above + atomicAdd(&info[2], 1u)] = (uint32_t)(v & 0xffffffffu);
+            }
+        }
+    } else {
+        const uint64_t vth = radix_select_u64(nvis, (uint32_t)k, 63, 0,
+                                              [&](int64_t i, uint64_t* v) { *v = rank_value(keys[i], i); return true; },
+                                              cnt256, info + 4);
+        for (int64_t j = tid; j < nvis; j += NT)
+            if (rank_value(keys[j], j) <= vth) win[atomicAdd(&info[2], 1u)] = (uint32_t)j;
     }
     __syncthreads();
-    const uint32_t nc = info[1];
-    const bool fast = nc >= (uint32_t)k && nc <= (uint32_t)kBoundaryCap;
 
-    // ---- 3. exact k-th best in rank order
-    uint64_t vth;
-    if (fast) {
-        vth = radix_select_u64((int64_t)nc, (uint32_t)k, 63, 0,
-                               [&](int64_t i, uint64_t* v) { *v = cand[i]; return true; }, hist, info + 4);
-    } else {
-        vth = radix_select_u64(nvis, (uint32_t)k, 63, 0,
-                               [&](int64_t i, uint64_t* v) { *v = rank_value(keys[i], i); return true; }, hist,
-                               info + 4);
-    }
-
-    // ---- 4. winners (rank value <= vth), written in index order
+    // winners in index order
     if (nvis <= (int64_t)kBitmapWords * 32) {
         const int words = (int)((nvis + 31) / 32);
-        for (int i = tid; i < words; i += kSelThreads) bits[i] = 0u;
+        for (int i = tid; i < words; i += NT) bits[i] = 0u;
         __syncthreads();
-        if (fast) {
-            for (uint32_t i = tid; i < nc; i += kSelThreads) {
-                const uint64_t v = cand[i];
-                if (v <= vth) {
-                    const uint32_t j = (uint32_t)(v & 0xffffffffu);
-                    atomicOr(&bits[j >> 5], 1u << (j & 31));
-                }
-            }
-        } else {
-            for (int64_t j = tid; j < nvis; j += kSelThreads)
-                if (rank_value(keys[j], j) <= vth) atomicOr(&bits[j >> 5], 1u << (j & 31));
-        }
+        for (int i = tid; i < k; i += NT) atomicOr(&bits[win[i] >> 5], 1u << (win[i] & 31));
         __syncthreads();
         // each thread owns a contiguous run of words
-        const int per = (words + kSelThreads - 1) / kSelThreads;
+        const int per = (words + NT - 1) / NT;
         const int w0 = tid * per, w1 = min(words, w0 + per);
         uint32_t c = 0;
         for (int i = w0; i < w1; ++i) c += __builtin_popcount(bits[i]);
         uint32_t tot;
-        uint32_t pos = block_excl_scan(c, wsum, &tot);
+        uint32_t pos = block_excl_scan<NT>(c, wsum, &tot);
         for (int i = w0; i < w1; ++i) {
             uint32_t bw = bits[i];
             while (bw) {
@@ -489,38 +679,42 @@ __global__ __launch_bounds__(kSelThreads) void idx_topk_kernel(const IndexerArgs
             }
         }
     } else {
-        // wide entry range: gather the k winners and sort them by index
-        uint32_t* srt = reinterpret_cast<uint32_t*>(bits);  // k <= 4096 <= 8192 words
+        // wide entry range: sort the k winners by index (k <= 4096 <= 8192 words)
+        uint32_t* srt = bits;
         int n2 = 1;
         while (n2 < k) n2 <<= 1;
-        for (int i = tid; i < n2; i += kSelThreads) srt[i] = 0xffffffffu;
-        if (tid == 0) info[3] = 0u;
-        __syncthreads();
-        if (fast) {
-            for (uint32_t i = tid; i < nc; i += kSelThreads) {
-                const uint64_t v = cand[i];
-                if (v <= vth) srt[atomicAdd(&info[3], 1u)] = (uint32_t)(v & 0xffffffffu);
-            }
-        } else {
-            for (int64_t j = tid; j < nvis; j += kSelThreads)
-                if (rank_value(keys[j], j) <= vth) srt[atomicAdd(&info[3], 1u)] = (uint32_t)j;
-        }
+        for (int i = tid; i < n2; i += NT) srt[i] = i < k ? win[i] : 0xffffffffu;
         __syncthreads();
         bitonic_sort_u32(srt, n2);
-        for (int i = tid; i < k; i += kSelThreads) out[i] = (int32_t)srt[i];
+        for (int i = tid; i < k; i += NT) out[i] = (int32_t)srt[i];
     }
 }
 
+// Workspace: score keys [BQ][N], histograms [BQ][kHistStride], lists A
+// [BQ][kTopkCap] (entry indices) and B [BQ][kCandCap] (rank values), each
+// region 256-byte aligned.
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 size_t indexer_workspace_bytes(int64_t BQ, int64_t N, int32_t k) {
     (void)k;
-    return ((size_t)BQ * (size_t)N * 4 + 255) & ~(size_t)255;  // score keys
+    return al256((size_t)BQ * (size_t)N * 4) + al256((size_t)BQ * kHistStride * 4) +
+           al256((size_t)BQ * kTopkCap * 4) + al256((size_t)BQ * kCandCap * 8);
 }
 
 int launch_indexer_topk(IndexerArgs& a, int64_t BQ, bool fp8_mode, void* ws, hipStream_t stream) {
     if (BQ == 0) return 0;
-    a.keys = reinterpret_cast<uint32_t*>(ws);
+    uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+    a.keys = reinterpret_cast<uint32_t*>(w);
+    w += al256((size_t)BQ * (size_t)a.N * 4);
+    a.hist = reinterpret_cast<uint32_t*>(w);
+    w += al256((size_t)BQ * kHistStride * 4);
+    a.cand_a = reinterpret_cast<uint32_t*>(w);
+    w += al256((size_t)BQ * kTopkCap * 4);
+    a.cand_b = reinterpret_cast<uint64_t*>(w);
     dim3 g1((unsigned)a.n_chunks, (unsigned)BQ);
     if (a.N > 0) {
+        static_assert(kHistStride % 4 == 0, "histogram block in 16-byte units");
+        hipLaunchKernelGGL(idx_zero_kernel, dim3((unsigned)BQ), dim3(256), 0, stream, reinterpret_cast<u32x4*>(a.hist));
         if (fp8_mode) {
             if (a.HI == 64 && a.dI == 128) hipLaunchKernelGGL((idx_score_fp8_kernel<2, 8>), g1, dim3(256), 0, stream, a);
             else if (a.HI == 32 && a.dI == 128) hipLaunchKernelGGL((idx_score_fp8_kernel<1, 8>), g1, dim3(256), 0, stream, a);
@@ -530,9 +724,9 @@ int launch_indexer_topk(IndexerArgs& a, int64_t BQ, bool fp8_mode, void* ws, hip
         } else {
             hipLaunchKernelGGL(idx_score_f32_kernel, g1, dim3(256), 0, stream, a);
         }
-        if (hipGetLastError() != hipSuccess) return -4;
+        hipLaunchKernelGGL(idx_refine_kernel, g1, dim3(256), 0, stream, a);
     }
-    hipLaunchKernelGGL(idx_topk_kernel, dim3((unsigned)BQ), dim3(kSelThreads), 0, stream, a);
+    hipLaunchKernelGGL(idx_select_kernel, dim3((unsigned)BQ), dim3(kSelThreads), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return -4;
     return 0;
 }

@@ -124,6 +124,29 @@ def test_indexer_fp32_bit_exact_sizes(N, k, Q):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("tied", [3000, 10000])
+def test_indexer_fp32_tied_block_at_threshold(tied):
+    """A block of entries with one exact score straddles the k-th place: the
+    tie at the boundary is broken by the lower index, through the boundary
+    radix select (3000 tied) or the whole-array select (10000 tied)."""
+    say(f"indexer fp32 tied block {tied}")
+    rng = np.random.default_rng(tied)
+    B, Q, HI, dI, m, N, k = 1, 2, 8, 32, 4, 20000, 1024
+    q = rng.standard_normal((B, Q, HI, dI)).astype(np.float32)
+    wgt = np.abs(rng.standard_normal((B, Q, HI))).astype(np.float32)
+    keys = rng.standard_normal((B, N, dI)).astype(np.float32)
+    qpos = np.full((B, Q), 4 * N, dtype=np.int32)
+    q[0, 1] = q[0, 0]
+    wgt[0, 1] = wgt[0, 0]
+    scores, _ = oracle.indexer_scores(q, wgt, qpos, m, k_f32=keys)
+    j700 = int(np.argsort(-scores[0].astype(np.float64), kind="stable")[700])
+    pos = rng.choice(N, size=tied, replace=False)
+    keys[0, pos] = keys[0, j700]
+    ref = oracle.indexer_topk(q, wgt, qpos, m, k, k_f32=keys)
+    got = cakv.indexer_topk(_d(q), _d(wgt), _d(keys), None, _d(qpos), m, k).cpu().numpy().reshape(ref.shape)
+    assert np.array_equal(got, ref)
+
+
 def _recall_check(got, ref, scores, nvis, k):
     recalls, worst_gap = [], 0.0
     for r in range(ref.shape[0]):
