@@ -69,7 +69,7 @@ int attn_splits(int64_t BQ, int64_t max_slots) {
 size_t attn_workspace(int64_t BQ, int32_t H, int32_t D, int64_t max_slots) {
     const int S = attn_splits(BQ, max_slots);
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    return al((size_t)BQ * S * H * D * 4) + al((size_t)BQ * S * H * 2 * 4);
+    return al((size_t)BQ * S * ((H + 1) / 2) * D * 4) + al((size_t)BQ * S * H * 2 * 4);
 }
 
 int check_attn_common(const cakv_attn_params* p, const void* q, const void* kv_c, const void* kv_raw,
@@ -147,9 +147,9 @@ int run_attn(cakv::AttnArgs& a, int64_t BQ, int32_t H, int32_t D, int64_t max_sl
     REQUIRE(ws_bytes >= need, CAKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
     REQUIRE(ws && (reinterpret_cast<uintptr_t>(ws) & 255u) == 0, CAKV_EWORKSPACE,
             "workspace must be non-NULL and 256-byte aligned");
-    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_o = reinterpret_cast<uint32_t*>(ws);
     a.part_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) +
-                                         (((size_t)BQ * S * H * D * 4 + 255) & ~(size_t)255));
+                                         (((size_t)BQ * S * ((H + 1) / 2) * D * 4 + 255) & ~(size_t)255));
     a.n_splits = S;
     return rc_from(cakv::launch_mqa_fwd(a, BQ, D, act_f32, reinterpret_cast<hipStream_t>(stream)));
 }

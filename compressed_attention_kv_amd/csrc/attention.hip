@@ -252,8 +252,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
 
     // Four tile buffers in a ring: at step it, buffer it%4 holds the tile
     // being multiplied, (it+1)%4 gets its row scales and rotation, (it+2)%4
-    // and (it+3)%4 are still landing.  Before the tile loop the four buffers
-    // stage the query heads (one 32-head block per wave).
+    // and (it+3)%4 are still landing.
     __shared__ __attribute__((aligned(16))) uint8_t ring[4][BUF];
     __shared__ TileMeta meta[MS];
     __shared__ __attribute__((aligned(16))) float invs[MS][TK];  // 1/rms of each row (0: empty slot)
@@ -261,6 +260,8 @@ void mqa_fwd_kernel(const AttnArgs a) {
     __shared__ float2 qcs[kMaxRopePairs];
     __shared__ double turns[kMaxRopePairs];
     __shared__ float gkv_s[D];
+    __shared__ float gq_s[D];
+    __shared__ __attribute__((aligned(16))) float il_s[4][32];  // 1/l of each head (epilogue)
     __shared__ uint32_t dummy[64];    // write target of inactive rotation items
     __shared__ uint32_t redo;
 
@@ -334,6 +335,17 @@ void mqa_fwd_kernel(const AttnArgs a) {
     };
 
     // ---------------------------------------------------------------- prologue
+    // The query rows are requested first; while they and the first tiles'
+    // entry indices are in flight, wave 0 fills the rotation tables.  Then
+    // the first three tiles start landing and Q~ is built in registers.
+    const bool has_heads = 32 * wave < H;
+    const int qhead = 32 * wave + lrow;
+    typename LD::raw_t qr[KSTEPS];  // lane: head qhead, channels 16 s + 8 lh + (0..7)
+    {
+        const TIn* qrow = reinterpret_cast<const TIn*>(a.q) + (bq * H + (qhead < H ? qhead : 0)) * (int64_t)D + 8 * lh;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) qr[s] = qhead < H ? LD::load(qrow + 16 * s) : LD::zero();
+    }
     if (wave == 0 && lane < n_pairs) {
         const double tn = rope_turns(a.rope_base, lane, a.rope_dims);
         turns[lane] = tn;
@@ -341,81 +353,74 @@ void mqa_fwd_kernel(const AttnArgs a) {
         sincos_turns((double)g.t * tn, &sn, &cs);
         qcs[lane] = make_float2(cs, sn);
     }
-    for (int i = tid; i < D; i += 256) gkv_s[i] = a.gamma_kv ? a.gamma_kv[i] : 1.0f;
-    // metadata of the first four tiles and the indices of the fifth
+    for (int i = tid; i < D; i += 256) {
+        gkv_s[i] = a.gamma_kv ? a.gamma_kv[i] : 1.0f;
+        gq_s[i] = a.gamma_q ? a.gamma_q[i] : 1.0f;
+    }
+    // metadata of the first four tiles and the indices of the fifth (the
+    // entry-index loads are all issued before any is used)
     auto meta_start = [&]() __attribute__((always_inline)) {
         if (wave == 0) {
+            const int ol = opaque_tid() & 63;
+            int32_t j[5];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int ol = opaque_tid() & 63;
+            for (int k = 0; k < 5; ++k) {
                 const int t = tile0 + k;
-                const int32_t j = (SPARSE && ol < TK && t < tile1) ? slot_entry<SPARSE>(a, g, bq, t * TK + ol) : 0;
-                tile_meta(t, k, j);
+                j[k] = (SPARSE && ol < TK && t < tile1) ? slot_entry<SPARSE>(a, g, bq, t * TK + ol) : 0;
             }
-            if (SPARSE) {
-                const int ol = opaque_tid() & 63;
-                const int t = tile0 + 4;
-                idxs[4][ol] = (ol < TK && t < tile1) ? slot_entry<SPARSE>(a, g, bq, t * TK + ol) : 0;
-            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) tile_meta(tile0 + k, k, j[k]);
+            if (SPARSE) idxs[4][ol] = j[4];
         }
     };
+    // the first three tiles start landing; T0 is prepared once it has
+    auto start_tiles = [&]() __attribute__((always_inline)) {
+        if (tile0 < tile1) tile_load(0, ring[0]);
+        if (tile0 + 1 < tile1) tile_load(1, ring[1]);
+        if (tile0 + 2 < tile1) tile_load(2, ring[2]);
+    };
     meta_start();
-    barrier_vm<0>();
+    barrier_vm<0>();  // (the query rows have landed too)
+    start_tiles();
 
     // Q~ = RoPE_t(gamma_q * q / rms(q)) * softmax scale * log2(e), with the
     // KV gain gamma_kv folded into the unrotated channels (the rotated ones
-    // carry it on the key side); bf16.  Wave w stages its 32 heads in ring
-    // buffer w (row = head).  Query rows are read eight heads at a time so
-    // that eight loads are in flight per lane.
-    const bool has_heads = 32 * wave < H;
-    {
-        uint8_t* qstage = ring[wave];
-        constexpr int QB = 8;
-        for (int h0 = 0; h0 < 32; h0 += QB) {
-            typename LD::raw_t qr[QB];
-#pragma unroll
-            for (int u = 0; u < QB; ++u) {
-                const int head = 32 * wave + h0 + u;  // heads >= H are staged as zeros
-                const TIn* qrow = reinterpret_cast<const TIn*>(a.q) + (bq * H + (head < H ? head : 0)) * (int64_t)D;
-                qr[u] = (lane < G && head < H) ? LD::load(qrow + 8 * lane) : LD::zero();
-            }
-#pragma unroll
-            for (int u = 0; u < QB; ++u) {
-                const int hh = h0 + u;
-                float v[8];
-                LD::to_f32(qr[u], v);
-                float ss = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
-                ss = wave_sum_uniform(ss);
-                const float inv = __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps) * a.scale_log2;
-                if (lane < G) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) v[i] *= inv * (a.gamma_q ? a.gamma_q[8 * lane + i] : 1.0f);
-                    if (8 * lane >= rope_lo) {
-#pragma unroll
-                        for (int i = 0; i < 8; i += 2) {
-                            const float2 c = qcs[(8 * lane + i - rope_lo) >> 1];
-                            const float x0 = v[i], x1 = v[i + 1];
-                            v[i] = x0 * c.x - x1 * c.y;
-                            v[i + 1] = x0 * c.y + x1 * c.x;
-                        }
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) v[i] *= gkv_s[8 * lane + i];
-                    }
-                    u32x4 w4 = {OP::pack(v[0], v[1]), OP::pack(v[2], v[3]), OP::pack(v[4], v[5]), OP::pack(v[6], v[7])};
-                    *reinterpret_cast<u32x4*>(qstage + hh * RS + 16 * lane) = w4;
-                }
-            }
-        }
-    }
-    barrier_lds();
+    // carry it on the key side), in the B-operand layout of the QK MFMAs:
+    // lane (head lrow, half lh) holds channels 16 s + 8 lh + (0..7) for
+    // k-step s, so a head's sum of squares is this lane's plus lane l ^ 32's.
     opvec qf[KSTEPS];
     {
-        const uint8_t* qrow = ring[wave] + lrow * RS;
+        float ss = 0.0f;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const opvec*>(qrow + 16 * (2 * s + lh));
+        for (int s = 0; s < KSTEPS; ++s) {
+            float v[8];
+            LD::to_f32(qr[s], v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
+        }
+        ss = xor32_sum(ss);
+        const float inv = __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps) * a.scale_log2;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+            float v[8];
+            LD::to_f32(qr[s], v);
+            const int d0 = 16 * s + 8 * lh;
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                const int d = d0 + i;
+                const float x0 = v[i] * inv * gq_s[d], x1 = v[i + 1] * inv * gq_s[d + 1];
+                if (d >= rope_lo) {  // rope_dims is even: pairs never straddle rope_lo
+                    const float2 c = qcs[(d - rope_lo) >> 1];
+                    v[i] = x0 * c.x - x1 * c.y;
+                    v[i + 1] = x0 * c.y + x1 * c.x;
+                } else {
+                    v[i] = x0 * gkv_s[d];
+                    v[i + 1] = x1 * gkv_s[d + 1];
+                }
+            }
+            qf[s] = __builtin_bit_cast(opvec, u32x4{OP::pack(v[0], v[1]), OP::pack(v[2], v[3]),
+                                                     OP::pack(v[4], v[5]), OP::pack(v[6], v[7])});
+        }
     }
 
     // ---------------------------------------------------------------- tile prep
@@ -864,7 +869,6 @@ void mqa_fwd_kernel(const AttnArgs a) {
         barrier_vm<NU>();
     };
 
-    barrier_lds();  // every wave has read its Q~ block: the ring is free
     for (int pass = 0; pass < 2; ++pass) {
         active = has_heads && (pass == 0 || flagged);
         if (pass == 1) {
@@ -875,6 +879,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
             }
             meta_start();
             barrier_vm<0>();
+            start_tiles();
         }
         if (active) {
 #pragma unroll
@@ -882,10 +887,6 @@ void mqa_fwd_kernel(const AttnArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
         }
-        // the first three tiles start landing; T0 is prepared once it has
-        if (tile0 < tile1) tile_load(0, ring[0]);
-        if (tile0 + 1 < tile1) tile_load(1, ring[1]);
-        if (tile0 + 2 < tile1) tile_load(2, ring[2]);
         if (tile0 + 2 < tile1) barrier_vm<2 * NU>();
         else if (tile0 + 1 < tile1) barrier_vm<NU>();
         else barrier_vm<0>();
@@ -911,77 +912,104 @@ void mqa_fwd_kernel(const AttnArgs a) {
     if (!has_heads) return;
 
     // ---------------------------------------------------------------- epilogue
-    // (max, sum, unnormalised O) of this split; the combine kernel folds in
-    // the sink, normalises, rotates back and stores.
-    const int head = 32 * wave + lrow;
+    // (max, sum) of this split and its output normalised by its own sum, O/l
+    // (a convex combination of normalised rows, so fp16 holds it), with the
+    // heads of an even/odd pair packed in one word.  The combine kernel folds
+    // in the sink, merges the splits, rotates back and stores.
+    // (lane indices re-derived here: nothing lane-dependent stays live across the loop)
+    const int el = opaque_tid() & 63, erow = el & 31, eh = el >> 5;
+    const int head = 32 * wave + erow;
     const int S = a.n_splits;
     const int64_t base = (bq * S + split) * (int64_t)H;
-    if (lane < 32 && head < H) {
-        a.part_ml[(base + head) * 2] = m_use;
-        a.part_ml[(base + head) * 2 + 1] = l_run;
+    if (el < 32) {
+        if (head < H) {
+            a.part_ml[(base + head) * 2] = m_use;
+            a.part_ml[(base + head) * 2 + 1] = l_run;
+        }
+        il_s[wave][erow] = l_run > 0.0f ? 1.0f / l_run : 0.0f;
     }
+    f32x4 il[4];  // 1/l of this lane's accumulator rows 8 (r/4) + 4 eh + r%4
+#pragma unroll
+    for (int m = 0; m < 4; ++m) il[m] = *reinterpret_cast<const f32x4*>(&il_s[wave][8 * m + 4 * eh]);
+    const int64_t pbase = (bq * S + split) * (int64_t)((H + 1) >> 1);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int hr = 32 * wave + 8 * (r >> 2) + 4 * lh + (r & 3);
-            if (hr < H) a.part_o[(base + hr) * D + 32 * dt + lrow] = acc[dt][r];
+        for (int r = 0; r < 16; r += 2) {
+            const int hr = 32 * wave + 8 * (r >> 2) + 4 * eh + (r & 3);  // even
+            if (hr < H)
+                a.part_o[(pbase + (hr >> 1)) * D + 32 * dt + erow] =
+                    pack_f16x2(acc[dt][r] * il[r >> 2][r & 3], acc[dt][r + 1] * il[r >> 2][(r & 3) + 1]);
         }
 }
 
-// Merge split partials: one workgroup per (query, head), one thread per
+// Merge split partials: one workgroup per (query, head pair), one thread per
 // channel pair (so the inverse rotation of a pair stays in one thread).
 template <int D>
 __global__ __launch_bounds__(256) void mqa_combine_kernel(const AttnArgs a) {
-    const int64_t bqh = blockIdx.x;
-    const int H = a.H;
-    const int64_t bq = bqh / H;
-    const int h = (int)(bqh % H);
+    const int H = a.H, Hp = (H + 1) >> 1;
+    const int64_t bq = blockIdx.x / Hp;
+    const int hp = (int)(blockIdx.x % Hp);
     const int S = a.n_splits;
     const int pr = threadIdx.x;  // pair index
     if (2 * pr >= D) return;
+    const int nh = (2 * hp + 1 < H) ? 2 : 1;
     const float LOG2E = 1.4426950408889634f;
-    const float z = a.sinks[h] * LOG2E;
-    float M = z;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_ml[((bq * S + s) * H + h) * 2]);
-    float o0 = 0.0f, o1 = 0.0f, Z = 0.0f;
-    if (M != -INFINITY) {
-        Z = __builtin_amdgcn_exp2f(z - M);
-        for (int s = 0; s < S; ++s) {
-            const int64_t base = (bq * S + s) * H + h;
-            const float ms = a.part_ml[base * 2];
-            if (ms == -INFINITY) continue;
-            const float e = __builtin_amdgcn_exp2f(ms - M);
-            Z += e * a.part_ml[base * 2 + 1];
-            const float2 ov = *reinterpret_cast<const float2*>(a.part_o + base * D + 2 * pr);
-            o0 = __builtin_fmaf(e, ov.x, o0);
-            o1 = __builtin_fmaf(e, ov.y, o1);
+    float M[2], Z[2], o[2][2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int h = 2 * hp + (e < nh ? e : 0);
+        M[e] = a.sinks[h] * LOG2E;
+        for (int s = 0; s < S; ++s) M[e] = fmaxf(M[e], a.part_ml[((bq * S + s) * H + h) * 2]);
+        Z[e] = M[e] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(a.sinks[h] * LOG2E - M[e]);
+        o[e][0] = o[e][1] = 0.0f;
+    }
+    for (int s = 0; s < S; ++s) {
+        const uint2 wv = *reinterpret_cast<const uint2*>(a.part_o + ((bq * S + s) * Hp + hp) * (int64_t)D + 2 * pr);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            if (e >= nh) continue;
+            const int64_t mi = ((bq * S + s) * H + 2 * hp + e) * 2;
+            const float ms = a.part_ml[mi];
+            if (ms == -INFINITY || M[e] == -INFINITY) continue;
+            const float wl = __builtin_amdgcn_exp2f(ms - M[e]) * a.part_ml[mi + 1];
+            Z[e] += wl;
+            const float v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(e ? wv.x >> 16 : wv.x & 0xffffu));
+            const float v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(e ? wv.y >> 16 : wv.y & 0xffffu));
+            o[e][0] = __builtin_fmaf(wl, v0, o[e][0]);
+            o[e][1] = __builtin_fmaf(wl, v1, o[e][1]);
         }
-        o0 /= Z;
-        o1 /= Z;
     }
     const int rope_lo = D - a.rope_dims;
-    if (2 * pr < rope_lo && a.gamma_kv) {  // the unrotated channels' KV gain (kept out of the key tiles)
-        o0 *= a.gamma_kv[2 * pr];
-        o1 *= a.gamma_kv[2 * pr + 1];
-    }
+    float sn = 0.0f, cs = 1.0f;
     if (2 * pr >= rope_lo) {
         int32_t t = a.q_pos[bq];
         t = t < 0 ? 0 : t;
-        float sn, cs;
         sincos_turns(-(double)t * rope_turns(a.rope_base, (2 * pr - rope_lo) >> 1, a.rope_dims), &sn, &cs);
-        const float x0 = o0, x1 = o1;
-        o0 = x0 * cs - x1 * sn;
-        o1 = x0 * sn + x1 * cs;
     }
-    const int64_t off = (bq * H + h) * (int64_t)D + 2 * pr;
-    if (a.out_f32) {
-        *reinterpret_cast<float2*>(reinterpret_cast<float*>(a.out) + off) = make_float2(o0, o1);
-    } else {
-        reinterpret_cast<uint32_t*>(a.out)[off >> 1] = f32_to_bf16_bits(o0) | (f32_to_bf16_bits(o1) << 16);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        if (e >= nh) continue;
+        const int h = 2 * hp + e;
+        float o0 = Z[e] > 0.0f ? o[e][0] / Z[e] : 0.0f, o1 = Z[e] > 0.0f ? o[e][1] / Z[e] : 0.0f;
+        if (2 * pr < rope_lo && a.gamma_kv) {  // the unrotated channels' KV gain (kept out of the key tiles)
+            o0 *= a.gamma_kv[2 * pr];
+            o1 *= a.gamma_kv[2 * pr + 1];
+        }
+        if (2 * pr >= rope_lo) {
+            const float x0 = o0, x1 = o1;
+            o0 = x0 * cs - x1 * sn;
+            o1 = x0 * sn + x1 * cs;
+        }
+        const int64_t off = (bq * H + h) * (int64_t)D + 2 * pr;
+        if (a.out_f32) {
+            *reinterpret_cast<float2*>(reinterpret_cast<float*>(a.out) + off) = make_float2(o0, o1);
+        } else {
+            reinterpret_cast<uint32_t*>(a.out)[off >> 1] = f32_to_bf16_bits(o0) | (f32_to_bf16_bits(o1) << 16);
+        }
+        if (pr == 0 && a.lse)
+            a.lse[bq * H + h] = (M[e] == -INFINITY) ? -INFINITY : (M[e] + __builtin_log2f(Z[e])) * 0.6931471805599453f;
     }
-    if (pr == 0 && a.lse)
-        a.lse[bq * H + h] = (M == -INFINITY) ? -INFINITY : (M + __builtin_log2f(Z)) * 0.6931471805599453f;
 }
 
 template <int D, bool SPARSE, typename TIn>
@@ -989,8 +1017,8 @@ static int launch_one(const AttnArgs& a, int64_t BQ, hipStream_t stream) {
     dim3 grid((unsigned)a.n_splits, (unsigned)BQ);
     hipLaunchKernelGGL((mqa_fwd_kernel<D, SPARSE, TIn>), grid, dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return -4;
-    hipLaunchKernelGGL((mqa_combine_kernel<D>), dim3((unsigned)(BQ * a.H)), dim3(D / 2 < 64 ? 64 : D / 2), 0,
-                       stream, a);
+    hipLaunchKernelGGL((mqa_combine_kernel<D>), dim3((unsigned)(BQ * ((a.H + 1) / 2))), dim3(D / 2 < 64 ? 64 : D / 2),
+                       0, stream, a);
     if (hipGetLastError() != hipSuccess) return -4;
     return 0;
 }

@@ -28,7 +28,7 @@ struct AttnArgs {
     const float* gamma_kv;
     void* out;
     float* lse;
-    float* part_o;   // [BQ][S][H][D]   split partial outputs (S > 1)
+    uint32_t* part_o;  // [BQ][S][(H+1)/2][D] split outputs O/l, fp16, heads (2p, 2p+1) in one word
     float* part_ml;  // [BQ][S][H][2]   split partial (max, sum), max in log2 units
     int64_t Q;
     int64_t N;
