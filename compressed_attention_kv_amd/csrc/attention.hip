@@ -55,6 +55,14 @@ struct ActLoad<bf16_t> {
             v[2 * i + 1] = bf16_bits_to_f32(r[i] >> 16);
         }
     }
+    static __device__ __forceinline__ float sumsq(const raw_t& r, float acc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bf16x2_t w2 = word_as_bf16x2(r[i]);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(w2, w2, acc, false);
+        }
+        return acc;
+    }
 };
 
 template <>
@@ -80,6 +88,14 @@ struct ActLoad<float> {
             v[i] = r.a[i];
             v[4 + i] = r.b[i];
         }
+    }
+    static __device__ __forceinline__ float sumsq(const raw_t& r, float acc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc = __builtin_fmaf(r.a[i], r.a[i], acc);
+            acc = __builtin_fmaf(r.b[i], r.b[i], acc);
+        }
+        return acc;
     }
 };
 
@@ -147,6 +163,17 @@ __device__ __forceinline__ void sincos_turns_fast(double x, float* s_out, float*
     const float f = (float)(x - __builtin_floor(x));
     *s_out = __builtin_amdgcn_sinf(f);
     *c_out = __builtin_amdgcn_cosf(f);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (linear id mod 8).
+// xcd_order maps linear ids to an order in which contiguous ranges sit on
+// one XCD, so that consecutive work items (the splits of a query, the head
+// pairs of a query in the combine) share that XCD's L2.  A bijection on
+// [0, total).
+__device__ __forceinline__ int64_t xcd_order(int64_t lin, int64_t total) {
+    const int64_t q = total >> 3, rem = total & 7;
+    const int64_t x = lin & 7, r = lin >> 3;
+    return x < rem ? x * (q + 1) + r : rem * (q + 1) + (x - rem) * q + r;
 }
 
 // Per-tile row metadata, written four tiles ahead by wave 0.
@@ -257,10 +284,10 @@ void mqa_fwd_kernel(const AttnArgs a) {
     __shared__ TileMeta meta[MS];
     __shared__ __attribute__((aligned(16))) float invs[MS][TK];  // 1/rms of each row (0: empty slot)
     __shared__ int32_t idxs[MS][64];  // sparse: entry indices of a tile (lanes >= TK unused)
-    __shared__ float2 qcs[kMaxRopePairs];
+    __shared__ __attribute__((aligned(16))) float2 qcs[kMaxRopePairs];
     __shared__ double turns[kMaxRopePairs];
     __shared__ float gkv_s[D];
-    __shared__ float gq_s[D];
+    __shared__ __attribute__((aligned(16))) float fq_s[D];  // gamma_q, times gamma_kv on unrotated channels
     __shared__ __attribute__((aligned(16))) float il_s[4][32];  // 1/l of each head (epilogue)
     __shared__ uint32_t dummy[64];    // write target of inactive rotation items
     __shared__ uint32_t redo;
@@ -270,8 +297,9 @@ void mqa_fwd_kernel(const AttnArgs a) {
     const int lane = tid & 63;
     const int lrow = lane & 31;
     const int lh = lane >> 5;
-    const int64_t bq = blockIdx.y;
-    const int split = blockIdx.x;
+    const int64_t wg = xcd_order(blockIdx.x + (int64_t)gridDim.x * blockIdx.y, (int64_t)gridDim.x * gridDim.y);
+    const int64_t bq = wg / a.n_splits;
+    const int split = (int)(wg % a.n_splits);
     const int H = a.H;
     const int rope_lo = D - a.rope_dims;
     const int n_pairs = a.rope_dims >> 1;
@@ -354,8 +382,9 @@ void mqa_fwd_kernel(const AttnArgs a) {
         qcs[lane] = make_float2(cs, sn);
     }
     for (int i = tid; i < D; i += 256) {
-        gkv_s[i] = a.gamma_kv ? a.gamma_kv[i] : 1.0f;
-        gq_s[i] = a.gamma_q ? a.gamma_q[i] : 1.0f;
+        const float gkv = a.gamma_kv ? a.gamma_kv[i] : 1.0f;
+        gkv_s[i] = gkv;
+        fq_s[i] = (a.gamma_q ? a.gamma_q[i] : 1.0f) * (i < rope_lo ? gkv : 1.0f);
     }
     // metadata of the first four tiles and the indices of the fifth (the
     // entry-index loads are all issued before any is used)
@@ -392,30 +421,43 @@ void mqa_fwd_kernel(const AttnArgs a) {
     {
         float ss = 0.0f;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-            float v[8];
-            LD::to_f32(qr[s], v);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
-        }
+        for (int s = 0; s < KSTEPS; ++s) ss = LD::sumsq(qr[s], ss);
         ss = xor32_sum(ss);
         const float inv = __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps) * a.scale_log2;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
             float v[8];
             LD::to_f32(qr[s], v);
-            const int d0 = 16 * s + 8 * lh;
+            const int d0 = 16 * s + 8 * lh;  // this lane's 8-channel chunk
+            const f32x4 f0 = *reinterpret_cast<const f32x4*>(&fq_s[d0]);
+            const f32x4 f1 = *reinterpret_cast<const f32x4*>(&fq_s[d0 + 4]);
 #pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                const int d = d0 + i;
-                const float x0 = v[i] * inv * gq_s[d], x1 = v[i + 1] * inv * gq_s[d + 1];
-                if (d >= rope_lo) {  // rope_dims is even: pairs never straddle rope_lo
-                    const float2 c = qcs[(d - rope_lo) >> 1];
-                    v[i] = x0 * c.x - x1 * c.y;
-                    v[i + 1] = x0 * c.y + x1 * c.x;
-                } else {
-                    v[i] = x0 * gkv_s[d];
-                    v[i + 1] = x1 * gkv_s[d + 1];
+            for (int i = 0; i < 4; ++i) {
+                v[i] *= inv * f0[i];
+                v[4 + i] *= inv * f1[i];
+            }
+            // which channels of k-step s rotate is the same for the whole
+            // wave (both halves) unless the boundary falls inside the step
+            if (16 * s >= rope_lo && (rope_lo & 7) == 0) {  // uniform: four pairs per lane
+                const f32x4 c01 = *reinterpret_cast<const f32x4*>(&qcs[(d0 - rope_lo) >> 1]);
+                const f32x4 c23 = *reinterpret_cast<const f32x4*>(&qcs[((d0 - rope_lo) >> 1) + 2]);
+                const float cs[4] = {c01[0], c01[2], c23[0], c23[2]}, sn[4] = {c01[1], c01[3], c23[1], c23[3]};
+#pragma unroll
+                for (int pi = 0; pi < 4; ++pi) {
+                    const float x0 = v[2 * pi], x1 = v[2 * pi + 1];
+                    v[2 * pi] = x0 * cs[pi] - x1 * sn[pi];
+                    v[2 * pi + 1] = x0 * sn[pi] + x1 * cs[pi];
+                }
+            } else if (16 * s + 16 > rope_lo) {  // uniform: the step holding the boundary, pair by pair
+#pragma unroll
+                for (int pi = 0; pi < 4; ++pi) {
+                    const int d = d0 + 2 * pi;
+                    const bool rot = d >= rope_lo;  // rope_dims is even: pairs never straddle it
+                    const float2 c = qcs[rot ? (d - rope_lo) >> 1 : 0];
+                    const float cs = rot ? c.x : 1.0f, sn = rot ? c.y : 0.0f;
+                    const float x0 = v[2 * pi], x1 = v[2 * pi + 1];
+                    v[2 * pi] = x0 * cs - x1 * sn;
+                    v[2 * pi + 1] = x0 * sn + x1 * cs;
                 }
             }
             qf[s] = __builtin_bit_cast(opvec, u32x4{OP::pack(v[0], v[1]), OP::pack(v[2], v[3]),
@@ -948,8 +990,9 @@ void mqa_fwd_kernel(const AttnArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) void mqa_combine_kernel(const AttnArgs a) {
     const int H = a.H, Hp = (H + 1) >> 1;
-    const int64_t bq = blockIdx.x / Hp;
-    const int hp = (int)(blockIdx.x % Hp);
+    const int64_t wg = xcd_order(blockIdx.x, gridDim.x);
+    const int64_t bq = wg / Hp;
+    const int hp = (int)(wg % Hp);
     const int S = a.n_splits;
     const int pr = threadIdx.x;  // pair index
     if (2 * pr >= D) return;
