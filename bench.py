@@ -5,14 +5,18 @@ position 131072 over 32768 compressed entries (m=4) with fp8 indexer keys,
 top-1024 selection, then sparse MQA (128 heads x 512) over the selection plus
 the 128-token raw window and the sinks.  One step = indexer_topk +
 sparse_mqa_fwd for the batch, inputs resident in HBM.  Other workloads
-(--workload): csa_decode_1m, hca_decode_1m (dense_compressed_mqa_fwd only).
+(--workload): csa_decode_1m, hca_decode_1m (dense_compressed_mqa_fwd only),
+prefill_chunk_256k (CSA + HCA layers of an 8192-token prefill chunk after a
+262,144-token prefix: the chunk's three compressions into the caches, the
+indexer, sparse attention, dense attention).
 
-The timed region cycles through several copies of the caches so that the
-256 MiB Infinity Cache cannot hold a step's working set between steps.
+Decode steps cycle through several copies of the caches so that the 256 MiB
+Infinity Cache cannot hold a step's working set between steps.
 
-Prints one JSON line (metric, value, roofline of the dominant kernel call,
-CPU-oracle baseline).  --gpus N with N > 1 is not supported: this build runs
-on one GPU.
+Prints one JSON line: the metric, the roofline of the dominant kernel (its
+launches timed with HIP events recorded by the library around that kernel,
+inside the timed region) and the CPU-oracle baseline.  --gpus N with N > 1 is
+not supported: this build runs on one GPU.
 """
 from __future__ import annotations
 
@@ -38,41 +42,40 @@ BF16_PEAK_TFS = 2500.0
 CACHE_BYTES = 256 << 20
 
 
-def _alg_bytes_indexer(w) -> int:
-    # per query: fp8 keys + per-entry scales of every visible entry, the
-    # indexer query heads (bf16), head weights (f32), the k output indices
-    nv = min(w.t // w.m, w.N)
-    return nv * w.dI + nv * 4 + w.HI * w.dI * 2 + w.HI * 4 + w.k * 4
+def _nvis(w, t) -> int:
+    return min(t // w.m, w.N) if w.N else t // w.m
 
 
-def _alg_bytes_attention(w, sparse: bool) -> int:
-    nv = min(w.t // w.m, w.N)
-    rows = (w.k if sparse else nv) + w.n_win
-    return rows * w.D * 2 + w.H * w.D * 2 * 2 + (w.k * 4 if sparse else 0) + w.H * 4
+# ---------------------------------------------------------------- algorithmic work per query
+def _indexer_score(w, nv: int):
+    """bytes, flops of scoring one query: fp8 keys + scales of every visible
+    entry, the indexer query heads (bf16) and head weights (f32)."""
+    return nv * w.dI + nv * 4 + w.HI * w.dI * 2 + w.HI * 4, 2 * w.HI * w.dI * nv
 
 
-def _alg_flops_attention(w, sparse: bool) -> int:
-    nv = min(w.t // w.m, w.N)
-    rows = (w.k if sparse else nv) + w.n_win
-    return 4 * w.H * w.D * rows
-
-
-def _alg_flops_indexer(w) -> int:
-    nv = min(w.t // w.m, w.N)
-    return 2 * w.HI * w.dI * nv
+def _attention(w, rows: int, sparse: bool):
+    """bytes, flops of one query's attention: the key rows (bf16), q, the
+    output, the indices and the sinks; QK and PV products."""
+    return rows * w.D * 2 + 2 * w.H * w.D * 2 + (w.k * 4 if sparse else 0) + w.H * 4, 4 * w.H * w.D * rows
 
 
 class Step:
-    """Device-resident inputs (several copies of the caches) and one step of the path."""
+    """Device-resident inputs and one step of the path for a workload."""
 
     def __init__(self, name: str):
         self.name = name
+        self.prefill = name.startswith("prefill")
+        self.i = 0
+        (self._init_prefill if self.prefill else self._init_decode)(name)
+
+    # ------------------------------------------------------------ decode
+    def _init_decode(self, name):
         inp = make_inputs(name)
         w = self.w = inp["workload"]
         dev = "cuda"
         self.sparse = w.csa
-        ws_bytes = 0
         nq = w.B * w.Q
+        nv = _nvis(w, w.t)
         if self.sparse:
             # the indexer key cache in fp8 + per-entry scale: kv_compress with
             # m = 1 is exactly the per-entry quantiser
@@ -80,9 +83,21 @@ class Step:
             codes, scale = cakv.kv_compress(kf, torch.zeros(kf.shape[:2], dtype=torch.float32, device=dev), 1,
                                             out_dtype=torch.float8_e4m3fn)
             del kf
-            step_bytes = (_alg_bytes_indexer(w) + _alg_bytes_attention(w, True)) * nq
+            b_s, f_s = _indexer_score(w, nv)
+            b_a, f_a = _attention(w, w.k + w.n_win, True)
+            step_bytes = (b_s + b_a) * nq
+            # kernel -> (algorithmic bytes, flops) per launch
+            self.kernels = {"idx_score_fp8_kernel": (b_s * nq, f_s * nq), "mqa_fwd_kernel": (b_a * nq, f_a * nq),
+                            "idx_select_kernel": (w.k * 4 * nq, 0), "idx_refine_kernel": (nv * 4 * nq, 0),
+                            "mqa_combine_kernel": (2 * w.H * w.D * 2 * nq, 0)}
+            self.calls = {"indexer_topk": (b_s * nq, f_s * nq), "sparse_mqa_fwd": (b_a * nq, f_a * nq)}
         else:
-            step_bytes = _alg_bytes_attention(w, False) * nq
+            b_a, f_a = _attention(w, nv + w.n_win, False)
+            step_bytes = b_a * nq
+            self.kernels = {"mqa_fwd_kernel": (b_a * nq, f_a * nq),
+                            "mqa_combine_kernel": (2 * w.H * w.D * 2 * nq, 0)}
+            self.calls = {"dense_compressed_mqa_fwd": (b_a * nq, f_a * nq)}
+        self.bound = "hbm"
         # enough copies of the caches that one step's data is evicted from the
         # Infinity Cache before the copy is used again
         self.copies = max(1, math.ceil(3 * CACHE_BYTES / step_bytes))
@@ -107,9 +122,68 @@ class Step:
         self.out = torch.empty((w.B, w.Q, w.H, w.D), dtype=torch.bfloat16, device=dev)
         self.kw = dict(m=w.m, n_win=w.n_win, rope_dims=w.rope_dims, rope_base=w.rope_base)
         self.inp = inp
-        self.i = 0
 
+    # ------------------------------------------------------------ prefill
+    def _init_prefill(self, name):
+        inp = make_inputs(name)
+        w = self.w = inp["workload"]
+        dev = "cuda"
+        self.sparse = True
+        self.copies = 1  # a step's working set (q, outputs) is several GB
+        P, T, Q = w.q_pos0, w.T, w.Q
+        assert P % w.m_hca == 0 and T % w.m_hca == 0 and w.B == 1
+        self.P = P
+        self.kv_raw = inp["kv_raw"].to(dev)  # the raw KV of prefix + chunk (window source)
+        self.gate = inp["gate"].to(dev)
+        self.hca_gate = inp["hca_gate"].to(dev)
+        self.k_raw = inp["k_idx"].to(dev)
+        self.k_gate = inp["k_gate"].to(dev)
+        # prefix caches, built once outside the timed region (the chunk's part
+        # is rewritten by every step)
+        self.kvc = cakv.kv_compress(self.kv_raw, self.gate, w.m)
+        self.kvh = cakv.kv_compress(self.kv_raw, self.hca_gate, w.m_hca)
+        self.codes, self.kscale = cakv.kv_compress(self.k_raw, self.k_gate, w.m, out_dtype=torch.float8_e4m3fn)
+        self.q = inp["q"].to(dev)
+        self.q_hca = inp["q_hca"].to(dev)
+        self.q_idx = inp["q_idx"].to(dev)
+        self.wts = inp["w"].to(dev)
+        self.q_pos = inp["q_pos"].to(dev)
+        self.raw_pos0 = inp["raw_pos0"].to(dev)
+        self.sinks = inp["sinks"].to(dev)
+        self.sinks_hca = inp["sinks_hca"].to(dev)
+        N, Nh = T // w.m, T // w.m_hca
+        self.idx = torch.empty((1, Q, w.k), dtype=torch.int32, device=dev)
+        self.ws_idx = torch.empty(cakv.indexer_topk_workspace_bytes(1, Q, N, w.k), dtype=torch.uint8, device=dev)
+        self.ws_csa = torch.empty(cakv.sparse_mqa_workspace_bytes(1, Q, w.H, w.D, w.k, w.n_win), dtype=torch.uint8,
+                                  device=dev)
+        self.ws_hca = torch.empty(cakv.dense_mqa_workspace_bytes(1, Q, w.H, w.D, Nh, w.n_win), dtype=torch.uint8,
+                                  device=dev)
+        self.out = torch.empty((1, Q, w.H, w.D), dtype=torch.bfloat16, device=dev)
+        self.out_hca = torch.empty_like(self.out)
+        self.kw = dict(n_win=w.n_win, rope_dims=w.rope_dims, rope_base=w.rope_base)
+        self.inp = inp
+        # algorithmic work of the whole chunk, summed over its query positions
+        qs = P + np.arange(Q)
+        nv_c, nv_h = qs // w.m, qs // w.m_hca
+        win = np.minimum(qs + 1, w.n_win)
+        f_score = int(np.sum(2 * w.HI * w.dI * nv_c))
+        b_score = N * (w.dI + 4) + Q * (w.HI * w.dI * 2 + w.HI * 4)  # unique bytes: keys, scales, q_I, w
+        rows_c = np.minimum(nv_c, w.k) + win
+        rows_h = nv_h + win
+        f_csa = int(np.sum(4 * w.H * w.D * rows_c))
+        f_hca = int(np.sum(4 * w.H * w.D * rows_h))
+        b_attn = (N + T) * w.D * 2 + 2 * Q * w.H * w.D * 2  # unique: caches, raw KV, q, out
+        self.kernels = {"idx_score_fp8_kernel": (b_score, f_score), "mqa_fwd_kernel#0": (b_attn, f_csa),
+                        "mqa_fwd_kernel#1": ((Nh + T) * w.D * 2 + 2 * Q * w.H * w.D * 2, f_hca)}
+        self.calls = {"kv_compress x3": (0, 0), "indexer_topk": (b_score, f_score),
+                      "sparse_mqa_fwd": (b_attn, f_csa), "dense_compressed_mqa_fwd": (0, f_hca)}
+        self.bound = "mfma"
+
+    # ------------------------------------------------------------ one step
     def run(self, ev=None):
+        (self._run_prefill if self.prefill else self._run_decode)(ev)
+
+    def _run_decode(self, ev):
         c = self.i % self.copies
         self.i += 1
         if ev is not None:
@@ -129,10 +203,47 @@ class Step:
         if ev is not None:
             ev[2].record()
 
+    def _run_prefill(self, ev):
+        w, P = self.w, self.P
+        if ev is not None:
+            ev[0].record()
+        cakv.kv_compress(self.kv_raw[:, P:], self.gate[:, P:], w.m, out=self.kvc[:, P // w.m:])
+        cakv.kv_compress(self.kv_raw[:, P:], self.hca_gate[:, P:], w.m_hca, out=self.kvh[:, P // w.m_hca:])
+        cakv.kv_compress(self.k_raw[:, P:], self.k_gate[:, P:], w.m, out=self.codes[:, P // w.m:],
+                         scale=self.kscale[:, P // w.m:])
+        if ev is not None:
+            ev[1].record()
+        cakv.indexer_topk(self.q_idx, self.wts, self.codes, self.kscale, self.q_pos, w.m, w.k, out=self.idx,
+                          workspace=self.ws_idx)
+        if ev is not None:
+            ev[2].record()
+        cakv.sparse_mqa_fwd(self.q, self.kvc, self.idx, self.kv_raw, self.raw_pos0, self.q_pos, self.sinks, m=w.m,
+                            want_lse=False, out=self.out, workspace=self.ws_csa, **self.kw)
+        if ev is not None:
+            ev[3].record()
+        cakv.dense_compressed_mqa_fwd(self.q_hca, self.kvh, self.kv_raw, self.raw_pos0, self.q_pos, self.sinks_hca,
+                                      m=w.m_hca, want_lse=False, out=self.out_hca, workspace=self.ws_hca, **self.kw)
+        if ev is not None:
+            ev[4].record()
+
+    @property
+    def n_events(self) -> int:
+        return 5 if self.prefill else 3
+
+    def call_ms(self, evs):
+        """Mean duration of each call of the step over the event-timed steps."""
+        names = list(self.calls)
+        if not self.prefill and not self.sparse:
+            return {names[0]: float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))}
+        return {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+
+    # ------------------------------------------------------------ oracle
     def cpu_baseline(self, max_queries: int):
-        """The oracle on the first `n` queries of the same inputs (all host cores)."""
+        """The oracle on a bounded sample of the same inputs (all host cores)."""
         import oracle
         w, inp = self.w, self.inp
+        if self.prefill:
+            return self._cpu_baseline_prefill(oracle, max_queries)
         n = min(max_queries, w.B * w.Q)
         rows = np.arange(n, dtype=np.int64)
         if self.sparse:  # input preparation, outside the timed region
@@ -150,11 +261,44 @@ class Step:
             oracle.attention(inp["q"], inp["kv"], inp["kv_raw"], inp["raw_pos0"], inp["q_pos"], inp["sinks"],
                              rows=rows, **kw)
         dt = time.perf_counter() - t0
-        cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
-        return {"value": n / dt, "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
+        return {"value": n / dt, "unit": "query-tokens/s", "cores": _cores(), "kind": "oracle",
                 "sample": f"{n} of the {w.B * w.Q} queries of {w.name} (oracle indexer + attention)"
                 if self.sparse else f"{n} of the {w.B * w.Q} queries of {w.name} (oracle attention)",
                 "seconds": round(dt, 3)}
+
+    def _cpu_baseline_prefill(self, oracle, max_queries: int):
+        """The oracle's chunk compressions in full, then indexer + both
+        attention layers for the first n query tokens of the chunk."""
+        w, inp, P = self.w, self.inp, self.P
+        n = min(max_queries, w.Q)
+        sl = slice(0, n)
+        kv_chunk, kr_chunk = inp["kv"][:, P:], inp["k_idx"][:, P:]
+        # prefix caches: input preparation, outside the timed region
+        kvc_pre = oracle.kv_compress(inp["kv"][:, :P], inp["gate"][:, :P], w.m)
+        kvh_pre = oracle.kv_compress(inp["kv"][:, :P], inp["hca_gate"][:, :P], w.m_hca)
+        keys_pre = oracle.kv_compress(inp["k_idx"][:, :P], inp["k_gate"][:, :P], w.m)
+        t0 = time.perf_counter()
+        kvc = np.concatenate([kvc_pre, oracle.kv_compress(kv_chunk, inp["gate"][:, P:], w.m)], axis=1)
+        kvh = np.concatenate([kvh_pre, oracle.kv_compress(kv_chunk, inp["hca_gate"][:, P:], w.m_hca)], axis=1)
+        keys = np.concatenate([keys_pre, oracle.kv_compress(kr_chunk, inp["k_gate"][:, P:], w.m)], axis=1)
+        codes, scale = oracle.q8_quantize(keys)
+        idx = oracle.indexer_topk(inp["q_idx"][:, sl], inp["w"][:, sl], inp["q_pos"][:, sl], w.m, w.k,
+                                  k_code=codes, k_scale=scale).reshape(1, n, w.k)
+        kvc_t = torch.from_numpy(kvc).to(torch.bfloat16)
+        kvh_t = torch.from_numpy(kvh).to(torch.bfloat16)
+        oracle.attention(inp["q"][:, sl], kvc_t, inp["kv_raw"], inp["raw_pos0"], inp["q_pos"][:, sl], inp["sinks"],
+                         idx=idx, m=w.m, **self.kw)
+        oracle.attention(inp["q_hca"][:, sl], kvh_t, inp["kv_raw"], inp["raw_pos0"], inp["q_pos"][:, sl],
+                         inp["sinks_hca"], m=w.m_hca, **self.kw)
+        dt = time.perf_counter() - t0
+        return {"value": n / dt, "unit": "query-tokens/s", "cores": _cores(), "kind": "oracle",
+                "sample": f"the chunk's three compressions, then indexer + CSA and HCA attention for the first {n} "
+                          f"of the {w.Q} query tokens of {w.name}",
+                "seconds": round(dt, 3)}
+
+
+def _cores() -> int:
+    return int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
 
 
 def copy_calibration(mib: int):
@@ -170,13 +314,35 @@ def copy_calibration(mib: int):
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
+def _kernel_launches(st: Step, kernel: str, steps: int):
+    """(name, occurrence) of a kernel table entry: 'mqa_fwd_kernel#1' is the
+    second launch of mqa_fwd_kernel in a step."""
+    name, _, occ = kernel.partition("#")
+    per_step = 2 if (st.prefill and name == "mqa_fwd_kernel") else 1
+    return name, int(occ or 0), per_step
+
+
+def _time_kernel(st: Step, kernel: str, steps: int, run_steps):
+    """Mean duration (ms) of one kernel's launches over `steps` steps, from
+    event pairs the library records around them."""
+    name, occ, per_step = _kernel_launches(st, kernel, steps)
+    n = steps * per_step
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    cakv.profile_kernel_events(name, starts, ends)
+    run_steps()
+    torch.cuda.synchronize()
+    cakv.profile_kernel_events(None)
+    return float(np.mean([starts[i].elapsed_time(ends[i]) for i in range(occ, n, per_step)]))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 50; 5 for the prefill chunk)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 5; 2 for the prefill chunk)")
     ap.add_argument("--workload", default="csa_decode_128k",
-                    choices=["csa_decode_128k", "csa_decode_1m", "hca_decode_1m"])
+                    choices=["csa_decode_128k", "csa_decode_1m", "hca_decode_1m", "prefill_chunk_256k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-queries", type=int, default=32)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -189,59 +355,82 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
+    prefill = args.workload.startswith("prefill")
+    steps = args.steps if args.steps is not None else (5 if prefill else 50)
+    warmup = args.warmup if args.warmup is not None else (2 if prefill else 5)
     st = Step(args.workload)
     w = st.w
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         st.run()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    # the dominant kernel: the longest of the step's main kernels on a short probe
+    probe = {k: _time_kernel(st, k, 2, lambda: [st.run() for _ in range(2)]) for k in st.kernels}
+    dom = max(probe, key=probe.get)
+    dom_name, _, per_step = _kernel_launches(st, dom, steps)
+
+    # timed region: `steps` steps; HIP events around each call of the step
+    # and, recorded by the library, around each launch of the dominant kernel
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(st.n_events)] for _ in range(steps)]
+    ks = [torch.cuda.Event(enable_timing=True) for _ in range(steps * per_step)]
+    ke = [torch.cuda.Event(enable_timing=True) for _ in range(steps * per_step)]
+    cakv.profile_kernel_events(dom_name, ks, ke)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         st.run(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    idx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    att_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    ms = wall * 1e3 / args.steps
+    cakv.profile_kernel_events(None)
+    _, occ, _ = _kernel_launches(st, dom, steps)
+    kms = float(np.mean([ks[i].elapsed_time(ke[i]) for i in range(occ, steps * per_step, per_step)]))
+    ms = wall * 1e3 / steps
     nq = w.B * w.Q
     value = nq / (ms * 1e-3)
 
-    # roofline of the dominant call (HBM-bound): algorithmic bytes / its event-timed duration
-    if st.sparse:
-        b_idx = _alg_bytes_indexer(w) * nq
-        b_att = _alg_bytes_attention(w, True) * nq
-        calls = {"indexer_topk": (b_idx, idx_ms, _alg_flops_indexer(w) * nq),
-                 "sparse_mqa_fwd": (b_att, att_ms, _alg_flops_attention(w, True) * nq)}
+    bytes_, flops = st.kernels[dom]
+    if st.bound == "hbm":
+        achieved, peak, unit = bytes_ / (kms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
     else:
-        calls = {"dense_compressed_mqa_fwd": (_alg_bytes_attention(w, False) * nq, att_ms,
-                                              _alg_flops_attention(w, False) * nq)}
-    dom = max(calls, key=lambda c: calls[c][1])
-    bytes_, dms, flops = calls[dom]
-    achieved = bytes_ / (dms * 1e-3) / 1e9
-    per_call = {c: {"ms": round(v[1], 4), "alg_GBps": round(v[0] / (v[1] * 1e-3) / 1e9, 1),
-                    "hbm_frac": round(v[0] / (v[1] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                    "alg_TFLOPs": round(v[2] / (v[1] * 1e-3) / 1e12, 1),
-                    "mfma_frac_bf16": round(v[2] / (v[1] * 1e-3) / 1e12 / BF16_PEAK_TFS, 4)}
-                for c, v in calls.items()}
-    total_bytes = sum(v[0] for v in calls.values())
-    roof_ms = total_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
+        achieved, peak, unit = flops / (kms * 1e-3) / 1e12, BF16_PEAK_TFS, "TFLOP/s"
+    cms = st.call_ms(evs)
+    per_call = {}
+    for c, (b, f) in st.calls.items():
+        d = {"ms": round(cms[c], 4)}
+        if b:
+            d["alg_GBps"] = round(b / (cms[c] * 1e-3) / 1e9, 1)
+            d["hbm_frac"] = round(b / (cms[c] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        if f:
+            d["alg_TFLOPs"] = round(f / (cms[c] * 1e-3) / 1e12, 1)
+            d["mfma_frac_bf16"] = round(f / (cms[c] * 1e-3) / 1e12 / BF16_PEAK_TFS, 4)
+        per_call[c] = d
+    if st.bound == "hbm":
+        roof_ms = sum(b for b, _ in st.calls.values()) / (HBM_PEAK_GBS * 1e9) * 1e3
+    else:
+        roof_ms = sum(f for _, f in st.calls.values()) / (BF16_PEAK_TFS * 1e12) * 1e3
+    if prefill:
+        config = {"workload": w.name, "query_tokens": w.Q, "prefix_tokens": w.q_pos0, "m": w.m, "m_hca": w.m_hca,
+                  "heads": w.H, "head_dim": w.D, "topk": w.k, "window": w.n_win, "indexer_heads": w.HI,
+                  "layers": "CSA + HCA"}
+    else:
+        config = {"workload": w.name, "batch": nq, "context": w.t, "compressed_entries": w.N, "m": w.m,
+                  "heads": w.H, "head_dim": w.D, "topk": w.k if st.sparse else None, "window": w.n_win,
+                  "indexer_heads": w.HI if st.sparse else None, "cache_copies_cycled": st.copies}
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8 keys decoded to bf16 MFMA (indexer), f16 MFMA (attention), fp32 accumulate",
-        "data": "synthetic",
-        "config": {"workload": w.name, "batch": nq, "context": w.t, "compressed_entries": w.N, "m": w.m,
-                   "heads": w.H, "head_dim": w.D, "topk": w.k if st.sparse else None, "window": w.n_win,
-                   "indexer_heads": w.HI if st.sparse else None, "cache_copies_cycled": st.copies},
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "dtype_detail": "bf16 MFMA with fp32 accumulation (indexer: fp8 keys decoded exactly to bf16)",
+        "data": "synthetic", "config": config,
+        "roofline": {"kernel": dom, "bound": st.bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": None, "kernel_ms": round(kms, 4),
+                     "launches_timed": steps},
         "path_roofline_frac": round(roof_ms / ms, 4),
         "per_call": per_call,
+        "kernel_probe_ms": {k: round(v, 4) for k, v in probe.items()},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = st.cpu_baseline(args.cpu_queries)
+        rec["cpu_baseline"] = st.cpu_baseline(args.cpu_queries if not prefill else min(args.cpu_queries, 8))
     print(json.dumps(rec), flush=True)
 
 

@@ -42,7 +42,7 @@ _i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_
 
 EXPORTS = ("cakv_version", "cakv_last_error", "cakv_kv_compress", "cakv_indexer_topk_workspace",
            "cakv_indexer_topk", "cakv_sparse_mqa_workspace", "cakv_sparse_mqa_fwd",
-           "cakv_dense_mqa_workspace", "cakv_dense_compressed_mqa_fwd")
+           "cakv_dense_mqa_workspace", "cakv_dense_compressed_mqa_fwd", "cakv_profile_kernel_events")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -55,6 +55,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     lib.cakv_version.restype = ctypes.c_int
     lib.cakv_last_error.restype = ctypes.c_char_p
+    lib.cakv_profile_kernel_events.argtypes = [ctypes.c_char_p, ctypes.POINTER(_p), ctypes.POINTER(_p), ctypes.c_int]
     lib.cakv_kv_compress.argtypes = [_p, ctypes.c_int, _p, _i64, _i64, _i64, _i32, _p, ctypes.c_int, _p, _p]
     lib.cakv_indexer_topk_workspace.argtypes = [_i64, _i64, _i64, _i32]
     lib.cakv_indexer_topk_workspace.restype = _sz
@@ -97,16 +98,24 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
-def kv_compress(x: torch.Tensor, gate: torch.Tensor, m: int, out_dtype: torch.dtype = None):
+def kv_compress(x: torch.Tensor, gate: torch.Tensor, m: int, out_dtype: torch.dtype = None,
+                out: torch.Tensor = None, scale: torch.Tensor = None):
     """Softmax-gated compression of every m tokens.  x [B,T,D] f32/bf16, gate [B,T] f32.
     Returns out [B,T//m,D] (out_dtype: float32, bfloat16 or float8_e4m3fn) and, for fp8,
-    the per-entry float32 scale [B,T//m]."""
+    the per-entry float32 scale [B,T//m].  `out` / `scale` may be given (contiguous,
+    e.g. the tail of a cache); they are written in place."""
     lib = load_library()
     B, T, D = x.shape
-    out_dtype = out_dtype or x.dtype
+    out_dtype = out.dtype if out is not None else (out_dtype or x.dtype)
     nb = T // m
-    out = torch.empty((B, nb, D), dtype=out_dtype, device=x.device)
-    scale = torch.empty((B, nb), dtype=torch.float32, device=x.device) if out_dtype == torch.float8_e4m3fn else None
+    if out is None:
+        out = torch.empty((B, nb, D), dtype=out_dtype, device=x.device)
+    elif tuple(out.shape) != (B, nb, D) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [{B}, {nb}, {D}] tensor")
+    if out_dtype == torch.float8_e4m3fn and scale is None:
+        scale = torch.empty((B, nb), dtype=torch.float32, device=x.device)
+    elif out_dtype != torch.float8_e4m3fn:
+        scale = None
     _check(lib.cakv_kv_compress(_dev(x, "x"), _DT[x.dtype], _dev(gate, "gate"), B, T, D, m, _dev(out, "out"),
                                 _DT[out_dtype], _dev(scale, "scale"), _stream()))
     return (out, scale) if scale is not None else out
@@ -199,3 +208,20 @@ def dense_compressed_mqa_fwd(q, kv_c, kv_raw, raw_pos0, q_pos, sinks, *, m: int,
 
 def version() -> int:
     return int(load_library().cakv_version())
+
+
+def profile_kernel_events(kernel: str | None, starts=(), ends=()) -> None:
+    """Profiling aid: the library records the given torch.cuda.Event pairs around
+    the next len(starts) launches of `kernel` made from this thread (None clears).
+    The events are created here if they have not been recorded yet."""
+    lib = load_library()
+    n = len(starts)
+    if kernel is None or n == 0:
+        _check(lib.cakv_profile_kernel_events(None, None, None, 0))
+        return
+    for e in list(starts) + list(ends):
+        if e.cuda_event == 0:
+            e.record()
+    arr = (_p * n)
+    _check(lib.cakv_profile_kernel_events(kernel.encode(), arr(*[e.cuda_event for e in starts]),
+                                          arr(*[e.cuda_event for e in ends]), n))

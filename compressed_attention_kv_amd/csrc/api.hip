@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <string>
+#include <vector>
 
 #include "../../include/cakv.h"
 #include "cakv_internal.hpp"
@@ -156,9 +157,41 @@ int run_attn(cakv::AttnArgs& a, int64_t BQ, int32_t H, int32_t D, int64_t max_sl
 
 }  // namespace
 
+namespace cakv {
+
+// Pending kernel-event pairs of the calling thread (cakv_profile_kernel_events).
+struct ProfEvents {
+    std::string kernel;
+    std::vector<hipEvent_t> starts, ends;
+    size_t next = 0;
+};
+thread_local ProfEvents g_prof;
+
+void prof_mark(const char* kernel, bool after, hipStream_t stream) {
+    if (g_prof.next >= g_prof.starts.size() || g_prof.kernel != kernel) return;
+    (void)hipEventRecord(after ? g_prof.ends[g_prof.next] : g_prof.starts[g_prof.next], stream);
+    if (after) ++g_prof.next;
+}
+
+}  // namespace cakv
+
 extern "C" {
 
 int cakv_version(void) { return 100; }
+
+int cakv_profile_kernel_events(const char* kernel, void* const* starts, void* const* ends, int n) {
+    REQUIRE(n >= 0, CAKV_EINVAL, "n=%d must be >= 0", n);
+    cakv::g_prof = cakv::ProfEvents{};
+    if (n == 0 || kernel == nullptr) return ok();
+    REQUIRE(starts && ends, CAKV_EINVAL, "starts and ends must not be NULL when n > 0");
+    for (int i = 0; i < n; ++i) REQUIRE(starts[i] && ends[i], CAKV_EINVAL, "event %d is NULL", i);
+    cakv::g_prof.kernel = kernel;
+    for (int i = 0; i < n; ++i) {
+        cakv::g_prof.starts.push_back(reinterpret_cast<hipEvent_t>(starts[i]));
+        cakv::g_prof.ends.push_back(reinterpret_cast<hipEvent_t>(ends[i]));
+    }
+    return ok();
+}
 
 const char* cakv_last_error(void) { return g_err.c_str(); }
 

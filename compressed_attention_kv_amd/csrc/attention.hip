@@ -1058,10 +1058,14 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(const AttnArgs a) {
 template <int D, bool SPARSE, typename TIn>
 static int launch_one(const AttnArgs& a, int64_t BQ, hipStream_t stream) {
     dim3 grid((unsigned)a.n_splits, (unsigned)BQ);
+    prof_mark("mqa_fwd_kernel", false, stream);
     hipLaunchKernelGGL((mqa_fwd_kernel<D, SPARSE, TIn>), grid, dim3(256), 0, stream, a);
+    prof_mark("mqa_fwd_kernel", true, stream);
     if (hipGetLastError() != hipSuccess) return -4;
+    prof_mark("mqa_combine_kernel", false, stream);
     hipLaunchKernelGGL((mqa_combine_kernel<D>), dim3((unsigned)(BQ * ((a.H + 1) / 2))), dim3(D / 2 < 64 ? 64 : D / 2),
                        0, stream, a);
+    prof_mark("mqa_combine_kernel", true, stream);
     if (hipGetLastError() != hipSuccess) return -4;
     return 0;
 }

@@ -58,6 +58,10 @@ int launch_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B,
 // sparse (idx != NULL) or dense MQA forward; act_f32: inputs are float32
 int launch_mqa_fwd(const AttnArgs& a, int64_t BQ, int D, bool act_f32, hipStream_t stream);
 
+// Profiling aid (cakv_profile_kernel_events): record the calling thread's
+// pending start (after = false) or end event around a launch of `kernel`.
+void prof_mark(const char* kernel, bool after, hipStream_t stream);
+
 struct IndexerArgs {
     const void* q_idx;
     const float* w;

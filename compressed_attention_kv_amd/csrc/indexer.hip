@@ -714,19 +714,29 @@ int launch_indexer_topk(IndexerArgs& a, int64_t BQ, bool fp8_mode, void* ws, hip
     dim3 g1((unsigned)a.n_chunks, (unsigned)BQ);
     if (a.N > 0) {
         static_assert(kHistStride % 4 == 0, "histogram block in 16-byte units");
+        prof_mark("idx_zero_kernel", false, stream);
         hipLaunchKernelGGL(idx_zero_kernel, dim3((unsigned)BQ), dim3(256), 0, stream, reinterpret_cast<u32x4*>(a.hist));
+        prof_mark("idx_zero_kernel", true, stream);
         if (fp8_mode) {
+            if (!((a.HI == 32 || a.HI == 64) && (a.dI == 64 || a.dI == 128))) return -2;
+            prof_mark("idx_score_fp8_kernel", false, stream);
             if (a.HI == 64 && a.dI == 128) hipLaunchKernelGGL((idx_score_fp8_kernel<2, 8>), g1, dim3(256), 0, stream, a);
             else if (a.HI == 32 && a.dI == 128) hipLaunchKernelGGL((idx_score_fp8_kernel<1, 8>), g1, dim3(256), 0, stream, a);
             else if (a.HI == 64 && a.dI == 64) hipLaunchKernelGGL((idx_score_fp8_kernel<2, 4>), g1, dim3(256), 0, stream, a);
-            else if (a.HI == 32 && a.dI == 64) hipLaunchKernelGGL((idx_score_fp8_kernel<1, 4>), g1, dim3(256), 0, stream, a);
-            else return -2;
+            else hipLaunchKernelGGL((idx_score_fp8_kernel<1, 4>), g1, dim3(256), 0, stream, a);
+            prof_mark("idx_score_fp8_kernel", true, stream);
         } else {
+            prof_mark("idx_score_f32_kernel", false, stream);
             hipLaunchKernelGGL(idx_score_f32_kernel, g1, dim3(256), 0, stream, a);
+            prof_mark("idx_score_f32_kernel", true, stream);
         }
+        prof_mark("idx_refine_kernel", false, stream);
         hipLaunchKernelGGL(idx_refine_kernel, g1, dim3(256), 0, stream, a);
+        prof_mark("idx_refine_kernel", true, stream);
     }
+    prof_mark("idx_select_kernel", false, stream);
     hipLaunchKernelGGL(idx_select_kernel, dim3((unsigned)BQ), dim3(kSelThreads), 0, stream, a);
+    prof_mark("idx_select_kernel", true, stream);
     if (hipGetLastError() != hipSuccess) return -4;
     return 0;
 }

@@ -163,6 +163,7 @@ int launch_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B,
 #define CAKV_KC(TIN, OK)                                                                          \
     hipLaunchKernelGGL((kv_compress_kernel<TIN, OK>), dim3((unsigned)grid), dim3(256), 0, stream, \
                        (const TIN*)x, gate, T, (int)D, m, nblk, total, tpe, epw, out, out_scale)
+    prof_mark("kv_compress_kernel", false, stream);
     if (x_dtype == 0) {
         if (out_dtype == 0) CAKV_KC(float, 0);
         else if (out_dtype == 1) CAKV_KC(float, 1);
@@ -173,6 +174,7 @@ int launch_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B,
         else CAKV_KC(bf16_t, 2);
     }
 #undef CAKV_KC
+    prof_mark("kv_compress_kernel", true, stream);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -66,6 +66,18 @@ int cakv_version(void);
 /* Message describing the last error returned on this thread ("" if none). */
 const char* cakv_last_error(void);
 
+/* Profiling aid (not part of the method): for the next n launches, made by
+ * calls on the calling thread, of the kernel whose function name is `kernel`
+ * (one of kv_compress_kernel, idx_zero_kernel, idx_score_fp8_kernel,
+ * idx_score_f32_kernel, idx_refine_kernel, idx_select_kernel, mqa_fwd_kernel,
+ * mqa_combine_kernel), record starts[i] on the call's stream just before the
+ * i-th such launch and ends[i] just after it.  The events are hipEvent_t
+ * handles created and owned by the caller; the library copies the n handles
+ * and keeps them until the n launches have happened or the next call of this
+ * function (n = 0 or kernel = NULL clears them).  Results are unaffected.
+ * Errors: EINVAL (n < 0, or a NULL array or event with n > 0). */
+int cakv_profile_kernel_events(const char* kernel, void* const* starts, void* const* ends, int n);
+
 /* ---------------------------------------------------------------------------
  * kv_compress  [V4 digest, CSA step 1 and HCA paragraph; V4-Pro card: CSA
  * compresses every m=4 tokens, HCA every m'=128, into one KV entry;

@@ -99,3 +99,12 @@ def test_workspace_queries_are_monotone(lib):
     b = lib.cakv_dense_mqa_workspace(32, 1, 128, 512, 8192, 128)
     assert a > 0 and b > 0
     assert lib.cakv_sparse_mqa_workspace(64, 1, 128, 512, 1024, 128) >= a
+
+
+def test_profile_kernel_events_arguments(lib):
+    # n < 0 and NULL event arrays are rejected on the host; n = 0 clears
+    assert lib.cakv_profile_kernel_events(b"mqa_fwd_kernel", None, None, -1) == -1
+    assert lib.cakv_profile_kernel_events(b"mqa_fwd_kernel", None, None, 2) == -1
+    null2 = (ctypes.c_void_p * 2)(None, None)
+    assert lib.cakv_profile_kernel_events(b"mqa_fwd_kernel", null2, null2, 2) == -1
+    assert lib.cakv_profile_kernel_events(None, None, None, 0) == 0

@@ -253,6 +253,64 @@ def test_dense_attention_hca_decode_1m():
     assert np.abs(lse.cpu().numpy().reshape(lse_ref.shape) - lse_ref).max() < 1e-2
 
 
+def test_prefill_chunk_256k_sampled_rows():
+    """The CSA + HCA chunked prefill at full size (8192 query tokens after a
+    262,144-token prefix) in the launch configuration the benchmark times;
+    sampled rows (chunk ends and m / 128-token block boundaries) are checked
+    against the oracle: the compressed caches, the selection (fp8 recall) and
+    both attention layers, each fed the same inputs on both sides."""
+    say("prefill chunk 256K: inputs")
+    inp = make_inputs("prefill_chunk_256k")
+    w = inp["workload"]
+    T, Q = w.T, w.Q
+    rows = np.array([0, 1, 2, 3, 127, 128, 129, 2047, 2048, 4095, 4096, 4097, 6143, 6144,
+                     8060, 8188, 8189, 8190, 8191, 511, 1000, 3333, 5555, 7777], dtype=np.int64)
+    sel = torch.from_numpy(rows)
+    kw = _attn_kw(w)
+
+    # S1 at full size: GPU compression of every raw token against the oracle's
+    say("  kv_compress: CSA (m=4), HCA (m=128), indexer keys (m=4, fp8)")
+    kv_d = _d(inp["kv"])
+    for gate, mm in ((inp["gate"], w.m), (inp["hca_gate"], w.m_hca)):
+        got = cakv.kv_compress(kv_d, _d(gate), mm).float().cpu()
+        ent = torch.tensor([0, 1, T // mm // 2, T // mm - 2, T // mm - 1])
+        ref = oracle.kv_compress(inp["kv"][:, : T // mm * mm].view(1, T // mm, mm, -1)[:, ent].reshape(1, -1, w.D),
+                                 gate[:, : T // mm * mm].view(1, T // mm, mm)[:, ent].reshape(1, -1), mm)
+        diff = np.abs(got[:, ent].numpy() - ref)
+        assert np.all(diff <= 2.0 ** -7 * np.abs(ref) + 1e-6), diff.max()  # one bf16 ulp
+
+    # caches from the oracle, fed to both sides from here on
+    kvc = torch.from_numpy(oracle.kv_compress(inp["kv"], inp["gate"], w.m)).to(torch.bfloat16)
+    kvh = torch.from_numpy(oracle.kv_compress(inp["kv"], inp["hca_gate"], w.m_hca)).to(torch.bfloat16)
+    keys = oracle.kv_compress(inp["k_idx"], inp["k_gate"], w.m)
+    codes, scale = oracle.q8_quantize(keys)
+
+    say("  indexer top-k, 8192 queries x 67,584 entries")
+    idx = cakv.indexer_topk(_d(inp["q_idx"]), _d(inp["w"]), _d(codes), _d(scale), _d(inp["q_pos"]), w.m, w.k)
+    idx_rows = idx[:, sel].cpu().numpy()
+    scores, nvis = oracle.indexer_scores(inp["q_idx"][:, sel], inp["w"][:, sel], inp["q_pos"][:, sel], w.m,
+                                         k_code=codes, k_scale=scale)
+    ref = oracle.topk(scores, nvis, w.k)
+    recall, gap = _recall_check(idx_rows.reshape(ref.shape), ref, scores, nvis, w.k)
+    say(f"  recall {recall:.5f} worst relative gap of a swapped entry {gap:.2e}")
+    assert recall >= 0.995 and gap <= 1e-3
+
+    say("  CSA layer: sparse attention over the selection + window + sinks")
+    out, _ = cakv.sparse_mqa_fwd(_d(inp["q"]), _d(kvc), idx, kv_d, _d(inp["raw_pos0"]), _d(inp["q_pos"]),
+                                 _d(inp["sinks"]), want_lse=False, **kw)
+    ref, _ = oracle.attention(inp["q"][:, sel], kvc, inp["kv_raw"], inp["raw_pos0"], inp["q_pos"][:, sel],
+                              inp["sinks"], idx=idx_rows, **kw)
+    _attn_check(out[:, sel].float().cpu().numpy().reshape(ref.shape), ref, "CSA out")
+
+    say("  HCA layer: dense attention over every visible entry + window + sinks")
+    kwh = dict(kw, m=w.m_hca)
+    out, _ = cakv.dense_compressed_mqa_fwd(_d(inp["q_hca"]), _d(kvh), kv_d, _d(inp["raw_pos0"]), _d(inp["q_pos"]),
+                                           _d(inp["sinks_hca"]), want_lse=False, **kwh)
+    ref, _ = oracle.attention(inp["q_hca"][:, sel], kvh, inp["kv_raw"], inp["raw_pos0"], inp["q_pos"][:, sel],
+                              inp["sinks_hca"], **kwh)
+    _attn_check(out[:, sel].float().cpu().numpy().reshape(ref.shape), ref, "HCA out")
+
+
 def test_attention_edge_cases():
     """Early rows (t < m: window and sink only), an empty key set with a -inf
     sink, K = 0 slots, duplicate-free padding, positions outside the raw rows."""
