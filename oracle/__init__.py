@@ -57,6 +57,8 @@ def _load():
         lib.oracle_indexer_scores.argtypes = [_p, ctypes.c_int, _p, _p, _p, _p, _p, _i64, _i64, _i64,
                                               ctypes.c_int, ctypes.c_int, ctypes.c_int, _p, _i64, _p, _p]
         lib.oracle_topk.argtypes = [_p, _p, _i64, _i64, ctypes.c_int, _p]
+        lib.oracle_kv_prepare.argtypes = [_p, ctypes.c_int, _p, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double, _p]
         lib.oracle_attention.argtypes = [ctypes.POINTER(AttnParams), _p, _p, _p, ctypes.c_int, _p, _p,
                                          _p, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
                                          _i64, _p, _i64, _p, _p]
@@ -174,6 +176,22 @@ def topk(scores: np.ndarray, n_vis: np.ndarray, k: int) -> np.ndarray:
 def indexer_topk(q_idx, w, q_pos, m: int, k: int, k_f32=None, k_code=None, k_scale=None, rows=None):
     s, nv = indexer_scores(q_idx, w, q_pos, m, k_f32=k_f32, k_code=k_code, k_scale=k_scale, rows=rows)
     return topk(s, nv, k)
+
+
+def kv_prepare(kv_c, *, m: int, rope_dims: int, rope_base: float = 10000.0, entry_pos_offset: int = 0,
+               rms_eps: float = 1e-6, gamma_kv=None, j0: int = 0, n=None) -> np.ndarray:
+    """Key/value vectors of compressed entries j0 .. j0+n-1 (all by default):
+    RMSNorm with gamma_kv, the last rope_dims dims rotated by j*m + entry_pos_offset.
+    fp64 [B, n, D]."""
+    lib = _load()
+    ka, kd = _act(kv_c)
+    B, N, D = ka.shape
+    n = N - j0 if n is None else n
+    gk = None if gamma_kv is None else _np(gamma_kv, np.float32)
+    out = np.empty((B, n, D), dtype=np.float64)
+    _check(lib.oracle_kv_prepare(_ptr(ka), kd, _ptr(gk), B, N, D, j0, n, m, rope_dims, rope_base,
+                                 entry_pos_offset, rms_eps, _ptr(out)), "kv_prepare")
+    return out
 
 
 def attention(q, kv_c, kv_raw, raw_pos0, q_pos, sinks, *, idx=None, m: int, n_win: int,

@@ -346,6 +346,32 @@ static void rope(double* x, i64 D, int r, double base, double pos) {
     }
 }
 
+/* The key (= value) vector of compressed entry j, a function of the entry
+ * alone: RMSNorm with gamma_kv, then the trailing r dims rotated by the
+ * entry's position j*m + entry_pos_offset.  [V4-Pro card, "Hybrid
+ * attention": RMSNorm on the single compressed KV head before the dot
+ * product; RoPE on the last 64 dims of each KV entry.]  Entries j0 .. j0+n-1
+ * of each of the B sequences (N entries each); out is [B][n][D].  This is the
+ * same per-entry computation the attention below applies to compressed rows. */
+int oracle_kv_prepare(const void* kv_c, int act_dtype, const float* gamma_kv, i64 B, i64 N, i64 D,
+                      i64 j0, i64 n, int m, int rope_dims, double rope_base, int entry_pos_offset,
+                      double rms_eps, double* out) {
+    if (B < 0 || N < 0 || D < 1 || j0 < 0 || n < 0 || j0 + n > N || m < 1 || rope_dims < 0 ||
+        (rope_dims & 1) || rope_dims > D)
+        return OR_EINVAL;
+    double* tmp = (double*)malloc(sizeof(double) * (size_t)D);
+    for (i64 b = 0; b < B; ++b)
+        for (i64 i = 0; i < n; ++i) {
+            i64 j = j0 + i;
+            for (i64 d = 0; d < D; ++d) tmp[d] = load_elem(kv_c, act_dtype, (b * N + j) * D + d);
+            double* y = out + (b * n + i) * D;
+            rms_normalise(tmp, gamma_kv, D, rms_eps, y);
+            rope(y, D, rope_dims, rope_base, (double)(j * m + entry_pos_offset));
+        }
+    free(tmp);
+    return OR_OK;
+}
+
 /* idx == NULL: dense over all visible entries (HCA); otherwise the K slots
  * of idx (entries that are -1 or not visible are skipped).
  * rows: flattened (b*Q+q) rows to compute, or NULL for all; out is

@@ -432,3 +432,75 @@ def test_attention_softmax_scale_and_gamma_q():
     b, lb = oracle.attention(*args, m=4, n_win=4, rope_dims=8, softmax_scale=2.0 / math.sqrt(D))
     np.testing.assert_allclose(a, b, atol=1e-12)
     np.testing.assert_allclose(la, lb, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# O5 entry preparation (the key half of the Q/K prep step)
+# --------------------------------------------------------------------------
+
+def test_kv_prepare_normalisation_closed_form():
+    """No rotation: y = gamma * x / sqrt(mean(x^2) + eps) (catches a sum in place of a
+    mean, a missing eps or gamma, a wrong row)."""
+    rng = np.random.default_rng(30)
+    B, N, D = 2, 5, 24
+    x = rng.standard_normal((B, N, D)).astype(np.float32)
+    g = rng.uniform(0.5, 2, D).astype(np.float32)
+    y = oracle.kv_prepare(x, m=4, rope_dims=0, gamma_kv=g, rms_eps=0.25)
+    xd = x.astype(np.float64)
+    want = xd / np.sqrt((xd ** 2).mean(axis=-1, keepdims=True) + 0.25) * g
+    np.testing.assert_allclose(y, want, rtol=1e-14, atol=1e-15)
+    # a sub-range of entries is the same slice of the full result
+    np.testing.assert_array_equal(oracle.kv_prepare(x, m=4, rope_dims=0, gamma_kv=g, rms_eps=0.25, j0=2, n=2),
+                                  y[:, 2:4])
+
+
+def test_kv_prepare_rotation_worked_example():
+    """D = 6, r = 4, base 4; entry j = 3 with m = 2 and offset 1 sits at position p = 7: pair
+    (2,3) turns by p * 4^0 = 7 rad, pair (4,5) by p * 4^(-1/2) = 3.5 rad, dims 0,1 stay (catches
+    the wrong pairs, a wrong sign of the angle, a wrong per-pair frequency or position)."""
+    x = np.array([[[0, 0, 0, 0, 0, 0]] * 3 + [[1.0, -2.0, 3.0, 4.0, -1.0, 2.0]]], np.float32)
+    y = oracle.kv_prepare(x, m=2, rope_dims=4, rope_base=4.0, entry_pos_offset=1, rms_eps=0.0)[0, 3]
+    s = math.sqrt((1 + 4 + 9 + 16 + 1 + 4) / 6)
+    a0, a1 = 7.0, 3.5
+    want = np.array([1.0, -2.0,
+                     3.0 * math.cos(a0) - 4.0 * math.sin(a0), 3.0 * math.sin(a0) + 4.0 * math.cos(a0),
+                     -1.0 * math.cos(a1) - 2.0 * math.sin(a1), -1.0 * math.sin(a1) + 2.0 * math.cos(a1)]) / s
+    np.testing.assert_allclose(y, want, atol=1e-14)
+
+
+def test_kv_prepare_pairwise_dots_depend_on_distance_only():
+    """Shifting every entry's position by the same amount leaves all k_i . k_j unchanged
+    while the vectors themselves change (RoPE is relative)."""
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((1, 9, 32)).astype(np.float32)
+    kw = dict(m=4, rope_dims=16, rope_base=100.0)
+    a = oracle.kv_prepare(x, **kw)[0]
+    b = oracle.kv_prepare(x, entry_pos_offset=37, **kw)[0]
+    assert np.abs(a - b).max() > 0.1
+    np.testing.assert_allclose(a @ a.T, b @ b.T, atol=1e-11)
+
+
+def test_kv_prepare_gives_the_attention_keys():
+    """fp64 brute force on a tiny case: softmax attention (with the sink) over the prepared
+    entries reproduces the attention oracle's log-sum-exp and its unrotated output dims.
+    The query vector is prepared by the same rule at position t (m = 1, offset t)."""
+    rng = np.random.default_rng(32)
+    H, D, N, m, r = 3, 16, 7, 4, 8
+    t = m * N + 2
+    q = rng.standard_normal((1, 1, H, D)).astype(np.float32)
+    kv = rng.standard_normal((1, N, D)).astype(np.float32)
+    sinks = rng.standard_normal(H).astype(np.float32)
+    gk = rng.uniform(0.5, 2, D).astype(np.float32)
+    gq = rng.uniform(0.5, 2, D).astype(np.float32)
+    kw = dict(rope_dims=r, rope_base=30.0, rms_eps=1e-6)
+    out, lse = oracle.attention(q, kv, np.zeros((1, 1, D), np.float32), np.array([0], np.int32),
+                                np.array([[t]], np.int32), sinks, m=m, n_win=0, entry_pos_offset=3,
+                                gamma_q=gq, gamma_kv=gk, **kw)
+    keys = oracle.kv_prepare(kv, m=m, entry_pos_offset=3, gamma_kv=gk, **kw)[0]
+    for h in range(H):
+        qh = oracle.kv_prepare(q[:, 0, h:h + 1], m=1, entry_pos_offset=t, gamma_kv=gq, **kw)[0, 0]
+        lg = keys @ qh / math.sqrt(D)
+        z = math.exp(sinks[h]) + np.exp(lg).sum()
+        assert lse[0, h] == pytest.approx(math.log(z), abs=1e-12)
+        o = (np.exp(lg)[:, None] * keys).sum(axis=0) / z
+        np.testing.assert_allclose(out[0, h, :D - r], o[:D - r], atol=1e-12)
