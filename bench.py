@@ -7,8 +7,10 @@ the 128-token raw window and the sinks.  One step = indexer_topk +
 sparse_mqa_fwd for the batch, inputs resident in HBM.  Other workloads
 (--workload): csa_decode_1m, hca_decode_1m (dense_compressed_mqa_fwd only),
 prefill_chunk_256k (CSA + HCA layers of an 8192-token prefill chunk after a
-262,144-token prefix: the chunk's three compressions into the caches, the
-indexer, sparse attention, dense attention).
+262,144-token prefix: the chunk's three compressions into the caches and
+the preparation of its new attention entries and window rows, the indexer,
+sparse attention, dense attention).  Decode caches and window rows hold
+prepared keys (kv_prepare runs once per entry or token, when it is written).
 
 Decode steps cycle through several copies of the caches so that the 256 MiB
 Infinity Cache cannot hold a step's working set between steps.
@@ -102,7 +104,10 @@ class Step:
         # enough copies of the caches that one step's data is evicted from the
         # Infinity Cache before the copy is used again
         self.copies = max(1, math.ceil(3 * CACHE_BYTES / step_bytes))
-        self.kv = [inp["kv"].to(dev) for _ in range(self.copies)]
+        # the resident cache and window rows hold prepared keys (kv_prepare runs
+        # once per entry or token, when it is written; not part of a decode step)
+        self.kv = [cakv.kv_prepare(inp["kv"].to(dev), m=w.m, rope_dims=w.rope_dims, rope_base=w.rope_base)
+                   for _ in range(self.copies)]
         if self.sparse:
             self.kidx = [codes] + [codes.clone() for _ in range(self.copies - 1)]
             self.kscale = [scale] + [scale.clone() for _ in range(self.copies - 1)]
@@ -116,7 +121,8 @@ class Step:
             ws_bytes = cakv.dense_mqa_workspace_bytes(w.B, w.Q, w.H, w.D, w.N, w.n_win)
         self.ws_attn = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
         self.q = inp["q"].to(dev)
-        self.kv_raw = inp["kv_raw"].to(dev)
+        self.kv_raw = cakv.kv_prepare_raw(inp["kv_raw"].to(dev), inp["raw_pos0"].tolist(), rope_dims=w.rope_dims,
+                                          rope_base=w.rope_base)
         self.raw_pos0 = inp["raw_pos0"].to(dev)
         self.q_pos = inp["q_pos"].to(dev)
         self.sinks = inp["sinks"].to(dev)
@@ -143,6 +149,12 @@ class Step:
         # is rewritten by every step)
         self.kvc = cakv.kv_compress(self.kv_raw, self.gate, w.m)
         self.kvh = cakv.kv_compress(self.kv_raw, self.hca_gate, w.m_hca)
+        self.prep = dict(rope_dims=w.rope_dims, rope_base=w.rope_base)
+        cakv.kv_prepare(self.kvc, m=w.m, **self.prep)
+        cakv.kv_prepare(self.kvh, m=w.m_hca, **self.prep)
+        # window rows: the raw tokens prepared at their positions (raw_pos0 = 0)
+        self.kv_win = torch.empty_like(self.kv_raw)
+        cakv.kv_prepare(self.kv_raw, m=1, j0=0, n=P, out=self.kv_win, **self.prep)
         self.codes, self.kscale = cakv.kv_compress(self.k_raw, self.k_gate, w.m, out_dtype=torch.float8_e4m3fn)
         self.q = inp["q"].to(dev)
         self.q_hca = inp["q_hca"].to(dev)
@@ -176,7 +188,7 @@ class Step:
         b_attn = (N + T) * w.D * 2 + 2 * Q * w.H * w.D * 2  # unique: caches, raw KV, q, out
         self.kernels = {"idx_score_fp8_kernel": (b_score, f_score), "mqa_fwd_kernel#0": (b_attn, f_csa),
                         "mqa_fwd_kernel#1": ((Nh + T) * w.D * 2 + 2 * Q * w.H * w.D * 2, f_hca)}
-        self.calls = {"kv_compress x3": (0, 0), "indexer_topk": (b_score, f_score),
+        self.calls = {"kv_compress x3, kv_prepare x3": (0, 0), "indexer_topk": (b_score, f_score),
                       "sparse_mqa_fwd": (b_attn, f_csa), "dense_compressed_mqa_fwd": (0, f_hca)}
         self.bound = "mfma"
 
@@ -212,17 +224,21 @@ class Step:
         cakv.kv_compress(self.kv_raw[:, P:], self.hca_gate[:, P:], w.m_hca, out=self.kvh[:, P // w.m_hca:])
         cakv.kv_compress(self.k_raw[:, P:], self.k_gate[:, P:], w.m, out=self.codes[:, P // w.m:],
                          scale=self.kscale[:, P // w.m:])
+        # the chunk's new attention entries and its tokens' window rows enter prepared
+        cakv.kv_prepare(self.kvc, m=w.m, j0=P // w.m, **self.prep)
+        cakv.kv_prepare(self.kvh, m=w.m_hca, j0=P // w.m_hca, **self.prep)
+        cakv.kv_prepare(self.kv_raw, m=1, j0=P, out=self.kv_win, **self.prep)
         if ev is not None:
             ev[1].record()
         cakv.indexer_topk(self.q_idx, self.wts, self.codes, self.kscale, self.q_pos, w.m, w.k, out=self.idx,
                           workspace=self.ws_idx)
         if ev is not None:
             ev[2].record()
-        cakv.sparse_mqa_fwd(self.q, self.kvc, self.idx, self.kv_raw, self.raw_pos0, self.q_pos, self.sinks, m=w.m,
+        cakv.sparse_mqa_fwd(self.q, self.kvc, self.idx, self.kv_win, self.raw_pos0, self.q_pos, self.sinks, m=w.m,
                             want_lse=False, out=self.out, workspace=self.ws_csa, **self.kw)
         if ev is not None:
             ev[3].record()
-        cakv.dense_compressed_mqa_fwd(self.q_hca, self.kvh, self.kv_raw, self.raw_pos0, self.q_pos, self.sinks_hca,
+        cakv.dense_compressed_mqa_fwd(self.q_hca, self.kvh, self.kv_win, self.raw_pos0, self.q_pos, self.sinks_hca,
                                       m=w.m_hca, want_lse=False, out=self.out_hca, workspace=self.ws_hca, **self.kw)
         if ev is not None:
             ev[4].record()

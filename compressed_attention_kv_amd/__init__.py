@@ -7,6 +7,8 @@ fallback: if the library is missing or no GPU is present, calls raise.
 
 Functions (names follow the C ABI):
   kv_compress(x, gate, m, out_dtype)                      -> out (, scale)
+  kv_prepare(kv_c, m, rope_dims, ...)                     -> prepared entries (in place by default)
+  kv_prepare_raw(kv_raw, raw_pos0, rope_dims, ...)        -> prepared window rows (per-sequence positions)
   indexer_topk(q_idx, w, k_idx, k_scale, q_pos, m, k)     -> idx
   sparse_mqa_fwd(q, kv_c, idx, kv_raw, raw_pos0, q_pos, sinks, ...) -> (out, lse)
   dense_compressed_mqa_fwd(q, kv_c, kv_raw, raw_pos0, q_pos, sinks, ...) -> (out, lse)
@@ -32,15 +34,15 @@ class CakvError(RuntimeError):
 
 class AttnParams(ctypes.Structure):
     _fields_ = [("m", ctypes.c_int32), ("n_win", ctypes.c_int32), ("rope_dims", ctypes.c_int32),
-                ("entry_pos_offset", ctypes.c_int32), ("rope_base", ctypes.c_float),
+                ("rope_base", ctypes.c_float),
                 ("softmax_scale", ctypes.c_float), ("rms_eps", ctypes.c_float),
-                ("gamma_q", ctypes.c_void_p), ("gamma_kv", ctypes.c_void_p)]
+                ("gamma_q", ctypes.c_void_p)]
 
 
 _lib = None
 _i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
 
-EXPORTS = ("cakv_version", "cakv_last_error", "cakv_kv_compress", "cakv_indexer_topk_workspace",
+EXPORTS = ("cakv_version", "cakv_last_error", "cakv_kv_compress", "cakv_kv_prepare", "cakv_indexer_topk_workspace",
            "cakv_indexer_topk", "cakv_sparse_mqa_workspace", "cakv_sparse_mqa_fwd",
            "cakv_dense_mqa_workspace", "cakv_dense_compressed_mqa_fwd", "cakv_profile_kernel_events")
 
@@ -57,6 +59,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.cakv_last_error.restype = ctypes.c_char_p
     lib.cakv_profile_kernel_events.argtypes = [ctypes.c_char_p, ctypes.POINTER(_p), ctypes.POINTER(_p), ctypes.c_int]
     lib.cakv_kv_compress.argtypes = [_p, ctypes.c_int, _p, _i64, _i64, _i64, _i32, _p, ctypes.c_int, _p, _p]
+    lib.cakv_kv_prepare.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _p, _i32, _i32,
+                                    ctypes.c_float, _i32, ctypes.c_float, _p]
     lib.cakv_indexer_topk_workspace.argtypes = [_i64, _i64, _i64, _i32]
     lib.cakv_indexer_topk_workspace.restype = _sz
     lib.cakv_indexer_topk.argtypes = [_p, ctypes.c_int, _p, _p, ctypes.c_int, _p, _p, _i64, _i64, _i64, _i32,
@@ -121,6 +125,36 @@ def kv_compress(x: torch.Tensor, gate: torch.Tensor, m: int, out_dtype: torch.dt
     return (out, scale) if scale is not None else out
 
 
+def kv_prepare(kv_c: torch.Tensor, *, m: int, rope_dims: int, rope_base: float = 10000.0,
+               entry_pos_offset: int = 0, rms_eps: float = 1e-6, gamma_kv=None, j0: int = 0, n: int = None,
+               out: torch.Tensor = None) -> torch.Tensor:
+    """Key/value vectors of compressed entries j0 .. j0+n-1 (all by default) of kv_c [B,N,D]
+    (f32/bf16): RMSNorm with gamma_kv, the last rope_dims dims rotated by j*m + entry_pos_offset.
+    Written into `out` (same shape) or, by default, in place into kv_c; returns it.  The
+    attention calls read compressed entries in this form."""
+    lib = load_library()
+    B, N, D = kv_c.shape
+    n = N - j0 if n is None else n
+    out = kv_c if out is None else out
+    if tuple(out.shape) != (B, N, D) or out.dtype != kv_c.dtype:
+        raise ValueError("out must match kv_c in shape and dtype")
+    _check(lib.cakv_kv_prepare(_dev(kv_c, "kv_c"), _dev(out, "out"), _DT[kv_c.dtype], B, N, D, j0, n,
+                               _dev(gamma_kv, "gamma_kv"), m, rope_dims, rope_base, entry_pos_offset, rms_eps,
+                               _stream()))
+    return out
+
+
+def kv_prepare_raw(kv_raw: torch.Tensor, raw_pos0, *, rope_dims: int, rope_base: float = 10000.0,
+                   rms_eps: float = 1e-6, gamma_kv=None, out: torch.Tensor = None) -> torch.Tensor:
+    """Window rows of kv_raw [B,R,D] prepared at their positions raw_pos0[b] + r
+    (kv_prepare with m = 1, one call per sequence); raw_pos0 is a host sequence of B ints."""
+    out = kv_raw if out is None else out
+    for b, p0 in enumerate(int(v) for v in raw_pos0):
+        kv_prepare(kv_raw[b:b + 1], m=1, rope_dims=rope_dims, rope_base=rope_base, entry_pos_offset=p0,
+                   rms_eps=rms_eps, gamma_kv=gamma_kv, out=out[b:b + 1])
+    return out
+
+
 def indexer_topk_workspace_bytes(B: int, Q: int, N: int, k: int) -> int:
     return int(load_library().cakv_indexer_topk_workspace(B, Q, N, k))
 
@@ -144,9 +178,8 @@ def indexer_topk(q_idx: torch.Tensor, w: torch.Tensor, k_idx: torch.Tensor, k_sc
     return out
 
 
-def _params(m, n_win, rope_dims, rope_base, entry_pos_offset, softmax_scale, rms_eps, gamma_q, gamma_kv):
-    return AttnParams(m, n_win, rope_dims, entry_pos_offset, rope_base, softmax_scale, rms_eps,
-                      _dev(gamma_q, "gamma_q"), _dev(gamma_kv, "gamma_kv"))
+def _params(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, gamma_q):
+    return AttnParams(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, _dev(gamma_q, "gamma_q"))
 
 
 def sparse_mqa_workspace_bytes(B, Q, H, D, K, n_win) -> int:
@@ -158,11 +191,13 @@ def dense_mqa_workspace_bytes(B, Q, H, D, N, n_win) -> int:
 
 
 def sparse_mqa_fwd(q, kv_c, idx, kv_raw, raw_pos0, q_pos, sinks, *, m: int, n_win: int, rope_dims: int,
-                   rope_base: float = 10000.0, entry_pos_offset: int = 0, softmax_scale: float = 0.0,
-                   rms_eps: float = 1e-6, gamma_q=None, gamma_kv=None, out_dtype=None, want_lse=True,
+                   rope_base: float = 10000.0, softmax_scale: float = 0.0,
+                   rms_eps: float = 1e-6, gamma_q=None, out_dtype=None, want_lse=True,
                    out=None, workspace=None):
     """CSA core attention over the selected entries + raw window + sink.
-    q [B,Q,H,D], kv_c [B,N,D], idx [B,Q,K] int32, kv_raw [B,R,D]; returns (out, lse)."""
+    q [B,Q,H,D], kv_c [B,N,D], idx [B,Q,K] int32, kv_raw [B,R,D]; returns (out, lse).
+    kv_c and kv_raw hold rows prepared by kv_prepare (raw row r of sequence b at
+    position raw_pos0[b] + r: kv_prepare_raw)."""
     lib = load_library()
     B, Q, H, D = q.shape
     N, R, K = kv_c.shape[1], kv_raw.shape[1], idx.shape[-1]
@@ -173,7 +208,7 @@ def sparse_mqa_fwd(q, kv_c, idx, kv_raw, raw_pos0, q_pos, sinks, *, m: int, n_wi
     need = int(lib.cakv_sparse_mqa_workspace(B, Q, H, D, K, n_win))
     if workspace is None or workspace.numel() < need:
         workspace = _workspace(need, q.device)
-    prm = _params(m, n_win, rope_dims, rope_base, entry_pos_offset, softmax_scale, rms_eps, gamma_q, gamma_kv)
+    prm = _params(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, gamma_q)
     _check(lib.cakv_sparse_mqa_fwd(ctypes.byref(prm), _dev(q, "q"), _dev(kv_c, "kv_c"), _dev(idx, "idx"),
                                    _dev(kv_raw, "kv_raw"), _dev(raw_pos0, "raw_pos0"), _dev(q_pos, "q_pos"),
                                    _dev(sinks, "sinks"), _DT[q.dtype], B, Q, H, D, N, K, R, _dev(out, "out"),
@@ -183,10 +218,11 @@ def sparse_mqa_fwd(q, kv_c, idx, kv_raw, raw_pos0, q_pos, sinks, *, m: int, n_wi
 
 
 def dense_compressed_mqa_fwd(q, kv_c, kv_raw, raw_pos0, q_pos, sinks, *, m: int, n_win: int, rope_dims: int,
-                             rope_base: float = 10000.0, entry_pos_offset: int = 0, softmax_scale: float = 0.0,
-                             rms_eps: float = 1e-6, gamma_q=None, gamma_kv=None, out_dtype=None, want_lse=True,
+                             rope_base: float = 10000.0, softmax_scale: float = 0.0,
+                             rms_eps: float = 1e-6, gamma_q=None, out_dtype=None, want_lse=True,
                              out=None, workspace=None):
-    """HCA core attention over every visible compressed entry + raw window + sink."""
+    """HCA core attention over every visible compressed entry + raw window + sink
+    (rows prepared as for sparse_mqa_fwd)."""
     lib = load_library()
     B, Q, H, D = q.shape
     N, R = kv_c.shape[1], kv_raw.shape[1]
@@ -197,7 +233,7 @@ def dense_compressed_mqa_fwd(q, kv_c, kv_raw, raw_pos0, q_pos, sinks, *, m: int,
     need = int(lib.cakv_dense_mqa_workspace(B, Q, H, D, N, n_win))
     if workspace is None or workspace.numel() < need:
         workspace = _workspace(need, q.device)
-    prm = _params(m, n_win, rope_dims, rope_base, entry_pos_offset, softmax_scale, rms_eps, gamma_q, gamma_kv)
+    prm = _params(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, gamma_q)
     _check(lib.cakv_dense_compressed_mqa_fwd(ctypes.byref(prm), _dev(q, "q"), _dev(kv_c, "kv_c"),
                                              _dev(kv_raw, "kv_raw"), _dev(raw_pos0, "raw_pos0"),
                                              _dev(q_pos, "q_pos"), _dev(sinks, "sinks"), _DT[q.dtype], B, Q, H, D,

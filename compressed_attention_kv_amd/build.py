@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libcakv.so")
-SOURCES = ["api.hip", "kv_compress.hip", "indexer.hip", "attention.hip"]
+SOURCES = ["api.hip", "kv_compress.hip", "kv_prepare.hip", "indexer.hip", "attention.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

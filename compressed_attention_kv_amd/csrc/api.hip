@@ -103,7 +103,6 @@ int check_attn_common(const cakv_attn_params* p, const void* q, const void* kv_c
     if (R > 0) REQUIRE_PTR(kv_raw, "kv_raw");
     if (lse) REQUIRE(aligned16(lse), CAKV_EINVAL, "lse must be 16-byte aligned");
     if (p->gamma_q) REQUIRE(aligned16(p->gamma_q), CAKV_EINVAL, "gamma_q must be 16-byte aligned");
-    if (p->gamma_kv) REQUIRE(aligned16(p->gamma_kv), CAKV_EINVAL, "gamma_kv must be 16-byte aligned");
     REQUIRE(B * Q <= 0x7fffffffLL, CAKV_EUNSUPPORTED, "B*Q too large");
     return CAKV_OK;
 }
@@ -120,7 +119,6 @@ void fill_attn(cakv::AttnArgs& a, const cakv_attn_params* p, const void* q, cons
     a.q_pos = q_pos;
     a.sinks = sinks;
     a.gamma_q = p->gamma_q;
-    a.gamma_kv = p->gamma_kv;
     a.out = out;
     a.lse = lse;
     a.part_o = nullptr;
@@ -133,7 +131,6 @@ void fill_attn(cakv::AttnArgs& a, const cakv_attn_params* p, const void* q, cons
     a.m = p->m;
     a.n_win = p->n_win;
     a.rope_dims = p->rope_dims;
-    a.entry_pos_offset = p->entry_pos_offset;
     const double tau = p->softmax_scale > 0.0f ? (double)p->softmax_scale : 1.0 / sqrt((double)D);
     a.scale_log2 = (float)(tau * 1.4426950408889634);
     a.rms_eps = p->rms_eps;
@@ -212,6 +209,30 @@ int cakv_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B, i
     if (out_scale) REQUIRE(aligned16(out_scale), CAKV_EINVAL, "out_scale must be 16-byte aligned");
     return rc_from(cakv::launch_kv_compress(x, x_dtype, gate, B, T, D, m, out, out_dtype, out_scale,
                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cakv_kv_prepare(const void* kv_in, void* kv_out, int act_dtype, int64_t B, int64_t N, int64_t D,
+                    int64_t j0, int64_t n, const float* gamma_kv, int32_t m, int32_t rope_dims, float rope_base,
+                    int32_t entry_pos_offset, float rms_eps, void* stream) {
+    REQUIRE(B >= 0 && N >= 0 && j0 >= 0 && n >= 0 && j0 + n <= N, CAKV_EINVAL,
+            "entries [%lld, %lld) outside 0..N=%lld (B=%lld)", (long long)j0, (long long)(j0 + n), (long long)N,
+            (long long)B);
+    REQUIRE(act_dtype == CAKV_F32 || act_dtype == CAKV_BF16, CAKV_EINVAL, "act_dtype must be F32 or BF16");
+    REQUIRE(D >= 8 && D <= 4096 && D % 8 == 0, CAKV_EUNSUPPORTED, "D=%lld: 8..4096, a multiple of 8", (long long)D);
+    REQUIRE(m >= 1, CAKV_EINVAL, "m=%d must be >= 1", m);
+    REQUIRE(rope_dims >= 0 && (rope_dims & 1) == 0 && rope_dims <= D, CAKV_EINVAL, "rope_dims=%d: even, 0..D",
+            rope_dims);
+    REQUIRE(rope_base > 0.0f && isfinite(rope_base), CAKV_EINVAL, "rope_base must be positive");
+    REQUIRE(rms_eps >= 0.0f && isfinite(rms_eps), CAKV_EINVAL, "rms_eps must be >= 0");
+    REQUIRE((N - 1) * (int64_t)m + entry_pos_offset <= 0x7fffffffLL && entry_pos_offset >= -0x7fffffffLL,
+            CAKV_EINVAL, "entry positions must fit in int32");
+    if (B * n == 0) return ok();
+    REQUIRE_PTR(kv_in, "kv_in");
+    REQUIRE_PTR(kv_out, "kv_out");
+    if (gamma_kv) REQUIRE(aligned16(gamma_kv), CAKV_EINVAL, "gamma_kv must be 16-byte aligned");
+    return rc_from(cakv::launch_kv_prepare(kv_in, kv_out, act_dtype == CAKV_F32 ? 0 : 1, B, N, D, j0, n, gamma_kv,
+                                           m, rope_dims, rope_base, entry_pos_offset, rms_eps,
+                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t cakv_indexer_topk_workspace(int64_t B, int64_t Q, int64_t N, int32_t k) {

@@ -9,28 +9,31 @@
 // back by -t).  K and V are the same normalised, rotated vector.
 //
 // Design (one workgroup = one query token, all heads, a range of key tiles):
-//   * 4 waves; wave w owns heads [32w, 32w+32).  Its normalised, rotated
-//     query block Q^_w (32 x D, f16) stays in VGPRs for the whole kernel as
-//     the B operand of S^T = K^ Q^_w^T (v_mfma_f32_32x32x16_f16, keys as rows).
-//   * A tile is 32 key slots (selected entries, or visible entries, then the
-//     window).  All 256 threads gather the tile rows straight from HBM (each
-//     wave instruction reads whole 1 KiB rows), RMS-normalise them (wave
-//     reductions), rotate them, convert to f16 and write two LDS copies: K^
-//     row-major (QK A operand) and V^T (PV B operand), XOR-swizzled so that
-//     MFMA operand reads and the writes are bank-conflict free.  Tiles are
-//     double-buffered; the next tile's HBM reads are in flight during the
-//     current tile's MFMAs.
-//   * Softmax in base 2 with a lazily updated running max (the accumulator
-//     is rescaled only when a head's max grows by more than 2^8), so P fits
-//     f16 and the 32 x D fp32 accumulator per wave is rarely touched by VALU.
-//   * S^T's accumulator layout is exactly the A-operand layout of P for
-//     O = P V (keys permuted consistently in V^T), so P never leaves VGPRs.
-//   * f16 operands: QK-RMSNorm bounds |x| <= sqrt(D) * max|gamma|, so f16's
-//     range is safe and its 11-bit significand is 8x finer than bf16's.
-//   * Splits over key tiles write (max, sum, O) partials; a combine kernel
-//     merges them with the sink.  With one split the epilogue is fused.
-#include <type_traits>
-
+//   * 4 waves, one per SIMD; wave w owns heads [32w, 32w+32).  Its query
+//     block Q~_w (32 x D: RMS-normalised, rotated, times the softmax scale
+//     and log2 e; bf16) stays in VGPRs as the B operand of S^T = K Q~_w^T
+//     (v_mfma_f32_32x32x16_bf16, keys as rows), and its 32 x D fp32 output
+//     accumulator stays in AGPRs.
+//   * A tile is 32 key slots: selected (or visible) compressed entries, then
+//     the window.  Every key row arrives prepared: kv_prepare normalised and
+//     rotated it once, when it was written (a key depends only on its own
+//     token or entry and position), so rows are used exactly as they land.
+//     Rows are copied
+//     HBM -> LDS asynchronously (global_load_lds, 1 KiB per wave instruction)
+//     three tiles ahead into a ring of four tile buffers; 16-byte granules are
+//     XOR-permuted per row so that both the QK reads and the transposed PV
+//     reads (ds_read_b64_tr_b16) run near full LDS rate.  The one LDS tile is
+//     both the K and the V operand.
+//   * Softmax in base 2 against a per-head reference m_use fixed at the first
+//     tile's max, so P = 2^(l - m_use) is never rescaled; a head whose logits
+//     later exceed m_use + 15 flags its wave, and a second pass recomputes
+//     that wave's heads with the true max.  S^T's accumulator layout is the
+//     A-operand layout of P for O = P V (keys permuted consistently in the V
+//     reads), so P never leaves VGPRs.
+//   * f32 activations (head dims up to 128) run the same schedule on f16
+//     operands: their rows are rounded to f16 in LDS one step before use.
+//   * Splits over key tiles write (max, sum, O/l) partials; a combine kernel
+//     merges them with the sink and rotates the output back.
 #include "cakv_device.hpp"
 #include "cakv_internal.hpp"
 
@@ -137,14 +140,12 @@ __device__ __forceinline__ int32_t slot_entry(const AttnArgs& a, const QueryGeom
     return slot < g.n_c ? a.idx[bq * a.K + slot] : 0;
 }
 
-// Source row and rotary position of key slot `slot` whose entry index is j
-// (from slot_entry); nullptr for an empty or invalid slot.
+// Source row of key slot `slot` whose entry index is j (from slot_entry);
+// nullptr for an empty or invalid slot.
 template <typename TIn>
-__device__ __forceinline__ const TIn* slot_row(const AttnArgs& a, const QueryGeom& g, int slot, int32_t j,
-                                               int D, int32_t* pos) {
+__device__ __forceinline__ const TIn* slot_row(const AttnArgs& a, const QueryGeom& g, int slot, int32_t j, int D) {
     if (slot < g.n_c) {
         if (j < 0 || j >= g.n_vis) return nullptr;
-        *pos = j * a.m + a.entry_pos_offset;
         return reinterpret_cast<const TIn*>(a.kv_c) + (g.b * a.N + j) * (int64_t)D;
     }
     int s = slot - g.n_c;
@@ -152,17 +153,7 @@ __device__ __forceinline__ const TIn* slot_row(const AttnArgs& a, const QueryGeo
     int32_t p = g.p_lo + s;
     int64_t row = (int64_t)p - g.raw0;
     if (row < 0 || row >= a.R) return nullptr;
-    *pos = p;
     return reinterpret_cast<const TIn*>(a.kv_raw) + (g.b * a.R + row) * (int64_t)D;
-}
-
-// (sin, cos) of 2 pi x for an angle x in turns: the fractional turn is taken
-// in fp64 (x can exceed 2^17 turns), then the hardware v_sin_f32 / v_cos_f32,
-// whose input is in turns.
-__device__ __forceinline__ void sincos_turns_fast(double x, float* s_out, float* c_out) {
-    const float f = (float)(x - __builtin_floor(x));
-    *s_out = __builtin_amdgcn_sinf(f);
-    *c_out = __builtin_amdgcn_cosf(f);
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (linear id mod 8).
@@ -179,7 +170,6 @@ __device__ __forceinline__ int64_t xcd_order(int64_t lin, int64_t total) {
 // Per-tile row metadata, written four tiles ahead by wave 0.
 struct TileMeta {
     uint64_t rowp[TK];  // source row address, 0 for an empty / invalid slot
-    int32_t pos[TK];    // rotary position of the row
     uint32_t mask;      // bit rho set when row rho is a valid key
 };
 
@@ -216,7 +206,7 @@ __device__ __forceinline__ void barrier_vm() {
 }
 
 // MFMA operand element of the attention kernel: bf16 for bf16 activations
-// (key rows are used exactly as they landed, unnormalised), f16 for f32
+// (prepared key rows are used exactly as they landed), f16 for f32
 // activations (rows are normalised first, so their range is bounded and
 // f16's finer significand keeps more of the f32 input).
 template <bool F16>
@@ -278,18 +268,14 @@ void mqa_fwd_kernel(const AttnArgs a) {
     typedef typename OP::vec opvec;
 
     // Four tile buffers in a ring: at step it, buffer it%4 holds the tile
-    // being multiplied, (it+1)%4 gets its row scales and rotation, (it+2)%4
-    // and (it+3)%4 are still landing.
+    // being multiplied, (it+1)%4 has landed (f32 rows: rounded to f16 here),
+    // (it+2)%4 and (it+3)%4 are still landing.
     __shared__ __attribute__((aligned(16))) uint8_t ring[4][BUF];
     __shared__ TileMeta meta[MS];
-    __shared__ __attribute__((aligned(16))) float invs[MS][TK];  // 1/rms of each row (0: empty slot)
     __shared__ int32_t idxs[MS][64];  // sparse: entry indices of a tile (lanes >= TK unused)
     __shared__ __attribute__((aligned(16))) float2 qcs[kMaxRopePairs];
-    __shared__ double turns[kMaxRopePairs];
-    __shared__ float gkv_s[D];
-    __shared__ __attribute__((aligned(16))) float fq_s[D];  // gamma_q, times gamma_kv on unrotated channels
+    __shared__ __attribute__((aligned(16))) float fq_s[D];   // gamma_q
     __shared__ __attribute__((aligned(16))) float il_s[4][32];  // 1/l of each head (epilogue)
-    __shared__ uint32_t dummy[64];    // write target of inactive rotation items
     __shared__ uint32_t redo;
 
     const int tid = threadIdx.x;
@@ -317,16 +303,12 @@ void mqa_fwd_kernel(const AttnArgs a) {
     auto tile_meta = [&](int tile, int slot, int32_t j) __attribute__((always_inline)) {
         if (wave != 0) return;
         const int ol = opaque_tid() & 63;
-        int32_t pos = 0;
         const TIn* row = nullptr;
         if (ol < TK && tile < tile1) {
             const int sl = tile * TK + ol;
-            row = slot_row<TIn>(a, g, sl, SPARSE ? j : sl, D, &pos);
+            row = slot_row<TIn>(a, g, sl, SPARSE ? j : sl, D);
         }
-        if (ol < TK) {
-            meta[slot].rowp[ol] = reinterpret_cast<uint64_t>(row);
-            meta[slot].pos[ol] = pos;
-        }
+        if (ol < TK) meta[slot].rowp[ol] = reinterpret_cast<uint64_t>(row);
         const uint64_t bal = __ballot(row != nullptr);
         if (ol == 0) meta[slot].mask = (uint32_t)bal;
     };
@@ -376,16 +358,11 @@ void mqa_fwd_kernel(const AttnArgs a) {
     }
     if (wave == 0 && lane < n_pairs) {
         const double tn = rope_turns(a.rope_base, lane, a.rope_dims);
-        turns[lane] = tn;
         float sn, cs;
         sincos_turns((double)g.t * tn, &sn, &cs);
         qcs[lane] = make_float2(cs, sn);
     }
-    for (int i = tid; i < D; i += 256) {
-        const float gkv = a.gamma_kv ? a.gamma_kv[i] : 1.0f;
-        gkv_s[i] = gkv;
-        fq_s[i] = (a.gamma_q ? a.gamma_q[i] : 1.0f) * (i < rope_lo ? gkv : 1.0f);
-    }
+    for (int i = tid; i < D; i += 256) fq_s[i] = a.gamma_q ? a.gamma_q[i] : 1.0f;
     // metadata of the first four tiles and the indices of the fifth (the
     // entry-index loads are all issued before any is used)
     auto meta_start = [&]() __attribute__((always_inline)) {
@@ -412,9 +389,8 @@ void mqa_fwd_kernel(const AttnArgs a) {
     barrier_vm<0>();  // (the query rows have landed too)
     start_tiles();
 
-    // Q~ = RoPE_t(gamma_q * q / rms(q)) * softmax scale * log2(e), with the
-    // KV gain gamma_kv folded into the unrotated channels (the rotated ones
-    // carry it on the key side), in the B-operand layout of the QK MFMAs:
+    // Q~ = RoPE_t(gamma_q * q / rms(q)) * softmax scale * log2(e), in the
+    // B-operand layout of the QK MFMAs:
     // lane (head lrow, half lh) holds channels 16 s + 8 lh + (0..7) for
     // k-step s, so a head's sum of squares is this lane's plus lane l ^ 32's.
     opvec qf[KSTEPS];
@@ -466,85 +442,31 @@ void mqa_fwd_kernel(const AttnArgs a) {
     }
 
     // ---------------------------------------------------------------- tile prep
-    // K = V = RoPE(gamma_kv * v / rms(v)) is never materialised: the bf16
-    // rows stay as they landed and multiply Q~ directly; 1/rms(v) of each row
-    // (0 for an empty slot) scales its logit and its softmax weight, and
-    // gamma_kv of the unrotated channels sits in Q~ and in the combine step.
-    // Only the last r channels are rewritten, in place, as RoPE(gamma_kv * v)
-    // in bf16.  (f32 rows are first normalised and rounded to f16 in place,
-    // with a row scale of 1; their operands are f16 throughout.)  Lane (row = 8 w + l/8, j = l%8) owns the
-    // 8-channel chunks j, j+8, ...; the eight lanes of a row reduce their sums
-    // of squares with three DPP steps.
+    // f32 rows (already prepared) are rounded to f16 in place, their operand
+    // type; bf16 rows are used exactly as they landed.  Lane (row = 8 w + l/8,
+    // j = l%8) owns the 8-channel chunks j, j+8, ... of its row; every lane of
+    // the wave has read its chunks before any of the writes (LDS operations of
+    // one wave complete in order).
     auto prep_tile = [&](int mslot, uint8_t* buf) __attribute__((always_inline)) {
-        const int ot = opaque_tid();
-        const int ol = ot & 63;
-        const int row = 8 * (ot >> 6) + (ol >> 3);
-        const int jj = ol & 7;
-        const bool valid = (meta[mslot].mask >> row) & 1u;
-        float ss = 0.0f;
-        uint8_t* rb = buf + row * RS;
-        if (RAW_F32) {
-            float xs[CH][8];
+        (void)mslot;
+        if constexpr (RAW_F32) {
+            const int ot = opaque_tid();
+            const int ol = ot & 63;
+            const int row = 8 * (ot >> 6) + (ol >> 3);
+            const int jj = ol & 7;
+            uint8_t* rb = buf + row * RS;
+            f32x4 x[CH][2];
 #pragma unroll
             for (int k = 0; k < CH; ++k) {
                 const int c = jj + 8 * k;
-                const f32x4 x0 = *reinterpret_cast<const f32x4*>(rb + 32 * c);
-                const f32x4 x1 = *reinterpret_cast<const f32x4*>(rb + 32 * c + 16);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    xs[k][i] = x0[i];
-                    xs[k][4 + i] = x1[i];
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(xs[k][i], xs[k][i], ss);
+                x[k][0] = *reinterpret_cast<const f32x4*>(rb + 32 * c);
+                x[k][1] = *reinterpret_cast<const f32x4*>(rb + 32 * c + 16);
             }
-            ss = row8_sum(ss);
-            const float inv = valid ? __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps) : 0.0f;
-#pragma unroll
-            for (int k = 0; k < CH; ++k) {
-                const int c = jj + 8 * k;
-                *reinterpret_cast<u32x4*>(rb + 16 * (c ^ gperm(row))) =
-                    u32x4{OP::pack(xs[k][0] * inv, xs[k][1] * inv), OP::pack(xs[k][2] * inv, xs[k][3] * inv),
-                          OP::pack(xs[k][4] * inv, xs[k][5] * inv), OP::pack(xs[k][6] * inv, xs[k][7] * inv)};
-            }
-            if (jj == 0) invs[mslot][row] = 1.0f;
-        } else {
-            u32x4 r[CH];  // all chunk reads in flight before the first product
-#pragma unroll
-            for (int k = 0; k < CH; ++k) r[k] = *reinterpret_cast<const u32x4*>(rb + 16 * (jj + 8 * k));
 #pragma unroll
             for (int k = 0; k < CH; ++k)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bf16x2_t pr = word_as_bf16x2(r[k][i]);
-                    ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
-                }
-            __builtin_amdgcn_sched_group_barrier(0x100, CH, 1);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4 * CH, 1);
-            ss = row8_sum(ss);
-            const float inv = valid ? __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps) : 0.0f;
-            if (jj == 0) invs[mslot][row] = inv;
-        }
-        // rotation of this wave's 8 rows: item = pair * 8 + row, 4 per lane,
-        // branch-free (items past the rotated pairs touch `dummy`).  Every
-        // lane of the wave has read its chunks above before any of these
-        // writes (LDS operations of one wave complete in order).
-        const int row0 = 8 * (ot >> 6);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int item = ol + 64 * k;
-            const int rr = row0 + (item & 7);
-            const int pr = item >> 3;
-            const bool on = pr < n_pairs;
-            const int dim = rope_lo + 2 * pr;
-            uint32_t* pw = on ? reinterpret_cast<uint32_t*>(buf + rr * RS + 16 * ((dim >> 3) ^ gperm(rr)) + 2 * (dim & 7))
-                              : &dummy[ol];
-            float sn, cs;
-            sincos_turns_fast((double)meta[mslot].pos[rr] * turns[on ? pr : 0], &sn, &cs);
-            const uint32_t hv = *pw;
-            const float x0 = OP::lo(hv) * gkv_s[on ? dim : 0];
-            const float x1 = OP::hi(hv) * gkv_s[on ? dim + 1 : 0];
-            *pw = OP::pack(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+                *reinterpret_cast<u32x4*>(rb + 16 * (jj + 8 * k)) =
+                    u32x4{OP::pack(x[k][0][0], x[k][0][1]), OP::pack(x[k][0][2], x[k][0][3]),
+                          OP::pack(x[k][1][0], x[k][1][1]), OP::pack(x[k][1][2], x[k][1][3])};
         }
     };
 
@@ -561,10 +483,9 @@ void mqa_fwd_kernel(const AttnArgs a) {
     bool flagged = false;  // wave-uniform
     bool active = has_heads;
 
-    // QK, softmax and PV on a prepared tile.  S^T = K Q~_w^T (keys as rows),
-    // each row then scaled by its 1/rms; the accumulator layout is the
-    // A-operand layout of P for O = P V with the tile's keys in the order
-    // (4 lh + j, then 8 + 4 lh + j), P carrying each key's 1/rms: the V
+    // QK, softmax and PV on a prepared tile.  S^T = K Q~_w^T (keys as rows);
+    // the accumulator layout is the A-operand layout of P for O = P V with
+    // the tile's keys in the order (4 lh + j, then 8 + 4 lh + j): the V
     // operand is read in that order straight from the row-major tile with
     // ds_read_b64_tr_b16 (in each 16-lane group, lane i receives element
     // i % 4 of the 8-byte chunks addressed by lanes 4k + i / 4, k = 0..3).
@@ -604,12 +525,6 @@ void mqa_fwd_kernel(const AttnArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, QPF, 2);
-        // row scales of this lane's rows 8*(r/4) + 4*lh + r%4
-        f32x4 iv[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) iv[m] = *reinterpret_cast<const f32x4*>(&invs[mslot][8 * m + 4 * oh]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[r] *= iv[r >> 2][r & 3];
         // logits are in log2 units (Q~ carries the softmax scale)
         float mx = -INFINITY;
         if (mask != 0xffffffffu) {
@@ -633,7 +548,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
             const float p0 = live ? __builtin_amdgcn_exp2f(st[r] - m_use) : 0.0f;
             const float p1 = live ? __builtin_amdgcn_exp2f(st[r + 1] - m_use) : 0.0f;
             psum += p0 + p1;
-            pk[r >> 1] = OP::pack(p0 * iv[r >> 2][r & 3], p1 * iv[r >> 2][(r & 3) + 1]);
+            pk[r >> 1] = OP::pack(p0, p1);
         }
         psum += __shfl_xor(psum, 32, 64);
         l_run += psum;
@@ -690,7 +605,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
     // One pipeline step (tile T = tile0 + it):
     //   wave 0 builds the metadata of T+4 from its indices (landed) and
     //   starts copying the indices of T+5; all waves start copying the rows
-    //   of T+3; T+1 gets its row scales and rotation while T is multiplied
+    //   of T+3; T+1's f32 rows are rounded to f16 while T is multiplied
     //   (different buffers, no barrier between them); the closing barrier
     //   waits until only T+3's rows are in flight.
     auto step = [&](int it) __attribute__((always_inline)) {
@@ -712,11 +627,11 @@ void mqa_fwd_kernel(const AttnArgs a) {
         else barrier_vm<0>();
     };
 
-    // Fast step (bf16 1 KiB rows, a full tile T, T+3 inside the split, an
-    // active wave that has not flagged): one block in three phases whose
-    // VALU work rides under MFMAs (branching only on a pass's first tile).
-    //   A: the QK MFMAs of T, with the copy of T+3 (one row unit every four
-    //      MFMAs), the row sums of T+1 and the rotation of T+1 between them;
+    // Fast step (bf16 1 KiB rows; T a full tile, T+3 inside the split; an
+    // active wave that has not flagged): one block in three phases whose VALU
+    // work rides under MFMAs (branching only on a pass's first tile).
+    //   A: the QK MFMAs of T, with the copy of T+3 between them (one row unit
+    //      every four MFMAs);
     //   B: P for the first eight keys of T (P no longer waits on the tile
     //      max: a tile that would flag the wave only spoils a pass that the
     //      second pass redoes);
@@ -729,9 +644,8 @@ void mqa_fwd_kernel(const AttnArgs a) {
             tile_meta(T + 4, (it + 4) & (MS - 1), SPARSE ? idxs[(it + 4) & (MS - 1)][ol0] : 0);
             if (SPARSE && T + 5 < tile1) idx_load(T + 5, (it + 5) & (MS - 1));
         }
-        const int ms0 = it & (MS - 1), ms1 = (it + 1) & (MS - 1), ms3 = (it + 3) & (MS - 1);
+        const int ms3 = (it + 3) & (MS - 1);
         const uint8_t* kh = ring[it & 3];
-        uint8_t* pb = ring[(it + 1) & 3];
         uint8_t* db = ring[(it + 3) & 3];
         const int ol = opaque_tid() & 63;
         // row pointers of T+3 (one row per unit: wave-uniform)
@@ -748,34 +662,6 @@ void mqa_fwd_kernel(const AttnArgs a) {
             const uint8_t* src = rp[k] ? reinterpret_cast<const uint8_t*>(rp[k]) : spare_row;
             lds_dma16_nc(src + 16 * ((ol % LPR) ^ gperm(u)), (uint32_t)(uintptr_t)(db + u * RS));
         };
-        // row sums of squares of T+1 (8 lanes per row, rows 8 wave + ol / 8);
-        // the chunk reads run PPF ahead of their products
-        const int prow = 8 * wave + (ol >> 3), pj = ol & 7;
-        constexpr int PPF = 2;
-        u32x4 pr[PPF];
-        auto pread = [&](int k) __attribute__((always_inline)) -> u32x4 {
-            return *reinterpret_cast<const u32x4*>(pb + prow * RS + 16 * (pj + 8 * k));
-        };
-        // rotation of T+1: lane pair rpi, rows 8 wave + ol / 32 + 2 k; the
-        // pair's turn rate and KV gains are per lane, the positions per row
-        const int rpi = ol & 31, rh = ol >> 5;
-        const bool ron = rpi < n_pairs;
-        const int rdim = rope_lo + 2 * (ron ? rpi : 0);
-        const double rturn = turns[ron ? rpi : 0];
-        const float rg0 = gkv_s[rdim], rg1 = gkv_s[rdim + 1];
-        auto rope_item = [&](int k) __attribute__((always_inline)) {
-            const int rr = 8 * wave + rh + 2 * k;
-            uint32_t* pw = ron ? reinterpret_cast<uint32_t*>(pb + rr * RS + 16 * ((rdim >> 3) ^ gperm(rr)) + 2 * (rdim & 7))
-                               : &dummy[ol];
-            float sn, cs;
-            sincos_turns_fast((double)meta[ms1].pos[rr] * rturn, &sn, &cs);
-            const uint32_t hv = *pw;
-            const float x0 = OP::lo(hv) * rg0;
-            const float x1 = OP::hi(hv) * rg1;
-            *pw = OP::pack(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
-        };
-#pragma unroll
-        for (int k = 0; k < PPF; ++k) pr[k] = pread(k);
         // ---- A: QK of T
         const int orow = ol & 31, oh = ol >> 5;
         const int ga = gperm(orow);
@@ -791,54 +677,33 @@ void mqa_fwd_kernel(const AttnArgs a) {
         f32x16 st;
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[r] = 0.0f;
-        float ss = 0.0f;
 #pragma unroll
         for (int s2 = 0; s2 < KSTEPS; ++s2) {
             const opvec av = kq[s2 % QPF];
             if (s2 + QPF < KSTEPS) kq[s2 % QPF] = kread(s2 + QPF);
             st = OP::mfma(av, qf[s2], st);
             if ((s2 & 3) == 1 && (s2 >> 2) < NU) dma_unit(s2 >> 2);
-            if (s2 < CH) {
-                const u32x4 c4 = pr[s2 % PPF];
-                if (s2 + PPF < CH) pr[s2 % PPF] = pread(s2 + PPF);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bf16x2_t w2 = word_as_bf16x2(c4[i]);
-                    ss = __builtin_amdgcn_fdot2_f32_bf16(w2, w2, ss, false);
-                }
-            }
-            // rotations after the last chunk read of the row sums (same rows)
-            if (s2 >= 12 && (s2 & 3) == 0 && ((s2 - 12) >> 2) < 4) rope_item((s2 - 12) >> 2);
         }
-        // pinned order: the first reads, then each MFMA followed by the reads
-        // that run ahead of it (else the prefetch collapses under pressure)
-        __builtin_amdgcn_sched_group_barrier(0x100, QPF + PPF, 2);
+        // pinned order: the first reads, then each MFMA followed by the read
+        // that runs ahead of it (else the prefetch collapses under pressure)
+        __builtin_amdgcn_sched_group_barrier(0x100, QPF, 2);
 #pragma unroll
         for (int s2 = 0; s2 < KSTEPS; ++s2) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
             if (s2 + QPF < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
-            if (s2 + PPF < CH) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
         }
         __builtin_amdgcn_sched_barrier(0);
-        ss = row8_sum(ss);
-        {
-            const bool pvalid = (meta[ms1].mask >> prow) & 1u;
-            invs[ms1][prow] = pvalid ? __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps) : 0.0f;  // 8 lanes, one value
-        }
         // ---- B: logits relative to m_use (log2 units), P of the first keys
-        f32x4 iv[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) iv[m] = *reinterpret_cast<const f32x4*>(&invs[ms0][8 * m + 4 * oh]);
         if (__ballot(m_use == -INFINITY)) {  // first tile of the pass: m_use is its max
             float m0 = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) m0 = fmaxf(m0, st[r] * iv[r >> 2][r & 3]);
+            for (int r = 0; r < 16; ++r) m0 = fmaxf(m0, st[r]);
             m0 = xor32_max(m0);
             m_use = (m_use == -INFINITY) ? m0 : m_use;
         }
         float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(st[r], iv[r >> 2][r & 3], -m_use);
+        for (int r = 0; r < 16; ++r) x[r] = st[r] - m_use;
         uint32_t pk[8];
         float psum = 0.0f;
 #pragma unroll
@@ -846,7 +711,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
             const float p0 = __builtin_amdgcn_exp2f(x[r]);
             const float p1 = __builtin_amdgcn_exp2f(x[r + 1]);
             psum += p0 + p1;
-            pk[r >> 1] = OP::pack(p0 * iv[r >> 2][r & 3], p1 * iv[r >> 2][(r & 3) + 1]);
+            pk[r >> 1] = OP::pack(p0, p1);
         }
         const opvec pa0 = __builtin_bit_cast(opvec, u32x4{pk[0], pk[1], pk[2], pk[3]});
         __builtin_amdgcn_sched_barrier(0);
@@ -887,7 +752,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
                 const float p0 = __builtin_amdgcn_exp2f(x[r]);
                 const float p1 = __builtin_amdgcn_exp2f(x[r + 1]);
                 psum += p0 + p1;
-                pk[4 + (j - 1)] = OP::pack(p0 * iv[r >> 2][r & 3], p1 * iv[r >> 2][(r & 3) + 1]);
+                pk[4 + (j - 1)] = OP::pack(p0, p1);
                 if (j == 4) pa1 = __builtin_bit_cast(opvec, u32x4{pk[4], pk[5], pk[6], pk[7]});
             }
             if (j == 6) {
@@ -908,7 +773,11 @@ void mqa_fwd_kernel(const AttnArgs a) {
         // the tile max only decides the flag and the second pass's m_use
         m_seen = fmaxf(m_seen, mx + m_use);
         if (__ballot(mx > 15.0f)) flagged = true;
-        barrier_vm<NU>();
+        barrier_vm<NU>();  // all but T+3's loads have landed
+    };
+    // a step can take the fast form when its tile is full
+    auto fast_tile = [&](int it) __attribute__((always_inline)) -> bool {
+        return __builtin_amdgcn_readfirstlane(meta[it & (MS - 1)].mask) == 0xffffffffu;
     };
 
     for (int pass = 0; pass < 2; ++pass) {
@@ -938,9 +807,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
         {
             int it = 0;
             if constexpr (PERM && !RAW_F32) {
-                for (; tile0 + it + 3 < tile1 && active && !flagged &&
-                       __builtin_amdgcn_readfirstlane(meta[it & (MS - 1)].mask) == 0xffffffffu; ++it)
-                    step_fast(it);
+                for (; tile0 + it + 3 < tile1 && active && !flagged && fast_tile(it); ++it) step_fast(it);
             }
             for (; tile0 + it < tile1; ++it) step(it);
         }
@@ -1035,10 +902,6 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(const AttnArgs a) {
         if (e >= nh) continue;
         const int h = 2 * hp + e;
         float o0 = Z[e] > 0.0f ? o[e][0] / Z[e] : 0.0f, o1 = Z[e] > 0.0f ? o[e][1] / Z[e] : 0.0f;
-        if (2 * pr < rope_lo && a.gamma_kv) {  // the unrotated channels' KV gain (kept out of the key tiles)
-            o0 *= a.gamma_kv[2 * pr];
-            o1 *= a.gamma_kv[2 * pr + 1];
-        }
         if (2 * pr >= rope_lo) {
             const float x0 = o0, x1 = o1;
             o0 = x0 * cs - x1 * sn;

@@ -25,7 +25,6 @@ struct AttnArgs {
     const int32_t* q_pos;
     const float* sinks;
     const float* gamma_q;
-    const float* gamma_kv;
     void* out;
     float* lse;
     uint32_t* part_o;  // [BQ][S][(H+1)/2][D] split outputs O/l, fp16, heads (2p, 2p+1) in one word
@@ -38,7 +37,6 @@ struct AttnArgs {
     int32_t m;
     int32_t n_win;
     int32_t rope_dims;
-    int32_t entry_pos_offset;
     float scale_log2;  // softmax scale * log2(e)
     float rms_eps;
     int32_t n_splits;
@@ -54,6 +52,11 @@ __device__ __forceinline__ double rope_turns(float base, int i, int rope_dims) {
 int launch_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B, int64_t T,
                        int64_t D, int32_t m, void* out, int out_dtype, float* out_scale,
                        hipStream_t stream);
+
+// dtype 0: float32, 1: bf16; entries j0 .. j0+n-1 of each of the B sequences
+int launch_kv_prepare(const void* in, void* out, int dtype, int64_t B, int64_t N, int64_t D, int64_t j0,
+                      int64_t n, const float* gamma, int32_t m, int32_t rope_dims, float rope_base,
+                      int32_t pos_off, float eps, hipStream_t stream);
 
 // sparse (idx != NULL) or dense MQA forward; act_f32: inputs are float32
 int launch_mqa_fwd(const AttnArgs& a, int64_t BQ, int D, bool act_f32, hipStream_t stream);

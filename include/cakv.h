@@ -105,6 +105,32 @@ int cakv_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B, i
                      void* stream);
 
 /* ---------------------------------------------------------------------------
+ * kv_prepare  [V4-Pro card, "Hybrid attention": RMSNorm on the single
+ * compressed KV head before the attention dot product; RoPE on the last 64
+ * dims of each KV entry]
+ *
+ * The key (= value) vector of compressed entries j0 .. j0+n-1 of each of the B
+ * sequences:
+ *     y = gamma_kv * c / sqrt(mean_d(c_d^2) + rms_eps),
+ * then the last rope_dims channels, in consecutive pairs (2i, 2i+1) counted
+ * from D - rope_dims, rotated by the angle pi * rope_base^(-2i/rope_dims) with
+ * pi = j*m + entry_pos_offset, the entry's position.  The attention calls
+ * read compressed entries in this form: run it once on every entry when the
+ * entry enters the cache (after kv_compress), not per attention call.
+ *   kv_in   [B, N, D]  act_dtype CAKV_F32 or CAKV_BF16, raw entries c
+ *   kv_out  [B, N, D]  same dtype; only entries j0 .. j0+n-1 are written
+ *           (bf16: round to nearest even).  kv_out == kv_in works in place;
+ *           other overlaps are undefined.
+ *   gamma_kv [D] float32 device pointer, NULL = all ones
+ *   D        8 .. 4096, a multiple of 8; rope_dims even, 0 .. D
+ * Arithmetic in fp32.  Errors: EINVAL (NULL pointers, alignment, ranges,
+ * positions beyond int32), EUNSUPPORTED (D).
+ * ------------------------------------------------------------------------- */
+int cakv_kv_prepare(const void* kv_in, void* kv_out, int act_dtype, int64_t B, int64_t N, int64_t D,
+                    int64_t j0, int64_t n, const float* gamma_kv, int32_t m, int32_t rope_dims,
+                    float rope_base, int32_t entry_pos_offset, float rms_eps, void* stream);
+
+/* ---------------------------------------------------------------------------
  * indexer_topk  [V4 digest, CSA step 2: a light indexer scores every
  * compressed entry for each query and keeps the top k; V4-Pro card: 64
  * Lightning-Indexer heads of dim 128 select k=1024 entries; Visualised:
@@ -146,15 +172,13 @@ int cakv_indexer_topk(const void* q_idx, int q_dtype, const float* w, const void
  * logits added to the softmax denominator]
  * ------------------------------------------------------------------------- */
 typedef struct cakv_attn_params {
-    int32_t m;                /* compression ratio of kv_c (visibility and positions) */
+    int32_t m;                /* compression ratio of kv_c (visibility) */
     int32_t n_win;            /* raw window length, 0 .. 4096 */
     int32_t rope_dims;        /* r: rotated trailing dims, even, 0 .. D */
-    int32_t entry_pos_offset; /* compressed entry j sits at position j*m + offset */
     float rope_base;          /* theta_i = rope_base^(-2i/r) */
     float softmax_scale;      /* 0 selects 1/sqrt(D) */
-    float rms_eps;            /* RMSNorm epsilon */
+    float rms_eps;            /* RMSNorm epsilon of the query heads */
     const float* gamma_q;     /* [D] device pointer, NULL = all ones */
-    const float* gamma_kv;    /* [D] device pointer, NULL = all ones */
 } cakv_attn_params;
 
 /* ---------------------------------------------------------------------------
@@ -167,13 +191,18 @@ typedef struct cakv_attn_params {
  *   - raw window rows at positions max(0, t-n_win+1) .. t that lie inside
  *     [raw_pos0[b], raw_pos0[b] + R) (kv_raw row p - raw_pos0[b]),
  *   - the sink: exp(sinks[h]) added to the denominator with a zero value.
- * Keys and values are the same vector: RoPE_pi(gamma_kv * v / rms(v)), pi the
- * key's position; the query is RoPE_t(gamma_q * q / rms(q)); logits are
+ * Keys and values are the same vector k_hat = RoPE_pi(gamma_kv * v / rms(v)),
+ * pi the key's position; the query is RoPE_t(gamma_q * q / rms(q)); logits are
  * softmax_scale * (q_hat . k_hat).  The output is rotated back by -t.
+ * Every key row is read as cakv_kv_prepare left it (already k_hat: a key
+ * depends only on its own entry or token and its position, so it is prepared
+ * once, when written): kv_c entry j prepared at j*m + offset, and kv_raw row r
+ * of sequence b prepared at position raw_pos0[b] + r (cakv_kv_prepare with
+ * m = 1 and entry_pos_offset = raw_pos0[b] on that sequence's rows).
  *   q       [B, Q, H, D]  act_dtype   CAKV_BF16 or CAKV_F32 (also kv_c, kv_raw)
- *   kv_c    [B, N, D]     compressed cache (ratio p->m)
+ *   kv_c    [B, N, D]     compressed cache (ratio p->m), prepared entries
  *   idx     [B, Q, K]     int32 selected entries (distinct; -1 = empty slot)
- *   kv_raw  [B, R, D]     raw rows for the window
+ *   kv_raw  [B, R, D]     prepared raw-token rows for the window
  *   raw_pos0 [B]          int32 position of kv_raw row 0
  *   q_pos   [B, Q]        int32 query positions (negative -> 0)
  *   sinks   [H]           float32 sink logits (-inf allowed)

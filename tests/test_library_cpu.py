@@ -25,7 +25,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert len(names) >= 9
+    assert len(names) >= 10
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(cakv.EXPORTS)
@@ -33,8 +33,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def _prm(**kw):
-    d = dict(m=4, n_win=128, rope_dims=64, entry_pos_offset=0, rope_base=10000.0, softmax_scale=0.0,
-             rms_eps=1e-6, gamma_q=None, gamma_kv=None)
+    d = dict(m=4, n_win=128, rope_dims=64, rope_base=10000.0, softmax_scale=0.0,
+             rms_eps=1e-6, gamma_q=None)
     d.update(kw)
     return cakv.AttnParams(**d)
 
@@ -79,6 +79,28 @@ def test_kv_compress_errors(lib):
     assert f(FAKE, cakv.BF16, FAKE, 1, 8, 512, 4, FAKE, cakv.FP8_E4M3, None, None) == -1  # scale missing
     assert f(FAKE, cakv.BF16, FAKE, 1, 8, 512, 4, FAKE, cakv.BF16, FAKE, None) == -1  # scale not wanted
     assert f(None, cakv.BF16, FAKE, 1, 8, 512, 4, FAKE, cakv.BF16, None, None) == -1
+
+
+def test_kv_prepare_errors(lib):
+    f = lib.cakv_kv_prepare
+    ok = dict(i=FAKE, o=FAKE, dt=cakv.BF16, B=1, N=8, D=512, j0=0, n=8, g=None, m=4, r=64, base=10000.0, off=0,
+              eps=1e-6)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["i"], a["o"], a["dt"], a["B"], a["N"], a["D"], a["j0"], a["n"], a["g"], a["m"], a["r"],
+                 a["base"], a["off"], a["eps"], None)
+    assert call(j0=4, n=5) == -1          # entries past N
+    assert call(n=-1) == -1
+    assert call(D=500) == -2              # D % 8
+    assert call(D=8192) == -2
+    assert call(dt=cakv.FP8_E4M3) == -1
+    assert call(r=3) == -1 and call(r=520) == -1
+    assert call(m=0) == -1
+    assert call(base=0.0) == -1 and call(eps=-1.0) == -1
+    assert call(i=None) == -1 and call(o=FAKE + 8) == -1 and call(g=FAKE + 4) == -1
+    assert call(N=1 << 30, n=1, m=4) == -1  # positions beyond int32
+    assert call(B=0, i=None, o=None) == 0 and call(n=0, i=None, o=None) == 0  # nothing to do
 
 
 def test_indexer_errors_and_workspace(lib):

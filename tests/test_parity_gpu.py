@@ -7,8 +7,12 @@ same seeded inputs.  Bars (the method's stated tolerances):
     oracle's dequantised value (same scale except at an exponent boundary);
   * indexer_topk: indices bit-exact in fp32 mode; fp8 mode recall >= 99.5 %
     with every miss within 1e-3 relative of the k-th best score;
+  * kv_prepare: bf16 within one bf16 ulp of the fp64 result plus 1e-6 of the
+    row scale, f32 within 2e-6 relative to the row scale;
   * attention (fed the oracle's indices): max-abs <= 2e-2 and
-    rel-RMS = ||o - o_ref|| / ||o_ref|| <= 5e-3.
+    rel-RMS = ||o - o_ref|| / ||o_ref|| <= 5e-3.  The GPU side reads key rows
+    (compressed entries and window rows) prepared by its own kv_prepare; the
+    oracle attends over the raw rows.
 """
 import math
 import sys
@@ -180,7 +184,54 @@ def test_indexer_fp8_recall(name, over):
     assert recall >= 0.995 and gap <= 1e-3
 
 
+# ------------------------------------------------------------------ kv_prepare
+
+@pytest.mark.parametrize("dtype,D,r,m,off,j0,n,gamma,inplace", [
+    ("bf16", 512, 64, 4, 0, 0, None, False, True), ("bf16", 512, 64, 128, 37, 100, 300, True, False),
+    ("f32", 128, 64, 4, 5, 3, 17, True, True), ("bf16", 64, 16, 1, 0, 0, None, True, False),
+    ("bf16", 4096, 64, 4, 0, 7, 9, False, True)])
+def test_kv_prepare(dtype, D, r, m, off, j0, n, gamma, inplace):
+    say(f"kv_prepare {dtype} D={D} r={r} m={m} off={off} j0={j0} n={n} gamma={gamma} inplace={inplace}")
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    g = torch.Generator().manual_seed(D + r + m)
+    B, N = 3, 1200 if D < 4096 else 40
+    x = (torch.randn(B, N, D, generator=g) * 3).to(tdt)
+    gk = torch.rand(D, generator=g) + 0.5 if gamma else None
+    kw = dict(m=m, rope_dims=r, rope_base=10000.0, entry_pos_offset=off, gamma_kv=gk, j0=j0, n=n)
+    ref = oracle.kv_prepare(x, **kw)
+    xd = _d(x)
+    kwd = dict(kw, gamma_kv=None if gk is None else _d(gk))
+    out = torch.full_like(xd, 7.0) if not inplace else None
+    got = cakv.kv_prepare(xd, out=out, **kwd)
+    nn = N - j0 if n is None else n
+    got_c = got.float().cpu().numpy()
+    # entries outside [j0, j0+n) are untouched
+    other = np.ones(N, bool)
+    other[j0:j0 + nn] = False
+    want_other = x.float().numpy() if inplace else np.full((B, N, D), 7.0)
+    assert np.array_equal(got_c[:, other], want_other[:, other])
+    got_c = got_c[:, j0:j0 + nn]
+    scale = np.abs(ref).max(axis=-1, keepdims=True)
+    if dtype == "f32":
+        assert np.all(np.abs(got_c - ref) <= 2e-6 * scale)
+    else:
+        assert np.all(np.abs(got_c - ref) <= _bf16_ulp(ref) + 1e-6 * scale)
+
+
 # ------------------------------------------------------------------ attention
+
+def _prep(kv, m, kw):
+    """The compressed cache as the attention calls read it: a device copy with
+    every entry prepared by kv_prepare."""
+    return cakv.kv_prepare(_d(kv).clone(), m=m, rope_dims=kw["rope_dims"], rope_base=kw.get("rope_base", 10000.0))
+
+
+def _prep_raw(raw, raw_pos0, kw):
+    """The window rows as the attention calls read them: a device copy with row r
+    of sequence b prepared at position raw_pos0[b] + r."""
+    return cakv.kv_prepare_raw(_d(raw).clone(), np.asarray(raw_pos0).tolist(), rope_dims=kw["rope_dims"],
+                               rope_base=kw.get("rope_base", 10000.0))
+
 
 def _attn_check(out, ref, what):
     out = out.astype(np.float64)
@@ -206,8 +257,9 @@ def test_sparse_attention_tiny_layer_f32():
     ref, lse_ref = oracle.attention(inp["q"], kvc, inp["kv_raw"], inp["raw_pos0"], inp["q_pos"], inp["sinks"],
                                     idx=idx, **kw)
     for odt in (torch.float32, torch.bfloat16):
-        out, lse = cakv.sparse_mqa_fwd(_d(inp["q"]), _d(kvc), _d(idx), _d(inp["kv_raw"]), _d(inp["raw_pos0"]),
-                                       _d(inp["q_pos"]), _d(inp["sinks"]), out_dtype=odt, **kw)
+        out, lse = cakv.sparse_mqa_fwd(_d(inp["q"]), _prep(kvc, w.m, kw), _d(idx),
+                                       _prep_raw(inp["kv_raw"], inp["raw_pos0"], kw),
+                                       _d(inp["raw_pos0"]), _d(inp["q_pos"]), _d(inp["sinks"]), out_dtype=odt, **kw)
         _attn_check(out.float().cpu().numpy().reshape(ref.shape), ref, f"out {odt}")
     assert np.abs(lse.cpu().numpy().reshape(lse_ref.shape) - lse_ref).max() < 1e-3
 
@@ -219,8 +271,10 @@ def test_dense_attention_tiny_hca_f32():
     kvc = oracle.kv_compress(inp["kv"], inp["gate"], 128).astype(np.float32)
     kw = _attn_kw(w)
     ref, lse_ref = oracle.attention(inp["q"], kvc, inp["kv_raw"], inp["raw_pos0"], inp["q_pos"], inp["sinks"], **kw)
-    out, lse = cakv.dense_compressed_mqa_fwd(_d(inp["q"]), _d(kvc), _d(inp["kv_raw"]), _d(inp["raw_pos0"]),
-                                             _d(inp["q_pos"]), _d(inp["sinks"]), out_dtype=torch.float32, **kw)
+    out, lse = cakv.dense_compressed_mqa_fwd(_d(inp["q"]), _prep(kvc, 128, kw),
+                                             _prep_raw(inp["kv_raw"], inp["raw_pos0"], kw),
+                                             _d(inp["raw_pos0"]), _d(inp["q_pos"]), _d(inp["sinks"]),
+                                             out_dtype=torch.float32, **kw)
     _attn_check(out.cpu().numpy().reshape(ref.shape), ref, "out")
     assert np.abs(lse.cpu().numpy().reshape(lse_ref.shape) - lse_ref).max() < 1e-3
 
@@ -234,8 +288,9 @@ def test_sparse_attention_csa_decode_128k():
     kw = _attn_kw(w)
     ref, lse_ref = oracle.attention(inp["q"], inp["kv"], inp["kv_raw"], inp["raw_pos0"], inp["q_pos"], inp["sinks"],
                                     idx=idx, **kw)
-    out, lse = cakv.sparse_mqa_fwd(_d(inp["q"]), _d(inp["kv"]), _d(idx), _d(inp["kv_raw"]), _d(inp["raw_pos0"]),
-                                   _d(inp["q_pos"]), _d(inp["sinks"]), **kw)
+    out, lse = cakv.sparse_mqa_fwd(_d(inp["q"]), _prep(inp["kv"], w.m, kw), _d(idx),
+                                   _prep_raw(inp["kv_raw"], inp["raw_pos0"], kw),
+                                   _d(inp["raw_pos0"]), _d(inp["q_pos"]), _d(inp["sinks"]), **kw)
     _attn_check(out.float().cpu().numpy().reshape(ref.shape), ref, "out bf16")
     assert np.abs(lse.cpu().numpy().reshape(lse_ref.shape) - lse_ref).max() < 1e-2
 
@@ -247,8 +302,9 @@ def test_dense_attention_hca_decode_1m():
     kw = _attn_kw(w)
     ref, lse_ref = oracle.attention(inp["q"], inp["kv"], inp["kv_raw"], inp["raw_pos0"], inp["q_pos"], inp["sinks"],
                                     **kw)
-    out, lse = cakv.dense_compressed_mqa_fwd(_d(inp["q"]), _d(inp["kv"]), _d(inp["kv_raw"]), _d(inp["raw_pos0"]),
-                                             _d(inp["q_pos"]), _d(inp["sinks"]), **kw)
+    out, lse = cakv.dense_compressed_mqa_fwd(_d(inp["q"]), _prep(inp["kv"], w.m, kw),
+                                             _prep_raw(inp["kv_raw"], inp["raw_pos0"], kw),
+                                             _d(inp["raw_pos0"]), _d(inp["q_pos"]), _d(inp["sinks"]), **kw)
     _attn_check(out.float().cpu().numpy().reshape(ref.shape), ref, "out bf16")
     assert np.abs(lse.cpu().numpy().reshape(lse_ref.shape) - lse_ref).max() < 1e-2
 
@@ -296,16 +352,17 @@ def test_prefill_chunk_256k_sampled_rows():
     assert recall >= 0.995 and gap <= 1e-3
 
     say("  CSA layer: sparse attention over the selection + window + sinks")
-    out, _ = cakv.sparse_mqa_fwd(_d(inp["q"]), _d(kvc), idx, kv_d, _d(inp["raw_pos0"]), _d(inp["q_pos"]),
-                                 _d(inp["sinks"]), want_lse=False, **kw)
+    win = _prep_raw(inp["kv"], inp["raw_pos0"], kw)
+    out, _ = cakv.sparse_mqa_fwd(_d(inp["q"]), _prep(kvc, w.m, kw), idx, win, _d(inp["raw_pos0"]),
+                                 _d(inp["q_pos"]), _d(inp["sinks"]), want_lse=False, **kw)
     ref, _ = oracle.attention(inp["q"][:, sel], kvc, inp["kv_raw"], inp["raw_pos0"], inp["q_pos"][:, sel],
                               inp["sinks"], idx=idx_rows, **kw)
     _attn_check(out[:, sel].float().cpu().numpy().reshape(ref.shape), ref, "CSA out")
 
     say("  HCA layer: dense attention over every visible entry + window + sinks")
     kwh = dict(kw, m=w.m_hca)
-    out, _ = cakv.dense_compressed_mqa_fwd(_d(inp["q_hca"]), _d(kvh), kv_d, _d(inp["raw_pos0"]), _d(inp["q_pos"]),
-                                           _d(inp["sinks_hca"]), want_lse=False, **kwh)
+    out, _ = cakv.dense_compressed_mqa_fwd(_d(inp["q_hca"]), _prep(kvh, w.m_hca, kw), win, _d(inp["raw_pos0"]),
+                                           _d(inp["q_pos"]), _d(inp["sinks_hca"]), want_lse=False, **kwh)
     ref, _ = oracle.attention(inp["q_hca"][:, sel], kvh, inp["kv_raw"], inp["raw_pos0"], inp["q_pos"][:, sel],
                               inp["sinks_hca"], **kwh)
     _attn_check(out[:, sel].float().cpu().numpy().reshape(ref.shape), ref, "HCA out")
@@ -331,16 +388,17 @@ def test_attention_edge_cases():
     idx[:, :, ::3] = -1
     kw = dict(m=4, n_win=4, rope_dims=64)
     ref, lse_ref = oracle.attention(q, kv, raw, raw0, qpos, sinks, idx=idx.numpy(), **kw)
-    out, lse = cakv.sparse_mqa_fwd(_d(q), _d(kv), _d(idx), _d(raw), _d(raw0), _d(qpos), _d(sinks),
+    kvp, rawp = _prep(kv, 4, kw), _prep_raw(raw, raw0, kw)
+    out, lse = cakv.sparse_mqa_fwd(_d(q), kvp, _d(idx), rawp, _d(raw0), _d(qpos), _d(sinks),
                                    out_dtype=torch.float32, **kw)
     _attn_check(out.cpu().numpy().reshape(ref.shape), ref, "sparse edge")
     ref2, _ = oracle.attention(q, kv, raw, raw0, qpos, sinks, **kw)
-    out2, _ = cakv.dense_compressed_mqa_fwd(_d(q), _d(kv), _d(raw), _d(raw0), _d(qpos), _d(sinks),
+    out2, _ = cakv.dense_compressed_mqa_fwd(_d(q), kvp, rawp, _d(raw0), _d(qpos), _d(sinks),
                                             out_dtype=torch.float32, **kw)
     _attn_check(out2.cpu().numpy().reshape(ref2.shape), ref2, "dense edge")
     # no window, no entries, -inf sinks: zero output, lse -inf
     sk = torch.full((H,), -math.inf)
-    out3, lse3 = cakv.dense_compressed_mqa_fwd(_d(q), _d(kv[:, :0]), _d(raw), _d(raw0), _d(qpos), _d(sk),
+    out3, lse3 = cakv.dense_compressed_mqa_fwd(_d(q), kvp[:, :0], rawp, _d(raw0), _d(qpos), _d(sk),
                                                out_dtype=torch.float32, m=4, n_win=0, rope_dims=64)
     assert torch.all(out3 == 0) and torch.all(torch.isneginf(lse3))
 
@@ -363,7 +421,8 @@ def test_attention_needle_forces_exact_max_pass():
     sinks = torch.randn(H, generator=g)
     kw = dict(m=4, n_win=128, rope_dims=0)
     ref, _ = oracle.attention(q, kv, raw, raw0, qpos, sinks, **kw)
-    out, _ = cakv.dense_compressed_mqa_fwd(_d(q), _d(kv), _d(raw), _d(raw0), _d(qpos), _d(sinks),
+    out, _ = cakv.dense_compressed_mqa_fwd(_d(q), _prep(kv, 4, kw), _prep_raw(raw, raw0, kw), _d(raw0), _d(qpos),
+                                           _d(sinks),
                                            out_dtype=torch.float32, **kw)
     _attn_check(out.cpu().numpy().reshape(ref.shape), ref, "needle")
     assert np.abs(ref[0, 5]).max() > 0.5  # the needle dominates that head
@@ -374,8 +433,9 @@ def test_determinism():
     inp = make_inputs("csa_decode_128k", B=4)
     w = inp["workload"]
     idx = torch.randint(0, w.N, (w.B, w.Q, w.k), dtype=torch.int32)
-    args = (_d(inp["q"]), _d(inp["kv"]), _d(idx), _d(inp["kv_raw"]), _d(inp["raw_pos0"]), _d(inp["q_pos"]),
-            _d(inp["sinks"]))
+    args = (_d(inp["q"]), _prep(inp["kv"], w.m, _attn_kw(w)), _d(idx),
+            _prep_raw(inp["kv_raw"], inp["raw_pos0"], _attn_kw(w)), _d(inp["raw_pos0"]),
+            _d(inp["q_pos"]), _d(inp["sinks"]))
     a, la = cakv.sparse_mqa_fwd(*args, **_attn_kw(w))
     b, lb = cakv.sparse_mqa_fwd(*args, **_attn_kw(w))
     assert torch.equal(a, b) and torch.equal(la, lb)
