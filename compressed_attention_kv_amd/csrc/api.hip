@@ -69,6 +69,7 @@ int attn_splits(int64_t BQ, int64_t max_slots) {
 
 size_t attn_workspace(int64_t BQ, int32_t H, int32_t D, int64_t max_slots) {
     const int S = attn_splits(BQ, max_slots);
+    if (S == 1) return 0;  // one split: the forward kernel writes the output itself
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     return al((size_t)BQ * S * ((H + 1) / 2) * D * 4) + al((size_t)BQ * S * H * 2 * 4);
 }
@@ -143,11 +144,13 @@ int run_attn(cakv::AttnArgs& a, int64_t BQ, int32_t H, int32_t D, int64_t max_sl
     const int S = attn_splits(BQ, max_slots);
     const size_t need = attn_workspace(BQ, H, D, max_slots);
     REQUIRE(ws_bytes >= need, CAKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
-    REQUIRE(ws && (reinterpret_cast<uintptr_t>(ws) & 255u) == 0, CAKV_EWORKSPACE,
-            "workspace must be non-NULL and 256-byte aligned");
-    a.part_o = reinterpret_cast<uint32_t*>(ws);
-    a.part_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) +
-                                         (((size_t)BQ * S * ((H + 1) / 2) * D * 4 + 255) & ~(size_t)255));
+    if (need > 0) {
+        REQUIRE(ws && (reinterpret_cast<uintptr_t>(ws) & 255u) == 0, CAKV_EWORKSPACE,
+                "workspace must be non-NULL and 256-byte aligned");
+        a.part_o = reinterpret_cast<uint32_t*>(ws);
+        a.part_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) +
+                                             (((size_t)BQ * S * ((H + 1) / 2) * D * 4 + 255) & ~(size_t)255));
+    }
     a.n_splits = S;
     return rc_from(cakv::launch_mqa_fwd(a, BQ, D, act_f32, reinterpret_cast<hipStream_t>(stream)));
 }

@@ -234,7 +234,10 @@ struct MmaOp<true> {
     }
 };
 
-template <int D, bool SPARSE, typename TIn>
+// FINAL: the launch has one split per query and writes the output itself
+// (two instantiations rather than a runtime branch: the final epilogue's
+// values would otherwise stay live in scalar registers across the tile loop).
+template <int D, bool SPARSE, typename TIn, bool FINAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mqa_fwd_kernel(const AttnArgs a) {
     constexpr int G = D / 8;                   // 16-byte bf16 granules per K row
@@ -276,6 +279,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
     __shared__ __attribute__((aligned(16))) float2 qcs[kMaxRopePairs];
     __shared__ __attribute__((aligned(16))) float fq_s[D];   // gamma_q
     __shared__ __attribute__((aligned(16))) float il_s[4][32];  // 1/l of each head (epilogue)
+    __shared__ float sink_s[FINAL ? 128 : 1];  // sink logits, log2 units (one-split epilogue)
     __shared__ uint32_t redo;
 
     const int tid = threadIdx.x;
@@ -345,39 +349,37 @@ void mqa_fwd_kernel(const AttnArgs a) {
     };
 
     // ---------------------------------------------------------------- prologue
-    // The query rows are requested first; while they and the first tiles'
-    // entry indices are in flight, wave 0 fills the rotation tables.  Then
-    // the first three tiles start landing and Q~ is built in registers.
+    // Wave 0 requests the entry indices of the first five tiles, then all
+    // waves request their query rows; while those are in flight wave 1 fills
+    // the rotation table and wave 0 turns the indices into the metadata of the
+    // first four tiles.  The first three tiles start landing before the query
+    // rows are awaited, and Q~ is built while they land.
     const bool has_heads = 32 * wave < H;
     const int qhead = 32 * wave + lrow;
-    typename LD::raw_t qr[KSTEPS];  // lane: head qhead, channels 16 s + 8 lh + (0..7)
-    {
-        const TIn* qrow = reinterpret_cast<const TIn*>(a.q) + (bq * H + (qhead < H ? qhead : 0)) * (int64_t)D + 8 * lh;
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) qr[s] = qhead < H ? LD::load(qrow + 16 * s) : LD::zero();
-    }
-    if (wave == 0 && lane < n_pairs) {
-        const double tn = rope_turns(a.rope_base, lane, a.rope_dims);
-        float sn, cs;
-        sincos_turns((double)g.t * tn, &sn, &cs);
-        qcs[lane] = make_float2(cs, sn);
-    }
-    for (int i = tid; i < D; i += 256) fq_s[i] = a.gamma_q ? a.gamma_q[i] : 1.0f;
     // metadata of the first four tiles and the indices of the fifth (the
     // entry-index loads are all issued before any is used)
-    auto meta_start = [&]() __attribute__((always_inline)) {
+    int32_t jst[5];
+    auto meta_issue = [&]() __attribute__((always_inline)) {
         if (wave == 0) {
             const int ol = opaque_tid() & 63;
-            int32_t j[5];
 #pragma unroll
             for (int k = 0; k < 5; ++k) {
                 const int t = tile0 + k;
-                j[k] = (SPARSE && ol < TK && t < tile1) ? slot_entry<SPARSE>(a, g, bq, t * TK + ol) : 0;
+                jst[k] = (SPARSE && ol < TK && t < tile1) ? slot_entry<SPARSE>(a, g, bq, t * TK + ol) : 0;
             }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) tile_meta(tile0 + k, k, j[k]);
-            if (SPARSE) idxs[4][ol] = j[4];
         }
+    };
+    auto meta_finish = [&]() __attribute__((always_inline)) {
+        if (wave == 0) {
+            const int ol = opaque_tid() & 63;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) tile_meta(tile0 + k, k, jst[k]);
+            if (SPARSE) idxs[4][ol] = jst[4];
+        }
+    };
+    auto meta_start = [&]() __attribute__((always_inline)) {
+        meta_issue();
+        meta_finish();
     };
     // the first three tiles start landing; T0 is prepared once it has
     auto start_tiles = [&]() __attribute__((always_inline)) {
@@ -385,32 +387,79 @@ void mqa_fwd_kernel(const AttnArgs a) {
         if (tile0 + 1 < tile1) tile_load(1, ring[1]);
         if (tile0 + 2 < tile1) tile_load(2, ring[2]);
     };
-    meta_start();
-    barrier_vm<0>();  // (the query rows have landed too)
+    meta_issue();
+    // small parameters are requested before the query rows, so that storing
+    // them in LDS does not wait for those (loads complete in issue order)
+    const bool has_gq = a.gamma_q != nullptr;
+    constexpr int GQ = (D + 255) / 256;
+    float gq_pre[GQ];
+#pragma unroll
+    for (int k = 0; k < GQ; ++k) gq_pre[k] = (has_gq && tid + 256 * k < D) ? a.gamma_q[tid + 256 * k] : 1.0f;
+    const float sink_pre = (FINAL && tid < H) ? a.sinks[tid] : 0.0f;
+    typename LD::raw_t qr[KSTEPS];  // lane: head qhead, channels 16 s + 8 lh + (0..7)
+    {
+        const TIn* qrow = reinterpret_cast<const TIn*>(a.q) + (bq * H + (qhead < H ? qhead : 0)) * (int64_t)D + 8 * lh;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) qr[s] = qhead < H ? LD::load(qrow + 16 * s) : LD::zero();
+    }
+    if (wave == 1 && lane < n_pairs) {
+        const double tn = rope_turns(a.rope_base, lane, a.rope_dims);
+        float sn, cs;
+        sincos_turns((double)g.t * tn, &sn, &cs);
+        qcs[lane] = make_float2(cs, sn);
+    }
+#pragma unroll
+    for (int k = 0; k < GQ; ++k)
+        if (has_gq && tid + 256 * k < D) fq_s[tid + 256 * k] = gq_pre[k];
+    if (FINAL && tid < H) sink_s[tid] = sink_pre * 1.4426950408889634f;
+    meta_finish();
+    barrier_lds();  // metadata, rotation table and gamma_q visible
     start_tiles();
+    // the query rows are older than the tile copies just issued
+    if (tile0 + 2 < tile1) wait_vm<3 * NU>();
+    else if (tile0 + 1 < tile1) wait_vm<2 * NU>();
+    else if (tile0 < tile1) wait_vm<NU>();
+    else wait_vm<0>();
 
-    // Q~ = RoPE_t(gamma_q * q / rms(q)) * softmax scale * log2(e), in the
-    // B-operand layout of the QK MFMAs:
-    // lane (head lrow, half lh) holds channels 16 s + 8 lh + (0..7) for
-    // k-step s, so a head's sum of squares is this lane's plus lane l ^ 32's.
+    // Q~ = RoPE_t(gamma_q * q) in the B-operand layout of the QK MFMAs: lane
+    // (head lrow, half lh) holds channels 16 s + 8 lh + (0..7) for k-step s,
+    // so a head's sum of squares is this lane's plus lane l ^ 32's.  The
+    // head's 1/rms(q) and the softmax scale (times log2 e) multiply its
+    // logits instead: invq, per lane (the logits' column is the head).  f16
+    // operands (f32 activations) take 1/rms inside Q~ to bound their range.
     opvec qf[KSTEPS];
+    float invq;
     {
         float ss = 0.0f;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) ss = LD::sumsq(qr[s], ss);
         ss = xor32_sum(ss);
-        const float inv = __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps) * a.scale_log2;
+        const float inv = __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps);
+        invq = RAW_F32 ? a.scale_log2 : inv * a.scale_log2;
+        const float qs = RAW_F32 ? inv : 1.0f;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
+            const int d0 = 16 * s + 8 * lh;  // this lane's 8-channel chunk
+            const bool rot_any = 16 * s + 16 > rope_lo;  // uniform
+            if constexpr (!RAW_F32) {
+                if (!has_gq && !rot_any) {  // uniform: the bf16 row as it is
+                    qf[s] = __builtin_bit_cast(opvec, qr[s]);
+                    continue;
+                }
+            }
             float v[8];
             LD::to_f32(qr[s], v);
-            const int d0 = 16 * s + 8 * lh;  // this lane's 8-channel chunk
-            const f32x4 f0 = *reinterpret_cast<const f32x4*>(&fq_s[d0]);
-            const f32x4 f1 = *reinterpret_cast<const f32x4*>(&fq_s[d0 + 4]);
+            if (has_gq) {
+                const f32x4 f0 = *reinterpret_cast<const f32x4*>(&fq_s[d0]);
+                const f32x4 f1 = *reinterpret_cast<const f32x4*>(&fq_s[d0 + 4]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[i] *= inv * f0[i];
-                v[4 + i] *= inv * f1[i];
+                for (int i = 0; i < 4; ++i) {
+                    v[i] *= qs * f0[i];
+                    v[4 + i] *= qs * f1[i];
+                }
+            } else if (RAW_F32) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] *= qs;
             }
             // which channels of k-step s rotate is the same for the whole
             // wave (both halves) unless the boundary falls inside the step
@@ -525,7 +574,9 @@ void mqa_fwd_kernel(const AttnArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, QPF, 2);
-        // logits are in log2 units (Q~ carries the softmax scale)
+        // logits in log2 units: the head's 1/rms(q) times the softmax scale
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[r] *= invq;
         float mx = -INFINITY;
         if (mask != 0xffffffffu) {
             const uint32_t mrow = mask >> (4 * oh);  // rows 8*(r/4) + 4*oh + r%4
@@ -698,12 +749,12 @@ void mqa_fwd_kernel(const AttnArgs a) {
             float m0 = -INFINITY;
 #pragma unroll
             for (int r = 0; r < 16; ++r) m0 = fmaxf(m0, st[r]);
-            m0 = xor32_max(m0);
+            m0 = xor32_max(m0) * invq;
             m_use = (m_use == -INFINITY) ? m0 : m_use;
         }
         float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = st[r] - m_use;
+        for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(st[r], invq, -m_use);
         uint32_t pk[8];
         float psum = 0.0f;
 #pragma unroll
@@ -821,13 +872,100 @@ void mqa_fwd_kernel(const AttnArgs a) {
     if (!has_heads) return;
 
     // ---------------------------------------------------------------- epilogue
-    // (max, sum) of this split and its output normalised by its own sum, O/l
-    // (a convex combination of normalised rows, so fp16 holds it), with the
-    // heads of an even/odd pair packed in one word.  The combine kernel folds
-    // in the sink, merges the splits, rotates back and stores.
     // (lane indices re-derived here: nothing lane-dependent stays live across the loop)
     const int el = opaque_tid() & 63, erow = el & 31, eh = el >> 5;
     const int head = 32 * wave + erow;
+    if constexpr (FINAL) {
+        // One split: the final output straight from the accumulator.  Per head,
+        // in log2 units, Z = l + 2^(sink - m_use) and out = O / Z; the last r
+        // channels are rotated back by -t (channel pairs sit in lanes 2i, 2i+1);
+        // lse = ln 2 * (m_use + log2 Z).  No keys: out = 0, lse = the sink.
+        if (el < 32) {
+            const float sk = head < H ? sink_s[head] : -INFINITY;
+            float zi = 0.0f, lse = sk;
+            if (m_use != -INFINITY) {
+                const float z = l_run + __builtin_amdgcn_exp2f(sk - m_use);
+                zi = 1.0f / z;
+                lse = m_use + __builtin_log2f(z);
+            }
+            il_s[wave][erow] = zi;
+            if (head < H && a.lse) a.lse[bq * H + head] = lse * 0.6931471805599453f;
+        }
+        f32x4 zi[4];  // 1/Z of this lane's accumulator rows 8 (r/4) + 4 eh + r%4
+#pragma unroll
+        for (int m = 0; m < 4; ++m) zi[m] = *reinterpret_cast<const f32x4*>(&il_s[wave][8 * m + 4 * eh]);
+        // rope_dims <= 64, so only the last two column tiles hold rotated
+        // channels; the rotation by -t reuses the query's table of +t
+        float rsn[2], rcs[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int d = 32 * (DT - 2 + k) + erow;
+            rsn[k] = 0.0f;
+            rcs[k] = 1.0f;
+            if (DT - 2 + k >= 0 && d >= rope_lo) {
+                const float2 c = qcs[(d - rope_lo) >> 1];
+                rcs[k] = c.x;
+                rsn[k] = -c.y;
+            }
+        }
+        // Rows r, r+1 of a column-pair of lanes (2i, 2i+1) become two 4-byte
+        // bf16 pairs (8 bytes for f32): the even lane sends row r+1's value and
+        // the odd lane row r's, so the even lane holds row r's channel pair and
+        // the odd lane row r+1's.  bf16 rows are then staged in this wave's
+        // (now idle) tile buffer and leave as whole rows, 16 bytes per lane;
+        // the word index of rows 4..7 of each group of 8 is XORed with 32 so
+        // that the four rows one write instruction touches use distinct banks.
+        const bool odd = erow & 1;
+        const bool f32o = a.out_f32 != 0;
+        uint8_t* ob = ring[wave];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const bool tile_rot = dt >= DT - 2 && 32 * dt + 32 > rope_lo;  // uniform
+            const float sn = dt >= DT - 2 ? rsn[dt - (DT - 2)] : 0.0f;
+            const float cs = dt >= DT - 2 ? rcs[dt - (DT - 2)] : 1.0f;
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                float v[2];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    v[k] = acc[dt][r + k] * zi[(r + k) >> 2][(r + k) & 3];
+                    if (tile_rot) {
+                        const float o = lane_swap1(v[k]);  // the other channel of the pair
+                        v[k] = odd ? o * sn + v[k] * cs : v[k] * cs - o * sn;
+                    }
+                }
+                const float recv = lane_swap1(odd ? v[0] : v[1]);
+                const float lo = odd ? recv : v[0], hi = odd ? v[1] : recv;
+                const int row = 8 * (r >> 2) + 4 * eh + (r & 3) + (odd ? 1 : 0);
+                if (f32o) {
+                    const int hr = 32 * wave + row;
+                    if (hr < H)
+                        *reinterpret_cast<float2*>(reinterpret_cast<float*>(a.out) + (bq * H + hr) * (int64_t)D + 32 * dt +
+                                                   (erow & ~1)) = make_float2(lo, hi);
+                } else {
+                    const int word = (16 * dt + (erow >> 1)) ^ (((row >> 2) & 1) << 5);
+                    *reinterpret_cast<uint32_t*>(ob + row * RS + 4 * word) = pack_bf16x2(lo, hi);
+                }
+            }
+        }
+        if (!f32o) {
+            constexpr int LPRO = D / 8;     // lanes per bf16 output row (16 bytes each)
+            constexpr int RPI = 64 / LPRO;  // rows per instruction
+#pragma unroll
+            for (int h0 = 0; h0 < 32; h0 += RPI) {
+                const int h = h0 + el / LPRO, c = el % LPRO;
+                const int hr = 32 * wave + h;
+                const u32x4 w = *reinterpret_cast<const u32x4*>(ob + h * RS + 4 * ((4 * c) ^ (((h >> 2) & 1) << 5)));
+                if (hr < H)
+                    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + (bq * H + hr) * (int64_t)D + 8 * c) = w;
+            }
+        }
+        return;
+    }
+    // Several splits: (max, sum) of this split and its output normalised by its
+    // own sum, O/l (a convex combination of normalised rows, so fp16 holds it),
+    // with the heads of an even/odd pair packed in one word.  The combine
+    // kernel folds in the sink, merges the splits, rotates back and stores.
     const int S = a.n_splits;
     const int64_t base = (bq * S + split) * (int64_t)H;
     if (el < 32) {
@@ -853,9 +991,12 @@ void mqa_fwd_kernel(const AttnArgs a) {
 }
 
 // Merge split partials: one workgroup per (query, head pair), one thread per
-// channel pair (so the inverse rotation of a pair stays in one thread).
+// channel pair (so the inverse rotation of a pair stays in one thread).  One
+// pass over the splits with a running maximum (log2 units): the loads of
+// eight splits are issued before any of their arithmetic.
 template <int D>
 __global__ __launch_bounds__(256) void mqa_combine_kernel(const AttnArgs a) {
+    constexpr int SB = 8;  // splits per batch of loads
     const int H = a.H, Hp = (H + 1) >> 1;
     const int64_t wg = xcd_order(blockIdx.x, gridDim.x);
     const int64_t bq = wg / Hp;
@@ -870,24 +1011,39 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(const AttnArgs a) {
     for (int e = 0; e < 2; ++e) {
         const int h = 2 * hp + (e < nh ? e : 0);
         M[e] = a.sinks[h] * LOG2E;
-        for (int s = 0; s < S; ++s) M[e] = fmaxf(M[e], a.part_ml[((bq * S + s) * H + h) * 2]);
-        Z[e] = M[e] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(a.sinks[h] * LOG2E - M[e]);
+        Z[e] = M[e] == -INFINITY ? 0.0f : 1.0f;
         o[e][0] = o[e][1] = 0.0f;
     }
-    for (int s = 0; s < S; ++s) {
-        const uint2 wv = *reinterpret_cast<const uint2*>(a.part_o + ((bq * S + s) * Hp + hp) * (int64_t)D + 2 * pr);
+    const uint2* po = reinterpret_cast<const uint2*>(a.part_o) + (bq * S * Hp + hp) * (int64_t)(D / 2) + pr;
+    const float2* pml = reinterpret_cast<const float2*>(a.part_ml) + bq * S * H + 2 * hp;
+    for (int s0 = 0; s0 < S; s0 += SB) {
+        uint2 wv[SB];
+        float2 ml[SB][2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            if (e >= nh) continue;
-            const int64_t mi = ((bq * S + s) * H + 2 * hp + e) * 2;
-            const float ms = a.part_ml[mi];
-            if (ms == -INFINITY || M[e] == -INFINITY) continue;
-            const float wl = __builtin_amdgcn_exp2f(ms - M[e]) * a.part_ml[mi + 1];
-            Z[e] += wl;
-            const float v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(e ? wv.x >> 16 : wv.x & 0xffffu));
-            const float v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(e ? wv.y >> 16 : wv.y & 0xffffu));
-            o[e][0] = __builtin_fmaf(wl, v0, o[e][0]);
-            o[e][1] = __builtin_fmaf(wl, v1, o[e][1]);
+        for (int j = 0; j < SB; ++j) {
+            const int s = s0 + j < S ? s0 + j : S - 1;  // past the end: repeat the last, unused
+            wv[j] = po[(int64_t)s * Hp * (D / 2)];
+            ml[j][0] = pml[(int64_t)s * H];
+            ml[j][1] = pml[(int64_t)s * H + (nh > 1 ? 1 : 0)];
+        }
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            if (s0 + j >= S) break;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                if (e >= nh) continue;
+                const float ms = ml[j][e].x;
+                if (ms == -INFINITY) continue;
+                const float mn = fmaxf(M[e], ms);
+                const float keep = M[e] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M[e] - mn);
+                const float wl = __builtin_amdgcn_exp2f(ms - mn) * ml[j][e].y;
+                const float v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(e ? wv[j].x >> 16 : wv[j].x & 0xffffu));
+                const float v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(e ? wv[j].y >> 16 : wv[j].y & 0xffffu));
+                Z[e] = __builtin_fmaf(Z[e], keep, wl);
+                o[e][0] = __builtin_fmaf(wl, v0, o[e][0] * keep);
+                o[e][1] = __builtin_fmaf(wl, v1, o[e][1] * keep);
+                M[e] = mn;
+            }
         }
     }
     const int rope_lo = D - a.rope_dims;
@@ -911,7 +1067,7 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(const AttnArgs a) {
         if (a.out_f32) {
             *reinterpret_cast<float2*>(reinterpret_cast<float*>(a.out) + off) = make_float2(o0, o1);
         } else {
-            reinterpret_cast<uint32_t*>(a.out)[off >> 1] = f32_to_bf16_bits(o0) | (f32_to_bf16_bits(o1) << 16);
+            reinterpret_cast<uint32_t*>(a.out)[off >> 1] = pack_bf16x2(o0, o1);
         }
         if (pr == 0 && a.lse)
             a.lse[bq * H + h] = (M[e] == -INFINITY) ? -INFINITY : (M[e] + __builtin_log2f(Z[e])) * 0.6931471805599453f;
@@ -922,9 +1078,13 @@ template <int D, bool SPARSE, typename TIn>
 static int launch_one(const AttnArgs& a, int64_t BQ, hipStream_t stream) {
     dim3 grid((unsigned)a.n_splits, (unsigned)BQ);
     prof_mark("mqa_fwd_kernel", false, stream);
-    hipLaunchKernelGGL((mqa_fwd_kernel<D, SPARSE, TIn>), grid, dim3(256), 0, stream, a);
+    if (a.n_splits == 1)
+        hipLaunchKernelGGL((mqa_fwd_kernel<D, SPARSE, TIn, true>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((mqa_fwd_kernel<D, SPARSE, TIn, false>), grid, dim3(256), 0, stream, a);
     prof_mark("mqa_fwd_kernel", true, stream);
     if (hipGetLastError() != hipSuccess) return -4;
+    if (a.n_splits == 1) return 0;  // the forward kernel wrote the output itself
     prof_mark("mqa_combine_kernel", false, stream);
     hipLaunchKernelGGL((mqa_combine_kernel<D>), dim3((unsigned)(BQ * ((a.H + 1) / 2))), dim3(D / 2 < 64 ? 64 : D / 2),
                        0, stream, a);

@@ -126,6 +126,11 @@ __device__ __forceinline__ float dpp_add(float v) {
     return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
 }
 
+// v of the neighbouring lane l ^ 1 (DPP quad_perm [1,0,3,2]), all lanes active
+__device__ __forceinline__ float lane_swap1(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xf, 0xf, true));
+}
+
 // Sum over each row of 16 lanes, returned in every lane of the row: four DPP
 // butterfly steps (lane ^ 1, lane ^ 2, then the 8- and 16-lane mirrors, which
 // pair each lane with one in the other half), no LDS round trip.

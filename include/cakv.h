@@ -210,7 +210,9 @@ typedef struct cakv_attn_params {
  *   lse     [B, Q, H]     float32 log-sum-exp (natural log) incl. the sink, or NULL
  * A query with no keys and a -inf sink gets a zero output and lse = -inf.
  * Supported: D in {64, 128, 256, 512}, 1 <= H <= 128, K <= 65536.
- * Workspace: cakv_sparse_mqa_workspace(...) bytes (0 is possible), 256-byte aligned.
+ * Workspace: cakv_sparse_mqa_workspace(...) bytes, 256-byte aligned.  It holds
+ * the partials of the key-range splits; 0 (workspace may be NULL) when every
+ * query runs as a single split, whose kernel writes the output directly.
  * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE.
  * ------------------------------------------------------------------------- */
 size_t cakv_sparse_mqa_workspace(int64_t B, int64_t Q, int32_t H, int32_t D, int32_t K,

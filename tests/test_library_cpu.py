@@ -44,7 +44,7 @@ FAKE = 0x10000  # 16-byte aligned non-NULL address; validation rejects before it
 
 def _sparse(lib, prm, **kw):
     a = dict(q=FAKE, kv_c=FAKE, idx=FAKE, kv_raw=FAKE, raw0=FAKE, qpos=FAKE, sinks=FAKE, act=cakv.BF16, B=1,
-             Q=1, H=128, D=512, N=16, K=8, R=4, out=FAKE, odt=cakv.BF16, lse=None, ws=FAKE, wsb=1 << 30)
+             Q=1, H=128, D=512, N=16, K=1024, R=4, out=FAKE, odt=cakv.BF16, lse=None, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return lib.cakv_sparse_mqa_fwd(ctypes.byref(prm), a["q"], a["kv_c"], a["idx"], a["kv_raw"], a["raw0"],
                                    a["qpos"], a["sinks"], a["act"], a["B"], a["Q"], a["H"], a["D"], a["N"], a["K"],
@@ -121,6 +121,8 @@ def test_workspace_queries_are_monotone(lib):
     b = lib.cakv_dense_mqa_workspace(32, 1, 128, 512, 8192, 128)
     assert a > 0 and b > 0
     assert lib.cakv_sparse_mqa_workspace(64, 1, 128, 512, 1024, 128) >= a
+    # enough queries to fill the GPU with one split each: no partials, no workspace
+    assert lib.cakv_sparse_mqa_workspace(1, 8192, 128, 512, 1024, 128) == 0
 
 
 def test_profile_kernel_events_arguments(lib):

@@ -392,6 +392,9 @@ def test_attention_edge_cases():
     out, lse = cakv.sparse_mqa_fwd(_d(q), kvp, _d(idx), rawp, _d(raw0), _d(qpos), _d(sinks),
                                    out_dtype=torch.float32, **kw)
     _attn_check(out.cpu().numpy().reshape(ref.shape), ref, "sparse edge")
+    lg = lse.cpu().numpy().reshape(lse_ref.shape)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lg), fin) and np.abs(lg[fin] - lse_ref[fin]).max() < 1e-2  # bf16 logits
     ref2, _ = oracle.attention(q, kv, raw, raw0, qpos, sinks, **kw)
     out2, _ = cakv.dense_compressed_mqa_fwd(_d(q), kvp, rawp, _d(raw0), _d(qpos), _d(sinks),
                                             out_dtype=torch.float32, **kw)
