@@ -126,6 +126,19 @@ __device__ __forceinline__ float dpp_add(float v) {
     return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
 }
 
+// max(v, +0) on the bit pattern (negative floats are negative integers):
+// one integer max, no NaN canonicalisation.  Through scalar copies, like
+// word_as_bf16x2: a bit cast written directly on an ext_vector element has
+// been compiled as if it named element 0.
+__device__ __forceinline__ float relu_bits(float v) {
+    int b;
+    __builtin_memcpy(&b, &v, 4);
+    b = b > 0 ? b : 0;
+    float r;
+    __builtin_memcpy(&r, &b, 4);
+    return r;
+}
+
 // v of the neighbouring lane l ^ 1 (DPP quad_perm [1,0,3,2]), all lanes active
 __device__ __forceinline__ float lane_swap1(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xf, 0xf, true));

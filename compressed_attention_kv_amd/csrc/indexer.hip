@@ -49,48 +49,19 @@ __device__ __forceinline__ void flush_hist(const uint32_t* h, uint32_t* g, int n
 
 // ------------------------------------------------------------------ fp8 mode
 // HT: head tiles of 32 (HI = 32*HT); KS: MFMA k-steps of 16 (dI = 16*KS).
-// Each wave streams its own 32-entry key groups (j0 = j_begin + 32 wave +
-// 128 n) through a private ring of kSlots LDS slots filled by asynchronous
-// HBM->LDS copies, kSlots - 1 groups ahead of the group it multiplies: the
-// bytes in flight cost no registers and no barrier (the wave that copies a
-// group is the one that reads it).  In a slot, 16-byte chunk c of row r holds
-// the row's chunk c ^ (r mod chunks-per-row), which makes the per-row operand
-// reads conflict-free.
-constexpr int kSlots = 4;  // at most 4 (wait_groups)
-
-template <int DI>
-struct ScoreRing {
-    static constexpr int GB = 32 * DI;        // key bytes of a group
-    static constexpr int NDMA = GB / 1024;    // 16-byte-per-lane copies of a group
-    static constexpr int CPR = DI / 16;       // 16-byte chunks per row
-    static constexpr int SLOT = GB + 256;     // keys, then 64 scales (32 used)
-    static constexpr int OPS = NDMA + 1;      // vector-memory operations per group
-};
-
-// Wait for a group's copies when nd later groups' copies (ops vector-memory
-// operations each) and ns single stores were issued after them (wave-uniform
-// nd, ns < kSlots).
-template <int OPS>
-__device__ __forceinline__ void wait_groups(int nd, int ns) {
-    switch (nd * 4 + ns) {
-#define CAKV_WAIT_CASE(d, s) \
-    case (d) * 4 + (s): wait_vm<(d) * OPS + (s)>(); break;
-        CAKV_WAIT_CASE(0, 0) CAKV_WAIT_CASE(0, 1) CAKV_WAIT_CASE(0, 2) CAKV_WAIT_CASE(0, 3)
-        CAKV_WAIT_CASE(1, 0) CAKV_WAIT_CASE(1, 1) CAKV_WAIT_CASE(1, 2) CAKV_WAIT_CASE(1, 3)
-        CAKV_WAIT_CASE(2, 0) CAKV_WAIT_CASE(2, 1) CAKV_WAIT_CASE(2, 2) CAKV_WAIT_CASE(2, 3)
-        CAKV_WAIT_CASE(3, 0) CAKV_WAIT_CASE(3, 1) CAKV_WAIT_CASE(3, 2) CAKV_WAIT_CASE(3, 3)
-#undef CAKV_WAIT_CASE
-        default: wait_vm<0>(); break;
-    }
-}
+// Each wave streams its own 32-entry key groups (entries first + 128 n +
+// lrow) straight into VGPRs with ordinary vector loads, kPD groups ahead of
+// the group it multiplies (a ring of kPD + 1 register sets, indexed
+// statically by unrolling): lane (entry lrow, half lh) loads the half row it
+// multiplies and the entry's scale.
+constexpr int kPD = 3;  // groups in flight ahead of the one multiplied
 
 template <int HT, int KS>
 __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs a) {
     constexpr int DI = 16 * KS;
-    typedef ScoreRing<DI> R;
     constexpr int HALF = DI / 2;        // bytes of a key row per half-wave lane
     constexpr int NLD = HALF / 16;      // 16-byte chunks per lane
-    __shared__ __attribute__((aligned(16))) uint8_t ring[4][kSlots][R::SLOT];
+    constexpr int RS = kPD + 1;         // register sets in the ring
     __shared__ uint32_t hist[kHistBins];
 
     const int64_t bq = blockIdx.y;
@@ -99,7 +70,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
     if (nvis <= a.k || j_begin >= nvis) return;
     const int64_t j_end = min(nvis, j_begin + a.chunk);
     const int tid = threadIdx.x, lane = tid & 63, lrow = lane & 31, lh = lane >> 5;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: ring addresses go to M0
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t first = j_begin + 32 * wave;
     const int ng = first < j_end ? (int)((j_end - first + 127) / 128) : 0;
 
@@ -107,27 +78,25 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_idx) + b * a.N * DI;
     const float* sbase = a.k_scale + b * a.N;
     uint32_t* kout = a.keys + bq * a.N;
-    uint8_t* slots = &ring[wave][0][0];
 
-    // copies of group n into slot n % kSlots (rows past the cache end read
-    // its last row: in bounds, never scored)
-    auto issue = [&](int n) {
-        const int64_t j0 = first + 128 * (int64_t)n;
-        uint8_t* slot = slots + (n % kSlots) * R::SLOT;
-#pragma unroll
-        for (int i = 0; i < R::NDMA; ++i) {
-            const int o = 1024 * i + 16 * lane;
-            const int r = o / DI, c = (o % DI) / 16;
-            const int64_t row = min(j0 + r, a.N - 1);
-            lds_dma16(kbase + row * DI + 16 * (c ^ (r & (R::CPR - 1))), (uint32_t)(uintptr_t)(slot + 1024 * i));
-        }
-        lds_dma4(sbase + min(j0 + lane, a.N - 1), (uint32_t)(uintptr_t)(slot + R::GB));
+    // group n's half rows and scales (rows past the cache end read its last
+    // row: in bounds, never scored)
+    struct Grp {
+        u32x4 c[NLD];
+        float sc;
     };
+    auto load_group = [&](int n, Grp& g) __attribute__((always_inline)) {
+        const int64_t row = min(first + 128 * (int64_t)n + lrow, a.N - 1);
+        const u32x4* src = reinterpret_cast<const u32x4*>(kbase + row * DI + lh * HALF);
 #pragma unroll
-    for (int n = 0; n < kSlots - 1; ++n)
-        if (n < ng) issue(n);
+        for (int i = 0; i < NLD; ++i) g.c[i] = src[i];
+        g.sc = sbase[row];
+    };
+    Grp ring[RS];
+#pragma unroll
+    for (int n = 0; n < kPD; ++n)
+        if (n < ng) load_group(n, ring[n]);
     for (int i = tid; i < kHistBins; i += 256) hist[i] = 0u;
-    barrier_lds();  // the copies stay in flight
 
     // A operand: query heads (rows) x features, k-permutation (s, half, e) -> half*DI/2 + 8s + e
     bf16x8 qa[HT][KS];
@@ -142,20 +111,9 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
 #pragma unroll
         for (int r = 0; r < 16; ++r) wv[ht][r] = a.w[bq * (32 * HT) + 32 * ht + 8 * (r >> 2) + 4 * lh + (r & 3)];
     }
+    __syncthreads();  // the histogram is clear
 
-    for (int n = 0; n < ng; ++n) {
-        // issue order: key store of group n-1, copies of group n+kSlots-1;
-        // then wait for group n: after its copies came the copies of groups
-        // n+1..min(n+kSlots-1, ng-1) and the stores of groups max(n-kSlots+1,0)..n-1
-        const int nd = min(kSlots - 1, ng - 1 - n), ns = min(n, kSlots - 1);
-        if (n + kSlots - 1 < ng) issue(n + kSlots - 1);
-        wait_groups<R::OPS>(nd, ns);
-        const uint8_t* slot = slots + (n % kSlots) * R::SLOT;
-        u32x4 cur[NLD];
-#pragma unroll
-        for (int i = 0; i < NLD; ++i)
-            cur[i] = *reinterpret_cast<const u32x4*>(slot + lrow * DI + 16 * ((lh * NLD + i) ^ (lrow & (R::CPR - 1))));
-        const float sc = *reinterpret_cast<const float*>(slot + R::GB + 4 * lrow);
+    auto score_group = [&](int n, const Grp& g) __attribute__((always_inline)) {
         f32x16 acc[HT];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht)
@@ -164,7 +122,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             // 8 fp8 bytes = dwords (2s, 2s+1) of this lane's half row
-            const uint32_t d0 = cur[s >> 1][(s & 1) * 2], d1 = cur[s >> 1][(s & 1) * 2 + 1];
+            const uint32_t d0 = g.c[s >> 1][(s & 1) * 2], d1 = g.c[s >> 1][(s & 1) * 2 + 1];
             u32x4 kb4;
             kb4[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false));
             kb4[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true));
@@ -179,20 +137,25 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float v = acc[ht][r];
-                sum = __builtin_fmaf(wv[ht][r], v > 0.0f ? v : 0.0f, sum);
-            }
-        sum += __shfl_xor(sum, 32, 64);
-        sum *= sc;
+            for (int r = 0; r < 16; ++r) sum = __builtin_fmaf(wv[ht][r], relu_bits(acc[ht][r]), sum);
+        sum = xor32_sum(sum) * g.sc;
         const int64_t j = first + 128 * (int64_t)n + lrow;
         if (lane < 32 && j < j_end) {
             const uint32_t key = score_key(sum);
             kout[j] = key;
             atomicAdd(&hist[key >> 21], 1u);
         }
+    };
+    for (int n0 = 0; n0 < ng; n0 += RS) {
+#pragma unroll
+        for (int u = 0; u < RS; ++u) {
+            const int n = n0 + u;
+            if (n >= ng) break;  // uniform
+            if (n + kPD < ng) load_group(n + kPD, ring[(u + kPD) % RS]);
+            score_group(n, ring[u]);
+        }
     }
-    barrier_lds();
+    __syncthreads();
     flush_hist(hist, a.hist + bq * kHistStride, 256);
 }
 
@@ -289,13 +252,18 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
 
 // Bin b of an 11-bit histogram h with (count above b) < want <= (count at
 // or above b), scanning from the top bin down; want >= 1 and at most the
-// histogram total.  Whole workgroup (NT threads); every thread gets the bin
-// and the count above it.  info: 2 words, wsum: NT/64 + 1 words.
+// histogram total (otherwise the result is bin 0 with 0 above: still a valid
+// index).  Whole workgroup (NT threads); every thread gets the bin and the
+// count above it.  info: 2 words, wsum: NT/64 + 1 words.
 template <int NT>
 __device__ void find_bin(const uint32_t* h, uint32_t want, uint32_t* wsum, uint32_t* info, uint32_t* bin,
                          uint32_t* above) {
     constexpr int BPT = kHistBins / NT;  // bins per thread, descending from the top
     const int t = threadIdx.x;
+    if (t == 0) {  // (the scan's barriers order this before the finder's write)
+        info[0] = 0u;
+        info[1] = 0u;
+    }
     uint32_t c[BPT];
     uint32_t local = 0;
 #pragma unroll
@@ -323,7 +291,8 @@ __device__ void find_bin(const uint32_t* h, uint32_t want, uint32_t* wsum, uint3
 }
 
 // The same search by one wave over an LDS histogram: lane l owns the 32
-// bins just below 2048 - 32 l; no barrier.  Writes (bin, above) to out.
+// bins just below 2048 - 32 l; no barrier.  Writes (bin, above) to out when
+// the histogram holds at least want (the caller zeroes out beforehand).
 __device__ void find_bin_wave(const uint32_t* h, uint32_t want, uint32_t* out) {
     const int lane = threadIdx.x & 63;
     const u32x4* hb = reinterpret_cast<const u32x4*>(h + kHistBins - 32 * (lane + 1));
@@ -579,7 +548,7 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(const IndexerAr
     // both histogram levels into LDS with one batch of loads
     static_assert(2 * kHistBins == 4 * NT, "histogram staging: one u32x4 per thread");
     reinterpret_cast<u32x4*>(hs)[tid] = reinterpret_cast<const u32x4*>(qh)[tid];
-    if (tid < 8) info[tid] = 0u;
+    if (tid < 16) info[tid] = 0u;  // (bins default to 0: valid indices whatever the histograms hold)
     __syncthreads();
     // wave 0 finds both threshold bins (level 2 only where it was built)
     if (tid < 64) {
