@@ -11,8 +11,8 @@
 //   0. zero: the per-query histogram blocks.
 //   1. score: one workgroup per (query, chunk of entries).
 //        fp8 mode: each wave streams its own 32-entry groups of keys and
-//        scales through a private LDS ring of asynchronous HBM->LDS copies,
-//        three groups ahead; keys are decoded exactly to bf16
+//        scales straight into a ring of VGPR sets, several groups ahead of
+//        the one it multiplies; keys are decoded exactly to bf16
 //        (v_cvt_scalef32_pk_bf16_fp8) and multiplied on
 //        v_mfma_f32_32x32x16_bf16 against the bf16 query heads held in VGPRs
 //        (heads x entries, fp32 accumulation); ReLU, the head weights and the
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void idx_score_f32_kernel(const IndexerArgs a)
 // lower index first), and writes the winners in index order.  If b1 holds
 // more than kCandCap keys, a radix select over the whole key array is used.
 constexpr int kBitmapWords = 8192;  // LDS bitmap covers 2^18 entries
-constexpr uint32_t kSmallBin = 512;
+constexpr uint32_t kSmallBin = 64;  // a threshold bin this small is ranked whole
 
 // Workgroup-wide exclusive prefix sum of one value per thread (NT threads);
 // every thread also receives the workgroup total.  wsum: NT/64 + 1 words.
@@ -525,7 +525,7 @@ constexpr int kBndCap = 4096;  // boundary entries ranked in LDS
 
 __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(const IndexerArgs a) {
     __shared__ uint32_t hs[2 * kHistBins];
-    __shared__ uint64_t bnd[kBndCap];
+    __shared__ __attribute__((aligned(16))) uint64_t bnd[kBndCap];
     __shared__ uint32_t bits[kBitmapWords];
     __shared__ uint32_t win[kTopkCap];
     __shared__ uint32_t cnt256[256];
@@ -602,7 +602,21 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(const IndexerAr
             for (uint32_t i = tid; i < nb; i += NT) {
                 const uint64_t v = bnd[i];
                 uint32_t r = 0;
-                for (uint32_t l = 0; l < nb; ++l) r += bnd[l] < v ? 1u : 0u;
+                // eight independent LDS reads per round, so their latencies overlap
+                uint32_t l = 0;
+                for (; l + 8 <= nb; l += 8) {
+                    const u32x4* p = reinterpret_cast<const u32x4*>(bnd + l);
+                    u32x4 w[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) w[u] = p[u];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint64_t x0 = (uint64_t)w[u][0] | ((uint64_t)w[u][1] << 32);
+                        const uint64_t x1 = (uint64_t)w[u][2] | ((uint64_t)w[u][3] << 32);
+                        r += (x0 < v ? 1u : 0u) + (x1 < v ? 1u : 0u);
+                    }
+                }
+                for (; l < nb; ++l) r += bnd[l] < v ? 1u : 0u;
                 if (r < need) win[above + r] = (uint32_t)(v & 0xffffffffu);  // ranks are distinct
             }
         } else {  // a crowded bin: radix select straight from list B
