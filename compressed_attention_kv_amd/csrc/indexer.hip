@@ -477,26 +477,40 @@ __global__ __launch_bounds__(256) void idx_refine_kernel(const IndexerArgs a) {
     const int64_t j_end = min(nvis, j_begin + a.chunk);
     const uint32_t* keys = a.keys + bq * a.N;
     uint32_t* qh = a.hist + bq * kHistStride;
-    uint32_t* cnt = qh + 2 * kHistBins;  // [0] list A, [1] list B
+    uint32_t* cnt = qh + 2 * kHistBins;  // [0] list A, [1] list B, [2] b1, [3] count above b1
     uint32_t* list_a = a.cand_a + bq * kTopkCap;
     uint64_t* list_b = a.cand_b + bq * kCandCap;
+    // keys are requested one round ahead; the first round before the
+    // threshold search, so that its latency overlaps the search
+    constexpr int64_t STEP = (int64_t)NT * KPT;
+    uint32_t kv[KPT];
+    auto load_keys = [&](int64_t j0, uint32_t* dst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const int64_t j = j0 + (int64_t)u * NT + tid;
+            dst[u] = j < j_end ? keys[j] : 0u;
+        }
+    };
+    load_keys(j_begin, kv);
     for (int i = tid; i < kHistBins; i += NT) h2[i] = 0u;
     uint32_t b1, a1;
     find_bin<NT>(qh, (uint32_t)k, wsum, info, &b1, &a1);  // (syncs, so h2 is clear)
     const uint32_t nb1 = qh[b1];
     const bool fits = nb1 <= (uint32_t)kCandCap, level2 = nb1 > kSmallBin;  // uniform
+    if (blockIdx.x == 0 && tid == 0) {  // for the select pass
+        cnt[2] = b1;
+        cnt[3] = a1;
+    }
 
     // ---- this workgroup's entries
-    for (int64_t j0 = j_begin; j0 < j_end; j0 += (int64_t)NT * KPT) {  // uniform trip count
-        uint32_t kv[KPT], jv[KPT];
+    for (int64_t j0 = j_begin; j0 < j_end; j0 += STEP) {  // uniform trip count
+        uint32_t jv[KPT], kn[KPT];
         uint64_t rv[KPT];
         bool sa[KPT], sb[KPT];
+        const bool more = j0 + STEP < j_end;  // uniform
+        if (more) load_keys(j0 + STEP, kn);
 #pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            const int64_t j = j0 + (int64_t)u * NT + tid;
-            jv[u] = (uint32_t)j;
-            kv[u] = j < j_end ? keys[j] : 0u;
-        }
+        for (int u = 0; u < KPT; ++u) jv[u] = (uint32_t)(j0 + (int64_t)u * NT + tid);
 #pragma unroll
         for (int u = 0; u < KPT; ++u) {
             const bool in = (int64_t)j0 + (int64_t)u * NT + tid < j_end;
@@ -508,6 +522,10 @@ __global__ __launch_bounds__(256) void idx_refine_kernel(const IndexerArgs a) {
         }
         wave_append<KPT>(list_a, cnt, sa, jv);
         if (fits) wave_append<KPT>(list_b, cnt + 1, sb, rv);
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < KPT; ++u) kv[u] = kn[u];
+        }
     }
     if (level2) {
         __syncthreads();
@@ -548,12 +566,19 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(const IndexerAr
     // both histogram levels into LDS with one batch of loads
     static_assert(2 * kHistBins == 4 * NT, "histogram staging: one u32x4 per thread");
     reinterpret_cast<u32x4*>(hs)[tid] = reinterpret_cast<const u32x4*>(qh)[tid];
-    if (tid < 16) info[tid] = 0u;  // (bins default to 0: valid indices whatever the histograms hold)
+    // the level-1 threshold bin and the count above it come from the refine
+    // pass (clamped, so that any word there gives in-bounds indices); other
+    // bins default to 0
+    if (tid < 16) {
+        uint32_t v = 0u;
+        if (tid == 8) v = qh[2 * kHistBins + 2] & (kHistBins - 1);
+        if (tid == 9) v = min(qh[2 * kHistBins + 3], (uint32_t)k);
+        info[tid] = v;
+    }
     __syncthreads();
-    // wave 0 finds both threshold bins (level 2 only where it was built)
+    // wave 0 finds the level-2 threshold bin where it was built
     if (tid < 64) {
-        find_bin_wave(hs, (uint32_t)k, info + 8);
-        const uint32_t b = (uint32_t)__shfl((int)info[8], 0, 64), ab = (uint32_t)__shfl((int)info[9], 0, 64);
+        const uint32_t b = info[8], ab = info[9];
         if (hs[b] > kSmallBin && hs[b] <= (uint32_t)kCandCap) find_bin_wave(hs + kHistBins, (uint32_t)k - ab, info + 10);
     }
     __syncthreads();
