@@ -365,16 +365,22 @@ void mqa_fwd_kernel(const AttnArgs a) {
 #pragma unroll
             for (int k = 0; k < 5; ++k) {
                 const int t = tile0 + k;
-                jst[k] = (SPARSE && ol < TK && t < tile1) ? slot_entry<SPARSE>(a, g, bq, t * TK + ol) : 0;
+                // an unconditional load from a clamped slot; meta_finish keeps
+                // it only for a slot of this split's tiles that holds an entry
+                jst[k] = (SPARSE && a.K > 0) ? a.idx[bq * a.K + min(t * TK + ol, a.K - 1)] : 0;
             }
         }
+    };
+    auto jst_kept = [&](int k, int ol) __attribute__((always_inline)) {
+        const int t = tile0 + k;
+        return (SPARSE && ol < TK && t < tile1 && t * TK + ol < g.n_c) ? jst[k] : 0;
     };
     auto meta_finish = [&]() __attribute__((always_inline)) {
         if (wave == 0) {
             const int ol = opaque_tid() & 63;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) tile_meta(tile0 + k, k, jst[k]);
-            if (SPARSE) idxs[4][ol] = jst[4];
+            for (int k = 0; k < 4; ++k) tile_meta(tile0 + k, k, jst_kept(k, ol));
+            if (SPARSE) idxs[4][ol] = jst_kept(4, ol);
         }
     };
     auto meta_start = [&]() __attribute__((always_inline)) {
@@ -392,15 +398,25 @@ void mqa_fwd_kernel(const AttnArgs a) {
     // them in LDS does not wait for those (loads complete in issue order)
     const bool has_gq = a.gamma_q != nullptr;
     constexpr int GQ = (D + 255) / 256;
+    // Every lane loads (from clamped addresses): loads under a per-lane
+    // condition become exec-masked branches, and the compiler then waits for
+    // each such load on the spot and for all loads before the first LDS
+    // store, which serialises the prologue's memory latencies.  Lanes past
+    // the last head load head 0's row; their results are never stored.
     float gq_pre[GQ];
+    if (has_gq) {
 #pragma unroll
-    for (int k = 0; k < GQ; ++k) gq_pre[k] = (has_gq && tid + 256 * k < D) ? a.gamma_q[tid + 256 * k] : 1.0f;
-    const float sink_pre = (FINAL && tid < H) ? a.sinks[tid] : 0.0f;
+        for (int k = 0; k < GQ; ++k) gq_pre[k] = a.gamma_q[min(tid + 256 * k, D - 1)];
+    } else {
+#pragma unroll
+        for (int k = 0; k < GQ; ++k) gq_pre[k] = 1.0f;
+    }
+    const float sink_pre = FINAL ? a.sinks[tid < H ? tid : H - 1] : 0.0f;
     typename LD::raw_t qr[KSTEPS];  // lane: head qhead, channels 16 s + 8 lh + (0..7)
     {
         const TIn* qrow = reinterpret_cast<const TIn*>(a.q) + (bq * H + (qhead < H ? qhead : 0)) * (int64_t)D + 8 * lh;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) qr[s] = qhead < H ? LD::load(qrow + 16 * s) : LD::zero();
+        for (int s = 0; s < KSTEPS; ++s) qr[s] = LD::load(qrow + 16 * s);
     }
     if (wave == 1 && lane < n_pairs) {
         const double tn = rope_turns(a.rope_base, lane, a.rope_dims);
