@@ -92,11 +92,6 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
         for (int i = 0; i < NLD; ++i) g.c[i] = src[i];
         g.sc = sbase[row];
     };
-    Grp ring[RS];
-#pragma unroll
-    for (int n = 0; n < kPD; ++n)
-        if (n < ng) load_group(n, ring[n]);
-    for (int i = tid; i < kHistBins; i += 256) hist[i] = 0u;
 
     // A operand: query heads (rows) x features, k-permutation (s, half, e) -> half*DI/2 + 8s + e
     bf16x8 qa[HT][KS];
@@ -111,6 +106,17 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
 #pragma unroll
         for (int r = 0; r < 16; ++r) wv[ht][r] = a.w[bq * (32 * HT) + 32 * ht + 8 * (r >> 2) + 4 * lh + (r & 3)];
     }
+    // The first groups are requested after the query operand and weights,
+    // which are then awaited explicitly: had any of those loads still been
+    // pending at the loop, the compiler would wait for them inside it on
+    // every turn, draining the groups in flight.  Groups past the last one
+    // load (clamped) rows too, for the same reason: a load under a condition
+    // leaves the count of loads in flight unknown.
+    Grp ring[RS];
+#pragma unroll
+    for (int n = 0; n < kPD; ++n) load_group(n, ring[n]);
+    for (int i = tid; i < kHistBins; i += 256) hist[i] = 0u;
+    wait_vm<kPD * (NLD + 1)>();
     __syncthreads();  // the histogram is clear
 
     auto score_group = [&](int n, const Grp& g) __attribute__((always_inline)) {
@@ -151,8 +157,12 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
         for (int u = 0; u < RS; ++u) {
             const int n = n0 + u;
             if (n >= ng) break;  // uniform
-            if (n + kPD < ng) load_group(n + kPD, ring[(u + kPD) % RS]);
+            load_group(n + kPD, ring[(u + kPD) % RS]);
+            // the next group's loads go out before this group's work, and
+            // each group's work stays in its own step
+            __builtin_amdgcn_sched_barrier(0);
             score_group(n, ring[u]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     __syncthreads();
