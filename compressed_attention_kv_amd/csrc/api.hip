@@ -136,7 +136,7 @@ void fill_attn(cakv::AttnArgs& a, const cakv_attn_params* p, const void* q, cons
     a.scale_log2 = (float)(tau * 1.4426950408889634);
     a.rms_eps = p->rms_eps;
     a.out_f32 = out_dtype == CAKV_F32;
-    a.rope_base = p->rope_base;
+    a.rope_ratio = cakv::rope_ratio_of(p->rope_base, p->rope_dims);
 }
 
 int run_attn(cakv::AttnArgs& a, int64_t BQ, int32_t H, int32_t D, int64_t max_slots, bool act_f32,
@@ -234,7 +234,7 @@ int cakv_kv_prepare(const void* kv_in, void* kv_out, int act_dtype, int64_t B, i
     REQUIRE_PTR(kv_out, "kv_out");
     if (gamma_kv) REQUIRE(aligned16(gamma_kv), CAKV_EINVAL, "gamma_kv must be 16-byte aligned");
     return rc_from(cakv::launch_kv_prepare(kv_in, kv_out, act_dtype == CAKV_F32 ? 0 : 1, B, N, D, j0, n, gamma_kv,
-                                           m, rope_dims, rope_base, entry_pos_offset, rms_eps,
+                                           m, rope_dims, cakv::rope_ratio_of(rope_base, rope_dims), entry_pos_offset, rms_eps,
                                            reinterpret_cast<hipStream_t>(stream)));
 }
 

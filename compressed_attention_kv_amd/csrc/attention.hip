@@ -419,7 +419,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
         for (int s = 0; s < KSTEPS; ++s) qr[s] = LD::load(qrow + 16 * s);
     }
     if (wave == 1 && lane < n_pairs) {
-        const double tn = rope_turns(a.rope_base, lane, a.rope_dims);
+        const double tn = rope_turns(a.rope_ratio, lane);
         float sn, cs;
         sincos_turns((double)g.t * tn, &sn, &cs);
         qcs[lane] = make_float2(cs, sn);
@@ -1067,7 +1067,7 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(const AttnArgs a) {
     if (2 * pr >= rope_lo) {
         int32_t t = a.q_pos[bq];
         t = t < 0 ? 0 : t;
-        sincos_turns(-(double)t * rope_turns(a.rope_base, (2 * pr - rope_lo) >> 1, a.rope_dims), &sn, &cs);
+        sincos_turns(-(double)t * rope_turns(a.rope_ratio, (2 * pr - rope_lo) >> 1), &sn, &cs);
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {

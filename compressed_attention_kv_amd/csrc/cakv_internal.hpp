@@ -41,12 +41,24 @@ struct AttnArgs {
     float rms_eps;
     int32_t n_splits;
     int32_t out_f32;   // 1: float32 output, 0: bf16
-    float rope_base;   // theta_i = rope_base^(-2i/rope_dims)
+    double rope_ratio; // rope_base^(-2/rope_dims), so theta_i = rope_ratio^i
 };
 
-// theta_i / (2 pi) in fp64: turns of rotary pair i per unit of position
-__device__ __forceinline__ double rope_turns(float base, int i, int rope_dims) {
-    return pow((double)base, -2.0 * i / (double)rope_dims) * 0.15915494309189533577;
+// rope_base^(-2/rope_dims) in fp64 (host side; 1 when nothing rotates)
+inline double rope_ratio_of(float rope_base, int rope_dims) {
+    return rope_dims > 0 ? pow((double)rope_base, -2.0 / (double)rope_dims) : 1.0;
+}
+
+// theta_i / (2 pi) in fp64: turns of rotary pair i per unit of position,
+// theta_i = ratio^i by repeated squaring (relative error ~1e-15, far below
+// what the fp32 sine and cosine resolve)
+__device__ __forceinline__ double rope_turns(double ratio, int i) {
+    double r = 1.0, b = ratio;
+    for (int e = i; e > 0; e >>= 1) {
+        if (e & 1) r *= b;
+        b *= b;
+    }
+    return r * 0.15915494309189533577;
 }
 
 int launch_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B, int64_t T,
@@ -55,7 +67,7 @@ int launch_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B,
 
 // dtype 0: float32, 1: bf16; entries j0 .. j0+n-1 of each of the B sequences
 int launch_kv_prepare(const void* in, void* out, int dtype, int64_t B, int64_t N, int64_t D, int64_t j0,
-                      int64_t n, const float* gamma, int32_t m, int32_t rope_dims, float rope_base,
+                      int64_t n, const float* gamma, int32_t m, int32_t rope_dims, double rope_ratio,
                       int32_t pos_off, float eps, hipStream_t stream);
 
 // sparse (idx != NULL) or dense MQA forward; act_f32: inputs are float32

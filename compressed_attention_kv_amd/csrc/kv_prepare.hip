@@ -62,7 +62,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void kv_prepare_kernel(const T* in, T* out,
                                                          const float* __restrict__ gamma, int64_t N, int D,
                                                          int64_t j0, int64_t n, int64_t rows, int m,
-                                                         int rope_dims, float rope_base, int pos_off,
+                                                         int rope_dims, double rope_ratio, int pos_off,
                                                          float eps) {
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;  // wave-uniform
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void kv_prepare_kernel(const T* in, T* out,
                     const int d = 8 * c + 2 * p;
                     if (d < rope_lo) continue;
                     float sn, cs;
-                    sincos_turns(pos * rope_turns(rope_base, (d - rope_lo) >> 1, rope_dims), &sn, &cs);
+                    sincos_turns(pos * rope_turns(rope_ratio, (d - rope_lo) >> 1), &sn, &cs);
                     const float x0 = v[k][2 * p], x1 = v[k][2 * p + 1];
                     v[k][2 * p] = x0 * cs - x1 * sn;
                     v[k][2 * p + 1] = x0 * sn + x1 * cs;
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void kv_prepare_kernel(const T* in, T* out,
 }
 
 int launch_kv_prepare(const void* in, void* out, int dtype, int64_t B, int64_t N, int64_t D, int64_t j0,
-                      int64_t n, const float* gamma, int32_t m, int32_t rope_dims, float rope_base,
+                      int64_t n, const float* gamma, int32_t m, int32_t rope_dims, double rope_ratio,
                       int32_t pos_off, float eps, hipStream_t stream) {
     const int64_t rows = B * n;
     if (rows == 0) return 0;
@@ -119,12 +119,12 @@ int launch_kv_prepare(const void* in, void* out, int dtype, int64_t B, int64_t N
     prof_mark("kv_prepare_kernel", false, stream);
     if (dtype == 0)
         hipLaunchKernelGGL((kv_prepare_kernel<float>), dim3((unsigned)grid), dim3(256), 0, stream,
-                           (const float*)in, (float*)out, gamma, N, (int)D, j0, n, rows, m, rope_dims, rope_base,
+                           (const float*)in, (float*)out, gamma, N, (int)D, j0, n, rows, m, rope_dims, rope_ratio,
                            pos_off, eps);
     else
         hipLaunchKernelGGL((kv_prepare_kernel<bf16_t>), dim3((unsigned)grid), dim3(256), 0, stream,
                            (const bf16_t*)in, (bf16_t*)out, gamma, N, (int)D, j0, n, rows, m, rope_dims,
-                           rope_base, pos_off, eps);
+                           rope_ratio, pos_off, eps);
     prof_mark("kv_prepare_kernel", true, stream);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
