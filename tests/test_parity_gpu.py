@@ -112,7 +112,7 @@ def test_indexer_fp32_bit_exact_tiny_layer():
     assert (ref == -1).any(axis=1).sum() >= 256  # rows with fewer visible entries than k
 
 
-@pytest.mark.parametrize("N,k,Q", [(3000, 64, 8), (70000, 1024, 2)])
+@pytest.mark.parametrize("N,k,Q", [(3000, 64, 8), (70000, 1024, 2), (20000, 4096, 2)])  # k = 4096: the largest
 def test_indexer_fp32_bit_exact_sizes(N, k, Q):
     say(f"indexer fp32 N={N} k={k}")
     rng = np.random.default_rng(N)
@@ -128,11 +128,15 @@ def test_indexer_fp32_bit_exact_sizes(N, k, Q):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("tied", [3000, 10000])
+@pytest.mark.parametrize("tied", [3000, 5000, 10000])
 def test_indexer_fp32_tied_block_at_threshold(tied):
     """A block of entries with one exact score straddles the k-th place: the
-    tie at the boundary is broken by the lower index, through the boundary
-    radix select (3000 tied) or the whole-array select (10000 tied)."""
+    tie at the boundary is broken by the lower index.  The tied keys share
+    both histogram levels, so each size takes another select path: 3,000 are
+    ranked by counting in LDS, 5,000 (more than the 4,096 ranked in LDS, fewer
+    than the 8,192 listed) by the radix select over the listed entries, and
+    10,000 (more than are listed) by the radix select over the whole key
+    array."""
     say(f"indexer fp32 tied block {tied}")
     rng = np.random.default_rng(tied)
     B, Q, HI, dI, m, N, k = 1, 2, 8, 32, 4, 20000, 1024
