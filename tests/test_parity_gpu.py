@@ -410,6 +410,29 @@ def test_attention_edge_cases():
     assert torch.all(out3 == 0) and torch.all(torch.isneginf(lse3))
 
 
+def test_attention_split_combine_odd_heads():
+    """Several key splits merged by the combine kernel: an odd head count (the
+    last head pair holds one head), a -inf sink and the lse."""
+    say("attention split combine, odd head count")
+    g = torch.Generator().manual_seed(11)
+    B, Q, H, D, N, R = 3, 1, 5, 128, 2000, 64
+    q = torch.randn(B, Q, H, D, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, N, D, generator=g).to(torch.bfloat16)
+    raw = torch.randn(B, R, D, generator=g).to(torch.bfloat16)
+    sinks = torch.randn(H, generator=g)
+    sinks[2] = -math.inf
+    qpos = torch.tensor([[4 * N + 10], [4 * N + 30], [3000]], dtype=torch.int32)
+    raw0 = (qpos[:, 0] - R + 1).to(torch.int32)
+    kw = dict(m=4, n_win=16, rope_dims=32)
+    ref, lse_ref = oracle.attention(q, kv, raw, raw0, qpos, sinks, **kw)
+    kvp, rawp = _prep(kv, 4, kw), _prep_raw(raw, raw0, kw)
+    out, lse = cakv.dense_compressed_mqa_fwd(_d(q), kvp, rawp, _d(raw0), _d(qpos), _d(sinks),
+                                             out_dtype=torch.float32, **kw)
+    _attn_check(out.cpu().numpy().reshape(ref.shape), ref, "split combine")
+    lg = lse.cpu().numpy().reshape(lse_ref.shape)
+    assert np.all(np.isfinite(lg)) and np.abs(lg - lse_ref).max() < 1e-2  # bf16 logits
+
+
 def test_attention_needle_forces_exact_max_pass():
     """A key equal to the query (logit sqrt(D), far above the rest) sitting in a
     late tile: the kernel's reference max from the first tiles is too small,
