@@ -85,8 +85,11 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
         u32x4 c[NLD];
         float sc;
     };
+    // (a group past the wave's last one reloads the last one's rows, which
+    // are in cache, instead of fetching rows of other waves' ranges)
     auto load_group = [&](int n, Grp& g) __attribute__((always_inline)) {
-        const int64_t row = min(first + 128 * (int64_t)n + lrow, a.N - 1);
+        const int nn = n < ng ? n : (ng > 0 ? ng - 1 : 0);
+        const int64_t row = min(first + 128 * (int64_t)nn + lrow, a.N - 1);
         const u32x4* src = reinterpret_cast<const u32x4*>(kbase + row * DI + lh * HALF);
 #pragma unroll
         for (int i = 0; i < NLD; ++i) g.c[i] = src[i];
