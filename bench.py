@@ -442,9 +442,13 @@ def main():
     torch.cuda.synchronize()
 
     pair_ms = _event_pair_ms()
-    # the dominant kernel: the longest of the step's main kernels on a short probe
-    probe = {k: _time_kernel(st, k, 2, lambda: [st.run() for _ in range(2)]) for k in st.kernels}
-    dom = max(probe, key=probe.get)
+    # the dominant kernel: the longest of the step's main kernels on a short
+    # probe; kernels within 10 % of the longest count as a tie, which goes to
+    # the one with the most algorithmic work (bytes at decode, flops at
+    # prefill), so that timing noise cannot flip the choice
+    probe = {k: _time_kernel(st, k, 4, lambda: [st.run() for _ in range(4)]) for k in st.kernels}
+    top = max(probe.values())
+    dom = max((k for k in probe if probe[k] >= 0.9 * top), key=lambda k: st.kernels[k][1 if st.prefill else 0])
     dom_name, _, per_step = _kernel_launches(st, dom, steps)
 
     # per-call breakdown: an untimed pass with HIP events around each call
