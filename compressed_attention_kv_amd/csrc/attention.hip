@@ -933,7 +933,12 @@ void mqa_fwd_kernel(const AttnArgs a) {
         // that the four rows one write instruction touches use distinct banks.
         const bool odd = erow & 1;
         const bool f32o = a.out_f32 != 0;
+        // the wave's 32 heads all exist (uniform): stores need no per-lane test
+        const bool full = 32 * wave + 32 <= H;
         uint8_t* ob = ring[wave];
+        // (one unrolled pass per output type: a branch on the type inside the
+        // unrolled loop costs a scalar branch and exec-mask set-up per store)
+        auto out_rows = [&](auto&& put) __attribute__((always_inline)) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             const bool tile_rot = dt >= DT - 2 && 32 * dt + 32 > rope_lo;  // uniform
@@ -953,18 +958,22 @@ void mqa_fwd_kernel(const AttnArgs a) {
                 const float recv = lane_swap1(odd ? v[0] : v[1]);
                 const float lo = odd ? recv : v[0], hi = odd ? v[1] : recv;
                 const int row = 8 * (r >> 2) + 4 * eh + (r & 3) + (odd ? 1 : 0);
-                if (f32o) {
-                    const int hr = 32 * wave + row;
-                    if (hr < H)
-                        *reinterpret_cast<float2*>(reinterpret_cast<float*>(a.out) + (bq * H + hr) * (int64_t)D + 32 * dt +
-                                                   (erow & ~1)) = make_float2(lo, hi);
-                } else {
-                    const int word = (16 * dt + (erow >> 1)) ^ (((row >> 2) & 1) << 5);
-                    *reinterpret_cast<uint32_t*>(ob + row * RS + 4 * word) = pack_bf16x2(lo, hi);
-                }
+                put(dt, row, lo, hi);
             }
         }
-        if (!f32o) {
+        };
+        if (f32o) {
+            out_rows([&](int dt, int row, float lo, float hi) __attribute__((always_inline)) {
+                const int hr = 32 * wave + row;
+                if (hr < H)
+                    *reinterpret_cast<float2*>(reinterpret_cast<float*>(a.out) + (bq * H + hr) * (int64_t)D + 32 * dt +
+                                               (erow & ~1)) = make_float2(lo, hi);
+            });
+        } else {
+            out_rows([&](int dt, int row, float lo, float hi) __attribute__((always_inline)) {
+                const int word = (16 * dt + (erow >> 1)) ^ (((row >> 2) & 1) << 5);
+                *reinterpret_cast<uint32_t*>(ob + row * RS + 4 * word) = pack_bf16x2(lo, hi);
+            });
             constexpr int LPRO = D / 8;     // lanes per bf16 output row (16 bytes each)
             constexpr int RPI = 64 / LPRO;  // rows per instruction
 #pragma unroll
@@ -972,7 +981,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
                 const int h = h0 + el / LPRO, c = el % LPRO;
                 const int hr = 32 * wave + h;
                 const u32x4 w = *reinterpret_cast<const u32x4*>(ob + h * RS + 4 * ((4 * c) ^ (((h >> 2) & 1) << 5)));
-                if (hr < H)
+                if (full || hr < H)
                     *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + (bq * H + hr) * (int64_t)D + 8 * c) = w;
             }
         }
@@ -995,15 +1004,20 @@ void mqa_fwd_kernel(const AttnArgs a) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) il[m] = *reinterpret_cast<const f32x4*>(&il_s[wave][8 * m + 4 * eh]);
     const int64_t pbase = (bq * S + split) * (int64_t)((H + 1) >> 1);
+    // (a wave whose 32 heads all exist stores without a per-lane test)
+    auto put_partials = [&](bool check) __attribute__((always_inline)) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            const int hr = 32 * wave + 8 * (r >> 2) + 4 * eh + (r & 3);  // even
-            if (hr < H)
-                a.part_o[(pbase + (hr >> 1)) * D + 32 * dt + erow] =
-                    pack_f16x2(acc[dt][r] * il[r >> 2][r & 3], acc[dt][r + 1] * il[r >> 2][(r & 3) + 1]);
-        }
+            for (int r = 0; r < 16; r += 2) {
+                const int hr = 32 * wave + 8 * (r >> 2) + 4 * eh + (r & 3);  // even
+                if (!check || hr < H)
+                    a.part_o[(pbase + (hr >> 1)) * D + 32 * dt + erow] =
+                        pack_f16x2(acc[dt][r] * il[r >> 2][r & 3], acc[dt][r + 1] * il[r >> 2][(r & 3) + 1]);
+            }
+    };
+    if (32 * wave + 32 <= H) put_partials(false);
+    else put_partials(true);
 }
 
 // Merge split partials: one workgroup per (query, head pair), one thread per
