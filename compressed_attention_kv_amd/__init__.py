@@ -83,14 +83,23 @@ def _check(rc: int):
         raise CakvError(f"cakv error {rc}: {_lib.cakv_last_error().decode()}")
 
 
-def _dev(t: torch.Tensor | None, name: str):
+def _dev(t: torch.Tensor | None, name: str, dtype: torch.dtype | None = None):
+    """Device pointer of a contiguous device tensor (None -> NULL); with
+    `dtype`, the tensor must hold exactly that element type (an int64 position
+    tensor, torch's default for integers, would otherwise be read as pairs of
+    int32 words)."""
     if t is None:
         return None
     if not t.is_cuda:
         raise CakvError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise CakvError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise CakvError(f"{name} must be {dtype}, got {t.dtype}")
     return t.data_ptr()
+
+
+_I32, _F32 = torch.int32, torch.float32
 
 
 def _stream() -> int:
@@ -120,8 +129,8 @@ def kv_compress(x: torch.Tensor, gate: torch.Tensor, m: int, out_dtype: torch.dt
         scale = torch.empty((B, nb), dtype=torch.float32, device=x.device)
     elif out_dtype != torch.float8_e4m3fn:
         scale = None
-    _check(lib.cakv_kv_compress(_dev(x, "x"), _DT[x.dtype], _dev(gate, "gate"), B, T, D, m, _dev(out, "out"),
-                                _DT[out_dtype], _dev(scale, "scale"), _stream()))
+    _check(lib.cakv_kv_compress(_dev(x, "x"), _DT[x.dtype], _dev(gate, "gate", _F32), B, T, D, m, _dev(out, "out"),
+                                _DT[out_dtype], _dev(scale, "scale", _F32), _stream()))
     return (out, scale) if scale is not None else out
 
 
@@ -139,7 +148,7 @@ def kv_prepare(kv_c: torch.Tensor, *, m: int, rope_dims: int, rope_base: float =
     if tuple(out.shape) != (B, N, D) or out.dtype != kv_c.dtype:
         raise ValueError("out must match kv_c in shape and dtype")
     _check(lib.cakv_kv_prepare(_dev(kv_c, "kv_c"), _dev(out, "out"), _DT[kv_c.dtype], B, N, D, j0, n,
-                               _dev(gamma_kv, "gamma_kv"), m, rope_dims, rope_base, entry_pos_offset, rms_eps,
+                               _dev(gamma_kv, "gamma_kv", _F32), m, rope_dims, rope_base, entry_pos_offset, rms_eps,
                                _stream()))
     return out
 
@@ -172,14 +181,20 @@ def indexer_topk(q_idx: torch.Tensor, w: torch.Tensor, k_idx: torch.Tensor, k_sc
     need = int(lib.cakv_indexer_topk_workspace(B, Q, N, k))
     if workspace is None or workspace.numel() < need:
         workspace = _workspace(need, q_idx.device)
-    _check(lib.cakv_indexer_topk(_dev(q_idx, "q_idx"), _DT[q_idx.dtype], _dev(w, "w"), _dev(k_idx, "k_idx"),
-                                 _DT[k_idx.dtype], _dev(k_scale, "k_scale"), _dev(q_pos, "q_pos"), B, Q, N, HI, dI,
-                                 m, k, _dev(out, "idx"), workspace.data_ptr(), workspace.numel(), _stream()))
+    _check(lib.cakv_indexer_topk(_dev(q_idx, "q_idx"), _DT[q_idx.dtype], _dev(w, "w", _F32), _dev(k_idx, "k_idx"),
+                                 _DT[k_idx.dtype], _dev(k_scale, "k_scale", _F32), _dev(q_pos, "q_pos", _I32), B, Q, N, HI, dI,
+                                 m, k, _dev(out, "idx", _I32), workspace.data_ptr(), workspace.numel(), _stream()))
     return out
 
 
+def _same_act(q, kv_c, kv_raw):
+    # the C ABI takes one activation type for q, the cache and the window rows
+    if not (q.dtype == kv_c.dtype == kv_raw.dtype):
+        raise CakvError(f"q, kv_c and kv_raw must share one dtype ({q.dtype}, {kv_c.dtype}, {kv_raw.dtype})")
+
+
 def _params(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, gamma_q):
-    return AttnParams(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, _dev(gamma_q, "gamma_q"))
+    return AttnParams(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, _dev(gamma_q, "gamma_q", _F32))
 
 
 def sparse_mqa_workspace_bytes(B, Q, H, D, K, n_win) -> int:
@@ -201,6 +216,7 @@ def sparse_mqa_fwd(q, kv_c, idx, kv_raw, raw_pos0, q_pos, sinks, *, m: int, n_wi
     lib = load_library()
     B, Q, H, D = q.shape
     N, R, K = kv_c.shape[1], kv_raw.shape[1], idx.shape[-1]
+    _same_act(q, kv_c, kv_raw)
     out_dtype = out_dtype or q.dtype
     if out is None:
         out = torch.empty((B, Q, H, D), dtype=out_dtype, device=q.device)
@@ -209,10 +225,10 @@ def sparse_mqa_fwd(q, kv_c, idx, kv_raw, raw_pos0, q_pos, sinks, *, m: int, n_wi
     if workspace is None or workspace.numel() < need:
         workspace = _workspace(need, q.device)
     prm = _params(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, gamma_q)
-    _check(lib.cakv_sparse_mqa_fwd(ctypes.byref(prm), _dev(q, "q"), _dev(kv_c, "kv_c"), _dev(idx, "idx"),
-                                   _dev(kv_raw, "kv_raw"), _dev(raw_pos0, "raw_pos0"), _dev(q_pos, "q_pos"),
-                                   _dev(sinks, "sinks"), _DT[q.dtype], B, Q, H, D, N, K, R, _dev(out, "out"),
-                                   _DT[out_dtype], _dev(lse, "lse"), workspace.data_ptr(), workspace.numel(),
+    _check(lib.cakv_sparse_mqa_fwd(ctypes.byref(prm), _dev(q, "q"), _dev(kv_c, "kv_c"), _dev(idx, "idx", _I32),
+                                   _dev(kv_raw, "kv_raw"), _dev(raw_pos0, "raw_pos0", _I32), _dev(q_pos, "q_pos", _I32),
+                                   _dev(sinks, "sinks", _F32), _DT[q.dtype], B, Q, H, D, N, K, R, _dev(out, "out"),
+                                   _DT[out_dtype], _dev(lse, "lse", _F32), workspace.data_ptr(), workspace.numel(),
                                    _stream()))
     return out, lse
 
@@ -226,6 +242,7 @@ def dense_compressed_mqa_fwd(q, kv_c, kv_raw, raw_pos0, q_pos, sinks, *, m: int,
     lib = load_library()
     B, Q, H, D = q.shape
     N, R = kv_c.shape[1], kv_raw.shape[1]
+    _same_act(q, kv_c, kv_raw)
     out_dtype = out_dtype or q.dtype
     if out is None:
         out = torch.empty((B, Q, H, D), dtype=out_dtype, device=q.device)
@@ -235,9 +252,9 @@ def dense_compressed_mqa_fwd(q, kv_c, kv_raw, raw_pos0, q_pos, sinks, *, m: int,
         workspace = _workspace(need, q.device)
     prm = _params(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, gamma_q)
     _check(lib.cakv_dense_compressed_mqa_fwd(ctypes.byref(prm), _dev(q, "q"), _dev(kv_c, "kv_c"),
-                                             _dev(kv_raw, "kv_raw"), _dev(raw_pos0, "raw_pos0"),
-                                             _dev(q_pos, "q_pos"), _dev(sinks, "sinks"), _DT[q.dtype], B, Q, H, D,
-                                             N, R, _dev(out, "out"), _DT[out_dtype], _dev(lse, "lse"),
+                                             _dev(kv_raw, "kv_raw"), _dev(raw_pos0, "raw_pos0", _I32),
+                                             _dev(q_pos, "q_pos", _I32), _dev(sinks, "sinks", _F32), _DT[q.dtype], B, Q, H, D,
+                                             N, R, _dev(out, "out"), _DT[out_dtype], _dev(lse, "lse", _F32),
                                              workspace.data_ptr(), workspace.numel(), _stream()))
     return out, lse
 

@@ -67,11 +67,25 @@ int attn_splits(int64_t BQ, int64_t max_slots) {
     return (int)s;
 }
 
+// workspace one attention launch over BQ queries uses: the split partials
 size_t attn_workspace(int64_t BQ, int32_t H, int32_t D, int64_t max_slots) {
     const int S = attn_splits(BQ, max_slots);
     if (S == 1) return 0;  // one split: the forward kernel writes the output itself
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     return al((size_t)BQ * S * ((H + 1) / 2) * D * 4) + al((size_t)BQ * S * H * 2 * 4);
+}
+
+// what the *_workspace queries report: the largest launch workspace over
+// every batch of 1 .. BQ queries, so that a workspace sized once for the
+// largest batch serves every smaller one (the split count grows as the batch
+// shrinks; beyond 256 queries there is one split and no partials)
+size_t attn_workspace_query(int64_t BQ, int32_t H, int32_t D, int64_t max_slots) {
+    size_t best = attn_workspace(BQ, H, D, max_slots);
+    for (int64_t b = 1; b <= BQ && b <= 256; ++b) {
+        const size_t w = attn_workspace(b, H, D, max_slots);
+        if (w > best) best = w;
+    }
+    return best;
 }
 
 int check_attn_common(const cakv_attn_params* p, const void* q, const void* kv_c, const void* kv_raw,
@@ -303,12 +317,12 @@ int cakv_indexer_topk(const void* q_idx, int q_dtype, const float* w, const void
 
 size_t cakv_sparse_mqa_workspace(int64_t B, int64_t Q, int32_t H, int32_t D, int32_t K, int32_t n_win) {
     if (B < 0 || Q < 0 || H < 1 || D < 1 || K < 0 || n_win < 0) return 0;
-    return attn_workspace(B * Q, H, D, (int64_t)K + n_win);
+    return attn_workspace_query(B * Q, H, D, (int64_t)K + n_win);
 }
 
 size_t cakv_dense_mqa_workspace(int64_t B, int64_t Q, int32_t H, int32_t D, int64_t N, int32_t n_win) {
     if (B < 0 || Q < 0 || H < 1 || D < 1 || N < 0 || n_win < 0) return 0;
-    return attn_workspace(B * Q, H, D, N + n_win);
+    return attn_workspace_query(B * Q, H, D, N + n_win);
 }
 
 int cakv_sparse_mqa_fwd(const cakv_attn_params* p, const void* q, const void* kv_c, const int32_t* idx,

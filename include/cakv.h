@@ -97,7 +97,7 @@ int cakv_profile_kernel_events(const char* kernel, void* const* starts, void* co
  *            entry, e the smallest integer >= -126 with max_d |c_d| <= 448 * 2^e
  *            (e = 0 for an all-zero entry), and codes E4M3(c_d / s) rounded to
  *            nearest even; the dequantised value is code * s.
- *   D        1 .. 4096, a multiple of 4 (of 8 for bf16 input)
+ *   D        4 .. 4096, a multiple of 4
  * Errors: EINVAL (NULL pointers, sizes, dtypes), EUNSUPPORTED (m, D).
  * ------------------------------------------------------------------------- */
 int cakv_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B, int64_t T,
@@ -123,8 +123,13 @@ int cakv_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B, i
  *           other overlaps are undefined.
  *   gamma_kv [D] float32 device pointer, NULL = all ones
  *   D        8 .. 4096, a multiple of 8; rope_dims even, 0 .. D
- * Arithmetic in fp32.  Errors: EINVAL (NULL pointers, alignment, ranges,
- * positions beyond int32), EUNSUPPORTED (D).
+ * Arithmetic in fp32.  Range: the attention calls keep their key-split
+ * partials (a convex combination of prepared rows) in fp16, so every
+ * prepared element must stay below 65,504 in magnitude; a normalised row
+ * has no element above sqrt(D), so this holds whenever every |gamma_kv|
+ * is at most 65504 / sqrt(D) (2,896 at D = 512).
+ * Errors: EINVAL (NULL pointers, alignment, ranges, positions beyond int32),
+ * EUNSUPPORTED (D).
  * ------------------------------------------------------------------------- */
 int cakv_kv_prepare(const void* kv_in, void* kv_out, int act_dtype, int64_t B, int64_t N, int64_t D,
                     int64_t j0, int64_t n, const float* gamma_kv, int32_t m, int32_t rope_dims,
@@ -152,10 +157,14 @@ int cakv_kv_prepare(const void* kv_in, void* kv_out, int act_dtype, int64_t B, i
  * ascending then heads ascending (bit-exact with a plain CPU loop in that
  * order); q bf16 + k fp8 computes the dot products on bf16 matrix cores with
  * fp32 accumulation (keys are decoded exactly; summation order differs).
- * Inputs must be finite.  HI <= 64 (bf16 mode: HI a multiple of 32 up to 64,
- * dI a multiple of 32 up to 256), k 1 .. 4096.
+ * Inputs must be finite.  Supported sizes: fp32 mode HI 1 .. 64, dI a
+ * multiple of 4, HI * dI <= 8192; bf16 mode HI in {32, 64} and dI in
+ * {64, 128}; k 1 .. 4096; N < 2^31.
  * Workspace: at least cakv_indexer_topk_workspace(B, Q, N, k) bytes, 256-byte
- * aligned; its contents on entry do not matter.
+ * aligned; its contents on entry do not matter.  The size depends only on
+ * B*Q and N: both modes share the top-k stage, whose buffers (one 4-byte
+ * score key per entry, per-query histograms and candidate lists) do not
+ * depend on the key or query dtype, so the query takes no dtype argument.
  * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE.
  * ------------------------------------------------------------------------- */
 size_t cakv_indexer_topk_workspace(int64_t B, int64_t Q, int64_t N, int32_t k);
@@ -209,10 +218,14 @@ typedef struct cakv_attn_params {
  *   out     [B, Q, H, D]  out_dtype CAKV_BF16 or CAKV_F32
  *   lse     [B, Q, H]     float32 log-sum-exp (natural log) incl. the sink, or NULL
  * A query with no keys and a -inf sink gets a zero output and lse = -inf.
- * Supported: D in {64, 128, 256, 512}, 1 <= H <= 128, K <= 65536.
+ * Supported: D in {128, 512} for CAKV_BF16 activations and D = 128 for
+ * CAKV_F32 activations, 1 <= H <= 128, 0 <= K <= 65536, m 1 .. 4096,
+ * n_win 0 .. 4096, rope_dims even and at most 64.
  * Workspace: cakv_sparse_mqa_workspace(...) bytes, 256-byte aligned.  It holds
  * the partials of the key-range splits; 0 (workspace may be NULL) when every
- * query runs as a single split, whose kernel writes the output directly.
+ * query runs as a single split, whose kernel writes the output directly.  The
+ * reported size never decreases as B*Q grows: a workspace sized for the
+ * largest batch serves every smaller batch of the same H, D, K and n_win.
  * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE.
  * ------------------------------------------------------------------------- */
 size_t cakv_sparse_mqa_workspace(int64_t B, int64_t Q, int32_t H, int32_t D, int32_t K,

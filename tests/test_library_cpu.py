@@ -121,8 +121,9 @@ def test_workspace_queries_are_monotone(lib):
     b = lib.cakv_dense_mqa_workspace(32, 1, 128, 512, 8192, 128)
     assert a > 0 and b > 0
     assert lib.cakv_sparse_mqa_workspace(64, 1, 128, 512, 1024, 128) >= a
-    # enough queries to fill the GPU with one split each: no partials, no workspace
-    assert lib.cakv_sparse_mqa_workspace(1, 8192, 128, 512, 1024, 128) == 0
+    # a large batch runs one split per query (no partials), but the reported
+    # size still covers every smaller batch, so it is not smaller than B*Q=32's
+    assert lib.cakv_sparse_mqa_workspace(1, 8192, 128, 512, 1024, 128) >= a
 
 
 def test_profile_kernel_events_arguments(lib):
@@ -132,3 +133,121 @@ def test_profile_kernel_events_arguments(lib):
     null2 = (ctypes.c_void_p * 2)(None, None)
     assert lib.cakv_profile_kernel_events(b"mqa_fwd_kernel", null2, null2, 2) == -1
     assert lib.cakv_profile_kernel_events(None, None, None, 0) == 0
+
+
+# ---------------------------------------------------------------- documented limits
+# Every size include/cakv.h calls supported is accepted and every other one is
+# refused.  "Accepted" is checked with an empty batch: sizes are validated
+# before the empty-batch return, and nothing is launched.
+
+@pytest.mark.parametrize("act,D,ok", [(cakv.BF16, 128, True), (cakv.BF16, 512, True), (cakv.F32, 128, True),
+                                      (cakv.F32, 512, False), (cakv.BF16, 64, False), (cakv.BF16, 256, False),
+                                      (cakv.BF16, 96, False), (cakv.BF16, 1024, False), (cakv.F32, 64, False)])
+def test_attention_head_dims(lib, act, D, ok):
+    rc = _sparse(lib, _prm(), B=0, act=act, D=D)
+    assert rc == (0 if ok else -2)
+    rc = lib.cakv_dense_compressed_mqa_fwd(ctypes.byref(_prm()), None, None, None, None, None, None, act, 0, 1, 128,
+                                           D, 16, 4, None, cakv.BF16, None, None, 0, None)
+    assert rc == (0 if ok else -2)
+
+
+@pytest.mark.parametrize("H,ok", [(1, True), (5, True), (64, True), (128, True), (0, False), (129, False)])
+def test_attention_head_counts(lib, H, ok):
+    assert _sparse(lib, _prm(), B=0, H=H) == (0 if ok else -2)
+
+
+@pytest.mark.parametrize("K,ok", [(0, True), (1, True), (65536, True), (-1, False), (65537, False)])
+def test_attention_topk_slots(lib, K, ok):
+    assert _sparse(lib, _prm(), B=0, K=K) == (0 if ok else -2)
+
+
+@pytest.mark.parametrize("kw,ok", [(dict(m=1), True), (dict(m=4096), True), (dict(m=4097), False),
+                                   (dict(n_win=0), True), (dict(n_win=4096), True), (dict(n_win=4097), False),
+                                   (dict(rope_dims=0), True), (dict(rope_dims=64), True),
+                                   (dict(rope_dims=66), False), (dict(rope_dims=7), False)])
+def test_attention_param_limits(lib, kw, ok):
+    assert _sparse(lib, _prm(**kw), B=0) == (0 if ok else -2)
+
+
+def _indexer(lib, qdt, kdt, HI, dI, k, ks=None, B=0):
+    return lib.cakv_indexer_topk(None, qdt, None, None, kdt, ks, None, B, 1, 64, HI, dI, 4, k, None, None, 0, None)
+
+
+@pytest.mark.parametrize("HI,dI,ok", [(32, 64, True), (32, 128, True), (64, 64, True), (64, 128, True),
+                                      (16, 128, False), (48, 128, False), (128, 128, False), (64, 32, False),
+                                      (64, 96, False), (64, 256, False)])
+def test_indexer_bf16_mode_sizes(lib, HI, dI, ok):
+    assert _indexer(lib, cakv.BF16, cakv.FP8_E4M3, HI, dI, 1024) == (0 if ok else -2)
+
+
+@pytest.mark.parametrize("HI,dI,ok", [(1, 4, True), (4, 32, True), (64, 128, True), (8, 1024, True),
+                                      (64, 129, False), (65, 32, False), (0, 32, False), (64, 132, False),
+                                      (4, 2, False)])
+def test_indexer_fp32_mode_sizes(lib, HI, dI, ok):
+    assert _indexer(lib, cakv.F32, cakv.F32, HI, dI, 64) == (0 if ok else -2)
+
+
+@pytest.mark.parametrize("k,ok", [(1, True), (1024, True), (4096, True), (0, False), (4097, False)])
+def test_indexer_k_range(lib, k, ok):
+    assert _indexer(lib, cakv.BF16, cakv.FP8_E4M3, 64, 128, k) == (0 if ok else -2)
+
+
+@pytest.mark.parametrize("qdt,kdt", [(cakv.F32, cakv.FP8_E4M3), (cakv.BF16, cakv.F32), (cakv.BF16, cakv.BF16)])
+def test_indexer_mode_dtypes(lib, qdt, kdt):
+    assert _indexer(lib, qdt, kdt, 64, 128, 64) == -2
+
+
+@pytest.mark.parametrize("xdt", [cakv.F32, cakv.BF16])
+@pytest.mark.parametrize("D,ok", [(4, True), (8, True), (12, True), (512, True), (4096, True), (2, False),
+                                  (510, False), (4100, False)])
+def test_kv_compress_dims(lib, xdt, D, ok):
+    rc = lib.cakv_kv_compress(None, xdt, None, 0, 8, D, 4, None, cakv.BF16, None, None)
+    assert rc == (0 if ok else -2)
+
+
+@pytest.mark.parametrize("m,ok", [(1, True), (4, True), (128, True), (4096, True), (0, False), (4097, False)])
+def test_kv_compress_ratios(lib, m, ok):
+    assert lib.cakv_kv_compress(None, cakv.BF16, None, 0, 8, 512, m, None, cakv.BF16, None, None) == (0 if ok else -2)
+
+
+@pytest.mark.parametrize("D,ok", [(8, True), (64, True), (512, True), (4096, True), (4, False), (12, False),
+                                  (4104, False)])
+def test_kv_prepare_dims(lib, D, ok):
+    rc = lib.cakv_kv_prepare(None, None, cakv.BF16, 0, 8, D, 0, 8, None, 4, 0, 10000.0, 0, 1e-6, None)
+    assert rc == (0 if ok else -2)
+
+
+def test_attention_workspace_never_shrinks_with_the_batch(lib):
+    """A workspace sized for the largest batch serves every smaller one: the
+    reported size is non-decreasing in B*Q (the split count grows as the batch
+    shrinks, so the launch workspace alone is not)."""
+    for K, nw in ((1024, 128), (64, 16), (0, 128)):
+        sizes = [lib.cakv_sparse_mqa_workspace(1, bq, 128, 512, K, nw) for bq in range(1, 600)]
+        assert all(b >= a for a, b in zip(sizes, sizes[1:])), K
+    sizes = [lib.cakv_dense_mqa_workspace(bq, 1, 128, 512, 8192, 128) for bq in range(1, 600)]
+    assert all(b >= a for a, b in zip(sizes, sizes[1:]))
+    assert sizes[-1] > 0
+
+
+def test_binding_rejects_wrong_element_types():
+    """The binding checks element types before calling the library (an int64
+    position tensor would otherwise be read as pairs of int32 words)."""
+    import torch
+
+    class FakeDev:  # stands in for a device tensor: only the fields _dev reads
+        is_cuda = True
+
+        def __init__(self, dtype):
+            self.dtype = dtype
+
+        def is_contiguous(self):
+            return True
+
+        def data_ptr(self):
+            return FAKE
+
+    assert cakv._dev(FakeDev(torch.int32), "q_pos", torch.int32) == FAKE
+    with pytest.raises(cakv.CakvError, match="q_pos must be torch.int32"):
+        cakv._dev(FakeDev(torch.int64), "q_pos", torch.int32)
+    with pytest.raises(cakv.CakvError, match="sinks must be torch.float32"):
+        cakv._dev(FakeDev(torch.bfloat16), "sinks", torch.float32)
