@@ -10,6 +10,7 @@ Functions (names follow the C ABI):
   kv_prepare(kv_c, m, rope_dims, ...)                     -> prepared entries (in place by default)
   kv_prepare_raw(kv_raw, raw_pos0, rope_dims, ...)        -> prepared window rows (per-sequence positions)
   indexer_topk(q_idx, w, k_idx, k_scale, q_pos, m, k)     -> idx
+  indexer_topk_noalloc(q_idx, w, k_idx, k_scale, q_pos, m, k, out) -> idx (static scratch)
   sparse_mqa_fwd(q, kv_c, idx, kv_raw, raw_pos0, q_pos, sinks, ...) -> (out, lse)
   dense_compressed_mqa_fwd(q, kv_c, kv_raw, raw_pos0, q_pos, sinks, ...) -> (out, lse)
 """
@@ -44,7 +45,8 @@ _i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_
 
 EXPORTS = ("cakv_version", "cakv_last_error", "cakv_kv_compress", "cakv_kv_prepare", "cakv_indexer_topk_workspace",
            "cakv_indexer_topk", "cakv_sparse_mqa_workspace", "cakv_sparse_mqa_fwd",
-           "cakv_dense_mqa_workspace", "cakv_dense_compressed_mqa_fwd", "cakv_profile_kernel_events")
+           "cakv_dense_mqa_workspace", "cakv_dense_compressed_mqa_fwd", "cakv_profile_kernel_events",
+           "cakv_indexer_topk_noalloc")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -65,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.cakv_indexer_topk_workspace.restype = _sz
     lib.cakv_indexer_topk.argtypes = [_p, ctypes.c_int, _p, _p, ctypes.c_int, _p, _p, _i64, _i64, _i64, _i32,
                                       _i32, _i32, _i32, _p, _p, _sz, _p]
+    lib.cakv_indexer_topk_noalloc.argtypes = [_p, ctypes.c_int, _p, _p, ctypes.c_int, _p, _p, _i64, _i64, _i64,
+                                              _i32, _i32, _i32, _i32, _p, _p]
     lib.cakv_sparse_mqa_workspace.argtypes = [_i64, _i64, _i32, _i32, _i32, _i32]
     lib.cakv_sparse_mqa_workspace.restype = _sz
     lib.cakv_dense_mqa_workspace.argtypes = [_i64, _i64, _i32, _i32, _i64, _i32]
@@ -191,6 +195,23 @@ def _same_act(q, kv_c, kv_raw):
     # the C ABI takes one activation type for q, the cache and the window rows
     if not (q.dtype == kv_c.dtype == kv_raw.dtype):
         raise CakvError(f"q, kv_c and kv_raw must share one dtype ({q.dtype}, {kv_c.dtype}, {kv_raw.dtype})")
+
+
+def indexer_topk_noalloc(q_idx: torch.Tensor, w: torch.Tensor, k_idx: torch.Tensor, k_scale: torch.Tensor | None,
+                         q_pos: torch.Tensor, m: int, k: int, out: torch.Tensor) -> torch.Tensor:
+    """indexer_topk into a caller-provided `out` [B,Q,k] int32, with the
+    library's static per-GPU scratch as its workspace (no device allocation
+    by the library or here)."""
+    lib = load_library()
+    B, Q, HI, dI = q_idx.shape
+    N = k_idx.shape[1]
+    if tuple(out.shape) != (B, Q, k):
+        raise CakvError(f"out must be [{B}, {Q}, {k}]")
+    _check(lib.cakv_indexer_topk_noalloc(_dev(q_idx, "q_idx"), _DT[q_idx.dtype], _dev(w, "w", _F32),
+                                         _dev(k_idx, "k_idx"), _DT[k_idx.dtype], _dev(k_scale, "k_scale", _F32),
+                                         _dev(q_pos, "q_pos", _I32), B, Q, N, HI, dI, m, k, _dev(out, "idx", _I32),
+                                         _stream()))
+    return out
 
 
 def _params(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, gamma_q):

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -169,6 +170,42 @@ int run_attn(cakv::AttnArgs& a, int64_t BQ, int32_t H, int32_t D, int64_t max_sl
     return rc_from(cakv::launch_mqa_fwd(a, BQ, D, act_f32, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int indexer_args(const void* q_idx, int q_dtype, const float* w, const void* k_idx, int k_dtype,
+                 const float* k_scale, const int32_t* q_pos, int64_t B, int64_t Q, int64_t N, int32_t HI,
+                 int32_t dI, int32_t m, int32_t k, int32_t* idx, cakv::IndexerArgs& a, bool& fp8_mode,
+                 bool& empty);
+
+// The allocation-free indexer call keeps its workspace here: one copy of the
+// array per GPU, held until the process ends.  Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the
+// symbol): the device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and kept per device.
+constexpr size_t kScratchBytes = CAKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(CAKV_ELAUNCH, "hipGetDevice failed: %s", hipGetErrorString(e));
+    REQUIRE(dev >= 0 && dev < kMaxDevices, CAKV_EUNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(CAKV_ELAUNCH, "hipGetSymbolAddress of the static scratch failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        REQUIRE((reinterpret_cast<uintptr_t>(p) & 255u) == 0, CAKV_ELAUNCH, "static scratch is not 256-byte aligned");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CAKV_OK;
+}
+
 }  // namespace
 
 namespace cakv {
@@ -261,6 +298,50 @@ int cakv_indexer_topk(const void* q_idx, int q_dtype, const float* w, const void
                       const float* k_scale, const int32_t* q_pos, int64_t B, int64_t Q, int64_t N,
                       int32_t HI, int32_t dI, int32_t m, int32_t k, int32_t* idx, void* workspace,
                       size_t workspace_bytes, void* stream) {
+    cakv::IndexerArgs a{};
+    bool fp8 = false, empty = false;
+    int rc = indexer_args(q_idx, q_dtype, w, k_idx, k_dtype, k_scale, q_pos, B, Q, N, HI, dI, m, k, idx, a, fp8,
+                          empty);
+    if (rc || empty) return rc;
+    const int64_t BQ = B * Q;
+    const size_t need = cakv::indexer_workspace_bytes(BQ, N, k);
+    REQUIRE(workspace_bytes >= need, CAKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    REQUIRE(workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, CAKV_EWORKSPACE,
+            "workspace must be non-NULL and 256-byte aligned");
+    return rc_from(cakv::launch_indexer_topk(a, BQ, fp8, workspace, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cakv_indexer_topk_noalloc(const void* q_idx, int q_dtype, const float* w, const void* k_idx, int k_dtype,
+                              const float* k_scale, const int32_t* q_pos, int64_t B, int64_t Q, int64_t N,
+                              int32_t HI, int32_t dI, int32_t m, int32_t k, int32_t* idx, void* stream) {
+    cakv::IndexerArgs a{};
+    bool fp8 = false, empty = false;
+    int rc = indexer_args(q_idx, q_dtype, w, k_idx, k_dtype, k_scale, q_pos, B, Q, N, HI, dI, m, k, idx, a, fp8,
+                          empty);
+    if (rc || empty) return rc;
+    const int64_t BQ = B * Q;
+    const size_t need = cakv::indexer_workspace_bytes(BQ, N, k);
+    REQUIRE(need <= kScratchBytes, CAKV_EWORKSPACE,
+            "B*Q=%lld queries over N=%lld entries need %zu bytes of scratch, more than the %zu bytes the "
+            "allocation-free call holds per GPU; use cakv_indexer_topk with a workspace",
+            (long long)BQ, (long long)N, need, kScratchBytes);
+    void* ws = nullptr;
+    rc = scratch_of_current_device(&ws);
+    if (rc) return rc;
+    return rc_from(cakv::launch_indexer_topk(a, BQ, fp8, ws, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validation of an indexer call and its launch arguments (shared by the
+// workspace and the allocation-free entry points).  `empty`: nothing to do.
+int indexer_args(const void* q_idx, int q_dtype, const float* w, const void* k_idx, int k_dtype,
+                 const float* k_scale, const int32_t* q_pos, int64_t B, int64_t Q, int64_t N, int32_t HI,
+                 int32_t dI, int32_t m, int32_t k, int32_t* idx, cakv::IndexerArgs& a, bool& fp8_mode,
+                 bool& empty) {
+    empty = false;
     REQUIRE(B >= 0 && Q >= 0 && N >= 0, CAKV_EINVAL, "negative size");
     REQUIRE(m >= 1, CAKV_EINVAL, "m=%d must be >= 1", m);
     REQUIRE(k >= 1 && k <= cakv::kTopkCap, CAKV_EUNSUPPORTED, "k=%d out of 1..%d", k, cakv::kTopkCap);
@@ -276,8 +357,12 @@ int cakv_indexer_topk(const void* q_idx, int q_dtype, const float* w, const void
         REQUIRE((HI == 32 || HI == 64) && (dI == 64 || dI == 128), CAKV_EUNSUPPORTED,
                 "fp8 mode: HI in {32,64}, dI in {64,128} (HI=%d dI=%d)", HI, dI);
     }
+    fp8_mode = fp8;
     const int64_t BQ = B * Q;
-    if (BQ == 0) return ok();
+    if (BQ == 0) {
+        empty = true;
+        return ok();
+    }
     REQUIRE(BQ <= 0x7fffffffLL, CAKV_EUNSUPPORTED, "B*Q too large");
     REQUIRE_PTR(q_idx, "q_idx");
     REQUIRE_PTR(w, "w");
@@ -287,11 +372,7 @@ int cakv_indexer_topk(const void* q_idx, int q_dtype, const float* w, const void
         REQUIRE_PTR(k_idx, "k_idx");
         if (fp8) REQUIRE_PTR(k_scale, "k_scale");
     }
-    const size_t need = cakv::indexer_workspace_bytes(BQ, N, k);
-    REQUIRE(workspace_bytes >= need, CAKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
-    REQUIRE(workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, CAKV_EWORKSPACE,
-            "workspace must be non-NULL and 256-byte aligned");
-    cakv::IndexerArgs a{};
+    a = cakv::IndexerArgs{};
     a.q_idx = q_idx;
     a.w = w;
     a.k_idx = k_idx;
@@ -312,8 +393,12 @@ int cakv_indexer_topk(const void* q_idx, int q_dtype, const float* w, const void
     a.chunk = (int32_t)(ceil_div(units, per_q) * 128);
     a.n_chunks = (int32_t)ceil_div(N > 0 ? N : 1, a.chunk);
     REQUIRE(a.n_chunks <= 65535 && BQ <= 65535, CAKV_EUNSUPPORTED, "grid too large (B*Q=%lld)", (long long)BQ);
-    return rc_from(cakv::launch_indexer_topk(a, BQ, fp8, workspace, reinterpret_cast<hipStream_t>(stream)));
+    return CAKV_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t cakv_sparse_mqa_workspace(int64_t B, int64_t Q, int32_t H, int32_t D, int32_t K, int32_t n_win) {
     if (B < 0 || Q < 0 || H < 1 || D < 1 || K < 0 || n_win < 0) return 0;

@@ -174,6 +174,31 @@ int cakv_indexer_topk(const void* q_idx, int q_dtype, const float* w, const void
                       int32_t* idx, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * indexer_topk_noalloc -- for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.
+ *
+ * cakv_indexer_topk with the same arguments, results and kernels, minus the
+ * workspace: the library keeps it in a static device array of
+ * CAKV_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held until the process ends.
+ * Nothing is allocated; the first call on each device looks up the array's
+ * device address with that device current.  Calls whose
+ * cakv_indexer_topk_workspace(B, Q, N, k) exceeds the array return
+ * CAKV_EWORKSPACE (for example B*Q = 8 queries over N = 262,144 entries need
+ * about 9 MB; B*Q = 64 queries over 262,144 entries still fit).  Every call
+ * on one GPU shares that GPU's array, and each call clears what it needs
+ * cleared itself: calls that can overlap on one GPU (two streams, two
+ * threads) race and must be serialised by the caller.
+ * Errors: as cakv_indexer_topk; EWORKSPACE (too large), ELAUNCH (the device
+ * address could not be looked up).
+ * ------------------------------------------------------------------------- */
+#define CAKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int cakv_indexer_topk_noalloc(const void* q_idx, int q_dtype, const float* w, const void* k_idx,
+                              int k_dtype, const float* k_scale, const int32_t* q_pos, int64_t B,
+                              int64_t Q, int64_t N, int32_t HI, int32_t dI, int32_t m, int32_t k,
+                              int32_t* idx, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Attention parameters shared by sparse_mqa_fwd and dense_compressed_mqa_fwd.
  * [V4-Pro card: RMSNorm on each query head and on the single compressed KV
  * head before the dot product; RoPE on the last 64 dims of query, KV entry and
