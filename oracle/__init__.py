@@ -50,6 +50,8 @@ def _load():
         build(force=False)
         lib = ctypes.CDLL(_SO)
         lib.oracle_kv_compress.argtypes = [_p, ctypes.c_int, _p, _i64, _i64, _i64, ctypes.c_int, _p]
+        lib.oracle_kv_compress_ex.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int,
+                                              ctypes.c_int, _p]
         lib.oracle_e4m3_decode.argtypes = [ctypes.c_int]
         lib.oracle_e4m3_decode.restype = ctypes.c_double
         lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
@@ -99,6 +101,25 @@ def kv_compress(x, gate, m: int) -> np.ndarray:
     B, T, D = xa.shape
     out = np.empty((B, T // m, D), dtype=np.float64)
     _check(lib.oracle_kv_compress(_ptr(xa), xd, _ptr(g), B, T, D, m, _ptr(out)), "kv_compress")
+    return out
+
+
+def kv_compress_ex(x, gate, m: int, span: int = None) -> np.ndarray:
+    """Compression variants: entry j is the softmax-gated sum of the `span`
+    tokens ending where block j ends (span >= m, cut at token 0); `gate` is
+    [B,T] (one logit per token) or [B,T,D] (one per token and channel).
+    fp64 [B, T//m, D]."""
+    lib = _load()
+    xa, xd = _act(x)
+    g = _np(gate, np.float32)
+    B, T, D = xa.shape
+    per_channel = g.ndim == 3
+    if g.shape != ((B, T, D) if per_channel else (B, T)):
+        raise ValueError("gate must be [B,T] or [B,T,D]")
+    span = m if span is None else span
+    out = np.empty((B, T // m, D), dtype=np.float64)
+    _check(lib.oracle_kv_compress_ex(_ptr(xa), xd, _ptr(g), int(per_channel), B, T, D, m, span, _ptr(out)),
+           "kv_compress_ex")
     return out
 
 

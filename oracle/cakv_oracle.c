@@ -110,6 +110,57 @@ int oracle_kv_compress(const void* x, int x_dtype, const float* g, i64 B, i64 T,
 }
 
 /* ------------------------------------------------------------------------ */
+/* O1x compression variants [V4 digest, HCA paragraph: the HCA compressor is */
+/*     stated to be non-overlapping, which leaves room for CSA blocks that   */
+/*     overlap; CSA step 1: the block is merged by learned, attention-like   */
+/*     weights] [Visualised, Dual Compression and Indexing: learned weighted */
+/*     averages].                                                            */
+/*     Readings: entry j still ends where block j ends, so its visibility is */
+/*     unchanged; it covers the `span` tokens before that end (span >= m;    */
+/*     span = m is the plain compressor), cut at token 0.  The gate is one   */
+/*     logit per token, or one per token and channel (then every channel has */
+/*     its own softmax over the entry's tokens):                             */
+/*       S_j = [max(0, (j+1)m - span), (j+1)m),                              */
+/*       a_{i,d} = exp(g_{i,d}) / sum_{i' in S_j} exp(g_{i',d}),             */
+/*       c_j[d]  = sum_{i in S_j} a_{i,d} x_i[d].                            */
+/*     Entries exist for the whole strides j < floor(T/m).                   */
+/* ------------------------------------------------------------------------ */
+int oracle_kv_compress_ex(const void* x, int x_dtype, const float* g, int gate_per_channel, i64 B, i64 T,
+                          i64 D, int m, int span, double* out) {
+    if (m < 1 || span < m || B < 0 || T < 0 || D < 1) return OR_EINVAL;
+    i64 nb = T / m;
+#pragma omp parallel for schedule(static)
+    for (i64 bj = 0; bj < B * nb; ++bj) {
+        i64 b = bj / nb, j = bj % nb;
+        i64 hi = (j + 1) * m, lo = hi - span < 0 ? 0 : hi - span;
+        i64 n = hi - lo;
+        double* a = (double*)malloc(sizeof(double) * (size_t)n);
+        double* o = out + (b * nb + j) * D;
+        for (i64 d = 0; d < D; ++d) {
+            /* the softmax of this channel's logits over the entry's tokens */
+            if (d == 0 || gate_per_channel) {
+                double mx = -INFINITY, z = 0.0;
+                for (i64 i = 0; i < n; ++i) {
+                    double gi = gate_per_channel ? (double)g[(b * T + lo + i) * D + d] : (double)g[b * T + lo + i];
+                    if (gi > mx) mx = gi;
+                }
+                for (i64 i = 0; i < n; ++i) {
+                    double gi = gate_per_channel ? (double)g[(b * T + lo + i) * D + d] : (double)g[b * T + lo + i];
+                    a[i] = exp(gi - mx);
+                    z += a[i];
+                }
+                for (i64 i = 0; i < n; ++i) a[i] /= z;
+            }
+            double s = 0.0;
+            for (i64 i = 0; i < n; ++i) s += a[i] * load_elem(x, x_dtype, (b * T + lo + i) * D + d);
+            o[d] = s;
+        }
+        free(a);
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* fp8 E4M3 (OCP "E4M3FN"): 1 sign bit, 4 exponent bits with bias 7, 3       */
 /* mantissa bits; exponent field 0 holds subnormals M * 2^-9; no infinities;  */
 /* S.1111.111 is NaN; largest finite magnitude 448.                          */

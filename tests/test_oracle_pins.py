@@ -504,3 +504,114 @@ def test_kv_prepare_gives_the_attention_keys():
         assert lse[0, h] == pytest.approx(math.log(z), abs=1e-12)
         o = (np.exp(lg)[:, None] * keys).sum(axis=0) / z
         np.testing.assert_allclose(out[0, h, :D - r], o[:D - r], atol=1e-12)
+
+
+# ---------------------------------------------------------------- compression variants
+
+def _compress_brute(x, gate, m, span):
+    """numpy fp64 from the definition: entry j sums the tokens
+    [max(0, (j+1)m - span), (j+1)m), each channel weighted by its own softmax
+    over those tokens (a per-token gate is the same logit on every channel)."""
+    import scipy.special
+    x = np.asarray(x, np.float64)
+    g = np.asarray(gate, np.float64)
+    B, T, D = x.shape
+    out = np.zeros((B, T // m, D))
+    for b in range(B):
+        for j in range(T // m):
+            hi = (j + 1) * m
+            lo = max(0, hi - span)
+            gg = g[b, lo:hi] if g.ndim == 3 else np.repeat(g[b, lo:hi, None], D, axis=1)
+            out[b, j] = (scipy.special.softmax(gg, axis=0) * x[b, lo:hi]).sum(axis=0)
+    return out
+
+
+@pytest.mark.parametrize("m", [1, 4, 128])
+def test_compress_ex_plain_case_is_the_compressor(m):
+    rng = np.random.default_rng(m)
+    x = rng.standard_normal((2, 3 * m + 5, 16)).astype(np.float32)
+    g = rng.standard_normal((2, 3 * m + 5)).astype(np.float32)
+    assert np.array_equal(oracle.kv_compress_ex(x, g, m), oracle.kv_compress(x, g, m))
+
+
+@pytest.mark.parametrize("m,span,per_channel", [(4, 4, True), (4, 8, False), (4, 8, True), (4, 13, True),
+                                                (3, 7, False), (128, 256, True), (1, 5, True)])
+def test_compress_ex_brute_force(m, span, per_channel):
+    rng = np.random.default_rng(100 * m + span)
+    T, D = 4 * m + 3, 12
+    x = rng.standard_normal((2, T, D)).astype(np.float32)
+    g = rng.standard_normal((2, T, D) if per_channel else (2, T)).astype(np.float32) * 3
+    got = oracle.kv_compress_ex(x, g, m, span)
+    want = _compress_brute(x, g, m, span)
+    assert got.shape == (2, T // m, D)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_compress_ex_per_channel_gate_constant_over_channels_is_per_token():
+    rng = np.random.default_rng(7)
+    x = torch.from_numpy(rng.standard_normal((2, 40, 8)).astype(np.float32)).to(torch.bfloat16)
+    g = rng.standard_normal((2, 40)).astype(np.float32)
+    g3 = np.repeat(g[:, :, None], 8, axis=2)
+    for span in (4, 10):
+        a = oracle.kv_compress_ex(x, g3, 4, span)
+        b = oracle.kv_compress_ex(x, g, 4, span)
+        assert np.array_equal(a, b)
+
+
+def test_compress_ex_closed_forms():
+    rng = np.random.default_rng(8)
+    m, span, T, D = 4, 8, 24, 6
+    x = rng.standard_normal((1, T, D)).astype(np.float32)
+    # equal logits: each entry is the mean of its span (cut at token 0 for j = 0)
+    out = oracle.kv_compress_ex(x, np.zeros((1, T, D), np.float32), m, span)
+    assert np.allclose(out[0, 0], x[0, 0:4].astype(np.float64).mean(0), rtol=1e-14, atol=1e-15)
+    for j in range(1, T // m):
+        assert np.allclose(out[0, j], x[0, (j + 1) * m - span:(j + 1) * m].astype(np.float64).mean(0), rtol=1e-14,
+                           atol=1e-15)
+    # logits ramping by 60 per token dominate every span: channels with a rising
+    # ramp take the span's newest token, channels with a falling ramp its
+    # oldest (the other weights are below e^-60)
+    ramp = 60.0 * np.arange(T, dtype=np.float32)[None, :, None]
+    sign = np.where(np.arange(D) % 2 == 0, 1.0, -1.0).astype(np.float32)
+    out = oracle.kv_compress_ex(x, ramp * sign, m, span)
+    for j in range(T // m):
+        newest, oldest = (j + 1) * m - 1, max(0, (j + 1) * m - span)
+        for d in range(D):
+            i = newest if d % 2 == 0 else oldest
+            assert abs(out[0, j, d] - x[0, i, d]) <= 1e-15 * abs(x[0, i, d]) + 1e-24
+
+
+def test_compress_ex_overlap_masked_to_the_block_is_plain():
+    """With span = 2m and the earlier block's logits pushed to -1e4 (weights
+    e^-1e4 = 0 in fp64), every entry equals the non-overlapping one."""
+    rng = np.random.default_rng(9)
+    m, T, D = 4, 40, 8
+    x = rng.standard_normal((2, T, D)).astype(np.float32)
+    g = rng.standard_normal((2, T)).astype(np.float32)
+    plain = oracle.kv_compress(x, g, m)
+    for j in range(T // m):
+        gm = g.copy()
+        gm[:, max(0, j * m - m):j * m] = -1e4
+        assert np.array_equal(oracle.kv_compress_ex(x, gm, m, 2 * m)[:, j], plain[:, j])
+
+
+def test_compress_ex_linear_and_per_channel_shift_invariant():
+    rng = np.random.default_rng(10)
+    # inputs on a coarse binary grid, so 0.5 x1 + 2 x2 and g + shift are exact in fp32
+    x1 = np.round(rng.standard_normal((1, 30, 5)) * 64) / 64
+    x2 = np.round(rng.standard_normal((1, 30, 5)) * 64) / 64
+    g = (np.round(rng.standard_normal((1, 30, 5)) * 256) / 256).astype(np.float32)
+    f = lambda x, gg: oracle.kv_compress_ex(x.astype(np.float32), gg, 3, 7)
+    assert np.allclose(f(0.5 * x1 + 2 * x2, g), 0.5 * f(x1, g) + 2 * f(x2, g), rtol=1e-13, atol=1e-14)
+    shift = rng.integers(-4, 5, size=(1, 1, 5)).astype(np.float32)  # a constant per channel
+    assert np.allclose(f(x1, g + shift), f(x1, g), rtol=1e-13, atol=1e-14)
+
+
+def test_compress_ex_counts_match_pages():
+    """Entries per stride are unchanged by the overlap: 1,048,576 tokens at
+    m = 4 give 262,144 entries with any span (the count the pages give)."""
+    T = 1048576
+    x = np.zeros((1, T, 4), np.float32)
+    g = np.zeros((1, T), np.float32)
+    assert oracle.kv_compress_ex(x, g, 4, 8).shape[1] == 262144
+    assert oracle.kv_compress_ex(x, g, 128, 128).shape[1] == 8192
