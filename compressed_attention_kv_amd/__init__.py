@@ -7,6 +7,8 @@ fallback: if the library is missing or no GPU is present, calls raise.
 
 Functions (names follow the C ABI):
   kv_compress(x, gate, m, out_dtype)                      -> out (, scale)
+  kv_compress_ex(x, gate, m, span, out_dtype)              -> out (, scale)   (overlap, per-channel gates)
+  kv_append(x_tok, gate_tok, pos, raw_ring, gate_ring, cache, ...)  streaming decode: one token per sequence
   kv_prepare(kv_c, m, rope_dims, ...)                     -> prepared entries (in place by default)
   kv_prepare_raw(kv_raw, raw_pos0, rope_dims, ...)        -> prepared window rows (per-sequence positions)
   indexer_topk(q_idx, w, k_idx, k_scale, q_pos, m, k)     -> idx
@@ -37,7 +39,12 @@ class AttnParams(ctypes.Structure):
     _fields_ = [("m", ctypes.c_int32), ("n_win", ctypes.c_int32), ("rope_dims", ctypes.c_int32),
                 ("rope_base", ctypes.c_float),
                 ("softmax_scale", ctypes.c_float), ("rms_eps", ctypes.c_float),
-                ("gamma_q", ctypes.c_void_p)]
+                ("gamma_q", ctypes.c_void_p), ("raw_ring", ctypes.c_int32)]
+
+
+class PrepParams(ctypes.Structure):
+    _fields_ = [("rope_dims", ctypes.c_int32), ("rope_base", ctypes.c_float), ("entry_pos_offset", ctypes.c_int32),
+                ("rms_eps", ctypes.c_float), ("gamma_kv", ctypes.c_void_p)]
 
 
 _lib = None
@@ -46,7 +53,7 @@ _i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_
 EXPORTS = ("cakv_version", "cakv_last_error", "cakv_kv_compress", "cakv_kv_prepare", "cakv_indexer_topk_workspace",
            "cakv_indexer_topk", "cakv_sparse_mqa_workspace", "cakv_sparse_mqa_fwd",
            "cakv_dense_mqa_workspace", "cakv_dense_compressed_mqa_fwd", "cakv_profile_kernel_events",
-           "cakv_indexer_topk_noalloc")
+           "cakv_indexer_topk_noalloc", "cakv_kv_compress_ex", "cakv_kv_append")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -61,6 +68,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.cakv_last_error.restype = ctypes.c_char_p
     lib.cakv_profile_kernel_events.argtypes = [ctypes.c_char_p, ctypes.POINTER(_p), ctypes.POINTER(_p), ctypes.c_int]
     lib.cakv_kv_compress.argtypes = [_p, ctypes.c_int, _p, _i64, _i64, _i64, _i32, _p, ctypes.c_int, _p, _p]
+    lib.cakv_kv_compress_ex.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p,
+                                        ctypes.c_int, _p, _p]
+    lib.cakv_kv_append.argtypes = [_p, _p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _p, _p, _i64, _p, _i64, _p,
+                                   ctypes.c_int, _p, _i64, _i32, _i32, ctypes.POINTER(PrepParams), _p]
     lib.cakv_kv_prepare.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _p, _i32, _i32,
                                     ctypes.c_float, _i32, ctypes.c_float, _p]
     lib.cakv_indexer_topk_workspace.argtypes = [_i64, _i64, _i64, _i32]
@@ -136,6 +147,58 @@ def kv_compress(x: torch.Tensor, gate: torch.Tensor, m: int, out_dtype: torch.dt
     _check(lib.cakv_kv_compress(_dev(x, "x"), _DT[x.dtype], _dev(gate, "gate", _F32), B, T, D, m, _dev(out, "out"),
                                 _DT[out_dtype], _dev(scale, "scale", _F32), _stream()))
     return (out, scale) if scale is not None else out
+
+
+def kv_compress_ex(x: torch.Tensor, gate: torch.Tensor, m: int, span: int = None, out_dtype: torch.dtype = None,
+                   out: torch.Tensor = None, scale: torch.Tensor = None):
+    """Compressor variants: entry j is the softmax-gated sum of the `span`
+    tokens ending where block j ends (span >= m); gate [B,T] (one logit per
+    token) or [B,T,D] (one per token and channel).  Otherwise as kv_compress."""
+    lib = load_library()
+    B, T, D = x.shape
+    span = m if span is None else span
+    per_channel = gate.dim() == 3
+    out_dtype = out.dtype if out is not None else (out_dtype or x.dtype)
+    nb = T // m
+    if out is None:
+        out = torch.empty((B, nb, D), dtype=out_dtype, device=x.device)
+    elif tuple(out.shape) != (B, nb, D) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [{B}, {nb}, {D}] tensor")
+    if out_dtype == torch.float8_e4m3fn and scale is None:
+        scale = torch.empty((B, nb), dtype=torch.float32, device=x.device)
+    elif out_dtype != torch.float8_e4m3fn:
+        scale = None
+    _check(lib.cakv_kv_compress_ex(_dev(x, "x"), _DT[x.dtype], _dev(gate, "gate", _F32), int(per_channel), B, T, D,
+                                   m, span, _dev(out, "out"), _DT[out_dtype], _dev(scale, "scale", _F32), _stream()))
+    return (out, scale) if scale is not None else out
+
+
+def kv_append(x_tok: torch.Tensor, gate_tok: torch.Tensor, pos: torch.Tensor, raw_ring: torch.Tensor,
+              gate_ring: torch.Tensor, cache: torch.Tensor, *, m: int, span: int = None,
+              cache_scale: torch.Tensor = None, win_ring: torch.Tensor = None, prep: dict | None = None) -> None:
+    """One new token per sequence into one compressor's state (see cakv_kv_append):
+    x_tok [B,D] at positions pos [B] int32 (-1: none) enters raw_ring [B,Rr,D]
+    (gates gate_ring [B,Rr] or [B,Rr,D]), prepared into win_ring [B,Rw,D] if
+    given, and a completed block's entry into cache [B,N,D] (prepared with
+    `prep` = dict(rope_dims, rope_base, entry_pos_offset, rms_eps, gamma_kv),
+    or fp8 codes + cache_scale when prep is None)."""
+    lib = load_library()
+    B, D = x_tok.shape
+    span = m if span is None else span
+    per_channel = gate_tok.dim() == 2
+    pp = None
+    if prep is not None:
+        pp = PrepParams(int(prep.get("rope_dims", 0)), float(prep.get("rope_base", 10000.0)),
+                        int(prep.get("entry_pos_offset", 0)), float(prep.get("rms_eps", 1e-6)),
+                        _dev(prep.get("gamma_kv"), "gamma_kv", _F32))
+    if raw_ring.dtype != x_tok.dtype or (win_ring is not None and win_ring.dtype != x_tok.dtype):
+        raise CakvError("raw_ring and win_ring must have x_tok's dtype")
+    _check(lib.cakv_kv_append(_dev(x_tok, "x_tok"), _dev(gate_tok, "gate_tok", _F32), int(per_channel),
+                              _dev(pos, "pos", _I32), _DT[x_tok.dtype], B, D, _dev(raw_ring, "raw_ring"),
+                              _dev(gate_ring, "gate_ring", _F32), raw_ring.shape[1], _dev(win_ring, "win_ring"),
+                              0 if win_ring is None else win_ring.shape[1], _dev(cache, "cache"), _DT[cache.dtype],
+                              _dev(cache_scale, "cache_scale", _F32), cache.shape[1], m, span,
+                              None if pp is None else ctypes.byref(pp), _stream()))
 
 
 def kv_prepare(kv_c: torch.Tensor, *, m: int, rope_dims: int, rope_base: float = 10000.0,
@@ -214,8 +277,9 @@ def indexer_topk_noalloc(q_idx: torch.Tensor, w: torch.Tensor, k_idx: torch.Tens
     return out
 
 
-def _params(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, gamma_q):
-    return AttnParams(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, _dev(gamma_q, "gamma_q", _F32))
+def _params(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, gamma_q, raw_ring=False):
+    return AttnParams(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, _dev(gamma_q, "gamma_q", _F32),
+                      int(bool(raw_ring)))
 
 
 def sparse_mqa_workspace_bytes(B, Q, H, D, K, n_win) -> int:
@@ -229,11 +293,13 @@ def dense_mqa_workspace_bytes(B, Q, H, D, N, n_win) -> int:
 def sparse_mqa_fwd(q, kv_c, idx, kv_raw, raw_pos0, q_pos, sinks, *, m: int, n_win: int, rope_dims: int,
                    rope_base: float = 10000.0, softmax_scale: float = 0.0,
                    rms_eps: float = 1e-6, gamma_q=None, out_dtype=None, want_lse=True,
-                   out=None, workspace=None):
+                   out=None, workspace=None, raw_ring: bool = False):
     """CSA core attention over the selected entries + raw window + sink.
     q [B,Q,H,D], kv_c [B,N,D], idx [B,Q,K] int32, kv_raw [B,R,D]; returns (out, lse).
     kv_c and kv_raw hold rows prepared by kv_prepare (raw row r of sequence b at
-    position raw_pos0[b] + r: kv_prepare_raw)."""
+    position raw_pos0[b] + r: kv_prepare_raw), or, with raw_ring=True, kv_raw is
+    the window ring kv_append keeps (row p mod R holds position p; raw_pos0 may
+    be None)."""
     lib = load_library()
     B, Q, H, D = q.shape
     N, R, K = kv_c.shape[1], kv_raw.shape[1], idx.shape[-1]
@@ -245,7 +311,7 @@ def sparse_mqa_fwd(q, kv_c, idx, kv_raw, raw_pos0, q_pos, sinks, *, m: int, n_wi
     need = int(lib.cakv_sparse_mqa_workspace(B, Q, H, D, K, n_win))
     if workspace is None or workspace.numel() < need:
         workspace = _workspace(need, q.device)
-    prm = _params(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, gamma_q)
+    prm = _params(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, gamma_q, raw_ring)
     _check(lib.cakv_sparse_mqa_fwd(ctypes.byref(prm), _dev(q, "q"), _dev(kv_c, "kv_c"), _dev(idx, "idx", _I32),
                                    _dev(kv_raw, "kv_raw"), _dev(raw_pos0, "raw_pos0", _I32), _dev(q_pos, "q_pos", _I32),
                                    _dev(sinks, "sinks", _F32), _DT[q.dtype], B, Q, H, D, N, K, R, _dev(out, "out"),
@@ -257,7 +323,7 @@ def sparse_mqa_fwd(q, kv_c, idx, kv_raw, raw_pos0, q_pos, sinks, *, m: int, n_wi
 def dense_compressed_mqa_fwd(q, kv_c, kv_raw, raw_pos0, q_pos, sinks, *, m: int, n_win: int, rope_dims: int,
                              rope_base: float = 10000.0, softmax_scale: float = 0.0,
                              rms_eps: float = 1e-6, gamma_q=None, out_dtype=None, want_lse=True,
-                             out=None, workspace=None):
+                             out=None, workspace=None, raw_ring: bool = False):
     """HCA core attention over every visible compressed entry + raw window + sink
     (rows prepared as for sparse_mqa_fwd)."""
     lib = load_library()
@@ -271,7 +337,7 @@ def dense_compressed_mqa_fwd(q, kv_c, kv_raw, raw_pos0, q_pos, sinks, *, m: int,
     need = int(lib.cakv_dense_mqa_workspace(B, Q, H, D, N, n_win))
     if workspace is None or workspace.numel() < need:
         workspace = _workspace(need, q.device)
-    prm = _params(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, gamma_q)
+    prm = _params(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, gamma_q, raw_ring)
     _check(lib.cakv_dense_compressed_mqa_fwd(ctypes.byref(prm), _dev(q, "q"), _dev(kv_c, "kv_c"),
                                              _dev(kv_raw, "kv_raw"), _dev(raw_pos0, "raw_pos0", _I32),
                                              _dev(q_pos, "q_pos", _I32), _dev(sinks, "sinks", _F32), _DT[q.dtype], B, Q, H, D,

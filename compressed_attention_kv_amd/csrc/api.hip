@@ -109,9 +109,13 @@ int check_attn_common(const cakv_attn_params* p, const void* q, const void* kv_c
     REQUIRE(p->rope_base > 0.0f && isfinite(p->rope_base), CAKV_EINVAL, "rope_base must be positive");
     REQUIRE(p->softmax_scale >= 0.0f && isfinite(p->softmax_scale), CAKV_EINVAL, "softmax_scale must be >= 0");
     REQUIRE(p->rms_eps >= 0.0f && isfinite(p->rms_eps), CAKV_EINVAL, "rms_eps must be >= 0");
+    REQUIRE(p->raw_ring == 0 || p->raw_ring == 1, CAKV_EINVAL, "raw_ring must be 0 or 1");
+    if (p->raw_ring)
+        REQUIRE(R >= p->n_win && R >= 1 && R <= 0x7fffffffLL, CAKV_EINVAL,
+                "ring mode: the window ring needs R >= n_win rows (R=%lld, n_win=%d)", (long long)R, p->n_win);
     if (B * Q == 0) return CAKV_OK;
     REQUIRE_PTR(q, "q");
-    REQUIRE_PTR(raw_pos0, "raw_pos0");
+    if (!p->raw_ring) REQUIRE_PTR(raw_pos0, "raw_pos0");
     REQUIRE_PTR(q_pos, "q_pos");
     REQUIRE_PTR(sinks, "sinks");
     REQUIRE_PTR(out, "out");
@@ -151,6 +155,7 @@ void fill_attn(cakv::AttnArgs& a, const cakv_attn_params* p, const void* q, cons
     a.scale_log2 = (float)(tau * 1.4426950408889634);
     a.rms_eps = p->rms_eps;
     a.out_f32 = out_dtype == CAKV_F32;
+    a.raw_ring = p->raw_ring;
     a.rope_ratio = cakv::rope_ratio_of(p->rope_base, p->rope_dims);
 }
 
@@ -248,8 +253,17 @@ const char* cakv_last_error(void) { return g_err.c_str(); }
 
 int cakv_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B, int64_t T, int64_t D,
                      int32_t m, void* out, int out_dtype, float* out_scale, void* stream) {
+    REQUIRE(m >= 1 && m <= 4096, CAKV_EUNSUPPORTED, "m=%d out of 1..4096", m);
+    return cakv_kv_compress_ex(x, x_dtype, gate, 0, B, T, D, m, m, out, out_dtype, out_scale, stream);
+}
+
+int cakv_kv_compress_ex(const void* x, int x_dtype, const float* gate, int gate_per_channel, int64_t B,
+                        int64_t T, int64_t D, int32_t m, int32_t span, void* out, int out_dtype, float* out_scale,
+                        void* stream) {
     REQUIRE(B >= 0 && T >= 0, CAKV_EINVAL, "negative size (B=%lld T=%lld)", (long long)B, (long long)T);
     REQUIRE(m >= 1 && m <= 4096, CAKV_EUNSUPPORTED, "m=%d out of 1..4096", m);
+    REQUIRE(span >= m && span <= 8192, CAKV_EUNSUPPORTED, "span=%d: m <= span <= 8192 (m=%d)", span, m);
+    REQUIRE(gate_per_channel == 0 || gate_per_channel == 1, CAKV_EINVAL, "gate_per_channel must be 0 or 1");
     REQUIRE(D >= 4 && D <= 4096 && D % 4 == 0, CAKV_EUNSUPPORTED, "D=%lld: 4..4096, a multiple of 4", (long long)D);
     REQUIRE(x_dtype == CAKV_F32 || x_dtype == CAKV_BF16, CAKV_EINVAL, "x_dtype must be F32 or BF16");
     REQUIRE(out_dtype == CAKV_F32 || out_dtype == CAKV_BF16 || out_dtype == CAKV_FP8_E4M3, CAKV_EINVAL,
@@ -261,8 +275,8 @@ int cakv_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B, i
     REQUIRE_PTR(gate, "gate");
     REQUIRE_PTR(out, "out");
     if (out_scale) REQUIRE(aligned16(out_scale), CAKV_EINVAL, "out_scale must be 16-byte aligned");
-    return rc_from(cakv::launch_kv_compress(x, x_dtype, gate, B, T, D, m, out, out_dtype, out_scale,
-                                            reinterpret_cast<hipStream_t>(stream)));
+    return rc_from(cakv::launch_kv_compress(x, x_dtype, gate, gate_per_channel != 0, B, T, D, m, span, out,
+                                            out_dtype, out_scale, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int cakv_kv_prepare(const void* kv_in, void* kv_out, int act_dtype, int64_t B, int64_t N, int64_t D,
@@ -287,6 +301,73 @@ int cakv_kv_prepare(const void* kv_in, void* kv_out, int act_dtype, int64_t B, i
     return rc_from(cakv::launch_kv_prepare(kv_in, kv_out, act_dtype == CAKV_F32 ? 0 : 1, B, N, D, j0, n, gamma_kv,
                                            m, rope_dims, cakv::rope_ratio_of(rope_base, rope_dims), entry_pos_offset, rms_eps,
                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cakv_kv_append(const void* x_tok, const float* gate_tok, int gate_per_channel, const int32_t* pos,
+                   int act_dtype, int64_t B, int64_t D, void* raw_ring, float* gate_ring, int64_t Rr,
+                   void* win_ring, int64_t Rw, void* cache, int cache_dtype, float* cache_scale, int64_t N,
+                   int32_t m, int32_t span, const cakv_prep_params* prep, void* stream) {
+    REQUIRE(B >= 0 && N >= 0, CAKV_EINVAL, "negative size (B=%lld N=%lld)", (long long)B, (long long)N);
+    REQUIRE(act_dtype == CAKV_F32 || act_dtype == CAKV_BF16, CAKV_EINVAL, "act_dtype must be F32 or BF16");
+    REQUIRE(cache_dtype == act_dtype || cache_dtype == CAKV_FP8_E4M3, CAKV_EINVAL,
+            "cache_dtype must be act_dtype or FP8_E4M3");
+    REQUIRE(gate_per_channel == 0 || gate_per_channel == 1, CAKV_EINVAL, "gate_per_channel must be 0 or 1");
+    REQUIRE(D >= 8 && D <= 4096 && D % 8 == 0, CAKV_EUNSUPPORTED, "D=%lld: 8..4096, a multiple of 8", (long long)D);
+    REQUIRE(m >= 1 && m <= 4096, CAKV_EUNSUPPORTED, "m=%d out of 1..4096", m);
+    REQUIRE(span >= m && span <= 8192, CAKV_EUNSUPPORTED, "span=%d: m <= span <= 8192 (m=%d)", span, m);
+    REQUIRE(Rr >= span && Rr <= 0x7fffffffLL, CAKV_EINVAL,
+            "raw ring of %lld rows: at least span=%d (the compressor reads the span's earlier tokens from it)",
+            (long long)Rr, span);
+    REQUIRE((cache_dtype == CAKV_FP8_E4M3) == (cache_scale != nullptr), CAKV_EINVAL,
+            "cache_scale is required for an FP8_E4M3 cache and must be NULL otherwise");
+    REQUIRE(!(prep && cache_dtype == CAKV_FP8_E4M3), CAKV_EINVAL, "fp8 caches hold unprepared entries: prep must be NULL");
+    REQUIRE(!win_ring || prep, CAKV_EINVAL, "a window ring holds prepared rows: prep is required");
+    if (win_ring) REQUIRE(Rw >= 1 && Rw <= 0x7fffffffLL, CAKV_EINVAL, "window ring rows Rw=%lld", (long long)Rw);
+    if (prep) {
+        REQUIRE(prep->rope_dims >= 0 && (prep->rope_dims & 1) == 0 && prep->rope_dims <= D, CAKV_EINVAL,
+                "rope_dims=%d: even, 0..D", prep->rope_dims);
+        REQUIRE(prep->rope_base > 0.0f && isfinite(prep->rope_base), CAKV_EINVAL, "rope_base must be positive");
+        REQUIRE(prep->rms_eps >= 0.0f && isfinite(prep->rms_eps), CAKV_EINVAL, "rms_eps must be >= 0");
+        REQUIRE((N - 1) * (int64_t)m + prep->entry_pos_offset <= 0x7fffffffLL &&
+                    prep->entry_pos_offset >= -0x7fffffffLL,
+                CAKV_EINVAL, "entry positions must fit in int32");
+        if (prep->gamma_kv) REQUIRE(aligned16(prep->gamma_kv), CAKV_EINVAL, "gamma_kv must be 16-byte aligned");
+    }
+    if (B == 0) return ok();
+    REQUIRE(B <= 0x7fffffffLL, CAKV_EUNSUPPORTED, "B too large");
+    REQUIRE_PTR(x_tok, "x_tok");
+    REQUIRE_PTR(gate_tok, "gate_tok");
+    REQUIRE_PTR(pos, "pos");
+    REQUIRE_PTR(raw_ring, "raw_ring");
+    REQUIRE_PTR(gate_ring, "gate_ring");
+    if (win_ring) REQUIRE(aligned16(win_ring), CAKV_EINVAL, "win_ring must be 16-byte aligned");
+    if (N > 0) REQUIRE_PTR(cache, "cache");
+    if (cache_scale) REQUIRE(aligned16(cache_scale), CAKV_EINVAL, "cache_scale must be 16-byte aligned");
+    cakv::AppendArgs a{};
+    a.x_tok = x_tok;
+    a.gate_tok = gate_tok;
+    a.pos = pos;
+    a.raw_ring = raw_ring;
+    a.gate_ring = gate_ring;
+    a.win_ring = win_ring;
+    a.cache = cache;
+    a.cache_scale = cache_scale;
+    a.Rr = Rr;
+    a.Rw = win_ring ? Rw : 1;
+    a.N = N;
+    a.D = (int32_t)D;
+    a.m = m;
+    a.span = span;
+    a.prep = prep != nullptr;
+    if (prep) {
+        a.gamma_kv = prep->gamma_kv;
+        a.rope_dims = prep->rope_dims;
+        a.pos_off = prep->entry_pos_offset;
+        a.eps = prep->rms_eps;
+        a.rope_ratio = cakv::rope_ratio_of(prep->rope_base, prep->rope_dims);
+    }
+    return rc_from(cakv::launch_kv_append(a, B, act_dtype, cache_dtype, gate_per_channel != 0,
+                                          reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t cakv_indexer_topk_workspace(int64_t B, int64_t Q, int64_t N, int32_t k) {

@@ -128,7 +128,9 @@ __device__ __forceinline__ QueryGeom query_geom(const AttnArgs& a, int64_t bq) {
     int32_t lo = t - a.n_win + 1;
     g.p_lo = lo < 0 ? 0 : lo;
     g.n_w = a.n_win > 0 ? t - g.p_lo + 1 : 0;
-    g.raw0 = a.raw_pos0[g.b];
+    // ring mode: position p sits at row p mod R; raw0 is the position of row
+    // 0 in the ring's current lap, so rows of earlier positions wrap around
+    g.raw0 = a.raw_ring ? (int32_t)(t - t % a.R) : a.raw_pos0[g.b];
     return g;
 }
 
@@ -152,6 +154,7 @@ __device__ __forceinline__ const TIn* slot_row(const AttnArgs& a, const QueryGeo
     if (s >= g.n_w) return nullptr;
     int32_t p = g.p_lo + s;
     int64_t row = (int64_t)p - g.raw0;
+    if (a.raw_ring && row < 0) row += a.R;
     if (row < 0 || row >= a.R) return nullptr;
     return reinterpret_cast<const TIn*>(a.kv_raw) + (g.b * a.R + row) * (int64_t)D;
 }

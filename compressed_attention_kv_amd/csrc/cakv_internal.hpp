@@ -41,6 +41,7 @@ struct AttnArgs {
     float rms_eps;
     int32_t n_splits;
     int32_t out_f32;   // 1: float32 output, 0: bf16
+    int32_t raw_ring;  // 1: kv_raw row p mod R holds position p (raw_pos0 unused)
     double rope_ratio; // rope_base^(-2/rope_dims), so theta_i = rope_ratio^i
 };
 
@@ -61,14 +62,45 @@ __device__ __forceinline__ double rope_turns(double ratio, int i) {
     return r * 0.15915494309189533577;
 }
 
-int launch_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B, int64_t T,
-                       int64_t D, int32_t m, void* out, int out_dtype, float* out_scale,
-                       hipStream_t stream);
+// entry j covers tokens [max(0, (j+1)m - span), (j+1)m); gate [B,T] or, with
+// gate_per_channel, [B,T,D]
+int launch_kv_compress(const void* x, int x_dtype, const float* gate, bool gate_per_channel, int64_t B,
+                       int64_t T, int64_t D, int32_t m, int32_t span, void* out, int out_dtype,
+                       float* out_scale, hipStream_t stream);
 
 // dtype 0: float32, 1: bf16; entries j0 .. j0+n-1 of each of the B sequences
 int launch_kv_prepare(const void* in, void* out, int dtype, int64_t B, int64_t N, int64_t D, int64_t j0,
                       int64_t n, const float* gamma, int32_t m, int32_t rope_dims, double rope_ratio,
                       int32_t pos_off, float eps, hipStream_t stream);
+
+// One streaming append (cakv_kv_append): a new token per sequence enters one
+// compressor's rings and, when it completes a block, its cache.
+struct AppendArgs {
+    const void* x_tok;      // [B][D] act
+    const float* gate_tok;  // [B] or [B][D]
+    const int32_t* pos;     // [B]
+    void* raw_ring;         // [B][Rr][D] act
+    float* gate_ring;       // [B][Rr] or [B][Rr][D]
+    void* win_ring;         // [B][Rw][D] act, prepared rows, or NULL
+    void* cache;            // [B][N][D] act (prepared when prep) or fp8 codes
+    float* cache_scale;     // [B][N] fp8 only
+    const float* gamma_kv;  // [D] or NULL
+    int64_t Rr;
+    int64_t Rw;
+    int64_t N;
+    int32_t D;
+    int32_t m;
+    int32_t span;
+    int32_t prep;           // 1: cache entries are prepared (RMSNorm + RoPE)
+    int32_t rope_dims;
+    int32_t pos_off;        // entry j sits at position j*m + pos_off
+    float eps;
+    double rope_ratio;
+};
+
+// act_dtype / cache_dtype: 0 f32, 1 bf16, 2 fp8 (cache only)
+int launch_kv_append(const AppendArgs& a, int64_t B, int act_dtype, int cache_dtype, bool gate_per_channel,
+                     hipStream_t stream);
 
 // sparse (idx != NULL) or dense MQA forward; act_f32: inputs are float32
 int launch_mqa_fwd(const AttnArgs& a, int64_t BQ, int D, bool act_f32, hipStream_t stream);

@@ -1,9 +1,13 @@
 // kv_compress.hip -- softmax-weighted block compression of KV tokens.
 //
 // [V4 digest, CSA step 1; HCA paragraph] [V4-Pro card, Hybrid attention]:
-// every m raw tokens (m = 4 for CSA, 128 for HCA; blocks do not overlap)
-// become one entry, a weighted sum whose weights are a softmax over the
-// block's per-token gate logits.
+// every m raw tokens (m = 4 for CSA, 128 for HCA; by default blocks do not
+// overlap) become one entry, a weighted sum whose weights are a softmax over
+// the block's per-token gate logits.
+//
+// Variants (cakv_kv_compress_ex): an entry's span may reach back over earlier
+// blocks (span > m; the entry still ends where its block ends), and the gate
+// may be one logit per token and channel (each channel its own softmax).
 //
 // Layout and schedule: a workgroup of 256 threads owns `epw` consecutive
 // output entries; each entry is handled by D/4 threads that each own four
@@ -12,34 +16,18 @@
 // is evaluated per thread from the block's m logits (a few L1-resident
 // scalars).  In fp8 mode the entry's max |c| is reduced through LDS and the
 // per-entry power-of-two scale is derived exactly from the fp32 exponent.
-#include "cakv_device.hpp"
+#include "cakv_compress.hpp"
 #include "cakv_internal.hpp"
 
 namespace cakv {
 
-template <typename TIn>
-__device__ __forceinline__ void load4(const TIn* p, float v[4]);
-
-template <>
-__device__ __forceinline__ void load4<float>(const float* p, float v[4]) {
-    f32x4 x = *reinterpret_cast<const f32x4*>(p);
-    v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
-}
-
-template <>
-__device__ __forceinline__ void load4<bf16_t>(const bf16_t* p, float v[4]) {
-    u32x2 x = *reinterpret_cast<const u32x2*>(p);
-    v[0] = bf16_bits_to_f32(x[0] & 0xffffu);
-    v[1] = bf16_bits_to_f32(x[0] >> 16);
-    v[2] = bf16_bits_to_f32(x[1] & 0xffffu);
-    v[3] = bf16_bits_to_f32(x[1] >> 16);
-}
-
-// OUTK: 0 = f32, 1 = bf16, 2 = fp8 E4M3 + per-entry scale
-template <typename TIn, int OUTK>
+// OUTK: 0 = f32, 1 = bf16, 2 = fp8 E4M3 + per-entry scale.  PC: one gate
+// logit per token and channel ([B,T,D]) instead of one per token ([B,T]).
+// Entry j covers tokens [max(0, (j+1)m - span), (j+1)m).
+template <typename TIn, int OUTK, bool PC>
 __global__ __launch_bounds__(256) void kv_compress_kernel(const TIn* __restrict__ x,
                                                           const float* __restrict__ gate, int64_t T,
-                                                          int D, int m, int64_t nblk,
+                                                          int D, int m, int span, int64_t nblk,
                                                           int64_t total, int tpe, int epw,
                                                           void* __restrict__ out,
                                                           float* __restrict__ out_scale) {
@@ -55,42 +43,28 @@ __global__ __launch_bounds__(256) void kv_compress_kernel(const TIn* __restrict_
     }
     const int nch = D / 4;  // 4-channel chunks per entry
     const int per = (nch + tpe - 1) / tpe;
-    float acc[4][4];
+    int ch[4];
+    bool ok[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-        acc[u][0] = acc[u][1] = acc[u][2] = acc[u][3] = 0.0f;
+    for (int u = 0; u < 4; ++u) {
+        ch[u] = c0 + u * tpe;
+        ok[u] = u < per && ch[u] < nch;
+    }
+    float acc[4][4];
     float amx = 0.0f;
     if (live) {
         const int64_t b = e / nblk, j = e % nblk;
-        const float* g = gate + b * T + j * m;
-        float mx = -INFINITY;
-        for (int i = 0; i < m; ++i) mx = fmaxf(mx, g[i]);
-        float z = 0.0f;
-        const TIn* xb = x + (b * T + j * m) * (int64_t)D;
-        for (int i = 0; i < m; ++i) {
-            float wgt = expf(g[i] - mx);
-            z += wgt;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                int ch = c0 + u * tpe;
-                if (u < per && ch < nch) {
-                    float v[4];
-                    load4<TIn>(xb + (int64_t)i * D + ch * 4, v);
-                    acc[u][0] = __builtin_fmaf(wgt, v[0], acc[u][0]);
-                    acc[u][1] = __builtin_fmaf(wgt, v[1], acc[u][1]);
-                    acc[u][2] = __builtin_fmaf(wgt, v[2], acc[u][2]);
-                    acc[u][3] = __builtin_fmaf(wgt, v[3], acc[u][3]);
-                }
-            }
-        }
-        const float rz = 1.0f / z;
+        const int64_t hi = (j + 1) * m, lo = hi - span > 0 ? hi - span : 0;
+        const TIn* xb = x + (b * T + lo) * (int64_t)D;
+        const float* gb = gate + (b * T + lo) * (PC ? (int64_t)D : 1);
+        compress_entry<TIn, PC>(
+            (int)(hi - lo), [&](int i) { return xb + (int64_t)i * D; }, [&](int i) { return gb[i]; },
+            [&](int i) { return gb + (int64_t)i * D; }, ch, ok, acc);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                acc[u][c] *= rz;
-                if (u < per && c0 + u * tpe < nch) amx = fmaxf(amx, __builtin_fabsf(acc[u][c]));
-            }
+            for (int c = 0; c < 4; ++c)
+                if (ok[u]) amx = fmaxf(amx, __builtin_fabsf(acc[u][c]));
     }
     if (OUTK == 2) {
         if (live) atomicMax(&amax[slot], __float_as_uint(amx));
@@ -101,53 +75,41 @@ __global__ __launch_bounds__(256) void kv_compress_kernel(const TIn* __restrict_
         float* o = reinterpret_cast<float*>(out) + e * D;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            int ch = c0 + u * tpe;
-            if (u < per && ch < nch) {
+            if (ok[u]) {
                 f32x4 v = {acc[u][0], acc[u][1], acc[u][2], acc[u][3]};
-                *reinterpret_cast<f32x4*>(o + ch * 4) = v;
+                *reinterpret_cast<f32x4*>(o + ch[u] * 4) = v;
             }
         }
     } else if (OUTK == 1) {
         uint16_t* o = reinterpret_cast<uint16_t*>(out) + e * D;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            int ch = c0 + u * tpe;
-            if (u < per && ch < nch) {
+            if (ok[u]) {
                 u32x2 v;
                 v[0] = f32_to_bf16_bits(acc[u][0]) | (f32_to_bf16_bits(acc[u][1]) << 16);
                 v[1] = f32_to_bf16_bits(acc[u][2]) | (f32_to_bf16_bits(acc[u][3]) << 16);
-                *reinterpret_cast<u32x2*>(o + ch * 4) = v;
+                *reinterpret_cast<u32x2*>(o + ch[u] * 4) = v;
             }
         }
     } else {
-        // s = 2^e, e the smallest integer >= -126 with A <= 448 * 2^e.
-        // A = f * 2^E with f in [0.5, 1) and 448 = 0.875 * 2^9.
-        const float A = __uint_as_float(amax[slot]);
-        int ex = 0;
-        if (A > 0.0f) {
-            int E;
-            float f = __builtin_frexpf(A, &E);
-            ex = (f <= 0.875f) ? E - 9 : E - 8;
-            ex = ex < -126 ? -126 : ex;
-        }
+        const int ex = q8_exponent(__uint_as_float(amax[slot]));
         uint8_t* o = reinterpret_cast<uint8_t*>(out) + e * D;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            int ch = c0 + u * tpe;
-            if (u < per && ch < nch) {
+            if (ok[u]) {
                 uint32_t w = 0;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) w |= e4m3_encode(__builtin_ldexpf(acc[u][c], -ex)) << (8 * c);
-                *reinterpret_cast<uint32_t*>(o + ch * 4) = w;
+                *reinterpret_cast<uint32_t*>(o + ch[u] * 4) = w;
             }
         }
         if (c0 == 0) out_scale[e] = __builtin_ldexpf(1.0f, ex);
     }
 }
 
-int launch_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B, int64_t T,
-                       int64_t D, int32_t m, void* out, int out_dtype, float* out_scale,
-                       hipStream_t stream) {
+int launch_kv_compress(const void* x, int x_dtype, const float* gate, bool gate_per_channel, int64_t B,
+                       int64_t T, int64_t D, int32_t m, int32_t span, void* out, int out_dtype,
+                       float* out_scale, hipStream_t stream) {
     const int64_t nblk = T / m;
     const int64_t total = B * nblk;
     if (total == 0) return 0;
@@ -160,19 +122,22 @@ int launch_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B,
     const int epw = 256 / tpe;
     const int64_t grid = (total + epw - 1) / epw;
     if (grid > 0x7fffffffLL) return -2;
-#define CAKV_KC(TIN, OK)                                                                          \
-    hipLaunchKernelGGL((kv_compress_kernel<TIN, OK>), dim3((unsigned)grid), dim3(256), 0, stream, \
-                       (const TIN*)x, gate, T, (int)D, m, nblk, total, tpe, epw, out, out_scale)
+#define CAKV_KC(TIN, OK, PC)                                                                          \
+    hipLaunchKernelGGL((kv_compress_kernel<TIN, OK, PC>), dim3((unsigned)grid), dim3(256), 0, stream, \
+                       (const TIN*)x, gate, T, (int)D, m, span, nblk, total, tpe, epw, out, out_scale)
+#define CAKV_KC2(TIN, PC)                \
+    if (out_dtype == 0) CAKV_KC(TIN, 0, PC); \
+    else if (out_dtype == 1) CAKV_KC(TIN, 1, PC); \
+    else CAKV_KC(TIN, 2, PC)
     prof_mark("kv_compress_kernel", false, stream);
     if (x_dtype == 0) {
-        if (out_dtype == 0) CAKV_KC(float, 0);
-        else if (out_dtype == 1) CAKV_KC(float, 1);
-        else CAKV_KC(float, 2);
+        if (gate_per_channel) { CAKV_KC2(float, true); }
+        else { CAKV_KC2(float, false); }
     } else {
-        if (out_dtype == 0) CAKV_KC(bf16_t, 0);
-        else if (out_dtype == 1) CAKV_KC(bf16_t, 1);
-        else CAKV_KC(bf16_t, 2);
+        if (gate_per_channel) { CAKV_KC2(bf16_t, true); }
+        else { CAKV_KC2(bf16_t, false); }
     }
+#undef CAKV_KC2
 #undef CAKV_KC
     prof_mark("kv_compress_kernel", true, stream);
     return hipGetLastError() == hipSuccess ? 0 : -4;

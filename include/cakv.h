@@ -105,6 +105,26 @@ int cakv_kv_compress(const void* x, int x_dtype, const float* gate, int64_t B, i
                      void* stream);
 
 /* ---------------------------------------------------------------------------
+ * kv_compress_ex  [V4 digest, HCA paragraph: HCA's compression is stated to
+ * be non-overlapping, which leaves CSA's free to overlap; CSA step 1: the
+ * merge uses learned, attention-like weights; Visualised, Dual Compression
+ * and Indexing: learned weighted averages]
+ *
+ * The compressor's variants.  Entry j covers the span
+ *     S_j = [max(0, (j+1)*m - span), (j+1)*m)
+ * of tokens ending where block j ends (span >= m; span = m is kv_compress),
+ * so entries keep the visibility rule of the other calls (entry j is visible
+ * at t >= (j+1)*m).  With gate_per_channel = 0 the gate is [B, T], one logit
+ * per token; with 1 it is [B, T, D] and every channel d has its own softmax:
+ *     a_{i,d} = softmax_{i in S_j}(gate[b, i, d]);  out[b, j, d] = sum_{i in S_j} a_{i,d} x[b, i, d]
+ * Entries exist for j < floor(T/m).  Other arguments, dtypes, the fp8 scale
+ * rule, sizes and errors as kv_compress; m <= span <= 8192.
+ * ------------------------------------------------------------------------- */
+int cakv_kv_compress_ex(const void* x, int x_dtype, const float* gate, int gate_per_channel, int64_t B,
+                        int64_t T, int64_t D, int32_t m, int32_t span, void* out, int out_dtype,
+                        float* out_scale, void* stream);
+
+/* ---------------------------------------------------------------------------
  * kv_prepare  [V4-Pro card, "Hybrid attention": RMSNorm on the single
  * compressed KV head before the attention dot product; RoPE on the last 64
  * dims of each KV entry]
@@ -213,7 +233,69 @@ typedef struct cakv_attn_params {
     float softmax_scale;      /* 0 selects 1/sqrt(D) */
     float rms_eps;            /* RMSNorm epsilon of the query heads */
     const float* gamma_q;     /* [D] device pointer, NULL = all ones */
+    int32_t raw_ring;         /* 0: kv_raw row r of sequence b holds position
+                                 raw_pos0[b] + r.  1: kv_raw is a ring of R rows,
+                                 row p mod R holding position p, kept by
+                                 cakv_kv_append (raw_pos0 is not read and may
+                                 be NULL); requires R >= n_win, and the ring
+                                 must hold the window of every query (its
+                                 last n_win positions up to t) */
 } cakv_attn_params;
+
+/* ---------------------------------------------------------------------------
+ * kv_append  [V4-Pro card, Hybrid attention: a window of the n_win most recent
+ * uncompressed tokens on every CSA/HCA layer, because compressed keys cannot
+ * reach inside the block being filled; V4 digest, CSA step 1 and HCA
+ * paragraph: every m tokens become one entry once the block is complete]
+ *
+ * The streaming side of a decode step: one new token per sequence enters one
+ * compressor's state.  For sequence b with the new token at t = pos[b]
+ * (t < 0: nothing for this sequence):
+ *   1. raw_ring[b, t mod Rr] = x_tok[b]; gate_ring[b, t mod Rr] = gate_tok[b];
+ *   2. if win_ring: win_ring[b, t mod Rw] = the token prepared at position t
+ *      (as cakv_kv_prepare computes it: RMSNorm with gamma_kv, RoPE);
+ *   3. if (t + 1) mod m == 0 and j = (t + 1)/m - 1 < N: entry j is compressed
+ *      as cakv_kv_compress_ex computes it from the tokens of its span
+ *      [max(0, t + 1 - span), t] (the earlier ones read from the raw ring) and
+ *      stored in cache[b, j]: prepared at position j*m + entry_pos_offset when
+ *      prep is given, else as is (fp8 caches: codes and cache_scale[b, j]).
+ * Streaming a sequence token by token this way leaves bitwise the cache and
+ * the prepared rows that the bulk calls (kv_compress_ex, kv_prepare) write.
+ *   x_tok     [B, D]      act_dtype CAKV_F32 or CAKV_BF16
+ *   gate_tok  [B] float32, or [B, D] with gate_per_channel = 1
+ *   pos       [B] int32
+ *   raw_ring  [B, Rr, D]  act_dtype; Rr >= span.  It must already hold the
+ *             span's earlier tokens (earlier appends leave them there)
+ *   gate_ring [B, Rr] float32, or [B, Rr, D]
+ *   win_ring  [B, Rw, D]  act_dtype prepared rows (prep required), or NULL;
+ *             the attention calls read it as kv_raw with raw_ring = 1
+ *   cache     [B, N, D]  cache_dtype = act_dtype (entries prepared when prep
+ *             is given, stored as compressed otherwise) or CAKV_FP8_E4M3
+ *             with cache_scale [B, N] float32 (prep NULL)
+ *   prep      RMSNorm/RoPE parameters of the cache entries and window rows,
+ *             or NULL for a cache of unprepared entries (indexer keys)
+ *   D 8 .. 4096 a multiple of 8; m 1 .. 4096; m <= span <= 8192.
+ * A decode step of a CSA layer is four calls on one stream: kv_append of the
+ * token's KV (cache kv_c, window ring), kv_append of its indexer key (fp8
+ * cache, no window), indexer_topk, sparse_mqa_fwd with raw_ring = 1; an HCA
+ * layer's is kv_append (m = 128) and dense_compressed_mqa_fwd.  Every call
+ * is asynchronous, allocates nothing and has a fixed launch shape, so a step
+ * can be captured in a HIP graph.
+ * Errors: EINVAL (pointers, dtypes, ring sizes, positions beyond int32),
+ * EUNSUPPORTED (D, m, span).
+ * ------------------------------------------------------------------------- */
+typedef struct cakv_prep_params {
+    int32_t rope_dims;        /* r: rotated trailing dims, even, 0 .. D */
+    float rope_base;
+    int32_t entry_pos_offset; /* entry j sits at position j*m + entry_pos_offset */
+    float rms_eps;
+    const float* gamma_kv;    /* [D] device pointer, NULL = all ones */
+} cakv_prep_params;
+
+int cakv_kv_append(const void* x_tok, const float* gate_tok, int gate_per_channel, const int32_t* pos,
+                   int act_dtype, int64_t B, int64_t D, void* raw_ring, float* gate_ring, int64_t Rr,
+                   void* win_ring, int64_t Rw, void* cache, int cache_dtype, float* cache_scale, int64_t N,
+                   int32_t m, int32_t span, const cakv_prep_params* prep, void* stream);
 
 /* ---------------------------------------------------------------------------
  * sparse_mqa_fwd  [V4 digest, CSA step 3: multi-query attention over the

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 def _prm(**kw):
     d = dict(m=4, n_win=128, rope_dims=64, rope_base=10000.0, softmax_scale=0.0,
-             rms_eps=1e-6, gamma_q=None)
+             rms_eps=1e-6, gamma_q=None, raw_ring=0)
     d.update(kw)
     return cakv.AttnParams(**d)
 
@@ -251,3 +251,53 @@ def test_binding_rejects_wrong_element_types():
         cakv._dev(FakeDev(torch.int64), "q_pos", torch.int32)
     with pytest.raises(cakv.CakvError, match="sinks must be torch.float32"):
         cakv._dev(FakeDev(torch.bfloat16), "sinks", torch.float32)
+
+
+# ---------------------------------------------------------------- compressor variants and the streaming append
+
+@pytest.mark.parametrize("m,span,pc,ok", [(4, 4, 0, True), (4, 8, 1, True), (128, 8192, 0, True), (4, 3, 0, False),
+                                          (4, 8193, 0, False), (0, 4, 0, False)])
+def test_kv_compress_ex_spans(lib, m, span, pc, ok):
+    rc = lib.cakv_kv_compress_ex(None, cakv.BF16, None, pc, 0, 8, 512, m, span, None, cakv.BF16, None, None)
+    assert rc == (0 if ok else -2)
+
+
+def test_kv_compress_ex_errors(lib):
+    f = lib.cakv_kv_compress_ex
+    assert f(FAKE, cakv.BF16, FAKE, 2, 1, 8, 512, 4, 4, FAKE, cakv.BF16, None, None) == -1  # gate kind
+    assert f(FAKE, cakv.BF16, FAKE, 1, 1, 8, 512, 4, 8, FAKE, cakv.FP8_E4M3, None, None) == -1  # scale missing
+    assert f(FAKE, cakv.BF16, None, 1, 1, 8, 512, 4, 8, FAKE, cakv.BF16, None, None) == -1  # gate NULL
+
+
+def _append(lib, **kw):
+    a = dict(x=FAKE, g=FAKE, pc=0, pos=FAKE, act=cakv.BF16, B=2, D=512, raw=FAKE, graw=FAKE, Rr=128, win=FAKE,
+             Rw=128, cache=FAKE, cdt=cakv.BF16, cs=None, N=64, m=4, span=4,
+             prep=ctypes.byref(cakv.PrepParams(64, 10000.0, 0, 1e-6, None)))
+    a.update(kw)
+    return lib.cakv_kv_append(a["x"], a["g"], a["pc"], a["pos"], a["act"], a["B"], a["D"], a["raw"], a["graw"],
+                              a["Rr"], a["win"], a["Rw"], a["cache"], a["cdt"], a["cs"], a["N"], a["m"], a["span"],
+                              a["prep"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0, x=None, pos=None), 0),                                   # nothing to do
+    (dict(Rr=3), -1), (dict(span=8, Rr=7), -1),                         # ring shorter than the span
+    (dict(cdt=cakv.FP8_E4M3), -1),                                      # fp8 cache: scale required
+    (dict(cdt=cakv.FP8_E4M3, cs=FAKE), -1),                             # ... and no preparation
+    (dict(cdt=cakv.FP8_E4M3, cs=FAKE, prep=None, win=None, B=0, x=None), 0),
+    (dict(cdt=cakv.F32), -1),                                           # cache type differs from the tokens'
+    (dict(prep=None), -1),                                              # a window ring needs preparation
+    (dict(D=500), -2), (dict(D=8192), -2), (dict(m=0), -2), (dict(span=3), -2),
+    (dict(pc=2), -1), (dict(x=None), -1), (dict(raw=FAKE + 4), -1),
+    (dict(prep=ctypes.byref(cakv.PrepParams(63, 10000.0, 0, 1e-6, None))), -1),
+    (dict(N=1 << 30, m=4), -1),                                          # entry positions beyond int32
+])
+def test_kv_append_errors(lib, kw, code):
+    assert _append(lib, **kw) == code
+
+
+def test_attention_ring_mode_needs_a_window_sized_ring(lib):
+    assert _sparse(lib, _prm(raw_ring=1), B=0, R=64) == -1      # n_win = 128 > R
+    assert _sparse(lib, _prm(raw_ring=1), B=0, R=128) == 0
+    assert _sparse(lib, _prm(raw_ring=1), raw0=None, R=128, B=0) == 0
+    assert _sparse(lib, _prm(raw_ring=2), B=0, R=128) == -1
