@@ -417,7 +417,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 50; 5 for the prefill chunk)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 5; 2 for the prefill chunk)")
     ap.add_argument("--workload", default="csa_decode_128k",
-                    choices=["csa_decode_128k", "csa_decode_1m", "hca_decode_1m", "prefill_chunk_256k"])
+                    choices=["csa_decode_128k", "csa_decode_1m", "hca_decode_1m", "prefill_chunk_256k",
+                             "flash_csa_decode_128k", "flash_hca_decode_1m"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-queries", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,

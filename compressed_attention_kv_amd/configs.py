@@ -66,6 +66,12 @@ WORKLOADS = {
     "prefill_chunk_256k": Workload(
         name="prefill_chunk_256k", seed=4, B=1, Q=8192, prefill=True, T=262144 + 8192,
         q_pos0=262144, csa=True, hca=True),
+    # V4-Flash attention shapes ("DeepSeek V4-Pro" card, Family: 64 query
+    # heads, CSA top-k 512) at the same contexts as the V4-Pro decode workloads
+    "flash_csa_decode_128k": Workload(
+        name="flash_csa_decode_128k", seed=5, B=32, Q=1, N=32768, t=131072, H=64, k=512),
+    "flash_hca_decode_1m": Workload(
+        name="flash_hca_decode_1m", seed=6, B=32, Q=1, N=8192, t=1048576, m=128, csa=False, hca=True, H=64),
 }
 
 

@@ -240,12 +240,19 @@ struct MmaOp<true> {
 // FINAL: the launch has one split per query and writes the output itself
 // (two instantiations rather than a runtime branch: the final epilogue's
 // values would otherwise stay live in scalar registers across the tile loop).
-template <int D, bool SPARSE, typename TIn, bool FINAL>
+// CS (channel split, H <= 64): wave w owns heads 32 (w & 1) .. +32 and the
+// channel half w >> 1: the QK product runs over its 256 channels and the two
+// waves of a head block add their partial logits through LDS (both then hold
+// the same logits, softmax and P), and the PV product covers its half of the
+// output dims.  Each wave then issues half the MFMAs and LDS reads of a tile,
+// so all four SIMDs stay busy when only 64 heads exist.
+template <int D, bool SPARSE, typename TIn, bool FINAL, bool CS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mqa_fwd_kernel(const AttnArgs a) {
-    constexpr int G = D / 8;                   // 16-byte bf16 granules per K row
-    constexpr int KSTEPS = D / 16;             // QK k-steps
-    constexpr int DT = D / 32;                 // output dim tiles
+    constexpr int KSTEPS = D / 16;             // QK k-steps of a whole row
+    constexpr int DT = D / 32;                 // output dim tiles of a whole row
+    constexpr int KW = CS ? KSTEPS / 2 : KSTEPS;  // k-steps of this wave
+    constexpr int DW = CS ? DT / 2 : DT;          // output dim tiles of this wave
     constexpr bool RAW_F32 = sizeof(TIn) == 4;
     constexpr int RB = D * (int)sizeof(TIn);   // bytes of one raw row
     constexpr int RPU = 1024 / RB;             // rows per 1 KiB asynchronous-load unit
@@ -268,6 +275,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
     constexpr int MS = 8;                      // metadata ring slots
     constexpr int CH = D / 64;                 // 8-channel chunks per lane in the row-norm pass
     static_assert(UNITS % 4 == 0 && RPU >= 1 && BUF >= 32 * (2 * D + PAD), "tile geometry");
+    static_assert(!CS || (PERM && !RAW_F32), "channel split: bf16 rows of 1 KiB");
     static_assert(NU + 1 < 64, "vmcnt range");
     typedef ActLoad<TIn> LD;
     typedef MmaOp<RAW_F32> OP;
@@ -284,12 +292,18 @@ void mqa_fwd_kernel(const AttnArgs a) {
     __shared__ __attribute__((aligned(16))) float il_s[4][32];  // 1/l of each head (epilogue)
     __shared__ float sink_s[FINAL ? 128 : 1];  // sink logits, log2 units (one-split epilogue)
     __shared__ uint32_t redo;
+    // channel split: each wave's partial logits (16 per lane), read by the
+    // other wave of its head block
+    __shared__ __attribute__((aligned(16))) float xch[CS ? 4 : 1][16][64];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
     const int lane = tid & 63;
     const int lrow = lane & 31;
     const int lh = lane >> 5;
+    const int hbk = CS ? (wave & 1) : wave;   // head block: heads 32 hbk .. +32
+    const int chalf = CS ? (wave >> 1) : 0;   // channel half (channel split)
+    const int cbyte = 512 * chalf;            // its byte offset in a K row (256 bf16 channels)
     const int64_t wg = xcd_order(blockIdx.x + (int64_t)gridDim.x * blockIdx.y, (int64_t)gridDim.x * gridDim.y);
     const int64_t bq = wg / a.n_splits;
     const int split = (int)(wg % a.n_splits);
@@ -357,8 +371,8 @@ void mqa_fwd_kernel(const AttnArgs a) {
     // the rotation table and wave 0 turns the indices into the metadata of the
     // first four tiles.  The first three tiles start landing before the query
     // rows are awaited, and Q~ is built while they land.
-    const bool has_heads = 32 * wave < H;
-    const int qhead = 32 * wave + lrow;
+    const bool has_heads = 32 * hbk < H;
+    const int qhead = 32 * hbk + lrow;
     // metadata of the first four tiles and the indices of the fifth (the
     // entry-index loads are all issued before any is used)
     int32_t jst[5];
@@ -415,11 +429,12 @@ void mqa_fwd_kernel(const AttnArgs a) {
         for (int k = 0; k < GQ; ++k) gq_pre[k] = 1.0f;
     }
     const float sink_pre = FINAL ? a.sinks[tid < H ? tid : H - 1] : 0.0f;
-    typename LD::raw_t qr[KSTEPS];  // lane: head qhead, channels 16 s + 8 lh + (0..7)
+    typename LD::raw_t qr[KW];  // lane: head qhead, channels 16 (s + KW chalf) + 8 lh + (0..7)
     {
-        const TIn* qrow = reinterpret_cast<const TIn*>(a.q) + (bq * H + (qhead < H ? qhead : 0)) * (int64_t)D + 8 * lh;
+        const TIn* qrow = reinterpret_cast<const TIn*>(a.q) + (bq * H + (qhead < H ? qhead : 0)) * (int64_t)D + 8 * lh +
+                          16 * KW * chalf;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) qr[s] = LD::load(qrow + 16 * s);
+        for (int s = 0; s < KW; ++s) qr[s] = LD::load(qrow + 16 * s);
     }
     if (wave == 1 && lane < n_pairs) {
         const double tn = rope_turns(a.rope_ratio, lane);
@@ -446,28 +461,36 @@ void mqa_fwd_kernel(const AttnArgs a) {
     // head's 1/rms(q) and the softmax scale (times log2 e) multiply its
     // logits instead: invq, per lane (the logits' column is the head).  f16
     // operands (f32 activations) take 1/rms inside Q~ to bound their range.
-    opvec qf[KSTEPS];
+    opvec qf[KW];
     float invq;
     {
         float ss = 0.0f;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) ss = LD::sumsq(qr[s], ss);
+        for (int s = 0; s < KW; ++s) ss = LD::sumsq(qr[s], ss);
         ss = xor32_sum(ss);
+        if constexpr (CS) {
+            // the head's sum of squares over both channel halves: this wave's
+            // plus the partner's (addition commutes, so both get the same bits)
+            if (lane < 32) il_s[wave][lrow] = ss;
+            barrier_lds();
+            ss = ss + il_s[wave ^ 2][lrow];
+        }
         const float inv = __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps);
         invq = RAW_F32 ? a.scale_log2 : inv * a.scale_log2;
         const float qs = RAW_F32 ? inv : 1.0f;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
+        for (int sl = 0; sl < KW; ++sl) {
+            const int s = sl + KW * chalf;  // k-step of the whole row (uniform)
             const int d0 = 16 * s + 8 * lh;  // this lane's 8-channel chunk
             const bool rot_any = 16 * s + 16 > rope_lo;  // uniform
             if constexpr (!RAW_F32) {
                 if (!has_gq && !rot_any) {  // uniform: the bf16 row as it is
-                    qf[s] = __builtin_bit_cast(opvec, qr[s]);
+                    qf[sl] = __builtin_bit_cast(opvec, qr[sl]);
                     continue;
                 }
             }
             float v[8];
-            LD::to_f32(qr[s], v);
+            LD::to_f32(qr[sl], v);
             if (has_gq) {
                 const f32x4 f0 = *reinterpret_cast<const f32x4*>(&fq_s[d0]);
                 const f32x4 f1 = *reinterpret_cast<const f32x4*>(&fq_s[d0 + 4]);
@@ -504,8 +527,8 @@ void mqa_fwd_kernel(const AttnArgs a) {
                     v[2 * pi + 1] = x0 * sn + x1 * cs;
                 }
             }
-            qf[s] = __builtin_bit_cast(opvec, u32x4{OP::pack(v[0], v[1]), OP::pack(v[2], v[3]),
-                                                     OP::pack(v[4], v[5]), OP::pack(v[6], v[7])});
+            qf[sl] = __builtin_bit_cast(opvec, u32x4{OP::pack(v[0], v[1]), OP::pack(v[2], v[3]),
+                                                      OP::pack(v[4], v[5]), OP::pack(v[6], v[7])});
         }
     }
 
@@ -546,7 +569,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
     // keeps tracking the true max m_seen, and the tile loop runs a second
     // pass for the flagged waves with m_use = m_seen (then P <= 1).  Typical
     // inputs never take the second pass.
-    f32x16 acc[DT];
+    f32x16 acc[DW];
     float m_use = -INFINITY, m_seen = -INFINITY, l_run = 0.0f;
     bool flagged = false;  // wave-uniform
     bool active = has_heads;
@@ -557,8 +580,30 @@ void mqa_fwd_kernel(const AttnArgs a) {
     // operand is read in that order straight from the row-major tile with
     // ds_read_b64_tr_b16 (in each 16-lane group, lane i receives element
     // i % 4 of the 8-byte chunks addressed by lanes 4k + i / 4, k = 0..3).
+    // channel split: add the other channel half's partial logits (the two
+    // waves of a head block exchange them through LDS; every wave takes part
+    // in the barrier, also one with no work in this step)
+    auto exchange = [&](f32x16& st, bool work) __attribute__((always_inline)) {
+        if constexpr (CS) {
+            const int ol = opaque_tid() & 63;
+            if (work) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xch[wave][r][ol] = st[r];
+            }
+            barrier_lds();
+            if (work) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) st[r] = st[r] + xch[wave ^ 2][r][ol];
+            }
+        }
+    };
+
     auto compute_tile = [&](int mslot, const uint8_t* kh) __attribute__((always_inline)) {
-        if (!active) return;
+        if (!active) {
+            f32x16 none;
+            exchange(none, false);
+            return;
+        }
         const uint32_t mask = __builtin_amdgcn_readfirstlane(meta[mslot].mask);
         const int ol = opaque_tid() & 63;
         const int orow = ol & 31, oh = ol >> 5;
@@ -566,10 +611,12 @@ void mqa_fwd_kernel(const AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[r] = 0.0f;
         // K row orow, logical granule 2s + oh, stored at (2s + oh) ^ a(orow):
-        // k-step s = 2m + j reads byte 64 m + 32 (j ^ (a >> 1)) + 16 (oh ^ (a & 1))
+        // k-step s = 2m + j reads byte 64 m + 32 (j ^ (a >> 1)) + 16 (oh ^ (a & 1));
+        // a channel half starts 512 bytes in (the permutation keeps the granule's
+        // high bits)
         const int ga = gperm(orow);
-        const uint8_t* kq0 = kh + orow * RS + 16 * (oh ^ (ga & 1)) + 32 * (ga >> 1);
-        const uint8_t* kq1 = kh + orow * RS + 16 * (oh ^ (ga & 1)) + 32 * ((ga >> 1) ^ 1);
+        const uint8_t* kq0 = kh + orow * RS + cbyte + 16 * (oh ^ (ga & 1)) + 32 * (ga >> 1);
+        const uint8_t* kq1 = kh + orow * RS + cbyte + 16 * (oh ^ (ga & 1)) + 32 * ((ga >> 1) ^ 1);
         auto kread = [&](int s) __attribute__((always_inline)) -> opvec {
             return *reinterpret_cast<const opvec*>(((s & 1) ? kq1 : kq0) + 64 * (s >> 1));
         };
@@ -581,18 +628,19 @@ void mqa_fwd_kernel(const AttnArgs a) {
 #pragma unroll
         for (int s = 0; s < QPF; ++s) kq[s] = kread(s);
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
+        for (int s = 0; s < KW; ++s) {
             const opvec av = kq[s % QPF];
-            if (s + QPF < KSTEPS) kq[s % QPF] = kread(s + QPF);
+            if (s + QPF < KW) kq[s % QPF] = kread(s + QPF);
             st = OP::mfma(av, qf[s], st);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, QPF, 2);
 #pragma unroll
-        for (int s = 0; s + QPF < KSTEPS; ++s) {
+        for (int s = 0; s + QPF < KW; ++s) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, QPF, 2);
+        exchange(st, true);
         // logits in log2 units: the head's 1/rms(q) times the softmax scale
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[r] *= invq;
@@ -633,7 +681,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int rr = 8 * hf + 4 * (q >> 1) + (i16 >> 2);
-            vrow[hf] = kh + rr * RS + 16 * ((2 * (q & 1) + ((i16 & 3) >> 1)) ^ gperm(rr)) + 8 * (i16 & 1);
+            vrow[hf] = kh + rr * RS + cbyte + 16 * ((2 * (q & 1) + ((i16 & 3) >> 1)) ^ gperm(rr)) + 8 * (i16 & 1);
         }
         // V operands of output tile dt+1 are read while tile dt is multiplied
         auto vread = [&](int dt, int ks) __attribute__((always_inline)) -> opvec {
@@ -651,8 +699,8 @@ void mqa_fwd_kernel(const AttnArgs a) {
             vb[d][1] = vread(d, 1);
         }
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            if (dt + VPF < DT) {
+        for (int dt = 0; dt < DW; ++dt) {
+            if (dt + VPF < DW) {
                 vb[(dt + VPF) % (VPF + 1)][0] = vread(dt + VPF, 0);
                 vb[(dt + VPF) % (VPF + 1)][1] = vread(dt + VPF, 1);
             }
@@ -663,7 +711,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
         // (MFMA, two reads VPF tiles ahead) pairs, then the last MFMAs
         __builtin_amdgcn_sched_group_barrier(0x100, 4 * VPF, 0);
 #pragma unroll
-        for (int dt = 0; dt + VPF < DT; ++dt) {
+        for (int dt = 0; dt + VPF < DW; ++dt) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -735,8 +783,8 @@ void mqa_fwd_kernel(const AttnArgs a) {
         // ---- A: QK of T
         const int orow = ol & 31, oh = ol >> 5;
         const int ga = gperm(orow);
-        const uint8_t* kq0 = kh + orow * RS + 16 * (oh ^ (ga & 1)) + 32 * (ga >> 1);
-        const uint8_t* kq1 = kh + orow * RS + 16 * (oh ^ (ga & 1)) + 32 * ((ga >> 1) ^ 1);
+        const uint8_t* kq0 = kh + orow * RS + cbyte + 16 * (oh ^ (ga & 1)) + 32 * (ga >> 1);
+        const uint8_t* kq1 = kh + orow * RS + cbyte + 16 * (oh ^ (ga & 1)) + 32 * ((ga >> 1) ^ 1);
         auto kread = [&](int s2) __attribute__((always_inline)) -> opvec {
             return *reinterpret_cast<const opvec*>(((s2 & 1) ? kq1 : kq0) + 64 * (s2 >> 1));
         };
@@ -747,21 +795,25 @@ void mqa_fwd_kernel(const AttnArgs a) {
         f32x16 st;
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[r] = 0.0f;
+        constexpr int DE = KW / NU;  // QK MFMAs per row copy of T+3
+        static_assert(DE >= 1 && KW % NU == 0, "copies between the QK MFMAs");
 #pragma unroll
-        for (int s2 = 0; s2 < KSTEPS; ++s2) {
+        for (int s2 = 0; s2 < KW; ++s2) {
             const opvec av = kq[s2 % QPF];
-            if (s2 + QPF < KSTEPS) kq[s2 % QPF] = kread(s2 + QPF);
+            if (s2 + QPF < KW) kq[s2 % QPF] = kread(s2 + QPF);
             st = OP::mfma(av, qf[s2], st);
-            if ((s2 & 3) == 1 && (s2 >> 2) < NU) dma_unit(s2 >> 2);
+            if (s2 % DE == (DE > 1 ? 1 : 0) && s2 / DE < NU) dma_unit(s2 / DE);
         }
         // pinned order: the first reads, then each MFMA followed by the read
         // that runs ahead of it (else the prefetch collapses under pressure)
         __builtin_amdgcn_sched_group_barrier(0x100, QPF, 2);
 #pragma unroll
-        for (int s2 = 0; s2 < KSTEPS; ++s2) {
+        for (int s2 = 0; s2 < KW; ++s2) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-            if (s2 + QPF < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+            if (s2 + QPF < KW) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        exchange(st, true);
         __builtin_amdgcn_sched_barrier(0);
         // ---- B: logits relative to m_use (log2 units), P of the first keys
         if (__ballot(m_use == -INFINITY)) {  // first tile of the pass: m_use is its max
@@ -791,17 +843,18 @@ void mqa_fwd_kernel(const AttnArgs a) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int rr = 8 * hf + 4 * (q >> 1) + (i16 >> 2);
-            vrow[hf] = kh + rr * RS + 16 * ((2 * (q & 1) + ((i16 & 3) >> 1)) ^ gperm(rr)) + 8 * (i16 & 1);
+            vrow[hf] = kh + rr * RS + cbyte + 16 * ((2 * (q & 1) + ((i16 & 3) >> 1)) ^ gperm(rr)) + 8 * (i16 & 1);
         }
         auto vread = [&](int j) __attribute__((always_inline)) -> opvec {
-            const int dt = j & (DT - 1), ks = j / DT;
+            const int dt = j & (DW - 1), ks = j / DW;
             const int off = ks * 16 * RS + 64 * dt;
             const h4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)const_cast<uint8_t*>(vrow[0] + off));
             const h4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)const_cast<uint8_t*>(vrow[1] + off));
             const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
             return __builtin_bit_cast(opvec, u32x4{w0[0], w0[1], w1[0], w1[1]});
         };
-        constexpr int VPF = 4, NJ = 2 * DT;
+        constexpr int VPF = 4, NJ = 2 * DW;
+        static_assert(!PERM || NJ > 8, "the second keys' P, the max and the sums ride under the PV MFMAs");
         opvec vb[VPF];
 #pragma unroll
         for (int j = 0; j < VPF; ++j) vb[j] = vread(j);
@@ -811,10 +864,10 @@ void mqa_fwd_kernel(const AttnArgs a) {
         for (int j = 0; j < NJ; ++j) {
             const opvec bv = vb[j % VPF];
             if (j + VPF < NJ) vb[j % VPF] = vread(j + VPF);
-            if (j < DT) {
+            if (j < DW) {
                 acc[j] = OP::mfma(pa0, bv, acc[j]);
             } else {
-                acc[j - DT] = OP::mfma(pa1, bv, acc[j - DT]);
+                acc[j - DW] = OP::mfma(pa1, bv, acc[j - DW]);
             }
             // the second keys' P (needed from k-step 1 on), the max, the sums
             if (j >= 1 && j <= 4) {
@@ -864,7 +917,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
         }
         if (active) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DW; ++dt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
         }
@@ -893,7 +946,8 @@ void mqa_fwd_kernel(const AttnArgs a) {
     // ---------------------------------------------------------------- epilogue
     // (lane indices re-derived here: nothing lane-dependent stays live across the loop)
     const int el = opaque_tid() & 63, erow = el & 31, eh = el >> 5;
-    const int head = 32 * wave + erow;
+    const int head = 32 * hbk + erow;
+    const int dt0 = DW * chalf;  // first output dim tile of this wave
     if constexpr (FINAL) {
         // One split: the final output straight from the accumulator.  Per head,
         // in log2 units, Z = l + 2^(sink - m_use) and out = O / Z; the last r
@@ -908,7 +962,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
                 lse = m_use + __builtin_log2f(z);
             }
             il_s[wave][erow] = zi;
-            if (head < H && a.lse) a.lse[bq * H + head] = lse * 0.6931471805599453f;
+            if (head < H && a.lse && chalf == 0) a.lse[bq * H + head] = lse * 0.6931471805599453f;
         }
         f32x4 zi[4];  // 1/Z of this lane's accumulator rows 8 (r/4) + 4 eh + r%4
 #pragma unroll
@@ -937,16 +991,18 @@ void mqa_fwd_kernel(const AttnArgs a) {
         const bool odd = erow & 1;
         const bool f32o = a.out_f32 != 0;
         // the wave's 32 heads all exist (uniform): stores need no per-lane test
-        const bool full = 32 * wave + 32 <= H;
+        const bool full = 32 * hbk + 32 <= H;
         uint8_t* ob = ring[wave];
         // (one unrolled pass per output type: a branch on the type inside the
         // unrolled loop costs a scalar branch and exec-mask set-up per store)
+        // dt: this wave's output tile, dtg = dt0 + dt the row's
         auto out_rows = [&](auto&& put) __attribute__((always_inline)) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const bool tile_rot = dt >= DT - 2 && 32 * dt + 32 > rope_lo;  // uniform
-            const float sn = dt >= DT - 2 ? rsn[dt - (DT - 2)] : 0.0f;
-            const float cs = dt >= DT - 2 ? rcs[dt - (DT - 2)] : 1.0f;
+        for (int dt = 0; dt < DW; ++dt) {
+            const int dtg = dt0 + dt;
+            const bool tile_rot = dtg >= DT - 2 && 32 * dtg + 32 > rope_lo;  // uniform
+            const float sn = dtg == DT - 2 ? rsn[0] : (dtg == DT - 1 ? rsn[1] : 0.0f);
+            const float cs = dtg == DT - 2 ? rcs[0] : (dtg == DT - 1 ? rcs[1] : 1.0f);
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
                 float v[2];
@@ -967,25 +1023,28 @@ void mqa_fwd_kernel(const AttnArgs a) {
         };
         if (f32o) {
             out_rows([&](int dt, int row, float lo, float hi) __attribute__((always_inline)) {
-                const int hr = 32 * wave + row;
+                const int hr = 32 * hbk + row;
                 if (hr < H)
-                    *reinterpret_cast<float2*>(reinterpret_cast<float*>(a.out) + (bq * H + hr) * (int64_t)D + 32 * dt +
-                                               (erow & ~1)) = make_float2(lo, hi);
+                    *reinterpret_cast<float2*>(reinterpret_cast<float*>(a.out) + (bq * H + hr) * (int64_t)D +
+                                               32 * (dt0 + dt) + (erow & ~1)) = make_float2(lo, hi);
             });
         } else {
+            // the wave's part of a row (all of it, or one channel half) is
+            // staged as DW * 16 words
             out_rows([&](int dt, int row, float lo, float hi) __attribute__((always_inline)) {
                 const int word = (16 * dt + (erow >> 1)) ^ (((row >> 2) & 1) << 5);
                 *reinterpret_cast<uint32_t*>(ob + row * RS + 4 * word) = pack_bf16x2(lo, hi);
             });
-            constexpr int LPRO = D / 8;     // lanes per bf16 output row (16 bytes each)
-            constexpr int RPI = 64 / LPRO;  // rows per instruction
+            constexpr int LPRO = DW * 32 / 8;  // lanes per bf16 output row part (16 bytes each)
+            constexpr int RPI = 64 / LPRO;     // rows per instruction
 #pragma unroll
             for (int h0 = 0; h0 < 32; h0 += RPI) {
                 const int h = h0 + el / LPRO, c = el % LPRO;
-                const int hr = 32 * wave + h;
+                const int hr = 32 * hbk + h;
                 const u32x4 w = *reinterpret_cast<const u32x4*>(ob + h * RS + 4 * ((4 * c) ^ (((h >> 2) & 1) << 5)));
                 if (full || hr < H)
-                    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + (bq * H + hr) * (int64_t)D + 8 * c) = w;
+                    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + (bq * H + hr) * (int64_t)D +
+                                              32 * dt0 + 8 * c) = w;
             }
         }
         return;
@@ -997,7 +1056,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
     const int S = a.n_splits;
     const int64_t base = (bq * S + split) * (int64_t)H;
     if (el < 32) {
-        if (head < H) {
+        if (head < H && chalf == 0) {
             a.part_ml[(base + head) * 2] = m_use;
             a.part_ml[(base + head) * 2 + 1] = l_run;
         }
@@ -1010,16 +1069,16 @@ void mqa_fwd_kernel(const AttnArgs a) {
     // (a wave whose 32 heads all exist stores without a per-lane test)
     auto put_partials = [&](bool check) __attribute__((always_inline)) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DW; ++dt)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                const int hr = 32 * wave + 8 * (r >> 2) + 4 * eh + (r & 3);  // even
+                const int hr = 32 * hbk + 8 * (r >> 2) + 4 * eh + (r & 3);  // even
                 if (!check || hr < H)
-                    a.part_o[(pbase + (hr >> 1)) * D + 32 * dt + erow] =
+                    a.part_o[(pbase + (hr >> 1)) * D + 32 * (dt0 + dt) + erow] =
                         pack_f16x2(acc[dt][r] * il[r >> 2][r & 3], acc[dt][r + 1] * il[r >> 2][(r & 3) + 1]);
             }
     };
-    if (32 * wave + 32 <= H) put_partials(false);
+    if (32 * hbk + 32 <= H) put_partials(false);
     else put_partials(true);
 }
 
@@ -1107,14 +1166,14 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(const AttnArgs a) {
     }
 }
 
-template <int D, bool SPARSE, typename TIn>
+template <int D, bool SPARSE, typename TIn, bool CS>
 static int launch_one(const AttnArgs& a, int64_t BQ, hipStream_t stream) {
     dim3 grid((unsigned)a.n_splits, (unsigned)BQ);
     prof_mark("mqa_fwd_kernel", false, stream);
     if (a.n_splits == 1)
-        hipLaunchKernelGGL((mqa_fwd_kernel<D, SPARSE, TIn, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((mqa_fwd_kernel<D, SPARSE, TIn, true, CS>), grid, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((mqa_fwd_kernel<D, SPARSE, TIn, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((mqa_fwd_kernel<D, SPARSE, TIn, false, CS>), grid, dim3(256), 0, stream, a);
     prof_mark("mqa_fwd_kernel", true, stream);
     if (hipGetLastError() != hipSuccess) return -4;
     if (a.n_splits == 1) return 0;  // the forward kernel wrote the output itself
@@ -1131,11 +1190,16 @@ static int launch_d(const AttnArgs& a, int64_t BQ, bool act_f32, hipStream_t str
     const bool sparse = a.idx != nullptr;
     if constexpr (D <= 128) {
         if (act_f32)
-            return sparse ? launch_one<D, true, float>(a, BQ, stream) : launch_one<D, false, float>(a, BQ, stream);
+            return sparse ? launch_one<D, true, float, false>(a, BQ, stream)
+                          : launch_one<D, false, float, false>(a, BQ, stream);
     } else {
         if (act_f32) return -2;  // f32 activations: head dims up to 128
+        // up to 64 heads: the channel-split geometry keeps all four waves busy
+        if (a.H <= 64)
+            return sparse ? launch_one<D, true, bf16_t, true>(a, BQ, stream)
+                          : launch_one<D, false, bf16_t, true>(a, BQ, stream);
     }
-    return sparse ? launch_one<D, true, bf16_t>(a, BQ, stream) : launch_one<D, false, bf16_t>(a, BQ, stream);
+    return sparse ? launch_one<D, true, bf16_t, false>(a, BQ, stream) : launch_one<D, false, bf16_t, false>(a, BQ, stream);
 }
 
 int launch_mqa_fwd(const AttnArgs& a, int64_t BQ, int D, bool act_f32, hipStream_t stream) {
