@@ -64,6 +64,16 @@ def _load():
         lib.oracle_attention.argtypes = [ctypes.POINTER(AttnParams), _p, _p, _p, ctypes.c_int, _p, _p,
                                          _p, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
                                          _i64, _p, _i64, _p, _p]
+        lib.oracle_kv_prepare_bwd.argtypes = [_p, ctypes.c_int, _p, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double, _p, _p,
+                                              _p]
+        lib.oracle_kv_compress_bwd.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int,
+                                               ctypes.c_int, _p, _p, _p]
+        lib.oracle_indexer_bwd.argtypes = [_p, ctypes.c_int, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, _p, ctypes.c_int, _p, _p, _p]
+        lib.oracle_attention_bwd.argtypes = [ctypes.POINTER(AttnParams), _p, _p, _p, ctypes.c_int, _p, _p, _p, _p,
+                                             _p, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _i64, _p, _p, _p,
+                                             _p, _p, _p]
         _lib = lib
     return _lib
 
@@ -248,3 +258,99 @@ def attention(q, kv_c, kv_raw, raw_pos0, q_pos, sinks, *, idx=None, m: int, n_wi
                                 _ptr(qp), _ptr(sk), _ptr(gq), _ptr(gk), qd, B, Q, H, D, N, R, _ptr(r), n,
                                 _ptr(out), _ptr(lse)), "attention")
     return out, lse
+
+
+# ---------------------------------------------------------------- backward (training)
+
+def kv_prepare_bwd(kv_c, dy, *, m: int, rope_dims: int, rope_base: float = 10000.0, entry_pos_offset: int = 0,
+                   rms_eps: float = 1e-6, gamma_kv=None, j0: int = 0, n=None):
+    """Gradient of kv_prepare: dy [B,n,D] of the prepared rows of entries
+    j0 .. j0+n-1 -> (dx [B,n,D] of the raw entries, dgamma_kv [D]), fp64."""
+    lib = _load()
+    ka, kd = _act(kv_c)
+    B, N, D = ka.shape
+    n = N - j0 if n is None else n
+    dya = np.ascontiguousarray(dy, dtype=np.float64)
+    assert dya.shape == (B, n, D)
+    gk = None if gamma_kv is None else _np(gamma_kv, np.float32)
+    dx = np.empty((B, n, D), dtype=np.float64)
+    dg = np.empty((D,), dtype=np.float64)
+    _check(lib.oracle_kv_prepare_bwd(_ptr(ka), kd, _ptr(gk), B, N, D, j0, n, m, rope_dims, rope_base,
+                                     entry_pos_offset, rms_eps, _ptr(dya), _ptr(dx), _ptr(dg)), "kv_prepare_bwd")
+    return dx, dg
+
+
+def kv_compress_bwd(x, gate, m: int, dc, span: int = None):
+    """Gradient of kv_compress_ex: dc [B,T//m,D] -> (dx [B,T,D], dgate of the
+    gate's shape), fp64."""
+    lib = _load()
+    xa, xd = _act(x)
+    g = _np(gate, np.float32)
+    B, T, D = xa.shape
+    per_channel = g.ndim == 3
+    span = m if span is None else span
+    dca = np.ascontiguousarray(dc, dtype=np.float64)
+    assert dca.shape == (B, T // m, D)
+    dx = np.empty((B, T, D), dtype=np.float64)
+    dg = np.empty(g.shape, dtype=np.float64)
+    _check(lib.oracle_kv_compress_bwd(_ptr(xa), xd, _ptr(g), int(per_channel), B, T, D, m, span, _ptr(dca),
+                                      _ptr(dx), _ptr(dg)), "kv_compress_bwd")
+    return dx, dg
+
+
+def indexer_bwd(q_idx, w, q_pos, m: int, idx, dS, k_f32=None, k_code=None, k_scale=None, absolute=False):
+    """Gradient of the indexer score over the selected entries idx [B,Q,K]
+    given dS [B,Q,K] -> (dq_idx [B,Q,HI,dI], dw [B,Q,HI], dk [B,N,dI]), fp64;
+    ReLU decisions on the canonical fp32 score.  absolute=True sums |terms|."""
+    lib = _load()
+    qa, qd = _act(q_idx)
+    B, Q, HI, dI = qa.shape
+    wa = _np(w, np.float32)
+    qp = _np(q_pos, np.int32)
+    ia = _np(idx, np.int32)
+    K = ia.shape[-1]
+    dsa = _np(dS, np.float32)
+    if k_code is not None:
+        kc, ks, kf = _np(k_code, np.uint8), _np(k_scale, np.float32), None
+        N = kc.shape[1]
+    else:
+        kf, kc, ks = _np(k_f32, np.float32), None, None
+        N = kf.shape[1]
+    dq = np.empty((B, Q, HI, dI), dtype=np.float64)
+    dw = np.empty((B, Q, HI), dtype=np.float64)
+    dk = np.empty((B, N, dI), dtype=np.float64)
+    _check(lib.oracle_indexer_bwd(_ptr(qa), qd, _ptr(wa), _ptr(kf), _ptr(kc), _ptr(ks), _ptr(qp), _ptr(ia), B, Q, N,
+                                  HI, dI, m, K, _ptr(dsa), int(absolute), _ptr(dq), _ptr(dw), _ptr(dk)),
+           "indexer_bwd")
+    return dq, dw, dk
+
+
+def attention_bwd(q, kv_c, kv_raw, raw_pos0, q_pos, sinks, dout, *, idx=None, m: int, n_win: int, rope_dims: int,
+                  rope_base: float = 10000.0, entry_pos_offset: int = 0, softmax_scale: float = 0.0,
+                  rms_eps: float = 1e-6, gamma_q=None, gamma_kv=None):
+    """Gradient of attention() given dout [B,Q,H,D] (kv_c and kv_raw raw rows,
+    prepared inside as the forward does).  Returns a dict of fp64 arrays:
+    dq [B,Q,H,D] (raw query heads), dkhat_c [B,N,D] and dkhat_raw [B,R,D]
+    (the prepared rows the attention calls read), dsinks [H], dgamma_q [D]."""
+    lib = _load()
+    qa, qd = _act(q)
+    ka, kd = _act(kv_c)
+    ra, rd = _act(kv_raw)
+    if not (qd == kd == rd):
+        raise ValueError("q, kv_c and kv_raw must share one storage type")
+    B, Q, H, D = qa.shape
+    N, R = ka.shape[1], ra.shape[1]
+    ia, K = (None, 0) if idx is None else (_np(idx, np.int32), np.asarray(idx).shape[-1])
+    rp, qp, sk = _np(raw_pos0, np.int32), _np(q_pos, np.int32), _np(sinks, np.float32)
+    gq = None if gamma_q is None else _np(gamma_q, np.float32)
+    gk = None if gamma_kv is None else _np(gamma_kv, np.float32)
+    do = _np(dout, np.float32)
+    assert do.shape == (B, Q, H, D)
+    res = dict(dq=np.empty((B, Q, H, D)), dkhat_c=np.empty((B, N, D)), dkhat_raw=np.empty((B, R, D)),
+               dsinks=np.empty((H,)), dgamma_q=np.empty((D,)))
+    prm = AttnParams(m, n_win, rope_dims, entry_pos_offset, rope_base, softmax_scale, rms_eps)
+    _check(lib.oracle_attention_bwd(ctypes.byref(prm), _ptr(qa), _ptr(ka), _ptr(ia), K, _ptr(ra), _ptr(rp), _ptr(qp),
+                                    _ptr(sk), _ptr(gq), _ptr(gk), qd, B, Q, H, D, N, R, _ptr(do), _ptr(res["dq"]),
+                                    _ptr(res["dkhat_c"]), _ptr(res["dkhat_raw"]), _ptr(res["dsinks"]),
+                                    _ptr(res["dgamma_q"])), "attention_bwd")
+    return res

@@ -509,3 +509,295 @@ int oracle_attention(const oracle_attn_params* p, const void* q, const void* kv_
     }
     return bad ? OR_EINVAL : OR_OK;
 }
+
+/* ======================================================================== */
+/* Backward pass (training)  [V4-Pro card, section 5 "1M context,            */
+/* gradually": sparse attention is trained from 64K context on, after a      */
+/* short warm-up of the Lightning Indexer].  The gradients of the forward    */
+/* steps above, by the chain rule, in fp64.                                   */
+/* ======================================================================== */
+
+/* RMSNorm backward for y = gamma * x / r, r = sqrt(mean(x^2) + eps):
+ *   dx_e = gamma_e dy_e / r - x_e sum_d(gamma_d dy_d x_d) / (D r^3),
+ *   dgamma_d += dy_d x_d / r.  dgamma may be NULL. */
+static void rms_normalise_bwd(const double* x, const float* gamma, i64 D, double eps, const double* dy, double* dx,
+                              double* dgamma) {
+    double ss = 0.0, dot = 0.0;
+    for (i64 d = 0; d < D; ++d) ss += x[d] * x[d];
+    double r = sqrt(ss / (double)D + eps);
+    for (i64 d = 0; d < D; ++d) dot += (gamma ? (double)gamma[d] : 1.0) * dy[d] * x[d];
+    for (i64 d = 0; d < D; ++d) {
+        double g = gamma ? (double)gamma[d] : 1.0;
+        dx[d] = g * dy[d] / r - x[d] * dot / ((double)D * r * r * r);
+        if (dgamma) dgamma[d] += dy[d] * x[d] / r;
+    }
+}
+
+/* Gradient of kv_prepare: entries j0 .. j0+n-1 of each sequence; dy [B][n][D]
+ * is the gradient of the prepared rows, dx [B][n][D] receives the raw
+ * entries' gradient, dgamma [D] (or NULL) accumulates gamma_kv's.  The
+ * rotation's transpose is the rotation by -position. */
+int oracle_kv_prepare_bwd(const void* kv_c, int act_dtype, const float* gamma_kv, i64 B, i64 N, i64 D, i64 j0,
+                          i64 n, int m, int rope_dims, double rope_base, int entry_pos_offset, double rms_eps,
+                          const double* dy, double* dx, double* dgamma) {
+    if (B < 0 || N < 0 || D < 1 || j0 < 0 || n < 0 || j0 + n > N || m < 1 || rope_dims < 0 ||
+        (rope_dims & 1) || rope_dims > D)
+        return OR_EINVAL;
+    double* x = (double*)malloc(sizeof(double) * (size_t)D);
+    double* du = (double*)malloc(sizeof(double) * (size_t)D);
+    if (dgamma)
+        for (i64 d = 0; d < D; ++d) dgamma[d] = 0.0;
+    for (i64 b = 0; b < B; ++b)
+        for (i64 i = 0; i < n; ++i) {
+            i64 j = j0 + i;
+            for (i64 d = 0; d < D; ++d) {
+                x[d] = load_elem(kv_c, act_dtype, (b * N + j) * D + d);
+                du[d] = dy[(b * n + i) * D + d];
+            }
+            rope(du, D, rope_dims, rope_base, -(double)(j * m + entry_pos_offset));
+            rms_normalise_bwd(x, gamma_kv, D, rms_eps, du, dx + (b * n + i) * D, dgamma);
+        }
+    free(x);
+    free(du);
+    return OR_OK;
+}
+
+/* Gradient of the compression variants (and of the plain compressor, span =
+ * m, per-token gates): for each entry j with span S_j and channel d,
+ *   c_d = sum_i a_{i,d} x_{i,d},   a = softmax over S_j of the gate,
+ *   dx_{i,d} += a_{i,d} dc_d,       dg_{i,d} += a_{i,d} (x_{i,d} - c_d) dc_d
+ * (per-token gates sum dg over the channels).  dc is [B][T/m][D]; dx
+ * [B][T][D] and dg ([B][T] or [B][T][D]) are overwritten; tokens outside
+ * every entry's span get zero. */
+int oracle_kv_compress_bwd(const void* x, int x_dtype, const float* g, int gate_per_channel, i64 B, i64 T, i64 D,
+                           int m, int span, const double* dc, double* dx, double* dg) {
+    if (m < 1 || span < m || B < 0 || T < 0 || D < 1) return OR_EINVAL;
+    i64 nb = T / m;
+    memset(dx, 0, sizeof(double) * (size_t)(B * T * D));
+    memset(dg, 0, sizeof(double) * (size_t)(B * T * (gate_per_channel ? D : 1)));
+    double* c = (double*)malloc(sizeof(double) * (size_t)D);
+    double* a = (double*)malloc(sizeof(double) * (size_t)span * (size_t)D);
+    for (i64 b = 0; b < B; ++b)
+        for (i64 j = 0; j < nb; ++j) {
+            i64 hi = (j + 1) * m, lo = hi - span < 0 ? 0 : hi - span, n = hi - lo;
+            for (i64 d = 0; d < D; ++d) {
+                double mx = -INFINITY, z = 0.0;
+                for (i64 i = 0; i < n; ++i) {
+                    double gi = gate_per_channel ? (double)g[(b * T + lo + i) * D + d] : (double)g[b * T + lo + i];
+                    if (gi > mx) mx = gi;
+                }
+                for (i64 i = 0; i < n; ++i) {
+                    double gi = gate_per_channel ? (double)g[(b * T + lo + i) * D + d] : (double)g[b * T + lo + i];
+                    a[i * D + d] = exp(gi - mx);
+                    z += a[i * D + d];
+                }
+                c[d] = 0.0;
+                for (i64 i = 0; i < n; ++i) {
+                    a[i * D + d] /= z;
+                    c[d] += a[i * D + d] * load_elem(x, x_dtype, (b * T + lo + i) * D + d);
+                }
+            }
+            const double* dcj = dc + (b * nb + j) * D;
+            for (i64 i = 0; i < n; ++i)
+                for (i64 d = 0; d < D; ++d) {
+                    double xi = load_elem(x, x_dtype, (b * T + lo + i) * D + d);
+                    dx[(b * T + lo + i) * D + d] += a[i * D + d] * dcj[d];
+                    double gg = a[i * D + d] * (xi - c[d]) * dcj[d];
+                    if (gate_per_channel) dg[(b * T + lo + i) * D + d] += gg;
+                    else dg[b * T + lo + i] += gg;
+                }
+        }
+    free(c);
+    free(a);
+    return OR_OK;
+}
+
+/* Gradient of the indexer score S(j) = sum_h w_h ReLU(q_h . k_j) over the
+ * selected entries idx[b,i,:] (slots that are -1 or not visible carry
+ * nothing), given dS [B][Q][K]:
+ *   dq_h += dS_j w_h [s_h > 0] k_j,   dw_h += dS_j ReLU(s_h),
+ *   dk_j += dS_j sum_h w_h [s_h > 0] q_h.
+ * Each ReLU decision [s_h > 0] is taken on the forward's canonical fp32 dot
+ * product (head dim ascending from +0 in fmaf), so both sides decide on the
+ * same fp32 value; ReLU(s_h) itself and the sums are fp64.  absolute = 1 accumulates |term| instead (with
+ * the same decisions): the magnitude of each sum, for error bounds.
+ * dq [B][Q][HI][dI], dw [B][Q][HI] and dk [B][N][dI] are overwritten. */
+int oracle_indexer_bwd(const void* q_idx, int q_dtype, const float* w, const float* k_f32, const uint8_t* k_code,
+                       const float* k_scale, const int32_t* q_pos, const int32_t* idx, i64 B, i64 Q, i64 N, int HI,
+                       int dI, int m, int K, const float* dS, int absolute, double* dq, double* dw, double* dk) {
+    if (B < 0 || Q < 0 || N < 0 || HI < 1 || dI < 1 || m < 1 || K < 0) return OR_EINVAL;
+    memset(dq, 0, sizeof(double) * (size_t)(B * Q * HI * dI));
+    memset(dw, 0, sizeof(double) * (size_t)(B * Q * HI));
+    memset(dk, 0, sizeof(double) * (size_t)(B * N * dI));
+    float* kr = (float*)malloc(sizeof(float) * (size_t)dI);
+    for (i64 bq = 0; bq < B * Q; ++bq) {
+        i64 b = bq / Q;
+        if (q_pos[bq] < 0) continue;
+        i64 nv = n_visible(q_pos[bq], m, N);
+        for (int s = 0; s < K; ++s) {
+            i64 j = idx[bq * K + s];
+            if (j < 0 || j >= nv) continue;
+            key_row(k_f32, k_code, k_scale, b * N + j, dI, kr);
+            double g = (double)dS[bq * K + s];
+            for (int h = 0; h < HI; ++h) {
+                float sh = 0.0f;
+                double s64 = 0.0;
+                for (int d = 0; d < dI; ++d) {
+                    sh = fmaf(load_elem_f(q_idx, q_dtype, (bq * HI + h) * dI + d), kr[d], sh);
+                    s64 += load_elem(q_idx, q_dtype, (bq * HI + h) * dI + d) * (double)kr[d];
+                }
+                double wh = (double)w[bq * HI + h];
+                /* the decision on the forward's fp32 score, the value exact */
+                double relu = sh > 0.0f ? s64 : 0.0;
+                dw[bq * HI + h] += absolute ? fabs(g * relu) : g * relu;
+                if (!(sh > 0.0f)) continue;
+                for (int d = 0; d < dI; ++d) {
+                    double qd = load_elem(q_idx, q_dtype, (bq * HI + h) * dI + d);
+                    double t1 = g * wh * (double)kr[d], t2 = g * wh * qd;
+                    dq[(bq * HI + h) * dI + d] += absolute ? fabs(t1) : t1;
+                    dk[(b * N + j) * dI + d] += absolute ? fabs(t2) : t2;
+                }
+            }
+        }
+    }
+    free(kr);
+    return OR_OK;
+}
+
+/* Gradient of the core attention (oracle_attention) given dout [B][Q][H][D]
+ * (float32) for every query row:
+ *   dq      [B][Q][H][D]  gradient of the raw query heads,
+ *   dkhat_c [B][N][D]     gradient of the prepared compressed rows k_hat
+ *                         (what the attention calls read), summed over
+ *                         heads and queries,
+ *   dkhat_raw [B][R][D]   the same for the prepared window rows,
+ *   dsinks [H], dgamma_q [D] (either may be NULL).
+ * Per query and head, with do = RoPE_t(dout) (the transpose of the output's
+ * rotation by -t), o = sum_u p_u k_u and delta = do . o:
+ *   dl_u = p_u (do . k_u - delta),   dz = -p_sink delta,
+ *   dq_hat = tau sum_u dl_u k_u,     dk_u += tau dl_u q_hat + p_u do,
+ * then dq through RoPE_t's transpose and the RMSNorm of q.  A query with no
+ * keys and a -inf sink has zero gradients.  All outputs are overwritten. */
+int oracle_attention_bwd(const oracle_attn_params* p, const void* q, const void* kv_c, const int32_t* idx, int K,
+                         const void* kv_raw, const int32_t* raw_pos0, const int32_t* q_pos, const float* sinks,
+                         const float* gamma_q, const float* gamma_kv, int act_dtype, i64 B, i64 Q, i64 H, i64 D,
+                         i64 N, i64 R, const float* dout, double* dq, double* dkhat_c, double* dkhat_raw,
+                         double* dsinks, double* dgamma_q) {
+    if (p->m < 1 || p->n_win < 0 || p->rope_dims < 0 || (p->rope_dims & 1) || p->rope_dims > D) return OR_EINVAL;
+    double tau = p->softmax_scale > 0.0 ? p->softmax_scale : 1.0 / sqrt((double)D);
+    memset(dq, 0, sizeof(double) * (size_t)(B * Q * H * D));
+    memset(dkhat_c, 0, sizeof(double) * (size_t)(B * N * D));
+    memset(dkhat_raw, 0, sizeof(double) * (size_t)(B * R * D));
+    if (dsinks) memset(dsinks, 0, sizeof(double) * (size_t)H);
+    if (dgamma_q) memset(dgamma_q, 0, sizeof(double) * (size_t)D);
+    for (i64 bq = 0; bq < B * Q; ++bq) {
+        if (q_pos[bq] < 0) return OR_EINVAL;
+        i64 b = bq / Q, t = q_pos[bq];
+        i64 nv = n_visible(t, p->m, N);
+        i64 ncomp = idx ? K : nv;
+        i64 cap = ncomp + p->n_win;
+        double* keys = (double*)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1) * D);
+        double** dst = (double**)malloc(sizeof(double*) * (size_t)(cap > 0 ? cap : 1));
+        double* tmp = (double*)malloc(sizeof(double) * (size_t)D);
+        i64 nk = 0;
+        for (i64 i = 0; i < ncomp; ++i) {
+            i64 j = idx ? idx[bq * K + i] : i;
+            if (j < 0 || j >= nv) continue;
+            for (i64 d = 0; d < D; ++d) tmp[d] = load_elem(kv_c, act_dtype, (b * N + j) * D + d);
+            rms_normalise(tmp, gamma_kv, D, p->rms_eps, keys + nk * D);
+            rope(keys + nk * D, D, p->rope_dims, p->rope_base, (double)(j * p->m + p->entry_pos_offset));
+            dst[nk++] = dkhat_c + (b * N + j) * D;
+        }
+        i64 p_lo = t - p->n_win + 1;
+        if (p_lo < 0) p_lo = 0;
+        for (i64 pos = p_lo; pos <= t && p->n_win > 0; ++pos) {
+            i64 row = pos - raw_pos0[b];
+            if (row < 0 || row >= R) continue;
+            for (i64 d = 0; d < D; ++d) tmp[d] = load_elem(kv_raw, act_dtype, (b * R + row) * D + d);
+            rms_normalise(tmp, gamma_kv, D, p->rms_eps, keys + nk * D);
+            rope(keys + nk * D, D, p->rope_dims, p->rope_base, (double)pos);
+            dst[nk++] = dkhat_raw + (b * R + row) * D;
+        }
+        /* per head: probabilities and logit gradients, then the key rows'
+         * gradients summed over heads (rows of one query are distinct) */
+        double* P = (double*)malloc(sizeof(double) * (size_t)(H * (nk > 0 ? nk : 1)));
+        double* DL = (double*)malloc(sizeof(double) * (size_t)(H * (nk > 0 ? nk : 1)));
+        double* QH = (double*)malloc(sizeof(double) * (size_t)(H * D));
+        double* DO = (double*)malloc(sizeof(double) * (size_t)(H * D));
+        int* live = (int*)malloc(sizeof(int) * (size_t)H);
+#pragma omp parallel for schedule(static)
+        for (i64 h = 0; h < H; ++h) {
+            double* x = (double*)malloc(sizeof(double) * (size_t)D);
+            double* u = (double*)malloc(sizeof(double) * (size_t)D);
+            double* o = (double*)malloc(sizeof(double) * (size_t)D);
+            double* qh = QH + h * D;
+            double* doh = DO + h * D;
+            for (i64 d = 0; d < D; ++d) x[d] = load_elem(q, act_dtype, (bq * H + h) * D + d);
+            rms_normalise(x, gamma_q, D, p->rms_eps, qh);
+            rope(qh, D, p->rope_dims, p->rope_base, (double)t);
+            double mx = (double)sinks[h];
+            for (i64 uu = 0; uu < nk; ++uu) {
+                double s = 0.0;
+                for (i64 d = 0; d < D; ++d) s += qh[d] * keys[uu * D + d];
+                P[h * nk + uu] = tau * s;
+                if (P[h * nk + uu] > mx) mx = P[h * nk + uu];
+            }
+            live[h] = mx != -INFINITY;
+            if (!live[h]) {
+                for (i64 uu = 0; uu < nk; ++uu) P[h * nk + uu] = DL[h * nk + uu] = 0.0;
+                for (i64 d = 0; d < D; ++d) doh[d] = 0.0;
+                free(x); free(u); free(o);
+                continue;
+            }
+            double z = exp((double)sinks[h] - mx);
+            for (i64 uu = 0; uu < nk; ++uu) {
+                P[h * nk + uu] = exp(P[h * nk + uu] - mx);
+                z += P[h * nk + uu];
+            }
+            for (i64 d = 0; d < D; ++d) o[d] = 0.0;
+            for (i64 uu = 0; uu < nk; ++uu) {
+                P[h * nk + uu] /= z;
+                for (i64 d = 0; d < D; ++d) o[d] += P[h * nk + uu] * keys[uu * D + d];
+            }
+            double psink = exp((double)sinks[h] - mx) / z;
+            for (i64 d = 0; d < D; ++d) doh[d] = (double)dout[(bq * H + h) * D + d];
+            rope(doh, D, p->rope_dims, p->rope_base, (double)t);
+            double delta = 0.0;
+            for (i64 d = 0; d < D; ++d) delta += doh[d] * o[d];
+            for (i64 d = 0; d < D; ++d) u[d] = 0.0;  /* dq_hat */
+            for (i64 uu = 0; uu < nk; ++uu) {
+                double dp = 0.0;
+                for (i64 d = 0; d < D; ++d) dp += doh[d] * keys[uu * D + d];
+                double dl = P[h * nk + uu] * (dp - delta);
+                DL[h * nk + uu] = dl;
+                for (i64 d = 0; d < D; ++d) u[d] += tau * dl * keys[uu * D + d];
+            }
+            if (dsinks) {
+#pragma omp atomic
+                dsinks[h] += -psink * delta;
+            }
+            /* back through the rotation by t and the RMSNorm of q */
+            rope(u, D, p->rope_dims, p->rope_base, -(double)t);
+            double* dgq = dgamma_q ? (double*)calloc((size_t)D, sizeof(double)) : NULL;
+            rms_normalise_bwd(x, gamma_q, D, p->rms_eps, u, dq + (bq * H + h) * D, dgq);
+            if (dgq) {
+                for (i64 d = 0; d < D; ++d) {
+#pragma omp atomic
+                    dgamma_q[d] += dgq[d];
+                }
+                free(dgq);
+            }
+            free(x); free(u); free(o);
+        }
+#pragma omp parallel for schedule(static)
+        for (i64 uu = 0; uu < nk; ++uu)
+            for (i64 h = 0; h < H; ++h) {
+                if (!live[h]) continue;
+                for (i64 d = 0; d < D; ++d)
+                    dst[uu][d] += tau * DL[h * nk + uu] * QH[h * D + d] + P[h * nk + uu] * DO[h * D + d];
+            }
+        free(P); free(DL); free(QH); free(DO); free(live);
+        free(keys); free(dst); free(tmp);
+    }
+    return OR_OK;
+}
