@@ -53,7 +53,9 @@ _i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_
 EXPORTS = ("cakv_version", "cakv_last_error", "cakv_kv_compress", "cakv_kv_prepare", "cakv_indexer_topk_workspace",
            "cakv_indexer_topk", "cakv_sparse_mqa_workspace", "cakv_sparse_mqa_fwd",
            "cakv_dense_mqa_workspace", "cakv_dense_compressed_mqa_fwd", "cakv_profile_kernel_events",
-           "cakv_indexer_topk_noalloc", "cakv_kv_compress_ex", "cakv_kv_append")
+           "cakv_indexer_topk_noalloc", "cakv_kv_compress_ex", "cakv_kv_append", "cakv_mqa_bwd_workspace",
+           "cakv_mqa_bwd", "cakv_kv_prepare_bwd", "cakv_kv_compress_bwd_workspace", "cakv_kv_compress_bwd",
+           "cakv_indexer_bwd")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -72,6 +74,19 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                         ctypes.c_int, _p, _p]
     lib.cakv_kv_append.argtypes = [_p, _p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _p, _p, _i64, _p, _i64, _p,
                                    ctypes.c_int, _p, _i64, _i32, _i32, ctypes.POINTER(PrepParams), _p]
+    lib.cakv_mqa_bwd_workspace.argtypes = [_i64, _i64, _i32, _i32, _i64, _i32]
+    lib.cakv_mqa_bwd_workspace.restype = _sz
+    lib.cakv_mqa_bwd.argtypes = [ctypes.POINTER(AttnParams), _p, _p, _p, _p, _p, _p, _p, ctypes.c_int, _i64, _i64,
+                                 _i32, _i32, _i64, _i32, _i64, _p, ctypes.c_int, _p, _p, _p, _p, _p, _p, _p, _p, _sz,
+                                 _p]
+    lib.cakv_kv_prepare_bwd.argtypes = [_p, ctypes.c_int, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _i32, _i32,
+                                        ctypes.c_float, _i32, ctypes.c_float, _p]
+    lib.cakv_kv_compress_bwd_workspace.argtypes = [_i64, _i64, _i64, _i32]
+    lib.cakv_kv_compress_bwd_workspace.restype = _sz
+    lib.cakv_kv_compress_bwd.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p, _p,
+                                         _p, _p, _sz, _p]
+    lib.cakv_indexer_bwd.argtypes = [_p, ctypes.c_int, _p, _p, ctypes.c_int, _p, _p, _p, _p, _i64, _i64, _i64, _i32,
+                                     _i32, _i32, _i32, _p, _p, _p, _p]
     lib.cakv_kv_prepare.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _p, _i32, _i32,
                                     ctypes.c_float, _i32, ctypes.c_float, _p]
     lib.cakv_indexer_topk_workspace.argtypes = [_i64, _i64, _i64, _i32]
@@ -365,3 +380,90 @@ def profile_kernel_events(kernel: str | None, starts=(), ends=()) -> None:
     arr = (_p * n)
     _check(lib.cakv_profile_kernel_events(kernel.encode(), arr(*[e.cuda_event for e in starts]),
                                           arr(*[e.cuda_event for e in ends]), n))
+
+
+# ---------------------------------------------------------------- backward (training)
+
+def mqa_bwd(q, kv_c, idx, kv_raw, raw_pos0, q_pos, sinks, out, lse, dout, *, m: int, n_win: int, rope_dims: int,
+            rope_base: float = 10000.0, softmax_scale: float = 0.0, rms_eps: float = 1e-6, gamma_q=None,
+            raw_ring: bool = False, dkv_c=None, dkv_raw=None, dsinks=None, dgamma_q=None, workspace=None):
+    """Gradient of sparse_mqa_fwd (idx given) or dense_compressed_mqa_fwd (idx
+    None) from the forward's inputs, out, lse and dout [B,Q,H,D] float32.
+    Returns dict(dq, dkv_c, dkv_raw, dsinks, dgamma_q): dq is new; the others
+    are accumulated into the given float32 tensors (zero-filled new ones by
+    default; dgamma_q only when gamma_q is given).  dkv_c / dkv_raw are the
+    gradients of the prepared rows (kv_prepare_bwd continues to raw rows)."""
+    lib = load_library()
+    B, Q, H, D = q.shape
+    N, R = kv_c.shape[1], kv_raw.shape[1]
+    K = idx.shape[-1] if idx is not None else 0
+    _same_act(q, kv_c, kv_raw)
+    dev = q.device
+    dq = torch.empty((B, Q, H, D), dtype=torch.float32, device=dev)
+    dkv_c = torch.zeros((B, N, D), dtype=torch.float32, device=dev) if dkv_c is None else dkv_c
+    dkv_raw = torch.zeros((B, R, D), dtype=torch.float32, device=dev) if dkv_raw is None else dkv_raw
+    dsinks = torch.zeros((H,), dtype=torch.float32, device=dev) if dsinks is None else dsinks
+    if gamma_q is not None and dgamma_q is None:
+        dgamma_q = torch.zeros((D,), dtype=torch.float32, device=dev)
+    n_keys = K if idx is not None else N
+    need = int(lib.cakv_mqa_bwd_workspace(B, Q, H, D, n_keys, n_win))
+    if workspace is None or workspace.numel() < need:
+        workspace = _workspace(need, dev)
+    prm = _params(m, n_win, rope_dims, rope_base, softmax_scale, rms_eps, gamma_q, raw_ring)
+    _check(lib.cakv_mqa_bwd(ctypes.byref(prm), _dev(q, "q"), _dev(kv_c, "kv_c"), _dev(idx, "idx", _I32),
+                            _dev(kv_raw, "kv_raw"), _dev(raw_pos0, "raw_pos0", _I32), _dev(q_pos, "q_pos", _I32),
+                            _dev(sinks, "sinks", _F32), _DT[q.dtype], B, Q, H, D, N, K, R, _dev(out, "out"),
+                            _DT[out.dtype], _dev(lse, "lse", _F32), _dev(dout, "dout", _F32), _dev(dq, "dq", _F32),
+                            _dev(dkv_c, "dkv_c", _F32), _dev(dkv_raw, "dkv_raw", _F32), _dev(dsinks, "dsinks", _F32),
+                            _dev(dgamma_q, "dgamma_q", _F32), workspace.data_ptr(), workspace.numel(), _stream()))
+    return dict(dq=dq, dkv_c=dkv_c, dkv_raw=dkv_raw, dsinks=dsinks, dgamma_q=dgamma_q)
+
+
+def kv_prepare_bwd(kv_in, dy, *, m: int, rope_dims: int, rope_base: float = 10000.0, entry_pos_offset: int = 0,
+                   rms_eps: float = 1e-6, gamma_kv=None, j0: int = 0, n: int = None, dx=None, dgamma_kv=None):
+    """Gradient of kv_prepare: dy [B,N,D] float32 of the prepared rows ->
+    dx [B,N,D] float32 of the raw entries (rows j0 .. j0+n-1; a new zero
+    tensor by default) and dgamma_kv (accumulated when given).  Returns dx."""
+    lib = load_library()
+    B, N, D = kv_in.shape
+    n = N - j0 if n is None else n
+    dx = torch.zeros((B, N, D), dtype=torch.float32, device=kv_in.device) if dx is None else dx
+    _check(lib.cakv_kv_prepare_bwd(_dev(kv_in, "kv_in"), _DT[kv_in.dtype], _dev(dy, "dy", _F32), _dev(dx, "dx", _F32),
+                                   _dev(dgamma_kv, "dgamma_kv", _F32), B, N, D, j0, n,
+                                   _dev(gamma_kv, "gamma_kv", _F32), m, rope_dims, rope_base, entry_pos_offset,
+                                   rms_eps, _stream()))
+    return dx
+
+
+def kv_compress_bwd(x, gate, m: int, dc, span: int = None):
+    """Gradient of kv_compress_ex: dc [B,T//m,D] float32 -> (dx [B,T,D],
+    dgate of gate's shape), float32."""
+    lib = load_library()
+    B, T, D = x.shape
+    span = m if span is None else span
+    per_channel = gate.dim() == 3
+    dx = torch.empty((B, T, D), dtype=torch.float32, device=x.device)
+    dg = torch.empty(gate.shape, dtype=torch.float32, device=x.device)
+    need = int(lib.cakv_kv_compress_bwd_workspace(B, T, D, m))
+    ws = _workspace(need, x.device)
+    _check(lib.cakv_kv_compress_bwd(_dev(x, "x"), _DT[x.dtype], _dev(gate, "gate", _F32), int(per_channel), B, T, D,
+                                    m, span, _dev(dc, "dc", _F32), _dev(dx, "dx", _F32), _dev(dg, "dgate", _F32),
+                                    ws.data_ptr(), ws.numel(), _stream()))
+    return dx, dg
+
+
+def indexer_bwd(q_idx, w, k_idx, k_scale, q_pos, idx, dS, m: int, dk=None):
+    """Gradient of the indexer score over the selected entries idx [B,Q,K]
+    given dS [B,Q,K] float32 -> (dq_idx [B,Q,HI,dI], dw [B,Q,HI], dk
+    [B,N,dI] accumulated; new zero tensor by default), float32."""
+    lib = load_library()
+    B, Q, HI, dI = q_idx.shape
+    N, K = k_idx.shape[1], idx.shape[-1]
+    dq = torch.empty((B, Q, HI, dI), dtype=torch.float32, device=q_idx.device)
+    dw = torch.empty((B, Q, HI), dtype=torch.float32, device=q_idx.device)
+    dk = torch.zeros((B, N, dI), dtype=torch.float32, device=q_idx.device) if dk is None else dk
+    _check(lib.cakv_indexer_bwd(_dev(q_idx, "q_idx"), _DT[q_idx.dtype], _dev(w, "w", _F32), _dev(k_idx, "k_idx"),
+                                _DT[k_idx.dtype], _dev(k_scale, "k_scale", _F32), _dev(q_pos, "q_pos", _I32),
+                                _dev(idx, "idx", _I32), _dev(dS, "dS", _F32), B, Q, N, HI, dI, m, K,
+                                _dev(dq, "dq_idx", _F32), _dev(dw, "dw", _F32), _dev(dk, "dk", _F32), _stream()))
+    return dq, dw, dk

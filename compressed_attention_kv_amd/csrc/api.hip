@@ -180,6 +180,20 @@ int indexer_args(const void* q_idx, int q_dtype, const float* w, const void* k_i
                  int32_t dI, int32_t m, int32_t k, int32_t* idx, cakv::IndexerArgs& a, bool& fp8_mode,
                  bool& empty);
 
+// workspace of an attention backward launch over BQ queries, and what the
+// query reports (the largest over every batch of 1 .. BQ queries)
+size_t bwd_workspace(int64_t BQ, int32_t H, int64_t max_slots) {
+    return cakv::mqa_bwd_workspace_bytes(BQ, H, max_slots, attn_splits(BQ, max_slots));
+}
+size_t bwd_workspace_query(int64_t BQ, int32_t H, int64_t max_slots) {
+    size_t best = bwd_workspace(BQ, H, max_slots);
+    for (int64_t b = 1; b <= BQ && b <= 256; ++b) {
+        const size_t w = bwd_workspace(b, H, max_slots);
+        if (w > best) best = w;
+    }
+    return best;
+}
+
 // The allocation-free indexer call keeps its workspace here: one copy of the
 // array per GPU, held until the process ends.  Host code never uses the
 // array's name as an address (on the host it is only a stand-in for the
@@ -480,6 +494,161 @@ int indexer_args(const void* q_idx, int q_dtype, const float* w, const void* k_i
 }  // namespace
 
 extern "C" {
+
+size_t cakv_mqa_bwd_workspace(int64_t B, int64_t Q, int32_t H, int32_t D, int64_t n_keys, int32_t n_win) {
+    if (B < 0 || Q < 0 || H < 1 || D < 1 || n_keys < 0 || n_win < 0) return 0;
+    return bwd_workspace_query(B * Q, H, n_keys + n_win);
+}
+
+int cakv_mqa_bwd(const cakv_attn_params* p, const void* q, const void* kv_c, const int32_t* idx, const void* kv_raw,
+                 const int32_t* raw_pos0, const int32_t* q_pos, const float* sinks, int act_dtype, int64_t B, int64_t Q,
+                 int32_t H, int32_t D, int64_t N, int32_t K, int64_t R, const void* out, int out_dtype,
+                 const float* lse, const float* dout, float* dq, float* dkv_c, float* dkv_raw, float* dsinks,
+                 float* dgamma_q, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_attn_common(p, q, kv_c, kv_raw, raw_pos0, q_pos, sinks, act_dtype, B, Q, H, D, N, R,
+                               const_cast<void*>(out), out_dtype, const_cast<float*>(lse));
+    if (rc) return rc;
+    REQUIRE(D == 512 && act_dtype == CAKV_BF16, CAKV_EUNSUPPORTED,
+            "backward: bf16 activations with D = 512 (D=%d)", D);
+    if (idx) REQUIRE(K >= 0 && K <= 65536, CAKV_EUNSUPPORTED, "K=%d out of 0..65536", K);
+    REQUIRE(N <= 0x7fffffffLL, CAKV_EUNSUPPORTED, "N too large");
+    if (B * Q == 0) return ok();
+    REQUIRE_PTR(out, "out");
+    REQUIRE_PTR(lse, "lse");
+    REQUIRE_PTR(dout, "dout");
+    REQUIRE_PTR(dq, "dq");
+    if (N > 0) REQUIRE_PTR(dkv_c, "dkv_c");
+    if (R > 0) REQUIRE_PTR(dkv_raw, "dkv_raw");
+    if (dsinks) REQUIRE(aligned16(dsinks), CAKV_EINVAL, "dsinks must be 16-byte aligned");
+    if (dgamma_q) REQUIRE(aligned16(dgamma_q), CAKV_EINVAL, "dgamma_q must be 16-byte aligned");
+    const int64_t BQ = B * Q;
+    REQUIRE(BQ <= 65535, CAKV_EUNSUPPORTED, "backward: B*Q=%lld above 65535", (long long)BQ);
+    const int64_t max_slots = (idx ? (int64_t)K : N) + p->n_win;
+    const size_t need = bwd_workspace(BQ, H, max_slots);
+    REQUIRE(workspace_bytes >= need, CAKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    REQUIRE(workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, CAKV_EWORKSPACE,
+            "workspace must be non-NULL and 256-byte aligned");
+    cakv::BwdArgs w{};
+    fill_attn(w.f, p, q, kv_c, idx, kv_raw, raw_pos0, q_pos, sinks, Q, H, D, N, idx ? K : 0, R,
+              const_cast<void*>(out), out_dtype, const_cast<float*>(lse));
+    w.f.n_splits = attn_splits(BQ, max_slots);
+    w.out = out;
+    w.out_f32 = out_dtype == CAKV_F32;
+    w.lse = lse;
+    w.dout = dout;
+    w.dq = dq;
+    w.dkv_c = dkv_c;
+    w.dkv_raw = dkv_raw;
+    w.dsinks = dsinks;
+    w.dgamma_q = dgamma_q;
+    w.tau = p->softmax_scale > 0.0f ? p->softmax_scale : (float)(1.0 / sqrt((double)D));
+    return rc_from(cakv::launch_mqa_bwd(w, BQ, max_slots, workspace, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cakv_kv_prepare_bwd(const void* kv_in, int act_dtype, const float* dy, float* dx, float* dgamma_kv, int64_t B,
+                        int64_t N, int64_t D, int64_t j0, int64_t n, const float* gamma_kv, int32_t m,
+                        int32_t rope_dims, float rope_base, int32_t entry_pos_offset, float rms_eps, void* stream) {
+    REQUIRE(B >= 0 && N >= 0 && j0 >= 0 && n >= 0 && j0 + n <= N, CAKV_EINVAL,
+            "entries [%lld, %lld) outside 0..N=%lld (B=%lld)", (long long)j0, (long long)(j0 + n), (long long)N,
+            (long long)B);
+    REQUIRE(act_dtype == CAKV_F32 || act_dtype == CAKV_BF16, CAKV_EINVAL, "act_dtype must be F32 or BF16");
+    REQUIRE(D >= 8 && D <= 4096 && D % 8 == 0, CAKV_EUNSUPPORTED, "D=%lld: 8..4096, a multiple of 8", (long long)D);
+    REQUIRE(m >= 1, CAKV_EINVAL, "m=%d must be >= 1", m);
+    REQUIRE(rope_dims >= 0 && (rope_dims & 1) == 0 && rope_dims <= D, CAKV_EINVAL, "rope_dims=%d: even, 0..D",
+            rope_dims);
+    REQUIRE(rope_base > 0.0f && isfinite(rope_base), CAKV_EINVAL, "rope_base must be positive");
+    REQUIRE(rms_eps >= 0.0f && isfinite(rms_eps), CAKV_EINVAL, "rms_eps must be >= 0");
+    REQUIRE((N - 1) * (int64_t)m + entry_pos_offset <= 0x7fffffffLL && entry_pos_offset >= -0x7fffffffLL,
+            CAKV_EINVAL, "entry positions must fit in int32");
+    if (B * n == 0) return ok();
+    REQUIRE_PTR(kv_in, "kv_in");
+    REQUIRE_PTR(dy, "dy");
+    REQUIRE_PTR(dx, "dx");
+    if (gamma_kv) REQUIRE(aligned16(gamma_kv), CAKV_EINVAL, "gamma_kv must be 16-byte aligned");
+    if (dgamma_kv) REQUIRE(aligned16(dgamma_kv), CAKV_EINVAL, "dgamma_kv must be 16-byte aligned");
+    return rc_from(cakv::launch_kv_prepare_bwd(kv_in, dy, dx, dgamma_kv, act_dtype == CAKV_F32 ? 0 : 1, B, N, D, j0,
+                                               n, gamma_kv, m, rope_dims, cakv::rope_ratio_of(rope_base, rope_dims),
+                                               entry_pos_offset, rms_eps, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t cakv_kv_compress_bwd_workspace(int64_t B, int64_t T, int64_t D, int32_t m) {
+    if (B < 0 || T < 0 || D < 1 || m < 1) return 0;
+    return cakv::kv_compress_bwd_workspace_bytes(B, T, D, m);
+}
+
+int cakv_kv_compress_bwd(const void* x, int x_dtype, const float* gate, int gate_per_channel, int64_t B, int64_t T,
+                         int64_t D, int32_t m, int32_t span, const float* dc, float* dx, float* dgate, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    REQUIRE(B >= 0 && T >= 0, CAKV_EINVAL, "negative size (B=%lld T=%lld)", (long long)B, (long long)T);
+    REQUIRE(m >= 1 && m <= 4096, CAKV_EUNSUPPORTED, "m=%d out of 1..4096", m);
+    REQUIRE(span >= m && span <= 8192, CAKV_EUNSUPPORTED, "span=%d: m <= span <= 8192 (m=%d)", span, m);
+    REQUIRE(gate_per_channel == 0 || gate_per_channel == 1, CAKV_EINVAL, "gate_per_channel must be 0 or 1");
+    REQUIRE(D >= 4 && D <= 4096 && D % 4 == 0, CAKV_EUNSUPPORTED, "D=%lld: 4..4096, a multiple of 4", (long long)D);
+    REQUIRE(x_dtype == CAKV_F32 || x_dtype == CAKV_BF16, CAKV_EINVAL, "x_dtype must be F32 or BF16");
+    if (B * T == 0) return ok();
+    REQUIRE_PTR(x, "x");
+    REQUIRE_PTR(gate, "gate");
+    REQUIRE_PTR(dx, "dx");
+    REQUIRE_PTR(dgate, "dgate");
+    if (T / m > 0) REQUIRE_PTR(dc, "dc");
+    const size_t need = cakv::kv_compress_bwd_workspace_bytes(B, T, D, m);
+    REQUIRE(workspace_bytes >= need, CAKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if (need) REQUIRE(workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, CAKV_EWORKSPACE,
+                      "workspace must be non-NULL and 256-byte aligned");
+    return rc_from(cakv::launch_kv_compress_bwd(x, x_dtype, gate, gate_per_channel != 0, B, T, D, m, span, dc, dx,
+                                                dgate, workspace, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cakv_indexer_bwd(const void* q_idx, int q_dtype, const float* w, const void* k_idx, int k_dtype,
+                     const float* k_scale, const int32_t* q_pos, const int32_t* idx, const float* dS, int64_t B,
+                     int64_t Q, int64_t N, int32_t HI, int32_t dI, int32_t m, int32_t K, float* dq_idx, float* dw,
+                     float* dk, void* stream) {
+    REQUIRE(B >= 0 && Q >= 0 && N >= 0, CAKV_EINVAL, "negative size");
+    REQUIRE(m >= 1, CAKV_EINVAL, "m=%d must be >= 1", m);
+    REQUIRE(K >= 0 && K <= 65536, CAKV_EUNSUPPORTED, "K=%d out of 0..65536", K);
+    REQUIRE(N <= 0x7fffffffLL, CAKV_EUNSUPPORTED, "N too large");
+    const bool f32 = q_dtype == CAKV_F32 && k_dtype == CAKV_F32;
+    const bool fp8 = q_dtype == CAKV_BF16 && k_dtype == CAKV_FP8_E4M3;
+    REQUIRE(f32 || fp8, CAKV_EUNSUPPORTED, "dtypes: (F32 q, F32 k) or (BF16 q, FP8_E4M3 k)");
+    REQUIRE(HI >= 1 && HI <= 64 && dI >= 4 && dI <= 256 && dI % 4 == 0 && HI * dI <= 8192, CAKV_EUNSUPPORTED,
+            "HI <= 64, dI a multiple of 4 up to 256, HI*dI <= 8192 (HI=%d dI=%d)", HI, dI);
+    REQUIRE(fp8 == (k_scale != nullptr), CAKV_EINVAL, "k_scale is required for FP8_E4M3 keys and NULL otherwise");
+    const int64_t BQ = B * Q;
+    if (BQ == 0) return ok();
+    REQUIRE(BQ <= 0x7fffffffLL, CAKV_EUNSUPPORTED, "B*Q too large");
+    REQUIRE_PTR(q_idx, "q_idx");
+    REQUIRE_PTR(w, "w");
+    REQUIRE_PTR(q_pos, "q_pos");
+    REQUIRE_PTR(dq_idx, "dq_idx");
+    REQUIRE_PTR(dw, "dw");
+    if (K > 0) {
+        REQUIRE_PTR(idx, "idx");
+        REQUIRE_PTR(dS, "dS");
+    }
+    if (N > 0) {
+        REQUIRE_PTR(k_idx, "k_idx");
+        REQUIRE_PTR(dk, "dk");
+        if (fp8) REQUIRE_PTR(k_scale, "k_scale");
+    }
+    cakv::IndexerBwdArgs a{};
+    a.q_idx = q_idx;
+    a.w = w;
+    a.k_idx = k_idx;
+    a.k_scale = k_scale;
+    a.q_pos = q_pos;
+    a.idx = idx;
+    a.dS = dS;
+    a.dq = dq_idx;
+    a.dw = dw;
+    a.dk = dk;
+    a.Q = Q;
+    a.N = N;
+    a.HI = HI;
+    a.dI = dI;
+    a.m = m;
+    a.K = K;
+    return rc_from(cakv::launch_indexer_bwd(a, BQ, f32, fp8, reinterpret_cast<hipStream_t>(stream)));
+}
 
 size_t cakv_sparse_mqa_workspace(int64_t B, int64_t Q, int32_t H, int32_t D, int32_t K, int32_t n_win) {
     if (B < 0 || Q < 0 || H < 1 || D < 1 || K < 0 || n_win < 0) return 0;

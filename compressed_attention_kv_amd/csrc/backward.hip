@@ -1,0 +1,839 @@
+// backward.hip -- gradients of the hot path for training, on gfx950.
+//
+// [V4-Pro card, section 5 "1M context, gradually"] sparse attention is
+// trained from 64K context on, after a short warm-up of the Lightning
+// Indexer.  This file computes the gradients of the forward steps:
+//
+//   * core attention (sparse or dense, window, sink), per query and head,
+//     with do = RoPE_t(dout) (the transpose of the output's rotation by -t),
+//     P = exp(l - lse) from the forward's lse, delta = do . o:
+//         dl = P (do . k - delta),  dsink = -P_sink delta,
+//         dq_hat = tau dl K,        dK += tau dl^T Q_hat + P^T dO,
+//     then dq through RoPE_t's transpose and q's RMSNorm.  Five launches:
+//       prep    (one wave per query and head): q_hat and do (bf16, rows and
+//               transposed), delta, the sink gradient;
+//       logits  (one workgroup per query and key split, 4 waves of 32
+//               heads): S^T = K Q_hat^T and dP^T = K dO^T on
+//               v_mfma_f32_32x32x16_bf16 (one K read feeds both), then P
+//               and dl, stored bf16 key-major and head-major;
+//       dkeys   (same grid, 8 waves of 64 output dims): dK = [tau dl^T |
+//               P^T] [Q_hat ; dO] on MFMA, the [Q_hat ; dO] operand held in
+//               VGPRs for the split, added into the key rows' gradient with
+//               float atomics (rows can be shared by queries);
+//       dquery  (same grid): dq_hat = dl K as the forward's P V product
+//               (dl in the A-operand layout, K read transposed from LDS);
+//       finish  (one wave per query and head): the splits' sum, the
+//               rotation's transpose and the RMSNorm gradient.
+//   * kv_prepare: one wave per row (rotation by -position, RMSNorm).
+//   * the compressor (spans, per-channel gates): entry statistics, then one
+//     workgroup per token summing over the entries whose span holds it.
+//   * the indexer score over the selected entries: one workgroup per query;
+//     the ReLU decisions use the forward's canonical fp32 dot product.
+//
+// Key rows are staged in LDS exactly as the forward stages them (1 KiB
+// rows padded to 1,088 bytes, 16-byte granule g of row r at g ^ ((r >> 2) & 3)),
+// so the same operand reads apply; tiles are double-buffered.
+#include "cakv_attn_common.hpp"
+#include "cakv_rows.hpp"
+
+namespace cakv {
+
+namespace {
+
+constexpr int kBD = 512;            // head dim of the attention backward
+constexpr int kRS = 1088;           // LDS row stride of a key tile
+constexpr int kBuf = TK * kRS;      // one tile
+constexpr int kKS = kBD / 16;       // QK k-steps
+constexpr int kDT = kBD / 32;       // output dim tiles
+
+typedef __fp16 f16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) f16x4_t lds_f16x4_t;
+
+__device__ __forceinline__ int gperm(int row) { return (row >> 2) & 3; }
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint16_t bf16_of(float f) { return (uint16_t)f32_to_bf16_bits(f); }
+
+// gradient row of key slot `slot` (mirrors slot_row): dkv_c row of a
+// visible compressed entry, dkv_raw row of a window position, or nullptr
+__device__ __forceinline__ float* slot_grad_row(const AttnArgs& a, const QueryGeom& g, int slot, int32_t j,
+                                                float* dkv_c, float* dkv_raw) {
+    if (slot < g.n_c) {
+        if (j < 0 || j >= g.n_vis) return nullptr;
+        return dkv_c + (g.b * a.N + j) * (int64_t)kBD;
+    }
+    const int s = slot - g.n_c;
+    if (s >= g.n_w) return nullptr;
+    const int32_t p = g.p_lo + s;
+    int64_t row = (int64_t)p - g.raw0;
+    if (a.raw_ring && row < 0) row += a.R;
+    if (row < 0 || row >= a.R) return nullptr;
+    return dkv_raw + (g.b * a.R + row) * (int64_t)kBD;
+}
+
+// The tile's 32 key rows into LDS buffer `dst` (wave w copies rows 8w .. 8w+7,
+// one 1 KiB row per instruction; an empty slot copies `spare` so that every
+// wave always has 8 copies in flight), and the tile's validity mask.
+template <bool SPARSE>
+__device__ __forceinline__ uint32_t load_tile(const AttnArgs& a, const QueryGeom& g, int64_t bq, int tile,
+                                              uint8_t* dst, const uint8_t* spare, int wave, int lane) {
+    const int slot = tile * TK + (lane & 31);
+    const bf16_t* row = nullptr;
+    if (lane < TK && slot < g.n_c + g.n_w) row = slot_row<bf16_t>(a, g, slot, slot_entry<SPARSE>(a, g, bq, slot), kBD);
+    const uint32_t mask = (uint32_t)__ballot(row != nullptr);
+    const uint64_t rp = reinterpret_cast<uint64_t>(row);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int r = 8 * wave + k;
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(rp >> 32), r);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)rp, r);
+        const uint64_t p = ((uint64_t)hi << 32) | lo;
+        const uint8_t* src = p ? reinterpret_cast<const uint8_t*>(p) : spare;
+        lds_dma16(src + 16 * (lane ^ gperm(r)), (uint32_t)(uintptr_t)(dst + r * kRS));
+    }
+    return mask;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- prep
+// One wave per (query, head); lane l owns channels 8l .. 8l+7.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs w) {
+    const AttnArgs& a = w.f;
+    const int lane = threadIdx.x & 63;
+    const int64_t bq = blockIdx.x;
+    const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+    if (h >= w.HP) return;  // wave-uniform
+    const int H = a.H;
+    uint16_t* qt = w.qt + bq * (int64_t)kBD * w.HP;
+    uint16_t* dt = w.dot + bq * (int64_t)kBD * w.HP;
+    if (h >= H) {  // padding heads: zero columns of the transposed operands
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            qt[(8 * lane + i) * (int64_t)w.HP + h] = 0;
+            dt[(8 * lane + i) * (int64_t)w.HP + h] = 0;
+        }
+        return;
+    }
+    int32_t t = a.q_pos[bq];
+    t = t < 0 ? 0 : t;
+    const int64_t row = (bq * H + h) * (int64_t)kBD + 8 * lane;
+    float x[8], g8[8], d8[8], o8[8];
+    Chunk8<bf16_t>::load(reinterpret_cast<const bf16_t*>(a.q) + row, x);
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(x[i], x[i], ss);
+    ss = wave_sum(ss);
+    const float inv = 1.0f / __builtin_sqrtf(ss / (float)kBD + a.rms_eps);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) g8[i] = x[i] * inv * (a.gamma_q ? a.gamma_q[8 * lane + i] : 1.0f);
+    Chunk8<float>::load(w.dout + row, d8);
+    if (w.out_f32) Chunk8<float>::load(reinterpret_cast<const float*>(w.out) + row, o8);
+    else Chunk8<bf16_t>::load(reinterpret_cast<const bf16_t*>(w.out) + row, o8);
+    // q_hat = RoPE_t(q_n), do = RoPE_t(dout), o = RoPE_t(out): every rotated
+    // pair of this lane's chunk turns by +t
+    const int rope_lo = kBD - a.rope_dims;
+#pragma unroll
+    for (int pi = 0; pi < 4; ++pi) {
+        const int d = 8 * lane + 2 * pi;
+        if (d < rope_lo) continue;
+        float sn, cs;
+        sincos_turns((double)t * rope_turns(a.rope_ratio, (d - rope_lo) >> 1), &sn, &cs);
+        float* v3[3] = {g8, d8, o8};
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const float x0 = v3[k][2 * pi], x1 = v3[k][2 * pi + 1];
+            v3[k][2 * pi] = x0 * cs - x1 * sn;
+            v3[k][2 * pi + 1] = x0 * sn + x1 * cs;
+        }
+    }
+    float dl = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dl = __builtin_fmaf(d8[i], o8[i], dl);
+    dl = wave_sum(dl);
+    const int64_t orow = (bq * w.HP + h) * (int64_t)kBD + 8 * lane;
+    u32x4 qw, dw4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        qw[i] = pack_bf16x2(g8[2 * i], g8[2 * i + 1]);
+        dw4[i] = pack_bf16x2(d8[2 * i], d8[2 * i + 1]);
+    }
+    *reinterpret_cast<u32x4*>(w.qh + orow) = qw;
+    *reinterpret_cast<u32x4*>(w.doh + orow) = dw4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        qt[(8 * lane + i) * (int64_t)w.HP + h] = bf16_of(g8[i]);
+        dt[(8 * lane + i) * (int64_t)w.HP + h] = bf16_of(d8[i]);
+    }
+    if (lane == 0) {
+        w.delta[bq * H + h] = dl;
+        const float z = a.sinks[h], lse = w.lse[bq * H + h];
+        if (z != -INFINITY && lse != -INFINITY && w.dsinks) unsafeAtomicAdd(w.dsinks + h, -expf(z - lse) * dl);
+    }
+}
+
+// ---------------------------------------------------------------- logits
+// S^T = K Q_hat^T and dP^T = K dO^T for each tile of the split; P and dl.
+template <bool SPARSE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_logits_kernel(const BwdArgs w) {
+    const AttnArgs& a = w.f;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[2][kBuf];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, lrow = lane & 31, lh = lane >> 5;
+    const int64_t wg = xcd_order(blockIdx.x + (int64_t)gridDim.x * blockIdx.y, (int64_t)gridDim.x * gridDim.y);
+    const int64_t bq = wg / a.n_splits;
+    const int split = (int)(wg % a.n_splits);
+    const int H = a.H;
+    const QueryGeom g = query_geom<SPARSE>(a, bq);
+    const int L = g.n_c + g.n_w;
+    const int n_tiles = (L + TK - 1) / TK;
+    const int tps = (n_tiles + a.n_splits - 1) / a.n_splits;
+    const int tile0 = split * tps, tile1 = min(n_tiles, tile0 + tps);
+    const uint8_t* spare = reinterpret_cast<const uint8_t*>(a.q) + bq * (int64_t)H * kBD * 2;
+    const bool has_heads = 32 * wave < w.HP;
+    const int head = 32 * wave + lrow;
+    bf16x8 qf[kKS], df[kKS];
+    {
+        const int hh = head < H ? head : 0;
+        const uint16_t* qr = w.qh + (bq * w.HP + hh) * (int64_t)kBD + 8 * lh;
+        const uint16_t* dr = w.doh + (bq * w.HP + hh) * (int64_t)kBD + 8 * lh;
+#pragma unroll
+        for (int s = 0; s < kKS; ++s) {
+            qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qr + 16 * s));
+            df[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dr + 16 * s));
+        }
+    }
+    const float LOG2E = 1.4426950408889634f;
+    const float sc = a.scale_log2;  // tau * log2 e
+    const float mlse = head < H ? w.lse[bq * H + head] * LOG2E : 0.0f;
+    const float dlta = head < H ? w.delta[bq * H + head] : 0.0f;
+    const bool hlive = head < H && mlse != -INFINITY;
+    const int64_t S = w.S;
+    uint32_t masks[2] = {0u, 0u};
+    if (tile0 < tile1) masks[0] = load_tile<SPARSE>(a, g, bq, tile0, ring[0], spare, wave, lane);
+    for (int T = tile0; T < tile1; ++T) {
+        const int cur = (T - tile0) & 1;
+        if (T + 1 < tile1) {
+            masks[cur ^ 1] = load_tile<SPARSE>(a, g, bq, T + 1, ring[cur ^ 1], spare, wave, lane);
+            wait_vm<8>();
+        } else {
+            wait_vm<0>();
+        }
+        barrier_lds();
+        const uint32_t mask = masks[cur];
+        if (has_heads) {
+            const uint8_t* kh = ring[cur];
+            const int ga = gperm(lrow);
+            const uint8_t* kq0 = kh + lrow * kRS + 16 * (lh ^ (ga & 1)) + 32 * (ga >> 1);
+            const uint8_t* kq1 = kh + lrow * kRS + 16 * (lh ^ (ga & 1)) + 32 * ((ga >> 1) ^ 1);
+            f32x16 st, dpt;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[r] = dpt[r] = 0.0f;
+#pragma unroll
+            for (int s = 0; s < kKS; ++s) {
+                const bf16x8 kv = *reinterpret_cast<const bf16x8*>(((s & 1) ? kq1 : kq0) + 64 * (s >> 1));
+                st = mfma_bf16(kv, qf[s], st);
+                dpt = mfma_bf16(kv, df[s], dpt);
+            }
+            // element r: key 8 (r/4) + 4 lh + r%4 of the tile, head `head`
+            uint16_t* ptp = w.pt + (bq * S + (int64_t)T * TK) * w.HP + head;
+            uint16_t* dtp = w.dlt + (bq * S + (int64_t)T * TK) * w.HP + head;
+            uint16_t* dlp = w.dl + (bq * w.HP + head) * S + (int64_t)T * TK;
+#pragma unroll
+            for (int r0 = 0; r0 < 16; r0 += 4) {
+                uint16_t dv[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int r = r0 + k;
+                    const int key = 8 * (r >> 2) + 4 * lh + (r & 3);
+                    const bool live = hlive && ((mask >> key) & 1u);
+                    const float p = live ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], sc, -mlse)) : 0.0f;
+                    const float dlv = p * (dpt[r] - dlta);
+                    ptp[key * (int64_t)w.HP] = bf16_of(p);
+                    dtp[key * (int64_t)w.HP] = bf16_of(w.tau * dlv);
+                    dv[k] = bf16_of(dlv);
+                }
+                const int key0 = 8 * (r0 >> 2) + 4 * lh;
+                *reinterpret_cast<u32x2*>(dlp + key0) =
+                    u32x2{(uint32_t)dv[0] | ((uint32_t)dv[1] << 16), (uint32_t)dv[2] | ((uint32_t)dv[3] << 16)};
+            }
+        }
+        barrier_lds();  // every wave is done with this buffer before it is refilled
+    }
+}
+
+// ---------------------------------------------------------------- dkeys
+// dK = [tau dl^T | P^T] [Q_hat ; dO]: 8 waves, wave w owns output dims
+// 64 w .. +64 (two 32-dim tiles); the [Q_hat ; dO] operand (k = 2 HP stacked
+// heads) stays in VGPRs for the whole split (2 x 16 k-steps x 4 VGPRs).
+template <bool SPARSE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkeys_kernel(const BwdArgs w) {
+    const AttnArgs& a = w.f;
+    constexpr int MAXK = 16;  // k-steps of 16 stacked heads: 2 HP / 16 for HP <= 128
+    constexpr int NT = 2;     // dim tiles per wave
+    __shared__ uint64_t gptr[TK];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, lrow = lane & 31, lh = lane >> 5;
+    const int64_t wg = xcd_order(blockIdx.x + (int64_t)gridDim.x * blockIdx.y, (int64_t)gridDim.x * gridDim.y);
+    const int64_t bq = wg / a.n_splits;
+    const int split = (int)(wg % a.n_splits);
+    const QueryGeom g = query_geom<SPARSE>(a, bq);
+    const int L = g.n_c + g.n_w;
+    const int n_tiles = (L + TK - 1) / TK;
+    const int tps = (n_tiles + a.n_splits - 1) / a.n_splits;
+    const int tile0 = split * tps, tile1 = min(n_tiles, tile0 + tps);
+    const int nks = 2 * w.HP / 16;  // uniform, <= MAXK
+    const int ksq = w.HP / 16;      // k-steps from Q_hat (the rest from dO)
+    const int64_t S = w.S;
+    // B operand of dim tile dt, k-step ks: lane (dim column lrow, half lh)
+    // holds stacked heads 16 ks + 8 lh .. +7 of that dim
+    bf16x8 bop[NT][MAXK];
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) {
+        const int dim = 64 * wave + 32 * dt + lrow;
+        const uint16_t* qc = w.qt + (bq * kBD + dim) * (int64_t)w.HP + 8 * lh;
+        const uint16_t* dc = w.dot + (bq * kBD + dim) * (int64_t)w.HP + 8 * lh;
+#pragma unroll
+        for (int ks = 0; ks < MAXK; ++ks) {
+            const uint16_t* src = ks < ksq ? qc + 16 * ks : dc + 16 * (ks - ksq);
+            bop[dt][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+            if (ks < nks) bop[dt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src));
+        }
+    }
+    for (int T = tile0; T < tile1; ++T) {
+        // the tile's gradient rows
+        if (wave == 0 && lane < TK) {
+            const int slot = T * TK + lane;
+            float* gr = nullptr;
+            if (slot < L) gr = slot_grad_row(a, g, slot, slot_entry<SPARSE>(a, g, bq, slot), w.dkv_c, w.dkv_raw);
+            gptr[lane] = reinterpret_cast<uint64_t>(gr);
+        }
+        barrier_lds();
+        // A operand, k-step ks: lane (key lrow, half lh) holds stacked heads
+        // 16 ks + 8 lh .. +7 of that key (tau dl^T, then P^T)
+        const uint16_t* ad = w.dlt + (bq * S + (int64_t)T * TK + lrow) * w.HP + 8 * lh;
+        const uint16_t* ap = w.pt + (bq * S + (int64_t)T * TK + lrow) * w.HP + 8 * lh;
+        f32x16 acc[NT];
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < MAXK; ++ks) {
+            if (ks < nks) {  // uniform
+                const uint16_t* src = ks < ksq ? ad + 16 * ks : ap + 16 * (ks - ksq);
+                const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src));
+#pragma unroll
+                for (int dt = 0; dt < NT; ++dt) acc[dt] = mfma_bf16(av, bop[dt][ks], acc[dt]);
+            }
+        }
+        // element r of tile dt: key 8 (r/4) + 4 lh + r%4, dim 64 w + 32 dt + lrow
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = 8 * (r >> 2) + 4 * lh + (r & 3);
+            float* gr = reinterpret_cast<float*>(gptr[key]);
+            if (gr) {
+#pragma unroll
+                for (int dt = 0; dt < NT; ++dt) unsafeAtomicAdd(gr + 64 * wave + 32 * dt + lrow, acc[dt][r]);
+            }
+        }
+        barrier_lds();  // gptr is rewritten for the next tile
+    }
+}
+
+// ---------------------------------------------------------------- dquery
+// dq_hat (without tau) = dl K per split: the forward's P V product with dl.
+template <bool SPARSE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dquery_kernel(const BwdArgs w) {
+    const AttnArgs& a = w.f;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[2][kBuf];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, lrow = lane & 31, lh = lane >> 5;
+    const int64_t wg = xcd_order(blockIdx.x + (int64_t)gridDim.x * blockIdx.y, (int64_t)gridDim.x * gridDim.y);
+    const int64_t bq = wg / a.n_splits;
+    const int split = (int)(wg % a.n_splits);
+    const int H = a.H;
+    const QueryGeom g = query_geom<SPARSE>(a, bq);
+    const int L = g.n_c + g.n_w;
+    const int n_tiles = (L + TK - 1) / TK;
+    const int tps = (n_tiles + a.n_splits - 1) / a.n_splits;
+    const int tile0 = split * tps, tile1 = min(n_tiles, tile0 + tps);
+    const uint8_t* spare = reinterpret_cast<const uint8_t*>(a.q) + bq * (int64_t)H * kBD * 2;
+    const bool has_heads = 32 * wave < w.HP;
+    const int head = 32 * wave + lrow;
+    const int64_t S = w.S;
+    f32x16 acc[kDT];
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
+    if (tile0 < tile1) load_tile<SPARSE>(a, g, bq, tile0, ring[0], spare, wave, lane);
+    for (int T = tile0; T < tile1; ++T) {
+        const int cur = (T - tile0) & 1;
+        if (T + 1 < tile1) {
+            load_tile<SPARSE>(a, g, bq, T + 1, ring[cur ^ 1], spare, wave, lane);
+            wait_vm<8>();
+        } else {
+            wait_vm<0>();
+        }
+        barrier_lds();
+        if (has_heads) {
+            // A operand (dl, heads x keys): lane (head lrow, half lh) holds
+            // keys 8 lh + 16 ks .. +7 of the tile in the order the V reads use
+            // (keys 4 lh + j and 8 + 4 lh + j of each 16: see below)
+            const uint16_t* dlr = w.dl + (bq * w.HP + head) * S + (int64_t)T * TK;
+            bf16x8 pa[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                // the forward's P layout: k-step ks covers keys 16 ks + {4 lh + j, 8 + 4 lh + j}, j < 4
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(dlr + 16 * ks + 4 * lh);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(dlr + 16 * ks + 8 + 4 * lh);
+                pa[ks] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
+            const uint8_t* kh = ring[cur];
+            const int q = lane >> 4, i16 = lane & 15;
+            const uint8_t* vrow[2];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int rr = 8 * hf + 4 * (q >> 1) + (i16 >> 2);
+                vrow[hf] = kh + rr * kRS + 16 * ((2 * (q & 1) + ((i16 & 3) >> 1)) ^ gperm(rr)) + 8 * (i16 & 1);
+            }
+#pragma unroll
+            for (int dt = 0; dt < kDT; ++dt) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int off = ks * 16 * kRS + 64 * dt;
+                    const f16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_f16x4_t*)const_cast<uint8_t*>(vrow[0] + off));
+                    const f16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_f16x4_t*)const_cast<uint8_t*>(vrow[1] + off));
+                    const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+                    const bf16x8 vb = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+                    acc[dt] = mfma_bf16(pa[ks], vb, acc[dt]);
+                }
+            }
+        }
+        barrier_lds();
+    }
+    if (!has_heads) return;
+    // partials [BQ][split][HP][D]: element r of tile dt is head 8 (r/4) + 4 lh + r%4, dim 32 dt + lrow
+    float* dst = w.dqp + ((bq * a.n_splits + split) * (int64_t)w.HP + 32 * wave) * kBD;
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            dst[(8 * (r >> 2) + 4 * lh + (r & 3)) * (int64_t)kBD + 32 * dt + lrow] = acc[dt][r];
+}
+
+// ---------------------------------------------------------------- finish
+// One wave per (query, head): dq_hat = tau * sum over splits, du = RoPE_-t(dq_hat),
+// then the RMSNorm gradient: dq = gamma du / r - x sum(gamma du x) / (D r^3).
+__global__ __launch_bounds__(256) void bwd_finish_kernel(const BwdArgs w) {
+    const AttnArgs& a = w.f;
+    const int lane = threadIdx.x & 63;
+    const int64_t bq = blockIdx.x;
+    const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+    if (h >= a.H) return;
+    int32_t t = a.q_pos[bq];
+    t = t < 0 ? 0 : t;
+    float du[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) du[i] = 0.0f;
+    for (int s = 0; s < a.n_splits; ++s) {
+        float v[8];
+        Chunk8<float>::load(w.dqp + ((bq * a.n_splits + s) * (int64_t)w.HP + h) * kBD + 8 * lane, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) du[i] += v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) du[i] *= w.tau;
+    const int rope_lo = kBD - a.rope_dims;
+#pragma unroll
+    for (int pi = 0; pi < 4; ++pi) {
+        const int d = 8 * lane + 2 * pi;
+        if (d < rope_lo) continue;
+        float sn, cs;
+        sincos_turns(-(double)t * rope_turns(a.rope_ratio, (d - rope_lo) >> 1), &sn, &cs);
+        const float x0 = du[2 * pi], x1 = du[2 * pi + 1];
+        du[2 * pi] = x0 * cs - x1 * sn;
+        du[2 * pi + 1] = x0 * sn + x1 * cs;
+    }
+    const int64_t row = (bq * a.H + h) * (int64_t)kBD + 8 * lane;
+    float x[8];
+    Chunk8<bf16_t>::load(reinterpret_cast<const bf16_t*>(a.q) + row, x);
+    float ss = 0.0f, dot = 0.0f;
+    float gm[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        gm[i] = a.gamma_q ? a.gamma_q[8 * lane + i] : 1.0f;
+        ss = __builtin_fmaf(x[i], x[i], ss);
+        dot = __builtin_fmaf(gm[i] * du[i], x[i], dot);
+    }
+    ss = wave_sum(ss);
+    dot = wave_sum(dot);
+    const float r = __builtin_sqrtf(ss / (float)kBD + a.rms_eps);
+    const float ir = 1.0f / r, c3 = dot / ((float)kBD * r * r * r);
+    float dq[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        dq[i] = gm[i] * du[i] * ir - x[i] * c3;
+        if (w.dgamma_q) unsafeAtomicAdd(w.dgamma_q + 8 * lane + i, du[i] * x[i] * ir);
+    }
+    Chunk8<float>::store(w.dq + row, dq);
+}
+
+// ---------------------------------------------------------------- kv_prepare
+template <typename T>
+__global__ __launch_bounds__(256) void kv_prepare_bwd_kernel(const T* in, const float* dy, float* dx,
+                                                             const float* __restrict__ gamma, float* dgamma,
+                                                             int64_t N, int D, int64_t j0, int64_t n, int64_t rows,
+                                                             int m, int rope_dims, double rope_ratio, int pos_off,
+                                                             float eps) {
+    const int64_t rw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (rw >= rows) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t b = rw / n, j = j0 + rw % n;
+    const int64_t off = (b * N + j) * (int64_t)D;
+    const int nch = D >> 3;
+    const double pos = (double)(j * m + pos_off);
+    const int rope_lo = D - rope_dims;
+    float x[kPrepMaxChunks][8], u[kPrepMaxChunks][8];
+    float ss = 0.0f, dot = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kPrepMaxChunks; ++k) {
+        const int c = lane + 64 * k;
+        if (c < nch) {
+            Chunk8<T>::load(in + off + 8 * c, x[k]);
+            Chunk8<float>::load(dy + off + 8 * c, u[k]);
+            if (8 * c + 8 > rope_lo) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const int d = 8 * c + 2 * p;
+                    if (d < rope_lo) continue;
+                    float sn, cs;
+                    sincos_turns(-pos * rope_turns(rope_ratio, (d - rope_lo) >> 1), &sn, &cs);
+                    const float x0 = u[k][2 * p], x1 = u[k][2 * p + 1];
+                    u[k][2 * p] = x0 * cs - x1 * sn;
+                    u[k][2 * p + 1] = x0 * sn + x1 * cs;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                ss = __builtin_fmaf(x[k][i], x[k][i], ss);
+                dot = __builtin_fmaf((gamma ? gamma[8 * c + i] : 1.0f) * u[k][i], x[k][i], dot);
+            }
+        }
+    }
+    ss = wave_sum(ss);
+    dot = wave_sum(dot);
+    const float r = __builtin_sqrtf(ss / (float)D + eps);
+    const float ir = 1.0f / r, c3 = dot / ((float)D * r * r * r);
+#pragma unroll
+    for (int k = 0; k < kPrepMaxChunks; ++k) {
+        const int c = lane + 64 * k;
+        if (c < nch) {
+            float o[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float gm = gamma ? gamma[8 * c + i] : 1.0f;
+                o[i] = gm * u[k][i] * ir - x[k][i] * c3;
+                if (dgamma) unsafeAtomicAdd(dgamma + 8 * c + i, u[k][i] * x[k][i] * ir);
+            }
+            Chunk8<float>::store(dx + off + 8 * c, o);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- kv_compress
+// Entry statistics per (entry, channel): mx, 1/z and c (the forward value in fp32).
+template <typename TIn, bool PC>
+__global__ __launch_bounds__(256) void kv_compress_stats_kernel(const TIn* x, const float* gate, int64_t T, int D,
+                                                                int m, int span, int64_t nblk, float* st) {
+    const int64_t e = blockIdx.x;  // b * nblk + j
+    const int64_t b = e / nblk, j = e % nblk;
+    const int64_t hi = (j + 1) * m, lo = hi - span > 0 ? hi - span : 0;
+    const int n = (int)(hi - lo);
+    for (int d = threadIdx.x; d < D; d += 256) {
+        float mx = -INFINITY;
+        for (int i = 0; i < n; ++i) {
+            const float gi = PC ? gate[(b * T + lo + i) * D + d] : gate[b * T + lo + i];
+            mx = fmaxf(mx, gi);
+        }
+        float z = 0.0f, c = 0.0f;
+        for (int i = 0; i < n; ++i) {
+            const float gi = PC ? gate[(b * T + lo + i) * D + d] : gate[b * T + lo + i];
+            const float wgt = expf(gi - mx);
+            z += wgt;
+            float xv;
+            if constexpr (sizeof(TIn) == 4) xv = reinterpret_cast<const float*>(x)[(b * T + lo + i) * D + d];
+            else xv = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[(b * T + lo + i) * D + d]);
+            c = __builtin_fmaf(wgt, xv, c);
+        }
+        const float rz = 1.0f / z;
+        float* o = st + (e * (int64_t)D + d) * 3;
+        o[0] = mx;
+        o[1] = rz;
+        o[2] = c * rz;
+    }
+}
+
+// One workgroup per token i: the entries whose span holds i are
+// j = ceil((i+1)/m) - 1 .. floor((i + span)/m) - 1 (below nblk).
+template <typename TIn, bool PC>
+__global__ __launch_bounds__(256) void kv_compress_bwd_kernel(const TIn* x, const float* gate, const float* dc,
+                                                              const float* st, int64_t T, int D, int m, int span,
+                                                              int64_t nblk, float* dx, float* dgate) {
+    __shared__ float red[4];
+    const int64_t bi = blockIdx.x;  // b * T + i
+    const int64_t b = bi / T, i = bi % T;
+    int64_t jlo = (i + m) / m - 1;  // ceil((i+1)/m) - 1
+    int64_t jhi = (i + span) / m - 1;
+    if (jhi > nblk - 1) jhi = nblk - 1;
+    float gsum = 0.0f;
+    for (int d = threadIdx.x; d < D; d += 256) {
+        float xv;
+        if constexpr (sizeof(TIn) == 4) xv = reinterpret_cast<const float*>(x)[bi * D + d];
+        else xv = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[bi * D + d]);
+        const float gi = PC ? gate[bi * D + d] : gate[bi];
+        float ax = 0.0f, ag = 0.0f;
+        for (int64_t j = jlo; j <= jhi; ++j) {
+            const float* s = st + ((b * nblk + j) * (int64_t)D + d) * 3;
+            const float a = expf(gi - s[0]) * s[1];
+            const float g = dc[(b * nblk + j) * (int64_t)D + d];
+            ax = __builtin_fmaf(a, g, ax);
+            ag = __builtin_fmaf(a * (xv - s[2]), g, ag);
+        }
+        dx[bi * D + d] = ax;
+        if (PC) dgate[bi * D + d] = ag;
+        else gsum += ag;
+    }
+    if (!PC) {
+        gsum = wave_sum(gsum);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = gsum;
+        __syncthreads();
+        if (threadIdx.x == 0) dgate[bi] = (red[0] + red[1]) + (red[2] + red[3]);
+    }
+}
+
+// ---------------------------------------------------------------- indexer
+// One workgroup per query; chunks of 32 selected entries.  The score's ReLU
+// decision is the forward's canonical fp32 dot (head dim ascending from +0).
+template <typename TQ, bool FP8>
+__global__ __launch_bounds__(256) void indexer_bwd_kernel(const IndexerBwdArgs a) {
+    __shared__ float qs[8192];   // [HI][dI]
+    __shared__ float ks[32 * 257];  // [32][dI + 1]: rows padded against bank conflicts
+    __shared__ float coef[64 * 32];  // [HI][32]: dS_j w_h [s > 0]
+    __shared__ float rl[64 * 32];    // [HI][32]: ReLU(s)
+    __shared__ float dsv[32];
+    __shared__ int32_t js[32];
+    const int tid = threadIdx.x;
+    const int64_t bq = blockIdx.x;
+    const int64_t b = bq / a.Q;
+    const int HI = a.HI, dI = a.dI, NE = HI * dI, KST = dI + 1;
+    int32_t t = a.q_pos[bq];
+    const int64_t nv = t < 0 ? 0 : ((int64_t)t / a.m < a.N ? (int64_t)t / a.m : a.N);
+    for (int e = tid; e < NE; e += 256) {
+        if constexpr (sizeof(TQ) == 4) qs[e] = reinterpret_cast<const float*>(a.q_idx)[bq * NE + e];
+        else qs[e] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.q_idx)[bq * NE + e]);
+    }
+    constexpr int PER = 32;  // dq elements per thread (HI * dI <= 8192)
+    float dq[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) dq[k] = 0.0f;
+    float dw = 0.0f;
+    __syncthreads();
+    for (int s0 = 0; s0 < a.K; s0 += 32) {
+        if (tid < 32) {
+            const int s = s0 + tid;
+            int32_t j = s < a.K ? a.idx[bq * a.K + s] : -1;
+            if (j < 0 || j >= nv) j = -1;
+            js[tid] = j;
+            dsv[tid] = (j >= 0) ? a.dS[bq * a.K + s] : 0.0f;
+        }
+        __syncthreads();
+        for (int e = tid; e < 32 * dI; e += 256) {
+            const int r = e / dI, d = e % dI;
+            const int32_t j = js[r];
+            float v = 0.0f;
+            if (j >= 0) {
+                if constexpr (FP8) {
+                    const uint8_t c = reinterpret_cast<const uint8_t*>(a.k_idx)[(b * a.N + j) * dI + d];
+                    v = e4m3_decode_f32(c) * a.k_scale[b * a.N + j];
+                } else {
+                    v = reinterpret_cast<const float*>(a.k_idx)[(b * a.N + j) * dI + d];
+                }
+            }
+            ks[r * KST + d] = v;
+        }
+        __syncthreads();
+        for (int e = tid; e < HI * 32; e += 256) {
+            const int h = e / 32, r = e % 32;
+            float sh = 0.0f;
+            for (int d = 0; d < dI; ++d) sh = __builtin_fmaf(qs[h * dI + d], ks[r * KST + d], sh);
+            const bool pos = js[r] >= 0 && sh > 0.0f;
+            coef[e] = pos ? dsv[r] * a.w[bq * HI + h] : 0.0f;
+            rl[e] = pos ? sh : 0.0f;
+        }
+        __syncthreads();
+        if (tid < HI) {
+            for (int r = 0; r < 32; ++r) dw = __builtin_fmaf(dsv[r], rl[tid * 32 + r], dw);
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int e = tid + 256 * k;
+            if (e < NE) {
+                const int h = e / dI, d = e % dI;
+                float acc = dq[k];
+                for (int r = 0; r < 32; ++r) acc = __builtin_fmaf(coef[h * 32 + r], ks[r * KST + d], acc);
+                dq[k] = acc;
+            }
+        }
+        for (int e = tid; e < 32 * dI; e += 256) {
+            const int r = e / dI, d = e % dI;
+            const int32_t j = js[r];
+            if (j < 0) continue;
+            float acc = 0.0f;
+            for (int h = 0; h < HI; ++h) acc = __builtin_fmaf(coef[h * 32 + r], qs[h * dI + d], acc);
+            if (acc != 0.0f) unsafeAtomicAdd(a.dk + (b * a.N + j) * dI + d, acc);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int e = tid + 256 * k;
+        if (e < NE) a.dq[bq * NE + e] = dq[k];
+    }
+    if (tid < HI) a.dw[bq * HI + tid] = dw;
+}
+
+// ---------------------------------------------------------------- launchers
+size_t mqa_bwd_workspace_bytes(int64_t BQ, int32_t H, int64_t max_slots, int n_splits) {
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const int64_t HP = (H + 31) / 32 * 32;
+    const int64_t S = (max_slots + TK - 1) / TK * TK;
+    size_t n = 0;
+    n += 4 * al((size_t)BQ * HP * kBD * 2);  // qh, doh, qt, dot
+    n += al((size_t)BQ * H * 4);             // delta
+    n += 3 * al((size_t)BQ * (S > 0 ? S : TK) * HP * 2);  // pt, dlt, dl
+    n += al((size_t)BQ * n_splits * HP * kBD * 4);  // dqp
+    return n;
+}
+
+int launch_mqa_bwd(BwdArgs& w, int64_t BQ, int64_t max_slots, void* ws, hipStream_t stream) {
+    if (BQ == 0) return 0;
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const int64_t HP = (w.f.H + 31) / 32 * 32;
+    const int64_t S = (max_slots + TK - 1) / TK * TK;
+    w.HP = (int32_t)HP;
+    w.S = (int32_t)(S > 0 ? S : TK);
+    uint8_t* p = reinterpret_cast<uint8_t*>(ws);
+    auto take = [&](size_t bytes) {
+        uint8_t* r = p;
+        p += al(bytes);
+        return r;
+    };
+    w.qh = reinterpret_cast<uint16_t*>(take((size_t)BQ * HP * kBD * 2));
+    w.doh = reinterpret_cast<uint16_t*>(take((size_t)BQ * HP * kBD * 2));
+    w.qt = reinterpret_cast<uint16_t*>(take((size_t)BQ * HP * kBD * 2));
+    w.dot = reinterpret_cast<uint16_t*>(take((size_t)BQ * HP * kBD * 2));
+    w.delta = reinterpret_cast<float*>(take((size_t)BQ * w.f.H * 4));
+    w.pt = reinterpret_cast<uint16_t*>(take((size_t)BQ * w.S * HP * 2));
+    w.dlt = reinterpret_cast<uint16_t*>(take((size_t)BQ * w.S * HP * 2));
+    w.dl = reinterpret_cast<uint16_t*>(take((size_t)BQ * w.S * HP * 2));
+    w.dqp = reinterpret_cast<float*>(take((size_t)BQ * w.f.n_splits * HP * kBD * 4));
+    const bool sparse = w.f.idx != nullptr;
+    const dim3 gp((unsigned)BQ, (unsigned)(HP / 4));
+    const dim3 gs((unsigned)w.f.n_splits, (unsigned)BQ);
+    prof_mark("bwd_prep_kernel", false, stream);
+    hipLaunchKernelGGL(bwd_prep_kernel, gp, dim3(256), 0, stream, w);
+    prof_mark("bwd_prep_kernel", true, stream);
+    prof_mark("bwd_logits_kernel", false, stream);
+    if (sparse) hipLaunchKernelGGL(bwd_logits_kernel<true>, gs, dim3(256), 0, stream, w);
+    else hipLaunchKernelGGL(bwd_logits_kernel<false>, gs, dim3(256), 0, stream, w);
+    prof_mark("bwd_logits_kernel", true, stream);
+    prof_mark("bwd_dkeys_kernel", false, stream);
+    if (sparse) hipLaunchKernelGGL(bwd_dkeys_kernel<true>, gs, dim3(512), 0, stream, w);
+    else hipLaunchKernelGGL(bwd_dkeys_kernel<false>, gs, dim3(512), 0, stream, w);
+    prof_mark("bwd_dkeys_kernel", true, stream);
+    prof_mark("bwd_dquery_kernel", false, stream);
+    if (sparse) hipLaunchKernelGGL(bwd_dquery_kernel<true>, gs, dim3(256), 0, stream, w);
+    else hipLaunchKernelGGL(bwd_dquery_kernel<false>, gs, dim3(256), 0, stream, w);
+    prof_mark("bwd_dquery_kernel", true, stream);
+    prof_mark("bwd_finish_kernel", false, stream);
+    hipLaunchKernelGGL(bwd_finish_kernel, dim3((unsigned)BQ, (unsigned)((w.f.H + 3) / 4)), dim3(256), 0, stream, w);
+    prof_mark("bwd_finish_kernel", true, stream);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_kv_prepare_bwd(const void* in, const float* dy, float* dx, float* dgamma, int dtype, int64_t B, int64_t N,
+                          int64_t D, int64_t j0, int64_t n, const float* gamma, int32_t m, int32_t rope_dims,
+                          double rope_ratio, int32_t pos_off, float eps, hipStream_t stream) {
+    const int64_t rows = B * n;
+    if (rows == 0) return 0;
+    if (D > 64 * 8 * kPrepMaxChunks) return -2;
+    const int64_t grid = (rows + 3) / 4;
+    if (grid > 0x7fffffffLL) return -2;
+    prof_mark("kv_prepare_bwd_kernel", false, stream);
+    if (dtype == 0)
+        hipLaunchKernelGGL((kv_prepare_bwd_kernel<float>), dim3((unsigned)grid), dim3(256), 0, stream,
+                           (const float*)in, dy, dx, gamma, dgamma, N, (int)D, j0, n, rows, m, rope_dims, rope_ratio,
+                           pos_off, eps);
+    else
+        hipLaunchKernelGGL((kv_prepare_bwd_kernel<bf16_t>), dim3((unsigned)grid), dim3(256), 0, stream,
+                           (const bf16_t*)in, dy, dx, gamma, dgamma, N, (int)D, j0, n, rows, m, rope_dims, rope_ratio,
+                           pos_off, eps);
+    prof_mark("kv_prepare_bwd_kernel", true, stream);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+size_t kv_compress_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int32_t m) {
+    return (size_t)B * (size_t)(T / m) * (size_t)D * 3 * 4;
+}
+
+int launch_kv_compress_bwd(const void* x, int x_dtype, const float* gate, bool pc, int64_t B, int64_t T, int64_t D,
+                           int32_t m, int32_t span, const float* dc, float* dx, float* dgate, void* ws,
+                           hipStream_t stream) {
+    const int64_t nblk = T / m;
+    if (B * T == 0) return 0;
+    if (B * nblk > 0x7fffffffLL || B * T > 0x7fffffffLL) return -2;
+    float* st = reinterpret_cast<float*>(ws);
+#define CAKV_CB(TIN, PC)                                                                                          \
+    do {                                                                                                         \
+        if (nblk > 0)                                                                                            \
+            hipLaunchKernelGGL((kv_compress_stats_kernel<TIN, PC>), dim3((unsigned)(B * nblk)), dim3(256), 0,   \
+                               stream, (const TIN*)x, gate, T, (int)D, m, span, nblk, st);                       \
+        hipLaunchKernelGGL((kv_compress_bwd_kernel<TIN, PC>), dim3((unsigned)(B * T)), dim3(256), 0, stream,    \
+                           (const TIN*)x, gate, dc, st, T, (int)D, m, span, nblk, dx, dgate);                    \
+    } while (0)
+    prof_mark("kv_compress_bwd_kernel", false, stream);
+    if (x_dtype == 0) {
+        if (pc) CAKV_CB(float, true);
+        else CAKV_CB(float, false);
+    } else {
+        if (pc) CAKV_CB(bf16_t, true);
+        else CAKV_CB(bf16_t, false);
+    }
+#undef CAKV_CB
+    prof_mark("kv_compress_bwd_kernel", true, stream);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_indexer_bwd(const IndexerBwdArgs& a, int64_t BQ, bool q_f32, bool fp8, hipStream_t stream) {
+    if (BQ == 0) return 0;
+    prof_mark("indexer_bwd_kernel", false, stream);
+    if (q_f32) {
+        if (fp8) hipLaunchKernelGGL((indexer_bwd_kernel<float, true>), dim3((unsigned)BQ), dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((indexer_bwd_kernel<float, false>), dim3((unsigned)BQ), dim3(256), 0, stream, a);
+    } else {
+        if (fp8) hipLaunchKernelGGL((indexer_bwd_kernel<bf16_t, true>), dim3((unsigned)BQ), dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((indexer_bwd_kernel<bf16_t, false>), dim3((unsigned)BQ), dim3(256), 0, stream, a);
+    }
+    prof_mark("indexer_bwd_kernel", true, stream);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // namespace cakv

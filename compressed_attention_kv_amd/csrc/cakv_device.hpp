@@ -78,6 +78,15 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v) {
     return code | sign;
 }
 
+// OCP E4M3 code -> its exact value (bias 7, three mantissa bits, exponent
+// field 0 holds subnormals m * 2^-9; the NaN code is never produced by the
+// encoder and decodes as the largest magnitude plus one step, 480)
+__device__ __forceinline__ float e4m3_decode_f32(uint32_t c) {
+    const int e = (c >> 3) & 15, m = c & 7;
+    const float v = e == 0 ? __builtin_ldexpf((float)m, -9) : __builtin_ldexpf((float)(8 + m), e - 10);
+    return (c & 0x80u) ? -v : v;
+}
+
 // ---------------------------------------------------------------- rotary sin / cos
 // sin and cos of 2*pi*x for a fraction of a turn x (any real, fp64).  The
 // integer part is dropped exactly in fp64, the rest is folded to an octant

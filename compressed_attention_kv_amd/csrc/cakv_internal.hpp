@@ -130,6 +130,65 @@ struct IndexerArgs {
     int32_t n_chunks;
 };
 
+// Attention backward: the forward's arguments plus the gradients and the
+// workspace arrays (laid out by launch_mqa_bwd).
+struct BwdArgs {
+    AttnArgs f;
+    const void* out;    // forward output [BQ][H][D], bf16 or f32 (out_f32)
+    const float* lse;   // [BQ][H]
+    const float* dout;  // [BQ][H][D]
+    float* dq;          // [BQ][H][D], written
+    float* dkv_c;       // [B][N][D], accumulated
+    float* dkv_raw;     // [B][R][D], accumulated
+    float* dsinks;      // [H], accumulated, or NULL
+    float* dgamma_q;    // [D], accumulated, or NULL
+    uint16_t* qh;       // [BQ][HP][D] bf16 q_hat
+    uint16_t* doh;      // [BQ][HP][D] bf16 do = RoPE_t(dout)
+    uint16_t* qt;       // [BQ][D][HP] bf16 q_hat transposed
+    uint16_t* dot;      // [BQ][D][HP] bf16 do transposed
+    float* delta;       // [BQ][H] do . o
+    uint16_t* pt;       // [BQ][S][HP] bf16 P (key-major)
+    uint16_t* dlt;      // [BQ][S][HP] bf16 tau * dl (key-major)
+    uint16_t* dl;       // [BQ][HP][S] bf16 dl (head-major)
+    float* dqp;         // [BQ][splits][HP][D] partial dq_hat / tau
+    int32_t out_f32;
+    int32_t HP;         // heads rounded up to 32
+    int32_t S;          // key slots per query, rounded up to 32
+    float tau;          // softmax scale
+};
+size_t mqa_bwd_workspace_bytes(int64_t BQ, int32_t H, int64_t max_slots, int n_splits);
+int launch_mqa_bwd(BwdArgs& w, int64_t BQ, int64_t max_slots, void* ws, hipStream_t stream);
+
+// dtype 0: float32, 1: bf16; dy, dx: [B][N][D] float32, rows j0 .. j0+n-1
+int launch_kv_prepare_bwd(const void* in, const float* dy, float* dx, float* dgamma, int dtype, int64_t B, int64_t N,
+                          int64_t D, int64_t j0, int64_t n, const float* gamma, int32_t m, int32_t rope_dims,
+                          double rope_ratio, int32_t pos_off, float eps, hipStream_t stream);
+
+size_t kv_compress_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int32_t m);
+int launch_kv_compress_bwd(const void* x, int x_dtype, const float* gate, bool pc, int64_t B, int64_t T, int64_t D,
+                           int32_t m, int32_t span, const float* dc, float* dx, float* dgate, void* ws,
+                           hipStream_t stream);
+
+struct IndexerBwdArgs {
+    const void* q_idx;    // [BQ][HI][dI] f32 or bf16
+    const float* w;       // [BQ][HI]
+    const void* k_idx;    // [B][N][dI] f32 or fp8 codes
+    const float* k_scale; // [B][N] (fp8)
+    const int32_t* q_pos; // [BQ]
+    const int32_t* idx;   // [BQ][K]
+    const float* dS;      // [BQ][K]
+    float* dq;            // [BQ][HI][dI], written
+    float* dw;            // [BQ][HI], written
+    float* dk;            // [B][N][dI], accumulated
+    int64_t Q;
+    int64_t N;
+    int32_t HI;
+    int32_t dI;
+    int32_t m;
+    int32_t K;
+};
+int launch_indexer_bwd(const IndexerBwdArgs& a, int64_t BQ, bool q_f32, bool fp8, hipStream_t stream);
+
 size_t indexer_workspace_bytes(int64_t BQ, int64_t N, int32_t k);
 int launch_indexer_topk(IndexerArgs& a, int64_t BQ, bool fp8_mode, void* ws, hipStream_t stream);
 

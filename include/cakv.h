@@ -362,6 +362,90 @@ int cakv_dense_compressed_mqa_fwd(const cakv_attn_params* p, const void* q, cons
                                   int64_t R, void* out, int out_dtype, float* lse,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* ===========================================================================
+ * Backward pass (training)  [V4-Pro card, section 5 "1M context, gradually":
+ * sparse attention is trained from 64K context on, after a short warm-up of
+ * the Lightning Indexer].  The gradients of the calls above.  Buffers named
+ * "accumulated" receive += (the caller zeroes them); all others are
+ * overwritten.  Float atomics add the contributions of different queries
+ * and heads, so accumulated results may differ in the last bits run to run.
+ * ======================================================================== */
+
+/* ---------------------------------------------------------------------------
+ * mqa_bwd: gradient of sparse_mqa_fwd (idx given) or dense_compressed_mqa_fwd
+ * (idx NULL), from the forward's inputs, its output `out` and `lse`, and
+ * dout [B,Q,H,D] float32.  Per query and head, with do = RoPE_t(dout) (the
+ * transpose of the output's rotation by -t), P the softmax weights
+ * exp(logit - lse), o = RoPE_t(out) and delta = do . o:
+ *     dl_u = P_u (do . k_u - delta),   dsink = -P_sink delta,
+ *     dq_hat = tau sum_u dl_u k_u,     dk_u += tau dl_u q_hat + P_u do,
+ * then dq through RoPE_t's transpose and the RMSNorm (with gamma_q) of q.
+ *   dq       [B,Q,H,D] float32, overwritten (gradient of the raw query)
+ *   dkv_c    [B,N,D]   float32, accumulated: gradient of the prepared cache
+ *            rows (what the forward reads; cakv_kv_prepare_bwd continues to
+ *            the raw entries)
+ *   dkv_raw  [B,R,D]   float32, accumulated: the same for the window rows
+ *   dsinks   [H] float32 accumulated, or NULL; dgamma_q [D] accumulated or NULL
+ * Supported: CAKV_BF16 activations with D = 512, 1 <= H <= 128,
+ * B*Q <= 65535; other parameters as the forward (ring mode included).
+ * Workspace: cakv_mqa_bwd_workspace(B, Q, H, D, n_keys, n_win) bytes with
+ * n_keys = K (sparse) or N (dense), 256-byte aligned.
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE.
+ * ------------------------------------------------------------------------- */
+size_t cakv_mqa_bwd_workspace(int64_t B, int64_t Q, int32_t H, int32_t D, int64_t n_keys, int32_t n_win);
+int cakv_mqa_bwd(const cakv_attn_params* p, const void* q, const void* kv_c, const int32_t* idx,
+                 const void* kv_raw, const int32_t* raw_pos0, const int32_t* q_pos, const float* sinks,
+                 int act_dtype, int64_t B, int64_t Q, int32_t H, int32_t D, int64_t N, int32_t K, int64_t R,
+                 const void* out, int out_dtype, const float* lse, const float* dout, float* dq,
+                 float* dkv_c, float* dkv_raw, float* dsinks, float* dgamma_q, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kv_prepare_bwd: gradient of cakv_kv_prepare for entries j0 .. j0+n-1:
+ * dy [B,N,D] float32 (gradient of the prepared rows) -> dx [B,N,D] float32
+ * (gradient of the raw entries kv_in, rows j0 .. j0+n-1 overwritten, the
+ * others untouched); dgamma_kv [D] accumulated, or NULL.  The rotation's
+ * transpose is the rotation by -position; then the RMSNorm gradient
+ *     dx = gamma du / r - x sum_d(gamma_d du_d x_d) / (D r^3).
+ * Arguments and limits otherwise as cakv_kv_prepare.
+ * ------------------------------------------------------------------------- */
+int cakv_kv_prepare_bwd(const void* kv_in, int act_dtype, const float* dy, float* dx, float* dgamma_kv,
+                        int64_t B, int64_t N, int64_t D, int64_t j0, int64_t n, const float* gamma_kv,
+                        int32_t m, int32_t rope_dims, float rope_base, int32_t entry_pos_offset,
+                        float rms_eps, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kv_compress_bwd: gradient of cakv_kv_compress_ex (and cakv_kv_compress:
+ * span = m, per-token gates).  dc [B, floor(T/m), D] float32 ->
+ *     dx[b,i,d] = sum_{j: i in S_j} a_{i,d} dc[b,j,d]
+ *     dgate[b,i(,d)] = sum_{j: i in S_j} (sum_d) a_{i,d} (x[b,i,d] - c[b,j,d]) dc[b,j,d]
+ * dx [B,T,D] float32 and dgate ([B,T] or [B,T,D] float32) overwritten
+ * (tokens in no entry's span get 0).  Workspace
+ * cakv_kv_compress_bwd_workspace(B, T, D, m) bytes (the entries' softmax
+ * statistics).  Arguments and limits otherwise as cakv_kv_compress_ex.
+ * ------------------------------------------------------------------------- */
+size_t cakv_kv_compress_bwd_workspace(int64_t B, int64_t T, int64_t D, int32_t m);
+int cakv_kv_compress_bwd(const void* x, int x_dtype, const float* gate, int gate_per_channel, int64_t B,
+                         int64_t T, int64_t D, int32_t m, int32_t span, const float* dc, float* dx,
+                         float* dgate, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * indexer_bwd: gradient of the indexer score S(j) = sum_h w_h ReLU(q_h . k_j)
+ * over the selected entries idx [B,Q,K] (slots that are -1 or not visible
+ * carry nothing), given dS [B,Q,K] float32:
+ *     dq_h += dS_j w_h [s_h > 0] k_j,  dw_h += dS_j ReLU(s_h),
+ *     dk_j += dS_j sum_h w_h [s_h > 0] q_h.
+ * Each ReLU decision is taken on the forward's canonical fp32 dot product
+ * (head dim ascending from +0 in fmaf, fp8 keys decoded exactly), whatever
+ * the mode.  dq_idx [B,Q,HI,dI] and dw [B,Q,HI] float32 overwritten; dk
+ * [B,N,dI] float32 accumulated.  Modes and dtypes as cakv_indexer_topk;
+ * HI <= 64, dI a multiple of 4 up to 256, HI*dI <= 8192, K <= 65536.
+ * ------------------------------------------------------------------------- */
+int cakv_indexer_bwd(const void* q_idx, int q_dtype, const float* w, const void* k_idx, int k_dtype,
+                     const float* k_scale, const int32_t* q_pos, const int32_t* idx, const float* dS, int64_t B,
+                     int64_t Q, int64_t N, int32_t HI, int32_t dI, int32_t m, int32_t K, float* dq_idx,
+                     float* dw, float* dk, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -301,3 +301,56 @@ def test_attention_ring_mode_needs_a_window_sized_ring(lib):
     assert _sparse(lib, _prm(raw_ring=1), B=0, R=128) == 0
     assert _sparse(lib, _prm(raw_ring=1), raw0=None, R=128, B=0) == 0
     assert _sparse(lib, _prm(raw_ring=2), B=0, R=128) == -1
+
+
+# ---------------------------------------------------------------- backward entry points
+
+def _mqa_bwd(lib, **kw):
+    a = dict(q=FAKE, kv_c=FAKE, idx=FAKE, kv_raw=FAKE, raw0=FAKE, qpos=FAKE, sinks=FAKE, act=cakv.BF16, B=1, Q=1,
+             H=128, D=512, N=16, K=64, R=128, out=FAKE, odt=cakv.F32, lse=FAKE, dout=FAKE, dq=FAKE, dkc=FAKE,
+             dkr=FAKE, ds=None, dg=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.cakv_mqa_bwd(ctypes.byref(_prm()), a["q"], a["kv_c"], a["idx"], a["kv_raw"], a["raw0"], a["qpos"],
+                            a["sinks"], a["act"], a["B"], a["Q"], a["H"], a["D"], a["N"], a["K"], a["R"], a["out"],
+                            a["odt"], a["lse"], a["dout"], a["dq"], a["dkc"], a["dkr"], a["ds"], a["dg"], a["ws"],
+                            a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [(dict(B=0, q=None), 0), (dict(D=128), -2), (dict(act=cakv.F32, D=128), -2),
+                                     (dict(H=129), -2), (dict(lse=None), -1), (dict(dout=None), -1),
+                                     (dict(dq=None), -1), (dict(dkc=None), -1), (dict(dkr=None), -1),
+                                     (dict(wsb=0), -3), (dict(ws=None), -3), (dict(K=65537), -2),
+                                     (dict(B=70000), -2), (dict(ds=FAKE + 4), -1)])
+def test_mqa_bwd_argument_errors(lib, kw, code):
+    assert _mqa_bwd(lib, **kw) == code
+
+
+def test_mqa_bwd_workspace_never_shrinks_with_the_batch(lib):
+    sizes = [lib.cakv_mqa_bwd_workspace(1, bq, 128, 512, 1024, 128) for bq in range(1, 400)]
+    assert all(b >= a for a, b in zip(sizes, sizes[1:])) and sizes[0] > 0
+
+
+def test_kv_prepare_bwd_and_compress_bwd_errors(lib):
+    f = lib.cakv_kv_prepare_bwd
+    assert f(FAKE, cakv.BF16, FAKE, FAKE, None, 1, 8, 500, 0, 8, None, 4, 64, 10000.0, 0, 1e-6, None) == -2
+    assert f(FAKE, cakv.BF16, None, FAKE, None, 1, 8, 512, 0, 8, None, 4, 64, 10000.0, 0, 1e-6, None) == -1
+    assert f(FAKE, cakv.BF16, FAKE, FAKE, None, 1, 8, 512, 4, 8, None, 4, 64, 10000.0, 0, 1e-6, None) == -1
+    assert f(None, cakv.BF16, None, None, None, 0, 8, 512, 0, 8, None, 4, 64, 10000.0, 0, 1e-6, None) == 0
+    g = lib.cakv_kv_compress_bwd
+    ws = lib.cakv_kv_compress_bwd_workspace(1, 64, 512, 4)
+    assert ws == 16 * 512 * 12
+    assert g(FAKE, cakv.BF16, FAKE, 0, 1, 64, 512, 4, 3, FAKE, FAKE, FAKE, FAKE, ws, None) == -2  # span < m
+    assert g(FAKE, cakv.BF16, FAKE, 0, 1, 64, 512, 4, 4, FAKE, FAKE, FAKE, FAKE, 0, None) == -3
+    assert g(FAKE, cakv.BF16, FAKE, 0, 1, 64, 512, 4, 4, None, FAKE, FAKE, FAKE, ws, None) == -1
+    assert g(None, cakv.BF16, None, 0, 0, 64, 512, 4, 4, None, None, None, None, 0, None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [(dict(), 0), (dict(HI=65), -2), (dict(dI=260), -2), (dict(dI=130), -2),
+                                     (dict(qdt=cakv.F32), -2), (dict(ks=None), -1), (dict(K=65537), -2)])
+def test_indexer_bwd_limits(lib, kw, code):
+    a = dict(qdt=cakv.BF16, kdt=cakv.FP8_E4M3, ks=FAKE, HI=64, dI=128, K=1024)
+    a.update(kw)
+    # an empty batch validates the sizes and launches nothing
+    rc = lib.cakv_indexer_bwd(None, a["qdt"], None, None, a["kdt"], a["ks"], None, None, None, 0, 1, 64, a["HI"],
+                              a["dI"], 4, a["K"], None, None, None, None)
+    assert rc == code
