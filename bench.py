@@ -1,25 +1,38 @@
 """Throughput of the compressed-attention hot path on one MI355X.
 
-Default workload: CSA decode at 128K context -- 32 sequences, each query at
-position 131072 over 32768 compressed entries (m=4) with fp8 indexer keys,
-top-1024 selection, then sparse MQA (128 heads x 512) over the selection plus
-the 128-token raw window and the sinks.  One step = indexer_topk +
-sparse_mqa_fwd for the batch, inputs resident in HBM.  Other workloads
-(--workload): csa_decode_1m, hca_decode_1m (dense_compressed_mqa_fwd only),
-prefill_chunk_256k (CSA + HCA layers of an 8192-token prefill chunk after a
-262,144-token prefix: the chunk's three compressions into the caches and
-the preparation of its new attention entries and window rows, the indexer,
-sparse attention, dense attention).  Decode caches and window rows hold
-prepared keys (kv_prepare runs once per entry or token, when it is written).
+Headline workload (the line's top-level figures): CSA decode at 128K context
+-- 32 sequences, each query at position 131072 over 32768 compressed entries
+(m=4) with fp8 indexer keys, top-1024 selection, then sparse MQA (128 heads x
+512) over the selection plus the 128-token raw window and the sinks.  One step
+= indexer_topk + sparse_mqa_fwd for the batch, inputs resident in HBM, and
+the CPU oracle timed beside it on a bounded sample.
 
-Decode steps cycle through several copies of the caches so that the 256 MiB
-Infinity Cache cannot hold a step's working set between steps.
+With --extras all (the default) every other workload is measured too and
+reported under "workloads" (same fields, no CPU baseline):
+  csa_decode_1m, hca_decode_1m (dense_compressed_mqa_fwd only),
+  prefill_chunk_256k (CSA + HCA layers of an 8192-token chunk after a
+    262,144-token prefix: the chunk's compressions and preparations, the
+    indexer, sparse attention, dense attention),
+  flash_csa_decode_128k, flash_hca_decode_1m (64 heads, top-512),
+  stream_decode_128k (the per-token decode step: kv_append of the new
+    token into the CSA, indexer-key and HCA state, then indexer and both
+    attention calls reading the window rings),
+  compress_variants_256k (kv_compress_ex: spans of 8 at m = 4 with
+    per-channel gates over a 262,144-token prefix),
+  backward_csa_decode_128k (training: mqa_bwd + indexer_bwd at the CSA 128K
+    decode shapes).
+Decode caches and window rows hold prepared keys (kv_prepare runs once per
+entry or token, when it is written).  Decode steps cycle through several
+copies of the caches so that the 256 MiB Infinity Cache cannot hold a
+step's working set between steps.
 
-Prints one JSON line: the metric, the roofline of the dominant kernel (its
-launches timed with HIP events recorded by the library around that kernel,
-inside the timed region, less the latency of an empty event pair), a per-call
-breakdown from a separate untimed pass, and the CPU-oracle baseline.  --gpus N with N > 1 is
-not supported: this build runs on one GPU.
+Each workload reports its roofline: the dominant kernel's launches timed
+with HIP events recorded by the library around that kernel inside the timed
+region (less the latency of an empty event pair; the raw figure and, when a
+committed rocprofv3 summary of the same sources exists, its mean duration
+are listed beside it), the whole step's roofline fraction, and a per-call
+breakdown from a separate untimed pass.  --gpus N with N > 1 is not
+supported: this build runs on one GPU.
 """
 from __future__ import annotations
 
@@ -42,6 +55,7 @@ from compressed_attention_kv_amd.gen import make_inputs  # noqa: E402
 METRIC = "CSA/HCA query-tokens/s at 128K-1M ctx; % of HBM BW and MFMA peak"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFS = 2500.0
+FP32_VALU_PEAK_TFS = 157.3
 CACHE_BYTES = 256 << 20
 
 
@@ -101,6 +115,9 @@ class Step:
                             "mqa_combine_kernel": (2 * w.H * w.D * 2 * nq, 0)}
             self.calls = {"dense_compressed_mqa_fwd": (b_a * nq, f_a * nq)}
         self.bound = "hbm"
+        self.launches = {}
+        self.n_tokens = nq
+        self.unit = "query-tokens/s"
         # enough copies of the caches that one step's data is evicted from the
         # Infinity Cache before the copy is used again
         self.copies = max(1, math.ceil(3 * CACHE_BYTES / step_bytes))
@@ -191,6 +208,9 @@ class Step:
         self.calls = {"kv_compress x3, kv_prepare x3": (0, 0), "indexer_topk": (b_score, f_score),
                       "sparse_mqa_fwd": (b_attn, f_csa), "dense_compressed_mqa_fwd": (0, f_hca)}
         self.bound = "mfma"
+        self.launches = {"mqa_fwd_kernel": 2}
+        self.n_tokens = Q
+        self.unit = "query-tokens/s"
 
     # ------------------------------------------------------------ one step
     def run(self, ev=None):
@@ -208,13 +228,13 @@ class Step:
                 ev[1].record()
             cakv.sparse_mqa_fwd(self.q, self.kv[c], self.idx, self.kv_raw, self.raw_pos0, self.q_pos, self.sinks,
                                 want_lse=False, out=self.out, workspace=self.ws_attn, **self.kw)
-        else:
             if ev is not None:
-                ev[1].record()
+                ev[2].record()
+        else:
             cakv.dense_compressed_mqa_fwd(self.q, self.kv[c], self.kv_raw, self.raw_pos0, self.q_pos, self.sinks,
                                           want_lse=False, out=self.out, workspace=self.ws_attn, **self.kw)
-        if ev is not None:
-            ev[2].record()
+            if ev is not None:
+                ev[1].record()
 
     def _run_prefill(self, ev):
         w, P = self.w, self.P
@@ -245,14 +265,11 @@ class Step:
 
     @property
     def n_events(self) -> int:
-        return 5 if self.prefill else 3
+        return len(self.calls) + 1
 
     def call_ms(self, evs):
         """Mean duration of each call of the step over the event-timed steps."""
-        names = list(self.calls)
-        if not self.prefill and not self.sparse:
-            return {names[0]: float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))}
-        return {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+        return {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(self.calls)}
 
     # ------------------------------------------------------------ oracle
     def cpu_baseline(self, max_queries: int, min_seconds: float):
@@ -320,6 +337,268 @@ class Step:
                 "seconds": round(dt, 3)}
 
 
+class StreamStep:
+    """The streaming decode step of a CSA layer and an HCA layer for 32
+    sequences at 128K context (NEXT to the whole-batch calls: one new token
+    per sequence per step).  Per step: kv_append of the token's KV into the
+    CSA cache and window ring, of its indexer key into the fp8 key cache, of
+    its KV into the HCA cache and window ring (a block completes every 4
+    tokens for CSA, every 128 for HCA), then indexer_topk, sparse_mqa_fwd and
+    dense_compressed_mqa_fwd reading the window rings.  The prefix (131,072
+    tokens: 32,768 CSA entries, 1,024 HCA entries) is built at set-up.  Three
+    independent copies of the state are cycled (each advances one position
+    every third step), so a step's caches are not Infinity-Cache resident."""
+
+    name = "stream_decode_128k"
+    prefill = False
+    bound = "hbm"
+
+    def __init__(self, copies: int = 3):
+        inp = make_inputs("csa_decode_128k")
+        w = self.w = inp["workload"]
+        dev = "cuda"
+        B, D, m, mh, t0 = w.B, w.D, w.m, w.m_hca, w.t
+        self.copies = copies
+        self.t = [t0] * copies
+        self.max_steps = 1 << 14
+        N = t0 // m + self.max_steps // m + 2
+        Nh = t0 // mh + self.max_steps // mh + 2
+        g = torch.Generator(device="cpu").manual_seed(11)
+        prep = self.prep = dict(rope_dims=w.rope_dims, rope_base=w.rope_base, entry_pos_offset=0, rms_eps=w.rms_eps)
+        self.state = []
+        kf = inp["k_idx"].to(dev)
+        codes, scale = cakv.kv_compress(kf, torch.zeros(kf.shape[:2], dtype=torch.float32, device=dev), 1,
+                                        out_dtype=torch.float8_e4m3fn)
+        del kf
+        hca_prefix = torch.randn(B, t0 // mh, D, generator=g).to(torch.bfloat16)
+        for c in range(copies):
+            st = {}
+            st["kv"] = torch.zeros(B, N, D, dtype=torch.bfloat16, device=dev)
+            st["kv"][:, : t0 // m] = inp["kv"].to(dev)
+            cakv.kv_prepare(st["kv"], m=m, n=t0 // m, **prep)
+            st["kh"] = torch.zeros(B, Nh, D, dtype=torch.bfloat16, device=dev)
+            st["kh"][:, : t0 // mh] = hca_prefix.to(dev)
+            cakv.kv_prepare(st["kh"], m=mh, n=t0 // mh, **prep)
+            st["kc"] = torch.zeros(B, N, w.dI, dtype=torch.uint8, device=dev).view(torch.float8_e4m3fn)
+            st["ks"] = torch.zeros(B, N, dtype=torch.float32, device=dev)
+            st["kc"][:, : t0 // m] = codes
+            st["ks"][:, : t0 // m] = scale
+            # rings: raw tokens and gates of the last 128 positions, window rows prepared at them
+            raw = torch.randn(B, 128, D, generator=g).to(torch.bfloat16).to(dev)
+            st["raw_c"], st["raw_h"] = raw.clone(), raw.clone()
+            st["graw_c"] = torch.randn(B, 128, generator=g).to(dev)
+            st["graw_h"] = torch.randn(B, 128, generator=g).to(dev)
+            st["kraw"] = torch.randn(B, 8, w.dI, generator=g).to(torch.bfloat16).to(dev)
+            st["kgraw"] = torch.randn(B, 8, generator=g).to(dev)
+            win = torch.empty_like(raw)
+            p = torch.arange(t0 - 128, t0, device=dev)
+            win[:, p % 128] = cakv.kv_prepare(raw[:, p % 128].contiguous(), m=1, entry_pos_offset=t0 - 128,
+                                              rope_dims=w.rope_dims, rope_base=w.rope_base)
+            st["win_c"], st["win_h"] = win.clone(), win.clone()
+            self.state.append(st)
+        # the new tokens: a pool cycled over the steps
+        P = 64
+        self.tok = torch.randn(P, B, D, generator=g).to(torch.bfloat16).to(dev)
+        self.ktok = torch.randn(P, B, w.dI, generator=g).to(torch.bfloat16).to(dev)
+        self.gtok = torch.randn(P, 3, B, generator=g).to(dev)
+        self.q = inp["q"].to(dev)
+        self.qh = inp["q"].to(dev).flip(2).contiguous()  # the HCA layer's query heads
+        self.q_idx = inp["q_idx"].to(dev)
+        self.wts = inp["w"].to(dev)
+        self.sinks = inp["sinks"].to(dev)
+        self.idx = torch.empty((B, 1, w.k), dtype=torch.int32, device=dev)
+        self.ws_idx = torch.empty(cakv.indexer_topk_workspace_bytes(B, 1, N, w.k), dtype=torch.uint8, device=dev)
+        self.ws_a = torch.empty(max(cakv.sparse_mqa_workspace_bytes(B, 1, w.H, D, w.k, w.n_win), 1),
+                                dtype=torch.uint8, device=dev)
+        self.ws_h = torch.empty(max(cakv.dense_mqa_workspace_bytes(B, 1, w.H, D, Nh, w.n_win), 1),
+                                dtype=torch.uint8, device=dev)
+        self.out = torch.empty((B, 1, w.H, D), dtype=torch.bfloat16, device=dev)
+        self.out_h = torch.empty_like(self.out)
+        # positions of every step, one row per step (no fill kernel inside a step)
+        self.pos_table = (t0 + torch.arange(self.max_steps, dtype=torch.int32, device=dev))[:, None].repeat(1, B)
+        self.P = P
+        self.i = 0
+        nv, nvh = t0 // m, t0 // mh
+        b_s, f_s = _indexer_score(w, nv)
+        b_a, f_a = _attention(w, w.k + w.n_win, True)
+        b_h, f_h = _attention(w, nvh + w.n_win, False)
+        b_app = 3 * D * 2 + 2 * D * 2 + w.dI * 2 + 3 * 4  # token rows in, ring and window rows out
+        self.kernels = {"idx_score_fp8_kernel": (b_s * B, f_s * B), "mqa_fwd_kernel#0": (b_a * B, f_a * B),
+                        "mqa_fwd_kernel#1": (b_h * B, f_h * B), "kv_append_kernel#0": (b_app * B, 0)}
+        self.launches = {"mqa_fwd_kernel": 2, "kv_append_kernel": 3}
+        self.calls = {"kv_append x3": (b_app * B, 0), "indexer_topk": (b_s * B, f_s * B),
+                      "sparse_mqa_fwd (ring window)": (b_a * B, f_a * B),
+                      "dense_compressed_mqa_fwd (ring window)": (b_h * B, f_h * B)}
+        self.n_tokens = B
+        self.unit = "query-tokens/s"
+        self.config = {"workload": self.name, "batch": B, "context": t0, "m": m, "m_hca": mh, "heads": w.H,
+                       "head_dim": D, "topk": w.k, "window": w.n_win, "state_copies_cycled": copies,
+                       "step": "kv_append x3 + indexer_topk + sparse_mqa_fwd + dense_compressed_mqa_fwd"}
+
+    @property
+    def n_events(self) -> int:
+        return len(self.calls) + 1
+
+    def call_ms(self, evs):
+        return {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(self.calls)}
+
+    def run(self, ev=None):
+        c = self.i % self.copies
+        j = (self.i // self.copies) % self.P
+        self.i += 1
+        st, w = self.state[c], self.w
+        if self.t[c] - w.t >= self.max_steps - 1:  # stay inside the allocated caches
+            self.t[c] = w.t
+        pos = self.pos_table[self.t[c] - w.t]
+        self.t[c] += 1
+        kw = dict(n_win=w.n_win, rope_dims=w.rope_dims, rope_base=w.rope_base)
+        if ev is not None:
+            ev[0].record()
+        tok = self.tok[j]
+        cakv.kv_append(tok, self.gtok[j, 0], pos, st["raw_c"], st["graw_c"], st["kv"], m=w.m, win_ring=st["win_c"],
+                       prep=self.prep)
+        cakv.kv_append(self.ktok[j], self.gtok[j, 1], pos, st["kraw"], st["kgraw"], st["kc"], m=w.m,
+                       cache_scale=st["ks"])
+        cakv.kv_append(tok, self.gtok[j, 2], pos, st["raw_h"], st["graw_h"], st["kh"], m=w.m_hca,
+                       win_ring=st["win_h"], prep=self.prep)
+        if ev is not None:
+            ev[1].record()
+        qpos = pos.view(-1, 1)
+        cakv.indexer_topk(self.q_idx, self.wts, st["kc"], st["ks"], qpos, w.m, w.k, out=self.idx,
+                          workspace=self.ws_idx)
+        if ev is not None:
+            ev[2].record()
+        cakv.sparse_mqa_fwd(self.q, st["kv"], self.idx, st["win_c"], None, qpos, self.sinks, m=w.m, raw_ring=True,
+                            want_lse=False, out=self.out, workspace=self.ws_a, **kw)
+        if ev is not None:
+            ev[3].record()
+        cakv.dense_compressed_mqa_fwd(self.qh, st["kh"], st["win_h"], None, qpos, self.sinks, m=w.m_hca,
+                                      raw_ring=True, want_lse=False, out=self.out_h, workspace=self.ws_h, **kw)
+        if ev is not None:
+            ev[4].record()
+
+
+class CompressStep:
+    """The compressor variants on a 262,144-token prefix: overlapping spans of
+    8 tokens at m = 4 with one gate logit per token and channel (bf16 KV
+    [1, 262144, 512], float32 gates [1, 262144, 512] ~N(0,1), seed 7), bf16
+    entries.  One step = one kv_compress_ex call (65,536 entries)."""
+
+    name = "compress_variants_256k"
+    prefill = False
+    bound = "hbm"
+
+    def __init__(self):
+        dev = "cuda"
+        T, D, self.m, self.span = 262144, 512, 4, 8
+        rng = np.random.Generator(np.random.PCG64(7))
+        self.x = torch.from_numpy(rng.standard_normal((1, T, D), dtype=np.float32)).to(torch.bfloat16).to(dev)
+        self.g = torch.from_numpy(rng.standard_normal((1, T, D), dtype=np.float32)).to(dev)
+        self.out = torch.empty((1, T // self.m, D), dtype=torch.bfloat16, device=dev)
+        b = T * D * 2 + T * D * 4 + (T // self.m) * D * 2  # tokens, gates, entries, each once
+        self.kernels = {"kv_compress_kernel": (b, 0)}
+        self.launches = {"kv_compress_kernel": 1}
+        self.calls = {"kv_compress_ex": (b, 0)}
+        self.copies = 1
+        self.n_tokens = T
+        self.unit = "tokens/s"
+        self.config = {"workload": self.name, "tokens": T, "head_dim": D, "m": self.m, "span": self.span,
+                       "gates": "per token and channel", "out": "bf16"}
+
+    @property
+    def n_events(self) -> int:
+        return 2
+
+    def call_ms(self, evs):
+        return {"kv_compress_ex": float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))}
+
+    def run(self, ev=None):
+        if ev is not None:
+            ev[0].record()
+        cakv.kv_compress_ex(self.x, self.g, self.m, self.span, out=self.out)
+        if ev is not None:
+            ev[1].record()
+
+
+class BackwardStep:
+    """The training backward of a CSA layer at the 128K decode shapes (32
+    queries, 128 heads x 512, 1,024 selected entries + a 128-token window,
+    64 indexer heads x 128 over the selection): mqa_bwd (dq, the prepared
+    key rows' and the sinks' gradients) and indexer_bwd.  Forward output, lse
+    and selection come from one forward pass at set-up; dout and dS are
+    ~N(0,1).  The gradient buffers accumulate across steps (as a gradient
+    accumulation would)."""
+
+    name = "backward_csa_decode_128k"
+    prefill = False
+    bound = "mfma"
+
+    def __init__(self):
+        inp = make_inputs("csa_decode_128k")
+        w = self.w = inp["workload"]
+        dev = "cuda"
+        B, Q, H, D = w.B, w.Q, w.H, w.D
+        kf = inp["k_idx"].to(dev)
+        self.codes, self.kscale = cakv.kv_compress(kf, torch.zeros(kf.shape[:2], dtype=torch.float32, device=dev),
+                                                   1, out_dtype=torch.float8_e4m3fn)
+        del kf
+        self.kv = cakv.kv_prepare(inp["kv"].to(dev), m=w.m, rope_dims=w.rope_dims, rope_base=w.rope_base)
+        self.kv_raw = cakv.kv_prepare_raw(inp["kv_raw"].to(dev), inp["raw_pos0"].tolist(), rope_dims=w.rope_dims,
+                                          rope_base=w.rope_base)
+        self.q, self.q_idx, self.wts = inp["q"].to(dev), inp["q_idx"].to(dev), inp["w"].to(dev)
+        self.raw_pos0, self.q_pos, self.sinks = inp["raw_pos0"].to(dev), inp["q_pos"].to(dev), inp["sinks"].to(dev)
+        self.kw = dict(m=w.m, n_win=w.n_win, rope_dims=w.rope_dims, rope_base=w.rope_base)
+        self.idx = cakv.indexer_topk(self.q_idx, self.wts, self.codes, self.kscale, self.q_pos, w.m, w.k)
+        self.out, self.lse = cakv.sparse_mqa_fwd(self.q, self.kv, self.idx, self.kv_raw, self.raw_pos0, self.q_pos,
+                                                 self.sinks, **self.kw)
+        g = torch.Generator(device="cpu").manual_seed(13)
+        self.dout = torch.randn(B, Q, H, D, generator=g).to(dev)
+        self.dS = torch.randn(B, Q, w.k, generator=g).to(dev)
+        self.dkv = torch.zeros(B, w.N, D, dtype=torch.float32, device=dev)
+        self.draw = torch.zeros(B, w.n_win, D, dtype=torch.float32, device=dev)
+        self.dsinks = torch.zeros(H, dtype=torch.float32, device=dev)
+        self.dk = torch.zeros(B, w.N, w.dI, dtype=torch.float32, device=dev)
+        self.ws = torch.empty(cakv.load_library().cakv_mqa_bwd_workspace(B, Q, H, D, w.k, w.n_win),
+                              dtype=torch.uint8, device=dev)
+        nq, rows = B * Q, w.k + w.n_win
+        # algorithmic work: attention 10 H D flops per key (S, dP, dq, and the two dK products), the key rows
+        # read and their gradients written once, q / out / dout / dq; indexer 6 HI dI flops per selected entry
+        f_att = 10 * H * D * rows * nq
+        b_att = (rows * D * 2 + rows * D * 4 + 4 * H * D * 4) * nq
+        f_idx = 6 * w.HI * w.dI * w.k * nq
+        b_idx = (w.k * (w.dI + 4) + w.k * w.dI * 4 + w.k * 8 + 2 * w.HI * w.dI * 4) * nq
+        self.kernels = {"bwd_logits_kernel": (0, 4 * H * D * rows * nq), "bwd_dkeys_kernel": (0, 4 * H * D * rows * nq),
+                        "bwd_dquery_kernel": (0, 2 * H * D * rows * nq), "indexer_bwd_kernel": (b_idx, f_idx)}
+        self.kernel_bound = {"indexer_bwd_kernel": "alu"}  # fp32 VALU (the canonical-order score)
+        self.launches = {}
+        self.calls = {"mqa_bwd": (b_att, f_att), "indexer_bwd": (b_idx, f_idx)}
+        self.copies = 1
+        self.n_tokens = nq
+        self.unit = "query-tokens/s"
+        self.config = {"workload": self.name, "batch": nq, "context": w.t, "heads": H, "head_dim": D, "topk": w.k,
+                       "window": w.n_win, "indexer_heads": w.HI, "step": "mqa_bwd + indexer_bwd"}
+
+    @property
+    def n_events(self) -> int:
+        return 3
+
+    def call_ms(self, evs):
+        return {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(self.calls)}
+
+    def run(self, ev=None):
+        if ev is not None:
+            ev[0].record()
+        cakv.mqa_bwd(self.q, self.kv, self.idx, self.kv_raw, self.raw_pos0, self.q_pos, self.sinks, self.out,
+                     self.lse, self.dout, dkv_c=self.dkv, dkv_raw=self.draw, dsinks=self.dsinks, workspace=self.ws,
+                     **self.kw)
+        if ev is not None:
+            ev[1].record()
+        cakv.indexer_bwd(self.q_idx, self.wts, self.codes, self.kscale, self.q_pos, self.idx, self.dS, self.w.m,
+                         dk=self.dk)
+        if ev is not None:
+            ev[2].record()
+
+
 def _repeat_for(fn, min_seconds: float):
     """Runs fn until at least min_seconds have passed (at least once);
     returns (passes, seconds)."""
@@ -349,18 +628,17 @@ def copy_calibration(mib: int):
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
-def _kernel_launches(st: Step, kernel: str, steps: int):
-    """(name, occurrence) of a kernel table entry: 'mqa_fwd_kernel#1' is the
-    second launch of mqa_fwd_kernel in a step."""
+def _kernel_launches(st, kernel: str):
+    """(name, occurrence, launches per step) of a kernel table entry:
+    'mqa_fwd_kernel#1' is the second launch of mqa_fwd_kernel in a step."""
     name, _, occ = kernel.partition("#")
-    per_step = 2 if (st.prefill and name == "mqa_fwd_kernel") else 1
-    return name, int(occ or 0), per_step
+    return name, int(occ or 0), getattr(st, "launches", {}).get(name, 1)
 
 
 def _time_kernel(st: Step, kernel: str, steps: int, run_steps):
     """Mean duration (ms) of one kernel's launches over `steps` steps, from
     event pairs the library records around them."""
-    name, occ, per_step = _kernel_launches(st, kernel, steps)
+    name, occ, per_step = _kernel_launches(st, kernel)
     n = steps * per_step
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -395,62 +673,42 @@ def _source_digest() -> str:
     return h.hexdigest()
 
 
-def _profiled_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary of
-    this workload (profiles/<workload>_kernels.md), or None when there is no
-    summary for it or the library sources changed since it was taken."""
+def _profiled(workload: str, kernel: str, key: str):
+    """A figure of `kernel` from the committed summary of this workload
+    (profiles/<workload>_kernels.md): the line '<key>: kernel=... value=...
+    source_sha256=...' taken while the library sources hashed to the same
+    digest as now, else None."""
     f = os.path.join(ROOT, "profiles", f"{workload}_kernels.md")
     if not os.path.exists(f):
         return None
     digest = _source_digest()
     for line in open(f):
-        if line.startswith("traffic:"):
-            kv = dict(t.split("=", 1) for t in line.split()[1:])
+        if line.startswith(key + ":"):
+            kv = dict(t.split("=", 1) for t in line.split()[1:] if "=" in t)
             if kv.get("kernel") == kernel and kv.get("source_sha256") == digest:
-                return int(kv["bytes_per_launch"])
+                return float(kv["value"])
     return None
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 50; 5 for the prefill chunk)")
-    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 5; 2 for the prefill chunk)")
-    ap.add_argument("--workload", default="csa_decode_128k",
-                    choices=["csa_decode_128k", "csa_decode_1m", "hca_decode_1m", "prefill_chunk_256k",
-                             "flash_csa_decode_128k", "flash_hca_decode_1m"])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-queries", type=int, default=32)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="the oracle baseline repeats its sample until this much host time has passed")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only run a plain device-to-device copy of MIB MiB five times (HBM counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-    torch.cuda.init()
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-    prefill = args.workload.startswith("prefill")
-    steps = args.steps if args.steps is not None else (5 if prefill else 50)
-    warmup = args.warmup if args.warmup is not None else (2 if prefill else 5)
-    st = Step(args.workload)
-    w = st.w
+PEAKS = {"hbm": (HBM_PEAK_GBS, "GB/s"), "mfma": (BF16_PEAK_TFS, "TFLOP/s"), "alu": (FP32_VALU_PEAK_TFS, "TFLOP/s")}
+
+
+def measure(st, steps: int, warmup: int) -> dict:
+    """Times `steps` steps of a workload (three windows, the median one
+    reported) and the roofline of its dominant kernel."""
     for _ in range(warmup):
         st.run()
     torch.cuda.synchronize()
-
     pair_ms = _event_pair_ms()
     # the dominant kernel: the longest of the step's main kernels on a short
     # probe; kernels within 10 % of the longest count as a tie, which goes to
-    # the one with the most algorithmic work (bytes at decode, flops at
-    # prefill), so that timing noise cannot flip the choice
+    # the one with the most algorithmic work (bytes when HBM-bound, flops
+    # otherwise), so that timing noise cannot flip the choice
     probe = {k: _time_kernel(st, k, 4, lambda: [st.run() for _ in range(4)]) for k in st.kernels}
     top = max(probe.values())
-    dom = max((k for k in probe if probe[k] >= 0.9 * top), key=lambda k: st.kernels[k][1 if st.prefill else 0])
-    dom_name, _, per_step = _kernel_launches(st, dom, steps)
+    dom = max((k for k in probe if probe[k] >= 0.9 * top), key=lambda k: st.kernels[k][0 if st.bound == "hbm" else 1])
+    dom_name, occ, per_step = _kernel_launches(st, dom)
+    bound = getattr(st, "kernel_bound", {}).get(dom_name, st.bound)
 
     # per-call breakdown: an untimed pass with HIP events around each call
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(st.n_events)] for _ in range(steps)]
@@ -463,7 +721,6 @@ def main():
     # windows run back to back and the median one is reported (all three are
     # listed): a host-side stall outside the kernels then cannot stand for
     # the path's throughput.
-    _, occ, _ = _kernel_launches(st, dom, steps)
     windows = []
     for _ in range(3):
         ks = [torch.cuda.Event(enable_timing=True) for _ in range(steps * per_step)]
@@ -481,14 +738,22 @@ def main():
     wall, kms_raw = sorted(windows)[1]
     kms = kms_raw - pair_ms
     ms = wall * 1e3 / steps
-    nq = w.B * w.Q
-    value = nq / (ms * 1e-3)
+    value = st.n_tokens / (ms * 1e-3)
 
     bytes_, flops = st.kernels[dom]
-    if st.bound == "hbm":
-        achieved, peak, unit = bytes_ / (kms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
-    else:
-        achieved, peak, unit = flops / (kms * 1e-3) / 1e12, BF16_PEAK_TFS, "TFLOP/s"
+    peak, unit = PEAKS[bound]
+    work = bytes_ if bound == "hbm" else flops
+    scale = 1e9 if bound == "hbm" else 1e12
+    achieved = work / (kms * 1e-3) / scale
+    rp_us = _profiled(st.name, dom_name, "duration_us")
+    roof = {"kernel": dom, "bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4),
+            "traffic": (lambda v: None if v is None else int(v))(_profiled(st.name, dom_name, "traffic_bytes")),
+            "kernel_ms": round(kms, 4), "kernel_ms_events_raw": round(kms_raw, 4), "event_pair_ms": round(pair_ms, 4),
+            "frac_events_raw": round(work / (kms_raw * 1e-3) / scale / peak, 4), "launches_timed": steps}
+    if rp_us:
+        roof["kernel_ms_rocprof"] = round(rp_us * 1e-3, 4)
+        roof["frac_rocprof"] = round(work / (rp_us * 1e-6) / scale / peak, 4)
     cms = st.call_ms(evs)
     per_call = {}
     for c, (b, f) in st.calls.items():
@@ -504,32 +769,91 @@ def main():
         roof_ms = sum(b for b, _ in st.calls.values()) / (HBM_PEAK_GBS * 1e9) * 1e3
     else:
         roof_ms = sum(f for _, f in st.calls.values()) / (BF16_PEAK_TFS * 1e12) * 1e3
-    if prefill:
-        config = {"workload": w.name, "query_tokens": w.Q, "prefix_tokens": w.q_pos0, "m": w.m, "m_hca": w.m_hca,
-                  "heads": w.H, "head_dim": w.D, "topk": w.k, "window": w.n_win, "indexer_heads": w.HI,
-                  "layers": "CSA + HCA"}
+    return {"value": round(value, 1), "unit": st.unit, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
+            "config": st.config, "windows_ms_per_step": [round(wl * 1e3 / steps, 4) for wl, _ in windows],
+            "roofline": roof, "path_roofline_frac": round(roof_ms / ms, 4), "path_bound": st.bound,
+            "per_call": per_call, "kernel_probe_ms": {k: round(v, 4) for k, v in probe.items()}}
+
+
+FORWARD = ["csa_decode_128k", "csa_decode_1m", "hca_decode_1m", "prefill_chunk_256k", "flash_csa_decode_128k",
+           "flash_hca_decode_1m"]
+EXTRA = {"stream_decode_128k": StreamStep, "compress_variants_256k": CompressStep,
+         "backward_csa_decode_128k": BackwardStep}
+HEADLINE = "csa_decode_128k"
+
+
+def make_step(name: str):
+    if name in EXTRA:
+        return EXTRA[name]()
+    st = Step(name)
+    st.name = name
+    w = st.w
+    if st.prefill:
+        st.config = {"workload": w.name, "query_tokens": w.Q, "prefix_tokens": w.q_pos0, "m": w.m, "m_hca": w.m_hca,
+                     "heads": w.H, "head_dim": w.D, "topk": w.k, "window": w.n_win, "indexer_heads": w.HI,
+                     "layers": "CSA + HCA"}
     else:
-        config = {"workload": w.name, "batch": nq, "context": w.t, "compressed_entries": w.N, "m": w.m,
-                  "heads": w.H, "head_dim": w.D, "topk": w.k if st.sparse else None, "window": w.n_win,
-                  "indexer_heads": w.HI if st.sparse else None, "cache_copies_cycled": st.copies}
-    rec = {
-        "metric": METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
-        "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "dtype_detail": "bf16 MFMA with fp32 accumulation (indexer: fp8 keys decoded exactly to bf16)",
-        "data": "synthetic", "config": config,
-        "windows_ms_per_step": [round(wl * 1e3 / steps, 4) for wl, _ in windows],
-        "roofline": {"kernel": dom, "bound": st.bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": _profiled_traffic(w.name, dom),
-                     "kernel_ms": round(kms, 4), "kernel_ms_events_raw": round(kms_raw, 4),
-                     "event_pair_ms": round(pair_ms, 4), "launches_timed": steps},
-        "path_roofline_frac": round(roof_ms / ms, 4),
-        "per_call": per_call,
-        "kernel_probe_ms": {k: round(v, 4) for k, v in probe.items()},
-    }
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = st.cpu_baseline(args.cpu_queries if not prefill else min(args.cpu_queries, 8), args.cpu_seconds)
-    print(json.dumps(rec), flush=True)
+        st.config = {"workload": w.name, "batch": w.B * w.Q, "context": w.t, "compressed_entries": w.N, "m": w.m,
+                     "heads": w.H, "head_dim": w.D, "topk": w.k if st.sparse else None, "window": w.n_win,
+                     "indexer_heads": w.HI if st.sparse else None, "cache_copies_cycled": st.copies}
+    return st
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 50; 5 for the prefill chunk)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 5; 2 for the prefill chunk)")
+    ap.add_argument("--workload", default=HEADLINE, choices=FORWARD + list(EXTRA),
+                    help="the workload of the line's top-level figures")
+    ap.add_argument("--extras", default="all", choices=["all", "none"],
+                    help="also measure every other workload (reported under 'workloads', no CPU baseline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-queries", type=int, default=32)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="the oracle baseline repeats its sample until this much host time has passed")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.init()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    def counts(name):
+        prefill = name.startswith("prefill")
+        return (args.steps if args.steps is not None else (5 if prefill else 50),
+                args.warmup if args.warmup is not None else (2 if prefill else 5))
+
+    steps, warmup = counts(args.workload)
+    st = make_step(args.workload)
+    rec = measure(st, steps, warmup)
+    line = {"metric": METRIC, "value": rec.pop("value"), "unit": rec.pop("unit"), "n_gpus": 1,
+            "steps": rec.pop("steps"), "warmup": rec.pop("warmup"), "ms_per_step": rec.pop("ms_per_step"),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "dtype_detail": "bf16 MFMA with fp32 accumulation (indexer: fp8 keys decoded exactly to bf16)",
+            "data": "synthetic", "config": rec.pop("config")}
+    line.update(rec)
+    if not args.no_cpu_baseline and hasattr(st, "cpu_baseline"):
+        q = args.cpu_queries if not st.prefill else min(args.cpu_queries, 8)
+        line["cpu_baseline"] = st.cpu_baseline(q, args.cpu_seconds)
+    del st
+    torch.cuda.empty_cache()
+    if args.extras == "all":
+        line["workloads"] = {}
+        for name in FORWARD + list(EXTRA):
+            if name == args.workload:
+                continue
+            s2, w2 = counts(name)
+            print(f"# measuring {name}", file=sys.stderr, flush=True)
+            st = make_step(name)
+            line["workloads"][name] = measure(st, s2, w2)
+            del st
+            torch.cuda.empty_cache()
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

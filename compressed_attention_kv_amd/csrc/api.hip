@@ -534,6 +534,10 @@ int cakv_mqa_bwd(const cakv_attn_params* p, const void* q, const void* kv_c, con
     w.f.n_splits = attn_splits(BQ, max_slots);
     w.out = out;
     w.out_f32 = out_dtype == CAKV_F32;
+    // one query per sequence: the selected entries of a query are distinct
+    // (a precondition) and sequences share no rows, so every key row is
+    // touched by one workgroup only
+    w.unique_rows = Q == 1;
     w.lse = lse;
     w.dout = dout;
     w.dq = dq;
@@ -610,12 +614,12 @@ int cakv_indexer_bwd(const void* q_idx, int q_dtype, const float* w, const void*
     const bool f32 = q_dtype == CAKV_F32 && k_dtype == CAKV_F32;
     const bool fp8 = q_dtype == CAKV_BF16 && k_dtype == CAKV_FP8_E4M3;
     REQUIRE(f32 || fp8, CAKV_EUNSUPPORTED, "dtypes: (F32 q, F32 k) or (BF16 q, FP8_E4M3 k)");
-    REQUIRE(HI >= 1 && HI <= 64 && dI >= 4 && dI <= 256 && dI % 4 == 0 && HI * dI <= 8192, CAKV_EUNSUPPORTED,
-            "HI <= 64, dI a multiple of 4 up to 256, HI*dI <= 8192 (HI=%d dI=%d)", HI, dI);
+    REQUIRE(HI >= 1 && HI <= 64 && dI >= 8 && dI <= 128 && dI % 8 == 0, CAKV_EUNSUPPORTED,
+            "HI <= 64, dI a multiple of 8 up to 128 (HI=%d dI=%d)", HI, dI);
     REQUIRE(fp8 == (k_scale != nullptr), CAKV_EINVAL, "k_scale is required for FP8_E4M3 keys and NULL otherwise");
     const int64_t BQ = B * Q;
     if (BQ == 0) return ok();
-    REQUIRE(BQ <= 0x7fffffffLL, CAKV_EUNSUPPORTED, "B*Q too large");
+    REQUIRE(BQ < (1LL << 23), CAKV_EUNSUPPORTED, "B*Q=%lld must be below 2^23", (long long)BQ);
     REQUIRE_PTR(q_idx, "q_idx");
     REQUIRE_PTR(w, "w");
     REQUIRE_PTR(q_pos, "q_pos");

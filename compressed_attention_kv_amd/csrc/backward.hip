@@ -19,7 +19,9 @@
 //       dkeys   (same grid, 8 waves of 64 output dims): dK = [tau dl^T |
 //               P^T] [Q_hat ; dO] on MFMA, the [Q_hat ; dO] operand held in
 //               VGPRs for the split, added into the key rows' gradient with
-//               float atomics (rows can be shared by queries);
+//               float atomics (rows can be shared by the queries of one
+//               sequence), or plain adds with one query per sequence, where
+//               no two workgroups touch the same row;
 //       dquery  (same grid): dq_hat = dl K as the forward's P V product
 //               (dl in the A-operand layout, K read transposed from LDS);
 //       finish  (one wave per query and head): the splits' sum, the
@@ -27,12 +29,17 @@
 //   * kv_prepare: one wave per row (rotation by -position, RMSNorm).
 //   * the compressor (spans, per-channel gates): entry statistics, then one
 //     workgroup per token summing over the entries whose span holds it.
-//   * the indexer score over the selected entries: one workgroup per query;
-//     the ReLU decisions use the forward's canonical fp32 dot product.
+//   * the indexer score over the selected entries: one workgroup per query
+//     and 128 selected slots; the ReLU decisions use the forward's canonical
+//     fp32 dot product (register-tiled fmaf chains), the two products that
+//     follow (dq, dk) run on fp32 MFMA.
 //
 // Key rows are staged in LDS exactly as the forward stages them (1 KiB
 // rows padded to 1,088 bytes, 16-byte granule g of row r at g ^ ((r >> 2) & 3)),
 // so the same operand reads apply; tiles are double-buffered.
+#include <algorithm>
+#include <type_traits>
+
 #include "cakv_attn_common.hpp"
 #include "cakv_rows.hpp"
 
@@ -333,13 +340,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
         // element r of tile dt: key 8 (r/4) + 4 lh + r%4, dim 64 w + 32 dt + lrow
+        if (w.unique_rows) {
+            // no other workgroup touches these rows: a plain read-modify-write,
+            // every load issued before the first add (empty slots skipped)
+            float old[16][NT];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = 8 * (r >> 2) + 4 * lh + (r & 3);
-            float* gr = reinterpret_cast<float*>(gptr[key]);
-            if (gr) {
+            for (int r = 0; r < 16; ++r) {
+                float* gr = reinterpret_cast<float*>(gptr[8 * (r >> 2) + 4 * lh + (r & 3)]);
 #pragma unroll
-                for (int dt = 0; dt < NT; ++dt) unsafeAtomicAdd(gr + 64 * wave + 32 * dt + lrow, acc[dt][r]);
+                for (int dt = 0; dt < NT; ++dt) old[r][dt] = gr ? gr[64 * wave + 32 * dt + lrow] : 0.0f;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float* gr = reinterpret_cast<float*>(gptr[8 * (r >> 2) + 4 * lh + (r & 3)]);
+                if (gr) {
+#pragma unroll
+                    for (int dt = 0; dt < NT; ++dt) gr[64 * wave + 32 * dt + lrow] = old[r][dt] + acc[dt][r];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float* gr = reinterpret_cast<float*>(gptr[8 * (r >> 2) + 4 * lh + (r & 3)]);
+                if (gr) {
+#pragma unroll
+                    for (int dt = 0; dt < NT; ++dt) unsafeAtomicAdd(gr + 64 * wave + 32 * dt + lrow, acc[dt][r]);
+                }
             }
         }
         barrier_lds();  // gptr is rewritten for the next tile
@@ -620,94 +646,257 @@ __global__ __launch_bounds__(256) void kv_compress_bwd_kernel(const TIn* x, cons
 }
 
 // ---------------------------------------------------------------- indexer
-// One workgroup per query; chunks of 32 selected entries.  The score's ReLU
-// decision is the forward's canonical fp32 dot (head dim ascending from +0).
+// Workgroup = (query, 128 selected slots), four waves; q (64 x 128), the 128
+// key rows and the coefficients coef[j][h] = dS_j w_h [s_jh > 0] sit in LDS
+// as fp32 (zero beyond HI, dI and for empty slots).
+//  1. scores: thread (slot group sg = lane % 32, head group hg = 2 wave +
+//     lane / 32) holds the 4 x 8 scores of slots sg + 32 i and heads hg + 8 u,
+//     each an fmaf chain in the canonical order (head dim ascending from +0),
+//     16-byte LDS reads reused across the tile; decisions, coef and the dw
+//     partials (summed over the 32 lanes of a head group) follow.
+//  2. dq (heads x dims) = coef^T K and 3. dk (slots x dims) = coef Q are dense
+//     fp32 contractions on v_mfma_f32_32x32x2f32: wave w owns dims 32 w .. +31
+//     of dq and slots 32 w .. +31 of dk.
+// dq and dw are sums over the workgroups of a query (float atomics into
+// zeroed outputs), dk over queries (float atomics, accumulated); each atomic
+// instruction covers 32 consecutive floats of two rows.
+constexpr int kIBS = 128;  // slots per workgroup
+
+__global__ __launch_bounds__(256) void indexer_bwd_zero_kernel(float* dq, int64_t nq, float* dw, int64_t nw) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nq; i += (int64_t)gridDim.x * 256) {
+        dq[i] = 0.0f;
+        if (i < nw) dw[i] = 0.0f;
+    }
+}
+
 template <typename TQ, bool FP8>
 __global__ __launch_bounds__(256) void indexer_bwd_kernel(const IndexerBwdArgs a) {
-    __shared__ float qs[8192];   // [HI][dI]
-    __shared__ float ks[32 * 257];  // [32][dI + 1]: rows padded against bank conflicts
-    __shared__ float coef[64 * 32];  // [HI][32]: dS_j w_h [s > 0]
-    __shared__ float rl[64 * 32];    // [HI][32]: ReLU(s)
-    __shared__ float dsv[32];
-    __shared__ int32_t js[32];
+    constexpr int QST = 128;  // q[h][d] row stride (floats)
+    constexpr int KST = 132;  // k[slot][d] row stride: 16-byte rows, 4-bank shift per row
+    constexpr int CST = 65;   // coef[slot][h] row stride: 1-bank shift per row
+    __shared__ __attribute__((aligned(16))) float qs[64 * QST];
+    __shared__ __attribute__((aligned(16))) float ks[kIBS * KST];
+    __shared__ float coef[kIBS * CST];
+    __shared__ float dsv[kIBS];
+    __shared__ float wsv[64];
+    __shared__ float dwsum[64];
+    __shared__ int32_t ents[kIBS];
     const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
     const int64_t bq = blockIdx.x;
     const int64_t b = bq / a.Q;
-    const int HI = a.HI, dI = a.dI, NE = HI * dI, KST = dI + 1;
-    int32_t t = a.q_pos[bq];
+    const int HI = a.HI, dI = a.dI, NE = HI * dI;
+    const int s0 = blockIdx.y * kIBS;
+    const int32_t t = a.q_pos[bq];
     const int64_t nv = t < 0 ? 0 : ((int64_t)t / a.m < a.N ? (int64_t)t / a.m : a.N);
-    for (int e = tid; e < NE; e += 256) {
-        if constexpr (sizeof(TQ) == 4) qs[e] = reinterpret_cast<const float*>(a.q_idx)[bq * NE + e];
-        else qs[e] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.q_idx)[bq * NE + e]);
-    }
-    constexpr int PER = 32;  // dq elements per thread (HI * dI <= 8192)
-    float dq[PER];
+    // staging, every global load of a round issued before its first LDS store:
+    // round 1 the selection, dS, w and q (16-byte chunks, each inside one head
+    // row since dI is a multiple of 8); round 2 the key rows
+    {
+        constexpr int QE = 16 / sizeof(TQ);          // q elements per chunk
+        constexpr int QCH = 64 * 128 / QE / 256;     // chunks per thread at HI = 64, dI = 128
+        const int nch = NE / QE;
+        u32x4 qc[QCH];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) dq[k] = 0.0f;
-    float dw = 0.0f;
-    __syncthreads();
-    for (int s0 = 0; s0 < a.K; s0 += 32) {
-        if (tid < 32) {
-            const int s = s0 + tid;
-            int32_t j = s < a.K ? a.idx[bq * a.K + s] : -1;
-            if (j < 0 || j >= nv) j = -1;
-            js[tid] = j;
-            dsv[tid] = (j >= 0) ? a.dS[bq * a.K + s] : 0.0f;
+        for (int i = 0; i < QCH; ++i) {
+            const int c = tid + 256 * i;
+            qc[i] = c < nch ? reinterpret_cast<const u32x4*>(a.q_idx)[(bq * NE) / QE + c] : u32x4{0u, 0u, 0u, 0u};
         }
-        __syncthreads();
-        for (int e = tid; e < 32 * dI; e += 256) {
-            const int r = e / dI, d = e % dI;
-            const int32_t j = js[r];
-            float v = 0.0f;
-            if (j >= 0) {
-                if constexpr (FP8) {
-                    const uint8_t c = reinterpret_cast<const uint8_t*>(a.k_idx)[(b * a.N + j) * dI + d];
-                    v = e4m3_decode_f32(c) * a.k_scale[b * a.N + j];
+        int32_t e = -1;
+        float g = 0.0f, wv = 0.0f;
+        const int s = s0 + tid;
+        if (tid < kIBS && s < a.K) {
+            e = a.idx[bq * a.K + s];
+            g = a.dS[bq * a.K + s];
+        }
+        if (tid >= kIBS && tid < kIBS + 64 && tid - kIBS < HI) wv = a.w[bq * HI + tid - kIBS];
+        if (tid < kIBS) {
+            if (e < 0 || e >= nv) e = -1;
+            ents[tid] = e;
+            dsv[tid] = e >= 0 ? g : 0.0f;
+        } else if (tid < kIBS + 64) {
+            wsv[tid - kIBS] = wv;
+        }
+#pragma unroll
+        for (int i = 0; i < QCH; ++i) {
+            const int c = tid + 256 * i;
+            if (c < nch) {
+                const int h = (c * QE) / dI, d = (c * QE) % dI;
+                float* dst = &qs[h * QST + d];
+                if constexpr (QE == 4) {
+                    *reinterpret_cast<f32x4*>(dst) = __builtin_bit_cast(f32x4, qc[i]);
                 } else {
-                    v = reinterpret_cast<const float*>(a.k_idx)[(b * a.N + j) * dI + d];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        dst[2 * k] = __builtin_bit_cast(float, qc[i][k] << 16);
+                        dst[2 * k + 1] = __builtin_bit_cast(float, qc[i][k] & 0xffff0000u);
+                    }
                 }
             }
-            ks[r * KST + d] = v;
         }
-        __syncthreads();
-        for (int e = tid; e < HI * 32; e += 256) {
-            const int h = e / 32, r = e % 32;
-            float sh = 0.0f;
-            for (int d = 0; d < dI; ++d) sh = __builtin_fmaf(qs[h * dI + d], ks[r * KST + d], sh);
-            const bool pos = js[r] >= 0 && sh > 0.0f;
-            coef[e] = pos ? dsv[r] * a.w[bq * HI + h] : 0.0f;
-            rl[e] = pos ? sh : 0.0f;
+        // zero padding (disjoint from the chunks above)
+        if (HI < 64 || dI < 128) {
+            for (int x = tid; x < 64 * QST; x += 256)
+                if (x / QST >= HI || x % QST >= dI) qs[x] = 0.0f;
         }
-        __syncthreads();
-        if (tid < HI) {
-            for (int r = 0; r < 32; ++r) dw = __builtin_fmaf(dsv[r], rl[tid * 32 + r], dw);
-        }
+    }
+    __syncthreads();
+    {
+        constexpr int KCH = kIBS * 16 / 256;  // 8-element chunks of the 128 (padded) dims per thread
+        using KV = typename std::conditional<FP8, u32x2, u32x4>::type;
+        KV lo[KCH], hi[KCH];
+        float sc[KCH];
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int e = tid + 256 * k;
-            if (e < NE) {
-                const int h = e / dI, d = e % dI;
-                float acc = dq[k];
-                for (int r = 0; r < 32; ++r) acc = __builtin_fmaf(coef[h * 32 + r], ks[r * KST + d], acc);
-                dq[k] = acc;
+        for (int i = 0; i < KCH; ++i) {
+            const int c = tid + 256 * i, r = c >> 4, d = (c & 15) * 8;
+            const int32_t e = ents[r];
+            lo[i] = KV{};
+            hi[i] = KV{};
+            sc[i] = 0.0f;
+            if (d < dI && e >= 0) {
+                const int64_t row = b * a.N + e;
+                if constexpr (FP8) {
+                    lo[i] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(a.k_idx) + row * dI + d);
+                    sc[i] = a.k_scale[row];
+                } else {
+                    const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(a.k_idx) + row * dI + d);
+                    lo[i] = src[0];
+                    hi[i] = src[1];
+                }
             }
         }
-        for (int e = tid; e < 32 * dI; e += 256) {
-            const int r = e / dI, d = e % dI;
-            const int32_t j = js[r];
-            if (j < 0) continue;
-            float acc = 0.0f;
-            for (int h = 0; h < HI; ++h) acc = __builtin_fmaf(coef[h * 32 + r], qs[h * dI + d], acc);
-            if (acc != 0.0f) unsafeAtomicAdd(a.dk + (b * a.N + j) * dI + d, acc);
-        }
-        __syncthreads();
-    }
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int e = tid + 256 * k;
-        if (e < NE) a.dq[bq * NE + e] = dq[k];
+        for (int i = 0; i < KCH; ++i) {
+            const int c = tid + 256 * i, r = c >> 4, d = (c & 15) * 8;
+            float v[8];
+            if constexpr (FP8) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v[k] = e4m3_decode_f32((lo[i][k >> 2] >> (8 * (k & 3))) & 0xffu) * sc[i];
+            } else {  // whole-vector casts (a cast of one vector element would read element 0)
+                const f32x4 fl = __builtin_bit_cast(f32x4, lo[i]), fh = __builtin_bit_cast(f32x4, hi[i]);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    v[k] = fl[k];
+                    v[4 + k] = fh[k];
+                }
+            }
+            *reinterpret_cast<f32x4*>(&ks[r * KST + d]) = f32x4{v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<f32x4*>(&ks[r * KST + d + 4]) = f32x4{v[4], v[5], v[6], v[7]};
+        }
     }
-    if (tid < HI) a.dw[bq * HI + tid] = dw;
+    __syncthreads();
+    // 1. scores, decisions, coef, dw
+    {
+        const int sg = l32, hg = 2 * wave + lh;
+        float acc[4][8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[i][u] = 0.0f;
+        for (int d = 0; d < dI; d += 4) {
+            f32x4 k4[4], q4[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) k4[i] = *reinterpret_cast<const f32x4*>(&ks[(sg + 32 * i) * KST + d]);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) q4[u] = *reinterpret_cast<const f32x4*>(&qs[(hg + 8 * u) * QST + d]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) acc[i][u] = __builtin_fmaf(q4[u][c], k4[i][c], acc[i][u]);
+        }
+        float dwp[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) dwp[u] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = sg + 32 * i;
+            const float g = dsv[r];
+            const bool live = ents[r] >= 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int h = hg + 8 * u;
+                const bool pos = live && h < HI && acc[i][u] > 0.0f;
+                coef[r * CST + h] = pos ? g * wsv[h] : 0.0f;
+                dwp[u] += pos ? g * acc[i][u] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float v = group_sum<32>(dwp[u]);
+            if (l32 == 0) dwsum[hg + 8 * u] = v;
+        }
+    }
+    __syncthreads();
+    // 2. dq[h][d] = sum_j coef[j][h] k[j][d]: A = coef^T (heads x slots), B = K;
+    // operands of 16 k-steps read into registers ahead of their MFMAs
+    const auto dq_tiles = [&](auto two_tiles) {
+        constexpr bool TWO = decltype(two_tiles)::value;
+        constexpr int BS = 16;
+        f32x16 c0 = {}, c1 = {};
+#pragma unroll
+        for (int blk = 0; blk < kIBS / (2 * BS); ++blk) {
+            float av0[BS], av1[BS], bv[BS];
+#pragma unroll
+            for (int u = 0; u < BS; ++u) {
+                const int r = 2 * (blk * BS + u) + lh;
+                bv[u] = ks[r * KST + 32 * wave + l32];
+                av0[u] = coef[r * CST + l32];
+                if constexpr (TWO) av1[u] = coef[r * CST + 32 + l32];
+            }
+#pragma unroll
+            for (int u = 0; u < BS; ++u) {
+                c0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av0[u], bv[u], c0, 0, 0, 0);
+                if constexpr (TWO) c1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av1[u], bv[u], c1, 0, 0, 0);
+            }
+        }
+        const int d = 32 * wave + l32;
+        if (d < dI) {
+            float* dq = a.dq + bq * NE + d;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int h = 8 * (i >> 2) + 4 * lh + (i & 3);
+                if (h < HI && c0[i] != 0.0f) unsafeAtomicAdd(dq + h * dI, c0[i]);
+                if constexpr (TWO)
+                    if (h + 32 < HI && c1[i] != 0.0f) unsafeAtomicAdd(dq + (h + 32) * dI, c1[i]);
+            }
+        }
+    };
+    if (32 * wave < dI) {
+        if (HI > 32) dq_tiles(std::true_type{});
+        else dq_tiles(std::false_type{});
+    }
+    // 3. dk[j][d] = sum_h coef[j][h] q[h][d]: A = coef (slots x heads), B = Q;
+    // blocks of 16 heads (zero beyond HI), all four 32-dim tiles (zero beyond dI)
+    {
+        f32x16 c[4] = {};
+        const int nblk = (HI + 15) / 16;
+        for (int blk = 0; blk < nblk; ++blk) {
+            float av[8], bv[8][4];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int h = 16 * blk + 2 * u + lh;
+                av[u] = coef[(32 * wave + l32) * CST + h];
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) bv[u][dt] = qs[h * QST + 32 * dt + l32];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) c[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u], bv[u][dt], c[dt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int32_t e = ents[32 * wave + 8 * (i >> 2) + 4 * lh + (i & 3)];
+            if (e < 0) continue;
+            float* dk = a.dk + (b * a.N + e) * dI + l32;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                if (32 * dt + l32 < dI && c[dt][i] != 0.0f) unsafeAtomicAdd(dk + 32 * dt, c[dt][i]);
+        }
+    }
+    if (tid < HI && dwsum[tid] != 0.0f) unsafeAtomicAdd(a.dw + bq * HI + tid, dwsum[tid]);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -824,13 +1013,20 @@ int launch_kv_compress_bwd(const void* x, int x_dtype, const float* gate, bool p
 
 int launch_indexer_bwd(const IndexerBwdArgs& a, int64_t BQ, bool q_f32, bool fp8, hipStream_t stream) {
     if (BQ == 0) return 0;
+    if (a.dI > 128 || a.HI > 64) return -2;
+    const int64_t nq = BQ * a.HI * a.dI, nw = BQ * a.HI;
+    // nw <= nq: the zero kernel's loop covers both
+    hipLaunchKernelGGL(indexer_bwd_zero_kernel, dim3((unsigned)std::min<int64_t>((nq + 255) / 256, 8192)), dim3(256),
+                       0, stream, a.dq, nq, a.dw, nw);
+    if (a.K == 0) return hipGetLastError() == hipSuccess ? 0 : -4;
+    const dim3 grid((unsigned)BQ, (unsigned)((a.K + kIBS - 1) / kIBS));
     prof_mark("indexer_bwd_kernel", false, stream);
     if (q_f32) {
-        if (fp8) hipLaunchKernelGGL((indexer_bwd_kernel<float, true>), dim3((unsigned)BQ), dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((indexer_bwd_kernel<float, false>), dim3((unsigned)BQ), dim3(256), 0, stream, a);
+        if (fp8) hipLaunchKernelGGL((indexer_bwd_kernel<float, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((indexer_bwd_kernel<float, false>), grid, dim3(256), 0, stream, a);
     } else {
-        if (fp8) hipLaunchKernelGGL((indexer_bwd_kernel<bf16_t, true>), dim3((unsigned)BQ), dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((indexer_bwd_kernel<bf16_t, false>), dim3((unsigned)BQ), dim3(256), 0, stream, a);
+        if (fp8) hipLaunchKernelGGL((indexer_bwd_kernel<bf16_t, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((indexer_bwd_kernel<bf16_t, false>), grid, dim3(256), 0, stream, a);
     }
     prof_mark("indexer_bwd_kernel", true, stream);
     return hipGetLastError() == hipSuccess ? 0 : -4;

@@ -152,6 +152,7 @@ struct BwdArgs {
     uint16_t* dl;       // [BQ][HP][S] bf16 dl (head-major)
     float* dqp;         // [BQ][splits][HP][D] partial dq_hat / tau
     int32_t out_f32;
+    int32_t unique_rows;  // 1: one query per sequence (no row is touched by two workgroups)
     int32_t HP;         // heads rounded up to 32
     int32_t S;          // key slots per query, rounded up to 32
     float tau;          // softmax scale

@@ -367,8 +367,9 @@ int cakv_dense_compressed_mqa_fwd(const cakv_attn_params* p, const void* q, cons
  * sparse attention is trained from 64K context on, after a short warm-up of
  * the Lightning Indexer].  The gradients of the calls above.  Buffers named
  * "accumulated" receive += (the caller zeroes them); all others are
- * overwritten.  Float atomics add the contributions of different queries
- * and heads, so accumulated results may differ in the last bits run to run.
+ * overwritten.  Where float atomics add the contributions of different
+ * workgroups (stated per call), results may differ in the last bits run to
+ * run.
  * ======================================================================== */
 
 /* ---------------------------------------------------------------------------
@@ -388,6 +389,10 @@ int cakv_dense_compressed_mqa_fwd(const cakv_attn_params* p, const void* q, cons
  *   dsinks   [H] float32 accumulated, or NULL; dgamma_q [D] accumulated or NULL
  * Supported: CAKV_BF16 activations with D = 512, 1 <= H <= 128,
  * B*Q <= 65535; other parameters as the forward (ring mode included).
+ * The selected entries of a query must be distinct (as for the forward):
+ * with Q = 1 every key row is then touched by one workgroup only, and its
+ * gradient is added without atomics (bitwise deterministic); with Q > 1
+ * rows shared by a sequence's queries are added with float atomics.
  * Workspace: cakv_mqa_bwd_workspace(B, Q, H, D, n_keys, n_win) bytes with
  * n_keys = K (sparse) or N (dense), 256-byte aligned.
  * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE.
@@ -439,7 +444,7 @@ int cakv_kv_compress_bwd(const void* x, int x_dtype, const float* gate, int gate
  * (head dim ascending from +0 in fmaf, fp8 keys decoded exactly), whatever
  * the mode.  dq_idx [B,Q,HI,dI] and dw [B,Q,HI] float32 overwritten; dk
  * [B,N,dI] float32 accumulated.  Modes and dtypes as cakv_indexer_topk;
- * HI <= 64, dI a multiple of 4 up to 256, HI*dI <= 8192, K <= 65536.
+ * HI <= 64, dI a multiple of 8 up to 128, K <= 65536, B*Q < 2^23.
  * ------------------------------------------------------------------------- */
 int cakv_indexer_bwd(const void* q_idx, int q_dtype, const float* w, const void* k_idx, int k_dtype,
                      const float* k_scale, const int32_t* q_pos, const int32_t* idx, const float* dS, int64_t B,

@@ -180,16 +180,26 @@ def test_kv_compress_backward(m, span, per_channel, dtype):
         assert np.all(np.abs(got - ref) <= bound)
 
 
+# (B, Q, HI, dI, N, K): the V4 indexer shape, then ragged ones (odd head
+# counts, head dims that fill part of a 32-wide tile, a partial last block of
+# 128 slots, a query before the first entry)
+INDEXER_BWD_SHAPES = [(2, 3, 64, 128, 3000, 512), (2, 2, 5, 24, 700, 300), (1, 3, 33, 72, 500, 130)]
+
+
+@pytest.mark.parametrize("shape", INDEXER_BWD_SHAPES, ids=["v4", "ragged_small", "ragged_mid"])
 @pytest.mark.parametrize("mode", ["f32", "fp8"])
-def test_indexer_backward(mode):
-    say(f"indexer backward {mode}")
+def test_indexer_backward(mode, shape):
+    say(f"indexer backward {mode} {shape}")
     rng = np.random.default_rng(42)
-    B, Q, HI, dI, N, K, m = 2, 3, 64, 128, 3000, 512, 4
+    B, Q, HI, dI, N, K = shape
+    m = 4
     q = rng.standard_normal((B, Q, HI, dI)).astype(np.float32)
     w = rng.standard_normal((B, Q, HI)).astype(np.float32)
     keys = rng.standard_normal((B, N, dI)).astype(np.float32)
     qpos = np.full((B, Q), 4 * N, dtype=np.int32)
-    qpos[0, 1] = 4 * 1000  # fewer visible entries
+    qpos[0, 1] = 4 * (N // 3)  # fewer visible entries
+    if shape != INDEXER_BWD_SHAPES[0]:
+        qpos[-1, 0] = -1  # no visible entry: zero gradients
     idx = np.stack([np.stack([rng.permutation(N)[:K] for _ in range(Q)]) for _ in range(B)]).astype(np.int32)
     idx[:, :, ::11] = -1
     dS = rng.standard_normal((B, Q, K)).astype(np.float32)
@@ -215,7 +225,7 @@ def test_indexer_backward(mode):
         for i in range(Q):
             nv = min(int(qpos[b, i]) // m, N)
             sel = [(s, j) for s, j in enumerate(idx[b, i]) if 0 <= j < nv]
-            js = np.array([j for _, j in sel])
+            js = np.array([j for _, j in sel], dtype=np.int64)
             ds = np.abs(np.array([dS[b, i, s] for s, _ in sel], dtype=np.float64))
             extra[b, i] = dI * U * (np.abs(qf[b, i]).astype(np.float64) @ np.abs(kf[b, js]).T.astype(np.float64)) @ ds
     for what, g_, r_, a_, ex in (("dq", got[0], ref[0], absr[0], 0.0), ("dw", got[1], ref[1], absr[1], extra),

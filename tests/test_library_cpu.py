@@ -345,7 +345,8 @@ def test_kv_prepare_bwd_and_compress_bwd_errors(lib):
     assert g(None, cakv.BF16, None, 0, 0, 64, 512, 4, 4, None, None, None, None, 0, None) == 0
 
 
-@pytest.mark.parametrize("kw,code", [(dict(), 0), (dict(HI=65), -2), (dict(dI=260), -2), (dict(dI=130), -2),
+@pytest.mark.parametrize("kw,code", [(dict(), 0), (dict(HI=65), -2), (dict(dI=136), -2), (dict(dI=132), -2),
+                                     (dict(dI=64), 0), (dict(dI=20), -2),
                                      (dict(qdt=cakv.F32), -2), (dict(ks=None), -1), (dict(K=65537), -2)])
 def test_indexer_bwd_limits(lib, kw, code):
     a = dict(qdt=cakv.BF16, kdt=cakv.FP8_E4M3, ks=FAKE, HI=64, dI=128, K=1024)
@@ -354,3 +355,13 @@ def test_indexer_bwd_limits(lib, kw, code):
     rc = lib.cakv_indexer_bwd(None, a["qdt"], None, None, a["kdt"], a["ks"], None, None, None, 0, 1, 64, a["HI"],
                               a["dI"], 4, a["K"], None, None, None, None)
     assert rc == code
+
+
+def test_indexer_bwd_batch_limit(lib):
+    # one workgroup column per query: B*Q must stay below 2^23 (checked before any pointer)
+    rc = lib.cakv_indexer_bwd(None, cakv.BF16, None, None, cakv.FP8_E4M3, FAKE, None, None, None, 1 << 23, 1, 64, 64,
+                              128, 4, 1024, None, None, None, None)
+    assert rc == -2
+    rc = lib.cakv_indexer_bwd(None, cakv.BF16, None, None, cakv.FP8_E4M3, FAKE, None, None, None, (1 << 23) - 1, 1,
+                              64, 64, 128, 4, 1024, None, None, None, None)
+    assert rc == -1  # within the limit: the NULL q_idx is the first error
