@@ -16,7 +16,16 @@ import torch
 
 import oracle
 
-torch.set_default_dtype(torch.float64)
+
+
+@pytest.fixture(autouse=True)
+def _fp64_default():
+    """fp64 tensors by default inside these tests only (restored afterwards, so
+    other test modules collected in the same process keep torch's default)"""
+    prev = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(prev)
 
 
 def _rope_t(x, pos, r, base=10000.0):
