@@ -47,6 +47,46 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def asan_runtime() -> str:
+    """Path of the ROCm clang's shared ASan runtime (to preload into a host
+    process that loads a sanitized library)."""
+    r = subprocess.run([os.path.join(os.path.dirname(HIPCC), "..", "llvm", "bin", "clang"),
+                        "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isfile(path):
+        raise RuntimeError("clang's shared ASan runtime was not found")
+    return path
+
+
+def build_sanitized(out_dir: str) -> str:
+    """A copy of libcakv.so whose host code in api.hip (argument validation,
+    workspace sizing, launch geometry, the static-scratch lookup) is built
+    with AddressSanitizer and UndefinedBehaviorSanitizer; the device code is
+    not instrumented (the sanitizer flags reach the host pass only), and the
+    other sources' objects come from the regular build.  Returns its path."""
+    objdir = os.path.join(HERE, "_build")
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "api.hip"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise FileNotFoundError("regular build objects missing: " + ", ".join(missing))
+    host_san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+    api_obj = os.path.join(out_dir, "api_sanitized.o")
+    flags = [f if f != "-O3" else "-O1" for f in FLAGS]
+    cmd = [HIPCC, *flags, "-g", *host_san, "-c", os.path.join(CSRC, "api.hip"), "-o", api_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for the sanitized api.hip:\n" + r.stdout + r.stderr)
+    lib = os.path.join(out_dir, "libcakv_sanitized.so")
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", api_obj, *objs,
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-shared-libasan", "-o", lib]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed for the sanitized library:\n" + r.stdout + r.stderr)
+    return lib
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

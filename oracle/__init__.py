@@ -33,6 +33,18 @@ def build(force: bool = True) -> str:
     return _SO
 
 
+def build_sanitized(out_dir: str) -> str:
+    """A copy of the oracle built with AddressSanitizer and
+    UndefinedBehaviorSanitizer (same arithmetic flags); returns its path.  A
+    process loads it with CAKV_ORACLE_LIBRARY set to that path and gcc's
+    libasan preloaded."""
+    so = os.path.join(out_dir, "libcakv_oracle_sanitized.so")
+    flags = [f for f in GCC_FLAGS if f != "-O2"] + ["-O1", "-g", "-fno-omit-frame-pointer",
+                                                    "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+    subprocess.run(["gcc", *flags, _SRC, "-o", so, "-lm"], check=True)
+    return so
+
+
 _lib = None
 _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
@@ -47,8 +59,11 @@ class AttnParams(ctypes.Structure):
 def _load():
     global _lib
     if _lib is None:
-        build(force=False)
-        lib = ctypes.CDLL(_SO)
+        path = os.environ.get("CAKV_ORACLE_LIBRARY")  # another build of the same source (sanitizer runs)
+        if not path:
+            build(force=False)
+            path = _SO
+        lib = ctypes.CDLL(path)
         lib.oracle_kv_compress.argtypes = [_p, ctypes.c_int, _p, _i64, _i64, _i64, ctypes.c_int, _p]
         lib.oracle_kv_compress_ex.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int,
                                               ctypes.c_int, _p]

@@ -20,7 +20,9 @@ def _declared_functions():
 
 @pytest.fixture(scope="module")
 def lib():
-    return cakv.load_library()
+    # CAKV_TEST_LIBRARY: run these checks against another build of the same
+    # sources (the sanitizer test uses it); the first load is the one cached
+    return cakv.load_library(os.environ.get("CAKV_TEST_LIBRARY", cakv.LIB_PATH))
 
 
 def test_exports_every_declared_symbol(lib):
