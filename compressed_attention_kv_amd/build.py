@@ -10,6 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libcakv.so")
+DEBUG_LIB = os.path.join(HERE, "libcakv_debug.so")  # beside libcakv.so: both ship with the tree
 SOURCES = ["api.hip", "kv_compress.hip", "kv_prepare.hip", "decode.hip", "indexer.hip", "attention.hip", "backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -20,9 +21,9 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-I" + os.path.join(ROOT, "include")]
 
 
-def _compile(src: str, objdir: str) -> str:
+def _compile(src: str, objdir: str, extra=()) -> str:
     obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in ln]
     if r.returncode != 0:
@@ -30,21 +31,26 @@ def _compile(src: str, objdir: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libcakv.so; returns its path."""
-    objdir = os.path.join(HERE, "_build")
+def build(verbose: bool = False, debug: bool = False) -> str:
+    """Compile every source and link libcakv.so; returns its path.  With
+    debug=True, the debug build instead: the same sources with the kernels'
+    device-side index checks compiled in (-DCAKV_DEBUG), as libcakv_debug.so
+    (objects in _build/debug/)."""
+    objdir = os.path.join(HERE, "_build", "debug") if debug else os.path.join(HERE, "_build")
+    out = DEBUG_LIB if debug else LIB
     os.makedirs(objdir, exist_ok=True)
+    extra = ["-DCAKV_DEBUG"] if debug else []
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, objdir), SOURCES))
-    tmp = LIB + f".tmp{os.getpid()}"
+        objs = list(ex.map(lambda s: _compile(s, objdir, extra), SOURCES))
+    tmp = out + f".tmp{os.getpid()}"
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out)
+    return out
 
 
 def asan_runtime() -> str:
@@ -88,5 +94,5 @@ def build_sanitized(out_dir: str) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, debug="--debug" in sys.argv[1:])
     sys.exit(0)

@@ -248,6 +248,7 @@ void mqa_fwd_kernel(const AttnArgs a) {
     const int tps = (n_tiles + a.n_splits - 1) / a.n_splits;
     const int tile0 = split * tps;
     const int tile1 = min(n_tiles, tile0 + tps);
+    CAKV_DCHECK(bq < (int64_t)gridDim.x * gridDim.y && split < a.n_splits);
     // a row of this query that always exists: the source of loads for empty slots
     const uint8_t* spare_row = reinterpret_cast<const uint8_t*>(a.q) + bq * (int64_t)H * RB;
 

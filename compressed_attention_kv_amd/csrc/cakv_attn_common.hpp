@@ -79,7 +79,9 @@ __device__ __forceinline__ const TIn* slot_row(const AttnArgs& a, const QueryGeo
 __device__ __forceinline__ int64_t xcd_order(int64_t lin, int64_t total) {
     const int64_t q = total >> 3, rem = total & 7;
     const int64_t x = lin & 7, r = lin >> 3;
-    return x < rem ? x * (q + 1) + r : rem * (q + 1) + (x - rem) * q + r;
+    const int64_t o = x < rem ? x * (q + 1) + r : rem * (q + 1) + (x - rem) * q + r;
+    CAKV_DCHECK(o >= 0 && o < total);
+    return o;
 }
 
 }  // namespace cakv

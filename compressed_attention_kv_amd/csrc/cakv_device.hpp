@@ -9,6 +9,22 @@
 
 namespace cakv {
 
+// Device-side checks of the kernels' own index invariants, compiled in only
+// with -DCAKV_DEBUG (the debug build): a failed check prints its condition
+// and traps.  In the regular build they cost nothing.
+#ifdef CAKV_DEBUG
+#define CAKV_DCHECK(cond)                                                                        \
+    do {                                                                                         \
+        if (!(cond)) {                                                                           \
+            printf("CAKV_DCHECK failed: %s at %s:%d (block %d)\n", #cond, __FILE__, __LINE__,    \
+                   (int)blockIdx.x);                                                             \
+            __builtin_trap();                                                                    \
+        }                                                                                        \
+    } while (0)
+#else
+#define CAKV_DCHECK(cond) ((void)0)
+#endif
+
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

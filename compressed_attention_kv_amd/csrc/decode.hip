@@ -50,6 +50,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const AppendArgs a) {
 
     if (complete) {
         const int64_t hi = (int64_t)t + 1, lo = hi - a.span > 0 ? hi - a.span : 0;
+        CAKV_DCHECK(hi - lo <= a.Rr && D <= 4096);  // the span fits the ring, the entry the LDS row
         const T* raw = reinterpret_cast<const T*>(a.raw_ring) + b * a.Rr * (int64_t)D;
         const float* gr = a.gate_ring + b * a.Rr * (PC ? (int64_t)D : 1);
         const float* gt = a.gate_tok + b * (PC ? (int64_t)D : 1);

@@ -682,7 +682,10 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(const IndexerAr
         const int words = (int)((nvis + 31) / 32);
         for (int i = tid; i < words; i += NT) bits[i] = 0u;
         __syncthreads();
-        for (int i = tid; i < k; i += NT) atomicOr(&bits[win[i] >> 5], 1u << (win[i] & 31));
+        for (int i = tid; i < k; i += NT) {
+            CAKV_DCHECK(win[i] < (uint32_t)nvis);
+            atomicOr(&bits[win[i] >> 5], 1u << (win[i] & 31));
+        }
         __syncthreads();
         // each thread owns a contiguous run of words
         const int per = (words + NT - 1) / NT;
@@ -691,6 +694,7 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(const IndexerAr
         for (int i = w0; i < w1; ++i) c += __builtin_popcount(bits[i]);
         uint32_t tot;
         uint32_t pos = block_excl_scan<NT>(c, wsum, &tot);
+        CAKV_DCHECK(tot == (uint32_t)k);  // k distinct winners
         for (int i = w0; i < w1; ++i) {
             uint32_t bw = bits[i];
             while (bw) {

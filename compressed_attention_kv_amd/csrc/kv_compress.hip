@@ -135,6 +135,7 @@ __global__ __launch_bounds__(256) void kv_compress_run_kernel(const TIn* __restr
     const int64_t b = r / runs_per_seq;
     const int64_t j0 = (r % runs_per_seq) * RUN;
     const int64_t j1 = j0 + RUN < nblk ? j0 + RUN : nblk;
+    CAKV_DCHECK(j0 < nblk);
     const TIn* xb = x + b * T * (int64_t)D + 4 * c;
     const float* gb = PC ? gate + b * T * (int64_t)D + 4 * c : gate + b * T;
     // window slot s holds token (j+1) M - SPAN + s of entry j
