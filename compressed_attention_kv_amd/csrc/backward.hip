@@ -9,9 +9,10 @@
 //     P = exp(l - lse) from the forward's lse, delta = do . o:
 //         dl = P (do . k - delta),  dsink = -P_sink delta,
 //         dq_hat = tau dl K,        dK += tau dl^T Q_hat + P^T dO,
-//     then dq through RoPE_t's transpose and q's RMSNorm.  Five launches:
-//       prep    (one wave per query and head): q_hat and do (bf16, rows and
-//               transposed), delta, the sink gradient;
+//     then dq through RoPE_t's transpose and q's RMSNorm.  Four launches:
+//       prep    (one wave per query and head, 16 heads per workgroup):
+//               q_hat and do (bf16, rows and, through LDS, transposed),
+//               delta, the sink gradient;
 //       logits  (one workgroup per query and key split, 4 waves of 32
 //               heads): S^T = K Q_hat^T and dP^T = K dO^T on
 //               v_mfma_f32_32x32x16_bf16 (one K read feeds both), then P
@@ -22,10 +23,11 @@
 //               float atomics (rows can be shared by the queries of one
 //               sequence), or plain adds with one query per sequence, where
 //               no two workgroups touch the same row;
-//       dquery  (same grid): dq_hat = dl K as the forward's P V product
-//               (dl in the A-operand layout, K read transposed from LDS);
-//       finish  (one wave per query and head): the splits' sum, the
-//               rotation's transpose and the RMSNorm gradient.
+//       dquery  (one workgroup per query and block of 32 heads, over all
+//               of the query's keys: no split partials): dq_hat = dl K as the
+//               forward's P V product (dl in the A-operand layout, K read
+//               transposed from LDS), then from LDS the rotation's transpose
+//               and the RMSNorm gradient.
 //   * kv_prepare: one wave per row (rotation by -position, RMSNorm).
 //   * the compressor (spans, per-channel gates): entry statistics, then one
 //     workgroup per token summing over the entries whose span holds it.
@@ -107,78 +109,102 @@ __device__ __forceinline__ uint32_t load_tile(const AttnArgs& a, const QueryGeom
 }  // namespace
 
 // ---------------------------------------------------------------- prep
-// One wave per (query, head); lane l owns channels 8l .. 8l+7.
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs w) {
+// One workgroup of 16 waves per (query, block of 16 heads), one head per
+// wave, lane l owning channels 8l .. 8l+7 of the head's rows.  The bf16 q_hat
+// and do rows are also staged in LDS, so that the transposed copies
+// ([D][HP]) leave as pairs of adjacent 16-byte stores (16 heads of one dim).
+constexpr int kPrepHeads = 16;
+__global__ __launch_bounds__(64 * kPrepHeads) void bwd_prep_kernel(const BwdArgs w) {
+    constexpr int RW = kBD + 8;  // LDS row stride (elements): 16-byte rows
+    __shared__ __attribute__((aligned(16))) uint16_t sq[kPrepHeads * RW];
+    __shared__ __attribute__((aligned(16))) uint16_t sd[kPrepHeads * RW];
     const AttnArgs& a = w.f;
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t bq = blockIdx.x;
-    const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
-    if (h >= w.HP) return;  // wave-uniform
+    const int h0 = kPrepHeads * blockIdx.y;  // grid.y = HP / 16
     const int H = a.H;
-    uint16_t* qt = w.qt + bq * (int64_t)kBD * w.HP;
-    uint16_t* dt = w.dot + bq * (int64_t)kBD * w.HP;
-    if (h >= H) {  // padding heads: zero columns of the transposed operands
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            qt[(8 * lane + i) * (int64_t)w.HP + h] = 0;
-            dt[(8 * lane + i) * (int64_t)w.HP + h] = 0;
-        }
-        return;
-    }
     int32_t t = a.q_pos[bq];
     t = t < 0 ? 0 : t;
-    const int64_t row = (bq * H + h) * (int64_t)kBD + 8 * lane;
-    float x[8], g8[8], d8[8], o8[8];
-    Chunk8<bf16_t>::load(reinterpret_cast<const bf16_t*>(a.q) + row, x);
-    float ss = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(x[i], x[i], ss);
-    ss = wave_sum(ss);
-    const float inv = 1.0f / __builtin_sqrtf(ss / (float)kBD + a.rms_eps);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) g8[i] = x[i] * inv * (a.gamma_q ? a.gamma_q[8 * lane + i] : 1.0f);
-    Chunk8<float>::load(w.dout + row, d8);
-    if (w.out_f32) Chunk8<float>::load(reinterpret_cast<const float*>(w.out) + row, o8);
-    else Chunk8<bf16_t>::load(reinterpret_cast<const bf16_t*>(w.out) + row, o8);
-    // q_hat = RoPE_t(q_n), do = RoPE_t(dout), o = RoPE_t(out): every rotated
-    // pair of this lane's chunk turns by +t
     const int rope_lo = kBD - a.rope_dims;
+    {
+        const int hl = wave, h = h0 + hl;
+        u32x4* lq = reinterpret_cast<u32x4*>(sq + hl * RW + 8 * lane);
+        u32x4* ld = reinterpret_cast<u32x4*>(sd + hl * RW + 8 * lane);
+        const int64_t orow = (bq * w.HP + h) * (int64_t)kBD + 8 * lane;
+        if (h >= H) {  // padding head (wave-uniform): zero rows and transposed columns
+            *lq = u32x4{0u, 0u, 0u, 0u};
+            *ld = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(w.qh + orow) = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(w.doh + orow) = u32x4{0u, 0u, 0u, 0u};
+        } else {
+            const int64_t row = (bq * H + h) * (int64_t)kBD + 8 * lane;
+            float x[8], g8[8], d8[8], o8[8];
+            Chunk8<bf16_t>::load(reinterpret_cast<const bf16_t*>(a.q) + row, x);
+            Chunk8<float>::load(w.dout + row, d8);
+            if (w.out_f32) Chunk8<float>::load(reinterpret_cast<const float*>(w.out) + row, o8);
+            else Chunk8<bf16_t>::load(reinterpret_cast<const bf16_t*>(w.out) + row, o8);
+            float ss = 0.0f;
 #pragma unroll
-    for (int pi = 0; pi < 4; ++pi) {
-        const int d = 8 * lane + 2 * pi;
-        if (d < rope_lo) continue;
-        float sn, cs;
-        sincos_turns((double)t * rope_turns(a.rope_ratio, (d - rope_lo) >> 1), &sn, &cs);
-        float* v3[3] = {g8, d8, o8};
+            for (int k = 0; k < 8; ++k) ss = __builtin_fmaf(x[k], x[k], ss);
+            ss = wave_sum(ss);
+            const float inv = 1.0f / __builtin_sqrtf(ss / (float)kBD + a.rms_eps);
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            const float x0 = v3[k][2 * pi], x1 = v3[k][2 * pi + 1];
-            v3[k][2 * pi] = x0 * cs - x1 * sn;
-            v3[k][2 * pi + 1] = x0 * sn + x1 * cs;
+            for (int k = 0; k < 8; ++k) g8[k] = x[k] * inv * (a.gamma_q ? a.gamma_q[8 * lane + k] : 1.0f);
+            // q_hat = RoPE_t(q_n), do = RoPE_t(dout), o = RoPE_t(out): every rotated
+            // pair of this lane's chunk turns by +t
+#pragma unroll
+            for (int pi = 0; pi < 4; ++pi) {
+                const int d = 8 * lane + 2 * pi;
+                if (d < rope_lo) continue;
+                float sn, cs;
+                sincos_turns((double)t * rope_turns(a.rope_ratio, (d - rope_lo) >> 1), &sn, &cs);
+                float* v3[3] = {g8, d8, o8};
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {
+                    const float x0 = v3[k][2 * pi], x1 = v3[k][2 * pi + 1];
+                    v3[k][2 * pi] = x0 * cs - x1 * sn;
+                    v3[k][2 * pi + 1] = x0 * sn + x1 * cs;
+                }
+            }
+            float dl = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) dl = __builtin_fmaf(d8[k], o8[k], dl);
+            dl = wave_sum(dl);
+            u32x4 qw, dw4;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                qw[k] = pack_bf16x2(g8[2 * k], g8[2 * k + 1]);
+                dw4[k] = pack_bf16x2(d8[2 * k], d8[2 * k + 1]);
+            }
+            *reinterpret_cast<u32x4*>(w.qh + orow) = qw;
+            *reinterpret_cast<u32x4*>(w.doh + orow) = dw4;
+            *lq = qw;
+            *ld = dw4;
+            if (lane == 0) {
+                w.delta[bq * H + h] = dl;
+                const float z = a.sinks[h], lse = w.lse[bq * H + h];
+                if (z != -INFINITY && lse != -INFINITY && w.dsinks) unsafeAtomicAdd(w.dsinks + h, -expf(z - lse) * dl);
+            }
         }
     }
-    float dl = 0.0f;
+    __syncthreads();
+    // transposed copies: thread (dim d, part p) stores heads 8p .. 8p+7 of the
+    // block for dim d, 16 bytes (the two parts of a dim are adjacent threads)
+    uint16_t* qt = w.qt + bq * (int64_t)kBD * w.HP + h0;
+    uint16_t* dt = w.dot + bq * (int64_t)kBD * w.HP + h0;
+    const int part = threadIdx.x & 1;
+    static_assert(64 * kPrepHeads == 2 * kBD, "one thread per (dim, 8 heads)");
+    {
+        const int d = threadIdx.x >> 1;
+        u32x4 vq, vd;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dl = __builtin_fmaf(d8[i], o8[i], dl);
-    dl = wave_sum(dl);
-    const int64_t orow = (bq * w.HP + h) * (int64_t)kBD + 8 * lane;
-    u32x4 qw, dw4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        qw[i] = pack_bf16x2(g8[2 * i], g8[2 * i + 1]);
-        dw4[i] = pack_bf16x2(d8[2 * i], d8[2 * i + 1]);
-    }
-    *reinterpret_cast<u32x4*>(w.qh + orow) = qw;
-    *reinterpret_cast<u32x4*>(w.doh + orow) = dw4;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        qt[(8 * lane + i) * (int64_t)w.HP + h] = bf16_of(g8[i]);
-        dt[(8 * lane + i) * (int64_t)w.HP + h] = bf16_of(d8[i]);
-    }
-    if (lane == 0) {
-        w.delta[bq * H + h] = dl;
-        const float z = a.sinks[h], lse = w.lse[bq * H + h];
-        if (z != -INFINITY && lse != -INFINITY && w.dsinks) unsafeAtomicAdd(w.dsinks + h, -expf(z - lse) * dl);
+        for (int k = 0; k < 4; ++k) {
+            const int h = 8 * part + 2 * k;
+            vq[k] = (uint32_t)sq[h * RW + d] | ((uint32_t)sq[(h + 1) * RW + d] << 16);
+            vd[k] = (uint32_t)sd[h * RW + d] | ((uint32_t)sd[(h + 1) * RW + d] << 16);
+        }
+        *reinterpret_cast<u32x4*>(qt + d * (int64_t)w.HP + 8 * part) = vq;
+        *reinterpret_cast<u32x4*>(dt + d * (int64_t)w.HP + 8 * part) = vd;
     }
 }
 
@@ -373,143 +399,193 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------- dquery
-// dq_hat (without tau) = dl K per split: the forward's P V product with dl.
-template <bool SPARSE>
+// dq: one workgroup per (query, block of 32 heads) over all of the query's key
+// tiles (no key splits, so no partials).  Wave w forms dims 128 w .. +127 of
+// dq_hat / tau = dl K for the block's heads: the forward's P V product with dl
+// in the A-operand layout and K read transposed from the LDS tile.  Tiles
+// land in a ring of four LDS buffers, three in flight: each holds the tile's
+// rows and its dl block (32 heads x 32 keys), all copied asynchronously, nine
+// copies per wave per tile (so a count of copies in flight says which tiles
+// have landed).  A query's selected entry indices are staged in LDS once
+// (when there are at most kDqIdxCap), so that building a tile's row pointers
+// waits on no load.  The block's dq_hat then goes through LDS (over the ring)
+// to the finish, one wave per head in turn: tau, the rotation's transpose and
+// the RMSNorm gradient
+//     dq = gamma du / r - x sum(gamma du x) / (D r^3),  du = RoPE_-t(dq_hat).
+constexpr int kDqRow = kBD + 4;   // LDS row stride (floats) of the dq_hat block
+constexpr int kDqBuf = kBuf + 3072;  // a tile's rows, its dl block (2 KiB), the idle waves' copy (1 KiB)
+constexpr int kDqIdxCap = 2048;   // selected slots whose entry indices are staged in LDS
+// IDX_LDS (sparse, K <= kDqIdxCap): the indices come from LDS; otherwise from
+// memory (each tile's row pointers then wait for that load, and with it for
+// the copies in flight: correct, with a shallower pipeline).  A compile-time
+// choice: with both paths in one kernel the compiler waits for the union of
+// their loads where they join, on every tile.
+// HB: heads per workgroup, 32 or 16 (16 when 32-head blocks would leave CUs
+// idle: the MFMA rows of the other 16 heads then hold zeros).
+template <bool SPARSE, bool IDX_LDS, int HB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dquery_kernel(const BwdArgs w) {
+    static_assert(SPARSE || !IDX_LDS, "indices exist only for the sparse call");
+    static_assert(HB == 16 || HB == 32, "head blocks of 16 or 32");
     const AttnArgs& a = w.f;
-    __shared__ __attribute__((aligned(16))) uint8_t ring[2][kBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[4][kDqBuf];
+    __shared__ int32_t sidx[IDX_LDS ? kDqIdxCap : 1];
+    static_assert(32 * kDqRow * 4 <= 4 * kDqBuf, "the dq_hat block fits over the ring");
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, lrow = lane & 31, lh = lane >> 5;
+    const int nhb = w.HP / HB;
     const int64_t wg = xcd_order(blockIdx.x + (int64_t)gridDim.x * blockIdx.y, (int64_t)gridDim.x * gridDim.y);
-    const int64_t bq = wg / a.n_splits;
-    const int split = (int)(wg % a.n_splits);
+    const int64_t bq = wg / nhb;
+    const int h0 = HB * (int)(wg % nhb);
     const int H = a.H;
     const QueryGeom g = query_geom<SPARSE>(a, bq);
     const int L = g.n_c + g.n_w;
     const int n_tiles = (L + TK - 1) / TK;
-    const int tps = (n_tiles + a.n_splits - 1) / a.n_splits;
-    const int tile0 = split * tps, tile1 = min(n_tiles, tile0 + tps);
     const uint8_t* spare = reinterpret_cast<const uint8_t*>(a.q) + bq * (int64_t)H * kBD * 2;
-    const bool has_heads = 32 * wave < w.HP;
-    const int head = 32 * wave + lrow;
     const int64_t S = w.S;
-    f32x16 acc[kDT];
+    if constexpr (IDX_LDS) {
+        for (int i = tid; i < g.n_c; i += 256) sidx[i] = a.idx[bq * a.K + i];
+        __syncthreads();
+    }
+    // copies of tile T into buf: rows (8 per wave, as load_tile) and the dl
+    // block (waves 0-1: 16 heads each; waves 2-3 copy wave 0's rows into the
+    // idle kilobyte, so that every wave has nine copies per tile)
+    auto issue = [&](int T, uint8_t* buf) __attribute__((always_inline)) {
+        const int slot = T * TK + (lane & 31);
+        const bf16_t* row = nullptr;
+        if (lane < TK && slot < L) {
+            int32_t j = slot;
+            if constexpr (IDX_LDS) j = slot < g.n_c ? sidx[slot] : 0;
+            else if constexpr (SPARSE) j = slot < g.n_c ? a.idx[bq * a.K + slot] : 0;
+            row = slot_row<bf16_t>(a, g, slot, j, kBD);
+        }
+        const uint64_t rp = reinterpret_cast<uint64_t>(row);
 #pragma unroll
-    for (int dt = 0; dt < kDT; ++dt)
+        for (int k = 0; k < 8; ++k) {
+            const int r = 8 * wave + k;
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(rp >> 32), r);
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)rp, r);
+            const uint64_t p = ((uint64_t)hi << 32) | lo;
+            const uint8_t* src = p ? reinterpret_cast<const uint8_t*>(p) : spare;
+            lds_dma16(src + 16 * (lane ^ gperm(r)), (uint32_t)(uintptr_t)(buf + r * kRS));
+        }
+        const int dr = (HB == 32 ? 16 * (wave & 1) : 0) + (lane >> 2);  // dl row (head of the block)
+        const uint16_t* dsrc = w.dl + (bq * w.HP + h0 + dr) * S + (int64_t)T * TK + 8 * (lane & 3);
+        lds_dma16(dsrc, (uint32_t)(uintptr_t)(buf + kBuf + (wave < 2 ? 1024 * wave : 2048)));
+    };
+    constexpr int WDT = kDT / 4;  // output dim tiles of a wave
+    f32x16 acc[WDT];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
-    if (tile0 < tile1) load_tile<SPARSE>(a, g, bq, tile0, ring[0], spare, wave, lane);
-    for (int T = tile0; T < tile1; ++T) {
-        const int cur = (T - tile0) & 1;
-        if (T + 1 < tile1) {
-            load_tile<SPARSE>(a, g, bq, T + 1, ring[cur ^ 1], spare, wave, lane);
-            wait_vm<8>();
+    for (int i = 0; i < WDT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+#pragma unroll
+    for (int T = 0; T < 3; ++T)
+        if (T < n_tiles) issue(T, ring[T]);
+    for (int T = 0; T < n_tiles; ++T) {
+        if (T + 3 < n_tiles) {
+            issue(T + 3, ring[(T + 3) & 3]);
+            wait_vm<27>();
+        } else if (T + 2 < n_tiles) {
+            wait_vm<18>();
+        } else if (T + 1 < n_tiles) {
+            wait_vm<9>();
         } else {
             wait_vm<0>();
         }
         barrier_lds();
-        if (has_heads) {
-            // A operand (dl, heads x keys): lane (head lrow, half lh) holds
-            // keys 8 lh + 16 ks .. +7 of the tile in the order the V reads use
-            // (keys 4 lh + j and 8 + 4 lh + j of each 16: see below)
-            const uint16_t* dlr = w.dl + (bq * w.HP + head) * S + (int64_t)T * TK;
-            bf16x8 pa[2];
+        const uint8_t* kh = ring[T & 3];
+        // A operand (dl, heads x keys): lane (head lrow, half lh) holds keys
+        // 16 ks + {4 lh + j, 8 + 4 lh + j}, j < 4 (the order the V reads use)
+        const uint8_t* dlr = kh + kBuf + 64 * lrow;
+        bf16x8 pa[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const u32x2 plo = *reinterpret_cast<const u32x2*>(dlr + 2 * (16 * ks + 4 * lh));
+            const u32x2 phi = *reinterpret_cast<const u32x2*>(dlr + 2 * (16 * ks + 8 + 4 * lh));
+            pa[ks] = (HB == 32 || lrow < HB) ? __builtin_bit_cast(bf16x8, u32x4{plo[0], plo[1], phi[0], phi[1]})
+                                             : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        }
+        const int q = lane >> 4, i16 = lane & 15;
+        const uint8_t* vrow[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int rr = 8 * hf + 4 * (q >> 1) + (i16 >> 2);
+            vrow[hf] = kh + rr * kRS + 16 * ((2 * (q & 1) + ((i16 & 3) >> 1)) ^ gperm(rr)) + 8 * (i16 & 1);
+        }
+#pragma unroll
+        for (int i = 0; i < WDT; ++i) {
+            const int dt = WDT * wave + i;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                // the forward's P layout: k-step ks covers keys 16 ks + {4 lh + j, 8 + 4 lh + j}, j < 4
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(dlr + 16 * ks + 4 * lh);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(dlr + 16 * ks + 8 + 4 * lh);
-                pa[ks] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-            }
-            const uint8_t* kh = ring[cur];
-            const int q = lane >> 4, i16 = lane & 15;
-            const uint8_t* vrow[2];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int rr = 8 * hf + 4 * (q >> 1) + (i16 >> 2);
-                vrow[hf] = kh + rr * kRS + 16 * ((2 * (q & 1) + ((i16 & 3) >> 1)) ^ gperm(rr)) + 8 * (i16 & 1);
-            }
-#pragma unroll
-            for (int dt = 0; dt < kDT; ++dt) {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const int off = ks * 16 * kRS + 64 * dt;
-                    const f16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_f16x4_t*)const_cast<uint8_t*>(vrow[0] + off));
-                    const f16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_f16x4_t*)const_cast<uint8_t*>(vrow[1] + off));
-                    const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
-                    const bf16x8 vb = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
-                    acc[dt] = mfma_bf16(pa[ks], vb, acc[dt]);
-                }
+                const int off = ks * 16 * kRS + 64 * dt;
+                const f16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_f16x4_t*)const_cast<uint8_t*>(vrow[0] + off));
+                const f16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_f16x4_t*)const_cast<uint8_t*>(vrow[1] + off));
+                const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+                const bf16x8 vb = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+                acc[i] = mfma_bf16(pa[ks], vb, acc[i]);
             }
         }
-        barrier_lds();
+        barrier_lds();  // before the buffer takes tile T + 4
     }
-    if (!has_heads) return;
-    // partials [BQ][split][HP][D]: element r of tile dt is head 8 (r/4) + 4 lh + r%4, dim 32 dt + lrow
-    float* dst = w.dqp + ((bq * a.n_splits + split) * (int64_t)w.HP + 32 * wave) * kBD;
+    // the dq_hat block over the ring (every tile has been consumed): element r
+    // of tile i is head 8 (r/4) + 4 lh + r%4 of the block, dim 32 (WDT wave + i) + lrow
+    float* dqs = reinterpret_cast<float*>(&ring[0][0]);
 #pragma unroll
-    for (int dt = 0; dt < kDT; ++dt)
+    for (int i = 0; i < WDT; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            dst[(8 * (r >> 2) + 4 * lh + (r & 3)) * (int64_t)kBD + 32 * dt + lrow] = acc[dt][r];
-}
-
-// ---------------------------------------------------------------- finish
-// One wave per (query, head): dq_hat = tau * sum over splits, du = RoPE_-t(dq_hat),
-// then the RMSNorm gradient: dq = gamma du / r - x sum(gamma du x) / (D r^3).
-__global__ __launch_bounds__(256) void bwd_finish_kernel(const BwdArgs w) {
-    const AttnArgs& a = w.f;
-    const int lane = threadIdx.x & 63;
-    const int64_t bq = blockIdx.x;
-    const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
-    if (h >= a.H) return;
+            dqs[(8 * (r >> 2) + 4 * lh + (r & 3)) * kDqRow + 32 * (WDT * wave + i) + lrow] = acc[i][r];
+    __syncthreads();
     int32_t t = a.q_pos[bq];
     t = t < 0 ? 0 : t;
-    float du[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) du[i] = 0.0f;
-    for (int s = 0; s < a.n_splits; ++s) {
-        float v[8];
-        Chunk8<float>::load(w.dqp + ((bq * a.n_splits + s) * (int64_t)w.HP + h) * kBD + 8 * lane, v);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) du[i] += v[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) du[i] *= w.tau;
     const int rope_lo = kBD - a.rope_dims;
+    for (int hl = wave; hl < HB; hl += 4) {
+        const int h = h0 + hl;
+        if (h >= H) break;  // wave-uniform
+        float du[8];
+        {
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(&dqs[hl * kDqRow + 8 * lane]);
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(&dqs[hl * kDqRow + 8 * lane + 4]);
 #pragma unroll
-    for (int pi = 0; pi < 4; ++pi) {
-        const int d = 8 * lane + 2 * pi;
-        if (d < rope_lo) continue;
-        float sn, cs;
-        sincos_turns(-(double)t * rope_turns(a.rope_ratio, (d - rope_lo) >> 1), &sn, &cs);
-        const float x0 = du[2 * pi], x1 = du[2 * pi + 1];
-        du[2 * pi] = x0 * cs - x1 * sn;
-        du[2 * pi + 1] = x0 * sn + x1 * cs;
-    }
-    const int64_t row = (bq * a.H + h) * (int64_t)kBD + 8 * lane;
-    float x[8];
-    Chunk8<bf16_t>::load(reinterpret_cast<const bf16_t*>(a.q) + row, x);
-    float ss = 0.0f, dot = 0.0f;
-    float gm[8];
+            for (int k = 0; k < 4; ++k) {
+                du[k] = v0[k] * w.tau;
+                du[4 + k] = v1[k] * w.tau;
+            }
+        }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        gm[i] = a.gamma_q ? a.gamma_q[8 * lane + i] : 1.0f;
-        ss = __builtin_fmaf(x[i], x[i], ss);
-        dot = __builtin_fmaf(gm[i] * du[i], x[i], dot);
-    }
-    ss = wave_sum(ss);
-    dot = wave_sum(dot);
-    const float r = __builtin_sqrtf(ss / (float)kBD + a.rms_eps);
-    const float ir = 1.0f / r, c3 = dot / ((float)kBD * r * r * r);
-    float dq[8];
+        for (int pi = 0; pi < 4; ++pi) {
+            const int d = 8 * lane + 2 * pi;
+            if (d < rope_lo) continue;
+            float sn, cs;
+            sincos_turns(-(double)t * rope_turns(a.rope_ratio, (d - rope_lo) >> 1), &sn, &cs);
+            const float x0 = du[2 * pi], x1 = du[2 * pi + 1];
+            du[2 * pi] = x0 * cs - x1 * sn;
+            du[2 * pi + 1] = x0 * sn + x1 * cs;
+        }
+        const int64_t row = (bq * H + h) * (int64_t)kBD + 8 * lane;
+        float x[8];
+        Chunk8<bf16_t>::load(reinterpret_cast<const bf16_t*>(a.q) + row, x);
+        float ss = 0.0f, dot = 0.0f;
+        float gm[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        dq[i] = gm[i] * du[i] * ir - x[i] * c3;
-        if (w.dgamma_q) unsafeAtomicAdd(w.dgamma_q + 8 * lane + i, du[i] * x[i] * ir);
+        for (int k = 0; k < 8; ++k) {
+            gm[k] = a.gamma_q ? a.gamma_q[8 * lane + k] : 1.0f;
+            ss = __builtin_fmaf(x[k], x[k], ss);
+            dot = __builtin_fmaf(gm[k] * du[k], x[k], dot);
+        }
+        ss = wave_sum(ss);
+        dot = wave_sum(dot);
+        const float rr = __builtin_sqrtf(ss / (float)kBD + a.rms_eps);
+        const float ir = 1.0f / rr, c3 = dot / ((float)kBD * rr * rr * rr);
+        float dq[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            dq[k] = gm[k] * du[k] * ir - x[k] * c3;
+            if (w.dgamma_q) unsafeAtomicAdd(w.dgamma_q + 8 * lane + k, du[k] * x[k] * ir);
+        }
+        Chunk8<float>::store(w.dq + row, dq);
     }
-    Chunk8<float>::store(w.dq + row, dq);
 }
 
 // ---------------------------------------------------------------- kv_prepare
@@ -908,7 +984,7 @@ size_t mqa_bwd_workspace_bytes(int64_t BQ, int32_t H, int64_t max_slots, int n_s
     n += 4 * al((size_t)BQ * HP * kBD * 2);  // qh, doh, qt, dot
     n += al((size_t)BQ * H * 4);             // delta
     n += 3 * al((size_t)BQ * (S > 0 ? S : TK) * HP * 2);  // pt, dlt, dl
-    n += al((size_t)BQ * n_splits * HP * kBD * 4);  // dqp
+    (void)n_splits;  // the dq kernel runs over all of a query's keys: no split partials
     return n;
 }
 
@@ -933,12 +1009,11 @@ int launch_mqa_bwd(BwdArgs& w, int64_t BQ, int64_t max_slots, void* ws, hipStrea
     w.pt = reinterpret_cast<uint16_t*>(take((size_t)BQ * w.S * HP * 2));
     w.dlt = reinterpret_cast<uint16_t*>(take((size_t)BQ * w.S * HP * 2));
     w.dl = reinterpret_cast<uint16_t*>(take((size_t)BQ * w.S * HP * 2));
-    w.dqp = reinterpret_cast<float*>(take((size_t)BQ * w.f.n_splits * HP * kBD * 4));
     const bool sparse = w.f.idx != nullptr;
-    const dim3 gp((unsigned)BQ, (unsigned)(HP / 4));
+    const dim3 gp((unsigned)BQ, (unsigned)(HP / kPrepHeads));
     const dim3 gs((unsigned)w.f.n_splits, (unsigned)BQ);
     prof_mark("bwd_prep_kernel", false, stream);
-    hipLaunchKernelGGL(bwd_prep_kernel, gp, dim3(256), 0, stream, w);
+    hipLaunchKernelGGL(bwd_prep_kernel, gp, dim3(64 * kPrepHeads), 0, stream, w);
     prof_mark("bwd_prep_kernel", true, stream);
     prof_mark("bwd_logits_kernel", false, stream);
     if (sparse) hipLaunchKernelGGL(bwd_logits_kernel<true>, gs, dim3(256), 0, stream, w);
@@ -948,13 +1023,18 @@ int launch_mqa_bwd(BwdArgs& w, int64_t BQ, int64_t max_slots, void* ws, hipStrea
     if (sparse) hipLaunchKernelGGL(bwd_dkeys_kernel<true>, gs, dim3(512), 0, stream, w);
     else hipLaunchKernelGGL(bwd_dkeys_kernel<false>, gs, dim3(512), 0, stream, w);
     prof_mark("bwd_dkeys_kernel", true, stream);
+    // 16-head blocks while 32-head ones would give fewer workgroups than CUs
+    const bool hb16 = BQ * (HP / 32) < 256;
+    const dim3 gq((unsigned)(HP / (hb16 ? 16 : 32)), (unsigned)BQ);
+#define CAKV_DQ(SP, IL)                                                                                  \
+    if (hb16) hipLaunchKernelGGL((bwd_dquery_kernel<SP, IL, 16>), gq, dim3(256), 0, stream, w);        \
+    else hipLaunchKernelGGL((bwd_dquery_kernel<SP, IL, 32>), gq, dim3(256), 0, stream, w)
     prof_mark("bwd_dquery_kernel", false, stream);
-    if (sparse) hipLaunchKernelGGL(bwd_dquery_kernel<true>, gs, dim3(256), 0, stream, w);
-    else hipLaunchKernelGGL(bwd_dquery_kernel<false>, gs, dim3(256), 0, stream, w);
+    if (sparse && w.f.K <= kDqIdxCap) { CAKV_DQ(true, true); }
+    else if (sparse) { CAKV_DQ(true, false); }
+    else { CAKV_DQ(false, false); }
+#undef CAKV_DQ
     prof_mark("bwd_dquery_kernel", true, stream);
-    prof_mark("bwd_finish_kernel", false, stream);
-    hipLaunchKernelGGL(bwd_finish_kernel, dim3((unsigned)BQ, (unsigned)((w.f.H + 3) / 4)), dim3(256), 0, stream, w);
-    prof_mark("bwd_finish_kernel", true, stream);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

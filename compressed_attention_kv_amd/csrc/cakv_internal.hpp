@@ -150,7 +150,6 @@ struct BwdArgs {
     uint16_t* pt;       // [BQ][S][HP] bf16 P (key-major)
     uint16_t* dlt;      // [BQ][S][HP] bf16 tau * dl (key-major)
     uint16_t* dl;       // [BQ][HP][S] bf16 dl (head-major)
-    float* dqp;         // [BQ][splits][HP][D] partial dq_hat / tau
     int32_t out_f32;
     int32_t unique_rows;  // 1: one query per sequence (no row is touched by two workgroups)
     int32_t HP;         // heads rounded up to 32
