@@ -363,28 +363,59 @@ __global__ __launch_bounds__(256) void idx_zero_kernel(u32x4* p) {
     for (int i = threadIdx.x; i < kHistStride / 4; i += 256) q[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
-// Append the val[u] with sel[u] (KPT per lane) to list (counter cnt): one
-// atomic per wave.  Every lane of the wave must call it.
-template <int KPT, typename T>
-__device__ __forceinline__ void wave_append(T* list, uint32_t* cnt, const bool (&sel)[KPT], const T (&val)[KPT]) {
-    const int lane = threadIdx.x & 63;
-    uint32_t c = 0;
+// Append the values of the whole workgroup (NT threads, KPT per thread)
+// whose flag is set to two lists at once: the waves' counts meet in LDS and
+// one returning atomic per list and workgroup reserves the space (the lists'
+// counters are shared by all workgroups of a query).  Every thread calls it;
+// sh: 2 NT/64 + 2 words of LDS.
+template <int NT, int KPT, typename TA, typename TB>
+__device__ __forceinline__ void block_append2(TA* la, uint32_t* ca, const bool (&sa)[KPT], const TA (&va)[KPT],
+                                              bool use_b, TB* lb, uint32_t* cb, const bool (&sb)[KPT],
+                                              const TB (&vb)[KPT], uint32_t* sh) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t c_a = 0, c_b = 0;
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) c += sel[u] ? 1u : 0u;
-    uint32_t incl = c;
+    for (int u = 0; u < KPT; ++u) {
+        c_a += sa[u] ? 1u : 0u;
+        c_b += (use_b && sb[u]) ? 1u : 0u;
+    }
+    uint32_t inc_a = c_a, inc_b = c_b;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
+        const uint32_t ta = __shfl_up(inc_a, o, 64), tb = __shfl_up(inc_b, o, 64);
+        if (lane >= o) {
+            inc_a += ta;
+            inc_b += tb;
+        }
     }
-    const uint32_t tot = (uint32_t)__shfl((int)incl, 63, 64);
-    if (tot == 0) return;  // wave-uniform
-    uint32_t base = 0;
-    if (lane == 63) base = atomicAdd(cnt, tot);
-    uint32_t p = (uint32_t)__shfl((int)base, 63, 64) + incl - c;
+    if (lane == 63) {
+        sh[wave] = inc_a;
+        sh[NW + wave] = inc_b;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t ta = 0, tb = 0;
 #pragma unroll
-    for (int u = 0; u < KPT; ++u)
-        if (sel[u]) list[p++] = val[u];
+        for (int w = 0; w < NW; ++w) {
+            ta += sh[w];
+            tb += sh[NW + w];
+        }
+        sh[2 * NW] = ta ? atomicAdd(ca, ta) : 0u;
+        sh[2 * NW + 1] = tb ? atomicAdd(cb, tb) : 0u;
+    }
+    __syncthreads();
+    uint32_t pa = sh[2 * NW] + inc_a - c_a, pb = sh[2 * NW + 1] + inc_b - c_b;
+    for (int w = 0; w < wave; ++w) {
+        pa += sh[w];
+        pb += sh[NW + w];
+    }
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+        if (sa[u]) la[pa++] = va[u];
+        if (use_b && sb[u]) lb[pb++] = vb[u];
+    }
+    __syncthreads();  // sh is reused by the next call
 }
 
 // Wave 0 finds the digit d with below(d) < r <= below(d) + cnt[d] over 256
@@ -480,6 +511,7 @@ __global__ __launch_bounds__(256) void idx_refine_kernel(const IndexerArgs a) {
     __shared__ uint32_t h2[kHistBins];
     __shared__ uint32_t wsum[5];
     __shared__ uint32_t info[2];
+    __shared__ uint32_t ash[2 * 4 + 2];
     constexpr int NT = 256, KPT = 8;
     const int64_t bq = blockIdx.y;
     const int tid = threadIdx.x;
@@ -533,8 +565,7 @@ __global__ __launch_bounds__(256) void idx_refine_kernel(const IndexerArgs a) {
             rv[u] = rank_value(kv[u], jv[u]);
             if (level2 && sb[u]) atomicAdd(&h2[(kv[u] >> 10) & (kHistBins - 1)], 1u);
         }
-        wave_append<KPT>(list_a, cnt, sa, jv);
-        if (fits) wave_append<KPT>(list_b, cnt + 1, sb, rv);
+        block_append2<NT, KPT>(list_a, cnt, sa, jv, fits, list_b, cnt + 1, sb, rv, ash);
         if (more) {
 #pragma unroll
             for (int u = 0; u < KPT; ++u) kv[u] = kn[u];
