@@ -76,6 +76,7 @@ def _attn_case(seed, B, Q, H, N, R, K, sparse, n_win=32, gamma=True, m=4):
     ("sparse, 256 queries (one split)", 2, 128, 32, 200, 160, 48, True),
     ("sparse, 64 heads", 2, 2, 64, 500, 64, 256, True),
     ("dense, 40 heads (padded head block)", 1, 3, 40, 400, 48, 0, False),
+    ("sparse, 2,100 selected (dq reads the indices from memory)", 1, 1, 128, 3000, 64, 2100, True),
 ])
 def test_attention_backward(name, B, Q, H, N, R, K, sparse):
     say(f"attention backward: {name}")
