@@ -101,6 +101,49 @@ def test_attention_backward(name, B, Q, H, N, R, K, sparse):
     assert got["dsinks"][H // 2].item() == 0.0  # a -inf sink has no gradient
 
 
+def test_attention_backward_degenerate_queries():
+    """Four queries over raw rows that hold positions 0 .. 7: position 0 (no
+    compressed entry yet, its own window row only), position 5 with every
+    selection slot empty (window only), position 200 with an empty selection
+    and a window outside the raw rows (no key at all), position 150 (selected
+    entries only, some of them not yet visible); half the sinks are -inf.  The
+    keyless query's gradients are exactly zero on every head (output 0, lse
+    -inf on the heads with a -inf sink, the sink's own on the others), a -inf
+    sink has no gradient, and the rest match the oracle."""
+    say("attention backward, degenerate queries")
+    g = torch.Generator().manual_seed(31)
+    B, Q, H, N, R, K, D = 1, 4, 32, 40, 8, 16, 512
+    q = torch.randn(B, Q, H, D, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, N, D, generator=g).to(torch.bfloat16)
+    raw = torch.randn(B, R, D, generator=g).to(torch.bfloat16)
+    sinks = torch.randn(H, generator=g)
+    sinks[::2] = -math.inf
+    qpos = torch.tensor([[0, 5, 200, 150]], dtype=torch.int32)
+    raw0 = torch.tensor([0], dtype=torch.int32)
+    idx = torch.stack([torch.randperm(N, generator=g)[:K] for _ in range(Q)]).view(B, Q, K).to(torch.int32)
+    idx[0, 1:3] = -1
+    dout = torch.randn(B, Q, H, D, generator=g)
+    kw = dict(m=4, n_win=4, rope_dims=64, rope_base=10000.0, softmax_scale=0.0, rms_eps=1e-6)
+    out_ref, lse_ref = oracle.attention(q, kv, raw, raw0, qpos, sinks, idx=idx.numpy(), **kw)
+    ref = oracle.attention_bwd(q, kv, raw, raw0, qpos, sinks, dout, idx=idx.numpy(), **kw)
+    assert np.all(np.isneginf(lse_ref[2, ::2])) and np.all(out_ref[2] == 0.0)
+    assert np.all(ref["dq"][0, 2] == 0.0)
+    kvp = cakv.kv_prepare(_d(kv).clone(), m=4, rope_dims=64)
+    rawp = cakv.kv_prepare_raw(_d(raw).clone(), raw0.tolist(), rope_dims=64)
+    out = torch.from_numpy(out_ref.astype(np.float32)).view(B, Q, H, D)
+    lse = torch.from_numpy(lse_ref.astype(np.float32)).view(B, Q, H)
+    got = cakv.mqa_bwd(_d(q), kvp, _d(idx), rawp, _d(raw0), _d(qpos), _d(sinks), _d(out), _d(lse), _d(dout), **kw)
+    dq = got["dq"].cpu().numpy().reshape(ref["dq"].shape)
+    assert np.all(np.isfinite(dq)) and np.all(dq[0, 2] == 0.0)
+    live = [0, 1, 3]
+    _grad_check(dq[0, live], ref["dq"][0, live], "dq (queries with keys)")
+    _grad_check(got["dkv_c"].cpu().numpy(), ref["dkhat_c"], "dkv_c (position 150's entries)")
+    _grad_check(got["dkv_raw"].cpu().numpy(), ref["dkhat_raw"], "dkv_raw (positions 0 .. 5)")
+    ds = got["dsinks"].cpu().numpy()
+    assert np.all(ds[::2] == 0.0)
+    _grad_check(ds[1::2], ref["dsinks"][1::2], "dsinks (finite sinks)")
+
+
 def test_attention_backward_ring_window():
     """The window read from a ring (row p mod R holds position p), as the
     streaming decode step keeps it: the window rows' gradient lands in the
