@@ -664,12 +664,14 @@ def _event_pair_ms(n: int = 50) -> float:
 
 
 def _source_digest() -> str:
-    """sha256 of the library sources (kernels, headers), sorted by name."""
+    """sha256 of libcakv.so's sources (its kernels and the headers), sorted
+    by name; the measurement probes are built apart and left out."""
     import hashlib
+    from compressed_attention_kv_amd.build import SOURCES
     h = hashlib.sha256()
     cs = os.path.join(ROOT, "compressed_attention_kv_amd", "csrc")
     for f in sorted(os.listdir(cs)):
-        if f.endswith((".hip", ".hpp")):
+        if f.endswith(".hpp") or f in SOURCES:
             h.update(f.encode())
             h.update(open(os.path.join(cs, f), "rb").read())
     return h.hexdigest()
@@ -693,6 +695,43 @@ def _profiled(workload: str, kernel: str, key: str):
 
 
 PEAKS = {"hbm": (HBM_PEAK_GBS, "GB/s"), "mfma": (BF16_PEAK_TFS, "TFLOP/s"), "alu": (FP32_VALU_PEAK_TFS, "TFLOP/s")}
+# what this GPU reaches, measured by attainable_peaks() before the workloads
+# (empty: the fractions against it are left out)
+ATTAINABLE = {}
+_ATT_KEY = {"hbm": "hbm_read_GBps", "mfma": "bf16_mfma_TFLOPs"}
+
+
+def attainable_peaks(read_gib: int = 4, mfma_iters: int = 32768, mfma_blocks: int = 512) -> dict:
+    """The GPU's attainable peaks from libcakv_probes.so: a streaming read of
+    a read_gib GiB buffer (2,048 workgroups on contiguous ranges, nontemporal
+    16-byte loads, eight in flight per thread; median of five after one
+    untimed read) and the bf16 MFMA loop
+    (mfma_blocks workgroups of four waves, two per SIMD, each running four
+    independent 32x32x16 chains; median of three after one untimed launch)."""
+    def timed(fn, n):
+        ts = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+    nbytes = read_gib << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")  # (written once: no first-touch cost)
+    sink = torch.empty(2048, dtype=torch.int32, device="cuda")
+    cakv.probe_read(buf, sink)
+    t_read = timed(lambda: cakv.probe_read(buf, sink), 5)
+    del buf
+    msink = torch.empty(4 * mfma_blocks, dtype=torch.float32, device="cuda")
+    flops = cakv.probe_mfma_bf16(mfma_iters, mfma_blocks, msink)
+    t_mfma = timed(lambda: cakv.probe_mfma_bf16(mfma_iters, mfma_blocks, msink), 3)
+    torch.cuda.empty_cache()
+    return {"hbm_read_GBps": round(nbytes / (t_read * 1e-3) / 1e9, 1), "read_bytes": nbytes,
+            "read_ms": round(t_read, 4), "bf16_mfma_TFLOPs": round(flops / (t_mfma * 1e-3) / 1e12, 1),
+            "mfma_flops": flops, "mfma_ms": round(t_mfma, 4),
+            "probes": "libcakv_probes.so (include/cakv_probes.h): streaming read, bf16 MFMA loop"}
 
 
 def measure(st, steps: int, warmup: int) -> dict:
@@ -758,6 +797,10 @@ def measure(st, steps: int, warmup: int) -> dict:
     if rp_us:
         roof["kernel_ms_rocprof"] = round(rp_us * 1e-3, 4)
         roof["frac_rocprof"] = round(work / (rp_us * 1e-6) / scale / peak, 4)
+    att = ATTAINABLE.get(_ATT_KEY.get(bound, ""))
+    if att:
+        roof["attainable_peak"] = att
+        roof["frac_attainable"] = round(achieved / att, 4)
     cms = st.call_ms(evs)
     per_call = {}
     for c, (b, f) in st.calls.items():
@@ -773,10 +816,15 @@ def measure(st, steps: int, warmup: int) -> dict:
         roof_ms = sum(b for b, _ in st.calls.values()) / (HBM_PEAK_GBS * 1e9) * 1e3
     else:
         roof_ms = sum(f for _, f in st.calls.values()) / (BF16_PEAK_TFS * 1e12) * 1e3
-    return {"value": round(value, 1), "unit": st.unit, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
-            "config": st.config, "windows_ms_per_step": [round(wl * 1e3 / steps, 4) for wl, _ in windows],
-            "roofline": roof, "path_roofline_frac": round(roof_ms / ms, 4), "path_bound": st.bound,
-            "per_call": per_call, "kernel_probe_ms": {k: round(v, 4) for k, v in probe.items()}}
+    rec = {"value": round(value, 1), "unit": st.unit, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
+           "config": st.config, "windows_ms_per_step": [round(wl * 1e3 / steps, 4) for wl, _ in windows],
+           "roofline": roof, "path_roofline_frac": round(roof_ms / ms, 4), "path_bound": st.bound,
+           "per_call": per_call, "kernel_probe_ms": {k: round(v, 4) for k, v in probe.items()}}
+    path_att = ATTAINABLE.get(_ATT_KEY.get(st.bound, ""))
+    if path_att:
+        # the same roofline time priced at what this GPU reaches
+        rec["path_roofline_frac_attainable"] = round(roof_ms * PEAKS[st.bound][0] / path_att / ms, 4)
+    return rec
 
 
 FORWARD = ["csa_decode_128k", "csa_decode_1m", "hca_decode_1m", "prefill_chunk_256k", "flash_csa_decode_128k",
@@ -818,6 +866,8 @@ def main():
                     help="the oracle baseline repeats its sample until this much host time has passed")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (HBM counter calibration)")
+    ap.add_argument("--no-attainable", action="store_true",
+                    help="skip the attainable-peak probes (fractions against the published peaks only)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -832,6 +882,8 @@ def main():
         return (args.steps if args.steps is not None else (5 if prefill else 50),
                 args.warmup if args.warmup is not None else (2 if prefill else 5))
 
+    if not args.no_attainable:
+        ATTAINABLE.update(attainable_peaks())
     steps, warmup = counts(args.workload)
     st = make_step(args.workload)
     rec = measure(st, steps, warmup)
@@ -841,6 +893,8 @@ def main():
             "dtype_detail": "bf16 MFMA with fp32 accumulation (indexer: fp8 keys decoded exactly to bf16)",
             "data": "synthetic", "config": rec.pop("config")}
     line.update(rec)
+    if ATTAINABLE:
+        line["attainable"] = dict(ATTAINABLE)
     if not args.no_cpu_baseline and hasattr(st, "cpu_baseline"):
         q = args.cpu_queries if not st.prefill else min(args.cpu_queries, 8)
         line["cpu_baseline"] = st.cpu_baseline(q, args.cpu_seconds)

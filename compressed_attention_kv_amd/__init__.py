@@ -467,3 +467,53 @@ def indexer_bwd(q_idx, w, k_idx, k_scale, q_pos, idx, dS, m: int, dk=None):
                                 _dev(idx, "idx", _I32), _dev(dS, "dS", _F32), B, Q, N, HI, dI, m, K,
                                 _dev(dq, "dq_idx", _F32), _dev(dw, "dw", _F32), _dev(dk, "dk", _F32), _stream()))
     return dq, dw, dk
+
+
+# ---------------------------------------------------------------- measurement probes (include/cakv_probes.h)
+
+PROBES_PATH = os.path.join(_HERE, "libcakv_probes.so")
+PROBE_EXPORTS = ("cakv_probe_read", "cakv_probe_mfma_bf16")
+_probes = None
+
+
+def load_probes(path: str = PROBES_PATH) -> ctypes.CDLL:
+    """Load libcakv_probes.so, the attainable-peak probes (built with the library)."""
+    global _probes
+    if _probes is not None:
+        return _probes
+    if not os.path.exists(path):
+        raise CakvError(f"{path} is missing: build it first (python -m compressed_attention_kv_amd.build)")
+    lib = ctypes.CDLL(path)
+    lib.cakv_probe_read.argtypes = [_p, _sz, _p, _i32, _p]
+    lib.cakv_probe_read.restype = ctypes.c_int
+    lib.cakv_probe_mfma_bf16.argtypes = [_i64, _i32, _p, _p]
+    lib.cakv_probe_mfma_bf16.restype = ctypes.c_int
+    _probes = lib
+    return lib
+
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int = 0) -> None:
+    """Streaming read of every byte of `buf` (contiguous, on the GPU, a
+    multiple of 16 bytes); workgroup g writes the XOR of the 32-bit words it
+    read to sink[g] (int32, at least `blocks` elements; blocks 0 means 2048)."""
+    lib = load_probes()
+    if not (buf.is_cuda and buf.is_contiguous() and sink.is_cuda and sink.is_contiguous()):
+        raise CakvError("probe_read: buf and sink must be contiguous tensors on the GPU")
+    if sink.dtype != torch.int32 or sink.numel() < (blocks or 2048):
+        raise CakvError("probe_read: sink must be int32 with one element per workgroup")
+    rc = lib.cakv_probe_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), blocks, _stream())
+    if rc != 0:
+        raise CakvError(f"cakv_probe_read returned {rc}")
+
+
+def probe_mfma_bf16(iters: int, blocks: int, sink: torch.Tensor) -> float:
+    """The bf16 MFMA loop: `blocks` workgroups of four waves, `iters` rounds
+    of four independent 32x32x16 MFMAs per wave; sink (float32, 4 * blocks)
+    gets one sum per wave.  Returns the flops the launch performs."""
+    lib = load_probes()
+    if not (sink.is_cuda and sink.is_contiguous() and sink.dtype == torch.float32 and sink.numel() >= 4 * blocks):
+        raise CakvError("probe_mfma_bf16: sink must be a contiguous float32 GPU tensor of 4 * blocks elements")
+    rc = lib.cakv_probe_mfma_bf16(iters, blocks, sink.data_ptr(), _stream())
+    if rc != 0:
+        raise CakvError(f"cakv_probe_mfma_bf16 returned {rc}")
+    return float(blocks) * 4 * iters * 4 * 32768

@@ -11,7 +11,9 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libcakv.so")
 DEBUG_LIB = os.path.join(HERE, "libcakv_debug.so")  # beside libcakv.so: both ship with the tree
+PROBES_LIB = os.path.join(HERE, "libcakv_probes.so")  # attainable-peak probes (measurement only)
 SOURCES = ["api.hip", "kv_compress.hip", "kv_prepare.hip", "decode.hip", "indexer.hip", "attention.hip", "backward.hip"]
+PROBE_SOURCES = ["probes.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -31,17 +33,33 @@ def _compile(src: str, objdir: str, extra=()) -> str:
     return obj
 
 
+def _link(objs, out: str) -> None:
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, out)
+
+
 def build(verbose: bool = False, debug: bool = False) -> str:
-    """Compile every source and link libcakv.so; returns its path.  With
-    debug=True, the debug build instead: the same sources with the kernels'
-    device-side index checks compiled in (-DCAKV_DEBUG), as libcakv_debug.so
-    (objects in _build/debug/)."""
+    """Compile every source and link libcakv.so; returns its path.  The
+    regular build also links the measurement probes, libcakv_probes.so.
+    With debug=True, the debug build instead: the same sources with the
+    kernels' device-side index checks compiled in (-DCAKV_DEBUG), as
+    libcakv_debug.so (objects in _build/debug/)."""
     objdir = os.path.join(HERE, "_build", "debug") if debug else os.path.join(HERE, "_build")
     out = DEBUG_LIB if debug else LIB
     os.makedirs(objdir, exist_ok=True)
     extra = ["-DCAKV_DEBUG"] if debug else []
+    srcs = SOURCES if debug else SOURCES + PROBE_SOURCES
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, objdir, extra), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, objdir, extra), srcs))
+    if not debug:
+        _link(objs[len(SOURCES):], PROBES_LIB)
+        objs = objs[:len(SOURCES)]
+        if verbose:
+            print("built", PROBES_LIB)
     tmp = out + f".tmp{os.getpid()}"
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

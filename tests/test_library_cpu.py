@@ -367,3 +367,31 @@ def test_indexer_bwd_batch_limit(lib):
     rc = lib.cakv_indexer_bwd(None, cakv.BF16, None, None, cakv.FP8_E4M3, FAKE, None, None, None, (1 << 23) - 1, 1,
                               64, 64, 128, 4, 1024, None, None, None, None)
     assert rc == -1  # within the limit: the NULL q_idx is the first error
+
+
+# ------------------------------------------------------------------ measurement probes
+
+def _probe_functions():
+    src = open(os.path.join(ROOT, "include", "cakv_probes.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(cakv_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_probes_library_exports_its_declared_symbols():
+    p = cakv.load_probes()
+    names = _probe_functions()
+    assert set(names) == set(cakv.PROBE_EXPORTS) and len(names) == 2
+    for n in names:
+        assert hasattr(p, n), n
+
+
+@pytest.mark.parametrize("buf,nbytes,sink,blocks", [
+    (None, 16, FAKE, 1), (FAKE, 16, None, 1), (FAKE + 4, 16, FAKE, 1), (FAKE, 24, FAKE, 1),
+    (FAKE, 16, FAKE, -1), (FAKE, 16, FAKE, 65536)])
+def test_probe_read_rejects_bad_arguments(buf, nbytes, sink, blocks):
+    assert cakv.load_probes().cakv_probe_read(buf, nbytes, sink, blocks, None) == -1
+
+
+@pytest.mark.parametrize("iters,blocks,sink", [(-1, 1, FAKE), (1, 0, FAKE), (1, 65536, FAKE), (1, 1, None)])
+def test_probe_mfma_rejects_bad_arguments(iters, blocks, sink):
+    assert cakv.load_probes().cakv_probe_mfma_bf16(iters, blocks, sink, None) == -1
