@@ -56,7 +56,52 @@ __device__ __forceinline__ void flush_hist(const uint32_t* h, uint32_t* g, int n
 // multiplies and the entry's scale.
 constexpr int kPD = 3;  // groups in flight ahead of the one multiplied
 
-template <int HT, int KS>
+// DPP partner in a quad of lanes: lane ^ D (quad_perm [1,0,3,2] or [2,3,0,1])
+template <int D>
+__device__ __forceinline__ uint32_t quad_xor(uint32_t x) {
+    static_assert(D == 1 || D == 2, "quad partner");
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, D == 1 ? 0xB1 : 0x4E, 0xF, 0xF, true);
+}
+
+// In every quad of lanes, the 4 x 4 transpose of (lane, register) over the
+// four 16-byte registers v[0..3]: afterwards lane 4q + a holds in v[i] what
+// lane 4q + i held in v[a].  Two butterfly stages per dword: partner lane ^ 1
+// on the register pairs (0, 1) and (2, 3), then lane ^ 2 on (0, 2) and (1, 3).
+__device__ __forceinline__ void quad_transpose4(u32x4 (&v)[4], int lane) {
+    const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+    auto stage = [](uint32_t& x, uint32_t& y, bool bit, auto xr) __attribute__((always_inline)) {
+        const uint32_t sy = xr(y), sx = xr(x);
+        const uint32_t nx = bit ? sy : x, ny = bit ? y : sx;
+        x = nx;
+        y = ny;
+    };
+    auto x1 = [](uint32_t t) __attribute__((always_inline)) { return quad_xor<1>(t); };
+    auto x2 = [](uint32_t t) __attribute__((always_inline)) { return quad_xor<2>(t); };
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        uint32_t r0 = v[0][d], r1 = v[1][d], r2 = v[2][d], r3 = v[3][d];
+        stage(r0, r1, b0, x1);
+        stage(r2, r3, b0, x1);
+        stage(r0, r2, b1, x2);
+        stage(r1, r3, b1, x2);
+        v[0][d] = r0;
+        v[1][d] = r1;
+        v[2][d] = r2;
+        v[3][d] = r3;
+    }
+}
+
+// COAL (128-dim keys, one query per sequence): whole-line loads.  Lane
+// (entry lrow, half lh) multiplies the 64 bytes of its half row as four
+// 16-byte chunks; the ordinary loads give it those chunks directly, so each
+// load instruction covers a quarter of 32 cache lines and the other three
+// instructions find the lines in cache.  With COAL, instruction j of lane
+// 4q + s loads chunk s of the half row that lane 4q + j multiplies, so each
+// instruction reads eight whole rows (both halves: quads q and q + 8), the
+// loads are nontemporal (nothing is read twice when each sequence has one
+// query), and a transpose in each quad of lanes hands every lane its own
+// chunks.
+template <int HT, int KS, bool COAL>
 __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs a) {
     constexpr int DI = 16 * KS;
     constexpr int HALF = DI / 2;        // bytes of a key row per half-wave lane
@@ -87,13 +132,26 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
     };
     // (a group past the wave's last one reloads the last one's rows, which
     // are in cache, instead of fetching rows of other waves' ranges)
+    static_assert(!COAL || NLD == 4, "whole-line loads: four chunks per lane");
     auto load_group = [&](int n, Grp& g) __attribute__((always_inline)) {
         const int nn = n < ng ? n : (ng > 0 ? ng - 1 : 0);
         const int64_t row = min(first + 128 * (int64_t)nn + lrow, a.N - 1);
-        const u32x4* src = reinterpret_cast<const u32x4*>(kbase + row * DI + lh * HALF);
+        if constexpr (COAL) {
+            // the target lane 4q + j is in this lane's half (same quad): its
+            // row is (lane & 28) + j of the group, its half lh
+            const int q4 = lrow & ~3, ch = lane & 3;
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) g.c[i] = src[i];
-        g.sc = sbase[row];
+            for (int j = 0; j < NLD; ++j) {
+                const int64_t rj = min(first + 128 * (int64_t)nn + q4 + j, a.N - 1);
+                g.c[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + rj * DI + lh * HALF) + ch);
+            }
+            g.sc = __builtin_nontemporal_load(sbase + row);
+        } else {
+            const u32x4* src = reinterpret_cast<const u32x4*>(kbase + row * DI + lh * HALF);
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) g.c[i] = src[i];
+            g.sc = sbase[row];
+        }
     };
 
     // A operand: query heads (rows) x features, k-permutation (s, half, e) -> half*DI/2 + 8s + e
@@ -123,6 +181,10 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
     __syncthreads();  // the histogram is clear
 
     auto score_group = [&](int n, const Grp& g) __attribute__((always_inline)) {
+        u32x4 c[NLD];  // chunk i of this lane's half row
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) c[i] = g.c[i];
+        if constexpr (COAL) quad_transpose4(c, lane);
         f32x16 acc[HT];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht)
@@ -131,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             // 8 fp8 bytes = dwords (2s, 2s+1) of this lane's half row
-            const uint32_t d0 = g.c[s >> 1][(s & 1) * 2], d1 = g.c[s >> 1][(s & 1) * 2 + 1];
+            const uint32_t d0 = c[s >> 1][(s & 1) * 2], d1 = c[s >> 1][(s & 1) * 2 + 1];
             u32x4 kb4;
             kb4[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false));
             kb4[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true));
@@ -776,10 +838,19 @@ int launch_indexer_topk(IndexerArgs& a, int64_t BQ, bool fp8_mode, void* ws, hip
         if (fp8_mode) {
             if (!((a.HI == 32 || a.HI == 64) && (a.dI == 64 || a.dI == 128))) return -2;
             prof_mark("idx_score_fp8_kernel", false, stream);
-            if (a.HI == 64 && a.dI == 128) hipLaunchKernelGGL((idx_score_fp8_kernel<2, 8>), g1, dim3(256), 0, stream, a);
-            else if (a.HI == 32 && a.dI == 128) hipLaunchKernelGGL((idx_score_fp8_kernel<1, 8>), g1, dim3(256), 0, stream, a);
-            else if (a.HI == 64 && a.dI == 64) hipLaunchKernelGGL((idx_score_fp8_kernel<2, 4>), g1, dim3(256), 0, stream, a);
-            else hipLaunchKernelGGL((idx_score_fp8_kernel<1, 4>), g1, dim3(256), 0, stream, a);
+            // whole-line nontemporal loads when each sequence's keys serve one query
+            const bool coal = a.Q == 1;
+            if (a.HI == 64 && a.dI == 128) {
+                if (coal) hipLaunchKernelGGL((idx_score_fp8_kernel<2, 8, true>), g1, dim3(256), 0, stream, a);
+                else hipLaunchKernelGGL((idx_score_fp8_kernel<2, 8, false>), g1, dim3(256), 0, stream, a);
+            } else if (a.HI == 32 && a.dI == 128) {
+                if (coal) hipLaunchKernelGGL((idx_score_fp8_kernel<1, 8, true>), g1, dim3(256), 0, stream, a);
+                else hipLaunchKernelGGL((idx_score_fp8_kernel<1, 8, false>), g1, dim3(256), 0, stream, a);
+            } else if (a.HI == 64 && a.dI == 64) {
+                hipLaunchKernelGGL((idx_score_fp8_kernel<2, 4, false>), g1, dim3(256), 0, stream, a);
+            } else {
+                hipLaunchKernelGGL((idx_score_fp8_kernel<1, 4, false>), g1, dim3(256), 0, stream, a);
+            }
             prof_mark("idx_score_fp8_kernel", true, stream);
         } else {
             prof_mark("idx_score_f32_kernel", false, stream);

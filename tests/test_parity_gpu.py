@@ -201,6 +201,30 @@ def test_indexer_fp8_recall(name, over):
     assert recall >= 0.995 and gap <= 1e-3
 
 
+@pytest.mark.parametrize("N,k", [(32768 + 77, 1024), (5000, 64)])
+def test_indexer_fp8_whole_line_loads_match(N, k):
+    """With one query per sequence the fp8 score kernel loads whole cache
+    lines and transposes them within lane quads; with several it loads each
+    lane's chunks directly.  Same arithmetic, so identical indices: two
+    sequences holding the same keys with one query each against one sequence
+    with both queries (a ragged entry count, a query with fewer visible
+    entries than k)."""
+    say(f"indexer fp8 whole-line loads, N={N} k={k}")
+    rng = np.random.default_rng(N + k)
+    HI, dI, m = 64, 128, 4
+    keys = rng.standard_normal((1, N, dI)).astype(np.float32)
+    codes, scale = oracle.q8_quantize(keys)
+    q = torch.from_numpy(rng.standard_normal((1, 2, HI, dI)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy(rng.standard_normal((1, 2, HI)).astype(np.float32))
+    qpos = np.array([[m * N + 3, m * (k // 2) + 1]], dtype=np.int32)
+    shared = cakv.indexer_topk(_d(q), _d(w), _d(codes), _d(scale), _d(qpos), m, k).cpu().numpy().reshape(2, k)
+    q1 = q.view(2, 1, HI, dI)
+    sep = cakv.indexer_topk(_d(q1), _d(w.view(2, 1, HI)), _d(np.concatenate([codes, codes])),
+                            _d(np.concatenate([scale, scale])), _d(qpos.reshape(2, 1)), m, k).cpu().numpy().reshape(2, k)
+    assert np.array_equal(sep, shared)
+    assert (shared[1] == -1).sum() == k - k // 2
+
+
 # ------------------------------------------------------------------ kv_prepare
 
 @pytest.mark.parametrize("dtype,D,r,m,off,j0,n,gamma,inplace", [

@@ -61,5 +61,9 @@ def test_debug_compressor_variants_and_streaming():
     S.test_streaming_decode_steps("cold_start_overlap_per_channel")
 
 
+def test_debug_indexer_fp8_whole_line_loads():
+    P.test_indexer_fp8_whole_line_loads_match(32768 + 77, 1024)
+
+
 def test_debug_indexer_backward():
     BW.test_indexer_backward("fp8", BW.INDEXER_BWD_SHAPES[1])
