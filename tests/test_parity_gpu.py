@@ -201,17 +201,18 @@ def test_indexer_fp8_recall(name, over):
     assert recall >= 0.995 and gap <= 1e-3
 
 
-@pytest.mark.parametrize("N,k", [(32768 + 77, 1024), (5000, 64)])
-def test_indexer_fp8_whole_line_loads_match(N, k):
+@pytest.mark.parametrize("N,k,HI", [(32768 + 77, 1024, 64), (5000, 64, 64), (9000, 512, 32)])
+def test_indexer_fp8_whole_line_loads_match(N, k, HI):
     """With one query per sequence the fp8 score kernel loads whole cache
     lines and transposes them within lane quads; with several it loads each
     lane's chunks directly.  Same arithmetic, so identical indices: two
     sequences holding the same keys with one query each against one sequence
     with both queries (a ragged entry count, a query with fewer visible
-    entries than k)."""
-    say(f"indexer fp8 whole-line loads, N={N} k={k}")
+    entries than k; 64 and 32 indexer heads, two or one head tiles per
+    wave)."""
+    say(f"indexer fp8 whole-line loads, N={N} k={k} HI={HI}")
     rng = np.random.default_rng(N + k)
-    HI, dI, m = 64, 128, 4
+    dI, m = 128, 4
     keys = rng.standard_normal((1, N, dI)).astype(np.float32)
     codes, scale = oracle.q8_quantize(keys)
     q = torch.from_numpy(rng.standard_normal((1, 2, HI, dI)).astype(np.float32)).to(torch.bfloat16)

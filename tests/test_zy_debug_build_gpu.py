@@ -62,7 +62,8 @@ def test_debug_compressor_variants_and_streaming():
 
 
 def test_debug_indexer_fp8_whole_line_loads():
-    P.test_indexer_fp8_whole_line_loads_match(32768 + 77, 1024)
+    P.test_indexer_fp8_whole_line_loads_match(32768 + 77, 1024, 64)
+    P.test_indexer_fp8_whole_line_loads_match(9000, 512, 32)
 
 
 def test_debug_indexer_backward():
