@@ -18,7 +18,9 @@
 //        (heads x entries, fp32 accumulation); ReLU, the head weights and the
 //        head reduction run on the accumulator registers and one half-wave
 //        exchange.  The per-entry scale multiplies the final sum (a power of
-//        two, so exact up to rounding order).
+//        two, so exact up to rounding order).  With one query per sequence
+//        (decode) the keys arrive by whole-line nontemporal loads and a
+//        transpose in each quad of lanes (COAL below).
 //        fp32 mode: one thread per entry runs the canonical fmaf chains.
 //      Each score is written as an order-preserving 32-bit key, and counted
 //      in an exact histogram of the top 11 key bits (LDS, then HBM atomics).
@@ -130,8 +132,8 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
         u32x4 c[NLD];
         float sc;
     };
-    // (a group past the wave's last one reloads the last one's rows, which
-    // are in cache, instead of fetching rows of other waves' ranges)
+    // (a group past the wave's last one reloads the last one's rows, usually
+    // still in cache, instead of fetching rows of other waves' ranges)
     static_assert(!COAL || NLD == 4, "whole-line loads: four chunks per lane");
     auto load_group = [&](int n, Grp& g) __attribute__((always_inline)) {
         const int nn = n < ng ? n : (ng > 0 ? ng - 1 : 0);
