@@ -14,9 +14,9 @@ reported under "workloads" (same fields, no CPU baseline):
     262,144-token prefix: the chunk's compressions and preparations, the
     indexer, sparse attention, dense attention),
   flash_csa_decode_128k, flash_hca_decode_1m (64 heads, top-512),
-  stream_decode_128k (the per-token decode step: kv_append of the new
-    token into the CSA, indexer-key and HCA state, then indexer and both
-    attention calls reading the window rings),
+  stream_decode_128k (the per-token decode step: one batched kv_append of
+    the new token into the CSA, indexer-key and HCA state, then indexer and
+    both attention calls reading the window rings),
   compress_variants_256k (kv_compress_ex: spans of 8 at m = 4 with
     per-channel gates over a 262,144-token prefix),
   backward_csa_decode_128k (training: mqa_bwd + indexer_bwd at the CSA 128K
@@ -340,11 +340,11 @@ class Step:
 class StreamStep:
     """The streaming decode step of a CSA layer and an HCA layer for 32
     sequences at 128K context (NEXT to the whole-batch calls: one new token
-    per sequence per step).  Per step: kv_append of the token's KV into the
-    CSA cache and window ring, of its indexer key into the fp8 key cache, of
-    its KV into the HCA cache and window ring (a block completes every 4
-    tokens for CSA, every 128 for HCA), then indexer_topk, sparse_mqa_fwd and
-    dense_compressed_mqa_fwd reading the window rings.  The prefix (131,072
+    per sequence per step).  Per step: one kv_append_batch of three appends
+    (the token's KV into the CSA cache and window ring, its indexer key into
+    the fp8 key cache, its KV into the HCA cache and window ring; a block
+    completes every 4 tokens for CSA, every 128 for HCA), then indexer_topk,
+    sparse_mqa_fwd and dense_compressed_mqa_fwd reading the window rings.  The prefix (131,072
     tokens: 32,768 CSA entries, 1,024 HCA entries) is built at set-up.  Three
     independent copies of the state are cycled (each advances one position
     every third step), so a step's caches are not Infinity-Cache resident."""
@@ -425,15 +425,15 @@ class StreamStep:
         b_app = 3 * D * 2 + 2 * D * 2 + w.dI * 2 + 3 * 4  # token rows in, ring and window rows out
         self.kernels = {"idx_score_fp8_kernel": (b_s * B, f_s * B), "mqa_fwd_kernel#0": (b_a * B, f_a * B),
                         "mqa_fwd_kernel#1": (b_h * B, f_h * B), "kv_append_kernel#0": (b_app * B, 0)}
-        self.launches = {"mqa_fwd_kernel": 2, "kv_append_kernel": 3}
-        self.calls = {"kv_append x3": (b_app * B, 0), "indexer_topk": (b_s * B, f_s * B),
+        self.launches = {"mqa_fwd_kernel": 2, "kv_append_kernel": 1}
+        self.calls = {"kv_append_batch (3 appends)": (b_app * B, 0), "indexer_topk": (b_s * B, f_s * B),
                       "sparse_mqa_fwd (ring window)": (b_a * B, f_a * B),
                       "dense_compressed_mqa_fwd (ring window)": (b_h * B, f_h * B)}
         self.n_tokens = B
         self.unit = "query-tokens/s"
         self.config = {"workload": self.name, "batch": B, "context": t0, "m": m, "m_hca": mh, "heads": w.H,
                        "head_dim": D, "topk": w.k, "window": w.n_win, "state_copies_cycled": copies,
-                       "step": "kv_append x3 + indexer_topk + sparse_mqa_fwd + dense_compressed_mqa_fwd"}
+                       "step": "kv_append_batch (3 appends) + indexer_topk + sparse_mqa_fwd + dense_compressed_mqa_fwd"}
 
     @property
     def n_events(self) -> int:
@@ -455,12 +455,13 @@ class StreamStep:
         if ev is not None:
             ev[0].record()
         tok = self.tok[j]
-        cakv.kv_append(tok, self.gtok[j, 0], pos, st["raw_c"], st["graw_c"], st["kv"], m=w.m, win_ring=st["win_c"],
-                       prep=self.prep)
-        cakv.kv_append(self.ktok[j], self.gtok[j, 1], pos, st["kraw"], st["kgraw"], st["kc"], m=w.m,
-                       cache_scale=st["ks"])
-        cakv.kv_append(tok, self.gtok[j, 2], pos, st["raw_h"], st["graw_h"], st["kh"], m=w.m_hca,
-                       win_ring=st["win_h"], prep=self.prep)
+        cakv.kv_append_batch([
+            dict(x_tok=tok, gate_tok=self.gtok[j, 0], raw_ring=st["raw_c"], gate_ring=st["graw_c"], cache=st["kv"],
+                 m=w.m, win_ring=st["win_c"], prep=self.prep),
+            dict(x_tok=self.ktok[j], gate_tok=self.gtok[j, 1], raw_ring=st["kraw"], gate_ring=st["kgraw"],
+                 cache=st["kc"], m=w.m, cache_scale=st["ks"]),
+            dict(x_tok=tok, gate_tok=self.gtok[j, 2], raw_ring=st["raw_h"], gate_ring=st["graw_h"], cache=st["kh"],
+                 m=w.m_hca, win_ring=st["win_h"], prep=self.prep)], pos)
         if ev is not None:
             ev[1].record()
         qpos = pos.view(-1, 1)

@@ -9,6 +9,7 @@ Functions (names follow the C ABI):
   kv_compress(x, gate, m, out_dtype)                      -> out (, scale)
   kv_compress_ex(x, gate, m, span, out_dtype)              -> out (, scale)   (overlap, per-channel gates)
   kv_append(x_tok, gate_tok, pos, raw_ring, gate_ring, cache, ...)  streaming decode: one token per sequence
+  kv_append_batch([dict of kv_append's arguments, ...], pos)       several of them in one launch
   kv_prepare(kv_c, m, rope_dims, ...)                     -> prepared entries (in place by default)
   kv_prepare_raw(kv_raw, raw_pos0, rope_dims, ...)        -> prepared window rows (per-sequence positions)
   indexer_topk(q_idx, w, k_idx, k_scale, q_pos, m, k)     -> idx
@@ -47,6 +48,16 @@ class PrepParams(ctypes.Structure):
                 ("rms_eps", ctypes.c_float), ("gamma_kv", ctypes.c_void_p)]
 
 
+class AppendCall(ctypes.Structure):
+    """cakv_append_call: one append of a cakv_kv_append_batch."""
+    _fields_ = [("x_tok", ctypes.c_void_p), ("gate_tok", ctypes.c_void_p), ("gate_per_channel", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("D", ctypes.c_int64), ("raw_ring", ctypes.c_void_p),
+                ("gate_ring", ctypes.c_void_p), ("Rr", ctypes.c_int64), ("win_ring", ctypes.c_void_p),
+                ("Rw", ctypes.c_int64), ("cache", ctypes.c_void_p), ("cache_dtype", ctypes.c_int32),
+                ("m", ctypes.c_int32), ("cache_scale", ctypes.c_void_p), ("N", ctypes.c_int64),
+                ("span", ctypes.c_int32), ("prep", ctypes.POINTER(PrepParams))]
+
+
 _lib = None
 _i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
 
@@ -55,7 +66,7 @@ EXPORTS = ("cakv_version", "cakv_last_error", "cakv_kv_compress", "cakv_kv_prepa
            "cakv_dense_mqa_workspace", "cakv_dense_compressed_mqa_fwd", "cakv_profile_kernel_events",
            "cakv_indexer_topk_noalloc", "cakv_kv_compress_ex", "cakv_kv_append", "cakv_mqa_bwd_workspace",
            "cakv_mqa_bwd", "cakv_kv_prepare_bwd", "cakv_kv_compress_bwd_workspace", "cakv_kv_compress_bwd",
-           "cakv_indexer_bwd")
+           "cakv_indexer_bwd", "cakv_kv_append_batch")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -72,6 +83,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.cakv_kv_compress.argtypes = [_p, ctypes.c_int, _p, _i64, _i64, _i64, _i32, _p, ctypes.c_int, _p, _p]
     lib.cakv_kv_compress_ex.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p,
                                         ctypes.c_int, _p, _p]
+    lib.cakv_kv_append_batch.argtypes = [ctypes.POINTER(AppendCall), _i32, _p, _i64, _p]
     lib.cakv_kv_append.argtypes = [_p, _p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _p, _p, _i64, _p, _i64, _p,
                                    ctypes.c_int, _p, _i64, _i32, _i32, ctypes.POINTER(PrepParams), _p]
     lib.cakv_mqa_bwd_workspace.argtypes = [_i64, _i64, _i32, _i32, _i64, _i32]
@@ -201,11 +213,7 @@ def kv_append(x_tok: torch.Tensor, gate_tok: torch.Tensor, pos: torch.Tensor, ra
     B, D = x_tok.shape
     span = m if span is None else span
     per_channel = gate_tok.dim() == 2
-    pp = None
-    if prep is not None:
-        pp = PrepParams(int(prep.get("rope_dims", 0)), float(prep.get("rope_base", 10000.0)),
-                        int(prep.get("entry_pos_offset", 0)), float(prep.get("rms_eps", 1e-6)),
-                        _dev(prep.get("gamma_kv"), "gamma_kv", _F32))
+    pp = _prep_params(prep)
     if raw_ring.dtype != x_tok.dtype or (win_ring is not None and win_ring.dtype != x_tok.dtype):
         raise CakvError("raw_ring and win_ring must have x_tok's dtype")
     _check(lib.cakv_kv_append(_dev(x_tok, "x_tok"), _dev(gate_tok, "gate_tok", _F32), int(per_channel),
@@ -214,6 +222,43 @@ def kv_append(x_tok: torch.Tensor, gate_tok: torch.Tensor, pos: torch.Tensor, ra
                               0 if win_ring is None else win_ring.shape[1], _dev(cache, "cache"), _DT[cache.dtype],
                               _dev(cache_scale, "cache_scale", _F32), cache.shape[1], m, span,
                               None if pp is None else ctypes.byref(pp), _stream()))
+
+
+def _prep_params(prep: dict | None):
+    if prep is None:
+        return None
+    return PrepParams(int(prep.get("rope_dims", 0)), float(prep.get("rope_base", 10000.0)),
+                      int(prep.get("entry_pos_offset", 0)), float(prep.get("rms_eps", 1e-6)),
+                      _dev(prep.get("gamma_kv"), "gamma_kv", _F32))
+
+
+def kv_append_batch(calls, pos: torch.Tensor) -> None:
+    """Several appends of the same new tokens (positions pos [B] int32) in one
+    launch (see cakv_kv_append_batch): each element of `calls` is a dict of
+    kv_append's arguments -- x_tok, gate_tok, raw_ring, gate_ring, cache, m,
+    and optionally span, cache_scale, win_ring, prep.  The results are those
+    of the same kv_append calls made one after another."""
+    lib = load_library()
+    n = len(calls)
+    B = pos.shape[0]
+    arr = (AppendCall * max(n, 1))()
+    preps = []  # the PrepParams stay referenced until the call returns
+    for i, c in enumerate(calls):
+        x, g, raw, graw, cache = c["x_tok"], c["gate_tok"], c["raw_ring"], c["gate_ring"], c["cache"]
+        win, cs = c.get("win_ring"), c.get("cache_scale")
+        if x.shape[0] != B:
+            raise CakvError(f"kv_append_batch: append {i} has {x.shape[0]} tokens, pos has {B}")
+        if raw.dtype != x.dtype or (win is not None and win.dtype != x.dtype):
+            raise CakvError("raw_ring and win_ring must have x_tok's dtype")
+        pp = _prep_params(c.get("prep"))
+        preps.append(pp)
+        m = int(c["m"])
+        arr[i] = AppendCall(_dev(x, "x_tok"), _dev(g, "gate_tok", _F32), int(g.dim() == 2), _DT[x.dtype], x.shape[1],
+                            _dev(raw, "raw_ring"), _dev(graw, "gate_ring", _F32), raw.shape[1], _dev(win, "win_ring"),
+                            0 if win is None else win.shape[1], _dev(cache, "cache"), _DT[cache.dtype], m,
+                            _dev(cs, "cache_scale", _F32), cache.shape[1], int(c.get("span") or m),
+                            None if pp is None else ctypes.pointer(pp))
+    _check(lib.cakv_kv_append_batch(arr, n, _dev(pos, "pos", _I32), B, _stream()))
 
 
 def kv_prepare(kv_c: torch.Tensor, *, m: int, rope_dims: int, rope_base: float = 10000.0,

@@ -317,10 +317,15 @@ int cakv_kv_prepare(const void* kv_in, void* kv_out, int act_dtype, int64_t B, i
                                            reinterpret_cast<hipStream_t>(stream)));
 }
 
-int cakv_kv_append(const void* x_tok, const float* gate_tok, int gate_per_channel, const int32_t* pos,
-                   int act_dtype, int64_t B, int64_t D, void* raw_ring, float* gate_ring, int64_t Rr,
-                   void* win_ring, int64_t Rw, void* cache, int cache_dtype, float* cache_scale, int64_t N,
-                   int32_t m, int32_t span, const cakv_prep_params* prep, void* stream) {
+// Validates one append and fills its kernel arguments and the batch kernel's
+// kind code (4 * activations bf16 + 2 * cache fp8 + per-channel gates);
+// empty is set when there is nothing to do (B == 0).
+static int append_args(const void* x_tok, const float* gate_tok, int gate_per_channel, const int32_t* pos,
+                       int act_dtype, int64_t B, int64_t D, void* raw_ring, float* gate_ring, int64_t Rr,
+                       void* win_ring, int64_t Rw, void* cache, int cache_dtype, float* cache_scale, int64_t N,
+                       int32_t m, int32_t span, const cakv_prep_params* prep, cakv::AppendArgs& a, int32_t& kind,
+                       bool& empty) {
+    empty = false;
     REQUIRE(B >= 0 && N >= 0, CAKV_EINVAL, "negative size (B=%lld N=%lld)", (long long)B, (long long)N);
     REQUIRE(act_dtype == CAKV_F32 || act_dtype == CAKV_BF16, CAKV_EINVAL, "act_dtype must be F32 or BF16");
     REQUIRE(cache_dtype == act_dtype || cache_dtype == CAKV_FP8_E4M3, CAKV_EINVAL,
@@ -347,7 +352,10 @@ int cakv_kv_append(const void* x_tok, const float* gate_tok, int gate_per_channe
                 CAKV_EINVAL, "entry positions must fit in int32");
         if (prep->gamma_kv) REQUIRE(aligned16(prep->gamma_kv), CAKV_EINVAL, "gamma_kv must be 16-byte aligned");
     }
-    if (B == 0) return ok();
+    if (B == 0) {
+        empty = true;
+        return ok();
+    }
     REQUIRE(B <= 0x7fffffffLL, CAKV_EUNSUPPORTED, "B too large");
     REQUIRE_PTR(x_tok, "x_tok");
     REQUIRE_PTR(gate_tok, "gate_tok");
@@ -357,7 +365,7 @@ int cakv_kv_append(const void* x_tok, const float* gate_tok, int gate_per_channe
     if (win_ring) REQUIRE(aligned16(win_ring), CAKV_EINVAL, "win_ring must be 16-byte aligned");
     if (N > 0) REQUIRE_PTR(cache, "cache");
     if (cache_scale) REQUIRE(aligned16(cache_scale), CAKV_EINVAL, "cache_scale must be 16-byte aligned");
-    cakv::AppendArgs a{};
+    a = cakv::AppendArgs{};
     a.x_tok = x_tok;
     a.gate_tok = gate_tok;
     a.pos = pos;
@@ -380,8 +388,49 @@ int cakv_kv_append(const void* x_tok, const float* gate_tok, int gate_per_channe
         a.eps = prep->rms_eps;
         a.rope_ratio = cakv::rope_ratio_of(prep->rope_base, prep->rope_dims);
     }
+    kind = 4 * (act_dtype == CAKV_BF16 ? 1 : 0) + 2 * (cache_dtype == CAKV_FP8_E4M3 ? 1 : 0) +
+           (gate_per_channel != 0 ? 1 : 0);
+    return ok();
+}
+
+int cakv_kv_append(const void* x_tok, const float* gate_tok, int gate_per_channel, const int32_t* pos,
+                   int act_dtype, int64_t B, int64_t D, void* raw_ring, float* gate_ring, int64_t Rr,
+                   void* win_ring, int64_t Rw, void* cache, int cache_dtype, float* cache_scale, int64_t N,
+                   int32_t m, int32_t span, const cakv_prep_params* prep, void* stream) {
+    cakv::AppendArgs a;
+    int32_t kind = 0;
+    bool empty = false;
+    const int rc = append_args(x_tok, gate_tok, gate_per_channel, pos, act_dtype, B, D, raw_ring, gate_ring, Rr,
+                               win_ring, Rw, cache, cache_dtype, cache_scale, N, m, span, prep, a, kind, empty);
+    if (rc || empty) return rc;
     return rc_from(cakv::launch_kv_append(a, B, act_dtype, cache_dtype, gate_per_channel != 0,
                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cakv_kv_append_batch(const cakv_append_call* calls, int32_t n, const int32_t* pos, int64_t B, void* stream) {
+    static_assert(CAKV_APPEND_BATCH_MAX == cakv::kAppendBatchMax, "batch size of the header and the kernel");
+    REQUIRE(calls, CAKV_EINVAL, "calls must not be NULL");
+    REQUIRE(n >= 1 && n <= CAKV_APPEND_BATCH_MAX, CAKV_EINVAL, "n=%d: 1 .. %d appends per batch", n,
+            CAKV_APPEND_BATCH_MAX);
+    cakv::AppendBatch ab{};
+    bool empty = false;
+    for (int i = 0; i < n; ++i) {
+        const cakv_append_call& c = calls[i];
+        const int rc = append_args(c.x_tok, c.gate_tok, c.gate_per_channel, pos, c.act_dtype, B, c.D, c.raw_ring,
+                                   c.gate_ring, c.Rr, c.win_ring, c.Rw, c.cache, c.cache_dtype, c.cache_scale, c.N,
+                                   c.m, c.span, c.prep, ab.a[i], ab.kind[i], empty);
+        if (rc) return rc;
+        // the appends run concurrently: no two may write the same buffer
+        for (int k = 0; k < i; ++k) {
+            const cakv_append_call& o = calls[k];
+            REQUIRE(c.raw_ring != o.raw_ring && c.gate_ring != o.gate_ring &&
+                        (!c.win_ring || c.win_ring != o.win_ring) && (!c.cache || c.cache != o.cache) &&
+                        (!c.cache_scale || c.cache_scale != o.cache_scale),
+                    CAKV_EINVAL, "appends %d and %d of a batch write the same buffer", k, i);
+        }
+    }
+    if (empty) return ok();
+    return rc_from(cakv::launch_kv_append_batch(ab, n, B, reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t cakv_indexer_topk_workspace(int64_t B, int64_t Q, int64_t N, int32_t k) {

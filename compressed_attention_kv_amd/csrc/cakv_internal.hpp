@@ -102,6 +102,15 @@ struct AppendArgs {
 int launch_kv_append(const AppendArgs& a, int64_t B, int act_dtype, int cache_dtype, bool gate_per_channel,
                      hipStream_t stream);
 
+// up to kAppendBatchMax appends of the same B tokens in one launch; kind[y] =
+// 4 * (activations bf16) + 2 * (cache fp8) + (per-channel gates)
+constexpr int kAppendBatchMax = 4;
+struct AppendBatch {
+    AppendArgs a[kAppendBatchMax];
+    int32_t kind[kAppendBatchMax];
+};
+int launch_kv_append_batch(const AppendBatch& ab, int32_t n, int64_t B, hipStream_t stream);
+
 // sparse (idx != NULL) or dense MQA forward; act_f32: inputs are float32
 int launch_mqa_fwd(const AttnArgs& a, int64_t BQ, int D, bool act_f32, hipStream_t stream);
 

@@ -31,11 +31,11 @@
 namespace cakv {
 
 // OUTK: 0 = f32, 1 = bf16, 2 = fp8 E4M3 + scale (the cache's type); PC:
-// per-channel gates.
+// per-channel gates.  The workgroup's LDS: erow, 4096 elements of T (the
+// completed entry, in the cache's rounding), and one word for the entry's
+// absolute maximum (fp8).
 template <typename T, int OUTK, bool PC>
-__global__ __launch_bounds__(256) void kv_append_kernel(const AppendArgs a) {
-    __shared__ __attribute__((aligned(16))) T erow[4096];  // the completed entry, in the cache's rounding
-    __shared__ uint32_t amax;
+__device__ __forceinline__ void append_body(const AppendArgs& a, T* erow, uint32_t& amax) {
     const int64_t b = blockIdx.x;
     const int32_t t = a.pos[b];
     if (t < 0) return;  // workgroup-uniform: no token for this sequence
@@ -158,6 +158,44 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const AppendArgs a) {
             if (l == 0) a.gate_ring[ring_row] = a.gate_tok[b];
         }
     }
+}
+
+template <typename T, int OUTK, bool PC>
+__global__ __launch_bounds__(256) void kv_append_kernel(const AppendArgs a) {
+    __shared__ __attribute__((aligned(16))) T erow[4096];
+    __shared__ uint32_t amax;
+    append_body<T, OUTK, PC>(a, erow, amax);
+}
+
+// Several appends of the same tokens (the compressors of a layer or of
+// several layers) in one launch: workgroup (b, y) runs append y for sequence
+// b.  kind = 4 * (activations bf16) + 2 * (cache fp8) + (per-channel gates).
+__global__ __launch_bounds__(256) void kv_append_batch_kernel(const AppendBatch ab) {
+    __shared__ __attribute__((aligned(16))) float erow[4096];  // f32 or bf16 rows
+    __shared__ uint32_t amax;
+    const int y = blockIdx.y;
+    CAKV_DCHECK(y < kAppendBatchMax);
+    const AppendArgs& a = ab.a[y];
+    bf16_t* erow_h = reinterpret_cast<bf16_t*>(erow);
+    switch (ab.kind[y]) {  // workgroup-uniform
+        case 0: append_body<float, 0, false>(a, erow, amax); break;
+        case 1: append_body<float, 0, true>(a, erow, amax); break;
+        case 2: append_body<float, 2, false>(a, erow, amax); break;
+        case 3: append_body<float, 2, true>(a, erow, amax); break;
+        case 4: append_body<bf16_t, 1, false>(a, erow_h, amax); break;
+        case 5: append_body<bf16_t, 1, true>(a, erow_h, amax); break;
+        case 6: append_body<bf16_t, 2, false>(a, erow_h, amax); break;
+        case 7: append_body<bf16_t, 2, true>(a, erow_h, amax); break;
+        default: break;
+    }
+}
+
+int launch_kv_append_batch(const AppendBatch& ab, int32_t n, int64_t B, hipStream_t stream) {
+    if (B == 0 || n == 0) return 0;
+    prof_mark("kv_append_kernel", false, stream);
+    hipLaunchKernelGGL(kv_append_batch_kernel, dim3((unsigned)B, (unsigned)n), dim3(256), 0, stream, ab);
+    prof_mark("kv_append_kernel", true, stream);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 int launch_kv_append(const AppendArgs& a, int64_t B, int act_dtype, int cache_dtype, bool gate_per_channel,

@@ -298,6 +298,47 @@ int cakv_kv_append(const void* x_tok, const float* gate_tok, int gate_per_channe
                    int32_t m, int32_t span, const cakv_prep_params* prep, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * kv_append_batch  [the same passages as kv_append]
+ *
+ * Up to CAKV_APPEND_BATCH_MAX appends of the same B new tokens (positions
+ * pos [B] int32, shared) in one launch, for example the three compressors a
+ * decode step feeds (a CSA layer's KV and indexer key, an HCA layer's KV):
+ * append i does exactly what cakv_kv_append does with the fields of
+ * calls[i] (same meaning, layouts and limits as its arguments), so the
+ * results are bitwise those of n separate calls.  The appends run
+ * concurrently: no two may write the same buffer (their raw rings, gate
+ * rings, window rings, caches and scales are distinct; calls whose pointers
+ * coincide are refused).  calls is a host array of n descriptors, read
+ * before the call returns.
+ * Errors: EINVAL (calls NULL, n outside 1 .. CAKV_APPEND_BATCH_MAX, two
+ * appends writing the same buffer), and every error of cakv_kv_append for
+ * any of the descriptors (nothing is launched then).
+ * ------------------------------------------------------------------------- */
+#define CAKV_APPEND_BATCH_MAX 4
+
+typedef struct cakv_append_call {
+    const void* x_tok;     /* [B, D] act_dtype */
+    const float* gate_tok; /* [B] or [B, D] */
+    int32_t gate_per_channel;
+    int32_t act_dtype;
+    int64_t D;
+    void* raw_ring;        /* [B, Rr, D] */
+    float* gate_ring;      /* [B, Rr] or [B, Rr, D] */
+    int64_t Rr;
+    void* win_ring;        /* [B, Rw, D] prepared rows, or NULL */
+    int64_t Rw;
+    void* cache;           /* [B, N, D] */
+    int32_t cache_dtype;
+    int32_t m;
+    float* cache_scale;    /* [B, N], fp8 caches only */
+    int64_t N;
+    int32_t span;
+    const cakv_prep_params* prep;
+} cakv_append_call;
+
+int cakv_kv_append_batch(const cakv_append_call* calls, int32_t n, const int32_t* pos, int64_t B, void* stream);
+
+/* ---------------------------------------------------------------------------
  * sparse_mqa_fwd  [V4 digest, CSA step 3: multi-query attention over the
  * selected compressed entries; V4-Pro card: shared-KV MQA, 128 heads of dim
  * 512, plus the raw window and the sink]

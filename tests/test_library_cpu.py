@@ -395,3 +395,45 @@ def test_probe_read_rejects_bad_arguments(buf, nbytes, sink, blocks):
 @pytest.mark.parametrize("iters,blocks,sink", [(-1, 1, FAKE), (1, 0, FAKE), (1, 65536, FAKE), (1, 1, None)])
 def test_probe_mfma_rejects_bad_arguments(iters, blocks, sink):
     assert cakv.load_probes().cakv_probe_mfma_bf16(iters, blocks, sink, None) == -1
+
+
+# ------------------------------------------------------------------ batched appends
+
+def test_append_call_layout(tmp_path):
+    """The binding's mirror of cakv_append_call has the C compiler's layout
+    (size and every field's offset, from a program built against cakv.h)."""
+    import subprocess
+    fields = [f for f, _ in cakv.AppendCall._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"cakv.h\"\nint main(void) {\n"
+                   "  printf(\"%zu\\n\", sizeof(cakv_append_call));\n" +
+                   "".join(f"  printf(\"%zu\\n\", offsetof(cakv_append_call, {f}));\n" for f in fields) +
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(cakv.AppendCall)
+    assert got[1:] == [getattr(cakv.AppendCall, f).offset for f in fields]
+
+
+def _append_call(**kw):
+    d = dict(x_tok=FAKE, gate_tok=FAKE, gate_per_channel=0, act_dtype=cakv.BF16, D=512, raw_ring=FAKE,
+             gate_ring=FAKE + 0x100, Rr=8, win_ring=None, Rw=0, cache=FAKE + 0x200, cache_dtype=cakv.BF16, m=4,
+             cache_scale=None, N=16, span=4, prep=None)
+    d.update(kw)
+    return cakv.AppendCall(**d)
+
+
+@pytest.mark.parametrize("calls,n,code", [
+    (None, 1, -1),
+    ([_append_call()], 0, -1),
+    ([_append_call()] * 5, 5, -1),
+    ([_append_call(D=7)], 1, -2),
+    ([_append_call(cache_dtype=cakv.FP8_E4M3)], 1, -1),  # fp8 without its scale
+    ([_append_call(), _append_call()], 2, -1),           # two appends writing the same rings
+    ([_append_call(), _append_call(raw_ring=FAKE + 0x300, gate_ring=FAKE + 0x400)], 2, -1),  # the same cache
+])
+def test_append_batch_rejects_bad_arguments(lib, calls, n, code):
+    arr = None if calls is None else (cakv.AppendCall * len(calls))(*calls)
+    assert lib.cakv_kv_append_batch(arr, n, FAKE, 4, None) == code
+    assert lib.cakv_last_error()

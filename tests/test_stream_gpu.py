@@ -293,3 +293,74 @@ def test_streaming_decode_steps(name):
         assert torch.equal(csa.raw[b, p % c["Rr"]].view(torch.int16), dev["raw"][b, p].view(torch.int16))
         # entries of blocks not yet complete were never written
         assert not csa.cache[b, nc:].any() and not hca.cache[b, nh:].any()
+
+
+# ------------------------------------------------------------------ batched appends
+
+# (activations, cache, per-channel gates, prepared entries with a window ring)
+_APPEND_KINDS = [
+    (torch.float32, torch.float32, False, True), (torch.float32, torch.float32, True, False),
+    (torch.float32, torch.float8_e4m3fn, False, False), (torch.float32, torch.float8_e4m3fn, True, False),
+    (torch.bfloat16, torch.bfloat16, False, True), (torch.bfloat16, torch.bfloat16, True, True),
+    (torch.bfloat16, torch.float8_e4m3fn, False, False), (torch.bfloat16, torch.float8_e4m3fn, True, False),
+]
+
+
+@pytest.mark.parametrize("group", [(0, 1, 2, 3), (4, 5, 6, 7), (5, 6, 4)])
+def test_kv_append_batch_matches_separate_calls(group):
+    """Every kind of append (f32 or bf16 tokens; a cache of their type or fp8
+    codes; one gate logit per token or per channel; prepared entries with a
+    window ring, or not) in batches of up to four, over 70 steps with
+    sequences that start late (position -1 before) and blocks of 4, 8 and 16
+    tokens with spans of one or two blocks: the batched launch leaves every
+    ring, cache and scale bitwise as the same appends made one by one."""
+    say(f"kv_append_batch, kinds {group}")
+    B, D, steps, Rr, Rw = 3, 64, 70, 32, 8
+    starts = np.array([0, 3, 10])
+    prep = dict(rope_dims=16, rope_base=10000.0, entry_pos_offset=0, rms_eps=1e-6)
+    g = torch.Generator().manual_seed(sum(group) + 101)
+    cfg, toks = [], []
+    for n_, kind in enumerate(group):
+        act, cdt, pc, pw = _APPEND_KINDS[kind]
+        m = (4, 8, 16, 4)[n_]
+        span = m * (1 + n_ % 2)
+        N = steps // m
+        cfg.append((act, cdt, pc, pw, m, span, N))
+        toks.append((torch.randn(steps, B, D, generator=g).to(act),
+                     torch.randn((steps, B, D) if pc else (steps, B), generator=g)))
+
+    def state():
+        out = []
+        for act, cdt, pc, pw, m, span, N in cfg:
+            st = dict(raw=torch.zeros(B, Rr, D, dtype=act, device=DEV),
+                      graw=torch.zeros((B, Rr, D) if pc else (B, Rr), dtype=torch.float32, device=DEV),
+                      win=torch.zeros(B, Rw, D, dtype=act, device=DEV) if pw else None,
+                      scale=torch.zeros(B, N, dtype=torch.float32, device=DEV) if cdt == torch.float8_e4m3fn else None)
+            st["cache"] = (torch.zeros(B, N, D, dtype=torch.uint8, device=DEV).view(torch.float8_e4m3fn)
+                           if cdt == torch.float8_e4m3fn else torch.zeros(B, N, D, dtype=cdt, device=DEV))
+            out.append(st)
+        return out
+
+    one, bat = state(), state()
+    for s in range(steps):
+        t = np.where(s >= starts, s - starts, -1).astype(np.int32)
+        pos = torch.from_numpy(t).to(DEV)
+        calls = []
+        for (act, cdt, pc, pw, m, span, N), (x, gt), a, b in zip(cfg, toks, one, bat):
+            xs, gs = _d(x[s]), _d(gt[s])
+            kw = dict(m=m, span=span, cache_scale=a["scale"], win_ring=a["win"], prep=prep if pw else None)
+            cakv.kv_append(xs, gs, pos, a["raw"], a["graw"], a["cache"], **kw)
+            calls.append(dict(x_tok=xs, gate_tok=gs, raw_ring=b["raw"], gate_ring=b["graw"], cache=b["cache"], m=m,
+                              span=span, cache_scale=b["scale"], win_ring=b["win"], prep=prep if pw else None))
+        cakv.kv_append_batch(calls, pos)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(one, bat)):
+        for key in ("raw", "graw", "win", "cache", "scale"):
+            if a[key] is None:
+                continue
+            x, y = a[key], b[key]
+            if x.dtype == torch.float8_e4m3fn:
+                x, y = x.view(torch.uint8), y.view(torch.uint8)
+            assert torch.equal(x, y), (group[i], key)
+        assert torch.count_nonzero(a["cache"].view(torch.uint8) if a["cache"].dtype == torch.float8_e4m3fn
+                                   else a["cache"]) > 0  # entries were written

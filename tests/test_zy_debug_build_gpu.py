@@ -4,7 +4,7 @@ the XCD mapping's range, the streaming append's span inside its ring) runs a
 selection of the parity tests, each against the oracle as in its own module:
 the compressor (both kernels), the indexer's select paths (including tied
 blocks at the k-th place), sparse and dense attention with splits and edge
-cases, the streaming append and the indexer backward.  The binding's cached
+cases, the streaming append (one call and batched) and the indexer backward.  The binding's cached
 library is swapped for the debug one for the length of each test.  Skipped
 when the debug build is absent (python -m compressed_attention_kv_amd.build
 --debug, which __graft_entry__.build() also runs)."""
@@ -59,6 +59,7 @@ def test_debug_attention():
 def test_debug_compressor_variants_and_streaming():
     S.test_kv_compress_ex(4, 8, True, "bf16")
     S.test_streaming_decode_steps("cold_start_overlap_per_channel")
+    S.test_kv_append_batch_matches_separate_calls((4, 5, 6, 7))
 
 
 def test_debug_indexer_fp8_whole_line_loads():
