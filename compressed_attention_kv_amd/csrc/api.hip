@@ -421,7 +421,8 @@ int cakv_kv_append_batch(const cakv_append_call* calls, int32_t n, const int32_t
                                    c.m, c.span, c.prep, ab.a[i], ab.kind[i], empty);
         if (rc) return rc;
         // the appends run concurrently: no two may write the same buffer
-        for (int k = 0; k < i; ++k) {
+        // (with no tokens nothing runs, and the buffers may be NULL)
+        for (int k = 0; k < i && !empty; ++k) {
             const cakv_append_call& o = calls[k];
             REQUIRE(c.raw_ring != o.raw_ring && c.gate_ring != o.gate_ring &&
                         (!c.win_ring || c.win_ring != o.win_ring) && (!c.cache || c.cache != o.cache) &&

@@ -437,3 +437,11 @@ def test_append_batch_rejects_bad_arguments(lib, calls, n, code):
     arr = None if calls is None else (cakv.AppendCall * len(calls))(*calls)
     assert lib.cakv_kv_append_batch(arr, n, FAKE, 4, None) == code
     assert lib.cakv_last_error()
+
+
+def test_append_batch_with_no_tokens_runs_nothing(lib):
+    # as cakv_kv_append: B = 0 validates the sizes and launches nothing, NULL buffers included
+    calls = (cakv.AppendCall * 2)(_append_call(x_tok=None, gate_tok=None, raw_ring=None, gate_ring=None, cache=None),
+                                  _append_call(x_tok=None, gate_tok=None, raw_ring=None, gate_ring=None, cache=None))
+    assert lib.cakv_kv_append_batch(calls, 2, None, 0, None) == 0
+    assert lib.cakv_kv_append_batch(calls, 2, None, -1, None) == -1
