@@ -436,7 +436,7 @@ int cakv_kv_append_batch(const cakv_append_call* calls, int32_t n, const int32_t
 
 size_t cakv_indexer_topk_workspace(int64_t B, int64_t Q, int64_t N, int32_t k) {
     if (B < 0 || Q < 0 || N < 0 || k < 1) return 0;
-    return cakv::indexer_workspace_bytes(B * Q, N, k);
+    return cakv::indexer_workspace_bytes(B, Q, N, k);
 }
 
 int cakv_indexer_topk(const void* q_idx, int q_dtype, const float* w, const void* k_idx, int k_dtype,
@@ -449,7 +449,7 @@ int cakv_indexer_topk(const void* q_idx, int q_dtype, const float* w, const void
                           empty);
     if (rc || empty) return rc;
     const int64_t BQ = B * Q;
-    const size_t need = cakv::indexer_workspace_bytes(BQ, N, k);
+    const size_t need = cakv::indexer_workspace_bytes(B, Q, N, k);
     REQUIRE(workspace_bytes >= need, CAKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
     REQUIRE(workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, CAKV_EWORKSPACE,
             "workspace must be non-NULL and 256-byte aligned");
@@ -465,7 +465,7 @@ int cakv_indexer_topk_noalloc(const void* q_idx, int q_dtype, const float* w, co
                           empty);
     if (rc || empty) return rc;
     const int64_t BQ = B * Q;
-    const size_t need = cakv::indexer_workspace_bytes(BQ, N, k);
+    const size_t need = cakv::indexer_workspace_bytes(B, Q, N, k);
     REQUIRE(need <= kScratchBytes, CAKV_EWORKSPACE,
             "B*Q=%lld queries over N=%lld entries need %zu bytes of scratch, more than the %zu bytes the "
             "allocation-free call holds per GPU; use cakv_indexer_topk with a workspace",

@@ -125,6 +125,7 @@ struct IndexerArgs {
     const float* k_scale;
     const int32_t* q_pos;
     int32_t* idx;
+    const void* kpack;   // fp8 keys repacked for the score kernel when Q > 1 (see indexer.hip), else NULL
     uint32_t* keys;      // [BQ][N] order-preserving score keys
     uint32_t* hist;      // [BQ][kHistStride] key histograms (top 11 bits; next 11 bits) + counters
     uint32_t* cand_a;    // [BQ][kTopkCap] entries above the threshold bin
@@ -198,7 +199,7 @@ struct IndexerBwdArgs {
 };
 int launch_indexer_bwd(const IndexerBwdArgs& a, int64_t BQ, bool q_f32, bool fp8, hipStream_t stream);
 
-size_t indexer_workspace_bytes(int64_t BQ, int64_t N, int32_t k);
+size_t indexer_workspace_bytes(int64_t B, int64_t Q, int64_t N, int32_t k);
 int launch_indexer_topk(IndexerArgs& a, int64_t BQ, bool fp8_mode, void* ws, hipStream_t stream);
 
 }  // namespace cakv

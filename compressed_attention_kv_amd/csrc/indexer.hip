@@ -20,12 +20,17 @@
 //        exchange.  The per-entry scale multiplies the final sum (a power of
 //        two, so exact up to rounding order).  With one query per sequence
 //        (decode) the keys arrive by whole-line nontemporal loads and a
-//        transpose in each quad of lanes (COAL below).
+//        transpose in each quad of lanes (kLoadLines below); with several
+//        (prefill) a pack pass first copies the keys into a layout where each
+//        load instruction reads 1 KiB of consecutive bytes (kLoadPacked).
 //        fp32 mode: one thread per entry runs the canonical fmaf chains.
 //      Each score is written as an order-preserving 32-bit key, and counted
 //      in an exact histogram of the top 11 key bits (LDS, then HBM atomics).
 //   2. refine (same grid): lists the entries above the threshold bin and in
 //      it; histograms the next 11 bits of the ones in it (see top-k below).
+//      When the fp8 score grid has one workgroup per query (many queries, as
+//      in a prefill chunk), that workgroup does this work itself after its
+//      score loop, and neither 0 nor 2 is launched.
 //   3. select: one workgroup per query ranks the threshold bin's entries and
 //      writes the k winners in index order.
 #include "cakv_device.hpp"
@@ -48,6 +53,10 @@ __device__ __forceinline__ void flush_hist(const uint32_t* h, uint32_t* g, int n
         if (c) __hip_atomic_fetch_add(g + i, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
+
+// the refine pass's work done by the score workgroup itself when it is the
+// only one of its query (defined with the top-k below)
+__device__ __forceinline__ void fused_refine(const IndexerArgs& a, int64_t bq, int64_t nvis, const uint32_t* h1);
 
 // ------------------------------------------------------------------ fp8 mode
 // HT: head tiles of 32 (HI = 32*HT); KS: MFMA k-steps of 16 (dI = 16*KS).
@@ -93,18 +102,45 @@ __device__ __forceinline__ void quad_transpose4(u32x4 (&v)[4], int lane) {
     }
 }
 
-// COAL (128-dim keys, one query per sequence): whole-line loads.  Lane
-// (entry lrow, half lh) multiplies the 64 bytes of its half row as four
-// 16-byte chunks; the ordinary loads give it those chunks directly, so each
-// load instruction covers a quarter of 32 cache lines and the other three
-// instructions find the lines in cache.  With COAL, instruction j of lane
-// 4q + s loads chunk s of the half row that lane 4q + j multiplies, so each
-// instruction reads eight whole rows (both halves: quads q and q + 8), the
-// loads are nontemporal (nothing is read twice when each sequence has one
-// query), and a transpose in each quad of lanes hands every lane its own
-// chunks.
-template <int HT, int KS, bool COAL>
+// How a lane gets the NLD 16-byte chunks of the half row it multiplies (lane
+// (entry lrow, half lh) of a 32-entry group):
+//   kLoadDirect: loads them from the row; each load instruction covers a
+//     quarter of 32 cache lines and the other instructions find the lines
+//     in cache.
+//   kLoadLines (128-dim keys, one query per sequence): instruction j of lane
+//     4q + s loads chunk s of the half row that lane 4q + j multiplies, so
+//     each instruction reads eight whole rows (both halves: quads q and
+//     q + 8), the loads are nontemporal (nothing is read twice when each
+//     sequence has one query), and a transpose in each quad of lanes hands
+//     every lane its own chunks.
+//   kLoadPacked (several queries per sequence): the pack pass has stored
+//     chunk i of every lane of group g at 16-byte slot (g NLD + i) 64 + lane
+//     of the sequence's packed keys, so instruction i of the wave reads 1 KiB
+//     of consecutive bytes; the keys are then read by every query of the
+//     sequence, and packed once per call.
+constexpr int kLoadDirect = 0, kLoadLines = 1, kLoadPacked = 2;
+
+// The pack pass: for sequence b and 32-entry group g, slot (g NLD + i) 64 + l
+// holds bytes [(l >> 5) DI/2 + 16 i, + 16) of row min(32 g + (l & 31), N - 1).
+// One thread per slot; G = ceil(N / 32) groups per sequence.
+template <int NLD>
+__global__ __launch_bounds__(256) void idx_pack_keys_kernel(const IndexerArgs a, int64_t B, int64_t G) {
+    constexpr int DI = 32 * NLD, HALF = DI / 2;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= B * G * NLD * 64) return;
+    const int l = (int)(t & 63);
+    const int64_t gi = t >> 6;
+    const int i = (int)(gi % NLD);
+    const int64_t bg = gi / NLD, b = bg / G, g = bg % G;
+    const int64_t row = min(32 * g + (l & 31), a.N - 1);
+    CAKV_DCHECK(b < B && row >= 0);
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.k_idx) + (b * a.N + row) * DI + (l >> 5) * HALF + 16 * i;
+    reinterpret_cast<u32x4*>(const_cast<void*>(a.kpack))[t] = *reinterpret_cast<const u32x4*>(src);
+}
+
+template <int HT, int KS, int LOAD>
 __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs a) {
+    constexpr bool COAL = LOAD == kLoadLines, PACKED = LOAD == kLoadPacked;
     constexpr int DI = 16 * KS;
     constexpr int HALF = DI / 2;        // bytes of a key row per half-wave lane
     constexpr int NLD = HALF / 16;      // 16-byte chunks per lane
@@ -125,6 +161,8 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_idx) + b * a.N * DI;
     const float* sbase = a.k_scale + b * a.N;
     uint32_t* kout = a.keys + bq * a.N;
+    const int64_t G = (a.N + 31) / 32;  // packed groups per sequence
+    const u32x4* pbase = PACKED ? reinterpret_cast<const u32x4*>(a.kpack) + b * G * NLD * 64 : nullptr;
 
     // group n's half rows and scales (rows past the cache end read its last
     // row: in bounds, never scored)
@@ -148,6 +186,13 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
                 g.c[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + rj * DI + lh * HALF) + ch);
             }
             g.sc = __builtin_nontemporal_load(sbase + row);
+        } else if constexpr (PACKED) {
+            // (a wave with no group reads the sequence's last group)
+            const int64_t gi = min((first + 128 * (int64_t)nn) / 32, G - 1);
+            CAKV_DCHECK(gi >= 0 && (first + 128 * (int64_t)nn) % 32 == 0);
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) g.c[i] = pbase[(gi * NLD + i) * 64 + lane];
+            g.sc = sbase[row];
         } else {
             const u32x4* src = reinterpret_cast<const u32x4*>(kbase + row * DI + lh * HALF);
 #pragma unroll
@@ -233,6 +278,10 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
         }
     }
     __syncthreads();
+    if (a.n_chunks == 1) {  // (uniform) the query's only workgroup: its histogram is the query's
+        fused_refine(a, bq, nvis, hist);
+        return;
+    }
     flush_hist(hist, a.hist + bq * kHistStride, 256);
 }
 
@@ -405,22 +454,6 @@ __device__ void find_bin_wave(const uint32_t* h, uint32_t want, uint32_t* out) {
     }
 }
 
-// Keys [j_begin, j_end) of a query, KPT per thread per batch, all of a
-// batch's loads issued before any is used; f(j, key) for each.
-template <int NT, int KPT, typename F>
-__device__ __forceinline__ void for_keys(const uint32_t* keys, int64_t j_begin, int64_t j_end, F f) {
-    for (int64_t j0 = j_begin; j0 < j_end; j0 += (int64_t)NT * KPT) {  // uniform trip count
-        uint32_t kv[KPT];
-#pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            const int64_t j = j0 + (int64_t)u * NT + threadIdx.x;
-            kv[u] = j < j_end ? keys[j] : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < KPT; ++u) f(j0 + (int64_t)u * NT + threadIdx.x, kv[u]);
-    }
-}
-
 // One workgroup per query's histogram block.
 __global__ __launch_bounds__(256) void idx_zero_kernel(u32x4* p) {
     u32x4* q = p + (int64_t)blockIdx.x * (kHistStride / 4);
@@ -566,6 +599,56 @@ __device__ __forceinline__ uint64_t rank_value(uint32_t key, int64_t j) {
     return ((uint64_t)(~key) << 32) | (uint64_t)j;
 }
 
+// Keys [j0, j0 + NT KPT) of a query that lie below j_end (others read as 0),
+// one per thread and u, all requested before any is used.
+template <int NT, int KPT>
+__device__ __forceinline__ void load_key_batch(const uint32_t* keys, int64_t j0, int64_t j_end, uint32_t (&dst)[KPT]) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+        const int64_t j = j0 + (int64_t)u * NT + threadIdx.x;
+        dst[u] = j < j_end ? keys[j] : 0u;
+    }
+}
+
+// The refine work on entries [j_begin, j_end) of a query: lists the ones
+// above the level-1 threshold bin b1 (list A) and in it (list B, if it fits),
+// and counts the next 11 key bits of b1's entries into h2 (if level2).
+// cnt_a and cnt_b are the lists' append counters; kv holds the first batch
+// of keys, already requested (each batch requests the next before it is
+// classified).  Every thread of the workgroup (256) calls it.
+template <int KPT>
+__device__ __forceinline__ void refine_entries(const uint32_t* keys, int64_t j_begin, int64_t j_end, uint32_t b1,
+                                               bool fits, bool level2, uint32_t (&kv)[KPT], uint32_t* h2,
+                                               uint32_t* list_a, uint32_t* cnt_a, uint64_t* list_b,
+                                               uint32_t* cnt_b, uint32_t* ash) {
+    constexpr int NT = 256;
+    constexpr int64_t STEP = (int64_t)NT * KPT;
+    const int tid = threadIdx.x;
+    for (int64_t j0 = j_begin; j0 < j_end; j0 += STEP) {  // uniform trip count
+        uint32_t jv[KPT], kn[KPT];
+        uint64_t rv[KPT];
+        bool sa[KPT], sb[KPT];
+        const bool more = j0 + STEP < j_end;  // uniform
+        if (more) load_key_batch<NT, KPT>(keys, j0 + STEP, j_end, kn);
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) jv[u] = (uint32_t)(j0 + (int64_t)u * NT + tid);
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const bool in = (int64_t)j0 + (int64_t)u * NT + tid < j_end;
+            const uint32_t top = kv[u] >> 21;
+            sa[u] = in && top > b1;
+            sb[u] = in && top == b1;
+            rv[u] = rank_value(kv[u], jv[u]);
+            if (level2 && sb[u]) atomicAdd(&h2[(kv[u] >> 10) & (kHistBins - 1)], 1u);
+        }
+        block_append2<NT, KPT>(list_a, cnt_a, sa, jv, fits, list_b, cnt_b, sb, rv, ash);
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < KPT; ++u) kv[u] = kn[u];
+        }
+    }
+}
+
 // Refine, on the score grid: every workgroup of a query lists its entries
 // above the level-1 threshold bin b1 (list A) and in it (list B) and adds
 // the level-2 histogram of b1.  (Handing the lists to one workgroup inside
@@ -587,20 +670,10 @@ __global__ __launch_bounds__(256) void idx_refine_kernel(const IndexerArgs a) {
     const uint32_t* keys = a.keys + bq * a.N;
     uint32_t* qh = a.hist + bq * kHistStride;
     uint32_t* cnt = qh + 2 * kHistBins;  // [0] list A, [1] list B, [2] b1, [3] count above b1
-    uint32_t* list_a = a.cand_a + bq * kTopkCap;
-    uint64_t* list_b = a.cand_b + bq * kCandCap;
     // keys are requested one round ahead; the first round before the
     // threshold search, so that its latency overlaps the search
-    constexpr int64_t STEP = (int64_t)NT * KPT;
     uint32_t kv[KPT];
-    auto load_keys = [&](int64_t j0, uint32_t* dst) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            const int64_t j = j0 + (int64_t)u * NT + tid;
-            dst[u] = j < j_end ? keys[j] : 0u;
-        }
-    };
-    load_keys(j_begin, kv);
+    load_key_batch<NT, KPT>(keys, j_begin, j_end, kv);
     for (int i = tid; i < kHistBins; i += NT) h2[i] = 0u;
     uint32_t b1, a1;
     find_bin<NT>(qh, (uint32_t)k, wsum, info, &b1, &a1);  // (syncs, so h2 is clear)
@@ -610,34 +683,52 @@ __global__ __launch_bounds__(256) void idx_refine_kernel(const IndexerArgs a) {
         cnt[2] = b1;
         cnt[3] = a1;
     }
-
-    // ---- this workgroup's entries
-    for (int64_t j0 = j_begin; j0 < j_end; j0 += STEP) {  // uniform trip count
-        uint32_t jv[KPT], kn[KPT];
-        uint64_t rv[KPT];
-        bool sa[KPT], sb[KPT];
-        const bool more = j0 + STEP < j_end;  // uniform
-        if (more) load_keys(j0 + STEP, kn);
-#pragma unroll
-        for (int u = 0; u < KPT; ++u) jv[u] = (uint32_t)(j0 + (int64_t)u * NT + tid);
-#pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            const bool in = (int64_t)j0 + (int64_t)u * NT + tid < j_end;
-            const uint32_t top = kv[u] >> 21;
-            sa[u] = in && top > b1;
-            sb[u] = in && top == b1;
-            rv[u] = rank_value(kv[u], jv[u]);
-            if (level2 && sb[u]) atomicAdd(&h2[(kv[u] >> 10) & (kHistBins - 1)], 1u);
-        }
-        block_append2<NT, KPT>(list_a, cnt, sa, jv, fits, list_b, cnt + 1, sb, rv, ash);
-        if (more) {
-#pragma unroll
-            for (int u = 0; u < KPT; ++u) kv[u] = kn[u];
-        }
-    }
+    refine_entries<KPT>(keys, j_begin, j_end, b1, fits, level2, kv, h2, a.cand_a + bq * kTopkCap, cnt,
+                        a.cand_b + bq * kCandCap, cnt + 1, ash);
     if (level2) {
         __syncthreads();
         flush_hist(h2, qh + kHistBins, NT);
+    }
+}
+
+// The refine work done by a query's only score workgroup, after its score
+// loop: h1 (LDS) is then the query's whole level-1 histogram, so the
+// threshold comes from it, the list counters live in LDS, and both
+// histogram levels and the threshold are written out for the select pass
+// without atomics.  The workgroup reads back the keys it wrote (its own
+// stores, ordered before the loads by the barrier after the score loop);
+// meanwhile the CU's other score workgroup keeps its matrix cores busy.
+// Nothing here needs the histogram block cleared beforehand, so calls whose
+// score grid has one workgroup per query launch neither the clearing nor the
+// refine kernel.
+__device__ __forceinline__ void fused_refine(const IndexerArgs& a, int64_t bq, int64_t nvis, const uint32_t* h1) {
+    __shared__ uint32_t h2[kHistBins];
+    __shared__ uint32_t wsum[5];
+    __shared__ uint32_t info[2];
+    __shared__ uint32_t ash[2 * 4 + 2];
+    __shared__ uint32_t lcnt[2];
+    constexpr int NT = 256, KPT = 8;
+    const int tid = threadIdx.x;
+    const uint32_t* keys = a.keys + bq * a.N;
+    uint32_t* qh = a.hist + bq * kHistStride;
+    uint32_t kv[KPT];
+    load_key_batch<NT, KPT>(keys, 0, nvis, kv);
+    for (int i = tid; i < kHistBins; i += NT) h2[i] = 0u;
+    if (tid < 2) lcnt[tid] = 0u;
+    uint32_t b1, a1;
+    find_bin<NT>(h1, (uint32_t)a.k, wsum, info, &b1, &a1);  // (syncs, so h2 and lcnt are clear)
+    const uint32_t nb1 = h1[b1];
+    const bool fits = nb1 <= (uint32_t)kCandCap, level2 = nb1 > kSmallBin;  // uniform
+    refine_entries<KPT>(keys, 0, nvis, b1, fits, level2, kv, h2, a.cand_a + bq * kTopkCap, lcnt,
+                        a.cand_b + bq * kCandCap, lcnt + 1, ash);  // (ends with a barrier)
+    static_assert(kHistBins % (4 * NT) == 0, "histogram copy in whole rounds");
+    for (int i = tid; i < kHistBins / 4; i += NT) {
+        reinterpret_cast<u32x4*>(qh)[i] = reinterpret_cast<const u32x4*>(h1)[i];
+        reinterpret_cast<u32x4*>(qh + kHistBins)[i] = reinterpret_cast<const u32x4*>(h2)[i];
+    }
+    if (tid == 0) {
+        qh[2 * kHistBins + 2] = b1;
+        qh[2 * kHistBins + 3] = a1;
     }
 }
 
@@ -811,14 +902,21 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(const IndexerAr
 }
 
 // Workspace: score keys [BQ][N], histograms [BQ][kHistStride], lists A
-// [BQ][kTopkCap] (entry indices) and B [BQ][kCandCap] (rank values), each
-// region 256-byte aligned.
+// [BQ][kTopkCap] (entry indices) and B [BQ][kCandCap] (rank values), and,
+// with several queries per sequence, the packed keys [B][ceil(N/32)][32 *
+// 128 bytes] (sized for the largest fp8 key width); each region 256-byte
+// aligned.
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t indexer_workspace_bytes(int64_t BQ, int64_t N, int32_t k) {
+static size_t packed_key_bytes(int64_t B, int64_t Q, int64_t N) {
+    return Q > 1 ? (size_t)B * (size_t)((N + 31) / 32) * 32 * 128 : 0;
+}
+
+size_t indexer_workspace_bytes(int64_t B, int64_t Q, int64_t N, int32_t k) {
     (void)k;
+    const int64_t BQ = B * Q;
     return al256((size_t)BQ * (size_t)N * 4) + al256((size_t)BQ * kHistStride * 4) +
-           al256((size_t)BQ * kTopkCap * 4) + al256((size_t)BQ * kCandCap * 8);
+           al256((size_t)BQ * kTopkCap * 4) + al256((size_t)BQ * kCandCap * 8) + al256(packed_key_bytes(B, Q, N));
 }
 
 int launch_indexer_topk(IndexerArgs& a, int64_t BQ, bool fp8_mode, void* ws, hipStream_t stream) {
@@ -831,27 +929,52 @@ int launch_indexer_topk(IndexerArgs& a, int64_t BQ, bool fp8_mode, void* ws, hip
     a.cand_a = reinterpret_cast<uint32_t*>(w);
     w += al256((size_t)BQ * kTopkCap * 4);
     a.cand_b = reinterpret_cast<uint64_t*>(w);
+    w += al256((size_t)BQ * kCandCap * 8);
+    const int64_t B = BQ / a.Q;
+    // several queries per sequence: the fp8 score kernel reads packed keys
+    const bool packed = fp8_mode && a.Q > 1 && a.N > 0;
+    a.kpack = packed ? w : nullptr;
     dim3 g1((unsigned)a.n_chunks, (unsigned)BQ);
+    // one fp8 score workgroup per query: it does the refine work itself
+    const bool fused = fp8_mode && a.n_chunks == 1;
     if (a.N > 0) {
         static_assert(kHistStride % 4 == 0, "histogram block in 16-byte units");
-        prof_mark("idx_zero_kernel", false, stream);
-        hipLaunchKernelGGL(idx_zero_kernel, dim3((unsigned)BQ), dim3(256), 0, stream, reinterpret_cast<u32x4*>(a.hist));
-        prof_mark("idx_zero_kernel", true, stream);
+        if (!fused) {
+            prof_mark("idx_zero_kernel", false, stream);
+            hipLaunchKernelGGL(idx_zero_kernel, dim3((unsigned)BQ), dim3(256), 0, stream,
+                               reinterpret_cast<u32x4*>(a.hist));
+            prof_mark("idx_zero_kernel", true, stream);
+        }
         if (fp8_mode) {
             if (!((a.HI == 32 || a.HI == 64) && (a.dI == 64 || a.dI == 128))) return -2;
+            if (packed) {
+                const int64_t G = (a.N + 31) / 32, n = B * G * 2 * a.dI;  // 16-byte slots
+                if ((size_t)n * 16 > packed_key_bytes(B, a.Q, a.N)) return -2;  // (dI <= 128 keeps this false)
+                prof_mark("idx_pack_keys_kernel", false, stream);
+                if (a.dI == 128)
+                    hipLaunchKernelGGL(idx_pack_keys_kernel<4>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                                       a, B, G);
+                else
+                    hipLaunchKernelGGL(idx_pack_keys_kernel<2>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                                       a, B, G);
+                prof_mark("idx_pack_keys_kernel", true, stream);
+            }
             prof_mark("idx_score_fp8_kernel", false, stream);
-            // whole-line nontemporal loads when each sequence's keys serve one query
-            const bool coal = a.Q == 1;
+            // one query per sequence: whole-line nontemporal loads (128-dim
+            // keys) or direct loads; several: the packed keys
+            const bool lines = a.Q == 1;
             if (a.HI == 64 && a.dI == 128) {
-                if (coal) hipLaunchKernelGGL((idx_score_fp8_kernel<2, 8, true>), g1, dim3(256), 0, stream, a);
-                else hipLaunchKernelGGL((idx_score_fp8_kernel<2, 8, false>), g1, dim3(256), 0, stream, a);
+                if (lines) hipLaunchKernelGGL((idx_score_fp8_kernel<2, 8, kLoadLines>), g1, dim3(256), 0, stream, a);
+                else hipLaunchKernelGGL((idx_score_fp8_kernel<2, 8, kLoadPacked>), g1, dim3(256), 0, stream, a);
             } else if (a.HI == 32 && a.dI == 128) {
-                if (coal) hipLaunchKernelGGL((idx_score_fp8_kernel<1, 8, true>), g1, dim3(256), 0, stream, a);
-                else hipLaunchKernelGGL((idx_score_fp8_kernel<1, 8, false>), g1, dim3(256), 0, stream, a);
+                if (lines) hipLaunchKernelGGL((idx_score_fp8_kernel<1, 8, kLoadLines>), g1, dim3(256), 0, stream, a);
+                else hipLaunchKernelGGL((idx_score_fp8_kernel<1, 8, kLoadPacked>), g1, dim3(256), 0, stream, a);
             } else if (a.HI == 64 && a.dI == 64) {
-                hipLaunchKernelGGL((idx_score_fp8_kernel<2, 4, false>), g1, dim3(256), 0, stream, a);
+                if (lines) hipLaunchKernelGGL((idx_score_fp8_kernel<2, 4, kLoadDirect>), g1, dim3(256), 0, stream, a);
+                else hipLaunchKernelGGL((idx_score_fp8_kernel<2, 4, kLoadPacked>), g1, dim3(256), 0, stream, a);
             } else {
-                hipLaunchKernelGGL((idx_score_fp8_kernel<1, 4, false>), g1, dim3(256), 0, stream, a);
+                if (lines) hipLaunchKernelGGL((idx_score_fp8_kernel<1, 4, kLoadDirect>), g1, dim3(256), 0, stream, a);
+                else hipLaunchKernelGGL((idx_score_fp8_kernel<1, 4, kLoadPacked>), g1, dim3(256), 0, stream, a);
             }
             prof_mark("idx_score_fp8_kernel", true, stream);
         } else {
@@ -859,9 +982,11 @@ int launch_indexer_topk(IndexerArgs& a, int64_t BQ, bool fp8_mode, void* ws, hip
             hipLaunchKernelGGL(idx_score_f32_kernel, g1, dim3(256), 0, stream, a);
             prof_mark("idx_score_f32_kernel", true, stream);
         }
-        prof_mark("idx_refine_kernel", false, stream);
-        hipLaunchKernelGGL(idx_refine_kernel, g1, dim3(256), 0, stream, a);
-        prof_mark("idx_refine_kernel", true, stream);
+        if (!fused) {
+            prof_mark("idx_refine_kernel", false, stream);
+            hipLaunchKernelGGL(idx_refine_kernel, g1, dim3(256), 0, stream, a);
+            prof_mark("idx_refine_kernel", true, stream);
+        }
     }
     prof_mark("idx_select_kernel", false, stream);
     hipLaunchKernelGGL(idx_select_kernel, dim3((unsigned)BQ), dim3(kSelThreads), 0, stream, a);

@@ -182,9 +182,11 @@ int cakv_kv_prepare(const void* kv_in, void* kv_out, int act_dtype, int64_t B, i
  * {64, 128}; k 1 .. 4096; N < 2^31.
  * Workspace: at least cakv_indexer_topk_workspace(B, Q, N, k) bytes, 256-byte
  * aligned; its contents on entry do not matter.  The size depends only on
- * B*Q and N: both modes share the top-k stage, whose buffers (one 4-byte
+ * B, Q and N: both modes share the top-k stage, whose buffers (one 4-byte
  * score key per entry, per-query histograms and candidate lists) do not
- * depend on the key or query dtype, so the query takes no dtype argument.
+ * depend on the key or query dtype, and with Q > 1 it also holds a copy of
+ * the keys repacked for the score kernel (B * ceil(N/32) * 4 KiB, sized for
+ * dI = 128), so the query takes no dtype argument.
  * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE.
  * ------------------------------------------------------------------------- */
 size_t cakv_indexer_topk_workspace(int64_t B, int64_t Q, int64_t N, int32_t k);
@@ -205,7 +207,7 @@ int cakv_indexer_topk(const void* q_idx, int q_dtype, const float* w, const void
  * device address with that device current.  Calls whose
  * cakv_indexer_topk_workspace(B, Q, N, k) exceeds the array return
  * CAKV_EWORKSPACE (for example B*Q = 8 queries over N = 262,144 entries need
- * about 9 MB; B*Q = 64 queries over 262,144 entries still fit).  Every call
+ * about 9 MB; up to 58 one-query sequences over 262,144 entries fit).  Every call
  * on one GPU shares that GPU's array, and each call clears what it needs
  * cleared itself: calls that can overlap on one GPU (two streams, two
  * threads) race and must be serialised by the caller.

@@ -201,18 +201,20 @@ def test_indexer_fp8_recall(name, over):
     assert recall >= 0.995 and gap <= 1e-3
 
 
-@pytest.mark.parametrize("N,k,HI", [(32768 + 77, 1024, 64), (5000, 64, 64), (9000, 512, 32)])
-def test_indexer_fp8_whole_line_loads_match(N, k, HI):
+@pytest.mark.parametrize("N,k,HI,dI", [(32768 + 77, 1024, 64, 128), (5000, 64, 64, 128), (9000, 512, 32, 128),
+                                        (7000 + 5, 256, 64, 64), (3000, 128, 32, 64)])
+def test_indexer_fp8_whole_line_loads_match(N, k, HI, dI):
     """With one query per sequence the fp8 score kernel loads whole cache
-    lines and transposes them within lane quads; with several it loads each
-    lane's chunks directly.  Same arithmetic, so identical indices: two
-    sequences holding the same keys with one query each against one sequence
-    with both queries (a ragged entry count, a query with fewer visible
-    entries than k; 64 and 32 indexer heads, two or one head tiles per
-    wave)."""
-    say(f"indexer fp8 whole-line loads, N={N} k={k} HI={HI}")
+    lines and transposes them within lane quads (128-dim keys) or loads each
+    lane's chunks directly (64-dim keys); with several it first packs the
+    keys so that each load instruction reads 1 KiB of consecutive bytes.  The
+    same bytes reach the same lanes, so identical indices: two sequences
+    holding the same keys with one query each against one sequence with both
+    queries (a ragged entry count, a query with fewer visible entries than
+    k; 64 and 32 indexer heads, two or one head tiles per wave)."""
+    say(f"indexer fp8 whole-line and packed loads, N={N} k={k} HI={HI} dI={dI}")
     rng = np.random.default_rng(N + k)
-    dI, m = 128, 4
+    m = 4
     keys = rng.standard_normal((1, N, dI)).astype(np.float32)
     codes, scale = oracle.q8_quantize(keys)
     q = torch.from_numpy(rng.standard_normal((1, 2, HI, dI)).astype(np.float32)).to(torch.bfloat16)
@@ -224,6 +226,43 @@ def test_indexer_fp8_whole_line_loads_match(N, k, HI):
                             _d(np.concatenate([scale, scale])), _d(qpos.reshape(2, 1)), m, k).cpu().numpy().reshape(2, k)
     assert np.array_equal(sep, shared)
     assert (shared[1] == -1).sum() == k - k // 2
+
+
+@pytest.mark.parametrize("tied", [0, 3000, 5000, 10000])
+def test_indexer_fp8_fused_refine_matches(tied):
+    """With 512 or more queries the fp8 score grid has one workgroup per
+    query, and that workgroup does the refine pass's work itself (histogram
+    threshold from its own LDS, both levels written without atomics); with
+    fewer queries the score, clearing and refine kernels run apart.  The
+    scores are the same arithmetic, so the indices must be identical: 512
+    queries alternating between two (query, position) pairs against one call
+    with the two pairs.  A block of rows copied from one near the k-th place
+    gives a tie at the threshold of each size that takes another select path
+    (ranked by counting, radix select over the listed entries, radix select
+    over the whole key array)."""
+    say(f"indexer fp8 fused refine, tied block {tied}")
+    rng = np.random.default_rng(77 + tied)
+    HI, dI, m, N, k = 64, 128, 4, 20000 + 13, 1024
+    keys = rng.standard_normal((1, N, dI)).astype(np.float32)
+    codes, scale = oracle.q8_quantize(keys)
+    q2 = rng.standard_normal((1, 2, HI, dI)).astype(np.float32)
+    w2 = np.abs(rng.standard_normal((1, 2, HI))).astype(np.float32)
+    pos2 = np.array([[m * N + 2, m * (N // 3) + 1]], dtype=np.int32)
+    if tied:
+        scores, _ = oracle.indexer_scores(torch.from_numpy(q2).to(torch.bfloat16).float().numpy(), w2, pos2, m,
+                                          k_code=codes, k_scale=scale)
+        j700 = int(np.argsort(-scores[0].astype(np.float64), kind="stable")[700])
+        at = rng.choice(N, size=tied, replace=False)
+        codes[0, at] = codes[0, j700]
+        scale[0, at] = scale[0, j700]
+    qb = torch.from_numpy(q2).to(torch.bfloat16)
+    ref = cakv.indexer_topk(_d(qb), _d(w2), _d(codes), _d(scale), _d(pos2), m, k).cpu().numpy().reshape(2, k)
+    sel = np.arange(512) % 2
+    qm = qb[:, sel].contiguous()
+    got = cakv.indexer_topk(_d(qm), _d(w2[:, sel]), _d(codes), _d(scale), _d(pos2[:, sel]), m, k)
+    got = got.cpu().numpy().reshape(512, k)
+    assert np.array_equal(got, ref[sel])
+    assert (ref[0] >= 0).all() and (ref[1] >= 0).all()
 
 
 # ------------------------------------------------------------------ kv_prepare

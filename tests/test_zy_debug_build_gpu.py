@@ -47,6 +47,7 @@ def test_debug_indexer_select_paths():
     P.test_indexer_fp32_bit_exact_sizes(3000, 64, 8)
     for tied in (3000, 5000, 10000):
         P.test_indexer_fp32_tied_block_at_threshold(tied)
+        P.test_indexer_fp8_fused_refine_matches(tied)
 
 
 def test_debug_attention():
@@ -63,8 +64,9 @@ def test_debug_compressor_variants_and_streaming():
 
 
 def test_debug_indexer_fp8_whole_line_loads():
-    P.test_indexer_fp8_whole_line_loads_match(32768 + 77, 1024, 64)
-    P.test_indexer_fp8_whole_line_loads_match(9000, 512, 32)
+    P.test_indexer_fp8_whole_line_loads_match(32768 + 77, 1024, 64, 128)
+    P.test_indexer_fp8_whole_line_loads_match(9000, 512, 32, 128)
+    P.test_indexer_fp8_whole_line_loads_match(7000 + 5, 256, 64, 64)
 
 
 def test_debug_indexer_backward():
