@@ -118,6 +118,21 @@ def test_indexer_errors_and_workspace(lib):
     assert f(FAKE, cakv.F32, FAKE, FAKE, cakv.F32, FAKE, FAKE, 1, 1, 64, 4, 32, 4, 16, FAKE, FAKE, 1 << 20, None) == -1
 
 
+def test_indexer_workspace_holds_the_packed_keys(lib):
+    """With several queries per sequence the indexer workspace also holds the
+    keys repacked for the score kernel, B * ceil(N/32) * 4 KiB (sized for
+    128-dim keys), beyond what the same number of one-query sequences
+    needs; the size grows with B, Q and N."""
+    ws = lib.cakv_indexer_topk_workspace
+    for B, Q, N in [(1, 8192, 67584), (2, 3, 5000), (4, 2, 33), (1, 2, 1)]:
+        extra = ws(B, Q, N, 1024) - ws(B * Q, 1, N, 1024)
+        packed = B * ((N + 31) // 32) * 32 * 128
+        assert packed <= extra <= packed + 256, (B, Q, N)
+    sizes = [ws(B, Q, N, 1024) for B, Q, N in [(1, 1, 1000), (1, 2, 1000), (1, 3, 1000), (2, 3, 1000), (2, 3, 1001)]]
+    assert sizes == sorted(sizes)
+    assert ws(3, 1, 0, 64) > 0 and ws(1, 4, 0, 64) == ws(4, 1, 0, 64)  # no keys: nothing to pack
+
+
 def test_workspace_queries_are_monotone(lib):
     a = lib.cakv_sparse_mqa_workspace(32, 1, 128, 512, 1024, 128)
     b = lib.cakv_dense_mqa_workspace(32, 1, 128, 512, 8192, 128)
