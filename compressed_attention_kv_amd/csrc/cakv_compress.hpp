@@ -44,9 +44,13 @@ __device__ __forceinline__ void compress_entry(int n, RowF row, GateTokF gate_to
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[u][0] = acc[u][1] = acc[u][2] = acc[u][3] = 0.0f;
     if constexpr (!PER_CHANNEL) {
+        // (the loops are unrolled so that several tokens' loads are in flight
+        // at once; the arithmetic stays one chain in token order)
         float mx = -INFINITY;
+#pragma unroll 8
         for (int i = 0; i < n; ++i) mx = fmaxf(mx, gate_tok(i));
         float z = 0.0f;
+#pragma unroll 8
         for (int i = 0; i < n; ++i) {
             const float wgt = expf(gate_tok(i) - mx);
             z += wgt;

@@ -10,9 +10,10 @@
 // may be one logit per token and channel (each channel its own softmax).
 //
 // Layout and schedule: a workgroup of 256 threads owns `epw` consecutive
-// output entries; each entry is handled by D/4 threads that each own four
-// consecutive channels, so every load instruction of a wave reads contiguous
-// rows (coalesced streaming reduction, fp32 accumulation).  The gate softmax
+// output entries; each entry is handled by up to D/4 threads that each own
+// one to four 4-channel chunks (one for spans of 32 tokens or more), so every
+// load instruction of a wave reads contiguous rows (coalesced streaming
+// reduction, fp32 accumulation).  The gate softmax
 // is evaluated per thread from the block's m logits (a few L1-resident
 // scalars).  In fp8 mode the entry's max |c| is reduced through LDS and the
 // per-entry power-of-two scale is derived exactly from the fp32 exponent.
@@ -269,11 +270,14 @@ int launch_kv_compress(const void* x, int x_dtype, const float* gate, bool gate_
     const int64_t total = B * nblk;
     if (total == 0) return 0;
     const int nch = (int)(D / 4);
-    // up to four chunks per thread; threads per entry a power of two so that
-    // entries never straddle a wave unevenly
+    // up to four chunks per thread (one per thread for long spans, whose
+    // entries are few and each a long chain of tokens: m = 128 compresses
+    // 8,192 tokens into only 64 entries); threads per entry a power of two so
+    // that entries never straddle a wave unevenly
+    const int cpt = span >= 32 ? 1 : 4;
     int tpe = 1;
-    while (tpe * 4 < nch) tpe <<= 1;
-    if (tpe > 256) return -2;
+    while (tpe * cpt < nch && tpe < 256) tpe <<= 1;
+    if (nch > 4 * tpe) return -2;
     const int epw = 256 / tpe;
     const int64_t grid = (total + epw - 1) / epw;
     if (grid > 0x7fffffffLL) return -2;
