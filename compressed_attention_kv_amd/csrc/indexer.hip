@@ -742,8 +742,13 @@ constexpr int kBndCap = 4096;  // boundary entries ranked in LDS
 
 __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(const IndexerArgs a) {
     __shared__ uint32_t hs[2 * kHistBins];
-    __shared__ __attribute__((aligned(16))) uint64_t bnd[kBndCap];
-    __shared__ uint32_t bits[kBitmapWords];
+    // the ranked boundary entries and the winners' bitmap are never live at
+    // once (a barrier separates the ranking from the bitmap), so they share
+    // LDS: two select workgroups then fit on a CU
+    __shared__ __attribute__((aligned(16))) uint64_t bnd_bits[kBndCap];
+    static_assert(kBitmapWords * 4 <= kBndCap * 8, "the bitmap fits the boundary entries' space");
+    uint64_t* const bnd = bnd_bits;
+    uint32_t* const bits = reinterpret_cast<uint32_t*>(bnd_bits);
     __shared__ uint32_t win[kTopkCap];
     __shared__ uint32_t cnt256[256];
     __shared__ uint32_t wsum[kSelThreads / 64 + 1];
