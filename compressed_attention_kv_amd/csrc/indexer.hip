@@ -696,11 +696,11 @@ __global__ __launch_bounds__(256) void idx_refine_kernel(const IndexerArgs a) {
 // threshold comes from it, the list counters live in LDS, and both
 // histogram levels and the threshold are written out for the select pass
 // without atomics.  The workgroup reads back the keys it wrote (its own
-// stores, ordered before the loads by the barrier after the score loop);
-// meanwhile the CU's other score workgroup keeps its matrix cores busy.
+// stores, ordered before the loads by the barrier after the score loop).
 // Nothing here needs the histogram block cleared beforehand, so calls whose
 // score grid has one workgroup per query launch neither the clearing nor the
-// refine kernel.
+// refine kernel.  (The read-back is not hidden: the workgroups of a round,
+// whose queries see nearly equal entry counts, reach it together.)
 __device__ __forceinline__ void fused_refine(const IndexerArgs& a, int64_t bq, int64_t nvis, const uint32_t* h1) {
     __shared__ uint32_t h2[kHistBins];
     __shared__ uint32_t wsum[5];
