@@ -265,6 +265,34 @@ def test_indexer_fp8_fused_refine_matches(tied):
     assert (ref[0] >= 0).all() and (ref[1] >= 0).all()
 
 
+@pytest.mark.parametrize("N,Q", [(40, 1), (100, 3), (128, 2), (129, 1), (129, 4)])
+def test_indexer_fp8_small_key_arrays(N, Q):
+    """Key arrays of at most a few 128-entry granules: one score workgroup per
+    query (the refine work inside the score kernel, also with one query per
+    sequence), and for several queries per sequence the pack pass over fewer
+    than five 32-entry groups with a ragged last one.  Against the oracle on
+    the same dequantised keys (recall and the gap of any swapped entry), and
+    rows whose queries see fewer entries than k are the identity."""
+    say(f"indexer fp8 small key arrays N={N} Q={Q}")
+    rng = np.random.default_rng(1000 * N + Q)
+    B, HI, dI, m, k = 2, 64, 128, 4, 16
+    keys = rng.standard_normal((B, N, dI)).astype(np.float32)
+    codes, scale = oracle.q8_quantize(keys)
+    q = torch.from_numpy(rng.standard_normal((B, Q, HI, dI)).astype(np.float32)).to(torch.bfloat16)
+    w = rng.standard_normal((B, Q, HI)).astype(np.float32)
+    pos = rng.integers(m * (k + 1), m * N + 3, size=(B, Q)).astype(np.int32)
+    pos[0, 0] = m * N
+    pos[B - 1, Q - 1] = m * (k // 2) + 1  # fewer visible entries than k
+    scores, nvis = oracle.indexer_scores(q.float().numpy(), w, pos, m, k_code=codes, k_scale=scale)
+    ref = oracle.topk(scores, nvis, k)
+    got = cakv.indexer_topk(_d(q), _d(w), _d(codes), _d(scale), _d(pos), m, k).cpu().numpy().reshape(ref.shape)
+    recall, gap = _recall_check(got, ref, scores, nvis, k)
+    say(f"  recall {recall:.5f} worst relative gap of a swapped entry {gap:.2e}")
+    assert recall >= 0.995 and gap <= 1e-3
+    short = got[-1]
+    assert np.array_equal(short[: k // 2], np.arange(k // 2)) and (short[k // 2:] == -1).all()
+
+
 # ------------------------------------------------------------------ kv_prepare
 
 @pytest.mark.parametrize("dtype,D,r,m,off,j0,n,gamma,inplace", [
