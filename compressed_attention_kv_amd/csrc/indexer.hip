@@ -22,7 +22,9 @@
 //        (decode) the keys arrive by whole-line nontemporal loads and a
 //        transpose in each quad of lanes (kLoadLines below); with several
 //        (prefill) a pack pass first copies the keys into a layout where each
-//        load instruction reads 1 KiB of consecutive bytes (kLoadPacked).
+//        load instruction reads 1 KiB of consecutive bytes (kLoadPacked), and
+//        each step issues one group's MFMAs together with the previous
+//        group's reduction (software-pipelined, two accumulator sets).
 //        fp32 mode: one thread per entry runs the canonical fmaf chains.
 //      Each score is written as an order-preserving 32-bit key, and counted
 //      in an exact histogram of the top 11 key bits (LDS, then HBM atomics).
@@ -141,6 +143,12 @@ __global__ __launch_bounds__(256) void idx_pack_keys_kernel(const IndexerArgs a,
 template <int HT, int KS, int LOAD>
 __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs a) {
     constexpr bool COAL = LOAD == kLoadLines, PACKED = LOAD == kLoadPacked;
+    // software-pipelined steps with the head weights in LDS: packed loads
+    // (several queries per sequence, bound by instruction issue) at 64 heads
+    // of 128 dims.  (At other shapes the second accumulator set would cost a
+    // wave per SIMD; the decode kernel, bound by its key stream, was slower
+    // with it: 32-34 -> 35-36 us at 128K, 53-56 -> 59-63 us at 1M.)
+    constexpr bool PIPE = PACKED && HT == 2 && KS == 8;
     constexpr int DI = 16 * KS;
     constexpr int HALF = DI / 2;        // bytes of a key row per half-wave lane
     constexpr int NLD = HALF / 16;      // 16-byte chunks per lane
@@ -204,6 +212,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
     // A operand: query heads (rows) x features, k-permutation (s, half, e) -> half*DI/2 + 8s + e
     bf16x8 qa[HT][KS];
     float wv[HT][16];
+    __shared__ __attribute__((aligned(16))) float w_s[PIPE ? 32 * HT : 1];
     const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.q_idx) + bq * (int64_t)(32 * HT) * DI;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
@@ -211,9 +220,13 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
         for (int s = 0; s < KS; ++s)
             qa[ht][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                                                         qbase + (32 * ht + lrow) * DI + lh * HALF + 8 * s));
+        if constexpr (!PIPE) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) wv[ht][r] = a.w[bq * (32 * HT) + 32 * ht + 8 * (r >> 2) + 4 * lh + (r & 3)];
+            for (int r = 0; r < 16; ++r) wv[ht][r] = a.w[bq * (32 * HT) + 32 * ht + 8 * (r >> 2) + 4 * lh + (r & 3)];
+        }
     }
+    if constexpr (PIPE)
+        for (int i = tid; i < 32 * HT; i += 256) w_s[i] = a.w[bq * (32 * HT) + i];
     // The first groups are requested after the query operand and weights,
     // which are then awaited explicitly: had any of those loads still been
     // pending at the loop, the compiler would wait for them inside it on
@@ -227,12 +240,12 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
     wait_vm<kPD * (NLD + 1)>();
     __syncthreads();  // the histogram is clear
 
-    auto score_group = [&](int n, const Grp& g) __attribute__((always_inline)) {
+    // group g's dot products: acc[ht] = heads of tile ht x the group's entries
+    auto mfma_group = [&](const Grp& g, f32x16 (&acc)[HT]) __attribute__((always_inline)) {
         u32x4 c[NLD];  // chunk i of this lane's half row
 #pragma unroll
         for (int i = 0; i < NLD; ++i) c[i] = g.c[i];
         if constexpr (COAL) quad_transpose4(c, lane);
-        f32x16 acc[HT];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
@@ -251,12 +264,20 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
             for (int ht = 0; ht < HT; ++ht)
                 acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][s], kv, acc[ht], 0, 0, 0);
         }
+    };
+    // the weighted head sum of ReLU'd accumulators, times the entries' scales
+    auto reduce_group = [&](const f32x16 (&acc)[HT], float sc) __attribute__((always_inline)) -> float {
         float sum = 0.0f;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sum = __builtin_fmaf(wv[ht][r], relu_bits(acc[ht][r]), sum);
-        sum = xor32_sum(sum) * g.sc;
+            for (int r = 0; r < 16; ++r)
+                sum = __builtin_fmaf(PIPE ? w_s[32 * ht + 8 * (r >> 2) + 4 * lh + (r & 3)] : wv[ht][r],
+                                     relu_bits(acc[ht][r]), sum);
+        return xor32_sum(sum) * sc;
+    };
+    // group n's scores into the key array and the LDS histogram
+    auto put_group = [&](int n, float sum) __attribute__((always_inline)) {
         const int64_t j = first + 128 * (int64_t)n + lrow;
         if (lane < 32 && j < j_end) {
             const uint32_t key = score_key(sum);
@@ -264,17 +285,57 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
             atomicAdd(&hist[key >> 21], 1u);
         }
     };
-    for (int n0 = 0; n0 < ng; n0 += RS) {
+    auto score_group = [&](int n, const Grp& g) __attribute__((always_inline)) {
+        f32x16 acc[HT];
+        mfma_group(g, acc);
+        put_group(n, reduce_group(acc, g.sc));
+    };
+    if constexpr (PIPE) {
+        // Software-pipelined: a step issues group n's conversions and MFMAs
+        // and the reduction of group n - 1 (from the other accumulator set;
+        // the sets alternate with the group's parity, which the ring's even
+        // length keeps across turns), with no dependence between them, so the
+        // VALU work rides under the MFMAs; then it stores group n - 1's scores.
+        static_assert(RS % 2 == 0, "accumulator sets alternate by group parity");
+        f32x16 accb[2][HT];
 #pragma unroll
-        for (int u = 0; u < RS; ++u) {
-            const int n = n0 + u;
-            if (n >= ng) break;  // uniform
-            load_group(n + kPD, ring[(u + kPD) % RS]);
-            // the next group's loads go out before this group's work, and
-            // each group's work stays in its own step
-            __builtin_amdgcn_sched_barrier(0);
-            score_group(n, ring[u]);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) accb[1][ht][r] = 0.0f;
+        float scp = 0.0f;
+        for (int n0 = 0; n0 < ng; n0 += RS) {
+#pragma unroll
+            for (int u = 0; u < RS; ++u) {
+                const int n = n0 + u;
+                if (n >= ng) break;  // uniform
+                load_group(n + kPD, ring[(u + kPD) % RS]);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_group(ring[u], accb[u & 1]);
+                const float sp = reduce_group(accb[(u + 1) & 1], scp);  // (group n - 1; unused at n = 0)
+                scp = ring[u].sc;
+                __builtin_amdgcn_sched_barrier(0);
+                if (n > 0) put_group(n - 1, sp);
+            }
+        }
+        if (ng > 0) {  // the last group (a uniform branch keeps both sets in registers)
+            float sl;
+            if ((ng - 1) & 1) sl = reduce_group(accb[1], scp);
+            else sl = reduce_group(accb[0], scp);
+            put_group(ng - 1, sl);
+        }
+    } else {
+        for (int n0 = 0; n0 < ng; n0 += RS) {
+#pragma unroll
+            for (int u = 0; u < RS; ++u) {
+                const int n = n0 + u;
+                if (n >= ng) break;  // uniform
+                load_group(n + kPD, ring[(u + kPD) % RS]);
+                // the next group's loads go out before this group's work, and
+                // each group's work stays in its own step
+                __builtin_amdgcn_sched_barrier(0);
+                score_group(n, ring[u]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
     __syncthreads();
