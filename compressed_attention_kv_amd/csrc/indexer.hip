@@ -143,12 +143,15 @@ __global__ __launch_bounds__(256) void idx_pack_keys_kernel(const IndexerArgs a,
 template <int HT, int KS, int LOAD>
 __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs a) {
     constexpr bool COAL = LOAD == kLoadLines, PACKED = LOAD == kLoadPacked;
-    // software-pipelined steps with the head weights in LDS: packed loads
-    // (several queries per sequence, bound by instruction issue) at 64 heads
-    // of 128 dims.  (At other shapes the second accumulator set would cost a
-    // wave per SIMD; the decode kernel, bound by its key stream, was slower
-    // with it: 32-34 -> 35-36 us at 128K, 53-56 -> 59-63 us at 1M.)
+    // software-pipelined steps for packed loads (several queries per
+    // sequence, bound by instruction issue) at 64 heads of 128 dims; the
+    // second accumulator set takes the registers of two of the three groups
+    // in flight (the packed keys mostly come from L2).  (At other shapes it
+    // would cost a wave per SIMD; the decode kernel, bound by its key
+    // stream, was slower with it: 32-34 -> 35-36 us at 128K, 53-56 -> 59-63
+    // us at 1M.)
     constexpr bool PIPE = PACKED && HT == 2 && KS == 8;
+    constexpr int kPD = PIPE ? 1 : cakv::kPD;  // groups in flight ahead of the one multiplied
     constexpr int DI = 16 * KS;
     constexpr int HALF = DI / 2;        // bytes of a key row per half-wave lane
     constexpr int NLD = HALF / 16;      // 16-byte chunks per lane
@@ -212,7 +215,6 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
     // A operand: query heads (rows) x features, k-permutation (s, half, e) -> half*DI/2 + 8s + e
     bf16x8 qa[HT][KS];
     float wv[HT][16];
-    __shared__ __attribute__((aligned(16))) float w_s[PIPE ? 32 * HT : 1];
     const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.q_idx) + bq * (int64_t)(32 * HT) * DI;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
@@ -220,13 +222,9 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
         for (int s = 0; s < KS; ++s)
             qa[ht][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                                                         qbase + (32 * ht + lrow) * DI + lh * HALF + 8 * s));
-        if constexpr (!PIPE) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) wv[ht][r] = a.w[bq * (32 * HT) + 32 * ht + 8 * (r >> 2) + 4 * lh + (r & 3)];
-        }
+        for (int r = 0; r < 16; ++r) wv[ht][r] = a.w[bq * (32 * HT) + 32 * ht + 8 * (r >> 2) + 4 * lh + (r & 3)];
     }
-    if constexpr (PIPE)
-        for (int i = tid; i < 32 * HT; i += 256) w_s[i] = a.w[bq * (32 * HT) + i];
     // The first groups are requested after the query operand and weights,
     // which are then awaited explicitly: had any of those loads still been
     // pending at the loop, the compiler would wait for them inside it on
@@ -272,8 +270,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_fp8_kernel(const IndexerArgs
         for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                sum = __builtin_fmaf(PIPE ? w_s[32 * ht + 8 * (r >> 2) + 4 * lh + (r & 3)] : wv[ht][r],
-                                     relu_bits(acc[ht][r]), sum);
+                sum = __builtin_fmaf(wv[ht][r], relu_bits(acc[ht][r]), sum);
         return xor32_sum(sum) * sc;
     };
     // group n's scores into the key array and the LDS histogram
