@@ -26,6 +26,61 @@
 
 namespace cakv {
 
+// compress_entry with per-token gates for an entry whose threads fill whole
+// waves and whose span is at most 512 tokens: lane l evaluates the weights
+// of tokens l, l + 64, ... once, instead of every thread evaluating all of
+// them, and each token's weight reaches the wave by v_readlane.  The same
+// operations in the same order (the max; exp of each gate minus it; the
+// sum and each channel's fma chain in token order; the product with 1/z),
+// so the entries are bitwise those of compress_entry (and of the streaming
+// append).
+template <typename TIn>
+__device__ __forceinline__ void compress_entry_wave(int n, const TIn* xb, const float* gb, int D, const int ch[4],
+                                                    const bool live[4], float acc[4][4]) {
+    constexpr int WPL = 8;  // tokens per lane (n <= 512)
+    const int lane = threadIdx.x & 63;
+    float g[WPL];
+#pragma unroll
+    for (int k = 0; k < WPL; ++k) g[k] = lane + 64 * k < n ? gb[lane + 64 * k] : -INFINITY;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < WPL; ++k) mx = fmaxf(mx, g[k]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    float w[WPL];
+#pragma unroll
+    for (int k = 0; k < WPL; ++k) w[k] = lane + 64 * k < n ? expf(g[k] - mx) : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u][0] = acc[u][1] = acc[u][2] = acc[u][3] = 0.0f;
+    float z = 0.0f;
+#pragma unroll
+    for (int k = 0; k < WPL; ++k) {
+        if (64 * k >= n) break;  // uniform
+        const int nt = n - 64 * k < 64 ? n - 64 * k : 64;
+        const int wk = __builtin_bit_cast(int, w[k]);
+#pragma unroll 8
+        for (int t = 0; t < nt; ++t) {
+            const float wgt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wk, t));
+            z += wgt;
+            const TIn* r = xb + (int64_t)(64 * k + t) * D;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (live[u]) {
+                    float v[4];
+                    load4<TIn>(r + ch[u] * 4, v);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[u][c] = __builtin_fmaf(wgt, v[c], acc[u][c]);
+                }
+            }
+        }
+    }
+    const float rz = 1.0f / z;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[u][c] *= rz;
+}
+
 // OUTK: 0 = f32, 1 = bf16, 2 = fp8 E4M3 + per-entry scale.  PC: one gate
 // logit per token and channel ([B,T,D]) instead of one per token ([B,T]).
 // Entry j covers tokens [max(0, (j+1)m - span), (j+1)m).
@@ -62,9 +117,14 @@ __global__ __launch_bounds__(256) void kv_compress_kernel(const TIn* __restrict_
         const int64_t hi = (j + 1) * m, lo = hi - span > 0 ? hi - span : 0;
         const TIn* xb = x + (b * T + lo) * (int64_t)D;
         const float* gb = gate + (b * T + lo) * (PC ? (int64_t)D : 1);
-        compress_entry<TIn, PC>(
-            (int)(hi - lo), [&](int i) { return xb + (int64_t)i * D; }, [&](int i) { return gb[i]; },
-            [&](int i) { return gb + (int64_t)i * D; }, ch, ok, acc);
+        // (tpe >= 64: an entry's threads fill whole waves, so `live` and the
+        // entry are uniform per wave)
+        if (!PC && tpe >= 64 && hi - lo <= 512)
+            compress_entry_wave<TIn>((int)(hi - lo), xb, gb, D, ch, ok, acc);
+        else
+            compress_entry<TIn, PC>(
+                (int)(hi - lo), [&](int i) { return xb + (int64_t)i * D; }, [&](int i) { return gb[i]; },
+                [&](int i) { return gb + (int64_t)i * D; }, ch, ok, acc);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
